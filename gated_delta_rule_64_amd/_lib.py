@@ -1,0 +1,70 @@
+"""ctypes loader for libkda.so (the C ABI declared in include/kda.h).
+
+The library is built in-tree by ``gated_delta_rule_64_amd.build``.  There is
+no fallback: if the shared object is missing or fails to load, every entry
+point raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libkda.so")
+
+KDA_OK = 0
+KDA_ERR_INVALID_ARGUMENT = 1
+KDA_ERR_UNSUPPORTED = 2
+KDA_ERR_WORKSPACE_TOO_SMALL = 3
+KDA_ERR_HIP = 4
+KDA_F32 = 0
+KDA_BF16 = 1
+
+# name -> (restype, argtypes); mirrors include/kda.h
+_i32, _i64, _vp, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
+PROTOTYPES = {
+    "kda_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "kda_last_error_detail": (ctypes.c_char_p, []),
+    "kda_abi_version": (ctypes.c_int, []),
+    "kda_preprocess": (ctypes.c_int, [_i64, _i32, _i32, _i32, _vp, _i32, _i32] + [_vp] * 8 + [_vp] + [_vp] * 5 + [_vp]),
+    "kda_prefill_workspace_bytes": (_sz, [_i64, _i32, _i32, _i32, _i32, _i32]),
+    "kda_prefill_chunked": (ctypes.c_int, [_i64, _i32, _i32, _i32, _vp, _i32, _i32, _i32] + [_vp] * 6 +
+                            [_vp, _vp, _vp, _vp, _sz, _vp]),
+    "kda_decode_step": (ctypes.c_int, [_i32, _i32, _i32, _i32, _i32, _i32] + [_vp] * 6 + [_vp, _vp, _vp]),
+}
+
+
+class KdaError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        self.detail = detail
+        super().__init__(f"{status_string(status)}: {detail}")
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library (raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"libkda is not built ({LIB_PATH} missing); run __graft_entry__.build() "
+                               "or python -m gated_delta_rule_64_amd.build")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in PROTOTYPES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().kda_status_string(status).decode()
+
+
+def check(status: int) -> None:
+    if status != KDA_OK:
+        raise KdaError(status, lib().kda_last_error_detail().decode())

@@ -1,0 +1,245 @@
+// C ABI of libkda: argument validation, status codes and dispatch to the
+// kernels.  See include/kda.h for the contract of every entry point.
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <vector>
+
+#include "kda.h"
+#include "kda_internal.h"
+
+namespace {
+
+thread_local char g_detail[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_detail, sizeof(g_detail), fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int ok() {
+    g_detail[0] = '\0';
+    return KDA_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+    return fail(KDA_ERR_HIP, "%s failed: %s", what, hipGetErrorString(e));
+}
+
+bool valid_head_dim(int32_t d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+bool valid_dtype(int32_t t) { return t == KDA_F32 || t == KDA_BF16; }
+size_t dsize(int32_t t) { return t == KDA_BF16 ? 2 : 4; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Span {
+    const char* name;
+    const void* p;
+    size_t bytes;
+    bool writes;
+};
+
+// Rejects NULL/misaligned pointers and any overlap that involves a written
+// buffer (read-only inputs may share memory with each other).
+int check_spans(const std::vector<Span>& v) {
+    for (const Span& s : v) {
+        if (s.bytes == 0) continue;
+        if (s.p == nullptr) return fail(KDA_ERR_INVALID_ARGUMENT, "%s is NULL", s.name);
+        if (!aligned16(s.p)) return fail(KDA_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", s.name);
+    }
+    for (size_t i = 0; i < v.size(); ++i) {
+        for (size_t j = i + 1; j < v.size(); ++j) {
+            const Span &a = v[i], &b = v[j];
+            if (a.bytes == 0 || b.bytes == 0 || !(a.writes || b.writes)) continue;
+            const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+            if (a0 < b0 + b.bytes && b0 < a0 + a.bytes)
+                return fail(KDA_ERR_INVALID_ARGUMENT, "%s overlaps %s", a.name, b.name);
+        }
+    }
+    return KDA_OK;
+}
+
+int check_sizes(int64_t T, int32_t H, int32_t dk, int32_t dv, int32_t N) {
+    if (T < 0 || T >= (int64_t(1) << 31)) return fail(KDA_ERR_INVALID_ARGUMENT, "T_tot=%lld out of range [0, 2^31)", (long long)T);
+    if (H < 1 || H > 65535) return fail(KDA_ERR_INVALID_ARGUMENT, "H=%d out of range [1, 65535]", H);
+    if (N < 1) return fail(KDA_ERR_INVALID_ARGUMENT, "N=%d must be >= 1", N);
+    if (!valid_head_dim(dk) || !valid_head_dim(dv))
+        return fail(KDA_ERR_UNSUPPORTED, "dk=%d, dv=%d: supported head sizes are 16, 32, 64, 128", dk, dv);
+    return KDA_OK;
+}
+
+// Optional host-side check of cu_seqlens contents (synchronises the stream).
+int debug_check_cu(const int32_t* cu, int32_t N, int64_t T, hipStream_t s) {
+    const char* env = getenv("KDA_DEBUG_CHECK");
+    if (cu == nullptr || env == nullptr || strcmp(env, "1") != 0) return KDA_OK;
+    std::vector<int32_t> h(static_cast<size_t>(N) + 1);
+    hipError_t e = hipMemcpyAsync(h.data(), cu, h.size() * 4, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "copy of cu_seqlens for KDA_DEBUG_CHECK");
+    if (h[0] != 0) return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens[0]=%d, expected 0", h[0]);
+    for (int32_t n = 0; n < N; ++n)
+        if (h[n + 1] < h[n]) return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens decreases at %d", n);
+    if (h[N] != T) return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens[N]=%d, expected T_tot=%lld", h[N], (long long)T);
+    return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kda_status_string(int status) {
+    switch (status) {
+        case KDA_OK: return "KDA_OK";
+        case KDA_ERR_INVALID_ARGUMENT: return "KDA_ERR_INVALID_ARGUMENT";
+        case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED";
+        case KDA_ERR_WORKSPACE_TOO_SMALL: return "KDA_ERR_WORKSPACE_TOO_SMALL";
+        case KDA_ERR_HIP: return "KDA_ERR_HIP";
+        default: return "KDA_ERR_UNKNOWN";
+    }
+}
+
+const char* kda_last_error_detail(void) { return g_detail; }
+
+int kda_abi_version(void) { return 100; }
+
+int kda_preprocess(int64_t T_tot, int32_t H, int32_t dk, int32_t dv, const int32_t* cu_seqlens, int32_t N,
+                   int32_t x_dtype, const void* q_in, const void* k_in, const void* v_in, const void* w_q,
+                   const void* w_k, const void* w_v, const void* g_alpha, const void* b_beta,
+                   float* conv_state, void* q_out, void* k_out, void* v_out, float* log_alpha_out,
+                   float* beta_out, void* stream) {
+    int st = check_sizes(T_tot, H, dk, dv, N);
+    if (st != KDA_OK) return st;
+    if (!valid_dtype(x_dtype)) return fail(KDA_ERR_INVALID_ARGUMENT, "x_dtype=%d is not KDA_F32 or KDA_BF16", x_dtype);
+    if (cu_seqlens == nullptr && N != 1) return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens is NULL but N=%d", N);
+    const size_t xs = dsize(x_dtype);
+    const size_t T = static_cast<size_t>(T_tot);
+    const size_t qk = T * H * dk, vv = T * H * dv;
+    const size_t cs_bytes = conv_state ? static_cast<size_t>(N) * 3 * H * (2 * dk + dv) * 4 : 0;
+    std::vector<Span> sp = {
+        {"q_in", q_in, qk * xs, false}, {"k_in", k_in, qk * xs, false}, {"v_in", v_in, vv * xs, false},
+        {"w_q", w_q, static_cast<size_t>(H) * dk * 4 * xs, false},
+        {"w_k", w_k, static_cast<size_t>(H) * dk * 4 * xs, false},
+        {"w_v", w_v, static_cast<size_t>(H) * dv * 4 * xs, false},
+        {"g_alpha", g_alpha, qk * xs, false}, {"b_beta", b_beta, T * H * xs, false},
+        {"conv_state", conv_state, cs_bytes, true},
+        {"q_out", q_out, qk * xs, true}, {"k_out", k_out, qk * xs, true}, {"v_out", v_out, vv * xs, true},
+        {"log_alpha_out", log_alpha_out, qk * 4, true}, {"beta_out", beta_out, T * H * 4, true},
+    };
+    if (cu_seqlens != nullptr && (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens is not 4-byte aligned");
+    // b_beta rows are H elements: only the base needs 16-byte alignment when H*xs is a multiple of 16;
+    // the kernel reads it one element at a time, so relax the check to element alignment.
+    sp[7].bytes = 0;
+    if (T * H > 0 && (b_beta == nullptr || (reinterpret_cast<uintptr_t>(b_beta) % xs) != 0))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "b_beta is NULL or misaligned");
+    st = check_spans(sp);
+    if (st != KDA_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    st = debug_check_cu(cu_seqlens, N, T_tot, s);
+    if (st != KDA_OK) return st;
+    kda::PreprocessArgs a;
+    a.T = T_tot; a.H = H; a.dk = dk; a.dv = dv; a.N = N; a.cu = cu_seqlens;
+    a.x = static_cast<kda::DT>(x_dtype);
+    a.q_in = q_in; a.k_in = k_in; a.v_in = v_in; a.w_q = w_q; a.w_k = w_k; a.w_v = w_v;
+    a.g = g_alpha; a.b = b_beta; a.conv_state = conv_state;
+    a.q_out = q_out; a.k_out = k_out; a.v_out = v_out; a.la_out = log_alpha_out; a.beta_out = beta_out;
+    hipError_t e = kda::launch_preprocess(a, s);
+    if (e != hipSuccess) return hip_fail(e, "preprocess launch");
+    return ok();
+}
+
+size_t kda_prefill_workspace_bytes(int64_t T_tot, int32_t N, int32_t H, int32_t dk, int32_t dv, int32_t x_dtype) {
+    if (T_tot < 0 || T_tot >= (int64_t(1) << 31) || N < 1 || H < 1 || H > 65535 || !valid_head_dim(dk) ||
+        !valid_head_dim(dv) || !valid_dtype(x_dtype))
+        return 0;
+    return kda::prefill_workspace_bytes(T_tot, N, H, dk, dv, static_cast<kda::DT>(x_dtype));
+}
+
+int kda_prefill_chunked(int64_t T_tot, int32_t H, int32_t dk, int32_t dv, const int32_t* cu_seqlens, int32_t N,
+                        int32_t x_dtype, int32_t gate_dtype, const void* q, const void* k, const void* v,
+                        const void* log_alpha, const void* beta, const void* out_gate,
+                        const float* initial_state, float* final_state, void* out, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+    int st = check_sizes(T_tot, H, dk, dv, N);
+    if (st != KDA_OK) return st;
+    if (!valid_dtype(x_dtype)) return fail(KDA_ERR_INVALID_ARGUMENT, "x_dtype=%d is not KDA_F32 or KDA_BF16", x_dtype);
+    if (!valid_dtype(gate_dtype)) return fail(KDA_ERR_INVALID_ARGUMENT, "gate_dtype=%d is not KDA_F32 or KDA_BF16", gate_dtype);
+    if (cu_seqlens == nullptr && N != 1) return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens is NULL but N=%d", N);
+    if (cu_seqlens != nullptr && (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens is not 4-byte aligned");
+    const size_t need = kda_prefill_workspace_bytes(T_tot, N, H, dk, dv, x_dtype);
+    if (workspace_bytes < need)
+        return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "workspace_bytes=%zu < %zu needed", workspace_bytes, need);
+    if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "workspace is NULL or not 256-byte aligned");
+    const size_t xs = dsize(x_dtype), gs = dsize(gate_dtype);
+    const size_t T = static_cast<size_t>(T_tot);
+    const size_t qk = T * H * dk, vv = T * H * dv;
+    const size_t state = static_cast<size_t>(N) * H * dk * dv * 4;
+    if (final_state != nullptr && initial_state != nullptr && final_state != initial_state) {
+        const uintptr_t a0 = reinterpret_cast<uintptr_t>(initial_state), b0 = reinterpret_cast<uintptr_t>(final_state);
+        if (a0 < b0 + state && b0 < a0 + state)
+            return fail(KDA_ERR_INVALID_ARGUMENT, "final_state partially overlaps initial_state");
+    }
+    std::vector<Span> sp = {
+        {"q", q, qk * xs, false}, {"k", k, qk * xs, false}, {"v", v, vv * xs, false},
+        {"log_alpha", log_alpha, qk * gs, false},
+        {"out_gate", out_gate, out_gate ? vv * xs : 0, false},
+        {"initial_state", initial_state, (initial_state && initial_state != final_state) ? state : 0, false},
+        {"final_state", final_state, final_state ? state : 0, true},
+        {"out", out, vv * xs, true},
+        {"workspace", workspace, need, true},
+    };
+    st = check_spans(sp);
+    if (st != KDA_OK) return st;
+    if (T * H > 0 && (beta == nullptr || (reinterpret_cast<uintptr_t>(beta) % gs) != 0))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "beta is NULL or misaligned");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    st = debug_check_cu(cu_seqlens, N, T_tot, s);
+    if (st != KDA_OK) return st;
+    kda::PrefillArgs a;
+    a.T = T_tot; a.H = H; a.dk = dk; a.dv = dv; a.N = N; a.cu = cu_seqlens;
+    a.x = static_cast<kda::DT>(x_dtype); a.gate = static_cast<kda::DT>(gate_dtype);
+    a.q = q; a.k = k; a.v = v; a.la = log_alpha; a.beta = beta; a.z = out_gate;
+    a.S0 = initial_state; a.S_out = final_state; a.out = out; a.ws = workspace; a.ws_bytes = workspace_bytes;
+    hipError_t e = kda::launch_prefill(a, s);
+    if (e != hipSuccess) return hip_fail(e, "prefill launch");
+    return ok();
+}
+
+int kda_decode_step(int32_t B, int32_t H, int32_t dk, int32_t dv, int32_t x_dtype, int32_t gate_dtype,
+                    const void* q, const void* k, const void* v, const void* log_alpha, const void* beta,
+                    const void* out_gate, float* state, void* out, void* stream) {
+    if (B < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "B=%d must be >= 0", B);
+    if (H < 1 || H > 65535) return fail(KDA_ERR_INVALID_ARGUMENT, "H=%d out of range [1, 65535]", H);
+    if (!valid_head_dim(dk) || !valid_head_dim(dv))
+        return fail(KDA_ERR_UNSUPPORTED, "dk=%d, dv=%d: supported head sizes are 16, 32, 64, 128", dk, dv);
+    if (!valid_dtype(x_dtype)) return fail(KDA_ERR_INVALID_ARGUMENT, "x_dtype=%d is not KDA_F32 or KDA_BF16", x_dtype);
+    if (!valid_dtype(gate_dtype)) return fail(KDA_ERR_INVALID_ARGUMENT, "gate_dtype=%d is not KDA_F32 or KDA_BF16", gate_dtype);
+    if (static_cast<int64_t>(B) * H >= (int64_t(1) << 31)) return fail(KDA_ERR_INVALID_ARGUMENT, "B*H too large");
+    const size_t xs = dsize(x_dtype), gs = dsize(gate_dtype);
+    const size_t BH = static_cast<size_t>(B) * H;
+    std::vector<Span> sp = {
+        {"q", q, BH * dk * xs, false}, {"k", k, BH * dk * xs, false}, {"v", v, BH * dv * xs, false},
+        {"log_alpha", log_alpha, BH * dk * gs, false},
+        {"out_gate", out_gate, out_gate ? BH * dv * xs : 0, false},
+        {"state", state, BH * dk * dv * 4, true},
+        {"out", out, BH * dv * xs, true},
+    };
+    int st = check_spans(sp);
+    if (st != KDA_OK) return st;
+    if (BH > 0 && (beta == nullptr || (reinterpret_cast<uintptr_t>(beta) % gs) != 0))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "beta is NULL or misaligned");
+    kda::DecodeArgs a;
+    a.B = B; a.H = H; a.dk = dk; a.dv = dv;
+    a.x = static_cast<kda::DT>(x_dtype); a.gate = static_cast<kda::DT>(gate_dtype);
+    a.q = q; a.k = k; a.v = v; a.la = log_alpha; a.beta = beta; a.z = out_gate; a.state = state; a.out = out;
+    hipError_t e = kda::launch_decode(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "decode launch");
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,105 @@
+// Device-side helpers shared by the libkda kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+// bf16 values travel as their 16-bit patterns.
+struct bf16 {
+    uint16_t bits;
+};
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// fp32 -> bf16, round to nearest, ties to even; NaN stays NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+// scalar load/store of an element type as fp32
+__device__ __forceinline__ float ld(const float* p) { return *p; }
+__device__ __forceinline__ float ld(const bf16* p) { return bf16_to_f32(p->bits); }
+__device__ __forceinline__ void st(float* p, float x) { *p = x; }
+__device__ __forceinline__ void st(bf16* p, float x) { p->bits = f32_to_bf16(x); }
+
+// 8 consecutive elements (16 B for bf16, 32 B for fp32), 16-byte aligned
+__device__ __forceinline__ void ld8(const float* p, float (&x)[8]) {
+    const float4 a = reinterpret_cast<const float4*>(p)[0];
+    const float4 b = reinterpret_cast<const float4*>(p)[1];
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+__device__ __forceinline__ void ld8(const bf16* p, float (&x)[8]) {
+    const uint4 a = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x[2 * i] = __uint_as_float(w[i] << 16);
+        x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+}
+__device__ __forceinline__ void st8(float* p, const float (&x)[8]) {
+    reinterpret_cast<float4*>(p)[0] = make_float4(x[0], x[1], x[2], x[3]);
+    reinterpret_cast<float4*>(p)[1] = make_float4(x[4], x[5], x[6], x[7]);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+__device__ __forceinline__ void st8(bf16* p, const float (&x)[8]) {
+    uint4 a;
+    a.x = pack_bf16x2(x[0], x[1]);
+    a.y = pack_bf16x2(x[2], x[3]);
+    a.z = pack_bf16x2(x[4], x[5]);
+    a.w = pack_bf16x2(x[6], x[7]);
+    *reinterpret_cast<uint4*>(p) = a;
+}
+
+// 4 consecutive elements
+__device__ __forceinline__ void ld4(const float* p, float (&x)[4]) {
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+}
+__device__ __forceinline__ void ld4(const bf16* p, float (&x)[4]) {
+    const uint2 a = *reinterpret_cast<const uint2*>(p);
+    x[0] = __uint_as_float(a.x << 16);
+    x[1] = __uint_as_float(a.x & 0xffff0000u);
+    x[2] = __uint_as_float(a.y << 16);
+    x[3] = __uint_as_float(a.y & 0xffff0000u);
+}
+__device__ __forceinline__ void st4(float* p, const float (&x)[4]) {
+    *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
+}
+__device__ __forceinline__ void st4(bf16* p, const float (&x)[4]) {
+    uint2 a;
+    a.x = pack_bf16x2(x[0], x[1]);
+    a.y = pack_bf16x2(x[2], x[3]);
+    *reinterpret_cast<uint2*>(p) = a;
+}
+
+// softplus(x) = log(1 + e^x) without overflow; -softplus is the log decay
+__device__ __forceinline__ float softplus(float x) {
+    return x > 0.f ? x + log1pf(expf(-x)) : log1pf(expf(x));
+}
+__device__ __forceinline__ float sigmoid(float x) { return 1.f / (1.f + expf(-x)); }
+
+// index of the sequence holding token t: the largest n with cu[n] <= t
+// (empty sequences never hold a token, so ties resolve to the non-empty one)
+__device__ __forceinline__ int find_seq(const int32_t* cu, int N, int64_t t) {
+    int lo = 0, hi = N;  // cu[lo] <= t < cu[hi]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (static_cast<int64_t>(cu[mid]) <= t) lo = mid; else hi = mid;
+    }
+    return lo;
+}
+
+constexpr int kChunk = 64;  // tokens per chunk of the prefill
+
+}  // namespace kda

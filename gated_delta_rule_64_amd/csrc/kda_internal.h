@@ -1,0 +1,53 @@
+// Host-side interface between the C ABI layer (kda_api.hip) and the kernel
+// translation units.  Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+enum class DT : int { F32 = 0, BF16 = 1 };
+
+struct PreprocessArgs {
+    int64_t T;
+    int H, dk, dv, N;
+    const int32_t* cu;  // never NULL here (the ABI layer substitutes a one-sequence map)
+    DT x;
+    const void *q_in, *k_in, *v_in, *w_q, *w_k, *w_v, *g, *b;
+    float* conv_state;
+    void *q_out, *k_out, *v_out;
+    float *la_out, *beta_out;
+};
+
+struct PrefillArgs {
+    int64_t T;
+    int H, dk, dv, N;
+    const int32_t* cu;  // may be NULL: one sequence [0, T)
+    DT x, gate;
+    const void *q, *k, *v, *la, *beta, *z;
+    const float* S0;
+    float* S_out;
+    void* out;
+    void* ws;
+    size_t ws_bytes;
+};
+
+struct DecodeArgs {
+    int B, H, dk, dv;
+    DT x, gate;
+    const void *q, *k, *v, *la, *beta, *z;
+    float* state;
+    void* out;
+};
+
+hipError_t launch_preprocess(const PreprocessArgs& a, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+
+// chunked prefill: workspace layout and the two implementations
+bool prefill_uses_mfma(int dk, int dv, DT x);
+size_t prefill_workspace_bytes(int64_t T, int N, int H, int dk, int dv, DT x);
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
+
+}  // namespace kda

@@ -1,0 +1,46 @@
+// Pieces shared by the two chunked-prefill implementations: the chunk map and
+// the workspace layout.
+//
+// Chunking.  Each sequence is cut into chunks of 64 tokens starting at its own
+// first token (the last chunk of a sequence may be shorter).  Chunk "slots"
+// are numbered sequence by sequence: sequence n owns slots
+// base[n] .. base[n+1]-1 with base[n] = sum_{m<n} ceil(L_m / 64).  A one-block
+// kernel computes base[] on the device, so the host never reads cu_seqlens;
+// grids are sized with the bound ceil(T/64) + N and surplus blocks exit.
+//
+// Chunked form of the recurrence (an exact rewrite of the token-by-token
+// rule, so only rounding differs).  Inside a chunk with local tokens r, s,
+// decay cumsums G_r = sum_{i<=r} log alpha_i (per key channel) and S the state
+// at the chunk start:
+//   A_rs = sum_c k_rc k_sc e^{G_rc - G_sc}   (s < r)
+//   M_rs = sum_c q_rc k_sc e^{G_rc - G_sc}   (s <= r)
+//   T    = (I + Diag(beta) A)^-1             (unit lower triangular)
+//   W    = T Diag(beta) (e^G * K),   U~ = T Diag(beta) V
+//   U    = U~ - W S                  (the chunk's delta-rule writes)
+//   O    = (e^G * Q) S + M U = Q' S + M U~,   Q' = e^G * Q - M W
+//   S   <- Diag(gamma) S + K^T U,    K^ = e^{G_last - G} * K, gamma = e^{G_last}
+// The state-independent parts (W, U~, Q', K^, M U~, gamma) are computed for
+// all chunks in parallel and stored per (chunk slot, head); a second kernel
+// walks each sequence's chunks in order carrying S in fp32.
+#pragma once
+
+#include "kda_common.h"
+
+namespace kda {
+
+__device__ __forceinline__ int64_t seq_begin(const int32_t* cu, int n) { return cu ? cu[n] : 0; }
+__device__ __forceinline__ int64_t seq_finish(const int32_t* cu, int n, int64_t T) {
+    return cu ? cu[n + 1] : T;
+}
+
+// base[0..N]: prefix sums of chunks per sequence (one workgroup of 1024)
+__global__ __launch_bounds__(1024) void chunk_map_kernel(const int32_t* __restrict__ cu, int N,
+                                                         int64_t T, int32_t* __restrict__ base);
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+inline size_t chunk_map_bytes(int N) { return align_up(static_cast<size_t>(N + 1) * 4, 256); }
+
+inline int64_t chunk_slots_bound(int64_t T, int N) { return (T + kChunk - 1) / kChunk + N; }
+
+}  // namespace kda

@@ -1,0 +1,315 @@
+// Chunked prefill, general path: any dk, dv in {16, 32, 64, 128}, fp32 or
+// bf16 inputs, all arithmetic in fp32 on the vector ALUs.  It serves fp32
+// inputs (where bf16 matrix-core operands would lose the precision the
+// caller asked for) and head sizes the matrix-core path does not cover.
+// The chunk algebra is described in kda_prefill_common.h.
+//
+// Every pairwise decay e^{G_r - G_s} (r >= s, so the exponent is <= 0) is
+// evaluated directly, so no factor can overflow whatever the decay rates.
+#include "kda_prefill_common.h"
+#include "kda_internal.h"
+#include "kda_prefill_mfma.h"
+
+namespace kda {
+
+__global__ __launch_bounds__(1024) void chunk_map_kernel(const int32_t* __restrict__ cu, int N,
+                                                         int64_t T, int32_t* __restrict__ base) {
+    __shared__ int32_t buf[1024];
+    __shared__ int32_t carry_s;
+    const int tid = threadIdx.x;
+    if (tid == 0) carry_s = 0;
+    __syncthreads();
+    for (int start = 0; start < N; start += 1024) {
+        const int i = start + tid;
+        int32_t c = 0;
+        if (i < N) {
+            const int64_t L = seq_finish(cu, i, T) - seq_begin(cu, i);
+            c = static_cast<int32_t>((L + kChunk - 1) / kChunk);
+        }
+        buf[tid] = c;
+        __syncthreads();
+        // Hillis-Steele inclusive scan
+        for (int off = 1; off < 1024; off <<= 1) {
+            const int32_t x = tid >= off ? buf[tid - off] : 0;
+            __syncthreads();
+            buf[tid] += x;
+            __syncthreads();
+        }
+        const int32_t carry = carry_s;
+        if (i < N) base[i] = carry + buf[tid] - c;
+        __syncthreads();
+        if (tid == 1023) carry_s = carry + buf[1023];
+        __syncthreads();
+    }
+    if (tid == 0) base[N] = carry_s;
+}
+
+namespace {
+
+struct GenRec {
+    int64_t W, U, Qp, Kh, Oi, gam, size;  // offsets in floats
+};
+
+__host__ __device__ inline GenRec gen_rec(int dk, int dv) {
+    GenRec r;
+    r.W = 0;
+    r.U = r.W + 64 * dk;
+    r.Qp = r.U + 64 * dv;
+    r.Kh = r.Qp + 64 * dk;
+    r.Oi = r.Kh + 64 * dk;
+    r.gam = r.Oi + 64 * dv;
+    r.size = (r.gam + dk + 63) / 64 * 64;
+    return r;
+}
+
+template <typename XT, typename GT>
+struct GenK {
+    int64_t T;
+    int H, dk, dv, N;
+    const int32_t* cu;
+    const int32_t* base;
+    const XT *q, *k, *v, *z;
+    const GT *la, *beta;
+    const float* S0;
+    float* S_out;
+    XT* out;
+    float* rec;
+};
+
+// ---- phase 1: per (chunk slot, head), the state-independent factors ----
+template <typename XT, typename GT>
+__global__ __launch_bounds__(256) void gen_intra_kernel(GenK<XT, GT> a) {
+    extern __shared__ float smem[];
+    const int dk = a.dk, dv = a.dv;
+    float* sK = smem;            // [64][dk] keys, later beta e^G K
+    float* sQ = sK + 64 * dk;    // [64][dk] queries, later e^G Q
+    float* sG = sQ + 64 * dk;    // [64][dk] decay cumsums, later W
+    float* sA = sG + 64 * dk;    // [64][64]
+    float* sM = sA + 4096;       // [64][64]
+    float* sT = sM + 4096;       // [64][64]
+    float* sB = sT + 4096;       // [64] beta
+    const int slot = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+    if (slot >= a.base[a.N]) return;
+    const int n = find_seq(a.base, a.N, slot);
+    const int64_t t0 = seq_begin(a.cu, n) + static_cast<int64_t>(slot - a.base[n]) * kChunk;
+    const int L = static_cast<int>(min(static_cast<int64_t>(kChunk), seq_finish(a.cu, n, a.T) - t0));
+    const GenRec R = gen_rec(dk, dv);
+    float* rec = a.rec + (static_cast<int64_t>(slot) * a.H + h) * R.size;
+
+    for (int i = tid; i < 64 * dk; i += 256) {
+        const int r = i / dk, c = i % dk;
+        const bool in = r < L;
+        const int64_t idx = ((t0 + r) * a.H + h) * dk + c;
+        sK[i] = in ? ld(a.k + idx) : 0.f;
+        sQ[i] = in ? ld(a.q + idx) : 0.f;
+        sG[i] = in ? ld(a.la + idx) : 0.f;  // padded tokens: no decay, no write
+    }
+    if (tid < 64) sB[tid] = tid < L ? ld(a.beta + (t0 + tid) * a.H + h) : 0.f;
+    __syncthreads();
+    if (tid < dk) {
+        float acc = 0.f;
+        for (int r = 0; r < 64; ++r) {
+            acc += sG[r * dk + tid];
+            sG[r * dk + tid] = acc;
+        }
+    }
+    __syncthreads();
+    // K^ and gamma (G_last = G_63: padded rows add no decay)
+    for (int i = tid; i < 64 * dk; i += 256) {
+        const int r = i / dk, c = i % dk;
+        rec[R.Kh + i] = expf(sG[63 * dk + c] - sG[i]) * sK[i];
+    }
+    if (tid < dk) rec[R.gam + tid] = expf(sG[63 * dk + tid]);
+    // A (strictly lower) and M (lower with diagonal)
+    for (int i = tid; i < 4096; i += 256) {
+        const int r = i >> 6, s = i & 63;
+        float av = 0.f, mv = 0.f;
+        if (s <= r) {
+            for (int c = 0; c < dk; ++c) {
+                const float ks = sK[s * dk + c] * expf(sG[r * dk + c] - sG[s * dk + c]);
+                av += sK[r * dk + c] * ks;
+                mv += sQ[r * dk + c] * ks;
+            }
+        }
+        sA[i] = s < r ? av : 0.f;
+        sM[i] = mv;
+    }
+    __syncthreads();
+    // T = (I + Diag(beta) A)^-1 by forward substitution, one row at a time
+    for (int r = 0; r < 64; ++r) {
+        if (tid < 64) {
+            const int c = tid;
+            float acc = r == c ? 1.f : 0.f;
+            if (c < r) {
+                float sum = 0.f;
+                for (int s = c; s < r; ++s) sum += sA[r * 64 + s] * sT[s * 64 + c];
+                acc = -sB[r] * sum;
+            }
+            sT[r * 64 + c] = acc;
+        }
+        __syncthreads();
+    }
+    // operands of the products: beta e^G K and e^G Q
+    for (int i = tid; i < 64 * dk; i += 256) {
+        const int r = i / dk;
+        const float e = expf(sG[i]);
+        sK[i] *= sB[r] * e;
+        sQ[i] *= e;
+    }
+    __syncthreads();
+    // W = T (beta e^G K), kept in LDS (over G) and stored
+    for (int i = tid; i < 64 * dk; i += 256) {
+        const int r = i / dk, c = i % dk;
+        float acc = 0.f;
+        for (int s = 0; s <= r; ++s) acc += sT[r * 64 + s] * sK[s * dk + c];
+        sG[i] = acc;
+        rec[R.W + i] = acc;
+    }
+    // U~ = T Diag(beta) V
+    for (int i = tid; i < 64 * dv; i += 256) {
+        const int r = i / dv, c = i % dv;
+        float acc = 0.f;
+        for (int s = 0; s <= r && s < L; ++s)
+            acc += sT[r * 64 + s] * sB[s] * ld(a.v + ((t0 + s) * a.H + h) * dv + c);
+        rec[R.U + i] = acc;
+    }
+    __syncthreads();
+    // Q' = e^G Q - M W;  M U~
+    for (int i = tid; i < 64 * dk; i += 256) {
+        const int r = i / dk, c = i % dk;
+        float acc = sQ[i];
+        for (int s = 0; s <= r; ++s) acc -= sM[r * 64 + s] * sG[s * dk + c];
+        rec[R.Qp + i] = acc;
+    }
+    for (int i = tid; i < 64 * dv; i += 256) {
+        const int r = i / dv, c = i % dv;
+        float acc = 0.f;
+        for (int s = 0; s <= r; ++s) acc += sM[r * 64 + s] * rec[R.U + s * dv + c];
+        rec[R.Oi + i] = acc;
+    }
+}
+
+// ---- phase 2: per (sequence, head, 16 state columns), chunks in order ----
+template <typename XT, typename GT>
+__global__ __launch_bounds__(256) void gen_state_kernel(GenK<XT, GT> a) {
+    __shared__ float sS[128 * 16];
+    __shared__ float sU[64 * 16];
+    const int dk = a.dk, dv = a.dv;
+    const int nsl = dv / 16;
+    const int sl = blockIdx.x % nsl;
+    const int h = (blockIdx.x / nsl) % a.H;
+    const int n = blockIdx.x / (nsl * a.H);
+    const int tid = threadIdx.x;
+    const GenRec R = gen_rec(dk, dv);
+    const int64_t sidx = (static_cast<int64_t>(n) * a.H + h) * dk * dv;
+    for (int e = tid; e < dk * 16; e += 256) {
+        const int c = e >> 4, j = e & 15;
+        sS[e] = a.S0 ? a.S0[sidx + c * dv + 16 * sl + j] : 0.f;
+    }
+    __syncthreads();
+    const int64_t sb = seq_begin(a.cu, n), se = seq_finish(a.cu, n, a.T);
+    const int nch = a.base[n + 1] - a.base[n];
+    const int r = tid >> 2, c4 = (tid & 3) * 4;
+    for (int j = 0; j < nch; ++j) {
+        const float* rec = a.rec + (static_cast<int64_t>(a.base[n] + j) * a.H + h) * R.size;
+        const int64_t t0 = sb + static_cast<int64_t>(j) * kChunk;
+        const int L = static_cast<int>(min(static_cast<int64_t>(kChunk), se - t0));
+        float u[4], o[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            u[i] = rec[R.U + r * dv + 16 * sl + c4 + i];
+            o[i] = rec[R.Oi + r * dv + 16 * sl + c4 + i];
+        }
+        for (int c = 0; c < dk; ++c) {
+            const float w = rec[R.W + r * dk + c], qp = rec[R.Qp + r * dk + c];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float s = sS[c * 16 + c4 + i];
+                u[i] -= w * s;
+                o[i] += qp * s;
+            }
+        }
+        if (r < L) {
+            const int64_t oidx = ((t0 + r) * a.H + h) * dv + 16 * sl + c4;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float y = o[i];
+                if (a.z) y *= sigmoid(ld(a.z + oidx + i));
+                st(a.out + oidx + i, y);
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sU[r * 16 + c4 + i] = u[i];
+        __syncthreads();
+        for (int e = tid; e < dk * 16; e += 256) {
+            const int c = e >> 4, jj = e & 15;
+            float acc = rec[R.gam + c] * sS[e];
+            for (int rr = 0; rr < 64; ++rr) acc += rec[R.Kh + rr * dk + c] * sU[rr * 16 + jj];
+            sS[e] = acc;
+        }
+        __syncthreads();
+    }
+    if (a.S_out) {
+        for (int e = tid; e < dk * 16; e += 256) {
+            const int c = e >> 4, jj = e & 15;
+            a.S_out[sidx + c * dv + 16 * sl + jj] = sS[e];
+        }
+    }
+}
+
+size_t gen_lds_bytes(int dk) { return (3 * 64 * dk + 3 * 4096 + 64) * sizeof(float); }
+
+template <typename XT, typename GT>
+hipError_t launch_gen_typed(const PrefillArgs& a, hipStream_t s, int32_t* base, float* rec) {
+    GenK<XT, GT> k;
+    k.T = a.T; k.H = a.H; k.dk = a.dk; k.dv = a.dv; k.N = a.N; k.cu = a.cu; k.base = base;
+    k.q = static_cast<const XT*>(a.q); k.k = static_cast<const XT*>(a.k);
+    k.v = static_cast<const XT*>(a.v); k.z = static_cast<const XT*>(a.z);
+    k.la = static_cast<const GT*>(a.la); k.beta = static_cast<const GT*>(a.beta);
+    k.S0 = a.S0; k.S_out = a.S_out; k.out = static_cast<XT*>(a.out); k.rec = rec;
+    const int64_t slots = chunk_slots_bound(a.T, a.N);
+    const size_t lds = gen_lds_bytes(a.dk);
+    if (slots > 0 && a.T > 0) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gen_intra_kernel<XT, GT>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           static_cast<int>(lds));
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((gen_intra_kernel<XT, GT>), dim3(static_cast<unsigned>(slots), a.H), dim3(256),
+                           lds, s, k);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const int64_t blocks = static_cast<int64_t>(a.N) * a.H * (a.dv / 16);
+    hipLaunchKernelGGL((gen_state_kernel<XT, GT>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, k);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool prefill_uses_mfma(int dk, int dv, DT x) { return mfma_prefill_supports(dk, dv, x); }
+
+size_t prefill_workspace_bytes(int64_t T, int N, int H, int dk, int dv, DT x) {
+    const size_t slots = static_cast<size_t>(chunk_slots_bound(T, N));
+    const size_t rec = prefill_uses_mfma(dk, dv, x) ? mfma_record_bytes()
+                                                    : static_cast<size_t>(gen_rec(dk, dv).size) * 4;
+    return chunk_map_bytes(N) + slots * static_cast<size_t>(H) * rec;
+}
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
+    int32_t* base = static_cast<int32_t*>(a.ws);
+    char* recs = static_cast<char*>(a.ws) + chunk_map_bytes(a.N);
+    hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(1024), 0, s, a.cu, a.N, a.T, base);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (prefill_uses_mfma(a.dk, a.dv, a.x)) return launch_prefill_mfma(a, s, base, recs);
+    float* rec = reinterpret_cast<float*>(recs);
+    if (a.x == DT::BF16) {
+        return a.gate == DT::BF16 ? launch_gen_typed<bf16, bf16>(a, s, base, rec)
+                                  : launch_gen_typed<bf16, float>(a, s, base, rec);
+    }
+    return a.gate == DT::BF16 ? launch_gen_typed<float, bf16>(a, s, base, rec)
+                              : launch_gen_typed<float, float>(a, s, base, rec);
+}
+
+}  // namespace kda

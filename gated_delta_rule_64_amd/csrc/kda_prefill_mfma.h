@@ -1,0 +1,16 @@
+// Matrix-core (MFMA) chunked prefill for dk = dv = 128 with bf16 inputs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "kda_internal.h"
+
+namespace kda {
+
+bool mfma_prefill_supports(int dk, int dv, DT x);
+size_t mfma_record_bytes();
+hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t s, int32_t* base, char* recs);
+
+}  // namespace kda

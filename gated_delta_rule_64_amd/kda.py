@@ -1,0 +1,111 @@
+"""Python binding of libkda: the same entry points, torch tensors in.
+
+Argument marshalling only: shapes are read from the tensors, outputs that the
+caller does not pass are allocated with torch (device memory is torch's
+plumbing), and each call goes straight to the C ABI on torch's current HIP
+stream.  Every step of the computation runs in libkda's kernels.
+"""
+
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from ._lib import KDA_BF16, KDA_F32, check, lib
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return KDA_F32
+    if t.dtype == torch.bfloat16:
+        return KDA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; libkda takes float32 or bfloat16")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("libkda takes device tensors")
+    if not t.is_contiguous():
+        raise ValueError("libkda takes contiguous tensors")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device=None):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _n_seqs(cu_seqlens):
+    if cu_seqlens is None:
+        return 1
+    if cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    return cu_seqlens.numel() - 1
+
+
+def kda_preprocess(q_in, k_in, v_in, w_q, w_k, w_v, g_alpha, b_beta, H, dk, dv,
+                   cu_seqlens=None, conv_state=None, out=None):
+    """Short conv + L2 norm + gates.  Inputs [T, H*d]; returns
+    (q [T,H,dk], k [T,H,dk], v [T,H,dv], log_alpha fp32 [T,H,dk], beta fp32 [T,H]).
+    ``conv_state`` (fp32 [N, 3, H*(2dk+dv)]) is read and rewritten in place."""
+    T = q_in.shape[0]
+    x = _dtype_code(q_in)
+    dev = q_in.device
+    if out is None:
+        out = (torch.empty((T, H, dk), dtype=q_in.dtype, device=dev),
+               torch.empty((T, H, dk), dtype=q_in.dtype, device=dev),
+               torch.empty((T, H, dv), dtype=q_in.dtype, device=dev),
+               torch.empty((T, H, dk), dtype=torch.float32, device=dev),
+               torch.empty((T, H), dtype=torch.float32, device=dev))
+    q_o, k_o, v_o, la_o, b_o = out
+    check(lib().kda_preprocess(T, H, dk, dv, _ptr(cu_seqlens), _n_seqs(cu_seqlens), x,
+                               _ptr(q_in), _ptr(k_in), _ptr(v_in), _ptr(w_q), _ptr(w_k), _ptr(w_v),
+                               _ptr(g_alpha), _ptr(b_beta), _ptr(conv_state),
+                               _ptr(q_o), _ptr(k_o), _ptr(v_o), _ptr(la_o), _ptr(b_o), _stream(dev)))
+    return out
+
+
+def kda_prefill_workspace_bytes(T_tot, N, H, dk, dv, x_dtype):
+    if isinstance(x_dtype, torch.dtype):
+        x_dtype = KDA_BF16 if x_dtype == torch.bfloat16 else KDA_F32
+    return int(lib().kda_prefill_workspace_bytes(T_tot, N, H, dk, dv, x_dtype))
+
+
+def kda_prefill_chunked(q, k, v, log_alpha, beta, out_gate=None, initial_state=None,
+                        final_state=None, cu_seqlens=None, workspace=None, out=None,
+                        want_final_state=True):
+    """Chunked recurrence over preprocessed tokens q,k [T,H,dk], v [T,H,dv].
+    Returns (out [T,H,dv], final_state fp32 [N,H,dk,dv] or None)."""
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    N = _n_seqs(cu_seqlens)
+    x = _dtype_code(q)
+    g = _dtype_code(log_alpha)
+    dev = q.device
+    if out is None:
+        out = torch.empty((T, H, dv), dtype=q.dtype, device=dev)
+    if final_state is None and want_final_state:
+        final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    need = kda_prefill_workspace_bytes(T, N, H, dk, dv, x)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    check(lib().kda_prefill_chunked(T, H, dk, dv, _ptr(cu_seqlens), N, x, g,
+                                    _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                                    _ptr(out_gate), _ptr(initial_state), _ptr(final_state), _ptr(out),
+                                    _ptr(workspace), workspace.numel(), _stream(dev)))
+    return out, final_state
+
+
+def kda_decode_step(q, k, v, log_alpha, beta, state, out_gate=None, out=None):
+    """One token per sequence; ``state`` fp32 [B,H,dk,dv] is updated in place.
+    Returns out [B,H,dv]."""
+    B, H, dk = q.shape
+    dv = v.shape[2]
+    if out is None:
+        out = torch.empty((B, H, dv), dtype=q.dtype, device=q.device)
+    check(lib().kda_decode_step(B, H, dk, dv, _dtype_code(q), _dtype_code(log_alpha),
+                                _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(out_gate),
+                                _ptr(state), _ptr(out), _stream(q.device)))
+    return out

@@ -1,0 +1,174 @@
+/*
+ * libkda -- the Kimi Delta Attention (KDA) token mixer on AMD Instinct
+ * MI355X (gfx950).  Plain C ABI: every tensor argument is a raw device
+ * pointer plus sizes; no framework types cross this boundary.
+ *
+ * What is computed.  KDA is the gated delta-rule linear attention of the page
+ * "Ling-3.0-flash: a 124B open MoE that runs like a 5B and reaches for 1M
+ * tokens", section "KDA: constant-size memory over a very long context".  Per
+ * sequence and head it keeps a fixed dk x dv state S (fp32 here).  For each
+ * token t, with alpha_t the per-key-channel decay, beta_t the write strength:
+ *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
+ *     o_t = S_t^T q_t,           y_t = o_t * sigmoid(z_t)  (when a gate is given)
+ * (that section's own equation is missing from the page text; this is the
+ * update its prose describes: decay as the erase, a delta-rule write, a read
+ * with the query).  Before the recurrence q and k pass through a width-4
+ * causal short conv and an L2 norm, v through a conv, alpha comes from a
+ * softplus gate and beta from a sigmoid (same section; the conv width and the
+ * 32 x 128 head shape are in the "Every architecture field" table of the page
+ * "Ling 3.0 Flash", llm-architectures-explained).
+ *
+ * Conventions shared by every call.
+ *  - Memory: every tensor pointer is a device pointer on the current HIP
+ *    device, owned by the caller.  The library never allocates, frees or
+ *    retains caller memory; scratch comes from a caller-provided workspace.
+ *  - Layout: tensors are dense, row-major, fastest index last, 16-byte
+ *    aligned.  [T, H, d] means token-major, then head, then channel.
+ *  - Aliasing: only the recurrent state may alias (final_state may equal
+ *    initial_state; the decode state is updated in place).  Any other overlap
+ *    is rejected with KDA_ERR_INVALID_ARGUMENT.
+ *  - Execution: calls enqueue work on `stream` (a hipStream_t; NULL is the
+ *    null stream) and return without synchronising.  Host-side validation
+ *    checks sizes, pointers, alignment and dtypes; the contents of cu_seqlens
+ *    are trusted (non-decreasing, cu_seqlens[0] = 0, cu_seqlens[N] = T_tot).
+ *  - Errors: calls return a status and never abort or throw.  After a non-OK
+ *    return, outputs are undefined; kda_last_error_detail() gives a
+ *    thread-local sentence naming the failing argument or HIP call.
+ *  - Supported shapes: dk, dv in {16, 32, 64, 128}; H >= 1; N >= 1;
+ *    T_tot >= 0 and below 2^31; sequences of length 0 are allowed.
+ *  - Thread safety: no global mutable state besides the per-thread error text.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kda_status {
+    KDA_OK = 0,
+    KDA_ERR_INVALID_ARGUMENT = 1,   /* bad size, NULL or misaligned pointer, overlap */
+    KDA_ERR_UNSUPPORTED = 2,        /* valid request this build does not implement */
+    KDA_ERR_WORKSPACE_TOO_SMALL = 3,
+    KDA_ERR_HIP = 4                 /* a HIP runtime call or kernel launch failed */
+} kda_status_t;
+
+typedef enum kda_dtype {
+    KDA_F32 = 0,
+    KDA_BF16 = 1
+} kda_dtype_t;
+
+/* Static text for a status code; never NULL. */
+const char* kda_status_string(int status);
+
+/* Thread-local detail of the last non-OK return on this thread ("" if none). */
+const char* kda_last_error_detail(void);
+
+/* ABI version of this header (major * 100 + minor). */
+int kda_abi_version(void);
+
+/*
+ * kda_preprocess -- fused short conv, L2 norm and gates for a packed batch.
+ *
+ * For every sequence n (tokens cu_seqlens[n] .. cu_seqlens[n+1]-1), head h
+ * and channel c:
+ *   conv:  x~_t[c] = sum_{j=0..3} w[c][j] * x_{t-3+j}[c]   (tap 3 = current
+ *          token; no bias, no activation).  Positions before the sequence
+ *          start read conv_state[n] (oldest first) if given, else zero.
+ *   norm:  q^ = q~ / sqrt(|q~|^2 + 1e-6) over the head's dk channels; same
+ *          for k; v^ = v~.
+ *   gates: log_alpha = -softplus(g) per key channel; beta = sigmoid(b) per head.
+ * Arguments:
+ *   T_tot, H, dk, dv     sizes; cu_seqlens: device int32 [N+1], or NULL for a
+ *                        single sequence (then N must be 1);
+ *   x_dtype              dtype of q_in, k_in, v_in, w_*, g_alpha, b_beta and
+ *                        of q_out, k_out, v_out;
+ *   q_in, k_in  [T_tot, H*dk];  v_in [T_tot, H*dv]   projected inputs;
+ *   w_q, w_k    [H*dk, 4];      w_v  [H*dv, 4]       conv taps;
+ *   g_alpha     [T_tot, H*dk]   decay logits;  b_beta [T_tot, H] write logits;
+ *   conv_state  NULL, or fp32 [N, 3, H*(2*dk+dv)] (q channels, then k, then v):
+ *               read as the history of each sequence, then overwritten with
+ *               the last three raw tokens of that sequence (reaching back into
+ *               the old history for sequences shorter than three);
+ *   q_out, k_out [T_tot, H, dk]; v_out [T_tot, H, dv] (x_dtype);
+ *   log_alpha_out fp32 [T_tot, H, dk]; beta_out fp32 [T_tot, H].
+ */
+int kda_preprocess(int64_t T_tot, int32_t H, int32_t dk, int32_t dv,
+                   const int32_t* cu_seqlens, int32_t N, int32_t x_dtype,
+                   const void* q_in, const void* k_in, const void* v_in,
+                   const void* w_q, const void* w_k, const void* w_v,
+                   const void* g_alpha, const void* b_beta,
+                   float* conv_state,
+                   void* q_out, void* k_out, void* v_out,
+                   float* log_alpha_out, float* beta_out,
+                   void* stream);
+
+/*
+ * Bytes of workspace kda_prefill_chunked needs for these sizes.  The bound
+ * does not depend on the sequence lengths: it counts ceil(T_tot/64) + N
+ * chunk slots (each sequence's chunks start at its own first token).
+ * Returns 0 for unsupported or invalid sizes.
+ */
+size_t kda_prefill_workspace_bytes(int64_t T_tot, int32_t N, int32_t H, int32_t dk,
+                                   int32_t dv, int32_t x_dtype);
+
+/*
+ * kda_prefill_chunked -- the recurrence over a packed batch of preprocessed
+ * tokens, in chunks of 64 tokens.  The result is that of the token-by-token
+ * recurrence above (chunking changes only rounding): within a chunk the
+ * writes are collected into a WY-style form (a unit-lower-triangular solve
+ * over the chunk's keys) and the fp32 state is carried across chunks in
+ * order, per sequence and head.
+ * Arguments:
+ *   cu_seqlens  device int32 [N+1], or NULL for a single sequence (N = 1);
+ *   x_dtype     dtype of q, k, v, out_gate and out;
+ *   gate_dtype  dtype of log_alpha and beta;
+ *   q, k        [T_tot, H, dk] (L2-normalised keys keep every write a
+ *               contraction);  v [T_tot, H, dv];
+ *   log_alpha   [T_tot, H, dk], entries <= 0;  beta [T_tot, H];
+ *   out_gate    NULL, or [T_tot, H, dv] logits z: out = o * sigmoid(z);
+ *   initial_state NULL (zeros) or fp32 [N, H, dk, dv];
+ *   final_state NULL (not wanted) or fp32 [N, H, dk, dv]; may equal
+ *               initial_state (then updated in place);
+ *   out         [T_tot, H, dv] (x_dtype);
+ *   workspace   device scratch of at least kda_prefill_workspace_bytes()
+ *               bytes, 256-byte aligned; contents on entry are ignored.
+ */
+int kda_prefill_chunked(int64_t T_tot, int32_t H, int32_t dk, int32_t dv,
+                        const int32_t* cu_seqlens, int32_t N,
+                        int32_t x_dtype, int32_t gate_dtype,
+                        const void* q, const void* k, const void* v,
+                        const void* log_alpha, const void* beta,
+                        const void* out_gate,
+                        const float* initial_state, float* final_state,
+                        void* out,
+                        void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/*
+ * kda_decode_step -- one token per sequence, state updated in place.
+ * For each (b, h):  S' = Diag(alpha) S;  u = S'^T k;  S <- S' + beta k (v - u)^T;
+ *                   o = S^T q;  out = o * sigmoid(z) (or o without a gate).
+ * The state is read once and written once.
+ * Arguments:
+ *   q, k [B, H, dk], v [B, H, dv] (x_dtype), preprocessed;
+ *   log_alpha [B, H, dk], beta [B, H] (gate_dtype);
+ *   out_gate NULL or [B, H, dv] logits (x_dtype);
+ *   state fp32 [B, H, dk, dv], in place;  out [B, H, dv] (x_dtype).
+ */
+int kda_decode_step(int32_t B, int32_t H, int32_t dk, int32_t dv,
+                    int32_t x_dtype, int32_t gate_dtype,
+                    const void* q, const void* k, const void* v,
+                    const void* log_alpha, const void* beta,
+                    const void* out_gate,
+                    float* state, void* out,
+                    void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

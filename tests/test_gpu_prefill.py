@@ -1,0 +1,95 @@
+"""Chunked prefill on the GPU against the fp64 token-by-token oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+from gated_delta_rule_64_amd import synth
+from kda_helpers import TOL, assert_close, f64, oracle_layer_inputs, to_dev, to_host64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def K():
+    from gated_delta_rule_64_amd import kda
+    return kda
+
+
+def gpu_layer(K, inp, initial_state=None, final_state=None):
+    """preprocess + chunked prefill (with the output gate when present)."""
+    H, dk, dv, T = inp["H"], inp["dk"], inp["dv"], inp["T_tot"]
+    cu = to_dev(inp["cu_seqlens"])
+    q, k, v, la, beta = K.kda_preprocess(to_dev(inp["q_in"]), to_dev(inp["k_in"]), to_dev(inp["v_in"]),
+                                         to_dev(inp["w_q"]), to_dev(inp["w_k"]), to_dev(inp["w_v"]),
+                                         to_dev(inp["g"]), to_dev(inp["b"]), H, dk, dv, cu_seqlens=cu)
+    z = to_dev(inp["z"]).view(T, H, dv) if inp["z"] is not None else None
+    if initial_state is None and inp["S0"] is not None:
+        initial_state = to_dev(inp["S0"])
+    out, S = K.kda_prefill_chunked(q, k, v, la, beta, out_gate=z, initial_state=initial_state,
+                                   final_state=final_state, cu_seqlens=cu)
+    torch.cuda.synchronize()
+    return out, S
+
+
+def test_core_tiny_workload(K, oracle_mod):
+    """1 x 64 tokens, 2 heads, d = 16, fp32, zero state (identity conv)."""
+    inp = synth.make("core_tiny")
+    out, S = gpu_layer(K, inp)
+    ref = oracle_mod.layer(oracle_layer_inputs(inp))
+    assert_close("o", to_host64(out), ref["y"], TOL["f32"])
+    assert_close("state", to_host64(S), ref["S"], TOL["f32"])
+
+
+@pytest.mark.parametrize("x_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dk,dv", [(16, 16), (32, 64), (64, 128), (128, 32)])
+def test_core_parity_ragged(K, oracle_mod, x_dtype, dk, dv):
+    lengths = [1, 63, 64, 0, 65, 200]
+    inp = synth.core(21, lengths, 3, dk, dv, x_dtype=x_dtype, s0_std=0.3, out_gate=True)
+    print(f"core x={x_dtype} dk={dk} dv={dv}", flush=True)
+    cu = to_dev(inp["cu_seqlens"])
+    out, S = K.kda_prefill_chunked(to_dev(inp["q"]), to_dev(inp["k"]), to_dev(inp["v"]),
+                                   to_dev(inp["log_alpha"]), to_dev(inp["beta"]), out_gate=to_dev(inp["z"]),
+                                   initial_state=to_dev(inp["S0"]), cu_seqlens=cu)
+    torch.cuda.synchronize()
+    y, Sr = oracle_mod.recurrence(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), f64(inp["log_alpha"]),
+                                  f64(inp["beta"]), z=f64(inp["z"]), S0=f64(inp["S0"]),
+                                  cu_seqlens=inp["cu_seqlens"])
+    assert_close("o", to_host64(out), y, TOL[x_dtype])
+    assert_close("state", to_host64(S), Sr, TOL[x_dtype])
+
+
+@pytest.mark.parametrize("lengths", [(1000,), (130, 0, 64, 1, 700)])
+def test_layer_bf16_d128_reduced(K, oracle_mod, lengths):
+    """Ling-shaped heads (d = 128, bf16) through preprocess and prefill."""
+    inp = synth.make("varlen_64", lengths=lengths, H=4)
+    print(f"layer bf16 d128 lengths={lengths}", flush=True)
+    out, S = gpu_layer(K, inp)
+    ref = oracle_mod.layer(oracle_layer_inputs(inp))
+    assert_close("y", to_host64(out), ref["y"], TOL["bf16"])
+    assert_close("state", to_host64(S), ref["S"], TOL["bf16"])
+
+
+def test_state_in_place_and_repeat_bit_identical(K, oracle_mod):
+    inp = synth.core(22, [150, 77], 2, 128, 128, x_dtype="bf16", s0_std=0.3, out_gate=True)
+    args = [to_dev(inp[n]) for n in ("q", "k", "v", "log_alpha", "beta")]
+    cu = to_dev(inp["cu_seqlens"])
+    S_sep = to_dev(inp["S0"]).clone()
+    o1, S1 = K.kda_prefill_chunked(*args, out_gate=to_dev(inp["z"]), initial_state=S_sep, cu_seqlens=cu)
+    S_in = to_dev(inp["S0"]).clone()
+    o2, S2 = K.kda_prefill_chunked(*args, out_gate=to_dev(inp["z"]), initial_state=S_in, final_state=S_in,
+                                   cu_seqlens=cu)
+    torch.cuda.synchronize()
+    assert S2.data_ptr() == S_in.data_ptr()
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+def test_zero_length_sequences_keep_state(K):
+    inp = synth.core(23, [0, 5, 0], 2, 64, 64, x_dtype="f32", s0_std=0.3)
+    cu = to_dev(inp["cu_seqlens"])
+    S0 = to_dev(inp["S0"])
+    out, S = K.kda_prefill_chunked(*[to_dev(inp[n]) for n in ("q", "k", "v", "log_alpha", "beta")],
+                                   initial_state=S0, cu_seqlens=cu)
+    torch.cuda.synchronize()
+    assert torch.equal(S[0], S0[0]) and torch.equal(S[2], S0[2])
+    assert not torch.equal(S[1], S0[1])
