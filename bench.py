@@ -1,0 +1,294 @@
+#!/usr/bin/env python3
+"""Benchmark of libkda on one MI355X.
+
+One step = one pass of the whole prefill path over one batch: the fused
+preprocess (conv4 + L2 norm + gates) and the chunked prefill with the output
+gate, on the 4096-token, 32-head, d = 128 bf16 layer (``layer_t4k``), inputs
+already resident in HBM.  ``value`` is prefill tokens/s over the K timed steps.
+
+The decode step (256 sequences x 32 heads x 128^2 fp32 state, in place) is
+timed in its own loop and reported under ``decode`` in GB/s of algorithmic
+traffic.  ``roofline`` covers the kernel with the largest share of the step:
+algorithmic bytes per launch / average launch time from HIP events recorded
+around each kernel during a second pass of the same K steps.  ``cpu_baseline``
+times the fp64 CPU oracle on the same workload (rank 0, one GPU only).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16, published
+METRIC = "KDA prefill tokens/s @H32 d128 T4K; decode-step achieved HBM GB/s"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--decode-steps", type=int, default=50)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--workload", default="layer_t4k")
+    return p.parse_args()
+
+
+def dev(arr):
+    import torch
+    arr = np.ascontiguousarray(arr)
+    if arr.dtype == np.uint16:
+        return torch.from_numpy(arr.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(arr).cuda()
+
+
+def threads_for_cpu():
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+# ---------------------------------------------------------------------------
+# algorithmic bytes per launch (what each kernel must move at least once)
+# ---------------------------------------------------------------------------
+
+def chunk_count(lengths):
+    return int(sum((L + 63) // 64 for L in lengths))
+
+
+def record_bytes(K, T, N, H, dk, dv, x_code):
+    ws = K.kda_prefill_workspace_bytes(T, N, H, dk, dv, x_code)
+    slots = (T + 63) // 64 + N
+    cmap = ((N + 1) * 4 + 255) // 256 * 256
+    return (ws - cmap) // (slots * H)
+
+
+def prefill_kernel_bytes(name, w, x, g, rec, has_s0, has_gate):
+    """x, g: bytes per input / gate element; rec: workspace bytes per (chunk, head)."""
+    T, H, dk, dv, N = w.T_tot, w.H, w.dk, w.dv, w.N
+    th = T * H
+    chunks = chunk_count(w.lengths) * H
+    state = N * H * dk * dv * 4
+    if name == "preprocess":
+        reads = th * (x * (2 * dk + dv) + x * dk + x) + H * (2 * dk + dv) * 4 * x
+        writes = th * (x * (2 * dk + dv) + 4 * dk + 4)
+        return reads + writes
+    if name.endswith("intra"):
+        return th * (x * (2 * dk + dv) + g * dk + g) + chunks * rec
+    if name.endswith("state"):
+        return chunks * rec + th * x * dv * (2 if has_gate else 1) + state * (2 if has_s0 else 1)
+    if name == "chunk_map":
+        return (N + 1) * 8
+    raise KeyError(name)
+
+
+def decode_bytes(B, H, dk, dv, x, g, has_gate):
+    per = 2 * dk * dv * 4 + x * (2 * dk + dv) + g * (dk + 1) + x * dv * (2 if has_gate else 1)
+    return B * H * per
+
+
+def traffic_entry(kernel):
+    """HBM bytes per launch measured with rocprofv3 counters, if the kernel's
+    source is unchanged since they were taken (else None)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        table = json.load(f)
+    e = table.get(kernel)
+    if not e:
+        return None
+    src = os.path.join(ROOT, "gated_delta_rule_64_amd", "csrc", e["source"])
+    if not os.path.exists(src):
+        return None
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    return e["bytes_per_launch"] if sha == e["source_sha256"] else None
+
+
+def roofline(kernel, bytes_per_launch, ms_per_launch):
+    achieved = bytes_per_launch / (ms_per_launch * 1e-3) / 1e9
+    return {"kernel": kernel, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic_entry(kernel), "bytes_per_launch": int(bytes_per_launch),
+            "us_per_launch": round(ms_per_launch * 1e3, 2)}
+
+
+# ---------------------------------------------------------------------------
+
+def bench_prefill(args):
+    import torch
+    from gated_delta_rule_64_amd import _lib, kda, synth
+
+    w = synth.workload(args.workload)
+    inp = synth.make(w)
+    H, dk, dv, T, N = w.H, w.dk, w.dv, w.T_tot, w.N
+    t = {k: dev(inp[k]) for k in ("q_in", "k_in", "v_in", "w_q", "w_k", "w_v", "g", "b")}
+    z = dev(inp["z"]).view(T, H, dv) if inp["z"] is not None else None
+    cu = dev(inp["cu_seqlens"])
+    S0 = dev(inp["S0"]) if inp["S0"] is not None else None
+    xdt = torch.bfloat16 if w.x_dtype == "bf16" else torch.float32
+    pre_out = (torch.empty((T, H, dk), dtype=xdt, device="cuda"), torch.empty((T, H, dk), dtype=xdt, device="cuda"),
+               torch.empty((T, H, dv), dtype=xdt, device="cuda"), torch.empty((T, H, dk), device="cuda"),
+               torch.empty((T, H), device="cuda"))
+    out = torch.empty((T, H, dv), dtype=xdt, device="cuda")
+    S_out = torch.empty((N, H, dk, dv), device="cuda")
+    x_code = 1 if w.x_dtype == "bf16" else 0
+    ws = torch.empty(kda.kda_prefill_workspace_bytes(T, N, H, dk, dv, x_code), dtype=torch.uint8, device="cuda")
+
+    def step():
+        q, k, v, la, beta = kda.kda_preprocess(t["q_in"], t["k_in"], t["v_in"], t["w_q"], t["w_k"], t["w_v"],
+                                               t["g"], t["b"], H, dk, dv, cu_seqlens=cu, out=pre_out)
+        kda.kda_prefill_chunked(q, k, v, la, beta, out_gate=z, initial_state=S0, final_state=S_out,
+                                cu_seqlens=cu, workspace=ws, out=out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    # second pass of the same K steps with per-kernel HIP events
+    _lib.profile_enable(True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed_ev = time.perf_counter() - t1
+    _lib.profile_enable(False)
+    times = _lib.profile_collect()
+
+    xb = 2 if w.x_dtype == "bf16" else 4
+    rec = record_bytes(kda, T, N, H, dk, dv, x_code)
+    kernels = {}
+    for name, (n, ms) in times.items():
+        per = ms / n
+        b = prefill_kernel_bytes(name, w, xb, 4, rec, S0 is not None, z is not None)
+        kernels[name] = {"launches": n, "us_per_launch": round(per * 1e3, 2),
+                         "algorithmic_bytes": int(b), "gbs": round(b / (per * 1e-3) / 1e9, 1)}
+    dom = max(times, key=lambda k: times[k][1])
+    dn, dms = times[dom]
+    roof = roofline(dom, kernels[dom]["algorithmic_bytes"], dms / dn)
+    return {"w": w, "inp": inp, "elapsed": elapsed, "elapsed_events": elapsed_ev, "kernels": kernels,
+            "roofline": roof}
+
+
+def bench_decode(args):
+    import torch
+    from gated_delta_rule_64_amd import _lib, kda, synth
+
+    inp = synth.make("decode_b256")
+    H, dk, dv, B = inp["H"], inp["dk"], inp["dv"], inp["N"]
+    cs = dev(inp["conv_state"])
+    q, k, v, la, beta = kda.kda_preprocess(*(dev(inp[n]) for n in ("q_in", "k_in", "v_in", "w_q", "w_k", "w_v",
+                                                                  "g", "b")), H, dk, dv,
+                                           cu_seqlens=dev(inp["cu_seqlens"]), conv_state=cs)
+    z = dev(inp["z"]).view(B, H, dv)
+    state = dev(inp["S0"])
+    out = torch.empty((B, H, dv), dtype=torch.bfloat16, device="cuda")
+    for _ in range(args.warmup):
+        kda.kda_decode_step(q, k, v, la, beta, state, out_gate=z, out=out)
+    torch.cuda.synchronize()
+    _lib.profile_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(args.decode_steps):
+        kda.kda_decode_step(q, k, v, la, beta, state, out_gate=z, out=out)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    _lib.profile_enable(False)
+    n, ms = _lib.profile_collect()["decode"]
+    per_ms = ms / n
+    b = decode_bytes(B, H, dk, dv, 2, 4, True)
+    return {"metric": "decode-step achieved HBM GB/s", "value": round(b / (per_ms * 1e-3) / 1e9, 1),
+            "unit": "GB/s", "workload": "decode_b256", "B": B, "H": H, "dk": dk, "dv": dv,
+            "steps": args.decode_steps, "us_per_step_events": round(per_ms * 1e3, 2),
+            "us_per_step_wall": round(elapsed / args.decode_steps * 1e6, 2),
+            "roofline": roofline("decode", b, per_ms)}
+
+
+def cpu_baseline(res):
+    import oracle
+    from gated_delta_rule_64_amd import synth
+
+    inp = res["inp"]
+    w = res["w"]
+    nth = threads_for_cpu()
+    f = synth.to_f64
+    o_in = {"q_in": f(inp["q_in"]), "k_in": f(inp["k_in"]), "v_in": f(inp["v_in"]), "w_q": f(inp["w_q"]),
+            "w_k": f(inp["w_k"]), "w_v": f(inp["w_v"]), "g": f(inp["g"]), "b": f(inp["b"]),
+            "z": f(inp["z"]) if inp["z"] is not None else None,
+            "S0": f(inp["S0"]) if inp["S0"] is not None else None, "conv_state": None,
+            "cu_seqlens": inp["cu_seqlens"].astype(np.int64), "H": w.H, "dk": w.dk, "dv": w.dv}
+    oracle.build(force=False)
+    t0 = time.perf_counter()
+    oracle.layer(o_in, nthreads=nth)
+    dt = time.perf_counter() - t0
+    return {"value": round(w.T_tot / dt, 1), "unit": "tokens/s", "cores": nth, "kind": "oracle",
+            "sample": f"full {w.name} workload ({w.T_tot} tokens x {w.H} heads, preprocess + recurrence), "
+                      f"one pass, fp64, {dt:.2f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path shards over "
+              "sequences and heads with no exchange, and no multi-GPU run is part of this build.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    from gated_delta_rule_64_amd import _lib
+    _lib.lib()  # fail loudly if libkda is not built
+
+    res = bench_prefill(args)
+    w = res["w"]
+    value = w.T_tot * args.steps / res["elapsed"]
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["elapsed"] / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.x_dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "T": w.T_tot, "N": w.N, "H": w.H, "dk": w.dk, "dv": w.dv,
+                   "chunk": 64, "out_gate": w.out_gate, "state": "fp32",
+                   "step": "kda_preprocess + kda_prefill_chunked"},
+        "roofline": res["roofline"],
+        "kernels": res["kernels"],
+        "ms_per_step_with_kernel_events": round(res["elapsed_events"] / args.steps * 1e3, 4),
+    }
+    line["decode"] = bench_decode(args)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(res)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -35,6 +35,14 @@ PROTOTYPES = {
 }
 
 
+class KernelTime(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 48), ("launches", ctypes.c_int64), ("total_ms", ctypes.c_double)]
+
+
+PROTOTYPES["kda_profile_enable"] = (ctypes.c_int, [ctypes.c_int])
+PROTOTYPES["kda_profile_collect"] = (ctypes.c_int, [ctypes.POINTER(KernelTime), ctypes.c_int])
+
+
 class KdaError(RuntimeError):
     def __init__(self, status: int, detail: str):
         self.status = status
@@ -68,3 +76,17 @@ def status_string(status: int) -> str:
 def check(status: int) -> None:
     if status != KDA_OK:
         raise KdaError(status, lib().kda_last_error_detail().decode())
+
+
+def profile_enable(on: bool) -> None:
+    """Per-kernel HIP-event timing of later calls on this thread (see kda.h)."""
+    lib().kda_profile_enable(1 if on else 0)
+
+
+def profile_collect() -> dict:
+    """{kernel name: (launches, total ms)} since the last collect."""
+    buf = (KernelTime * 64)()
+    n = lib().kda_profile_collect(buf, 64)
+    if n < 0:
+        raise KdaError(-n, "event timing failed")
+    return {buf[i].name.decode(): (int(buf[i].launches), float(buf[i].total_ms)) for i in range(n)}

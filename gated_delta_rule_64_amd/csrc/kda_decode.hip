@@ -18,6 +18,7 @@
 // of a wave with lane shuffles, then across the four waves through LDS.
 #include "kda_common.h"
 #include "kda_internal.h"
+#include "kda_profile.h"
 
 namespace kda {
 namespace {
@@ -148,6 +149,7 @@ template <int DK, int DV, typename XT, typename GT>
 hipError_t launch_typed(const DecodeArgs& a, hipStream_t s) {
     const unsigned grid = static_cast<unsigned>(a.B) * static_cast<unsigned>(a.H);
     if (grid == 0) return hipSuccess;
+    LaunchTimer timer("decode", s);
     hipLaunchKernelGGL((decode_kernel<DK, DV, XT, GT>), dim3(grid), dim3(256), 0, s,
                        static_cast<const XT*>(a.q), static_cast<const XT*>(a.k),
                        static_cast<const XT*>(a.v), static_cast<const GT*>(a.la),

@@ -8,6 +8,7 @@
 // evaluated directly, so no factor can overflow whatever the decay rates.
 #include "kda_prefill_common.h"
 #include "kda_internal.h"
+#include "kda_profile.h"
 #include "kda_prefill_mfma.h"
 
 namespace kda {
@@ -275,12 +276,14 @@ hipError_t launch_gen_typed(const PrefillArgs& a, hipStream_t s, int32_t* base, 
                                            hipFuncAttributeMaxDynamicSharedMemorySize,
                                            static_cast<int>(lds));
         if (e != hipSuccess) return e;
+        LaunchTimer timer("gen_intra", s);
         hipLaunchKernelGGL((gen_intra_kernel<XT, GT>), dim3(static_cast<unsigned>(slots), a.H), dim3(256),
                            lds, s, k);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     const int64_t blocks = static_cast<int64_t>(a.N) * a.H * (a.dv / 16);
+    LaunchTimer timer("gen_state", s);
     hipLaunchKernelGGL((gen_state_kernel<XT, GT>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, k);
     return hipGetLastError();
 }
@@ -299,8 +302,12 @@ size_t prefill_workspace_bytes(int64_t T, int N, int H, int dk, int dv, DT x) {
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
     int32_t* base = static_cast<int32_t*>(a.ws);
     char* recs = static_cast<char*>(a.ws) + chunk_map_bytes(a.N);
-    hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(1024), 0, s, a.cu, a.N, a.T, base);
-    hipError_t e = hipGetLastError();
+    hipError_t e;
+    {
+        LaunchTimer timer("chunk_map", s);
+        hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(1024), 0, s, a.cu, a.N, a.T, base);
+        e = hipGetLastError();
+    }
     if (e != hipSuccess) return e;
     if (prefill_uses_mfma(a.dk, a.dv, a.x)) return launch_prefill_mfma(a, s, base, recs);
     float* rec = reinterpret_cast<float*>(recs);

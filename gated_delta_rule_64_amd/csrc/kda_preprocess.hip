@@ -7,24 +7,28 @@
 // field" table of the page "Ling 3.0 Flash").
 //
 // Streaming design: the op reads each raw input once and writes each output
-// once, so it is bound by HBM.  A group of 16 lanes covers one head's 128
-// channels of a token row with 16-byte accesses (8 channels per lane), and
-// walks a run of 16 consecutive tokens, keeping the three previous raw rows
-// of its 8 channels in registers; the conv then reads every input row once
-// (plus a three-row halo per run).  The L2 norm reduces over the 16 lanes
-// with shuffles.  Runs respect sequence boundaries: history before a
-// sequence start is the caller's conv state or zero.  A second tiny kernel,
-// ordered after the first on the stream, rewrites the conv state, so the
-// read of the old state never races with the write of the new one.
+// once, so it is bound by HBM.  A workgroup covers 64 tokens of one head.  Its
+// four waves split the work by tensor (q, k, v, gates), which keeps each
+// lane's registers small (one filter, one history) and the occupancy high.
+// Inside a wave, a group of 16 lanes covers a 128-channel row of one token
+// with 16-byte accesses (8 channels per lane) and walks a run of 16
+// consecutive tokens, keeping the three previous raw rows of its channels in
+// registers: the conv reads every input row once, plus a three-row halo per
+// run.  The L2 norm reduces over the 16 lanes with shuffles.  Runs respect
+// sequence boundaries: history before a sequence start is the caller's conv
+// state or zero.  A second tiny kernel, ordered after the first on the
+// stream, rewrites the conv state, so the read of the old state never races
+// with the write of the new one.
 #include "kda_common.h"
 #include "kda_internal.h"
+#include "kda_profile.h"
 
 namespace kda {
 namespace {
 
 constexpr int kRun = 16;                 // tokens per 16-lane group
-constexpr int kGroups = 16;              // groups per workgroup
-constexpr int kTile = kRun * kGroups;    // tokens per workgroup
+constexpr int kTile = kRun * 4;          // tokens per workgroup (4 groups per wave)
+constexpr int kBatch = 4;                // rows loaded ahead
 constexpr float kL2Eps = 1e-6f;
 
 template <typename XT>
@@ -61,122 +65,113 @@ __device__ __forceinline__ void load_hist(const float* cs, int n, int tau, int64
     }
 }
 
+// one of q, k, v: conv (+ L2 norm for q and k) over a run of tokens
 template <typename XT>
-__global__ __launch_bounds__(256) void preprocess_kernel(PrepK<XT> a) {
-    const int h = blockIdx.y;
-    const int grp = threadIdx.x >> 4;
-    const int li = threadIdx.x & 15;
-    const int64_t t_begin = static_cast<int64_t>(blockIdx.x) * kTile + grp * kRun;
-    if (t_begin >= a.T) return;  // whole 16-lane group leaves together
-    const int64_t t_end = min(t_begin + kRun, a.T);
-
-    const int dk = a.dk, dv = a.dv;
-    const int64_t wk = static_cast<int64_t>(a.H) * dk, wv = static_cast<int64_t>(a.H) * dv;
-    const int64_t cs_width = 2 * wk + wv;
-    const bool aq = 8 * li < dk;  // lane covers q/k channels
-    const bool av = 8 * li < dv;  // lane covers v channels
-    const int64_t off_k = static_cast<int64_t>(h) * dk + 8 * li;
-    const int64_t off_v = static_cast<int64_t>(h) * dv + 8 * li;
-
-    // conv taps of this lane's 8 channels, for q, k, v
-    float wq[8][4], wkk[8][4], wvv[8][4];
+__device__ __forceinline__ void conv_run(const PrepK<XT>& a, const XT* src, const XT* wts, XT* dst,
+                                         int64_t width, int64_t off, int64_t cs_off, bool act, bool norm,
+                                         int64_t t_begin, int64_t t_end) {
+    float w[8][4];
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            wq[c][j] = aq ? ld(a.w_q + (off_k + c) * 4 + j) : 0.f;
-            wkk[c][j] = aq ? ld(a.w_k + (off_k + c) * 4 + j) : 0.f;
-            wvv[c][j] = av ? ld(a.w_v + (off_v + c) * 4 + j) : 0.f;
-        }
+        for (int j = 0; j < 4; ++j) w[c][j] = act ? ld(wts + (off + c) * 4 + j) : 0.f;
     }
-
+    const int64_t cs_width = static_cast<int64_t>(a.H) * (2 * a.dk + a.dv);
     int n = a.cu ? find_seq(a.cu, a.N, t_begin) : 0;
     int64_t seq_start = a.cu ? a.cu[n] : 0;
     int64_t seq_end = a.cu ? a.cu[n + 1] : a.T;
-
-    // history rows for positions t_begin-3 .. t_begin-1 (index 0 = oldest)
-    float hq[3][8], hk[3][8], hv[3][8];
+    float hst[3][8];  // raw rows t-3, t-2, t-1
 #pragma unroll
     for (int m = 0; m < 3; ++m) {
         const int64_t pos = t_begin - 3 + m;
-        if (pos >= seq_start) {
-            load_row(a.q_in, pos, wk, off_k, aq, hq[m]);
-            load_row(a.k_in, pos, wk, off_k, aq, hk[m]);
-            load_row(a.v_in, pos, wv, off_v, av, hv[m]);
-        } else {
-            const int tau = static_cast<int>(pos - seq_start);  // -3 .. -1
-            load_hist(a.cs, n, tau, cs_width, off_k, aq, hq[m]);
-            load_hist(a.cs, n, tau, cs_width, wk + off_k, aq, hk[m]);
-            load_hist(a.cs, n, tau, cs_width, 2 * wk + off_v, av, hv[m]);
-        }
+        if (pos >= seq_start) load_row(src, pos, width, off, act, hst[m]);
+        else load_hist(a.cs, n, static_cast<int>(pos - seq_start), cs_width, cs_off + off, act, hst[m]);
     }
-
-    for (int64_t t0 = t_begin; t0 < t_end; t0 += 4) {
-        // issue four rows of loads before using any of them
-        float xq[4][8], xk[4][8], xv[4][8], xg[4][8];
-        float xb[4];
+    for (int64_t t0 = t_begin; t0 < t_end; t0 += kBatch) {
+        float x[kBatch][8];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int64_t t = t0 + r;
-            const bool in = t < t_end;
-            load_row(a.q_in, t, wk, off_k, in && aq, xq[r]);
-            load_row(a.k_in, t, wk, off_k, in && aq, xk[r]);
-            load_row(a.v_in, t, wv, off_v, in && av, xv[r]);
-            load_row(a.g, t, wk, off_k, in && aq, xg[r]);
-            xb[r] = (in && li == 0) ? ld(a.b + t * a.H + h) : 0.f;
-        }
+        for (int r = 0; r < kBatch; ++r) load_row(src, t0 + r, width, off, act && (t0 + r < t_end), x[r]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
+        for (int r = 0; r < kBatch; ++r) {
             const int64_t t = t0 + r;
             if (t >= t_end) break;
             if (t >= seq_end) {
-                // entering a later sequence: skip empty ones, restart history
+                // entering a later sequence: skip empty ones, restart the history
                 do {
                     ++n;
                     seq_start = a.cu[n];
                     seq_end = a.cu[n + 1];
                 } while (seq_end <= t);
 #pragma unroll
-                for (int m = 0; m < 3; ++m) {
-                    load_hist(a.cs, n, m - 3, cs_width, off_k, aq, hq[m]);
-                    load_hist(a.cs, n, m - 3, cs_width, wk + off_k, aq, hk[m]);
-                    load_hist(a.cs, n, m - 3, cs_width, 2 * wk + off_v, av, hv[m]);
-                }
+                for (int m = 0; m < 3; ++m) load_hist(a.cs, n, m - 3, cs_width, cs_off + off, act, hst[m]);
             }
-            float cq[8], ck[8], cv[8];
-            float ssq = 0.f, ssk = 0.f;
+            float y[8];
+            float ss = 0.f;
 #pragma unroll
             for (int c = 0; c < 8; ++c) {
-                cq[c] = wq[c][0] * hq[0][c] + wq[c][1] * hq[1][c] + wq[c][2] * hq[2][c] + wq[c][3] * xq[r][c];
-                ck[c] = wkk[c][0] * hk[0][c] + wkk[c][1] * hk[1][c] + wkk[c][2] * hk[2][c] + wkk[c][3] * xk[r][c];
-                cv[c] = wvv[c][0] * hv[0][c] + wvv[c][1] * hv[1][c] + wvv[c][2] * hv[2][c] + wvv[c][3] * xv[r][c];
-                ssq += cq[c] * cq[c];
-                ssk += ck[c] * ck[c];
-                hq[0][c] = hq[1][c]; hq[1][c] = hq[2][c]; hq[2][c] = xq[r][c];
-                hk[0][c] = hk[1][c]; hk[1][c] = hk[2][c]; hk[2][c] = xk[r][c];
-                hv[0][c] = hv[1][c]; hv[1][c] = hv[2][c]; hv[2][c] = xv[r][c];
+                y[c] = w[c][0] * hst[0][c] + w[c][1] * hst[1][c] + w[c][2] * hst[2][c] + w[c][3] * x[r][c];
+                ss += y[c] * y[c];
+                hst[0][c] = hst[1][c];
+                hst[1][c] = hst[2][c];
+                hst[2][c] = x[r][c];
+            }
+            if (norm) {
+#pragma unroll
+                for (int o = 8; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 16);
+                const float inv = 1.f / sqrtf(ss + kL2Eps);
+#pragma unroll
+                for (int c = 0; c < 8; ++c) y[c] *= inv;
+            }
+            if (act) st8(dst + t * width + off, y);
+        }
+    }
+}
+
+template <typename XT>
+__global__ __launch_bounds__(256) void preprocess_kernel(PrepK<XT> a) {
+    // heads vary fastest across workgroups, so the workgroups in flight
+    // together cover whole token rows (all heads) of the [T, H*d] inputs
+    const int64_t bid = static_cast<int64_t>(blockIdx.y) * gridDim.x + blockIdx.x;
+    const int64_t tiles = (a.T + kTile - 1) / kTile;
+    if (bid >= tiles * a.H) return;
+    const int h = static_cast<int>(bid % a.H);
+    const int wave = threadIdx.x >> 6;  // 0: q, 1: k, 2: v, 3: gates
+    const int grp = (threadIdx.x >> 4) & 3;
+    const int li = threadIdx.x & 15;
+    const int64_t t_begin = (bid / a.H) * kTile + grp * kRun;
+    if (t_begin >= a.T) return;  // whole 16-lane group leaves together
+    const int64_t t_end = min(t_begin + kRun, a.T);
+    const int64_t wk = static_cast<int64_t>(a.H) * a.dk, wv = static_cast<int64_t>(a.H) * a.dv;
+    const int64_t off_k = static_cast<int64_t>(h) * a.dk + 8 * li;
+    const int64_t off_v = static_cast<int64_t>(h) * a.dv + 8 * li;
+    const bool aq = 8 * li < a.dk, av = 8 * li < a.dv;
+    if (wave < 3) {
+        const bool is_v = wave == 2;
+        const XT* src = wave == 0 ? a.q_in : (wave == 1 ? a.k_in : a.v_in);
+        const XT* wts = wave == 0 ? a.w_q : (wave == 1 ? a.w_k : a.w_v);
+        XT* dst = wave == 0 ? a.q_out : (wave == 1 ? a.k_out : a.v_out);
+        conv_run(a, src, wts, dst, is_v ? wv : wk, is_v ? off_v : off_k, wave * wk, is_v ? av : aq, !is_v,
+                 t_begin, t_end);
+    } else {
+        for (int64_t t0 = t_begin; t0 < t_end; t0 += kBatch) {
+            float x[kBatch][8];
+            float xb[kBatch];
+#pragma unroll
+            for (int r = 0; r < kBatch; ++r) {
+                const bool in = t0 + r < t_end;
+                load_row(a.g, t0 + r, wk, off_k, in && aq, x[r]);
+                xb[r] = (in && li == 0) ? ld(a.b + (t0 + r) * a.H + h) : 0.f;
             }
 #pragma unroll
-            for (int off = 8; off >= 1; off >>= 1) {
-                ssq += __shfl_xor(ssq, off, 16);
-                ssk += __shfl_xor(ssk, off, 16);
-            }
-            const float iq = 1.f / sqrtf(ssq + kL2Eps);
-            const float ik = 1.f / sqrtf(ssk + kL2Eps);
-            float la[8];
+            for (int r = 0; r < kBatch; ++r) {
+                const int64_t t = t0 + r;
+                if (t >= t_end) break;
+                float la[8];
 #pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                cq[c] *= iq;
-                ck[c] *= ik;
-                la[c] = -softplus(xg[r][c]);
+                for (int c = 0; c < 8; ++c) la[c] = -softplus(x[r][c]);
+                if (aq) st8(a.la_out + t * wk + off_k, la);
+                if (li == 0) a.beta_out[t * a.H + h] = sigmoid(xb[r]);
             }
-            if (aq) {
-                st8(a.q_out + t * wk + off_k, cq);
-                st8(a.k_out + t * wk + off_k, ck);
-                st8(a.la_out + t * wk + off_k, la);
-            }
-            if (av) st8(a.v_out + t * wv + off_v, cv);
-            if (li == 0) a.beta_out[t * a.H + h] = sigmoid(xb[r]);
         }
     }
 }
@@ -221,8 +216,11 @@ hipError_t launch_typed(const PreprocessArgs& a, hipStream_t s) {
     k.v_out = static_cast<XT*>(a.v_out);
     k.la_out = a.la_out; k.beta_out = a.beta_out;
     if (a.T > 0) {
-        const int64_t tiles = (a.T + kTile - 1) / kTile;
-        hipLaunchKernelGGL((preprocess_kernel<XT>), dim3(static_cast<unsigned>(tiles), a.H), dim3(256),
+        const int64_t blocks = (a.T + kTile - 1) / kTile * a.H;
+        const int64_t gx = blocks < (1 << 20) ? blocks : (1 << 20);
+        const int64_t gy = (blocks + gx - 1) / gx;
+        LaunchTimer timer("preprocess", s);
+        hipLaunchKernelGGL((preprocess_kernel<XT>), dim3(static_cast<unsigned>(gx), static_cast<unsigned>(gy)), dim3(256),
                            0, s, k);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -230,6 +228,7 @@ hipError_t launch_typed(const PreprocessArgs& a, hipStream_t s) {
     if (a.conv_state != nullptr && a.N > 0) {
         const int64_t width = static_cast<int64_t>(a.H) * (2 * a.dk + a.dv);
         const int bps = static_cast<int>((width + 255) / 256);
+        LaunchTimer timer("conv_state", s);
         hipLaunchKernelGGL((conv_state_kernel<XT>), dim3(static_cast<unsigned>(a.N) * bps), dim3(256), 0, s,
                            k, bps);
         return hipGetLastError();

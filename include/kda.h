@@ -36,7 +36,8 @@
  *    thread-local sentence naming the failing argument or HIP call.
  *  - Supported shapes: dk, dv in {16, 32, 64, 128}; H >= 1; N >= 1;
  *    T_tot >= 0 and below 2^31; sequences of length 0 are allowed.
- *  - Thread safety: no global mutable state besides the per-thread error text.
+ *  - Thread safety: no global mutable state; the error text and the optional
+ *    kernel-timing records (kda_profile_enable) are per host thread.
  */
 #ifndef KDA_H
 #define KDA_H
@@ -166,6 +167,25 @@ int kda_decode_step(int32_t B, int32_t H, int32_t dk, int32_t dv,
                     const void* out_gate,
                     float* state, void* out,
                     void* stream);
+
+/*
+ * Kernel timing for profiling tools (not needed for normal use).
+ * kda_profile_enable(1) makes every later call on the calling host thread
+ * bracket each kernel it launches with a pair of HIP events recorded on the
+ * call's stream; kda_profile_enable(0) stops it.  kda_profile_collect()
+ * waits for the recorded events, sums them per kernel name since the last
+ * collect, writes at most max_entries records to `out` and returns the number
+ * of distinct kernels (or -KDA_ERR_HIP if an event failed).  Event objects
+ * are pooled per thread; no device memory is allocated.
+ */
+typedef struct kda_kernel_time {
+    char name[48];
+    int64_t launches;
+    double total_ms;
+} kda_kernel_time_t;
+
+int kda_profile_enable(int on);
+int kda_profile_collect(kda_kernel_time_t* out, int max_entries);
 
 #ifdef __cplusplus
 }

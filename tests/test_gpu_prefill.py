@@ -93,3 +93,31 @@ def test_zero_length_sequences_keep_state(K):
     torch.cuda.synchronize()
     assert torch.equal(S[0], S0[0]) and torch.equal(S[2], S0[2])
     assert not torch.equal(S[1], S0[1])
+
+
+def test_layer_t4k_full(K, oracle_mod):
+    """The 4096-token, 32-head bf16 layer in the bench's launch configuration:
+    every output and every state entry against the oracle."""
+    inp = synth.make("layer_t4k")
+    print("layer_t4k full size", flush=True)
+    out, S = gpu_layer(K, inp)
+    ref = oracle_mod.layer(oracle_layer_inputs(inp))
+    assert_close("y", to_host64(out), ref["y"], TOL["bf16"])
+    assert_close("state", to_host64(S), ref["S"], TOL["bf16"])
+
+
+@pytest.mark.parametrize("case", ["fast_decay", "slow_decay", "beta_one", "zero_rows"])
+def test_stress_cases(K, oracle_mod, case):
+    """Decay rates at both extremes (the fast one takes the exact diagonal-tile
+    path), saturated writes, and all-zero q/k rows (must give 0, not NaN)."""
+    kw = {"fast_decay": dict(g_mean=4.0), "slow_decay": dict(g_mean=-6.0),
+          "beta_one": dict(b_mean=12.0), "zero_rows": {}}[case]
+    inp = synth.make("long_t256k", lengths=(700, 1300), H=3, **kw)
+    if case == "zero_rows":
+        inp["q_in"][100:180] = 0
+        inp["k_in"][100:180] = 0
+    print(f"stress {case}", flush=True)
+    out, S = gpu_layer(K, inp)
+    ref = oracle_mod.layer(oracle_layer_inputs(inp))
+    assert_close("y", to_host64(out), ref["y"], TOL["bf16"])
+    assert_close("state", to_host64(S), ref["S"], TOL["bf16"])
