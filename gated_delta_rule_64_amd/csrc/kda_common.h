@@ -102,4 +102,24 @@ __device__ __forceinline__ int find_seq(const int32_t* cu, int N, int64_t t) {
 
 constexpr int kChunk = 64;  // tokens per chunk of the prefill
 
+// Workgroup barrier for LDS traffic only.  __syncthreads() fences all memory
+// at workgroup scope, which makes every wave wait for its outstanding global
+// loads and stores (and LDS DMA copies) before the barrier.  This barrier
+// waits only for the wave's own LDS operations (lgkmcnt 0); the compiler-only
+// fences keep memory operations from moving across it.  A wave that needs
+// its global->LDS copies to be visible waits for them (vmcnt) first.
+__device__ __forceinline__ void lds_barrier() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt left at their maxima
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// wait until this wave has no global memory operation in flight (vmcnt 0)
+__device__ __forceinline__ void wait_vmem() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); lgkmcnt and expcnt at their maxima
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 }  // namespace kda

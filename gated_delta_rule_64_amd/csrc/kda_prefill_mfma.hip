@@ -96,24 +96,46 @@ struct MfmaK {
 // phase 1
 // ---------------------------------------------------------------------------
 
-constexpr size_t kIntraLds = (3 * 64 * KS) * 2 + (64 * GS + 3 * 4096 + 64 + 8 * 128) * 4 + 16;
+constexpr int kIntraThreads = 512;  // 8 waves: two per SIMD
+constexpr size_t kIntraLds = (3 * 64 * KS) * 2 + (64 * GS + 3 * 4096 + 64 + 16 * 128) * 4 + 16;
+
+__device__ __forceinline__ void unpack8(uint4 v, float (&x)[8]) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x[2 * i] = __uint_as_float(w[i] << 16);
+        x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+}
+
+__device__ __forceinline__ void lds8f(const float* p, float (&x)[8]) {
+    const float4 u = reinterpret_cast<const float4*>(p)[0];
+    const float4 v = reinterpret_cast<const float4*>(p)[1];
+    x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w;
+    x[4] = v.x; x[5] = v.y; x[6] = v.z; x[7] = v.w;
+}
+
+// (R, S) of tile i in the lower block triangle, row-major order
+__device__ __forceinline__ void tile_rs(int i, int& R, int& S) {
+    R = i >= 6 ? 3 : i >= 3 ? 2 : i >= 1 ? 1 : 0;
+    S = i - R * (R + 1) / 2;
+}
 
 template <typename GT>
-__global__ __launch_bounds__(256) void mfma_intra_kernel(MfmaK<GT> a) {
+__global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) {
     extern __shared__ __align__(16) char smem[];
-    uint16_t* sK = reinterpret_cast<uint16_t*>(smem);
-    uint16_t* sQ = sK + 64 * KS;
-    uint16_t* sV = sQ + 64 * KS;
-    float* sG = reinterpret_cast<float*>(sV + 64 * KS);
-    float* sA = sG + 64 * GS;
-    float* sM = sA + 4096;
-    float* sT = sM + 4096;
-    float* sB = sT + 4096;
-    float* sTot = sB + 64;
-    int* sFlag = reinterpret_cast<int*>(sTot + 8 * 128);
-    // staging for the transposes, over buffers that are dead by then
-    uint16_t* sStW = sV;                                  // [64][KS] bf16
-    uint16_t* sStQ = reinterpret_cast<uint16_t*>(sA);     // [64][128] bf16
+    uint16_t* sK = reinterpret_cast<uint16_t*>(smem);   // [64][KS] keys (bf16)
+    uint16_t* sQ = sK + 64 * KS;                        // [64][KS] queries
+    uint16_t* sV = sQ + 64 * KS;                        // [64][KS] values
+    float* sG = reinterpret_cast<float*>(sV + 64 * KS);  // [64][GS] decay cumsums
+    float* sA = sG + 64 * GS;                           // [64][64]
+    float* sM = sA + 4096;                              // [64][64]
+    float* sT = sM + 4096;                              // [64][64]
+    float* sB = sT + 4096;                              // [64] beta
+    float* sTot = sB + 64;                              // [16][128] scan partials, later scratch
+    int* sFlag = reinterpret_cast<int*>(sTot + 16 * 128);
+    uint16_t* sStW = sV;                                // staging of -W  [64][KS]
+    uint16_t* sStQ = reinterpret_cast<uint16_t*>(sA);   // staging of Q'  [64][128]
 
     const int slot = blockIdx.x, h = blockIdx.y;
     if (slot >= a.base[a.N]) return;
@@ -124,43 +146,46 @@ __global__ __launch_bounds__(256) void mfma_intra_kernel(MfmaK<GT> a) {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, c = lane & 15;
     char* rec = a.rec + (static_cast<int64_t>(slot) * H + h) * REC_BYTES;
 
-    // ---- load q, k, v (bf16 rows of 256 B) and the decay logs; zero past L
+    // ---- inputs to LDS.  Loads are branch-free (rows past L read row L-1 and
+    // are replaced by zero) so that all of them are in flight together.
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int idx = tid + 256 * i;
+    for (int i = 0; i < 2; ++i) {
+        const int idx = tid + kIntraThreads * i;
         const int r = idx >> 4, ch = idx & 15;
-        uint4 kk = make_uint4(0, 0, 0, 0), qq = kk, vv = kk;
-        if (r < L) {
-            const int64_t goff = ((t0 + r) * H + h) * 128 + ch * 8;
-            kk = *reinterpret_cast<const uint4*>(a.k + goff);
-            qq = *reinterpret_cast<const uint4*>(a.q + goff);
-            vv = *reinterpret_cast<const uint4*>(a.v + goff);
-        }
+        const bool in = r < L;
+        const int64_t goff = ((t0 + (in ? r : L - 1)) * H + h) * 128 + ch * 8;
+        uint4 kk = *reinterpret_cast<const uint4*>(a.k + goff);
+        uint4 qq = *reinterpret_cast<const uint4*>(a.q + goff);
+        uint4 vv = *reinterpret_cast<const uint4*>(a.v + goff);
+        if (!in) kk = qq = vv = make_uint4(0, 0, 0, 0);
         *reinterpret_cast<uint4*>(sK + r * KS + ch * 8) = kk;
         *reinterpret_cast<uint4*>(sQ + r * KS + ch * 8) = qq;
         *reinterpret_cast<uint4*>(sV + r * KS + ch * 8) = vv;
     }
-    const int cq = tid & 31, rg = tid >> 5;  // 4 channels x 8 rows per thread
-    float x[8][4];
+    const int cq = tid & 31, rg = tid >> 5;  // 4 channels x 4 rows per thread
+    float x[4][4];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int r = 8 * rg + j;
-        if (r < L) {
-            ld4(a.la + ((t0 + r) * H + h) * 128 + 4 * cq, x[j]);
-        } else {
-            x[j][0] = x[j][1] = x[j][2] = x[j][3] = 0.f;
-        }
+    for (int j = 0; j < 4; ++j) {
+        const int r = 4 * rg + j;
+        const bool in = r < L;
+        ld4(a.la + ((t0 + (in ? r : L - 1)) * H + h) * 128 + 4 * cq, x[j]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[j][e] = in ? x[j][e] : 0.f;  // padded tokens: no decay
     }
-    if (tid < 64) sB[tid] = tid < L ? ld(a.beta + (t0 + tid) * H + h) : 0.f;
+    if (tid < 64) {
+        const float bv = ld(a.beta + (t0 + (tid < L ? tid : L - 1)) * H + h);
+        sB[tid] = tid < L ? bv : 0.f;  // padded tokens: no write
+    }
     if (tid < 4) sFlag[tid] = 0;
-    for (int i = tid; i < 2 * 4096 / 4; i += 256)
-        reinterpret_cast<float4*>(sA)[i] = make_float4(0.f, 0.f, 0.f, 0.f);  // sA and sM
 #pragma unroll
-    for (int j = 1; j < 8; ++j)
+    for (int i = 0; i < 4; ++i)
+        reinterpret_cast<float4*>(sA)[tid + kIntraThreads * i] = make_float4(0.f, 0.f, 0.f, 0.f);  // sA, sM
+#pragma unroll
+    for (int j = 1; j < 4; ++j)
 #pragma unroll
         for (int e = 0; e < 4; ++e) x[j][e] += x[j - 1][e];
-    *reinterpret_cast<float4*>(sTot + rg * 128 + 4 * cq) = make_float4(x[7][0], x[7][1], x[7][2], x[7][3]);
-    __syncthreads();
+    *reinterpret_cast<float4*>(sTot + rg * 128 + 4 * cq) = make_float4(x[3][0], x[3][1], x[3][2], x[3][3]);
+    lds_barrier();
     {
         float off[4] = {0.f, 0.f, 0.f, 0.f};
         for (int q2 = 0; q2 < rg; ++q2) {
@@ -168,87 +193,92 @@ __global__ __launch_bounds__(256) void mfma_intra_kernel(MfmaK<GT> a) {
             off[0] += t4.x; off[1] += t4.y; off[2] += t4.z; off[3] += t4.w;
         }
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            *reinterpret_cast<float4*>(sG + (8 * rg + j) * GS + 4 * cq) =
+        for (int j = 0; j < 4; ++j)
+            *reinterpret_cast<float4*>(sG + (4 * rg + j) * GS + 4 * cq) =
                 make_float4(x[j][0] + off[0], x[j][1] + off[1], x[j][2] + off[2], x[j][3] + off[3]);
     }
-    __syncthreads();
+    lds_barrier();
     // sub-blocks whose decay inside 16 tokens is too steep for the factored form
     if (tid < 128) {
 #pragma unroll
         for (int R = 0; R < 4; ++R) {
             const float d = sG[(16 * R) * GS + tid] - sG[(16 * R + 15) * GS + tid];
-            if (d > kDiagRange) sFlag[R] = 1;  // benign race: all writers store 1
+            if (d > kDiagRange) sFlag[R] = 1;  // benign race: every writer stores 1
         }
     }
-    __syncthreads();
+    lds_barrier();
 
-    // ---- A and M: 10 tiles (R >= S), spread over the 4 waves
-    {
-        // tiles (R, S) per wave, one byte each (R in the high nibble), 0xFF = none
-        const uint32_t code = wave == 0 ? 0xFF3000u : wave == 1 ? 0x311110u : wave == 2 ? 0x322120u : 0xFF3322u;
-#pragma unroll
-        for (int ti = 0; ti < 3; ++ti) {
-            const uint32_t tile = (code >> (8 * ti)) & 0xFFu;
-            if (tile == 0xFFu) continue;
-            const int R = static_cast<int>(tile >> 4), S = static_cast<int>(tile & 15u);
-            const int b = 16 * R;
-            f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accM = accA;
-            if (R == S && sFlag[R]) {
-                // exact pairwise decays
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = b + 4 * g + i, s = 16 * S + c;
-                    float av = 0.f, mv = 0.f;
-                    if (s <= r) {
-                        for (int ch = 0; ch < 128; ++ch) {
-                            const float ks = bfv(sK + s * KS + ch) * expf(sG[r * GS + ch] - sG[s * GS + ch]);
-                            av += bfv(sK + r * KS + ch) * ks;
-                            mv += bfv(sQ + r * KS + ch) * ks;
-                        }
-                    }
-                    accA[i] = av;
-                    accM[i] = mv;
-                }
-            } else {
-                const int rl = b + c, sr = 16 * S + c;
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks) {
-                    float kl[8], ql[8], kr[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int ch = 32 * ks + 8 * g + e;
-                        const float gb = sG[b * GS + ch];
-                        const float el = expf(sG[rl * GS + ch] - gb);
-                        kl[e] = bfv(sK + rl * KS + ch) * el;
-                        ql[e] = bfv(sQ + rl * KS + ch) * el;
-                        kr[e] = bfv(sK + sr * KS + ch) * expf(gb - sG[sr * GS + ch]);
-                    }
-                    const bf16x8 bk = to_bf16x8(kr);
-                    accA = mfma(to_bf16x8(kl), bk, accA);
-                    accM = mfma(to_bf16x8(ql), bk, accM);
-                }
-            }
+    // ---- A and M: 10 tiles (R >= S); wave w takes tiles w and w + 8
+    for (int ti = wave; ti < 10; ti += 8) {
+        int R, S;
+        tile_rs(ti, R, S);
+        const int b = 16 * R;
+        f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accM = accA;
+        if (R == S && sFlag[R]) {
+            // exact pairwise decays (steep decay inside the block)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int r = b + 4 * g + i, s = 16 * S + c;
-                sA[r * 64 + s] = s < r ? accA[i] : 0.f;
-                sM[r * 64 + s] = s <= r ? accM[i] : 0.f;
+                const int r = b + 4 * g + i, s2 = 16 * S + c;
+                float av = 0.f, mv = 0.f;
+                if (s2 <= r) {
+                    for (int ch = 0; ch < 128; ++ch) {
+                        const float ks = bfv(sK + s2 * KS + ch) * expf(sG[r * GS + ch] - sG[s2 * GS + ch]);
+                        av += bfv(sK + r * KS + ch) * ks;
+                        mv += bfv(sQ + r * KS + ch) * ks;
+                    }
+                }
+                accA[i] = av;
+                accM[i] = mv;
+            }
+        } else {
+            const int rl = b + c, sr = 16 * S + c;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const int ch0 = 32 * ks + 8 * g;
+                float kl[8], ql[8], kr[8], gl[8], gb[8], gr[8];
+                unpack8(*reinterpret_cast<const uint4*>(sK + rl * KS + ch0), kl);
+                unpack8(*reinterpret_cast<const uint4*>(sQ + rl * KS + ch0), ql);
+                unpack8(*reinterpret_cast<const uint4*>(sK + sr * KS + ch0), kr);
+                lds8f(sG + rl * GS + ch0, gl);
+                lds8f(sG + b * GS + ch0, gb);
+                lds8f(sG + sr * GS + ch0, gr);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float el = __expf(gl[e] - gb[e]);  // <= 1
+                    kl[e] *= el;
+                    ql[e] *= el;
+                    kr[e] *= __expf(gb[e] - gr[e]);
+                }
+                const bf16x8 bk = to_bf16x8(kr);
+                accA = mfma(to_bf16x8(kl), bk, accA);
+                accM = mfma(to_bf16x8(ql), bk, accM);
             }
         }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = b + 4 * g + i, s2 = 16 * S + c;
+            sA[r * 64 + s2] = s2 < r ? accA[i] : 0.f;
+            sM[r * 64 + s2] = s2 <= r ? accM[i] : 0.f;
+        }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- T = (I + Diag(beta) A)^-1
-    // diagonal blocks: wave R, lane j < 16 owns column j of T_RR
-    {
+    // diagonal blocks: wave R < 4, lane j < 16 owns column j of T_RR in registers
+    if (wave < 4) {
         const int R = wave, j = lane;
         float t[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
+            float arow[16];
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const float4 v4 = *reinterpret_cast<const float4*>(sA + (16 * R + r) * 64 + 16 * R + 4 * q4);
+                arow[4 * q4] = v4.x; arow[4 * q4 + 1] = v4.y; arow[4 * q4 + 2] = v4.z; arow[4 * q4 + 3] = v4.w;
+            }
             float sum = 0.f;
 #pragma unroll
-            for (int s = 0; s < r; ++s) sum += sA[(16 * R + r) * 64 + 16 * R + s] * t[s];
+            for (int s2 = 0; s2 < r; ++s2) sum += arow[s2] * t[s2];
             t[r] = (r == j ? 1.f : 0.f) - sB[16 * R + r] * sum;
         }
         if (j < 16) {
@@ -256,190 +286,195 @@ __global__ __launch_bounds__(256) void mfma_intra_kernel(MfmaK<GT> a) {
             for (int r = 0; r < 16; ++r) sT[(16 * R + r) * 64 + 16 * R + j] = t[r];
         }
     }
-    __syncthreads();
-    // off-diagonal blocks by distance d = R - S:
+    lds_barrier();
+    // off-diagonal blocks by distance d = R - S (waves 0..2):
     //   Y = Diag(beta_R) sum_{J=S}^{R-1} A_RJ T_JS ;  T_RS = -T_RR Y
-    float* sY = sTot;  // 4 x 256 floats of scratch (the cumsum totals are dead)
+    float* sY = sTot;  // 3 x 256 floats of scratch (the scan partials are dead)
     for (int d = 1; d <= 3; ++d) {
         const int S = wave, R = wave + d;
-        const bool active = R <= 3;
+        const bool active = wave < 3 && R <= 3;
         if (active) {
+            float acc[4] = {0.f, 0.f, 0.f, 0.f};
+            for (int J = S; J < R; ++J) {
+                float tcol[16];
+#pragma unroll
+                for (int kk = 0; kk < 16; ++kk) tcol[kk] = sT[(16 * J + kk) * 64 + 16 * S + c];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float* arow = sA + (16 * R + 4 * g + i) * 64 + 16 * J;
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        const float4 v4 = reinterpret_cast<const float4*>(arow)[q4];
+                        acc[i] += v4.x * tcol[4 * q4] + v4.y * tcol[4 * q4 + 1] + v4.z * tcol[4 * q4 + 2] +
+                                  v4.w * tcol[4 * q4 + 3];
+                    }
+                }
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 4 * g + i;
-                float acc = 0.f;
-                for (int J = S; J < R; ++J)
-#pragma unroll
-                    for (int kk = 0; kk < 16; ++kk)
-                        acc += sA[(16 * R + r) * 64 + 16 * J + kk] * sT[(16 * J + kk) * 64 + 16 * S + c];
-                sY[wave * 256 + r * 16 + c] = sB[16 * R + r] * acc;
+                sY[wave * 256 + r * 16 + c] = sB[16 * R + r] * acc[i];
             }
         }
-        __syncthreads();
+        lds_barrier();
         if (active) {
+            float ycol[16];
+#pragma unroll
+            for (int kk = 0; kk < 16; ++kk) ycol[kk] = sY[wave * 256 + kk * 16 + c];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 4 * g + i;
+                const float* trow = sT + (16 * R + r) * 64 + 16 * R;
                 float acc = 0.f;
 #pragma unroll
-                for (int kk = 0; kk < 16; ++kk)
-                    acc += sT[(16 * R + r) * 64 + 16 * R + kk] * sY[wave * 256 + kk * 16 + c];
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const float4 v4 = reinterpret_cast<const float4*>(trow)[q4];
+                    acc += v4.x * ycol[4 * q4] + v4.y * ycol[4 * q4 + 1] + v4.z * ycol[4 * q4 + 2] +
+                           v4.w * ycol[4 * q4 + 3];
+                }
                 sT[(16 * R + r) * 64 + 16 * S + c] = -acc;
             }
         }
-        __syncthreads();
+        lds_barrier();
     }
-    // upper blocks of T stay unused: every product below skips them
+    // blocks of T above the diagonal are never written; every reader masks them
 
-    // ---- W = T (beta e^G K) and U~ = T (beta V): this wave's column tiles
-    f32x4 accW[2][4], accU[2][4];
+    // ---- W = T (beta e^G K) and U~ = T (beta V): column tile nt = wave
+    const int nt = wave;
+    const int chn = 16 * nt + c;
+    f32x4 accW[4], accU[4];
     {
         bf16x8 Ta[4][2];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
+                const int row = 16 * mt + c, col0 = 32 * ks + 8 * g;
                 float tv[8];
+                lds8f(sT + row * 64 + col0, tv);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int col = 32 * ks + 8 * g + e;
-                    tv[e] = col <= 16 * mt + c ? sT[(16 * mt + c) * 64 + col] : 0.f;
-                }
+                for (int e = 0; e < 8; ++e) tv[e] = col0 + e <= row ? tv[e] : 0.f;
                 Ta[mt][ks] = to_bf16x8(tv);
             }
 #pragma unroll
-        for (int q2 = 0; q2 < 2; ++q2) {
-            const int nt = 2 * wave + q2;
-            const int ch = 16 * nt + c;
+        for (int mt = 0; mt < 4; ++mt) {
+            accW[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            accU[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const int s0 = 32 * ks + 8 * g;
+            float bt[8], bk[8], bv[8];
+            lds8f(sB + s0, bt);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int s2 = s0 + e;
+                bk[e] = bt[e] * __expf(sG[s2 * GS + chn]) * bfv(sK + s2 * KS + chn);
+                bv[e] = bt[e] * bfv(sV + s2 * KS + chn);
+            }
+            const bf16x8 Bk = to_bf16x8(bk), Bv = to_bf16x8(bv);
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
-                accW[q2][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-                accU[q2][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            }
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                float bk[8], bv[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int s = 32 * ks + 8 * g + e;
-                    const float be = sB[s];
-                    bk[e] = be * expf(sG[s * GS + ch]) * bfv(sK + s * KS + ch);
-                    bv[e] = be * bfv(sV + s * KS + ch);
-                }
-                const bf16x8 Bk = to_bf16x8(bk), Bv = to_bf16x8(bv);
-#pragma unroll
-                for (int mt = 0; mt < 4; ++mt) {
-                    if (32 * ks > 16 * mt + 15) continue;  // T is lower triangular
-                    accW[q2][mt] = mfma(Ta[mt][ks], Bk, accW[q2][mt]);
-                    accU[q2][mt] = mfma(Ta[mt][ks], Bv, accU[q2][mt]);
-                }
-            }
-            // U~ in result layout, per 16-column slice nt
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                uint2 p;
-                p.x = pack_bf16x2(accU[q2][mt][0], accU[q2][mt][1]);
-                p.y = pack_bf16x2(accU[q2][mt][2], accU[q2][mt][3]);
-                *reinterpret_cast<uint2*>(rec + R_UT + ((nt * 4 + mt) * 64 + lane) * 8) = p;
+                if (32 * ks > 16 * mt + 15) continue;  // T is lower triangular
+                accW[mt] = mfma(Ta[mt][ks], Bk, accW[mt]);
+                accU[mt] = mfma(Ta[mt][ks], Bv, accU[mt]);
             }
         }
+        // U~ in result layout, slice nt
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            uint2 p;
+            p.x = pack_bf16x2(accU[mt][0], accU[mt][1]);
+            p.y = pack_bf16x2(accU[mt][2], accU[mt][3]);
+            *reinterpret_cast<uint2*>(rec + R_UT + ((nt * 4 + mt) * 64 + lane) * 8) = p;
+        }
     }
-    __syncthreads();  // V is dead: its buffer becomes the staging area of W
+    lds_barrier();  // V and A are dead: their buffers become the staging areas
 
-    // ---- Q' = e^G Q - M W and M U~; stage W and Q' for the transposes
+    // ---- Q' = e^G Q - M W and M U~; stage -W and Q' for the transposes
     {
         bf16x8 Mneg[4][2], Mpos[4][2];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                float mv[8], mn[8];
+                const float* mrow = sM + (16 * mt + c) * 64 + 32 * ks + 4 * g;
+                const float4 lo = *reinterpret_cast<const float4*>(mrow);
+                const float4 hi = *reinterpret_cast<const float4*>(mrow + 16);
+                const float mv[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+                float mn[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int col = 32 * ks + perm(g, e);
-                    mv[e] = sM[(16 * mt + c) * 64 + col];
-                    mn[e] = -mv[e];
-                }
+                for (int e = 0; e < 8; ++e) mn[e] = -mv[e];
                 Mpos[mt][ks] = to_bf16x8(mv);
                 Mneg[mt][ks] = to_bf16x8(mn);
             }
+        bf16x8 Bw[2], Bu[2];
 #pragma unroll
-        for (int q2 = 0; q2 < 2; ++q2) {
-            const int nt = 2 * wave + q2;
-            const int ch = 16 * nt + c;
-            bf16x8 Bw[2], Bu[2];
+        for (int ks = 0; ks < 2; ++ks) {
+            Bw[ks] = to_bf16x8(accW[2 * ks], accW[2 * ks + 1]);
+            Bu[ks] = to_bf16x8(accU[2 * ks], accU[2 * ks + 1]);
+        }
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                Bw[ks] = to_bf16x8(accW[q2][2 * ks], accW[q2][2 * ks + 1]);
-                Bu[ks] = to_bf16x8(accU[q2][2 * ks], accU[q2][2 * ks + 1]);
+        for (int mt = 0; mt < 4; ++mt) {
+            f32x4 qp, oi = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * mt + 4 * g + i;
+                qp[i] = __expf(sG[r * GS + chn]) * bfv(sQ + r * KS + chn);
             }
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                f32x4 qp, oi = {0.f, 0.f, 0.f, 0.f};
+            for (int ks = 0; ks < 2; ++ks) {
+                if (32 * ks > 16 * mt + 15) continue;  // M is lower triangular
+                qp = mfma(Mneg[mt][ks], Bw[ks], qp);
+                oi = mfma(Mpos[mt][ks], Bu[ks], oi);
+            }
+            uint2 p;
+            p.x = pack_bf16x2(oi[0], oi[1]);
+            p.y = pack_bf16x2(oi[2], oi[3]);
+            *reinterpret_cast<uint2*>(rec + R_OI + ((nt * 4 + mt) * 64 + lane) * 8) = p;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = 16 * mt + 4 * g + i;
-                    qp[i] = expf(sG[r * GS + ch]) * bfv(sQ + r * KS + ch);
-                }
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    if (32 * ks > 16 * mt + 15) continue;  // M is lower triangular
-                    qp = mfma(Mneg[mt][ks], Bw[ks], qp);
-                    oi = mfma(Mpos[mt][ks], Bu[ks], oi);
-                }
-                uint2 p;
-                p.x = pack_bf16x2(oi[0], oi[1]);
-                p.y = pack_bf16x2(oi[2], oi[3]);
-                *reinterpret_cast<uint2*>(rec + R_OI + ((nt * 4 + mt) * 64 + lane) * 8) = p;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = 16 * mt + 4 * g + i;
-                    sStW[r * KS + ch] = f32_to_bf16(-accW[q2][mt][i]);
-                    sStQ[r * 128 + ch] = f32_to_bf16(qp[i]);
-                }
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * mt + 4 * g + i;
+                sStW[r * KS + chn] = f32_to_bf16(-accW[mt][i]);
+                sStQ[r * 128 + chn] = f32_to_bf16(qp[i]);
             }
         }
     }
-    __syncthreads();
+    lds_barrier();
 
-    // ---- stores in the A-operand layout: -W, Q' (4 blocks per wave each), K^T
+    // ---- stores in the A-operand layout: -W, Q' (2 blocks per wave each), K^T
     {
-        const int mt = wave;
+        const int mt = wave >> 1;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
+        for (int k2 = 0; k2 < 2; ++k2) {
+            const int ks = 2 * (wave & 1) + k2;
             const int r = 16 * mt + c;
             const int c0 = 32 * ks + 4 * g;
-            uint4 w4, q4;
             const uint2 wlo = *reinterpret_cast<const uint2*>(sStW + r * KS + c0);
             const uint2 whi = *reinterpret_cast<const uint2*>(sStW + r * KS + c0 + 16);
             const uint2 qlo = *reinterpret_cast<const uint2*>(sStQ + r * 128 + c0);
             const uint2 qhi = *reinterpret_cast<const uint2*>(sStQ + r * 128 + c0 + 16);
-            w4 = make_uint4(wlo.x, wlo.y, whi.x, whi.y);
-            q4 = make_uint4(qlo.x, qlo.y, qhi.x, qhi.y);
             const int blk = (mt * 4 + ks) * 64 + lane;
-            *reinterpret_cast<uint4*>(rec + R_NEGW + blk * 16) = w4;
-            *reinterpret_cast<uint4*>(rec + R_QP + blk * 16) = q4;
+            *reinterpret_cast<uint4*>(rec + R_NEGW + blk * 16) = make_uint4(wlo.x, wlo.y, whi.x, whi.y);
+            *reinterpret_cast<uint4*>(rec + R_QP + blk * 16) = make_uint4(qlo.x, qlo.y, qhi.x, qhi.y);
         }
+        const int t = wave;
+        const int ch = 16 * t + c;
+        const float glast = sG[63 * GS + ch];
 #pragma unroll
-        for (int q2 = 0; q2 < 2; ++q2) {
-            const int t = 2 * wave + q2;
-            const int ch = 16 * t + c;
-            const float glast = sG[63 * GS + ch];
+        for (int ks = 0; ks < 2; ++ks) {
+            float kv[8];
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                float kv[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int s = 32 * ks + perm(g, e);
-                    kv[e] = expf(glast - sG[s * GS + ch]) * bfv(sK + s * KS + ch);
-                }
-                uint4 p;
-                p.x = pack_bf16x2(kv[0], kv[1]);
-                p.y = pack_bf16x2(kv[2], kv[3]);
-                p.z = pack_bf16x2(kv[4], kv[5]);
-                p.w = pack_bf16x2(kv[6], kv[7]);
-                *reinterpret_cast<uint4*>(rec + R_KHT + ((t * 2 + ks) * 64 + lane) * 16) = p;
+            for (int e = 0; e < 8; ++e) {
+                const int s2 = 32 * ks + perm(g, e);
+                kv[e] = __expf(glast - sG[s2 * GS + ch]) * bfv(sK + s2 * KS + ch);
             }
+            uint4 p;
+            p.x = pack_bf16x2(kv[0], kv[1]);
+            p.y = pack_bf16x2(kv[2], kv[3]);
+            p.z = pack_bf16x2(kv[4], kv[5]);
+            p.w = pack_bf16x2(kv[6], kv[7]);
+            *reinterpret_cast<uint4*>(rec + R_KHT + ((t * 2 + ks) * 64 + lane) * 16) = p;
         }
         if (tid < 128) reinterpret_cast<float*>(rec + R_GAM)[tid] = expf(sG[63 * GS + tid]);
     }
@@ -449,14 +484,20 @@ __global__ __launch_bounds__(256) void mfma_intra_kernel(MfmaK<GT> a) {
 // phase 2
 // ---------------------------------------------------------------------------
 
-// LDS image of one chunk for one 16-column slice
+// One workgroup (4 waves) per (sequence, head, half of the state columns);
+// wave w owns the 16 columns of slice 4*half + w.  The chunk's shared factors
+// (-W, Q', K^T: 48 KB) are copied into LDS once per workgroup, one chunk
+// ahead, with global_load_lds_dwordx4; the output tile of the chunk (64 tokens
+// x 64 columns) is staged in LDS and written with the output gate applied as
+// whole 128-byte row segments, one chunk behind.
+constexpr int kStateThreads = 256;
 constexpr int B_NEGW = 0;
 constexpr int B_QP = 16384;
 constexpr int B_KHT = 32768;
-constexpr int B_UT = 49152;   // 2 KB: this slice's U~
-constexpr int B_OI = 51200;   // 2 KB: this slice's M U~
-constexpr int B_GAM = 53248;  // 512 B
-constexpr int B_BYTES = 53760;
+constexpr int B_UT = 49152;   // 8 KB: U~ of the 4 slices of this half
+constexpr int B_OI = 57344;   // 8 KB: M U~ of the 4 slices
+constexpr int B_GAM = 65536;  // 512 B
+constexpr int B_BYTES = 66048;
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -464,75 +505,110 @@ __device__ __forceinline__ void lds_copy16(const char* gsrc, char* lds_dst) {
     __builtin_amdgcn_global_load_lds(static_cast<const void*>(gsrc), (lds_void*)(lds_dst), 16, 0, 0);
 }
 
-// issue the asynchronous copy of chunk record `r` (slice sl) into LDS buffer `buf`
-__device__ __forceinline__ void prefetch_chunk(const char* r, char* buf, int sl, int lane) {
+// asynchronous copy of one chunk record (this half's slices) into `buf`;
+// the 64.5 one-KB pieces are split over the four waves
+__device__ __forceinline__ void prefetch_chunk(const char* r, char* buf, int half, int wave, int lane) {
 #pragma unroll
-    for (int b = 0; b < 48; ++b) lds_copy16(r + b * 1024 + lane * 16, buf + b * 1024);
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-        lds_copy16(r + R_UT + sl * 2048 + b * 1024 + lane * 16, buf + B_UT + b * 1024);
-        lds_copy16(r + R_OI + sl * 2048 + b * 1024 + lane * 16, buf + B_OI + b * 1024);
+    for (int i = 0; i < 12; ++i) {
+        const int b = wave + 4 * i;  // 0..47: -W, Q', K^T
+        lds_copy16(r + b * 1024 + lane * 16, buf + b * 1024);
     }
-    if (lane < 32) lds_copy16(r + R_GAM + lane * 16, buf + B_GAM);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int b = wave + 4 * i;  // 0..7
+        lds_copy16(r + R_UT + half * 8192 + b * 1024 + lane * 16, buf + B_UT + b * 1024);
+        lds_copy16(r + R_OI + half * 8192 + b * 1024 + lane * 16, buf + B_OI + b * 1024);
+    }
+    if (wave == 0 && lane < 32) lds_copy16(r + R_GAM + lane * 16, buf + B_GAM);
 }
 
-template <typename GT>
-__global__ __launch_bounds__(64) void mfma_state_kernel(MfmaK<GT> a) {
-    extern __shared__ __align__(16) char smem[];
-    // blockIdx -> (sequence, head, slice): the 8 slices of one (sequence, head)
-    // share an XCD (workgroups are dealt round-robin over the 8 XCDs), so the
-    // records they all read are cached in one L2
+template <typename GT, bool kGate>
+__global__ __launch_bounds__(kStateThreads) void mfma_state_kernel(MfmaK<GT> a) {
+    // two chunk buffers and the output staging as separate LDS objects, so the
+    // compiler can tell copies into one buffer from reads of the other
+    __shared__ __align__(16) char buf0[B_BYTES];
+    __shared__ __align__(16) char buf1[B_BYTES];
+    __shared__ __align__(16) float stage[64 * 64];  // [64 tokens][64 columns]
+    // blockIdx -> (sequence, head, half): both halves of a (sequence, head)
+    // land on one XCD (workgroups are dealt round-robin over the 8 XCDs), so
+    // the chunk records they share are read through one L2
     const int bid = blockIdx.x;
-    const int xcd = bid & 7, sl = (bid >> 3) & 7;
-    const int64_t grp = static_cast<int64_t>(bid >> 6) * 8 + xcd;
+    const int xcd = bid & 7, half = (bid >> 3) & 1;
+    const int64_t grp = static_cast<int64_t>(bid >> 4) * 8 + xcd;
     if (grp >= a.groups) return;
     const int H = a.H;
     const int n = static_cast<int>(grp / H), h = static_cast<int>(grp % H);
-    const int lane = threadIdx.x, g = lane >> 4, c = lane & 15;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, c = lane & 15;
+    const int sl = 4 * half + wave;
     const int col = 16 * sl + c;
 
     // state S[16t + 4g + i][col] in registers
     f32x4 S[8];
     const int64_t sidx = grp * (128 * 128);
+    if (a.S0 != nullptr) {  // one uniform branch: all 32 loads in flight together
 #pragma unroll
-    for (int t = 0; t < 8; ++t)
+        for (int t = 0; t < 8; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) S[t][i] = a.S0 ? a.S0[sidx + (16 * t + 4 * g + i) * 128 + col] : 0.f;
+            for (int i = 0; i < 4; ++i) S[t][i] = a.S0[sidx + (16 * t + 4 * g + i) * 128 + col];
+    } else {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) S[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 
     const int64_t sb = seq_begin(a.cu, n), se = seq_finish(a.cu, n, a.T);
     const int slot0 = a.base[n];
     const int nch = a.base[n + 1] - slot0;
     auto rec_of = [&](int j) { return a.rec + (static_cast<int64_t>(slot0 + j) * H + h) * REC_BYTES; };
-
-    float zn[16];  // output-gate logits of the chunk being prefetched
-    auto load_z = [&](int j) {
-        const int64_t tc = sb + static_cast<int64_t>(j) * kChunk;
-        const int Lc = static_cast<int>(min(static_cast<int64_t>(kChunk), se - tc));
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 16 * mt + 4 * g + i;
-                zn[mt * 4 + i] = (a.z != nullptr && r < Lc) ? ld(a.z + ((tc + r) * H + h) * 128 + col) : 0.f;
-            }
+    auto chunk_len = [&](int j) {
+        return static_cast<int>(min(static_cast<int64_t>(kChunk), se - (sb + static_cast<int64_t>(j) * kChunk)));
     };
-    if (nch > 0) {
-        prefetch_chunk(rec_of(0), smem, sl, lane);
-        load_z(0);
-    }
-    for (int j = 0; j < nch; ++j) {
-        __builtin_amdgcn_s_waitcnt(0);  // chunk j has landed in LDS (and its z in registers)
-        __builtin_amdgcn_sched_barrier(0);
-        char* buf = smem + (j & 1) * B_BYTES;
-        float zc[16];
+
+    // cooperative output: thread -> token row orow, 16 columns starting at ocol
+    const int orow = tid >> 2, ocol = 16 * (tid & 3);
+    uint4 zraw[2];  // gate logits of the chunk whose output is written next
+    auto load_z = [&](int j) {
+        if (!kGate) return;
+        const int Lc = chunk_len(j);
+        const int64_t t = sb + static_cast<int64_t>(j) * kChunk + (orow < Lc ? orow : Lc - 1);
+        const bf16* zp = a.z + (t * H + h) * 128 + 64 * half + ocol;
+        zraw[0] = reinterpret_cast<const uint4*>(zp)[0];
+        zraw[1] = reinterpret_cast<const uint4*>(zp)[1];
+    };
+    auto store_out = [&](int j) {
+        const int Lc = chunk_len(j);
+        if (orow >= Lc) return;
+        const int64_t t = sb + static_cast<int64_t>(j) * kChunk + orow;
+        float y[16];
 #pragma unroll
-        for (int q2 = 0; q2 < 16; ++q2) zc[q2] = zn[q2];
-        if (j + 1 < nch) {
-            prefetch_chunk(rec_of(j + 1), smem + ((j + 1) & 1) * B_BYTES, sl, lane);
-            load_z(j + 1);
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const float4 v4 = *reinterpret_cast<const float4*>(stage + orow * 64 + ocol + 4 * q4);
+            y[4 * q4] = v4.x; y[4 * q4 + 1] = v4.y; y[4 * q4 + 2] = v4.z; y[4 * q4 + 3] = v4.w;
         }
-        const int64_t tc = sb + static_cast<int64_t>(j) * kChunk;
-        const int Lc = static_cast<int>(min(static_cast<int64_t>(kChunk), se - tc));
+        if (kGate) {
+            float zf[16];
+            unpack8(zraw[0], *reinterpret_cast<float(*)[8]>(&zf[0]));
+            unpack8(zraw[1], *reinterpret_cast<float(*)[8]>(&zf[8]));
+#pragma unroll
+            for (int e = 0; e < 16; ++e) y[e] *= 1.f / (1.f + __expf(-zf[e]));
+        }
+        uint4 o0, o1;
+        o0.x = pack_bf16x2(y[0], y[1]); o0.y = pack_bf16x2(y[2], y[3]);
+        o0.z = pack_bf16x2(y[4], y[5]); o0.w = pack_bf16x2(y[6], y[7]);
+        o1.x = pack_bf16x2(y[8], y[9]); o1.y = pack_bf16x2(y[10], y[11]);
+        o1.z = pack_bf16x2(y[12], y[13]); o1.w = pack_bf16x2(y[14], y[15]);
+        bf16* op = a.out + (t * H + h) * 128 + 64 * half + ocol;
+        reinterpret_cast<uint4*>(op)[0] = o0;
+        reinterpret_cast<uint4*>(op)[1] = o1;
+    };
+
+    // one chunk: its factors are in `cur`; the next chunk's go to `nxt`
+    auto step = [&](int j, const char* cur, char* nxt) {
+        wait_vmem();    // this wave's copies of chunk j (and its older stores) are done
+        lds_barrier();  // ... and every other wave's; the output staging of j-1 is full
+        if (j + 1 < nch) prefetch_chunk(rec_of(j + 1), nxt, half, wave, lane);
+        if (j > 0) store_out(j - 1);
+        load_z(j);
+        lds_barrier();  // the staging area has been read
 
         bf16x8 Sb[4];
 #pragma unroll
@@ -542,8 +618,8 @@ __global__ __launch_bounds__(64) void mfma_state_kernel(MfmaK<GT> a) {
         f32x4 U[4];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
-            const uint2 up = *reinterpret_cast<const uint2*>(buf + B_UT + (mt * 64 + lane) * 8);
-            const uint2 op = *reinterpret_cast<const uint2*>(buf + B_OI + (mt * 64 + lane) * 8);
+            const uint2 up = *reinterpret_cast<const uint2*>(cur + B_UT + ((wave * 4 + mt) * 64 + lane) * 8);
+            const uint2 op = *reinterpret_cast<const uint2*>(cur + B_OI + ((wave * 4 + mt) * 64 + lane) * 8);
             f32x4 u = {__uint_as_float(up.x << 16), __uint_as_float(up.x & 0xffff0000u),
                        __uint_as_float(up.y << 16), __uint_as_float(up.y & 0xffff0000u)};
             f32x4 o = {__uint_as_float(op.x << 16), __uint_as_float(op.x & 0xffff0000u),
@@ -551,21 +627,14 @@ __global__ __launch_bounds__(64) void mfma_state_kernel(MfmaK<GT> a) {
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 const int blk = (mt * 4 + ks) * 64 + lane;
-                const bf16x8 wa = *reinterpret_cast<const bf16x8*>(buf + B_NEGW + blk * 16);
-                const bf16x8 qa = *reinterpret_cast<const bf16x8*>(buf + B_QP + blk * 16);
+                const bf16x8 wa = *reinterpret_cast<const bf16x8*>(cur + B_NEGW + blk * 16);
+                const bf16x8 qa = *reinterpret_cast<const bf16x8*>(cur + B_QP + blk * 16);
                 u = mfma(wa, Sb[ks], u);
                 o = mfma(qa, Sb[ks], o);
             }
             U[mt] = u;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 16 * mt + 4 * g + i;
-                if (r < Lc) {
-                    float y = o[i];
-                    if (a.z != nullptr) y *= sigmoid(zc[mt * 4 + i]);
-                    a.out[((tc + r) * H + h) * 128 + col].bits = f32_to_bf16(y);
-                }
-            }
+            for (int i = 0; i < 4; ++i) stage[(16 * mt + 4 * g + i) * 64 + 16 * wave + c] = o[i];
         }
         // S <- Diag(gamma) S + K^T U
         bf16x8 Ub[2];
@@ -573,18 +642,27 @@ __global__ __launch_bounds__(64) void mfma_state_kernel(MfmaK<GT> a) {
         for (int ks = 0; ks < 2; ++ks) Ub[ks] = to_bf16x8(U[2 * ks], U[2 * ks + 1]);
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-            const float4 gm = *reinterpret_cast<const float4*>(buf + B_GAM + (16 * t + 4 * g) * 4);
+            const float4 gm = *reinterpret_cast<const float4*>(cur + B_GAM + (16 * t + 4 * g) * 4);
             S[t][0] *= gm.x;
             S[t][1] *= gm.y;
             S[t][2] *= gm.z;
             S[t][3] *= gm.w;
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                const bf16x8 ka = *reinterpret_cast<const bf16x8*>(buf + B_KHT + ((t * 2 + ks) * 64 + lane) * 16);
+                const bf16x8 ka = *reinterpret_cast<const bf16x8*>(cur + B_KHT + ((t * 2 + ks) * 64 + lane) * 16);
                 S[t] = mfma(ka, Ub[ks], S[t]);
             }
         }
-        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    if (nch > 0) prefetch_chunk(rec_of(0), buf0, half, wave, lane);
+    for (int j = 0; j < nch; j += 2) {
+        step(j, buf0, buf1);
+        if (j + 1 < nch) step(j + 1, buf1, buf0);
+    }
+    if (nch > 0) {
+        lds_barrier();
+        store_out(nch - 1);
     }
     if (a.S_out) {
 #pragma unroll
@@ -610,17 +688,23 @@ hipError_t launch_typed(const PrefillArgs& a, hipStream_t s, int32_t* base, char
                                            static_cast<int>(kIntraLds));
         if (e != hipSuccess) return e;
         LaunchTimer timer("mfma_intra", s);
-        hipLaunchKernelGGL((mfma_intra_kernel<GT>), dim3(static_cast<unsigned>(slots), a.H), dim3(256),
+        hipLaunchKernelGGL((mfma_intra_kernel<GT>), dim3(static_cast<unsigned>(slots), a.H), dim3(kIntraThreads),
                            kIntraLds, s, k);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&mfma_state_kernel<GT>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 2 * B_BYTES);
-    if (e != hipSuccess) return e;
-    const int64_t blocks = (k.groups + 7) / 8 * 64;
+    const void* fn = a.z ? reinterpret_cast<const void*>(&mfma_state_kernel<GT, true>)
+                         : reinterpret_cast<const void*>(&mfma_state_kernel<GT, false>);
+    (void)fn;
+    const int64_t blocks = (k.groups + 7) / 8 * 16;
     LaunchTimer timer("mfma_state", s);
-    hipLaunchKernelGGL((mfma_state_kernel<GT>), dim3(static_cast<unsigned>(blocks)), dim3(64), 2 * B_BYTES, s, k);
+    if (a.z) {
+        hipLaunchKernelGGL((mfma_state_kernel<GT, true>), dim3(static_cast<unsigned>(blocks)), dim3(kStateThreads),
+                           0, s, k);
+    } else {
+        hipLaunchKernelGGL((mfma_state_kernel<GT, false>), dim3(static_cast<unsigned>(blocks)), dim3(kStateThreads),
+                           0, s, k);
+    }
     return hipGetLastError();
 }
 

@@ -28,8 +28,42 @@ namespace {
 
 constexpr int kRun = 16;                 // tokens per 16-lane group
 constexpr int kTile = kRun * 4;          // tokens per workgroup (4 groups per wave)
-constexpr int kBatch = 4;                // rows loaded ahead
 constexpr float kL2Eps = 1e-6f;
+
+// One lane's 8 channels of a row, as loaded (bf16: 16 B, fp32: 32 B).  Rows
+// are loaded a whole batch ahead of their use and unpacked when consumed.
+template <typename XT> struct Raw;
+template <> struct Raw<bf16> {
+    uint4 v;
+    static constexpr int kBatch = 16;  // the whole 16-token run in flight
+    __device__ __forceinline__ void load(const bf16* p) { v = *reinterpret_cast<const uint4*>(p); }
+    __device__ __forceinline__ void unpack(float (&x)[8], bool keep) const {
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[2 * i] = keep ? __uint_as_float(w[i] << 16) : 0.f;
+            x[2 * i + 1] = keep ? __uint_as_float(w[i] & 0xffff0000u) : 0.f;
+        }
+    }
+};
+template <> struct Raw<float> {
+    float4 a, b;
+    static constexpr int kBatch = 8;
+    __device__ __forceinline__ void load(const float* p) {
+        a = reinterpret_cast<const float4*>(p)[0];
+        b = reinterpret_cast<const float4*>(p)[1];
+    }
+    __device__ __forceinline__ void unpack(float (&x)[8], bool keep) const {
+        const float y[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = keep ? y[i] : 0.f;
+    }
+};
+
+__device__ __forceinline__ float softplus_fast(float x) {
+    return fmaxf(x, 0.f) + __logf(1.f + __expf(-fabsf(x)));
+}
+__device__ __forceinline__ float sigmoid_fast(float x) { return 1.f / (1.f + __expf(-x)); }
 
 template <typename XT>
 struct PrepK {
@@ -42,23 +76,24 @@ struct PrepK {
     float *la_out, *beta_out;
 };
 
+// Loads are branch-free: an inactive lane or a row past the end reads a
+// valid clamped address and selects zero, so the compiler can keep several
+// rows in flight instead of waiting on each load inside a branch.
 template <typename XT>
-__device__ __forceinline__ void load_row(const XT* base, int64_t t, int64_t width, int64_t off,
-                                         bool active, float (&x)[8]) {
-    if (active) {
-        ld8(base + t * width + off, x);
-    } else {
+__device__ __forceinline__ void load_row(const XT* base, int64_t t, int64_t width, int64_t off, bool keep,
+                                         float (&x)[8]) {
+    ld8(base + t * width + off, x);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) x[i] = 0.f;
-    }
+    for (int i = 0; i < 8; ++i) x[i] = keep ? x[i] : 0.f;
 }
 
-// history row of position tau (< 0) of sequence n: conv state or zero
-__device__ __forceinline__ void load_hist(const float* cs, int n, int tau, int64_t cs_width,
-                                          int64_t off, bool active, float (&x)[8]) {
-    if (active && cs != nullptr) {
-        const float* p = cs + (static_cast<int64_t>(n) * 3 + (3 + tau)) * cs_width + off;
-        ld8(p, x);
+// history row of position tau (-3..-1) of sequence n: conv state or zero
+__device__ __forceinline__ void load_hist(const float* cs, int n, int tau, int64_t cs_width, int64_t off,
+                                          bool keep, float (&x)[8]) {
+    if (cs != nullptr) {  // uniform over the whole launch
+        ld8(cs + (static_cast<int64_t>(n) * 3 + (3 + tau)) * cs_width + off, x);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = keep ? x[i] : 0.f;
     } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i) x[i] = 0.f;
@@ -71,10 +106,16 @@ __device__ __forceinline__ void conv_run(const PrepK<XT>& a, const XT* src, cons
                                          int64_t width, int64_t off, int64_t cs_off, bool act, bool norm,
                                          int64_t t_begin, int64_t t_end) {
     float w[8][4];
+    {
+        float wl[32];
+        ld8(wts + off * 4, *reinterpret_cast<float(*)[8]>(&wl[0]));
+        ld8(wts + off * 4 + 8, *reinterpret_cast<float(*)[8]>(&wl[8]));
+        ld8(wts + off * 4 + 16, *reinterpret_cast<float(*)[8]>(&wl[16]));
+        ld8(wts + off * 4 + 24, *reinterpret_cast<float(*)[8]>(&wl[24]));
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
+        for (int c = 0; c < 8; ++c)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) w[c][j] = act ? ld(wts + (off + c) * 4 + j) : 0.f;
+            for (int j = 0; j < 4; ++j) w[c][j] = act ? wl[c * 4 + j] : 0.f;
     }
     const int64_t cs_width = static_cast<int64_t>(a.H) * (2 * a.dk + a.dv);
     int n = a.cu ? find_seq(a.cu, a.N, t_begin) : 0;
@@ -84,17 +125,28 @@ __device__ __forceinline__ void conv_run(const PrepK<XT>& a, const XT* src, cons
 #pragma unroll
     for (int m = 0; m < 3; ++m) {
         const int64_t pos = t_begin - 3 + m;
-        if (pos >= seq_start) load_row(src, pos, width, off, act, hst[m]);
-        else load_hist(a.cs, n, static_cast<int>(pos - seq_start), cs_width, cs_off + off, act, hst[m]);
-    }
-    for (int64_t t0 = t_begin; t0 < t_end; t0 += kBatch) {
-        float x[kBatch][8];
+        const bool in_seq = pos >= seq_start;
+        float xi[8], xh[8];
+        load_row(src, pos < 0 ? 0 : pos, width, off, act && in_seq, xi);
+        const int tau = in_seq ? -1 : static_cast<int>(pos - seq_start);
+        load_hist(a.cs, n, tau, cs_width, cs_off + off, act && !in_seq, xh);
 #pragma unroll
-        for (int r = 0; r < kBatch; ++r) load_row(src, t0 + r, width, off, act && (t0 + r < t_end), x[r]);
+        for (int i = 0; i < 8; ++i) hst[m][i] = xi[i] + xh[i];  // one of the two is zero
+    }
+    constexpr int kBatch = Raw<XT>::kBatch;
+    for (int64_t t0 = t_begin; t0 < t_end; t0 += kBatch) {
+        Raw<XT> raw[kBatch];
+#pragma unroll
+        for (int r = 0; r < kBatch; ++r) {
+            const int64_t t = t0 + r < t_end ? t0 + r : t_end - 1;
+            raw[r].load(src + t * width + off);
+        }
 #pragma unroll
         for (int r = 0; r < kBatch; ++r) {
             const int64_t t = t0 + r;
             if (t >= t_end) break;
+            float xr[8];
+            raw[r].unpack(xr, act);
             if (t >= seq_end) {
                 // entering a later sequence: skip empty ones, restart the history
                 do {
@@ -109,11 +161,11 @@ __device__ __forceinline__ void conv_run(const PrepK<XT>& a, const XT* src, cons
             float ss = 0.f;
 #pragma unroll
             for (int c = 0; c < 8; ++c) {
-                y[c] = w[c][0] * hst[0][c] + w[c][1] * hst[1][c] + w[c][2] * hst[2][c] + w[c][3] * x[r][c];
+                y[c] = w[c][0] * hst[0][c] + w[c][1] * hst[1][c] + w[c][2] * hst[2][c] + w[c][3] * xr[c];
                 ss += y[c] * y[c];
                 hst[0][c] = hst[1][c];
                 hst[1][c] = hst[2][c];
-                hst[2][c] = x[r][c];
+                hst[2][c] = xr[c];
             }
             if (norm) {
 #pragma unroll
@@ -142,9 +194,10 @@ __global__ __launch_bounds__(256) void preprocess_kernel(PrepK<XT> a) {
     if (t_begin >= a.T) return;  // whole 16-lane group leaves together
     const int64_t t_end = min(t_begin + kRun, a.T);
     const int64_t wk = static_cast<int64_t>(a.H) * a.dk, wv = static_cast<int64_t>(a.H) * a.dv;
-    const int64_t off_k = static_cast<int64_t>(h) * a.dk + 8 * li;
-    const int64_t off_v = static_cast<int64_t>(h) * a.dv + 8 * li;
     const bool aq = 8 * li < a.dk, av = 8 * li < a.dv;
+    // lanes past the head size keep a valid (clamped) column and store nothing
+    const int64_t off_k = static_cast<int64_t>(h) * a.dk + (aq ? 8 * li : 0);
+    const int64_t off_v = static_cast<int64_t>(h) * a.dv + (av ? 8 * li : 0);
     if (wave < 3) {
         const bool is_v = wave == 2;
         const XT* src = wave == 0 ? a.q_in : (wave == 1 ? a.k_in : a.v_in);
@@ -153,24 +206,26 @@ __global__ __launch_bounds__(256) void preprocess_kernel(PrepK<XT> a) {
         conv_run(a, src, wts, dst, is_v ? wv : wk, is_v ? off_v : off_k, wave * wk, is_v ? av : aq, !is_v,
                  t_begin, t_end);
     } else {
+        constexpr int kBatch = Raw<XT>::kBatch;
         for (int64_t t0 = t_begin; t0 < t_end; t0 += kBatch) {
-            float x[kBatch][8];
+            Raw<XT> raw[kBatch];
             float xb[kBatch];
 #pragma unroll
             for (int r = 0; r < kBatch; ++r) {
-                const bool in = t0 + r < t_end;
-                load_row(a.g, t0 + r, wk, off_k, in && aq, x[r]);
-                xb[r] = (in && li == 0) ? ld(a.b + (t0 + r) * a.H + h) : 0.f;
+                const int64_t t = t0 + r < t_end ? t0 + r : t_end - 1;
+                raw[r].load(a.g + t * wk + off_k);
+                xb[r] = ld(a.b + t * a.H + h);
             }
 #pragma unroll
             for (int r = 0; r < kBatch; ++r) {
                 const int64_t t = t0 + r;
                 if (t >= t_end) break;
-                float la[8];
+                float x[8], la[8];
+                raw[r].unpack(x, aq);
 #pragma unroll
-                for (int c = 0; c < 8; ++c) la[c] = -softplus(x[r][c]);
+                for (int c = 0; c < 8; ++c) la[c] = -softplus_fast(x[c]);
                 if (aq) st8(a.la_out + t * wk + off_k, la);
-                if (li == 0) a.beta_out[t * a.H + h] = sigmoid(xb[r]);
+                if (li == 0) a.beta_out[t * a.H + h] = sigmoid_fast(xb[r]);
             }
         }
     }
