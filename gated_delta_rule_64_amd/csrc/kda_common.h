@@ -15,12 +15,10 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
     return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// fp32 -> bf16, round to nearest, ties to even; NaN stays NaN.
+// fp32 -> bf16, round to nearest, ties to even (the gfx950 conversion
+// instruction; NaN stays NaN)
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return static_cast<uint16_t>(u >> 16);
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
 // scalar load/store of an element type as fp32
@@ -49,8 +47,11 @@ __device__ __forceinline__ void st8(float* p, const float (&x)[8]) {
     reinterpret_cast<float4*>(p)[0] = make_float4(x[0], x[1], x[2], x[3]);
     reinterpret_cast<float4*>(p)[1] = make_float4(x[4], x[5], x[6], x[7]);
 }
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+// two fp32 -> one word of two bf16 (lo in the low half), one packed conversion
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+    const bf16x2_t v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+    return __builtin_bit_cast(uint32_t, v);
 }
 __device__ __forceinline__ void st8(bf16* p, const float (&x)[8]) {
     uint4 a;
@@ -88,6 +89,8 @@ __device__ __forceinline__ float softplus(float x) {
     return x > 0.f ? x + log1pf(expf(-x)) : log1pf(expf(x));
 }
 __device__ __forceinline__ float sigmoid(float x) { return 1.f / (1.f + expf(-x)); }
+// sigmoid with the hardware exponential and reciprocal (about 2 ulp)
+__device__ __forceinline__ float sigmoid_fast(float x) { return __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
 
 // index of the sequence holding token t: the largest n with cu[n] <= t
 // (empty sequences never hold a token, so ties resolve to the non-empty one)

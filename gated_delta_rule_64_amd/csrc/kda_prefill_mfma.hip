@@ -43,7 +43,7 @@ constexpr int R_NEGW = 0;       // -W, A-operand layout, [4 m][4 k][64 lanes][8]
 constexpr int R_QP = 16384;     // Q', same layout
 constexpr int R_KHT = 32768;    // K^T (dk rows x 64 tokens), [8 m][2 k][64 lanes][8]
 constexpr int R_UT = 49152;     // U~, result layout per 16-column slice, [8 s][4 m][64 lanes][4]
-constexpr int R_OI = 65536;     // M U~, same layout
+constexpr int R_OI = 65536;     // M U~, transposed result layout: lane (g, c) holds [16m + c][16s + 4g + i]
 constexpr int R_GAM = 81920;    // gamma, fp32 [128]
 constexpr int REC_BYTES = 82432;
 
@@ -426,7 +426,9 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
             for (int ks = 0; ks < 2; ++ks) {
                 if (32 * ks > 16 * mt + 15) continue;  // M is lower triangular
                 qp = mfma(Mneg[mt][ks], Bw[ks], qp);
-                oi = mfma(Mpos[mt][ks], Bu[ks], oi);
+                // (M U~)^T = U~^T M^T: the operands swap roles, so lane (g, c)
+                // ends up with M U~[16mt + c][16nt + 4g + i]
+                oi = mfma(Bu[ks], Mpos[mt][ks], oi);
             }
             uint2 p;
             p.x = pack_bf16x2(oi[0], oi[1]);
@@ -484,20 +486,23 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
 // phase 2
 // ---------------------------------------------------------------------------
 
-// One workgroup (4 waves) per (sequence, head, half of the state columns);
-// wave w owns the 16 columns of slice 4*half + w.  The chunk's shared factors
-// (-W, Q', K^T: 48 KB) are copied into LDS once per workgroup, one chunk
-// ahead, with global_load_lds_dwordx4; the output tile of the chunk (64 tokens
-// x 64 columns) is staged in LDS and written with the output gate applied as
-// whole 128-byte row segments, one chunk behind.
-constexpr int kStateThreads = 256;
+// One workgroup per (sequence, head, half of the state columns), with two
+// roles.  Four compute waves (wave w owns the 16 columns of slice
+// 4*half + w) issue only loads: the chunk's shared factors (-W, Q', K^T,
+// gamma: 48.5 KB) go into one of three LDS buffers with
+// global_load_lds_dwordx4, two chunks ahead, and the wave's own U~, M U~ and
+// gate logits into registers, also two chunks ahead.  Because no store is in
+// flight on these waves, their memory counter retires in issue order and one
+// counted wait (vmcnt) per chunk confirms the copies two chunks back while
+// the later ones stay in flight.  Four output waves only read the gated
+// output tile from LDS and store it as whole 128-byte row segments, so the
+// compute waves never wait for stores to be acknowledged.
+constexpr int kStateThreads = 512;
 constexpr int B_NEGW = 0;
 constexpr int B_QP = 16384;
 constexpr int B_KHT = 32768;
-constexpr int B_UT = 49152;   // 8 KB: U~ of the 4 slices of this half
-constexpr int B_OI = 57344;   // 8 KB: M U~ of the 4 slices
-constexpr int B_GAM = 65536;  // 512 B
-constexpr int B_BYTES = 66048;
+constexpr int B_GAM = 49152;  // 512 B
+constexpr int B_BYTES = 49664;
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -505,30 +510,39 @@ __device__ __forceinline__ void lds_copy16(const char* gsrc, char* lds_dst) {
     __builtin_amdgcn_global_load_lds(static_cast<const void*>(gsrc), (lds_void*)(lds_dst), 16, 0, 0);
 }
 
-// asynchronous copy of one chunk record (this half's slices) into `buf`;
-// the 64.5 one-KB pieces are split over the four waves
-__device__ __forceinline__ void prefetch_chunk(const char* r, char* buf, int half, int wave, int lane) {
+// asynchronous copy of a chunk's shared factors into `buf`: 48 one-KB pieces
+// split over the four compute waves, plus gamma from wave 0 (12 or 13 copies
+// per wave)
+__device__ __forceinline__ void prefetch_chunk(const char* r, char* buf, int wave, int lane) {
 #pragma unroll
     for (int i = 0; i < 12; ++i) {
-        const int b = wave + 4 * i;  // 0..47: -W, Q', K^T
+        const int b = wave + 4 * i;
         lds_copy16(r + b * 1024 + lane * 16, buf + b * 1024);
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int b = wave + 4 * i;  // 0..7
-        lds_copy16(r + R_UT + half * 8192 + b * 1024 + lane * 16, buf + B_UT + b * 1024);
-        lds_copy16(r + R_OI + half * 8192 + b * 1024 + lane * 16, buf + B_OI + b * 1024);
     }
     if (wave == 0 && lane < 32) lds_copy16(r + R_GAM + lane * 16, buf + B_GAM);
 }
 
+// s_waitcnt with vmcnt(n) only (lgkmcnt and expcnt left at their maxima)
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(n >= 0 && n < 64, "vmcnt is 6 bits");
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | 0x70 | 0xF00);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// per-chunk registers of one compute wave, kept as loaded (bf16 bits) until use
+struct ChunkRegs {
+    uint2 ut[4], oi[4];  // U~ (result layout) and M U~ (transposed result layout)
+    uint2 z[4];          // gate logits at the wave's output positions
+};
+
 template <typename GT, bool kGate>
 __global__ __launch_bounds__(kStateThreads) void mfma_state_kernel(MfmaK<GT> a) {
-    // two chunk buffers and the output staging as separate LDS objects, so the
-    // compiler can tell copies into one buffer from reads of the other
     __shared__ __align__(16) char buf0[B_BYTES];
     __shared__ __align__(16) char buf1[B_BYTES];
-    __shared__ __align__(16) float stage[64 * 64];  // [64 tokens][64 columns]
+    __shared__ __align__(16) char buf2[B_BYTES];
+    __shared__ __align__(16) uint16_t stage[64 * 64];  // gated output, bf16 [64 tokens][64 columns]
     // blockIdx -> (sequence, head, half): both halves of a (sequence, head)
     // land on one XCD (workgroups are dealt round-robin over the 8 XCDs), so
     // the chunk records they share are read through one L2
@@ -539,12 +553,52 @@ __global__ __launch_bounds__(kStateThreads) void mfma_state_kernel(MfmaK<GT> a) 
     const int H = a.H;
     const int n = static_cast<int>(grp / H), h = static_cast<int>(grp % H);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, c = lane & 15;
+
+    const int64_t sb = seq_begin(a.cu, n), se = seq_finish(a.cu, n, a.T);
+    const int slot0 = a.base[n];
+    const int nch = a.base[n + 1] - slot0;
+    auto rec_of = [&](int j) { return a.rec + (static_cast<int64_t>(slot0 + j) * H + h) * REC_BYTES; };
+    auto chunk_len = [&](int j) {
+        return static_cast<int>(min(static_cast<int64_t>(kChunk), se - (sb + static_cast<int64_t>(j) * kChunk)));
+    };
+
+    if (wave >= 4) {
+        // ---- output waves: store the gated tile of every chunk
+        const int t2 = tid - 256;
+        const int orow = t2 >> 2, oq = t2 & 3;  // row, 16-column quarter
+        for (int j = 0; j < nch; ++j) {
+            lds_barrier();  // A: the compute waves may overwrite the staging of j-1
+            lds_barrier();  // B: the staging holds chunk j
+            const int Lc = chunk_len(j);
+            if (orow < Lc) {
+                const int64_t t = sb + static_cast<int64_t>(j) * kChunk + orow;
+                const uint4* src = reinterpret_cast<const uint4*>(stage + orow * 64 + 16 * oq);
+                uint4* dst = reinterpret_cast<uint4*>(a.out + (t * H + h) * 128 + 64 * half + 16 * oq);
+                const uint4 v0 = src[0], v1 = src[1];
+                dst[0] = v0;
+                dst[1] = v1;
+            }
+        }
+        return;
+    }
+
+    // ---- compute waves
     const int sl = 4 * half + wave;
     const int col = 16 * sl + c;
-
-    // state S[16t + 4g + i][col] in registers
-    f32x4 S[8];
+    f32x4 S[8];  // S[16t + 4g + i][col]
     const int64_t sidx = grp * (128 * 128);
+    if (nch == 0) {  // empty sequence: the state passes through
+        if (a.S_out) {
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int64_t e = sidx + (16 * t + 4 * g + i) * 128 + col;
+                    a.S_out[e] = a.S0 ? a.S0[e] : 0.f;
+                }
+        }
+        return;
+    }
     if (a.S0 != nullptr) {  // one uniform branch: all 32 loads in flight together
 #pragma unroll
         for (int t = 0; t < 8; ++t)
@@ -555,71 +609,54 @@ __global__ __launch_bounds__(kStateThreads) void mfma_state_kernel(MfmaK<GT> a) 
         for (int t = 0; t < 8; ++t) S[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    const int64_t sb = seq_begin(a.cu, n), se = seq_finish(a.cu, n, a.T);
-    const int slot0 = a.base[n];
-    const int nch = a.base[n + 1] - slot0;
-    auto rec_of = [&](int j) { return a.rec + (static_cast<int64_t>(slot0 + j) * H + h) * REC_BYTES; };
-    auto chunk_len = [&](int j) {
-        return static_cast<int>(min(static_cast<int64_t>(kChunk), se - (sb + static_cast<int64_t>(j) * kChunk)));
-    };
-
-    // cooperative output: thread -> token row orow, 16 columns starting at ocol
-    const int orow = tid >> 2, ocol = 16 * (tid & 3);
-    uint4 zraw[2];  // gate logits of the chunk whose output is written next
-    auto load_z = [&](int j) {
-        if (!kGate) return;
-        const int Lc = chunk_len(j);
-        const int64_t t = sb + static_cast<int64_t>(j) * kChunk + (orow < Lc ? orow : Lc - 1);
-        const bf16* zp = a.z + (t * H + h) * 128 + 64 * half + ocol;
-        zraw[0] = reinterpret_cast<const uint4*>(zp)[0];
-        zraw[1] = reinterpret_cast<const uint4*>(zp)[1];
-    };
-    auto store_out = [&](int j) {
-        const int Lc = chunk_len(j);
-        if (orow >= Lc) return;
-        const int64_t t = sb + static_cast<int64_t>(j) * kChunk + orow;
-        float y[16];
+    // issue every load of chunk j: the wave's registers first, then the
+    // shared factors into `buf` (so a wait for the copies covers both)
+    auto issue = [&](int j, char* buf, ChunkRegs& cr) {
+        const char* rp = rec_of(j);
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-            const float4 v4 = *reinterpret_cast<const float4*>(stage + orow * 64 + ocol + 4 * q4);
-            y[4 * q4] = v4.x; y[4 * q4 + 1] = v4.y; y[4 * q4 + 2] = v4.z; y[4 * q4 + 3] = v4.w;
+        for (int mt = 0; mt < 4; ++mt) {
+            cr.ut[mt] = *reinterpret_cast<const uint2*>(rp + R_UT + ((sl * 4 + mt) * 64 + lane) * 8);
+            cr.oi[mt] = *reinterpret_cast<const uint2*>(rp + R_OI + ((sl * 4 + mt) * 64 + lane) * 8);
         }
         if (kGate) {
-            float zf[16];
-            unpack8(zraw[0], *reinterpret_cast<float(*)[8]>(&zf[0]));
-            unpack8(zraw[1], *reinterpret_cast<float(*)[8]>(&zf[8]));
+            // the output is computed transposed: lane (g, c) holds token 16mt + c,
+            // columns 16sl + 4g .. +3, so its gate logits are one 8-byte load
+            const int Lc = chunk_len(j);
+            const int64_t tb = sb + static_cast<int64_t>(j) * kChunk;
 #pragma unroll
-            for (int e = 0; e < 16; ++e) y[e] *= 1.f / (1.f + __expf(-zf[e]));
+            for (int mt = 0; mt < 4; ++mt) {
+                const int r = 16 * mt + c;
+                cr.z[mt] = *reinterpret_cast<const uint2*>(a.z + ((tb + (r < Lc ? r : Lc - 1)) * H + h) * 128 +
+                                                          16 * sl + 4 * g);
+            }
         }
-        uint4 o0, o1;
-        o0.x = pack_bf16x2(y[0], y[1]); o0.y = pack_bf16x2(y[2], y[3]);
-        o0.z = pack_bf16x2(y[4], y[5]); o0.w = pack_bf16x2(y[6], y[7]);
-        o1.x = pack_bf16x2(y[8], y[9]); o1.y = pack_bf16x2(y[10], y[11]);
-        o1.z = pack_bf16x2(y[12], y[13]); o1.w = pack_bf16x2(y[14], y[15]);
-        bf16* op = a.out + (t * H + h) * 128 + 64 * half + ocol;
-        reinterpret_cast<uint4*>(op)[0] = o0;
-        reinterpret_cast<uint4*>(op)[1] = o1;
+        prefetch_chunk(rp, buf, wave, lane);
     };
+    // memory operations one issue() puts in flight on this wave
+    constexpr int kRegLoads = 8 + (kGate ? 4 : 0);
 
-    // one chunk: its factors are in `cur`; the next chunk's go to `nxt`
-    auto step = [&](int j, const char* cur, char* nxt) {
-        wait_vmem();    // this wave's copies of chunk j (and its older stores) are done
-        lds_barrier();  // ... and every other wave's; the output staging of j-1 is full
-        if (j + 1 < nch) prefetch_chunk(rec_of(j + 1), nxt, half, wave, lane);
-        if (j > 0) store_out(j - 1);
-        load_z(j);
-        lds_barrier();  // the staging area has been read
+    // one chunk: factors in `cur` and `cr`; chunk j+2 is issued into `nxt`, `nr`.
+    // Every step issues exactly once (past the last chunk it issues the last
+    // chunk again, into buffers nobody reads), so the number of operations in
+    // flight behind chunk j's loads is the same at every step: all of one issue
+    auto step = [&](int j, const char* cur, char* nxt, const ChunkRegs& cr, ChunkRegs& nr) {
+        // chunk j's loads are done once at most the operations issued after
+        // them are in flight (loads retire in issue order); wave 0's gamma
+        // copy is left out of the count, so it waits for one more than needed
+        wait_vmcnt<kRegLoads + 12>();
+        lds_barrier();  // A: every wave's copies of chunk j are in LDS
+        issue(min(j + 2, nch - 1), nxt, nr);
 
         bf16x8 Sb[4];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) Sb[ks] = to_bf16x8(S[2 * ks], S[2 * ks + 1]);
-
-        // U = U~ - W S  and  O = M U~ + Q' S
+        // U = U~ - W S, and the output transposed: O^T = (M U~)^T + S^T Q'^T
+        // (the state operand and the Q' operand swap roles); the gated output
+        // goes to the staging tile
         f32x4 U[4];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
-            const uint2 up = *reinterpret_cast<const uint2*>(cur + B_UT + ((wave * 4 + mt) * 64 + lane) * 8);
-            const uint2 op = *reinterpret_cast<const uint2*>(cur + B_OI + ((wave * 4 + mt) * 64 + lane) * 8);
+            const uint2 up = cr.ut[mt], op = cr.oi[mt];
             f32x4 u = {__uint_as_float(up.x << 16), __uint_as_float(up.x & 0xffff0000u),
                        __uint_as_float(up.y << 16), __uint_as_float(up.y & 0xffff0000u)};
             f32x4 o = {__uint_as_float(op.x << 16), __uint_as_float(op.x & 0xffff0000u),
@@ -630,12 +667,20 @@ __global__ __launch_bounds__(kStateThreads) void mfma_state_kernel(MfmaK<GT> a) 
                 const bf16x8 wa = *reinterpret_cast<const bf16x8*>(cur + B_NEGW + blk * 16);
                 const bf16x8 qa = *reinterpret_cast<const bf16x8*>(cur + B_QP + blk * 16);
                 u = mfma(wa, Sb[ks], u);
-                o = mfma(qa, Sb[ks], o);
+                o = mfma(Sb[ks], qa, o);
             }
             U[mt] = u;
+            if (kGate) {
+                const uint2 zp = cr.z[mt];
+                const float zf[4] = {__uint_as_float(zp.x << 16), __uint_as_float(zp.x & 0xffff0000u),
+                                     __uint_as_float(zp.y << 16), __uint_as_float(zp.y & 0xffff0000u)};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) stage[(16 * mt + 4 * g + i) * 64 + 16 * wave + c] = o[i];
+                for (int i = 0; i < 4; ++i) o[i] *= sigmoid_fast(zf[i]);
+            }
+            *reinterpret_cast<uint2*>(stage + (16 * mt + c) * 64 + 16 * wave + 4 * g) =
+                make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
         }
+        lds_barrier();  // B: the staging tile is complete
         // S <- Diag(gamma) S + K^T U
         bf16x8 Ub[2];
 #pragma unroll
@@ -655,15 +700,24 @@ __global__ __launch_bounds__(kStateThreads) void mfma_state_kernel(MfmaK<GT> a) 
         }
     };
 
-    if (nch > 0) prefetch_chunk(rec_of(0), buf0, half, wave, lane);
-    for (int j = 0; j < nch; j += 2) {
-        step(j, buf0, buf1);
-        if (j + 1 < nch) step(j + 1, buf1, buf0);
+    ChunkRegs r0, r1, r2;
+    issue(0, buf0, r0);
+    issue(min(1, nch - 1), buf1, r1);
+    // the initial state has arrived once at most the two issues above are in
+    // flight; settling it here keeps the loop free of waits for it
+    wait_vmcnt<2 * (kRegLoads + 12)>();
+    // whole rounds of three, then the last one or two chunks: inside the loop
+    // every path issues the same operations, so the compiler's own waits agree
+    // with the counted ones above
+    int j = 0;
+    for (; j + 3 <= nch; j += 3) {
+        step(j, buf0, buf2, r0, r2);
+        step(j + 1, buf1, buf0, r1, r0);
+        step(j + 2, buf2, buf1, r2, r1);
     }
-    if (nch > 0) {
-        lds_barrier();
-        store_out(nch - 1);
-    }
+    if (j < nch) step(j, buf0, buf2, r0, r2);
+    if (j + 1 < nch) step(j + 1, buf1, buf0, r1, r0);
+    wait_vmcnt<0>();  // the copies issued past the last chunk land before the workgroup ends
     if (a.S_out) {
 #pragma unroll
         for (int t = 0; t < 8; ++t)

@@ -63,7 +63,6 @@ template <> struct Raw<float> {
 __device__ __forceinline__ float softplus_fast(float x) {
     return fmaxf(x, 0.f) + __logf(1.f + __expf(-fabsf(x)));
 }
-__device__ __forceinline__ float sigmoid_fast(float x) { return 1.f / (1.f + __expf(-x)); }
 
 template <typename XT>
 struct PrepK {
