@@ -89,6 +89,7 @@ struct MfmaK {
     float* S_out;
     bf16* out;
     char* rec;
+    int64_t slots;   // chunk slots per head in the record array
     int64_t groups;  // N * H
 };
 
@@ -144,7 +145,7 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
     const int L = static_cast<int>(min(static_cast<int64_t>(kChunk), seq_finish(a.cu, n, a.T) - t0));
     const int H = a.H;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, c = lane & 15;
-    char* rec = a.rec + (static_cast<int64_t>(slot) * H + h) * REC_BYTES;
+    char* rec = a.rec + (h * a.slots + slot) * REC_BYTES;  // a head's chunks are contiguous
 
     // ---- inputs to LDS.  Loads are branch-free (rows past L read row L-1 and
     // are replaced by zero) so that all of them are in flight together.
@@ -487,62 +488,47 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
 // ---------------------------------------------------------------------------
 
 // One workgroup per (sequence, head, half of the state columns), with two
-// roles.  Four compute waves (wave w owns the 16 columns of slice
-// 4*half + w) issue only loads: the chunk's shared factors (-W, Q', K^T,
-// gamma: 48.5 KB) go into one of three LDS buffers with
-// global_load_lds_dwordx4, two chunks ahead, and the wave's own U~, M U~ and
-// gate logits into registers, also two chunks ahead.  Because no store is in
-// flight on these waves, their memory counter retires in issue order and one
-// counted wait (vmcnt) per chunk confirms the copies two chunks back while
-// the later ones stay in flight.  Four output waves only read the gated
-// output tile from LDS and store it as whole 128-byte row segments, so the
-// compute waves never wait for stores to be acknowledged.
+// roles.  Four memory waves only copy: everything one chunk needs (the shared
+// factors -W, Q', K^T and gamma, this half's U~ and M U~ tiles, and the gate
+// logits of its 64 output columns: 72.5 KB) goes into one of two LDS buffers
+// with global_load_lds_dwordx4, one chunk ahead of the compute.  Since these
+// waves only load, one vmcnt(0) per chunk confirms their copies.  Four
+// compute waves (wave w owns the 16 state columns of slice 4*half + w) read
+// only LDS and write the gated output straight to HBM; they never wait for
+// global memory, so store acknowledgements cost them nothing.
 constexpr int kStateThreads = 512;
-constexpr int B_NEGW = 0;
-constexpr int B_QP = 16384;
-constexpr int B_KHT = 32768;
-constexpr int B_GAM = 49152;  // 512 B
-constexpr int B_BYTES = 49664;
+// LDS buffer layout, bytes
+constexpr int B_NEGW = 0;       // -W, 16 KB
+constexpr int B_QP = 16384;     // Q', 16 KB
+constexpr int B_KHT = 32768;    // K^T, 16 KB
+constexpr int B_UT = 49152;     // U~ of the half's four slices, [4 s][4 m][64 lanes][4], 8 KB
+constexpr int B_OI = 57344;     // M U~ of the half's four slices, same layout, 8 KB
+constexpr int B_Z = 65536;      // gate logits, [64 tokens][64 columns] bf16, 16-byte pieces swizzled
+constexpr int B_GAM = 73728;    // gamma, fp32 [128]
+constexpr int B_BYTES = 74240;
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-__device__ __forceinline__ void lds_copy16(const char* gsrc, char* lds_dst) {
-    __builtin_amdgcn_global_load_lds(static_cast<const void*>(gsrc), (lds_void*)(lds_dst), 16, 0, 0);
+__device__ __forceinline__ void lds_copy16(const void* gsrc, char* lds_dst) {
+    __builtin_amdgcn_global_load_lds(gsrc, (lds_void*)(lds_dst), 16, 0, 0);
 }
 
-// asynchronous copy of a chunk's shared factors into `buf`: 48 one-KB pieces
-// split over the four compute waves, plus gamma from wave 0 (12 or 13 copies
-// per wave)
-__device__ __forceinline__ void prefetch_chunk(const char* r, char* buf, int wave, int lane) {
-#pragma unroll
-    for (int i = 0; i < 12; ++i) {
-        const int b = wave + 4 * i;
-        lds_copy16(r + b * 1024 + lane * 16, buf + b * 1024);
-    }
-    if (wave == 0 && lane < 32) lds_copy16(r + R_GAM + lane * 16, buf + B_GAM);
-}
+// The gate tile: token row r's 128 bytes hold 8 pieces of 16 bytes; piece q
+// of the row is kept at slot q ^ (r & 7), so the compute waves' reads (16
+// rows, one column group) spread over all banks.
+__device__ __forceinline__ int z_slot(int r, int q) { return q ^ (r & 7); }
 
-// s_waitcnt with vmcnt(n) only (lgkmcnt and expcnt left at their maxima)
-template <int n>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(n >= 0 && n < 64, "vmcnt is 6 bits");
+// s_waitcnt with vmcnt(0) only (lgkmcnt and expcnt left at their maxima)
+__device__ __forceinline__ void wait_vmcnt0() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | 0x70 | 0xF00);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
-
-// per-chunk registers of one compute wave, kept as loaded (bf16 bits) until use
-struct ChunkRegs {
-    uint2 ut[4], oi[4];  // U~ (result layout) and M U~ (transposed result layout)
-    uint2 z[4];          // gate logits at the wave's output positions
-};
 
 template <typename GT, bool kGate>
 __global__ __launch_bounds__(kStateThreads) void mfma_state_kernel(MfmaK<GT> a) {
     __shared__ __align__(16) char buf0[B_BYTES];
     __shared__ __align__(16) char buf1[B_BYTES];
-    __shared__ __align__(16) char buf2[B_BYTES];
-    __shared__ __align__(16) uint16_t stage[64 * 64];  // gated output, bf16 [64 tokens][64 columns]
     // blockIdx -> (sequence, head, half): both halves of a (sequence, head)
     // land on one XCD (workgroups are dealt round-robin over the 8 XCDs), so
     // the chunk records they share are read through one L2
@@ -557,27 +543,46 @@ __global__ __launch_bounds__(kStateThreads) void mfma_state_kernel(MfmaK<GT> a) 
     const int64_t sb = seq_begin(a.cu, n), se = seq_finish(a.cu, n, a.T);
     const int slot0 = a.base[n];
     const int nch = a.base[n + 1] - slot0;
-    auto rec_of = [&](int j) { return a.rec + (static_cast<int64_t>(slot0 + j) * H + h) * REC_BYTES; };
+    auto rec_of = [&](int j) { return a.rec + (h * a.slots + slot0 + j) * REC_BYTES; };
     auto chunk_len = [&](int j) {
         return static_cast<int>(min(static_cast<int64_t>(kChunk), se - (sb + static_cast<int64_t>(j) * kChunk)));
     };
 
     if (wave >= 4) {
-        // ---- output waves: store the gated tile of every chunk
-        const int t2 = tid - 256;
-        const int orow = t2 >> 2, oq = t2 & 3;  // row, 16-column quarter
-        for (int j = 0; j < nch; ++j) {
-            lds_barrier();  // A: the compute waves may overwrite the staging of j-1
-            lds_barrier();  // B: the staging holds chunk j
-            const int Lc = chunk_len(j);
-            if (orow < Lc) {
-                const int64_t t = sb + static_cast<int64_t>(j) * kChunk + orow;
-                const uint4* src = reinterpret_cast<const uint4*>(stage + orow * 64 + 16 * oq);
-                uint4* dst = reinterpret_cast<uint4*>(a.out + (t * H + h) * 128 + 64 * half + 16 * oq);
-                const uint4 v0 = src[0], v1 = src[1];
-                dst[0] = v0;
-                dst[1] = v1;
+        // ---- memory waves
+        const int wm = wave - 4;
+        auto issue = [&](int j, char* buf) {
+            const char* rp = rec_of(j);
+#pragma unroll
+            for (int i = 0; i < 12; ++i) {
+                const int b = wm + 4 * i;
+                lds_copy16(rp + b * 1024 + lane * 16, buf + b * 1024);
             }
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int b = wm + 4 * i;
+                lds_copy16(rp + R_UT + half * 8192 + b * 1024 + lane * 16, buf + B_UT + b * 1024);
+                lds_copy16(rp + R_OI + half * 8192 + b * 1024 + lane * 16, buf + B_OI + b * 1024);
+            }
+            if (kGate) {
+                const int Lc = chunk_len(j);
+                const int64_t tb = sb + static_cast<int64_t>(j) * kChunk;
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const int b = wm + 4 * i;
+                    const int r = 8 * b + (lane >> 3), slot = lane & 7;
+                    const int q = z_slot(r, slot);  // the slot map is its own inverse
+                    const bf16* src = a.z + ((tb + min(r, Lc - 1)) * H + h) * 128 + 64 * half + 8 * q;
+                    lds_copy16(src, buf + B_Z + b * 1024);
+                }
+            }
+            if (wm == 0 && lane < 32) lds_copy16(rp + R_GAM + lane * 16, buf + B_GAM);
+        };
+        if (nch > 0) issue(0, buf0);
+        for (int j = 0; j < nch; ++j) {
+            wait_vmcnt0();
+            lds_barrier();  // A: chunk j is in LDS; the other buffer is free
+            if (j + 1 < nch) issue(j + 1, (j & 1) ? buf0 : buf1);
         }
         return;
     }
@@ -587,18 +592,6 @@ __global__ __launch_bounds__(kStateThreads) void mfma_state_kernel(MfmaK<GT> a) 
     const int col = 16 * sl + c;
     f32x4 S[8];  // S[16t + 4g + i][col]
     const int64_t sidx = grp * (128 * 128);
-    if (nch == 0) {  // empty sequence: the state passes through
-        if (a.S_out) {
-#pragma unroll
-            for (int t = 0; t < 8; ++t)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int64_t e = sidx + (16 * t + 4 * g + i) * 128 + col;
-                    a.S_out[e] = a.S0 ? a.S0[e] : 0.f;
-                }
-        }
-        return;
-    }
     if (a.S0 != nullptr) {  // one uniform branch: all 32 loads in flight together
 #pragma unroll
         for (int t = 0; t < 8; ++t)
@@ -609,54 +602,23 @@ __global__ __launch_bounds__(kStateThreads) void mfma_state_kernel(MfmaK<GT> a) 
         for (int t = 0; t < 8; ++t) S[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    // issue every load of chunk j: the wave's registers first, then the
-    // shared factors into `buf` (so a wait for the copies covers both)
-    auto issue = [&](int j, char* buf, ChunkRegs& cr) {
-        const char* rp = rec_of(j);
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-            cr.ut[mt] = *reinterpret_cast<const uint2*>(rp + R_UT + ((sl * 4 + mt) * 64 + lane) * 8);
-            cr.oi[mt] = *reinterpret_cast<const uint2*>(rp + R_OI + ((sl * 4 + mt) * 64 + lane) * 8);
-        }
-        if (kGate) {
-            // the output is computed transposed: lane (g, c) holds token 16mt + c,
-            // columns 16sl + 4g .. +3, so its gate logits are one 8-byte load
-            const int Lc = chunk_len(j);
-            const int64_t tb = sb + static_cast<int64_t>(j) * kChunk;
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                const int r = 16 * mt + c;
-                cr.z[mt] = *reinterpret_cast<const uint2*>(a.z + ((tb + (r < Lc ? r : Lc - 1)) * H + h) * 128 +
-                                                          16 * sl + 4 * g);
-            }
-        }
-        prefetch_chunk(rp, buf, wave, lane);
-    };
-    // memory operations one issue() puts in flight on this wave
-    constexpr int kRegLoads = 8 + (kGate ? 4 : 0);
-
-    // one chunk: factors in `cur` and `cr`; chunk j+2 is issued into `nxt`, `nr`.
-    // Every step issues exactly once (past the last chunk it issues the last
-    // chunk again, into buffers nobody reads), so the number of operations in
-    // flight behind chunk j's loads is the same at every step: all of one issue
-    auto step = [&](int j, const char* cur, char* nxt, const ChunkRegs& cr, ChunkRegs& nr) {
-        // chunk j's loads are done once at most the operations issued after
-        // them are in flight (loads retire in issue order); wave 0's gamma
-        // copy is left out of the count, so it waits for one more than needed
-        wait_vmcnt<kRegLoads + 12>();
-        lds_barrier();  // A: every wave's copies of chunk j are in LDS
-        issue(min(j + 2, nch - 1), nxt, nr);
+    for (int j = 0; j < nch; ++j) {
+        const char* cur = (j & 1) ? buf1 : buf0;
+        lds_barrier();  // A: chunk j is in LDS
+        const int Lc = chunk_len(j);
+        const int64_t tb = sb + static_cast<int64_t>(j) * kChunk;
 
         bf16x8 Sb[4];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) Sb[ks] = to_bf16x8(S[2 * ks], S[2 * ks + 1]);
         // U = U~ - W S, and the output transposed: O^T = (M U~)^T + S^T Q'^T
-        // (the state operand and the Q' operand swap roles); the gated output
-        // goes to the staging tile
+        // (the state operand and the Q' operand swap roles): lane (g, c) holds
+        // token 16 mt + c, columns 16 sl + 4 g .. + 3
         f32x4 U[4];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
-            const uint2 up = cr.ut[mt], op = cr.oi[mt];
+            const uint2 up = *reinterpret_cast<const uint2*>(cur + B_UT + ((wave * 4 + mt) * 64 + lane) * 8);
+            const uint2 op = *reinterpret_cast<const uint2*>(cur + B_OI + ((wave * 4 + mt) * 64 + lane) * 8);
             f32x4 u = {__uint_as_float(up.x << 16), __uint_as_float(up.x & 0xffff0000u),
                        __uint_as_float(up.y << 16), __uint_as_float(up.y & 0xffff0000u)};
             f32x4 o = {__uint_as_float(op.x << 16), __uint_as_float(op.x & 0xffff0000u),
@@ -670,17 +632,20 @@ __global__ __launch_bounds__(kStateThreads) void mfma_state_kernel(MfmaK<GT> a) 
                 o = mfma(Sb[ks], qa, o);
             }
             U[mt] = u;
+            const int r = 16 * mt + c;
             if (kGate) {
-                const uint2 zp = cr.z[mt];
+                // columns 16 wave + 4 g .. + 3 of the half: piece 2 wave + g/2, bytes 8 (g & 1)
+                const uint2 zp = *reinterpret_cast<const uint2*>(cur + B_Z + r * 128 +
+                                                                 z_slot(r, 2 * wave + (g >> 1)) * 16 + 8 * (g & 1));
                 const float zf[4] = {__uint_as_float(zp.x << 16), __uint_as_float(zp.x & 0xffff0000u),
                                      __uint_as_float(zp.y << 16), __uint_as_float(zp.y & 0xffff0000u)};
 #pragma unroll
                 for (int i = 0; i < 4; ++i) o[i] *= sigmoid_fast(zf[i]);
             }
-            *reinterpret_cast<uint2*>(stage + (16 * mt + c) * 64 + 16 * wave + 4 * g) =
-                make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+            if (r < Lc)
+                *reinterpret_cast<uint2*>(a.out + ((tb + r) * H + h) * 128 + 16 * sl + 4 * g) =
+                    make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
         }
-        lds_barrier();  // B: the staging tile is complete
         // S <- Diag(gamma) S + K^T U
         bf16x8 Ub[2];
 #pragma unroll
@@ -698,26 +663,7 @@ __global__ __launch_bounds__(kStateThreads) void mfma_state_kernel(MfmaK<GT> a) 
                 S[t] = mfma(ka, Ub[ks], S[t]);
             }
         }
-    };
-
-    ChunkRegs r0, r1, r2;
-    issue(0, buf0, r0);
-    issue(min(1, nch - 1), buf1, r1);
-    // the initial state has arrived once at most the two issues above are in
-    // flight; settling it here keeps the loop free of waits for it
-    wait_vmcnt<2 * (kRegLoads + 12)>();
-    // whole rounds of three, then the last one or two chunks: inside the loop
-    // every path issues the same operations, so the compiler's own waits agree
-    // with the counted ones above
-    int j = 0;
-    for (; j + 3 <= nch; j += 3) {
-        step(j, buf0, buf2, r0, r2);
-        step(j + 1, buf1, buf0, r1, r0);
-        step(j + 2, buf2, buf1, r2, r1);
     }
-    if (j < nch) step(j, buf0, buf2, r0, r2);
-    if (j + 1 < nch) step(j + 1, buf1, buf0, r1, r0);
-    wait_vmcnt<0>();  // the copies issued past the last chunk land before the workgroup ends
     if (a.S_out) {
 #pragma unroll
         for (int t = 0; t < 8; ++t)
@@ -736,6 +682,7 @@ hipError_t launch_typed(const PrefillArgs& a, hipStream_t s, int32_t* base, char
     k.S0 = a.S0; k.S_out = a.S_out; k.out = static_cast<bf16*>(a.out); k.rec = recs;
     k.groups = static_cast<int64_t>(a.N) * a.H;
     const int64_t slots = chunk_slots_bound(a.T, a.N);
+    k.slots = slots;
     if (a.T > 0) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&mfma_intra_kernel<GT>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize,
