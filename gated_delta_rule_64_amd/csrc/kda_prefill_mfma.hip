@@ -488,16 +488,20 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
 // ---------------------------------------------------------------------------
 
 // One workgroup per (sequence, head, half of the state columns), with two
-// roles.  Four memory waves only copy: everything one chunk needs (the shared
-// factors -W, Q', K^T and gamma, this half's U~ and M U~ tiles, and the gate
-// logits of its 64 output columns: 72.5 KB) goes into one of two LDS buffers
-// with global_load_lds_dwordx4, one chunk ahead of the compute.  Since these
-// waves only load, one vmcnt(0) per chunk confirms their copies.  Four
-// compute waves (wave w owns the 16 state columns of slice 4*half + w) read
-// only LDS and write the gated output straight to HBM; they never wait for
-// global memory, so store acknowledgements cost them nothing.
+// roles.  Four compute waves (wave w owns the 16 state columns of slice
+// 4*half + w) touch only LDS inside the chunk loop: they read the chunk's
+// factors and write the gated output tile to an LDS staging area.  Four
+// memory waves do all global traffic: they copy what a chunk needs into one
+// of two LDS buffers with global_load_lds_dwordx4 and store the staged output
+// as whole 128-byte row pieces.  A chunk is copied in two parts: the part
+// the first half of a step reads (-W, Q', this half's U~ and M U~ tiles, the
+// gate logits: 56 KB) as soon as the compute waves are done with it two
+// chunks back, and the part the second half reads (K^T, gamma: 16.5 KB) one
+// step ahead.  The memory waves issue the same operations every step, so a
+// fixed count (vmcnt) tells when a part has landed while later ones stay in
+// flight (vector memory operations of one wave retire in issue order).
 constexpr int kStateThreads = 512;
-// LDS buffer layout, bytes
+// LDS buffer layout, bytes.  The first 48 KB mirror the record's first 48 KB.
 constexpr int B_NEGW = 0;       // -W, 16 KB
 constexpr int B_QP = 16384;     // Q', 16 KB
 constexpr int B_KHT = 32768;    // K^T, 16 KB
@@ -506,6 +510,9 @@ constexpr int B_OI = 57344;     // M U~ of the half's four slices, same layout, 
 constexpr int B_Z = 65536;      // gate logits, [64 tokens][64 columns] bf16, 16-byte pieces swizzled
 constexpr int B_GAM = 73728;    // gamma, fp32 [128]
 constexpr int B_BYTES = 74240;
+// operations one memory wave issues per part (wave 0 issues one more in the
+// second part: gamma) and per output tile
+constexpr int kPartA = 14, kPartB = 4, kStores = 2;
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -513,15 +520,17 @@ __device__ __forceinline__ void lds_copy16(const void* gsrc, char* lds_dst) {
     __builtin_amdgcn_global_load_lds(gsrc, (lds_void*)(lds_dst), 16, 0, 0);
 }
 
-// The gate tile: token row r's 128 bytes hold 8 pieces of 16 bytes; piece q
-// of the row is kept at slot q ^ (r & 7), so the compute waves' reads (16
-// rows, one column group) spread over all banks.
-__device__ __forceinline__ int z_slot(int r, int q) { return q ^ (r & 7); }
+// Tiles of 64 rows x 128 bytes (gate logits, staged output): piece q (16
+// bytes) of row r is kept at slot q ^ (r & 7), so reads and writes that walk
+// 16 rows of one column group spread over all banks.
+__device__ __forceinline__ int tile_slot(int r, int q) { return q ^ (r & 7); }
 
-// s_waitcnt with vmcnt(0) only (lgkmcnt and expcnt left at their maxima)
-__device__ __forceinline__ void wait_vmcnt0() {
+// s_waitcnt with vmcnt(n) only (lgkmcnt and expcnt left at their maxima)
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(n >= 0 && n < 64, "vmcnt is 6 bits");
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | 0x70 | 0xF00);
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
@@ -529,6 +538,7 @@ template <typename GT, bool kGate>
 __global__ __launch_bounds__(kStateThreads) void mfma_state_kernel(MfmaK<GT> a) {
     __shared__ __align__(16) char buf0[B_BYTES];
     __shared__ __align__(16) char buf1[B_BYTES];
+    __shared__ __align__(16) char stage[64 * 128];  // gated output tile, bf16, swizzled
     // blockIdx -> (sequence, head, half): both halves of a (sequence, head)
     // land on one XCD (workgroups are dealt round-robin over the 8 XCDs), so
     // the chunk records they share are read through one L2
@@ -547,14 +557,21 @@ __global__ __launch_bounds__(kStateThreads) void mfma_state_kernel(MfmaK<GT> a) 
     auto chunk_len = [&](int j) {
         return static_cast<int>(min(static_cast<int64_t>(kChunk), se - (sb + static_cast<int64_t>(j) * kChunk)));
     };
+    auto buf_of = [&](int j) { return (j & 1) ? buf1 : buf0; };
 
     if (wave >= 4) {
         // ---- memory waves
+        if (nch == 0) return;
         const int wm = wave - 4;
-        auto issue = [&](int j, char* buf) {
+        // part A of chunk min(j, nch-1): -W, Q', U~, M U~ and gate logits
+        // (past the end it copies the last chunk again into the free buffer
+        // the index selects, so that every step issues the same operations)
+        auto issue_a = [&](int jn) {
+            char* buf = buf_of(jn);
+            const int j = min(jn, nch - 1);
             const char* rp = rec_of(j);
 #pragma unroll
-            for (int i = 0; i < 12; ++i) {
+            for (int i = 0; i < 8; ++i) {
                 const int b = wm + 4 * i;
                 lds_copy16(rp + b * 1024 + lane * 16, buf + b * 1024);
             }
@@ -564,26 +581,61 @@ __global__ __launch_bounds__(kStateThreads) void mfma_state_kernel(MfmaK<GT> a) 
                 lds_copy16(rp + R_UT + half * 8192 + b * 1024 + lane * 16, buf + B_UT + b * 1024);
                 lds_copy16(rp + R_OI + half * 8192 + b * 1024 + lane * 16, buf + B_OI + b * 1024);
             }
-            if (kGate) {
-                const int Lc = chunk_len(j);
-                const int64_t tb = sb + static_cast<int64_t>(j) * kChunk;
+            const int Lc = chunk_len(j);
+            const int64_t tb = sb + static_cast<int64_t>(j) * kChunk;
 #pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    const int b = wm + 4 * i;
-                    const int r = 8 * b + (lane >> 3), slot = lane & 7;
-                    const int q = z_slot(r, slot);  // the slot map is its own inverse
-                    const bf16* src = a.z + ((tb + min(r, Lc - 1)) * H + h) * 128 + 64 * half + 8 * q;
-                    lds_copy16(src, buf + B_Z + b * 1024);
-                }
+            for (int i = 0; i < 2; ++i) {
+                const int b = wm + 4 * i;
+                const int r = 8 * b + (lane >> 3);
+                const int q = tile_slot(r, lane & 7);  // the slot map is its own inverse
+                // without a gate the tile is never read; copying keeps the count fixed
+                const bf16* src = kGate ? a.z + ((tb + min(r, Lc - 1)) * H + h) * 128 + 64 * half + 8 * q
+                                        : reinterpret_cast<const bf16*>(rp + R_UT + b * 1024 + lane * 16);
+                lds_copy16(src, buf + B_Z + b * 1024);
+            }
+        };
+        // part B of chunk min(j, nch-1): K^T and gamma
+        auto issue_b = [&](int jn) {
+            char* buf = buf_of(jn);
+            const int j = min(jn, nch - 1);
+            const char* rp = rec_of(j);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int b = 32 + wm + 4 * i;
+                lds_copy16(rp + b * 1024 + lane * 16, buf + b * 1024);
             }
             if (wm == 0 && lane < 32) lds_copy16(rp + R_GAM + lane * 16, buf + B_GAM);
         };
-        if (nch > 0) issue(0, buf0);
+        // issue order per step j: [A_j] B(j+1) [M_j] stores(j), A(j+2).
+        // Before A_j part A of chunk j must be in; after it came B(j),
+        // stores(j-1) and A(j+1).  Before M_j part B of chunk j must be in;
+        // after it came stores(j-1), A(j+1) and B(j+1).  (Wave 0's gamma copy
+        // is left out of the counts: it waits for one operation more than
+        // needed.)  In step 0 there were no stores(-1).
+        issue_a(0);
+        issue_b(0);
+        issue_a(1);
+        const int wr = 16 * wm + (lane >> 3), wq = lane & 7;  // store role: rows wr, wr + 8
         for (int j = 0; j < nch; ++j) {
-            wait_vmcnt0();
-            lds_barrier();  // A: chunk j is in LDS; the other buffer is free
-            if (j + 1 < nch) issue(j + 1, (j & 1) ? buf0 : buf1);
+            if (j == 0) wait_vmcnt<kPartB + kPartA>(); else wait_vmcnt<kPartB + kStores + kPartA>();
+            lds_barrier();  // A_j: part A of chunk j is in LDS; part B of chunk j+1 may be copied
+            issue_b(j + 1);
+            if (j == 0) wait_vmcnt<kPartA + kPartB>(); else wait_vmcnt<kStores + kPartA + kPartB>();
+            lds_barrier();  // M_j: part B of chunk j is in; the output tile of chunk j is staged
+            const int Lc = chunk_len(j);
+            const int64_t tb = sb + static_cast<int64_t>(j) * kChunk;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int r = wr + 8 * i;
+                const uint4 v = *reinterpret_cast<const uint4*>(stage + r * 128 + wq * 16);
+                const int q = tile_slot(r, wq);
+                // rows past the end exist only in a sequence's last chunk,
+                // after which no counted wait follows
+                if (r < Lc) *reinterpret_cast<uint4*>(a.out + ((tb + r) * H + h) * 128 + 64 * half + 8 * q) = v;
+            }
+            issue_a(j + 2);
         }
+        wait_vmcnt<0>();  // no copy may land after the workgroup has ended
         return;
     }
 
@@ -603,10 +655,8 @@ __global__ __launch_bounds__(kStateThreads) void mfma_state_kernel(MfmaK<GT> a) 
     }
 
     for (int j = 0; j < nch; ++j) {
-        const char* cur = (j & 1) ? buf1 : buf0;
-        lds_barrier();  // A: chunk j is in LDS
-        const int Lc = chunk_len(j);
-        const int64_t tb = sb + static_cast<int64_t>(j) * kChunk;
+        const char* cur = buf_of(j);
+        lds_barrier();  // A_j: part A of chunk j is in LDS; the staging tile is free
 
         bf16x8 Sb[4];
 #pragma unroll
@@ -632,20 +682,19 @@ __global__ __launch_bounds__(kStateThreads) void mfma_state_kernel(MfmaK<GT> a) 
                 o = mfma(Sb[ks], qa, o);
             }
             U[mt] = u;
+            // columns 16 wave + 4 g .. + 3 of the half: piece 2 wave + g/2, bytes 8 (g & 1)
             const int r = 16 * mt + c;
+            const int off = r * 128 + tile_slot(r, 2 * wave + (g >> 1)) * 16 + 8 * (g & 1);
             if (kGate) {
-                // columns 16 wave + 4 g .. + 3 of the half: piece 2 wave + g/2, bytes 8 (g & 1)
-                const uint2 zp = *reinterpret_cast<const uint2*>(cur + B_Z + r * 128 +
-                                                                 z_slot(r, 2 * wave + (g >> 1)) * 16 + 8 * (g & 1));
+                const uint2 zp = *reinterpret_cast<const uint2*>(cur + B_Z + off);
                 const float zf[4] = {__uint_as_float(zp.x << 16), __uint_as_float(zp.x & 0xffff0000u),
                                      __uint_as_float(zp.y << 16), __uint_as_float(zp.y & 0xffff0000u)};
 #pragma unroll
                 for (int i = 0; i < 4; ++i) o[i] *= sigmoid_fast(zf[i]);
             }
-            if (r < Lc)
-                *reinterpret_cast<uint2*>(a.out + ((tb + r) * H + h) * 128 + 16 * sl + 4 * g) =
-                    make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+            *reinterpret_cast<uint2*>(stage + off) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
         }
+        lds_barrier();  // M_j: the output tile is staged; part B of chunk j is in LDS
         // S <- Diag(gamma) S + K^T U
         bf16x8 Ub[2];
 #pragma unroll
