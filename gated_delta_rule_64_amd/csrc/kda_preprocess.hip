@@ -143,7 +143,7 @@ __device__ __forceinline__ void conv_run(const PrepK<XT>& a, const XT* src, cons
 #pragma unroll
         for (int r = 0; r < kBatch; ++r) {
             const int64_t t = t0 + r;
-            if (t >= t_end) break;
+            if (t >= t_end) continue;  // (not break: the loop must unroll so raw[] stays in registers)
             float xr[8];
             raw[r].unpack(xr, act);
             if (t >= seq_end) {
@@ -218,7 +218,7 @@ __global__ __launch_bounds__(256) void preprocess_kernel(PrepK<XT> a) {
 #pragma unroll
             for (int r = 0; r < kBatch; ++r) {
                 const int64_t t = t0 + r;
-                if (t >= t_end) break;
+                if (t >= t_end) continue;
                 float x[8], la[8];
                 raw[r].unpack(x, aq);
 #pragma unroll
