@@ -75,7 +75,8 @@ def chunk_count(lengths):
 def record_bytes(K, T, N, H, dk, dv, x_code):
     ws = K.kda_prefill_workspace_bytes(T, N, H, dk, dv, x_code)
     slots = (T + 63) // 64 + N
-    cmap = ((N + 1) * 4 + 255) // 256 * 256
+    # the chunk map (base[N+1], then the sequence of each slot) precedes the records
+    cmap = ((N + 1) * 4 + 255) // 256 * 256 + (slots * 16 + 255) // 256 * 256
     return (ws - cmap) // (slots * H)
 
 

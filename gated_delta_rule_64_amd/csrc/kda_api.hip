@@ -165,6 +165,9 @@ int kda_prefill_chunked(int64_t T_tot, int32_t H, int32_t dk, int32_t dv, const 
                         size_t workspace_bytes, void* stream) {
     int st = check_sizes(T_tot, H, dk, dv, N);
     if (st != KDA_OK) return st;
+    if ((T_tot / 64 + 1 + N) * static_cast<int64_t>(H) > 0xffffffffll)
+        return fail(KDA_ERR_UNSUPPORTED, "H x (T_tot/64 + N) = %lld chunk units exceed 2^32 - 1",
+                    static_cast<long long>((T_tot / 64 + 1 + N) * static_cast<int64_t>(H)));
     if (!valid_dtype(x_dtype)) return fail(KDA_ERR_INVALID_ARGUMENT, "x_dtype=%d is not KDA_F32 or KDA_BF16", x_dtype);
     if (!valid_dtype(gate_dtype)) return fail(KDA_ERR_INVALID_ARGUMENT, "gate_dtype=%d is not KDA_F32 or KDA_BF16", gate_dtype);
     if (cu_seqlens == nullptr && N != 1) return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens is NULL but N=%d", N);

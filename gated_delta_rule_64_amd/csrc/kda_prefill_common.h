@@ -33,14 +33,29 @@ __device__ __forceinline__ int64_t seq_finish(const int32_t* cu, int n, int64_t 
     return cu ? cu[n + 1] : T;
 }
 
-// base[0..N]: prefix sums of chunks per sequence (one workgroup of 1024)
+// The chunk map, built on the device by one workgroup of 1024 threads:
+//   base[0..N]       prefix sums of chunks per sequence;
+//   slot_info[slot]  for each used chunk slot, its first token, length and
+//                    sequence (slots past base[N] are left unwritten).
+struct SlotInfo {
+    int64_t t0;
+    int32_t len, seq;
+};
+static_assert(sizeof(SlotInfo) == 16, "one 16-byte record per slot");
+
 __global__ __launch_bounds__(1024) void chunk_map_kernel(const int32_t* __restrict__ cu, int N,
-                                                         int64_t T, int32_t* __restrict__ base);
+                                                         int64_t T, int32_t* __restrict__ base,
+                                                         SlotInfo* __restrict__ slot_info);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-inline size_t chunk_map_bytes(int N) { return align_up(static_cast<size_t>(N + 1) * 4, 256); }
-
 inline int64_t chunk_slots_bound(int64_t T, int N) { return (T + kChunk - 1) / kChunk + N; }
+
+inline size_t chunk_map_base_bytes(int N) { return align_up(static_cast<size_t>(N + 1) * 4, 256); }
+
+// base[] then slot_info[] (bounded by the slot count)
+inline size_t chunk_map_bytes(int64_t T, int N) {
+    return chunk_map_base_bytes(N) + align_up(static_cast<size_t>(chunk_slots_bound(T, N)) * sizeof(SlotInfo), 256);
+}
 
 }  // namespace kda

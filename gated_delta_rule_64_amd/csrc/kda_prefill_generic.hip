@@ -14,12 +14,14 @@
 namespace kda {
 
 __global__ __launch_bounds__(1024) void chunk_map_kernel(const int32_t* __restrict__ cu, int N,
-                                                         int64_t T, int32_t* __restrict__ base) {
+                                                         int64_t T, int32_t* __restrict__ base,
+                                                         SlotInfo* __restrict__ slot_info) {
     __shared__ int32_t buf[1024];
     __shared__ int32_t carry_s;
     const int tid = threadIdx.x;
     if (tid == 0) carry_s = 0;
     __syncthreads();
+    // sequences in blocks of 1024, one per thread
     for (int start = 0; start < N; start += 1024) {
         const int i = start + tid;
         int32_t c = 0;
@@ -38,6 +40,23 @@ __global__ __launch_bounds__(1024) void chunk_map_kernel(const int32_t* __restri
         }
         const int32_t carry = carry_s;
         if (i < N) base[i] = carry + buf[tid] - c;
+        // the block's slots, spread over all threads: slot carry + s belongs
+        // to the first sequence j of the block whose inclusive count exceeds s
+        const int32_t total = buf[1023];
+        for (int32_t s = tid; s < total; s += 1024) {
+            int lo = 0, hi = 1023;
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if (buf[mid] > s) hi = mid; else lo = mid + 1;
+            }
+            const int n = start + lo;
+            const int32_t j = s - (lo > 0 ? buf[lo - 1] : 0);  // chunk index inside the sequence
+            SlotInfo si;
+            si.t0 = seq_begin(cu, n) + static_cast<int64_t>(j) * kChunk;
+            si.len = static_cast<int32_t>(min(static_cast<int64_t>(kChunk), seq_finish(cu, n, T) - si.t0));
+            si.seq = n;
+            slot_info[carry + s] = si;
+        }
         __syncthreads();
         if (tid == 1023) carry_s = carry + buf[1023];
         __syncthreads();
@@ -296,20 +315,21 @@ size_t prefill_workspace_bytes(int64_t T, int N, int H, int dk, int dv, DT x) {
     const size_t slots = static_cast<size_t>(chunk_slots_bound(T, N));
     const size_t rec = prefill_uses_mfma(dk, dv, x) ? mfma_record_bytes()
                                                     : static_cast<size_t>(gen_rec(dk, dv).size) * 4;
-    return chunk_map_bytes(N) + slots * static_cast<size_t>(H) * rec;
+    return chunk_map_bytes(T, N) + slots * static_cast<size_t>(H) * rec;
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
     int32_t* base = static_cast<int32_t*>(a.ws);
-    char* recs = static_cast<char*>(a.ws) + chunk_map_bytes(a.N);
+    SlotInfo* slot_info = reinterpret_cast<SlotInfo*>(static_cast<char*>(a.ws) + chunk_map_base_bytes(a.N));
+    char* recs = static_cast<char*>(a.ws) + chunk_map_bytes(a.T, a.N);
     hipError_t e;
     {
         LaunchTimer timer("chunk_map", s);
-        hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(1024), 0, s, a.cu, a.N, a.T, base);
+        hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(1024), 0, s, a.cu, a.N, a.T, base, slot_info);
         e = hipGetLastError();
     }
     if (e != hipSuccess) return e;
-    if (prefill_uses_mfma(a.dk, a.dv, a.x)) return launch_prefill_mfma(a, s, base, recs);
+    if (prefill_uses_mfma(a.dk, a.dv, a.x)) return launch_prefill_mfma(a, s, base, slot_info, recs);
     float* rec = reinterpret_cast<float*>(recs);
     if (a.x == DT::BF16) {
         return a.gate == DT::BF16 ? launch_gen_typed<bf16, bf16>(a, s, base, rec)

@@ -6,11 +6,13 @@
 #include <stdint.h>
 
 #include "kda_internal.h"
+#include "kda_prefill_common.h"
 
 namespace kda {
 
 bool mfma_prefill_supports(int dk, int dv, DT x);
 size_t mfma_record_bytes();
-hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t s, int32_t* base, char* recs);
+hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t s, int32_t* base, const SlotInfo* slot_info,
+                               char* recs);
 
 }  // namespace kda

@@ -13,7 +13,9 @@
 // (e >= 4) inside a 32-wide step.  Matrices stored for the state pass are laid
 // out so that this permuted A operand is one 16-byte load per lane.
 //
-// Phase 1 (mfma_intra_kernel): one 256-thread workgroup per (chunk, head).
+// Phase 1 (mfma_intra_kernel): a persistent grid, one 512-thread workgroup
+// per CU, walking the (head, chunk) units; each unit's inputs are loaded into
+// registers during the previous unit.
 //  - A and M tiles (16 x 16, rows in sub-block R, columns in sub-block S <= R)
 //    use factored decays referenced to row b = 16R: left factor
 //    e^{G_r - G_b} <= 1 and right factor e^{G_b - G_s}, which is <= 1 off the
@@ -21,13 +23,12 @@
 //    inside those 16 tokens; if any channel decays by more than e^-40 there,
 //    that tile is computed exactly (pairwise e^{G_r - G_s}) on the vector ALUs.
 //  - T = (I + Diag(beta) A)^-1 in fp32: diagonal 16 x 16 blocks by forward
-//    substitution (one column per lane, in registers), off-diagonal blocks by
-//    block substitution.
-//  - W, U~, Q', M U~ on the matrix cores; outputs stored per (chunk, head).
-// Phase 2 (mfma_state_kernel): one wave per (sequence, head, 16 state
-//  columns); the 128 x 16 fp32 state lives in registers, the next chunk's
-//  factors stream into a second LDS buffer (global_load_lds_dwordx4) while
-//  the current chunk is computed.
+//    substitution (one column per lane, in registers), off-diagonal blocks
+//    from the inverses of the two 32 x 32 halves.
+//  - W, U~, Q', M U~ on the matrix cores; outputs stored per (head, chunk).
+// Phase 2 (mfma_state_kernel): per (sequence, head, half of the state
+//  columns), compute waves carry the fp32 state in registers through the
+//  chunks in order while copy waves stream each chunk's factors into LDS.
 #include "kda_prefill_common.h"
 #include "kda_prefill_mfma.h"
 #include "kda_profile.h"
@@ -83,6 +84,7 @@ struct MfmaK {
     int H, N;
     const int32_t* cu;
     const int32_t* base;
+    const SlotInfo* slot_info;  // first token and length of each chunk slot
     const bf16 *q, *k, *v, *z;
     const GT *la, *beta;
     const float* S0;
@@ -116,6 +118,38 @@ __device__ __forceinline__ void lds8f(const float* p, float (&x)[8]) {
     x[4] = v.x; x[5] = v.y; x[6] = v.z; x[7] = v.w;
 }
 
+// One int32 through the scalar cache, for addresses that are uniform across
+// the wave.  The wait sits in the same asm block, so the result register is
+// never read before the load has returned.
+__device__ __forceinline__ int32_t scalar_load(const int32_t* p) {
+    int32_t v;
+    asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+    return v;
+}
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+// 16 bytes (16-byte aligned) through the scalar cache, as scalar_load
+__device__ __forceinline__ i32x4 scalar_load4(const int32_t* p) {
+    i32x4 v;
+    asm volatile("s_load_dwordx4 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+    return v;
+}
+
+// Four consecutive gate values of one row, kept as loaded until used.
+template <typename GT> struct GateRaw;
+template <> struct GateRaw<float> {
+    float4 v;
+    __device__ __forceinline__ void load(const float* p) { v = *reinterpret_cast<const float4*>(p); }
+    __device__ __forceinline__ float get(int e) const { return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w; }
+};
+template <> struct GateRaw<bf16> {
+    uint2 v;
+    __device__ __forceinline__ void load(const bf16* p) { v = *reinterpret_cast<const uint2*>(p); }
+    __device__ __forceinline__ float get(int e) const {
+        const uint32_t w = e < 2 ? v.x : v.y;
+        return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+    }
+};
+
 // (R, S) of tile i in the lower block triangle, row-major order
 __device__ __forceinline__ void tile_rs(int i, int& R, int& S) {
     R = i >= 6 ? 3 : i >= 3 ? 2 : i >= 1 ? 1 : 0;
@@ -138,348 +172,473 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
     uint16_t* sStW = sV;                                // staging of -W  [64][KS]
     uint16_t* sStQ = reinterpret_cast<uint16_t*>(sA);   // staging of Q'  [64][128]
 
-    const int slot = blockIdx.x, h = blockIdx.y;
-    if (slot >= a.base[a.N]) return;
-    const int n = find_seq(a.base, a.N, slot);
-    const int64_t t0 = seq_begin(a.cu, n) + static_cast<int64_t>(slot - a.base[n]) * kChunk;
-    const int L = static_cast<int>(min(static_cast<int64_t>(kChunk), seq_finish(a.cu, n, a.T) - t0));
     const int H = a.H;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, c = lane & 15;
-    char* rec = a.rec + (h * a.slots + slot) * REC_BYTES;  // a head's chunks are contiguous
-
-    // ---- inputs to LDS.  Loads are branch-free (rows past L read row L-1 and
-    // are replaced by zero) so that all of them are in flight together.
+    const int ftid = threadIdx.x;  // the thread index as the prefetch uses it
+    // Units are (head, chunk slot) pairs, head-major; the grid is persistent
+    // (one workgroup per CU) and walks them with stride gridDim.x.
+    const int nslots = scalar_load(a.base + a.N);
+    const int64_t units = static_cast<int64_t>(H) * nslots;
+    struct Unit {
+        int h, L;
+        int64_t slot, t0;
+    };
+    // The unit's head, slot, first token and length.  The lookups are
+    // uniform, so they go through the scalar cache (a vector load here would
+    // also wait for the previous unit's record stores).
+    auto unit_of = [&](int64_t v) {
+        Unit u;
+        // unit indices fit 32 bits (the launcher checks the bound)
+        const uint32_t v32 = static_cast<uint32_t>(v), ns = static_cast<uint32_t>(nslots);
+        u.h = static_cast<int>(v32 / ns);
+        u.slot = v32 % ns;
+        const i32x4 si = scalar_load4(reinterpret_cast<const int32_t*>(a.slot_info + u.slot));
+        u.t0 = static_cast<int64_t>((static_cast<uint64_t>(static_cast<uint32_t>(si[1])) << 32) |
+                                    static_cast<uint32_t>(si[0]));
+        u.L = si[2];
+        return u;
+    };
+    // This thread's share of a unit's inputs, loaded one unit ahead into
+    // registers so the loads overlap the previous unit's work: rows
+    // (tid + 512 i) / 16 of q, k, v (8 channels each), rows 4 rg .. 4 rg + 3 of
+    // the decay logs (4 channels), and beta for tid < 64.  Loads are
+    // branch-free: rows past the chunk end read row L-1 and are zeroed on use.
+    const int fcq = ftid & 31, frg = ftid >> 5;
+    uint4 pk[2], pq[2], pv[2];
+    GateRaw<GT> px[4];  // decay logs as loaded; converted when written to LDS
+    GT pb{};
+    // part p of a unit's loads: 0 keys, 1 queries, 2 values, 3 decay logs and beta
+    auto fetch = [&](const Unit& u, int p) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int idx = tid + kIntraThreads * i;
-        const int r = idx >> 4, ch = idx & 15;
-        const bool in = r < L;
-        const int64_t goff = ((t0 + (in ? r : L - 1)) * H + h) * 128 + ch * 8;
-        uint4 kk = *reinterpret_cast<const uint4*>(a.k + goff);
-        uint4 qq = *reinterpret_cast<const uint4*>(a.q + goff);
-        uint4 vv = *reinterpret_cast<const uint4*>(a.v + goff);
-        if (!in) kk = qq = vv = make_uint4(0, 0, 0, 0);
-        *reinterpret_cast<uint4*>(sK + r * KS + ch * 8) = kk;
-        *reinterpret_cast<uint4*>(sQ + r * KS + ch * 8) = qq;
-        *reinterpret_cast<uint4*>(sV + r * KS + ch * 8) = vv;
-    }
-    const int cq = tid & 31, rg = tid >> 5;  // 4 channels x 4 rows per thread
-    float x[4][4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int r = 4 * rg + j;
-        const bool in = r < L;
-        ld4(a.la + ((t0 + (in ? r : L - 1)) * H + h) * 128 + 4 * cq, x[j]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) x[j][e] = in ? x[j][e] : 0.f;  // padded tokens: no decay
-    }
-    if (tid < 64) {
-        const float bv = ld(a.beta + (t0 + (tid < L ? tid : L - 1)) * H + h);
-        sB[tid] = tid < L ? bv : 0.f;  // padded tokens: no write
-    }
-    if (tid < 4) sFlag[tid] = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        reinterpret_cast<float4*>(sA)[tid + kIntraThreads * i] = make_float4(0.f, 0.f, 0.f, 0.f);  // sA, sM
-#pragma unroll
-    for (int j = 1; j < 4; ++j)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) x[j][e] += x[j - 1][e];
-    *reinterpret_cast<float4*>(sTot + rg * 128 + 4 * cq) = make_float4(x[3][0], x[3][1], x[3][2], x[3][3]);
-    lds_barrier();
-    {
-        float off[4] = {0.f, 0.f, 0.f, 0.f};
-        for (int q2 = 0; q2 < rg; ++q2) {
-            const float4 t4 = *reinterpret_cast<const float4*>(sTot + q2 * 128 + 4 * cq);
-            off[0] += t4.x; off[1] += t4.y; off[2] += t4.z; off[3] += t4.w;
+        for (int i = 0; i < 2; ++i) {
+            const int idx = ftid + kIntraThreads * i;
+            const int r = idx >> 4, ch = idx & 15;
+            const int64_t goff = ((u.t0 + min(r, u.L - 1)) * H + u.h) * 128 + ch * 8;
+            if (p == 0) pk[i] = *reinterpret_cast<const uint4*>(a.k + goff);
+            if (p == 1) pq[i] = *reinterpret_cast<const uint4*>(a.q + goff);
+            if (p == 2) pv[i] = *reinterpret_cast<const uint4*>(a.v + goff);
         }
+        if (p == 3) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                px[j].load(a.la + ((u.t0 + min(4 * frg + j, u.L - 1)) * H + u.h) * 128 + 4 * fcq);
+            if (ftid < 64) pb = a.beta[(u.t0 + min(ftid, u.L - 1)) * H + u.h];
+        }
+    };
+    auto fetch_all = [&](const Unit& u) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) fetch(u, p);
+    };
+
+    // A unit's prefetched inputs into LDS (padded rows are zero: no decay, no
+    // write), the first level of the decay scan, and cleared A, M and flags.
+    // Runs once the LDS buffers are free.
+    auto stage_inputs = [&](const Unit& u, int tid) {
+        const int cq = tid & 31, rg = tid >> 5;
+        const int L = u.L;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int idx = tid + kIntraThreads * i;
+            const int r = idx >> 4, ch = idx & 15;
+            const uint32_t m = r < L ? 0xffffffffu : 0u;  // masks, not selects: the arrays stay in registers
+            *reinterpret_cast<uint4*>(sK + r * KS + ch * 8) =
+                make_uint4(pk[i].x & m, pk[i].y & m, pk[i].z & m, pk[i].w & m);
+            *reinterpret_cast<uint4*>(sQ + r * KS + ch * 8) =
+                make_uint4(pq[i].x & m, pq[i].y & m, pq[i].z & m, pq[i].w & m);
+            *reinterpret_cast<uint4*>(sV + r * KS + ch * 8) =
+                make_uint4(pv[i].x & m, pv[i].y & m, pv[i].z & m, pv[i].w & m);
+        }
+        float x[4][4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[j][e] = 4 * rg + j < L ? px[j].get(e) : 0.f;
+        if (tid < 64) sB[tid] = tid < L ? ld(&pb) : 0.f;
+        if (tid < 4) sFlag[tid] = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            reinterpret_cast<float4*>(sA)[tid + kIntraThreads * i] = make_float4(0.f, 0.f, 0.f, 0.f);  // sA, sM
+#pragma unroll
+        for (int j = 1; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[j][e] += x[j - 1][e];
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             *reinterpret_cast<float4*>(sG + (4 * rg + j) * GS + 4 * cq) =
-                make_float4(x[j][0] + off[0], x[j][1] + off[1], x[j][2] + off[2], x[j][3] + off[3]);
-    }
-    lds_barrier();
-    // sub-blocks whose decay inside 16 tokens is too steep for the factored form
-    if (tid < 128) {
-#pragma unroll
-        for (int R = 0; R < 4; ++R) {
-            const float d = sG[(16 * R) * GS + tid] - sG[(16 * R + 15) * GS + tid];
-            if (d > kDiagRange) sFlag[R] = 1;  // benign race: every writer stores 1
-        }
-    }
-    lds_barrier();
+                make_float4(x[j][0], x[j][1], x[j][2], x[j][3]);
+        *reinterpret_cast<float4*>(sTot + rg * 128 + 4 * cq) = make_float4(x[3][0], x[3][1], x[3][2], x[3][3]);
+    };
 
-    // ---- A and M: 10 tiles (R >= S); wave w takes tiles w and w + 8
-    for (int ti = wave; ti < 10; ti += 8) {
-        int R, S;
-        tile_rs(ti, R, S);
-        const int b = 16 * R;
-        f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accM = accA;
-        if (R == S && sFlag[R]) {
-            // exact pairwise decays (steep decay inside the block)
+    int64_t v = blockIdx.x;
+    if (v >= units) return;
+    Unit nxt = unit_of(v);
+    fetch_all(nxt);
+    stage_inputs(nxt, ftid);
+    for (; v < units; v += gridDim.x) {
+        // Lane-dependent values are rederived from an opaque copy of the thread
+        // index in every unit, so the compiler does not hoist dozens of masks
+        // and addresses out of the loop (they would not fit in registers).
+        int tid = ftid;
+        asm volatile("" : "+v"(tid));
+        const int wave = tid >> 6, lane = tid & 63, g = lane >> 4, c = lane & 15;
+        const int cq = tid & 31, rg = tid >> 5;
+        const Unit cur = nxt;
+        const int h = cur.h;
+        const int64_t slot = cur.slot;
+        char* rec = a.rec + (h * a.slots + slot) * REC_BYTES;  // a head's chunks are contiguous
+        const bool more = v + gridDim.x < units;
+        lds_barrier();
+        {
+            float off[4] = {0.f, 0.f, 0.f, 0.f};
+            for (int q2 = 0; q2 < rg; ++q2) {
+                const float4 t4 = *reinterpret_cast<const float4*>(sTot + q2 * 128 + 4 * cq);
+                off[0] += t4.x; off[1] += t4.y; off[2] += t4.z; off[3] += t4.w;
+            }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = b + 4 * g + i, s2 = 16 * S + c;
-                float av = 0.f, mv = 0.f;
-                if (s2 <= r) {
-                    for (int ch = 0; ch < 128; ++ch) {
-                        const float ks = bfv(sK + s2 * KS + ch) * expf(sG[r * GS + ch] - sG[s2 * GS + ch]);
-                        av += bfv(sK + r * KS + ch) * ks;
-                        mv += bfv(sQ + r * KS + ch) * ks;
+            for (int j = 0; j < 4; ++j) {
+                float4* p = reinterpret_cast<float4*>(sG + (4 * rg + j) * GS + 4 * cq);
+                const float4 x4 = *p;
+                *p = make_float4(x4.x + off[0], x4.y + off[1], x4.z + off[2], x4.w + off[3]);
+            }
+        }
+        lds_barrier();
+        // sub-blocks whose decay inside 16 tokens is too steep for the factored form
+        if (tid < 128) {
+#pragma unroll
+            for (int R = 0; R < 4; ++R) {
+                const float d = sG[(16 * R) * GS + tid] - sG[(16 * R + 15) * GS + tid];
+                if (d > kDiagRange) sFlag[R] = 1;  // benign race: every writer stores 1
+            }
+        }
+        lds_barrier();
+
+        // ---- A and M: 10 tiles (R >= S) of 4 contraction steps each.  Wave w
+        // computes tile w whole; the steps of tiles 8 and 9 go one per wave
+        // (tile 8 + w/4, step w%4), and their partial tiles are summed in a fixed
+        // order afterwards, so the result does not depend on timing.
+        {
+            // A and M partials of tile (R, S) over contraction steps [k0, k1)
+            auto tile_part = [&](int R, int S, int k0, int k1, f32x4& accA, f32x4& accM) {
+                const int b = 16 * R;
+                if (R == S && sFlag[R]) {
+                    // exact pairwise decays (steep decay inside the block)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int r = b + 4 * g + i, s2 = 16 * S + c;
+                        float av = 0.f, mv = 0.f;
+                        if (s2 <= r) {
+                            for (int ch = 32 * k0; ch < 32 * k1; ++ch) {
+                                const float ks = bfv(sK + s2 * KS + ch) * expf(sG[r * GS + ch] - sG[s2 * GS + ch]);
+                                av += bfv(sK + r * KS + ch) * ks;
+                                mv += bfv(sQ + r * KS + ch) * ks;
+                            }
+                        }
+                        accA[i] += av;
+                        accM[i] += mv;
+                    }
+                } else {
+                    const int rl = b + c, sr = 16 * S + c;
+                    for (int ks = k0; ks < k1; ++ks) {
+                        const int ch0 = 32 * ks + 8 * g;
+                        float kl[8], ql[8], kr[8], gl[8], gb[8], gr[8];
+                        unpack8(*reinterpret_cast<const uint4*>(sK + rl * KS + ch0), kl);
+                        unpack8(*reinterpret_cast<const uint4*>(sQ + rl * KS + ch0), ql);
+                        unpack8(*reinterpret_cast<const uint4*>(sK + sr * KS + ch0), kr);
+                        lds8f(sG + rl * GS + ch0, gl);
+                        lds8f(sG + b * GS + ch0, gb);
+                        lds8f(sG + sr * GS + ch0, gr);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const float el = __expf(gl[e] - gb[e]);  // <= 1
+                            kl[e] *= el;
+                            ql[e] *= el;
+                            kr[e] *= __expf(gb[e] - gr[e]);
+                        }
+                        const bf16x8 bk = to_bf16x8(kr);
+                        accA = mfma(to_bf16x8(kl), bk, accA);
+                        accM = mfma(to_bf16x8(ql), bk, accM);
                     }
                 }
-                accA[i] = av;
-                accM[i] = mv;
-            }
-        } else {
-            const int rl = b + c, sr = 16 * S + c;
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const int ch0 = 32 * ks + 8 * g;
-                float kl[8], ql[8], kr[8], gl[8], gb[8], gr[8];
-                unpack8(*reinterpret_cast<const uint4*>(sK + rl * KS + ch0), kl);
-                unpack8(*reinterpret_cast<const uint4*>(sQ + rl * KS + ch0), ql);
-                unpack8(*reinterpret_cast<const uint4*>(sK + sr * KS + ch0), kr);
-                lds8f(sG + rl * GS + ch0, gl);
-                lds8f(sG + b * GS + ch0, gb);
-                lds8f(sG + sr * GS + ch0, gr);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float el = __expf(gl[e] - gb[e]);  // <= 1
-                    kl[e] *= el;
-                    ql[e] *= el;
-                    kr[e] *= __expf(gb[e] - gr[e]);
-                }
-                const bf16x8 bk = to_bf16x8(kr);
-                accA = mfma(to_bf16x8(kl), bk, accA);
-                accM = mfma(to_bf16x8(ql), bk, accM);
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = b + 4 * g + i, s2 = 16 * S + c;
-            sA[r * 64 + s2] = s2 < r ? accA[i] : 0.f;
-            sM[r * 64 + s2] = s2 <= r ? accM[i] : 0.f;
-        }
-    }
-    lds_barrier();
-
-    // ---- T = (I + Diag(beta) A)^-1
-    // diagonal blocks: wave R < 4, lane j < 16 owns column j of T_RR in registers
-    if (wave < 4) {
-        const int R = wave, j = lane;
-        float t[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float arow[16];
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const float4 v4 = *reinterpret_cast<const float4*>(sA + (16 * R + r) * 64 + 16 * R + 4 * q4);
-                arow[4 * q4] = v4.x; arow[4 * q4 + 1] = v4.y; arow[4 * q4 + 2] = v4.z; arow[4 * q4 + 3] = v4.w;
-            }
-            float sum = 0.f;
-#pragma unroll
-            for (int s2 = 0; s2 < r; ++s2) sum += arow[s2] * t[s2];
-            t[r] = (r == j ? 1.f : 0.f) - sB[16 * R + r] * sum;
-        }
-        if (j < 16) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) sT[(16 * R + r) * 64 + 16 * R + j] = t[r];
-        }
-    }
-    lds_barrier();
-    // off-diagonal blocks by distance d = R - S (waves 0..2):
-    //   Y = Diag(beta_R) sum_{J=S}^{R-1} A_RJ T_JS ;  T_RS = -T_RR Y
-    float* sY = sTot;  // 3 x 256 floats of scratch (the scan partials are dead)
-    for (int d = 1; d <= 3; ++d) {
-        const int S = wave, R = wave + d;
-        const bool active = wave < 3 && R <= 3;
-        if (active) {
-            float acc[4] = {0.f, 0.f, 0.f, 0.f};
-            for (int J = S; J < R; ++J) {
-                float tcol[16];
-#pragma unroll
-                for (int kk = 0; kk < 16; ++kk) tcol[kk] = sT[(16 * J + kk) * 64 + 16 * S + c];
+            };
+            auto store_tile = [&](int R, int S, const f32x4& accA, const f32x4& accM) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float* arow = sA + (16 * R + 4 * g + i) * 64 + 16 * J;
+                    const int r = 16 * R + 4 * g + i, s2 = 16 * S + c;
+                    sA[r * 64 + s2] = s2 < r ? accA[i] : 0.f;
+                    sM[r * 64 + s2] = s2 <= r ? accM[i] : 0.f;
+                }
+            };
+            int R, S;
+            f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accM = accA;
+            tile_rs(wave, R, S);
+            tile_part(R, S, 0, 4, accA, accM);
+            store_tile(R, S, accA, accM);
+            // one step of tile 8 or 9 into a partial block in sT (free until T is built)
+            const int tp = 8 + (wave >> 2), kp = wave & 3;
+            tile_rs(tp, R, S);
+            accA = f32x4{0.f, 0.f, 0.f, 0.f};
+            accM = accA;
+            tile_part(R, S, kp, kp + 1, accA, accM);
+            float* part = sT + wave * 512;  // [A 16x16][M 16x16], lane-major
 #pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4) {
-                        const float4 v4 = reinterpret_cast<const float4*>(arow)[q4];
-                        acc[i] += v4.x * tcol[4 * q4] + v4.y * tcol[4 * q4 + 1] + v4.z * tcol[4 * q4 + 2] +
-                                  v4.w * tcol[4 * q4 + 3];
+            for (int i = 0; i < 4; ++i) {
+                part[(4 * g + i) * 16 + c] = accA[i];
+                part[256 + (4 * g + i) * 16 + c] = accM[i];
+            }
+            lds_barrier();
+            if (wave < 2) {  // wave 0 sums tile 8, wave 1 tile 9, steps in order
+                tile_rs(8 + wave, R, S);
+                f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sm = sa;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const float* q = sT + (4 * wave + k) * 512;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        sa[i] += q[(4 * g + i) * 16 + c];
+                        sm[i] += q[256 + (4 * g + i) * 16 + c];
                     }
                 }
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 4 * g + i;
-                sY[wave * 256 + r * 16 + c] = sB[16 * R + r] * acc[i];
+                store_tile(R, S, sa, sm);
             }
         }
         lds_barrier();
-        if (active) {
-            float ycol[16];
+
+        // The next unit's loads go out in four parts, one after each of the
+        // phases from here on, and land during the rest of this unit's work.
+        // All workgroups run in near lockstep, so one burst of loads per unit
+        // would saturate HBM while it lasts and idle it the rest of the time.
+        if (more) {
+            nxt = unit_of(v + gridDim.x);
+            fetch(nxt, 0);
+        }
+
+        // ---- T = (I + Diag(beta) A)^-1
+        // diagonal blocks: wave R < 4, lane j < 16 owns column j of T_RR in registers
+        if (wave < 4) {
+            const int R = wave, j = lane;
+            float t[16];
 #pragma unroll
-            for (int kk = 0; kk < 16; ++kk) ycol[kk] = sY[wave * 256 + kk * 16 + c];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 4 * g + i;
-                const float* trow = sT + (16 * R + r) * 64 + 16 * R;
-                float acc = 0.f;
+            for (int r = 0; r < 16; ++r) {
+                float arow[16];
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4) {
-                    const float4 v4 = reinterpret_cast<const float4*>(trow)[q4];
-                    acc += v4.x * ycol[4 * q4] + v4.y * ycol[4 * q4 + 1] + v4.z * ycol[4 * q4 + 2] +
-                           v4.w * ycol[4 * q4 + 3];
+                    const float4 v4 = *reinterpret_cast<const float4*>(sA + (16 * R + r) * 64 + 16 * R + 4 * q4);
+                    arow[4 * q4] = v4.x; arow[4 * q4 + 1] = v4.y; arow[4 * q4 + 2] = v4.z; arow[4 * q4 + 3] = v4.w;
                 }
-                sT[(16 * R + r) * 64 + 16 * S + c] = -acc;
+                float sum = 0.f;
+#pragma unroll
+                for (int s2 = 0; s2 < r; ++s2) sum += arow[s2] * t[s2];
+                t[r] = (r == j ? 1.f : 0.f) - sB[16 * R + r] * sum;
+            }
+            if (j < 16) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) sT[(16 * R + r) * 64 + 16 * R + j] = t[r];
             }
         }
         lds_barrier();
-    }
-    // blocks of T above the diagonal are never written; every reader masks them
-
-    // ---- W = T (beta e^G K) and U~ = T (beta V): column tile nt = wave
-    const int nt = wave;
-    const int chn = 16 * nt + c;
-    f32x4 accW[4], accU[4];
-    {
-        bf16x8 Ta[4][2];
+        if (more) fetch(nxt, 1);
+        // Off-diagonal blocks of T from the two 32 x 32 halves (L = Diag(beta) A):
+        //   level 1: T_10 = -T_11 L_10 T_00,  T_32 = -T_33 L_32 T_22          (waves 0, 1)
+        //   level 2: X = L_hi,lo T_lo:  X_20 = L_20 T_00 + L_21 T_10,  X_21 = L_21 T_11,
+        //            X_30 = L_30 T_00 + L_31 T_10,  X_31 = L_31 T_11           (waves 0..3)
+        //   level 3: T_hi,lo = -T_hi X:  T_20 = -T_22 X_20,  T_21 = -T_22 X_21,
+        //            T_30 = -(T_32 X_20 + T_33 X_30),  T_31 = -(T_32 X_21 + T_33 X_31)
+        // Lane (g, c) computes rows 4g .. 4g+3, column c of a 16 x 16 block.
+        {
+            float* sX = sTot;  // 16 x 16 blocks with row stride 16 (the scan partials are dead)
+            // acc[i] += sum_k P[4g+i][k] Q[k][c] over a 16 x 16 pair
+            auto mm16 = [&](const float* P, int ldp, const float* Q, int ldq, float (&acc)[4]) {
+                float qc[16];
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
+                for (int kk = 0; kk < 16; ++kk) qc[kk] = Q[kk * ldq + c];
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const int row = 16 * mt + c, col0 = 32 * ks + 8 * g;
-                float tv[8];
-                lds8f(sT + row * 64 + col0, tv);
+                for (int i = 0; i < 4; ++i) {
+                    const float4* prow = reinterpret_cast<const float4*>(P + (4 * g + i) * ldp);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) tv[e] = col0 + e <= row ? tv[e] : 0.f;
-                Ta[mt][ks] = to_bf16x8(tv);
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        const float4 v4 = prow[q4];
+                        acc[i] += v4.x * qc[4 * q4] + v4.y * qc[4 * q4 + 1] + v4.z * qc[4 * q4 + 2] +
+                                  v4.w * qc[4 * q4 + 3];
+                    }
+                }
+            };
+            if (wave < 2) {
+                const int R = 2 * wave + 1, S = R - 1;
+                float y[4] = {0.f, 0.f, 0.f, 0.f};
+                mm16(sA + (16 * R) * 64 + 16 * S, 64, sT + (16 * S) * 64 + 16 * S, 64, y);
+                float* Y = sX + wave * 256;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) Y[(4 * g + i) * 16 + c] = sB[16 * R + 4 * g + i] * y[i];
+                // (a wave's LDS operations are performed in order: Y is complete here)
+                float t[4] = {0.f, 0.f, 0.f, 0.f};
+                mm16(sT + (16 * R) * 64 + 16 * R, 64, Y, 16, t);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sT[(16 * R + 4 * g + i) * 64 + 16 * S + c] = -t[i];
             }
+            lds_barrier();
+            const int R = 2 + (wave >> 1), S = wave & 1;  // block of waves 0..3
+            if (wave < 4) {
+                float x[4] = {0.f, 0.f, 0.f, 0.f};
+                for (int J = S; J < 2; ++J) mm16(sA + (16 * R) * 64 + 16 * J, 64, sT + (16 * J) * 64 + 16 * S, 64, x);
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-            accW[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            accU[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int i = 0; i < 4; ++i) sX[wave * 256 + (4 * g + i) * 16 + c] = sB[16 * R + 4 * g + i] * x[i];
+            }
+            lds_barrier();
+            if (wave < 4) {
+                float t[4] = {0.f, 0.f, 0.f, 0.f};
+                mm16(sT + (16 * R) * 64 + 32, 64, sX + S * 256, 16, t);                      // T_R2 X_2S
+                if (R == 3) mm16(sT + (16 * 3) * 64 + 48, 64, sX + (2 + S) * 256, 16, t);  // T_33 X_3S
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sT[(16 * R + 4 * g + i) * 64 + 16 * S + c] = -t[i];
+            }
         }
+        lds_barrier();
+        // blocks of T above the diagonal are never written; every reader masks them
+
+        if (more) fetch(nxt, 2);
+        // ---- W = T (beta e^G K) and U~ = T (beta V): column tile nt = wave
+        const int nt = wave;
+        const int chn = 16 * nt + c;
+        f32x4 accW[4], accU[4];
+        {
+            bf16x8 Ta[4][2];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const int s0 = 32 * ks + 8 * g;
-            float bt[8], bk[8], bv[8];
-            lds8f(sB + s0, bt);
+            for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int s2 = s0 + e;
-                bk[e] = bt[e] * __expf(sG[s2 * GS + chn]) * bfv(sK + s2 * KS + chn);
-                bv[e] = bt[e] * bfv(sV + s2 * KS + chn);
-            }
-            const bf16x8 Bk = to_bf16x8(bk), Bv = to_bf16x8(bv);
+                for (int ks = 0; ks < 2; ++ks) {
+                    const int row = 16 * mt + c, col0 = 32 * ks + 8 * g;
+                    float tv[8];
+                    lds8f(sT + row * 64 + col0, tv);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) tv[e] = col0 + e <= row ? tv[e] : 0.f;
+                    Ta[mt][ks] = to_bf16x8(tv);
+                }
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
-                if (32 * ks > 16 * mt + 15) continue;  // T is lower triangular
-                accW[mt] = mfma(Ta[mt][ks], Bk, accW[mt]);
-                accU[mt] = mfma(Ta[mt][ks], Bv, accU[mt]);
-            }
-        }
-        // U~ in result layout, slice nt
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-            uint2 p;
-            p.x = pack_bf16x2(accU[mt][0], accU[mt][1]);
-            p.y = pack_bf16x2(accU[mt][2], accU[mt][3]);
-            *reinterpret_cast<uint2*>(rec + R_UT + ((nt * 4 + mt) * 64 + lane) * 8) = p;
-        }
-    }
-    lds_barrier();  // V and A are dead: their buffers become the staging areas
-
-    // ---- Q' = e^G Q - M W and M U~; stage -W and Q' for the transposes
-    {
-        bf16x8 Mneg[4][2], Mpos[4][2];
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const float* mrow = sM + (16 * mt + c) * 64 + 32 * ks + 4 * g;
-                const float4 lo = *reinterpret_cast<const float4*>(mrow);
-                const float4 hi = *reinterpret_cast<const float4*>(mrow + 16);
-                const float mv[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-                float mn[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) mn[e] = -mv[e];
-                Mpos[mt][ks] = to_bf16x8(mv);
-                Mneg[mt][ks] = to_bf16x8(mn);
-            }
-        bf16x8 Bw[2], Bu[2];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            Bw[ks] = to_bf16x8(accW[2 * ks], accW[2 * ks + 1]);
-            Bu[ks] = to_bf16x8(accU[2 * ks], accU[2 * ks + 1]);
-        }
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-            f32x4 qp, oi = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 16 * mt + 4 * g + i;
-                qp[i] = __expf(sG[r * GS + chn]) * bfv(sQ + r * KS + chn);
+                accW[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                accU[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                if (32 * ks > 16 * mt + 15) continue;  // M is lower triangular
-                qp = mfma(Mneg[mt][ks], Bw[ks], qp);
-                // (M U~)^T = U~^T M^T: the operands swap roles, so lane (g, c)
-                // ends up with M U~[16mt + c][16nt + 4g + i]
-                oi = mfma(Bu[ks], Mpos[mt][ks], oi);
-            }
-            uint2 p;
-            p.x = pack_bf16x2(oi[0], oi[1]);
-            p.y = pack_bf16x2(oi[2], oi[3]);
-            *reinterpret_cast<uint2*>(rec + R_OI + ((nt * 4 + mt) * 64 + lane) * 8) = p;
+                const int s0 = 32 * ks + 8 * g;
+                float bt[8], bk[8], bv[8];
+                lds8f(sB + s0, bt);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 16 * mt + 4 * g + i;
-                sStW[r * KS + chn] = f32_to_bf16(-accW[mt][i]);
-                sStQ[r * 128 + chn] = f32_to_bf16(qp[i]);
+                for (int e = 0; e < 8; ++e) {
+                    const int s2 = s0 + e;
+                    bk[e] = bt[e] * __expf(sG[s2 * GS + chn]) * bfv(sK + s2 * KS + chn);
+                    bv[e] = bt[e] * bfv(sV + s2 * KS + chn);
+                }
+                const bf16x8 Bk = to_bf16x8(bk), Bv = to_bf16x8(bv);
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) {
+                    if (32 * ks > 16 * mt + 15) continue;  // T is lower triangular
+                    accW[mt] = mfma(Ta[mt][ks], Bk, accW[mt]);
+                    accU[mt] = mfma(Ta[mt][ks], Bv, accU[mt]);
+                }
+            }
+            // U~ in result layout, slice nt
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                uint2 p;
+                p.x = pack_bf16x2(accU[mt][0], accU[mt][1]);
+                p.y = pack_bf16x2(accU[mt][2], accU[mt][3]);
+                *reinterpret_cast<uint2*>(rec + R_UT + ((nt * 4 + mt) * 64 + lane) * 8) = p;
             }
         }
-    }
-    lds_barrier();
+        lds_barrier();  // V and A are dead: their buffers become the staging areas
 
-    // ---- stores in the A-operand layout: -W, Q' (2 blocks per wave each), K^T
-    {
-        const int mt = wave >> 1;
+        if (more) fetch(nxt, 3);
+        // ---- Q' = e^G Q - M W and M U~; stage -W and Q' for the transposes
+        {
+            bf16x8 Mneg[4][2], Mpos[4][2];
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-            const int ks = 2 * (wave & 1) + k2;
-            const int r = 16 * mt + c;
-            const int c0 = 32 * ks + 4 * g;
-            const uint2 wlo = *reinterpret_cast<const uint2*>(sStW + r * KS + c0);
-            const uint2 whi = *reinterpret_cast<const uint2*>(sStW + r * KS + c0 + 16);
-            const uint2 qlo = *reinterpret_cast<const uint2*>(sStQ + r * 128 + c0);
-            const uint2 qhi = *reinterpret_cast<const uint2*>(sStQ + r * 128 + c0 + 16);
-            const int blk = (mt * 4 + ks) * 64 + lane;
-            *reinterpret_cast<uint4*>(rec + R_NEGW + blk * 16) = make_uint4(wlo.x, wlo.y, whi.x, whi.y);
-            *reinterpret_cast<uint4*>(rec + R_QP + blk * 16) = make_uint4(qlo.x, qlo.y, qhi.x, qhi.y);
-        }
-        const int t = wave;
-        const int ch = 16 * t + c;
-        const float glast = sG[63 * GS + ch];
+            for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            float kv[8];
+                for (int ks = 0; ks < 2; ++ks) {
+                    const float* mrow = sM + (16 * mt + c) * 64 + 32 * ks + 4 * g;
+                    const float4 lo = *reinterpret_cast<const float4*>(mrow);
+                    const float4 hi = *reinterpret_cast<const float4*>(mrow + 16);
+                    const float mv[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+                    float mn[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int s2 = 32 * ks + perm(g, e);
-                kv[e] = __expf(glast - sG[s2 * GS + ch]) * bfv(sK + s2 * KS + ch);
+                    for (int e = 0; e < 8; ++e) mn[e] = -mv[e];
+                    Mpos[mt][ks] = to_bf16x8(mv);
+                    Mneg[mt][ks] = to_bf16x8(mn);
+                }
+            bf16x8 Bw[2], Bu[2];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                Bw[ks] = to_bf16x8(accW[2 * ks], accW[2 * ks + 1]);
+                Bu[ks] = to_bf16x8(accU[2 * ks], accU[2 * ks + 1]);
             }
-            uint4 p;
-            p.x = pack_bf16x2(kv[0], kv[1]);
-            p.y = pack_bf16x2(kv[2], kv[3]);
-            p.z = pack_bf16x2(kv[4], kv[5]);
-            p.w = pack_bf16x2(kv[6], kv[7]);
-            *reinterpret_cast<uint4*>(rec + R_KHT + ((t * 2 + ks) * 64 + lane) * 16) = p;
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                f32x4 qp, oi = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 16 * mt + 4 * g + i;
+                    qp[i] = __expf(sG[r * GS + chn]) * bfv(sQ + r * KS + chn);
+                }
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    if (32 * ks > 16 * mt + 15) continue;  // M is lower triangular
+                    qp = mfma(Mneg[mt][ks], Bw[ks], qp);
+                    // (M U~)^T = U~^T M^T: the operands swap roles, so lane (g, c)
+                    // ends up with M U~[16mt + c][16nt + 4g + i]
+                    oi = mfma(Bu[ks], Mpos[mt][ks], oi);
+                }
+                uint2 p;
+                p.x = pack_bf16x2(oi[0], oi[1]);
+                p.y = pack_bf16x2(oi[2], oi[3]);
+                *reinterpret_cast<uint2*>(rec + R_OI + ((nt * 4 + mt) * 64 + lane) * 8) = p;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 16 * mt + 4 * g + i;
+                    sStW[r * KS + chn] = f32_to_bf16(-accW[mt][i]);
+                    sStQ[r * 128 + chn] = f32_to_bf16(qp[i]);
+                }
+            }
         }
-        if (tid < 128) reinterpret_cast<float*>(rec + R_GAM)[tid] = expf(sG[63 * GS + tid]);
+        lds_barrier();
+
+        // ---- stores in the A-operand layout: -W, Q' (2 blocks per wave each), K^T
+        {
+            const int mt = wave >> 1;
+#pragma unroll
+            for (int k2 = 0; k2 < 2; ++k2) {
+                const int ks = 2 * (wave & 1) + k2;
+                const int r = 16 * mt + c;
+                const int c0 = 32 * ks + 4 * g;
+                const uint2 wlo = *reinterpret_cast<const uint2*>(sStW + r * KS + c0);
+                const uint2 whi = *reinterpret_cast<const uint2*>(sStW + r * KS + c0 + 16);
+                const uint2 qlo = *reinterpret_cast<const uint2*>(sStQ + r * 128 + c0);
+                const uint2 qhi = *reinterpret_cast<const uint2*>(sStQ + r * 128 + c0 + 16);
+                const int blk = (mt * 4 + ks) * 64 + lane;
+                *reinterpret_cast<uint4*>(rec + R_NEGW + blk * 16) = make_uint4(wlo.x, wlo.y, whi.x, whi.y);
+                *reinterpret_cast<uint4*>(rec + R_QP + blk * 16) = make_uint4(qlo.x, qlo.y, qhi.x, qhi.y);
+            }
+            const int t = wave;
+            const int ch = 16 * t + c;
+            const float glast = sG[63 * GS + ch];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                float kv[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int s2 = 32 * ks + perm(g, e);
+                    kv[e] = __expf(glast - sG[s2 * GS + ch]) * bfv(sK + s2 * KS + ch);
+                }
+                uint4 p;
+                p.x = pack_bf16x2(kv[0], kv[1]);
+                p.y = pack_bf16x2(kv[2], kv[3]);
+                p.z = pack_bf16x2(kv[4], kv[5]);
+                p.w = pack_bf16x2(kv[6], kv[7]);
+                *reinterpret_cast<uint4*>(rec + R_KHT + ((t * 2 + ks) * 64 + lane) * 16) = p;
+            }
+            if (tid < 128) reinterpret_cast<float*>(rec + R_GAM)[tid] = expf(sG[63 * GS + tid]);
+        }
+        lds_barrier();  // every LDS buffer is free for the next unit
+        if (more) stage_inputs(nxt, tid);
     }
 }
 
@@ -722,9 +881,9 @@ __global__ __launch_bounds__(kStateThreads) void mfma_state_kernel(MfmaK<GT> a) 
 }
 
 template <typename GT>
-hipError_t launch_typed(const PrefillArgs& a, hipStream_t s, int32_t* base, char* recs) {
+hipError_t launch_typed(const PrefillArgs& a, hipStream_t s, int32_t* base, const SlotInfo* slot_info, char* recs) {
     MfmaK<GT> k;
-    k.T = a.T; k.H = a.H; k.N = a.N; k.cu = a.cu; k.base = base;
+    k.T = a.T; k.H = a.H; k.N = a.N; k.cu = a.cu; k.base = base; k.slot_info = slot_info;
     k.q = static_cast<const bf16*>(a.q); k.k = static_cast<const bf16*>(a.k);
     k.v = static_cast<const bf16*>(a.v); k.z = static_cast<const bf16*>(a.z);
     k.la = static_cast<const GT*>(a.la); k.beta = static_cast<const GT*>(a.beta);
@@ -737,15 +896,18 @@ hipError_t launch_typed(const PrefillArgs& a, hipStream_t s, int32_t* base, char
                                            hipFuncAttributeMaxDynamicSharedMemorySize,
                                            static_cast<int>(kIntraLds));
         if (e != hipSuccess) return e;
+        // persistent grid: one workgroup per CU (the LDS footprint allows one)
+        int dev = 0, cus = 0;
+        e = hipGetDevice(&dev);
+        if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        const int64_t grid = min(slots * a.H, static_cast<int64_t>(max(cus, 1)));
         LaunchTimer timer("mfma_intra", s);
-        hipLaunchKernelGGL((mfma_intra_kernel<GT>), dim3(static_cast<unsigned>(slots), a.H), dim3(kIntraThreads),
+        hipLaunchKernelGGL((mfma_intra_kernel<GT>), dim3(static_cast<unsigned>(grid)), dim3(kIntraThreads),
                            kIntraLds, s, k);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    const void* fn = a.z ? reinterpret_cast<const void*>(&mfma_state_kernel<GT, true>)
-                         : reinterpret_cast<const void*>(&mfma_state_kernel<GT, false>);
-    (void)fn;
     const int64_t blocks = (k.groups + 7) / 8 * 16;
     LaunchTimer timer("mfma_state", s);
     if (a.z) {
@@ -764,8 +926,10 @@ bool mfma_prefill_supports(int dk, int dv, DT x) { return dk == 128 && dv == 128
 
 size_t mfma_record_bytes() { return REC_BYTES; }
 
-hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t s, int32_t* base, char* recs) {
-    return a.gate == DT::BF16 ? launch_typed<bf16>(a, s, base, recs) : launch_typed<float>(a, s, base, recs);
+hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t s, int32_t* base, const SlotInfo* slot_info,
+                               char* recs) {
+    return a.gate == DT::BF16 ? launch_typed<bf16>(a, s, base, slot_info, recs)
+                              : launch_typed<float>(a, s, base, slot_info, recs);
 }
 
 }  // namespace kda

@@ -137,6 +137,8 @@ size_t kda_prefill_workspace_bytes(int64_t T_tot, int32_t N, int32_t H, int32_t 
  *   out         [T_tot, H, dv] (x_dtype);
  *   workspace   device scratch of at least kda_prefill_workspace_bytes()
  *               bytes, 256-byte aligned; contents on entry are ignored.
+ * Sizes: H x (T_tot/64 + 1 + N) must stay below 2^32 (KDA_ERR_UNSUPPORTED
+ * otherwise).
  */
 int kda_prefill_chunked(int64_t T_tot, int32_t H, int32_t dk, int32_t dv,
                         const int32_t* cu_seqlens, int32_t N,
