@@ -29,6 +29,8 @@
 // Phase 2 (mfma_state_kernel): per (sequence, head, half of the state
 //  columns), compute waves carry the fp32 state in registers through the
 //  chunks in order while copy waves stream each chunk's factors into LDS.
+#include <stdlib.h>
+
 #include "kda_prefill_common.h"
 #include "kda_prefill_mfma.h"
 #include "kda_profile.h"
@@ -646,32 +648,47 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
 // phase 2
 // ---------------------------------------------------------------------------
 
-// One workgroup per (sequence, head, half of the state columns), with two
-// roles.  Four compute waves (wave w owns the 16 state columns of slice
-// 4*half + w) touch only LDS inside the chunk loop: they read the chunk's
-// factors and write the gated output tile to an LDS staging area.  Four
-// memory waves do all global traffic: they copy what a chunk needs into one
-// of two LDS buffers with global_load_lds_dwordx4 and store the staged output
-// as whole 128-byte row pieces.  A chunk is copied in two parts: the part
-// the first half of a step reads (-W, Q', this half's U~ and M U~ tiles, the
-// gate logits: 56 KB) as soon as the compute waves are done with it two
-// chunks back, and the part the second half reads (K^T, gamma: 16.5 KB) one
-// step ahead.  The memory waves issue the same operations every step, so a
-// fixed count (vmcnt) tells when a part has landed while later ones stay in
-// flight (vector memory operations of one wave retire in issue order).
-constexpr int kStateThreads = 512;
-// LDS buffer layout, bytes.  The first 48 KB mirror the record's first 48 KB.
-constexpr int B_NEGW = 0;       // -W, 16 KB
-constexpr int B_QP = 16384;     // Q', 16 KB
-constexpr int B_KHT = 32768;    // K^T, 16 KB
-constexpr int B_UT = 49152;     // U~ of the half's four slices, [4 s][4 m][64 lanes][4], 8 KB
-constexpr int B_OI = 57344;     // M U~ of the half's four slices, same layout, 8 KB
-constexpr int B_Z = 65536;      // gate logits, [64 tokens][64 columns] bf16, 16-byte pieces swizzled
-constexpr int B_GAM = 73728;    // gamma, fp32 [128]
-constexpr int B_BYTES = 74240;
-// operations one memory wave issues per part (wave 0 issues one more in the
-// second part: gamma) and per output tile
-constexpr int kPartA = 14, kPartB = 4, kStores = 2;
+// One workgroup per (sequence, head, group of SB = NS x SW 16-column slices
+// of the state), with two roles.  NS compute waves each own SW slices (the
+// state columns of slices SB*part + SW*w .. + SW-1, in registers): inside the
+// chunk loop they touch only LDS, reading the chunk's factors (each factor
+// read serves all SW slices of the wave) and writing the gated output tile
+// to an LDS staging area.  Four memory waves do all global traffic: they copy
+// what a chunk needs into one of two LDS buffers with global_load_lds_dwordx4
+// and store the staged output as whole row pieces.  A chunk is copied in two
+// parts: the part the first half of a step reads (-W, Q', the group's U~ and
+// M U~ tiles, its gate logits) as soon as the compute waves are done with it
+// two chunks back, and the part the second half reads (K^T, gamma) one step
+// ahead.  Every memory wave issues the same number of operations every step
+// (a wave with no piece of some tile copies into a dump area), so a fixed
+// count (vmcnt) tells when a part has landed while later ones stay in flight:
+// vector memory operations of one wave retire in issue order.
+// Smaller groups spread a head over more CUs, which suits few (sequence,
+// head) pairs; larger ones share each copied factor among more columns.
+template <int SB>
+struct StateCfg {
+    static_assert(SB == 1 || SB == 2 || SB == 4, "1, 2 or 4 slices per workgroup");
+    static constexpr int kRowBytes = 32 * SB;             // one token row of the group's columns, bf16
+    static constexpr int kPieces = 2 * SB;                // 1 KB pieces of each group tile (U~, M U~, z)
+    static constexpr int kPiecesPerWave = (kPieces + 3) / 4;
+    // LDS buffer layout, bytes.  The first 48 KB mirror the record's first 48 KB.
+    static constexpr int B_NEGW = 0;                      // -W, 16 KB
+    static constexpr int B_QP = 16384;                    // Q', 16 KB
+    static constexpr int B_KHT = 32768;                   // K^T, 16 KB
+    static constexpr int B_UT = 49152;                    // U~ of the group's slices, [SB s][4 m][64][4]
+    static constexpr int B_OI = B_UT + 1024 * kPieces;    // M U~, same layout
+    static constexpr int B_Z = B_OI + 1024 * kPieces;     // gate logits [64 tokens][kRowBytes], swizzled
+    static constexpr int B_GAM = B_Z + 1024 * kPieces;    // gamma, fp32 [128]
+    static constexpr int B_DUMP = B_GAM + 512;            // target of the filler copies, never read
+    static constexpr int B_BYTES = B_DUMP + 1024;
+    // operations one memory wave issues per part (wave 0 issues one more in
+    // the second part: gamma) and per output tile
+    static constexpr int kPartA = 8 + 3 * kPiecesPerWave;
+    static constexpr int kPartB = 4;
+    static constexpr int kStores = (SB + 1) / 2;           // 16 rows of kRowBytes per wave (half
+                                                           // the lanes idle when SB = 1)
+    static constexpr size_t kLds = 2 * static_cast<size_t>(B_BYTES) + 64 * kRowBytes;
+};
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -679,10 +696,11 @@ __device__ __forceinline__ void lds_copy16(const void* gsrc, char* lds_dst) {
     __builtin_amdgcn_global_load_lds(gsrc, (lds_void*)(lds_dst), 16, 0, 0);
 }
 
-// Tiles of 64 rows x 128 bytes (gate logits, staged output): piece q (16
-// bytes) of row r is kept at slot q ^ (r & 7), so reads and writes that walk
-// 16 rows of one column group spread over all banks.
-__device__ __forceinline__ int tile_slot(int r, int q) { return q ^ (r & 7); }
+// Tiles of 64 token rows x (2 SB) 16-byte pieces (gate logits, staged
+// output): piece q of row r is kept at slot q ^ (r mod 2 SB), so reads and
+// writes that walk 16 rows of one column group spread over the banks.
+template <int SB>
+__device__ __forceinline__ int tile_slot(int r, int q) { return q ^ (r & (2 * SB - 1)); }
 
 // s_waitcnt with vmcnt(n) only (lgkmcnt and expcnt left at their maxima)
 template <int n>
@@ -693,17 +711,24 @@ __device__ __forceinline__ void wait_vmcnt() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-template <typename GT, bool kGate>
-__global__ __launch_bounds__(kStateThreads) void mfma_state_kernel(MfmaK<GT> a) {
-    __shared__ __align__(16) char buf0[B_BYTES];
-    __shared__ __align__(16) char buf1[B_BYTES];
-    __shared__ __align__(16) char stage[64 * 128];  // gated output tile, bf16, swizzled
-    // blockIdx -> (sequence, head, half): both halves of a (sequence, head)
-    // land on one XCD (workgroups are dealt round-robin over the 8 XCDs), so
-    // the chunk records they share are read through one L2
+template <typename GT, bool kGate, int NS, int SW>
+__global__ __launch_bounds__(64 * (NS + 4)) void mfma_state_kernel(MfmaK<GT> a) {
+    constexpr int SB = NS * SW;
+    using C = StateCfg<SB>;
+    constexpr int P = 8 / SB;            // slice groups per head
+    constexpr int RB = C::kRowBytes;
+    constexpr int PR = 2 * SB;           // 16-byte pieces per tile row
+    constexpr int ROWS_PER_PIECE = 1024 / RB;
+    extern __shared__ __align__(16) char smem[];
+    char* const buf0 = smem;
+    char* const buf1 = smem + C::B_BYTES;
+    char* const stage = smem + 2 * C::B_BYTES;  // gated output tile, bf16 [64][RB], swizzled
+    // blockIdx -> (sequence, head, part): all parts of a (sequence, head) land
+    // on one XCD (workgroups are dealt round-robin over the 8 XCDs), so the
+    // chunk records they share are read through one L2
     const int bid = blockIdx.x;
-    const int xcd = bid & 7, half = (bid >> 3) & 1;
-    const int64_t grp = static_cast<int64_t>(bid >> 4) * 8 + xcd;
+    const int xcd = bid & 7, part = (bid >> 3) % P;
+    const int64_t grp = static_cast<int64_t>((bid >> 3) / P) * 8 + xcd;
     if (grp >= a.groups) return;
     const int H = a.H;
     const int n = static_cast<int>(grp / H), h = static_cast<int>(grp % H);
@@ -718,10 +743,10 @@ __global__ __launch_bounds__(kStateThreads) void mfma_state_kernel(MfmaK<GT> a) 
     };
     auto buf_of = [&](int j) { return (j & 1) ? buf1 : buf0; };
 
-    if (wave >= 4) {
+    if (wave >= NS) {
         // ---- memory waves
         if (nch == 0) return;
-        const int wm = wave - 4;
+        const int wm = wave - NS;
         // part A of chunk min(j, nch-1): -W, Q', U~, M U~ and gate logits
         // (past the end it copies the last chunk again into the free buffer
         // the index selects, so that every step issues the same operations)
@@ -734,23 +759,24 @@ __global__ __launch_bounds__(kStateThreads) void mfma_state_kernel(MfmaK<GT> a) 
                 const int b = wm + 4 * i;
                 lds_copy16(rp + b * 1024 + lane * 16, buf + b * 1024);
             }
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int b = wm + 4 * i;
-                lds_copy16(rp + R_UT + half * 8192 + b * 1024 + lane * 16, buf + B_UT + b * 1024);
-                lds_copy16(rp + R_OI + half * 8192 + b * 1024 + lane * 16, buf + B_OI + b * 1024);
-            }
             const int Lc = chunk_len(j);
             const int64_t tb = sb + static_cast<int64_t>(j) * kChunk;
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
+            for (int i = 0; i < C::kPiecesPerWave; ++i) {
                 const int b = wm + 4 * i;
-                const int r = 8 * b + (lane >> 3);
-                const int q = tile_slot(r, lane & 7);  // the slot map is its own inverse
+                const bool real = b < C::kPieces;
+                const int bb = real ? b : 0;
+                const char* ut = rp + R_UT + part * (1024 * C::kPieces) + bb * 1024 + lane * 16;
+                const char* oi = rp + R_OI + part * (1024 * C::kPieces) + bb * 1024 + lane * 16;
+                lds_copy16(ut, real ? buf + C::B_UT + b * 1024 : buf + C::B_DUMP);
+                lds_copy16(oi, real ? buf + C::B_OI + b * 1024 : buf + C::B_DUMP);
+                const int r = bb * ROWS_PER_PIECE + lane / PR;
+                const int q = tile_slot<SB>(r, lane % PR);  // the slot map is its own inverse
                 // without a gate the tile is never read; copying keeps the count fixed
-                const bf16* src = kGate ? a.z + ((tb + min(r, Lc - 1)) * H + h) * 128 + 64 * half + 8 * q
-                                        : reinterpret_cast<const bf16*>(rp + R_UT + b * 1024 + lane * 16);
-                lds_copy16(src, buf + B_Z + b * 1024);
+                const void* zs = kGate ? static_cast<const void*>(a.z + ((tb + min(r, Lc - 1)) * H + h) * 128 +
+                                                                  16 * SB * part + 8 * q)
+                                       : static_cast<const void*>(ut);
+                lds_copy16(zs, (real && kGate) ? buf + C::B_Z + b * 1024 : buf + C::B_DUMP);
             }
         };
         // part B of chunk min(j, nch-1): K^T and gamma
@@ -763,7 +789,7 @@ __global__ __launch_bounds__(kStateThreads) void mfma_state_kernel(MfmaK<GT> a) 
                 const int b = 32 + wm + 4 * i;
                 lds_copy16(rp + b * 1024 + lane * 16, buf + b * 1024);
             }
-            if (wm == 0 && lane < 32) lds_copy16(rp + R_GAM + lane * 16, buf + B_GAM);
+            if (wm == 0 && lane < 32) lds_copy16(rp + R_GAM + lane * 16, buf + C::B_GAM);
         };
         // issue order per step j: [A_j] B(j+1) [M_j] stores(j), A(j+2).
         // Before A_j part A of chunk j must be in; after it came B(j),
@@ -771,26 +797,31 @@ __global__ __launch_bounds__(kStateThreads) void mfma_state_kernel(MfmaK<GT> a) 
         // after it came stores(j-1), A(j+1) and B(j+1).  (Wave 0's gamma copy
         // is left out of the counts: it waits for one operation more than
         // needed.)  In step 0 there were no stores(-1).
+        constexpr int kA = C::kPartA, kB = C::kPartB, kS = C::kStores;
         issue_a(0);
         issue_b(0);
         issue_a(1);
-        const int wr = 16 * wm + (lane >> 3), wq = lane & 7;  // store role: rows wr, wr + 8
+        // store role: rows 16 wm .. 16 wm + 15, ROWS_PER_PIECE of them per
+        // instruction
+        const int wq = lane % PR;
         for (int j = 0; j < nch; ++j) {
-            if (j == 0) wait_vmcnt<kPartB + kPartA>(); else wait_vmcnt<kPartB + kStores + kPartA>();
+            if (j == 0) wait_vmcnt<kB + kA>(); else wait_vmcnt<kB + kS + kA>();
             lds_barrier();  // A_j: part A of chunk j is in LDS; part B of chunk j+1 may be copied
             issue_b(j + 1);
-            if (j == 0) wait_vmcnt<kPartA + kPartB>(); else wait_vmcnt<kStores + kPartA + kPartB>();
+            if (j == 0) wait_vmcnt<kA + kB>(); else wait_vmcnt<kS + kA + kB>();
             lds_barrier();  // M_j: part B of chunk j is in; the output tile of chunk j is staged
             const int Lc = chunk_len(j);
             const int64_t tb = sb + static_cast<int64_t>(j) * kChunk;
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int r = wr + 8 * i;
-                const uint4 v = *reinterpret_cast<const uint4*>(stage + r * 128 + wq * 16);
-                const int q = tile_slot(r, wq);
+            for (int i = 0; i < kS; ++i) {
+                const int rl = i * ROWS_PER_PIECE + lane / PR;  // row within the wave's 16
+                const int r = 16 * wm + min(rl, 15);
+                const uint4 v = *reinterpret_cast<const uint4*>(stage + r * RB + wq * 16);
+                const int q = tile_slot<SB>(r, wq);
                 // rows past the end exist only in a sequence's last chunk,
                 // after which no counted wait follows
-                if (r < Lc) *reinterpret_cast<uint4*>(a.out + ((tb + r) * H + h) * 128 + 64 * half + 8 * q) = v;
+                if (rl < 16 && r < Lc)
+                    *reinterpret_cast<uint4*>(a.out + ((tb + r) * H + h) * 128 + 16 * SB * part + 8 * q) = v;
             }
             issue_a(j + 2);
         }
@@ -798,86 +829,140 @@ __global__ __launch_bounds__(kStateThreads) void mfma_state_kernel(MfmaK<GT> a) 
         return;
     }
 
-    // ---- compute waves
-    const int sl = 4 * half + wave;
-    const int col = 16 * sl + c;
-    f32x4 S[8];  // S[16t + 4g + i][col]
+    // ---- compute waves: slices SW*wave .. SW*wave + SW-1 of the group
+    f32x4 S[SW][8];  // S[s][t][i] = state[16t + 4g + i][16 (SB part + SW wave + s) + c]
     const int64_t sidx = grp * (128 * 128);
-    if (a.S0 != nullptr) {  // one uniform branch: all 32 loads in flight together
+    const int col0 = 16 * (SB * part + SW * wave) + c;
+    if (a.S0 != nullptr) {  // one uniform branch: all loads in flight together
 #pragma unroll
-        for (int t = 0; t < 8; ++t)
+        for (int sw = 0; sw < SW; ++sw)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) S[t][i] = a.S0[sidx + (16 * t + 4 * g + i) * 128 + col];
+            for (int t = 0; t < 8; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) S[sw][t][i] = a.S0[sidx + (16 * t + 4 * g + i) * 128 + col0 + 16 * sw];
     } else {
 #pragma unroll
-        for (int t = 0; t < 8; ++t) S[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int sw = 0; sw < SW; ++sw)
+#pragma unroll
+            for (int t = 0; t < 8; ++t) S[sw][t] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
     for (int j = 0; j < nch; ++j) {
         const char* cur = buf_of(j);
         lds_barrier();  // A_j: part A of chunk j is in LDS; the staging tile is free
 
-        bf16x8 Sb[4];
+        bf16x8 Sb[SW][4];
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) Sb[ks] = to_bf16x8(S[2 * ks], S[2 * ks + 1]);
+        for (int sw = 0; sw < SW; ++sw)
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) Sb[sw][ks] = to_bf16x8(S[sw][2 * ks], S[sw][2 * ks + 1]);
         // U = U~ - W S, and the output transposed: O^T = (M U~)^T + S^T Q'^T
         // (the state operand and the Q' operand swap roles): lane (g, c) holds
-        // token 16 mt + c, columns 16 sl + 4 g .. + 3
-        f32x4 U[4];
+        // token 16 mt + c, columns 16 slice + 4 g .. + 3
+        f32x4 U[SW][4];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
-            const uint2 up = *reinterpret_cast<const uint2*>(cur + B_UT + ((wave * 4 + mt) * 64 + lane) * 8);
-            const uint2 op = *reinterpret_cast<const uint2*>(cur + B_OI + ((wave * 4 + mt) * 64 + lane) * 8);
-            f32x4 u = {__uint_as_float(up.x << 16), __uint_as_float(up.x & 0xffff0000u),
-                       __uint_as_float(up.y << 16), __uint_as_float(up.y & 0xffff0000u)};
-            f32x4 o = {__uint_as_float(op.x << 16), __uint_as_float(op.x & 0xffff0000u),
-                       __uint_as_float(op.y << 16), __uint_as_float(op.y & 0xffff0000u)};
+            f32x4 o[SW];
+#pragma unroll
+            for (int sw = 0; sw < SW; ++sw) {
+                const int ls = SW * wave + sw;  // slice within the group
+                const uint2 up = *reinterpret_cast<const uint2*>(cur + C::B_UT + ((ls * 4 + mt) * 64 + lane) * 8);
+                const uint2 op = *reinterpret_cast<const uint2*>(cur + C::B_OI + ((ls * 4 + mt) * 64 + lane) * 8);
+                U[sw][mt] = f32x4{__uint_as_float(up.x << 16), __uint_as_float(up.x & 0xffff0000u),
+                                  __uint_as_float(up.y << 16), __uint_as_float(up.y & 0xffff0000u)};
+                o[sw] = f32x4{__uint_as_float(op.x << 16), __uint_as_float(op.x & 0xffff0000u),
+                              __uint_as_float(op.y << 16), __uint_as_float(op.y & 0xffff0000u)};
+            }
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 const int blk = (mt * 4 + ks) * 64 + lane;
-                const bf16x8 wa = *reinterpret_cast<const bf16x8*>(cur + B_NEGW + blk * 16);
-                const bf16x8 qa = *reinterpret_cast<const bf16x8*>(cur + B_QP + blk * 16);
-                u = mfma(wa, Sb[ks], u);
-                o = mfma(Sb[ks], qa, o);
-            }
-            U[mt] = u;
-            // columns 16 wave + 4 g .. + 3 of the half: piece 2 wave + g/2, bytes 8 (g & 1)
-            const int r = 16 * mt + c;
-            const int off = r * 128 + tile_slot(r, 2 * wave + (g >> 1)) * 16 + 8 * (g & 1);
-            if (kGate) {
-                const uint2 zp = *reinterpret_cast<const uint2*>(cur + B_Z + off);
-                const float zf[4] = {__uint_as_float(zp.x << 16), __uint_as_float(zp.x & 0xffff0000u),
-                                     __uint_as_float(zp.y << 16), __uint_as_float(zp.y & 0xffff0000u)};
+                const bf16x8 wa = *reinterpret_cast<const bf16x8*>(cur + C::B_NEGW + blk * 16);
+                const bf16x8 qa = *reinterpret_cast<const bf16x8*>(cur + C::B_QP + blk * 16);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) o[i] *= sigmoid_fast(zf[i]);
+                for (int sw = 0; sw < SW; ++sw) {
+                    U[sw][mt] = mfma(wa, Sb[sw][ks], U[sw][mt]);
+                    o[sw] = mfma(Sb[sw][ks], qa, o[sw]);
+                }
             }
-            *reinterpret_cast<uint2*>(stage + off) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+#pragma unroll
+            for (int sw = 0; sw < SW; ++sw) {
+                // columns 16 ls + 4 g .. + 3 of the group: piece 2 ls + g/2, bytes 8 (g & 1)
+                const int ls = SW * wave + sw;
+                const int r = 16 * mt + c;
+                const int off = r * RB + tile_slot<SB>(r, 2 * ls + (g >> 1)) * 16 + 8 * (g & 1);
+                if (kGate) {
+                    const uint2 zp = *reinterpret_cast<const uint2*>(cur + C::B_Z + off);
+                    const float zf[4] = {__uint_as_float(zp.x << 16), __uint_as_float(zp.x & 0xffff0000u),
+                                         __uint_as_float(zp.y << 16), __uint_as_float(zp.y & 0xffff0000u)};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) o[sw][i] *= sigmoid_fast(zf[i]);
+                }
+                *reinterpret_cast<uint2*>(stage + off) =
+                    make_uint2(pack_bf16x2(o[sw][0], o[sw][1]), pack_bf16x2(o[sw][2], o[sw][3]));
+            }
         }
         lds_barrier();  // M_j: the output tile is staged; part B of chunk j is in LDS
         // S <- Diag(gamma) S + K^T U
-        bf16x8 Ub[2];
+        bf16x8 Ub[SW][2];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) Ub[ks] = to_bf16x8(U[2 * ks], U[2 * ks + 1]);
+        for (int sw = 0; sw < SW; ++sw)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) Ub[sw][ks] = to_bf16x8(U[sw][2 * ks], U[sw][2 * ks + 1]);
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-            const float4 gm = *reinterpret_cast<const float4*>(cur + B_GAM + (16 * t + 4 * g) * 4);
-            S[t][0] *= gm.x;
-            S[t][1] *= gm.y;
-            S[t][2] *= gm.z;
-            S[t][3] *= gm.w;
+            const float4 gm = *reinterpret_cast<const float4*>(cur + C::B_GAM + (16 * t + 4 * g) * 4);
+#pragma unroll
+            for (int sw = 0; sw < SW; ++sw) {
+                S[sw][t][0] *= gm.x;
+                S[sw][t][1] *= gm.y;
+                S[sw][t][2] *= gm.z;
+                S[sw][t][3] *= gm.w;
+            }
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                const bf16x8 ka = *reinterpret_cast<const bf16x8*>(cur + B_KHT + ((t * 2 + ks) * 64 + lane) * 16);
-                S[t] = mfma(ka, Ub[ks], S[t]);
+                const bf16x8 ka = *reinterpret_cast<const bf16x8*>(cur + C::B_KHT + ((t * 2 + ks) * 64 + lane) * 16);
+#pragma unroll
+                for (int sw = 0; sw < SW; ++sw) S[sw][t] = mfma(ka, Ub[sw][ks], S[sw][t]);
             }
         }
     }
     if (a.S_out) {
 #pragma unroll
-        for (int t = 0; t < 8; ++t)
+        for (int sw = 0; sw < SW; ++sw)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) a.S_out[sidx + (16 * t + 4 * g + i) * 128 + col] = S[t][i];
+            for (int t = 0; t < 8; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) a.S_out[sidx + (16 * t + 4 * g + i) * 128 + col0 + 16 * sw] = S[sw][t][i];
     }
+}
+
+template <typename GT, bool kGate, int NS, int SW>
+hipError_t launch_state(const MfmaK<GT>& k, hipStream_t s) {
+    using C = StateCfg<NS * SW>;
+    constexpr int P = 8 / (NS * SW);
+    const void* fn = reinterpret_cast<const void*>(&mfma_state_kernel<GT, kGate, NS, SW>);
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(C::kLds));
+    if (e != hipSuccess) return e;
+    const int64_t blocks = (k.groups + 7) / 8 * 8 * P;
+    hipLaunchKernelGGL((mfma_state_kernel<GT, kGate, NS, SW>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(64 * (NS + 4)), C::kLds, s, k);
+    return hipGetLastError();
+}
+
+// Workgroup shape of the state pass.  Few (sequence, head) pairs: spread
+// each head over 8 workgroups of one compute wave (one 16-column slice), so
+// every CU takes part.  Many: one workgroup of four compute waves per half
+// head, so each copied factor serves four slices.  KDA_STATE_SHAPE=1 or 4 in
+// the environment forces the number of compute waves (the tests use it to
+// cover both).
+template <typename GT, bool kGate>
+hipError_t launch_state_for(const MfmaK<GT>& k, hipStream_t s, int cus) {
+    int ns = k.groups * 8 <= cus ? 1 : 4;
+    if (const char* env = getenv("KDA_STATE_SHAPE")) {
+        const int f = atoi(env);
+        if (f == 1 || f == 4) ns = f;
+    }
+    return ns == 1 ? launch_state<GT, kGate, 1, 1>(k, s) : launch_state<GT, kGate, 4, 1>(k, s);
 }
 
 template <typename GT>
@@ -891,33 +976,25 @@ hipError_t launch_typed(const PrefillArgs& a, hipStream_t s, int32_t* base, cons
     k.groups = static_cast<int64_t>(a.N) * a.H;
     const int64_t slots = chunk_slots_bound(a.T, a.N);
     k.slots = slots;
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    cus = max(cus, 1);
     if (a.T > 0) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&mfma_intra_kernel<GT>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           static_cast<int>(kIntraLds));
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&mfma_intra_kernel<GT>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kIntraLds));
         if (e != hipSuccess) return e;
         // persistent grid: one workgroup per CU (the LDS footprint allows one)
-        int dev = 0, cus = 0;
-        e = hipGetDevice(&dev);
-        if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-        if (e != hipSuccess) return e;
-        const int64_t grid = min(slots * a.H, static_cast<int64_t>(max(cus, 1)));
+        const int64_t grid = min(slots * a.H, static_cast<int64_t>(cus));
         LaunchTimer timer("mfma_intra", s);
         hipLaunchKernelGGL((mfma_intra_kernel<GT>), dim3(static_cast<unsigned>(grid)), dim3(kIntraThreads),
                            kIntraLds, s, k);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    const int64_t blocks = (k.groups + 7) / 8 * 16;
     LaunchTimer timer("mfma_state", s);
-    if (a.z) {
-        hipLaunchKernelGGL((mfma_state_kernel<GT, true>), dim3(static_cast<unsigned>(blocks)), dim3(kStateThreads),
-                           0, s, k);
-    } else {
-        hipLaunchKernelGGL((mfma_state_kernel<GT, false>), dim3(static_cast<unsigned>(blocks)), dim3(kStateThreads),
-                           0, s, k);
-    }
-    return hipGetLastError();
+    return a.z ? launch_state_for<GT, true>(k, s, cus) : launch_state_for<GT, false>(k, s, cus);
 }
 
 }  // namespace
