@@ -1,10 +1,12 @@
 #!/usr/bin/env python3
 """Benchmark of libkda on one MI355X.
 
-One step = one pass of the whole prefill path over one batch: the fused
-preprocess (conv4 + L2 norm + gates) and the chunked prefill with the output
-gate, on the 4096-token, 32-head, d = 128 bf16 layer (``layer_t4k``), inputs
-already resident in HBM.  ``value`` is prefill tokens/s over the K timed steps.
+One step = one pass of the whole prefill path over one batch: short conv,
+L2 norm and gates, the chunked prefill and the output gate, as one
+``kda_prefill_layer`` call (the preprocess runs inside the chunk kernel), on
+the 4096-token, 32-head, d = 128 bf16 layer (``layer_t4k``), inputs already
+resident in HBM.  The same work as two calls (``kda_preprocess`` then
+``kda_prefill_chunked``) is timed beside it for reference.  ``value`` is prefill tokens/s over the K timed steps.
 
 The decode step (256 sequences x 32 heads x 128^2 fp32 state, in place) is
 timed in its own loop and reported under ``decode`` in GB/s of algorithmic
@@ -90,6 +92,8 @@ def prefill_kernel_bytes(name, w, x, g, rec, has_s0, has_gate):
         reads = th * (x * (2 * dk + dv) + x * dk + x) + H * (2 * dk + dv) * 4 * x
         writes = th * (x * (2 * dk + dv) + 4 * dk + 4)
         return reads + writes
+    if name == "mfma_prep_intra":  # raw q, k, v, decay and write logits in; records out
+        return th * (x * (2 * dk + dv) + x * dk + x) + chunks * rec
     if name.endswith("intra"):
         return th * (x * (2 * dk + dv) + g * dk + g) + chunks * rec
     if name.endswith("state"):
@@ -152,11 +156,16 @@ def bench_prefill(args):
     x_code = 1 if w.x_dtype == "bf16" else 0
     ws = torch.empty(kda.kda_prefill_workspace_bytes(T, N, H, dk, dv, x_code), dtype=torch.uint8, device="cuda")
 
-    def step():
+    def step_two_calls():
         q, k, v, la, beta = kda.kda_preprocess(t["q_in"], t["k_in"], t["v_in"], t["w_q"], t["w_k"], t["w_v"],
                                                t["g"], t["b"], H, dk, dv, cu_seqlens=cu, out=pre_out)
         kda.kda_prefill_chunked(q, k, v, la, beta, out_gate=z, initial_state=S0, final_state=S_out,
                                 cu_seqlens=cu, workspace=ws, out=out)
+
+    def step():
+        kda.kda_prefill_layer(t["q_in"], t["k_in"], t["v_in"], t["w_q"], t["w_k"], t["w_v"], t["g"], t["b"],
+                              H, dk, dv, out_gate=z, initial_state=S0, final_state=S_out, cu_seqlens=cu,
+                              workspace=ws, out=out)
 
     for _ in range(args.warmup):
         step()
@@ -178,6 +187,16 @@ def bench_prefill(args):
     _lib.profile_enable(False)
     times = _lib.profile_collect()
 
+    # the same work as two calls (preprocess, then chunked prefill), for reference
+    for _ in range(args.warmup):
+        step_two_calls()
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for _ in range(args.steps):
+        step_two_calls()
+    torch.cuda.synchronize()
+    elapsed_two = time.perf_counter() - t2
+
     xb = 2 if w.x_dtype == "bf16" else 4
     rec = record_bytes(kda, T, N, H, dk, dv, x_code)
     kernels = {}
@@ -190,7 +209,7 @@ def bench_prefill(args):
     dn, dms = times[dom]
     roof = roofline(dom, kernels[dom]["algorithmic_bytes"], dms / dn)
     return {"w": w, "inp": inp, "elapsed": elapsed, "elapsed_events": elapsed_ev, "kernels": kernels,
-            "roofline": roof}
+            "roofline": roof, "elapsed_two_calls": elapsed_two}
 
 
 def bench_decode(args):
@@ -300,10 +319,11 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "T": w.T_tot, "N": w.N, "H": w.H, "dk": w.dk, "dv": w.dv,
                    "chunk": 64, "out_gate": w.out_gate, "state": "fp32",
-                   "step": "kda_preprocess + kda_prefill_chunked"},
+                   "step": "kda_prefill_layer (short conv, L2 norm, gates, chunked prefill, output gate)"},
         "roofline": res["roofline"],
         "kernels": res["kernels"],
         "ms_per_step_with_kernel_events": round(res["elapsed_events"] / args.steps * 1e3, 4),
+        "ms_per_step_two_calls": round(res["elapsed_two_calls"] / args.steps * 1e3, 4),
     }
     line["decode"] = bench_decode(args)
     if args.copy_calibration:

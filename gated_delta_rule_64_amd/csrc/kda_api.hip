@@ -213,6 +213,69 @@ int kda_prefill_chunked(int64_t T_tot, int32_t H, int32_t dk, int32_t dv, const 
     return ok();
 }
 
+int kda_prefill_layer(int64_t T_tot, int32_t H, int32_t dk, int32_t dv, const int32_t* cu_seqlens, int32_t N,
+                      int32_t x_dtype, const void* q_in, const void* k_in, const void* v_in, const void* w_q,
+                      const void* w_k, const void* w_v, const void* g_alpha, const void* b_beta,
+                      float* conv_state, const void* out_gate, const float* initial_state, float* final_state,
+                      void* out, void* workspace, size_t workspace_bytes, void* stream) {
+    int st = check_sizes(T_tot, H, dk, dv, N);
+    if (st != KDA_OK) return st;
+    if (!valid_dtype(x_dtype)) return fail(KDA_ERR_INVALID_ARGUMENT, "x_dtype=%d is not KDA_F32 or KDA_BF16", x_dtype);
+    if (!kda::layer_fused_supported(dk, dv, static_cast<kda::DT>(x_dtype)))
+        return fail(KDA_ERR_UNSUPPORTED, "kda_prefill_layer covers dk = dv = 128 with bf16 inputs (got dk=%d, dv=%d, "
+                    "x_dtype=%d); use kda_preprocess + kda_prefill_chunked", dk, dv, x_dtype);
+    if ((T_tot / 64 + 1 + N) * static_cast<int64_t>(H) > 0xffffffffll)
+        return fail(KDA_ERR_UNSUPPORTED, "H x (T_tot/64 + N) = %lld chunk units exceed 2^32 - 1",
+                    static_cast<long long>((T_tot / 64 + 1 + N) * static_cast<int64_t>(H)));
+    if (cu_seqlens == nullptr && N != 1) return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens is NULL but N=%d", N);
+    if (cu_seqlens != nullptr && (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens is not 4-byte aligned");
+    const size_t need = kda_prefill_workspace_bytes(T_tot, N, H, dk, dv, x_dtype);
+    if (workspace_bytes < need)
+        return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "workspace_bytes=%zu < %zu needed", workspace_bytes, need);
+    if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "workspace is NULL or not 256-byte aligned");
+    const size_t xs = dsize(x_dtype);
+    const size_t T = static_cast<size_t>(T_tot);
+    const size_t qk = T * H * dk, vv = T * H * dv;
+    const size_t state = static_cast<size_t>(N) * H * dk * dv * 4;
+    const size_t cs_bytes = conv_state ? static_cast<size_t>(N) * 3 * H * (2 * dk + dv) * 4 : 0;
+    if (final_state != nullptr && initial_state != nullptr && final_state != initial_state) {
+        const uintptr_t a0 = reinterpret_cast<uintptr_t>(initial_state), b0 = reinterpret_cast<uintptr_t>(final_state);
+        if (a0 < b0 + state && b0 < a0 + state)
+            return fail(KDA_ERR_INVALID_ARGUMENT, "final_state partially overlaps initial_state");
+    }
+    std::vector<Span> sp = {
+        {"q_in", q_in, qk * xs, false}, {"k_in", k_in, qk * xs, false}, {"v_in", v_in, vv * xs, false},
+        {"w_q", w_q, static_cast<size_t>(H) * dk * 4 * xs, false},
+        {"w_k", w_k, static_cast<size_t>(H) * dk * 4 * xs, false},
+        {"w_v", w_v, static_cast<size_t>(H) * dv * 4 * xs, false},
+        {"g_alpha", g_alpha, qk * xs, false},
+        {"conv_state", conv_state, cs_bytes, true},
+        {"out_gate", out_gate, out_gate ? vv * xs : 0, false},
+        {"initial_state", initial_state, (initial_state && initial_state != final_state) ? state : 0, false},
+        {"final_state", final_state, final_state ? state : 0, true},
+        {"out", out, vv * xs, true},
+        {"workspace", workspace, need, true},
+    };
+    st = check_spans(sp);
+    if (st != KDA_OK) return st;
+    // b_beta rows are H elements, read one at a time: element alignment suffices
+    if (T * H > 0 && (b_beta == nullptr || (reinterpret_cast<uintptr_t>(b_beta) % xs) != 0))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "b_beta is NULL or misaligned");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    st = debug_check_cu(cu_seqlens, N, T_tot, s);
+    if (st != KDA_OK) return st;
+    kda::LayerArgs a{};
+    a.T = T_tot; a.H = H; a.dk = dk; a.dv = dv; a.N = N; a.cu = cu_seqlens;
+    a.q_in = q_in; a.k_in = k_in; a.v_in = v_in; a.w_q = w_q; a.w_k = w_k; a.w_v = w_v;
+    a.g = g_alpha; a.b = b_beta; a.z = out_gate; a.conv_state = conv_state;
+    a.S0 = initial_state; a.S_out = final_state; a.out = out; a.ws = workspace; a.ws_bytes = workspace_bytes;
+    hipError_t e = kda::launch_layer(a, s);
+    if (e != hipSuccess) return hip_fail(e, "layer launch");
+    return ok();
+}
+
 int kda_decode_step(int32_t B, int32_t H, int32_t dk, int32_t dv, int32_t x_dtype, int32_t gate_dtype,
                     const void* q, const void* k, const void* v, const void* log_alpha, const void* beta,
                     const void* out_gate, float* state, void* out, void* stream) {

@@ -91,6 +91,13 @@ __device__ __forceinline__ float softplus(float x) {
 __device__ __forceinline__ float sigmoid(float x) { return 1.f / (1.f + expf(-x)); }
 // sigmoid with the hardware exponential and reciprocal (about 2 ulp)
 __device__ __forceinline__ float sigmoid_fast(float x) { return __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
+// softplus with the hardware exponential and logarithm
+__device__ __forceinline__ float softplus_fast(float x) {
+    return fmaxf(x, 0.f) + __logf(1.f + __expf(-fabsf(x)));
+}
+
+// the L2 norm's epsilon: x / sqrt(|x|^2 + eps)
+constexpr float kL2Eps = 1e-6f;
 
 // index of the sequence holding token t: the largest n with cu[n] <= t
 // (empty sequences never hold a token, so ties resolve to the non-empty one)

@@ -42,7 +42,26 @@ struct DecodeArgs {
     void* out;
 };
 
+// The whole layer (preprocess + chunked prefill) with the preprocess fused
+// into the chunk kernel; bf16 inputs, dk = dv = 128.
+struct LayerArgs {
+    int64_t T;
+    int H, dk, dv, N;
+    const int32_t* cu;  // may be NULL: one sequence [0, T)
+    const void *q_in, *k_in, *v_in, *w_q, *w_k, *w_v, *g, *b, *z;
+    float* conv_state;
+    const float* S0;
+    float* S_out;
+    void* out;
+    void* ws;
+    size_t ws_bytes;
+};
+
 hipError_t launch_preprocess(const PreprocessArgs& a, hipStream_t s);
+// only the rewrite of the conv history after a call (the last three raw tokens)
+hipError_t launch_conv_state_update(const PreprocessArgs& a, hipStream_t s);
+bool layer_fused_supported(int dk, int dv, DT x);
+hipError_t launch_layer(const LayerArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 
 // chunked prefill: workspace layout and the two implementations

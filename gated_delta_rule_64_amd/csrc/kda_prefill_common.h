@@ -39,7 +39,8 @@ __device__ __forceinline__ int64_t seq_finish(const int32_t* cu, int n, int64_t 
 //                    sequence (slots past base[N] are left unwritten).
 struct SlotInfo {
     int64_t t0;
-    int32_t len, seq;
+    int32_t len;  // tokens in the chunk (bits 0..15); bit 16: the sequence's first chunk
+    int32_t seq;
 };
 static_assert(sizeof(SlotInfo) == 16, "one 16-byte record per slot");
 

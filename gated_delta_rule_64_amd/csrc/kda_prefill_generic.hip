@@ -53,7 +53,8 @@ __global__ __launch_bounds__(1024) void chunk_map_kernel(const int32_t* __restri
             const int32_t j = s - (lo > 0 ? buf[lo - 1] : 0);  // chunk index inside the sequence
             SlotInfo si;
             si.t0 = seq_begin(cu, n) + static_cast<int64_t>(j) * kChunk;
-            si.len = static_cast<int32_t>(min(static_cast<int64_t>(kChunk), seq_finish(cu, n, T) - si.t0));
+            si.len = static_cast<int32_t>(min(static_cast<int64_t>(kChunk), seq_finish(cu, n, T) - si.t0)) |
+                     (j == 0 ? (1 << 16) : 0);
             si.seq = n;
             slot_info[carry + s] = si;
         }
@@ -337,6 +338,28 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
     }
     return a.gate == DT::BF16 ? launch_gen_typed<float, bf16>(a, s, base, rec)
                               : launch_gen_typed<float, float>(a, s, base, rec);
+}
+
+bool layer_fused_supported(int dk, int dv, DT x) { return prefill_uses_mfma(dk, dv, x); }
+
+hipError_t launch_layer(const LayerArgs& a, hipStream_t s) {
+    int32_t* base = static_cast<int32_t*>(a.ws);
+    SlotInfo* slot_info = reinterpret_cast<SlotInfo*>(static_cast<char*>(a.ws) + chunk_map_base_bytes(a.N));
+    char* recs = static_cast<char*>(a.ws) + chunk_map_bytes(a.T, a.N);
+    hipError_t e;
+    {
+        LaunchTimer timer("chunk_map", s);
+        hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(1024), 0, s, a.cu, a.N, a.T, base, slot_info);
+        e = hipGetLastError();
+    }
+    if (e != hipSuccess) return e;
+    e = launch_layer_mfma(a, s, base, slot_info, recs);
+    if (e != hipSuccess) return e;
+    // the chunk kernel has read the old conv history; now it is replaced
+    PreprocessArgs p{};
+    p.T = a.T; p.H = a.H; p.dk = a.dk; p.dv = a.dv; p.N = a.N; p.cu = a.cu; p.x = DT::BF16;
+    p.q_in = a.q_in; p.k_in = a.k_in; p.v_in = a.v_in; p.conv_state = a.conv_state;
+    return launch_conv_state_update(p, s);
 }
 
 }  // namespace kda

@@ -14,5 +14,7 @@ bool mfma_prefill_supports(int dk, int dv, DT x);
 size_t mfma_record_bytes();
 hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t s, int32_t* base, const SlotInfo* slot_info,
                                char* recs);
+hipError_t launch_layer_mfma(const LayerArgs& a, hipStream_t s, int32_t* base, const SlotInfo* slot_info,
+                             char* recs);
 
 }  // namespace kda

@@ -93,6 +93,11 @@ struct MfmaK {
     float* S_out;
     bf16* out;
     char* rec;
+    // fused path only: q, k, v, la and beta above hold the raw inputs (q_in,
+    // k_in, v_in, decay logits g, write logits b), and these the conv taps
+    // and the optional conv history
+    const bf16 *w_q, *w_k, *w_v;
+    const float* cs;
     int64_t slots;   // chunk slots per head in the record array
     int64_t groups;  // N * H
 };
@@ -158,7 +163,11 @@ __device__ __forceinline__ void tile_rs(int i, int& R, int& S) {
     S = i - R * (R + 1) / 2;
 }
 
-template <typename GT>
+// kFused: the unit's inputs are the raw layer inputs, and staging them
+// applies the short conv, the L2 norm and the gates first (as kda_preprocess
+// does, in the same fp32 arithmetic), so the preprocessed tensors never go
+// through HBM.
+template <typename GT, bool kFused>
 __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) {
     extern __shared__ __align__(16) char smem[];
     uint16_t* sK = reinterpret_cast<uint16_t*>(smem);   // [64][KS] keys (bf16)
@@ -181,7 +190,8 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
     const int nslots = scalar_load(a.base + a.N);
     const int64_t units = static_cast<int64_t>(H) * nslots;
     struct Unit {
-        int h, L;
+        int h, L, n;
+        bool first;  // the sequence's first chunk (its conv history is the caller's)
         int64_t slot, t0;
     };
     // The unit's head, slot, first token and length.  The lookups are
@@ -196,7 +206,9 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
         const i32x4 si = scalar_load4(reinterpret_cast<const int32_t*>(a.slot_info + u.slot));
         u.t0 = static_cast<int64_t>((static_cast<uint64_t>(static_cast<uint32_t>(si[1])) << 32) |
                                     static_cast<uint32_t>(si[0]));
-        u.L = si[2];
+        u.L = si[2] & 0xffff;
+        u.first = (si[2] >> 16) != 0;
+        u.n = si[3];
         return u;
     };
     // This thread's share of a unit's inputs, loaded one unit ahead into
@@ -206,8 +218,13 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
     // branch-free: rows past the chunk end read row L-1 and are zeroed on use.
     const int fcq = ftid & 31, frg = ftid >> 5;
     uint4 pk[2], pq[2], pv[2];
-    GateRaw<GT> px[4];  // decay logs as loaded; converted when written to LDS
+    GateRaw<GT> px[4];  // decay logs (fused: decay logits) as loaded; converted when staged
     GT pb{};
+    // fused path: conv taps of 2 channels of one tensor (threads < 192) and
+    // one 8-channel piece of the 3-token conv history of one tensor
+    // (threads < 144), as loaded (bf16 bits, or fp32 from the caller's history)
+    uint4 pw = make_uint4(0, 0, 0, 0);
+    uint32_t ph[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     // part p of a unit's loads: 0 keys, 1 queries, 2 values, 3 decay logs and beta
     auto fetch = [&](const Unit& u, int p) {
 #pragma unroll
@@ -224,6 +241,30 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
             for (int j = 0; j < 4; ++j)
                 px[j].load(a.la + ((u.t0 + min(4 * frg + j, u.L - 1)) * H + u.h) * 128 + 4 * fcq);
             if (ftid < 64) pb = a.beta[(u.t0 + min(ftid, u.L - 1)) * H + u.h];
+            if (kFused) {
+                if (ftid < 192) {  // tensor ftid / 64 (q, k, v), channels 2 (ftid % 64) .. + 1
+                    const bf16* w = ftid < 64 ? a.w_q : (ftid < 128 ? a.w_k : a.w_v);
+                    pw = *reinterpret_cast<const uint4*>(w + (u.h * 128 + 2 * (ftid & 63)) * 4);
+                }
+                if (ftid < 144) {  // tensor ftid / 48, history token hr, channels 8 chh .. + 7
+                    const int tt = ftid / 48, hr = (ftid % 48) >> 4, chh = ftid & 15;
+                    if (!u.first) {
+                        const bf16* x = tt == 0 ? a.q : (tt == 1 ? a.k : a.v);
+                        const uint4 r = *reinterpret_cast<const uint4*>(x + ((u.t0 - 3 + hr) * H + u.h) * 128 + 8 * chh);
+                        ph[0] = r.x; ph[1] = r.y; ph[2] = r.z; ph[3] = r.w;
+                    } else if (a.cs != nullptr) {
+                        const int64_t width = static_cast<int64_t>(H) * 384;  // q, k, v channels of all heads
+                        const float* c0 = a.cs + (static_cast<int64_t>(u.n) * 3 + hr) * width +
+                                          static_cast<int64_t>(tt) * H * 128 + u.h * 128 + 8 * chh;
+                        const float4 lo = reinterpret_cast<const float4*>(c0)[0];
+                        const float4 hi = reinterpret_cast<const float4*>(c0)[1];
+                        ph[0] = __float_as_uint(lo.x); ph[1] = __float_as_uint(lo.y);
+                        ph[2] = __float_as_uint(lo.z); ph[3] = __float_as_uint(lo.w);
+                        ph[4] = __float_as_uint(hi.x); ph[5] = __float_as_uint(hi.y);
+                        ph[6] = __float_as_uint(hi.z); ph[7] = __float_as_uint(hi.w);
+                    }
+                }
+            }
         }
     };
     auto fetch_all = [&](const Unit& u) {
@@ -237,24 +278,126 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
     auto stage_inputs = [&](const Unit& u, int tid) {
         const int cq = tid & 31, rg = tid >> 5;
         const int L = u.L;
+        if (!kFused) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int idx = tid + kIntraThreads * i;
-            const int r = idx >> 4, ch = idx & 15;
-            const uint32_t m = r < L ? 0xffffffffu : 0u;  // masks, not selects: the arrays stay in registers
-            *reinterpret_cast<uint4*>(sK + r * KS + ch * 8) =
-                make_uint4(pk[i].x & m, pk[i].y & m, pk[i].z & m, pk[i].w & m);
-            *reinterpret_cast<uint4*>(sQ + r * KS + ch * 8) =
-                make_uint4(pq[i].x & m, pq[i].y & m, pq[i].z & m, pq[i].w & m);
-            *reinterpret_cast<uint4*>(sV + r * KS + ch * 8) =
-                make_uint4(pv[i].x & m, pv[i].y & m, pv[i].z & m, pv[i].w & m);
+            for (int i = 0; i < 2; ++i) {
+                const int idx = tid + kIntraThreads * i;
+                const int r = idx >> 4, ch = idx & 15;
+                const uint32_t m = r < L ? 0xffffffffu : 0u;  // masks, not selects: the arrays stay in registers
+                *reinterpret_cast<uint4*>(sK + r * KS + ch * 8) =
+                    make_uint4(pk[i].x & m, pk[i].y & m, pk[i].z & m, pk[i].w & m);
+                *reinterpret_cast<uint4*>(sQ + r * KS + ch * 8) =
+                    make_uint4(pq[i].x & m, pq[i].y & m, pq[i].z & m, pq[i].w & m);
+                *reinterpret_cast<uint4*>(sV + r * KS + ch * 8) =
+                    make_uint4(pv[i].x & m, pv[i].y & m, pv[i].z & m, pv[i].w & m);
+            }
+        } else {
+            // Raw rows (bf16, [64][KS] per tensor), the 3-token history (fp32
+            // [3][128] per tensor) and the conv taps (fp32 [3 tensors][4 taps][128]) go to
+            // buffers that are free until the gates are staged.
+            uint16_t* raw = reinterpret_cast<uint16_t*>(sG);
+            float* hist = reinterpret_cast<float*>(raw + 3 * 64 * KS);
+            float* taps = sTot;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int idx = tid + kIntraThreads * i;
+                const int r = idx >> 4, ch = idx & 15;
+                const uint32_t m = r < L ? 0xffffffffu : 0u;
+                *reinterpret_cast<uint4*>(raw + r * KS + ch * 8) =
+                    make_uint4(pq[i].x & m, pq[i].y & m, pq[i].z & m, pq[i].w & m);
+                *reinterpret_cast<uint4*>(raw + 64 * KS + r * KS + ch * 8) =
+                    make_uint4(pk[i].x & m, pk[i].y & m, pk[i].z & m, pk[i].w & m);
+                *reinterpret_cast<uint4*>(raw + 2 * 64 * KS + r * KS + ch * 8) =
+                    make_uint4(pv[i].x & m, pv[i].y & m, pv[i].z & m, pv[i].w & m);
+            }
+            if (tid < 144) {
+                const int tt = tid / 48, hr = (tid % 48) >> 4, chh = tid & 15;
+                float hv[8];
+                if (!u.first) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        hv[2 * e] = __uint_as_float(ph[e] << 16);
+                        hv[2 * e + 1] = __uint_as_float(ph[e] & 0xffff0000u);
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) hv[e] = __uint_as_float(ph[e]);  // zero without a history
+                }
+                float4* d = reinterpret_cast<float4*>(hist + (tt * 3 + hr) * 128 + 8 * chh);
+                d[0] = make_float4(hv[0], hv[1], hv[2], hv[3]);
+                d[1] = make_float4(hv[4], hv[5], hv[6], hv[7]);
+            }
+            if (tid < 192) {  // taps as [tensor][tap][channel]: a lane's 8 channels of one tap are contiguous
+                const uint32_t w4[4] = {pw.x, pw.y, pw.z, pw.w};
+                float* d = taps + (tid >> 6) * 512 + 2 * (tid & 63);
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {  // channel 2 (tid % 64) + e, taps 0..3
+                    d[0 * 128 + e] = __uint_as_float(w4[2 * e] << 16);
+                    d[1 * 128 + e] = __uint_as_float(w4[2 * e] & 0xffff0000u);
+                    d[2 * 128 + e] = __uint_as_float(w4[2 * e + 1] << 16);
+                    d[3 * 128 + e] = __uint_as_float(w4[2 * e + 1] & 0xffff0000u);
+                }
+            }
+            lds_barrier();
+            // conv (tap 3 is the current token), then the L2 norm of q and k
+            // over the 128 channels held by a 16-lane group
+#pragma unroll
+            for (int tt = 0; tt < 3; ++tt) {
+                const int ch8 = 8 * (tid & 15);
+                float w[4][8];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) lds8f(taps + tt * 512 + j * 128 + ch8, w[j]);
+                uint16_t* dst = tt == 0 ? sQ : (tt == 1 ? sK : sV);
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const int r = (tid + kIntraThreads * i) >> 4;
+                    float xv[4][8];
+                    if (r >= 3) {  // every tap inside the chunk: one straight run of reads
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            unpack8(*reinterpret_cast<const uint4*>(raw + tt * 64 * KS + (r - 3 + j) * KS + ch8), xv[j]);
+                    } else {  // the first three rows reach into the history
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const int rr = r - 3 + j;
+                            if (rr >= 0) unpack8(*reinterpret_cast<const uint4*>(raw + tt * 64 * KS + rr * KS + ch8), xv[j]);
+                            else lds8f(hist + (tt * 3 + rr + 3) * 128 + ch8, xv[j]);
+                        }
+                    }
+                    float y[8];
+#pragma unroll
+                    for (int c8 = 0; c8 < 8; ++c8)
+                        y[c8] = w[0][c8] * xv[0][c8] + w[1][c8] * xv[1][c8] + w[2][c8] * xv[2][c8] + w[3][c8] * xv[3][c8];
+                    if (tt < 2) {
+                        float ss = 0.f;
+#pragma unroll
+                        for (int c8 = 0; c8 < 8; ++c8) ss += y[c8] * y[c8];
+#pragma unroll
+                        for (int o = 8; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 16);
+                        const float inv = 1.f / sqrtf(ss + kL2Eps);
+#pragma unroll
+                        for (int c8 = 0; c8 < 8; ++c8) y[c8] *= inv;
+                    }
+                    const uint32_t m = r < L ? 0xffffffffu : 0u;  // padded rows: zero
+                    *reinterpret_cast<uint4*>(dst + r * KS + ch8) =
+                        make_uint4(pack_bf16x2(y[0], y[1]) & m, pack_bf16x2(y[2], y[3]) & m,
+                                   pack_bf16x2(y[4], y[5]) & m, pack_bf16x2(y[6], y[7]) & m);
+                }
+            }
+            lds_barrier();  // the raw rows, history and taps are dead
         }
         float x[4][4];
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) x[j][e] = 4 * rg + j < L ? px[j].get(e) : 0.f;
-        if (tid < 64) sB[tid] = tid < L ? ld(&pb) : 0.f;
+            for (int e = 0; e < 4; ++e) {
+                const float gv = px[j].get(e);
+                x[j][e] = 4 * rg + j < L ? (kFused ? -softplus_fast(gv) : gv) : 0.f;
+            }
+        if (tid < 64) {
+            const float bv = ld(&pb);
+            sB[tid] = tid < L ? (kFused ? sigmoid_fast(bv) : bv) : 0.f;
+        }
         if (tid < 4) sFlag[tid] = 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -965,36 +1108,43 @@ hipError_t launch_state_for(const MfmaK<GT>& k, hipStream_t s, int cus) {
     return ns == 1 ? launch_state<GT, kGate, 1, 1>(k, s) : launch_state<GT, kGate, 4, 1>(k, s);
 }
 
-template <typename GT>
-hipError_t launch_typed(const PrefillArgs& a, hipStream_t s, int32_t* base, const SlotInfo* slot_info, char* recs) {
-    MfmaK<GT> k;
-    k.T = a.T; k.H = a.H; k.N = a.N; k.cu = a.cu; k.base = base; k.slot_info = slot_info;
-    k.q = static_cast<const bf16*>(a.q); k.k = static_cast<const bf16*>(a.k);
-    k.v = static_cast<const bf16*>(a.v); k.z = static_cast<const bf16*>(a.z);
-    k.la = static_cast<const GT*>(a.la); k.beta = static_cast<const GT*>(a.beta);
-    k.S0 = a.S0; k.S_out = a.S_out; k.out = static_cast<bf16*>(a.out); k.rec = recs;
-    k.groups = static_cast<int64_t>(a.N) * a.H;
-    const int64_t slots = chunk_slots_bound(a.T, a.N);
+// the two kernels of the chunked prefill; kFused: k.q, k.k, k.v, k.la and
+// k.beta hold the raw layer inputs (see MfmaK)
+template <typename GT, bool kFused>
+hipError_t launch_kernels(MfmaK<GT>& k, hipStream_t s) {
+    const int64_t slots = chunk_slots_bound(k.T, k.N);
     k.slots = slots;
+    k.groups = static_cast<int64_t>(k.N) * k.H;
     int dev = 0, cus = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
     cus = max(cus, 1);
-    if (a.T > 0) {
-        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&mfma_intra_kernel<GT>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kIntraLds));
+    if (k.T > 0) {
+        const void* fn = reinterpret_cast<const void*>(&mfma_intra_kernel<GT, kFused>);
+        e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kIntraLds));
         if (e != hipSuccess) return e;
         // persistent grid: one workgroup per CU (the LDS footprint allows one)
-        const int64_t grid = min(slots * a.H, static_cast<int64_t>(cus));
-        LaunchTimer timer("mfma_intra", s);
-        hipLaunchKernelGGL((mfma_intra_kernel<GT>), dim3(static_cast<unsigned>(grid)), dim3(kIntraThreads),
+        const int64_t grid = min(slots * k.H, static_cast<int64_t>(cus));
+        LaunchTimer timer(kFused ? "mfma_prep_intra" : "mfma_intra", s);
+        hipLaunchKernelGGL((mfma_intra_kernel<GT, kFused>), dim3(static_cast<unsigned>(grid)), dim3(kIntraThreads),
                            kIntraLds, s, k);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     LaunchTimer timer("mfma_state", s);
-    return a.z ? launch_state_for<GT, true>(k, s, cus) : launch_state_for<GT, false>(k, s, cus);
+    return k.z ? launch_state_for<GT, true>(k, s, cus) : launch_state_for<GT, false>(k, s, cus);
+}
+
+template <typename GT>
+hipError_t launch_typed(const PrefillArgs& a, hipStream_t s, int32_t* base, const SlotInfo* slot_info, char* recs) {
+    MfmaK<GT> k{};
+    k.T = a.T; k.H = a.H; k.N = a.N; k.cu = a.cu; k.base = base; k.slot_info = slot_info;
+    k.q = static_cast<const bf16*>(a.q); k.k = static_cast<const bf16*>(a.k);
+    k.v = static_cast<const bf16*>(a.v); k.z = static_cast<const bf16*>(a.z);
+    k.la = static_cast<const GT*>(a.la); k.beta = static_cast<const GT*>(a.beta);
+    k.S0 = a.S0; k.S_out = a.S_out; k.out = static_cast<bf16*>(a.out); k.rec = recs;
+    return launch_kernels<GT, false>(k, s);
 }
 
 }  // namespace
@@ -1002,6 +1152,19 @@ hipError_t launch_typed(const PrefillArgs& a, hipStream_t s, int32_t* base, cons
 bool mfma_prefill_supports(int dk, int dv, DT x) { return dk == 128 && dv == 128 && x == DT::BF16; }
 
 size_t mfma_record_bytes() { return REC_BYTES; }
+
+hipError_t launch_layer_mfma(const LayerArgs& a, hipStream_t s, int32_t* base, const SlotInfo* slot_info,
+                             char* recs) {
+    MfmaK<bf16> k{};
+    k.T = a.T; k.H = a.H; k.N = a.N; k.cu = a.cu; k.base = base; k.slot_info = slot_info;
+    k.q = static_cast<const bf16*>(a.q_in); k.k = static_cast<const bf16*>(a.k_in);
+    k.v = static_cast<const bf16*>(a.v_in); k.z = static_cast<const bf16*>(a.z);
+    k.la = static_cast<const bf16*>(a.g); k.beta = static_cast<const bf16*>(a.b);
+    k.w_q = static_cast<const bf16*>(a.w_q); k.w_k = static_cast<const bf16*>(a.w_k);
+    k.w_v = static_cast<const bf16*>(a.w_v); k.cs = a.conv_state;
+    k.S0 = a.S0; k.S_out = a.S_out; k.out = static_cast<bf16*>(a.out); k.rec = recs;
+    return launch_kernels<bf16, true>(k, s);
+}
 
 hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t s, int32_t* base, const SlotInfo* slot_info,
                                char* recs) {

@@ -28,7 +28,6 @@ namespace {
 
 constexpr int kRun = 16;                 // tokens per 16-lane group
 constexpr int kTile = kRun * 4;          // tokens per workgroup (4 groups per wave)
-constexpr float kL2Eps = 1e-6f;
 
 // One lane's 8 channels of a row, as loaded (bf16: 16 B, fp32: 32 B).  Rows
 // are loaded a whole batch ahead of their use and unpacked when consumed.
@@ -60,9 +59,6 @@ template <> struct Raw<float> {
     }
 };
 
-__device__ __forceinline__ float softplus_fast(float x) {
-    return fmaxf(x, 0.f) + __logf(1.f + __expf(-fabsf(x)));
-}
 
 template <typename XT>
 struct PrepK {
@@ -258,7 +254,17 @@ __global__ __launch_bounds__(256) void conv_state_kernel(PrepK<XT> a, int blocks
 }
 
 template <typename XT>
-hipError_t launch_typed(const PreprocessArgs& a, hipStream_t s) {
+hipError_t launch_conv_state(const PrepK<XT>& k, hipStream_t s) {
+    if (k.cs == nullptr || k.N <= 0) return hipSuccess;
+    const int64_t width = static_cast<int64_t>(k.H) * (2 * k.dk + k.dv);
+    const int bps = static_cast<int>((width + 255) / 256);
+    LaunchTimer timer("conv_state", s);
+    hipLaunchKernelGGL((conv_state_kernel<XT>), dim3(static_cast<unsigned>(k.N) * bps), dim3(256), 0, s, k, bps);
+    return hipGetLastError();
+}
+
+template <typename XT>
+PrepK<XT> prep_args(const PreprocessArgs& a) {
     PrepK<XT> k;
     k.T = a.T; k.H = a.H; k.dk = a.dk; k.dv = a.dv; k.N = a.N; k.cu = a.cu;
     k.q_in = static_cast<const XT*>(a.q_in); k.k_in = static_cast<const XT*>(a.k_in);
@@ -269,6 +275,12 @@ hipError_t launch_typed(const PreprocessArgs& a, hipStream_t s) {
     k.q_out = static_cast<XT*>(a.q_out); k.k_out = static_cast<XT*>(a.k_out);
     k.v_out = static_cast<XT*>(a.v_out);
     k.la_out = a.la_out; k.beta_out = a.beta_out;
+    return k;
+}
+
+template <typename XT>
+hipError_t launch_typed(const PreprocessArgs& a, hipStream_t s) {
+    const PrepK<XT> k = prep_args<XT>(a);
     if (a.T > 0) {
         const int64_t blocks = (a.T + kTile - 1) / kTile * a.H;
         const int64_t gx = blocks < (1 << 20) ? blocks : (1 << 20);
@@ -279,21 +291,18 @@ hipError_t launch_typed(const PreprocessArgs& a, hipStream_t s) {
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    if (a.conv_state != nullptr && a.N > 0) {
-        const int64_t width = static_cast<int64_t>(a.H) * (2 * a.dk + a.dv);
-        const int bps = static_cast<int>((width + 255) / 256);
-        LaunchTimer timer("conv_state", s);
-        hipLaunchKernelGGL((conv_state_kernel<XT>), dim3(static_cast<unsigned>(a.N) * bps), dim3(256), 0, s,
-                           k, bps);
-        return hipGetLastError();
-    }
-    return hipSuccess;
+    return launch_conv_state<XT>(k, s);
 }
 
 }  // namespace
 
 hipError_t launch_preprocess(const PreprocessArgs& a, hipStream_t s) {
     return a.x == DT::BF16 ? launch_typed<bf16>(a, s) : launch_typed<float>(a, s);
+}
+
+hipError_t launch_conv_state_update(const PreprocessArgs& a, hipStream_t s) {
+    return a.x == DT::BF16 ? launch_conv_state<bf16>(prep_args<bf16>(a), s)
+                           : launch_conv_state<float>(prep_args<float>(a), s);
 }
 
 }  // namespace kda

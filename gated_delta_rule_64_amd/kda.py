@@ -109,3 +109,29 @@ def kda_decode_step(q, k, v, log_alpha, beta, state, out_gate=None, out=None):
                                 _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(out_gate),
                                 _ptr(state), _ptr(out), _stream(q.device)))
     return out
+
+
+def kda_prefill_layer(q_in, k_in, v_in, w_q, w_k, w_v, g_alpha, b_beta, H, dk, dv, out_gate=None,
+                      initial_state=None, final_state=None, cu_seqlens=None, conv_state=None, workspace=None,
+                      out=None, want_final_state=True):
+    """kda_preprocess + kda_prefill_chunked in one call (bf16, dk = dv = 128):
+    raw inputs [T, H*d] as for kda_preprocess, the rest as for
+    kda_prefill_chunked.  Returns (out [T,H,dv], final_state fp32 [N,H,dk,dv] or None).
+    ``conv_state`` (fp32 [N, 3, H*(2dk+dv)]) is read and rewritten in place."""
+    T = q_in.shape[0]
+    N = _n_seqs(cu_seqlens)
+    x = _dtype_code(q_in)
+    dev = q_in.device
+    if out is None:
+        out = torch.empty((T, H, dv), dtype=q_in.dtype, device=dev)
+    if final_state is None and want_final_state:
+        final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    need = kda_prefill_workspace_bytes(T, N, H, dk, dv, x)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    check(lib().kda_prefill_layer(T, H, dk, dv, _ptr(cu_seqlens), N, x,
+                                  _ptr(q_in), _ptr(k_in), _ptr(v_in), _ptr(w_q), _ptr(w_k), _ptr(w_v),
+                                  _ptr(g_alpha), _ptr(b_beta), _ptr(conv_state), _ptr(out_gate),
+                                  _ptr(initial_state), _ptr(final_state), _ptr(out),
+                                  _ptr(workspace), workspace.numel(), _stream(dev)))
+    return out, final_state

@@ -152,6 +152,31 @@ int kda_prefill_chunked(int64_t T_tot, int32_t H, int32_t dk, int32_t dv,
                         void* stream);
 
 /*
+ * kda_prefill_layer -- kda_preprocess followed by kda_prefill_chunked in one
+ * call, for bf16 inputs with dk = dv = 128 (the Ling-shaped heads): the
+ * short conv, the L2 norm and the gates run inside the chunk kernel, so the
+ * preprocessed q, k, v, log-decay and beta never go through device memory.
+ * The result equals the two-call path up to rounding order.
+ * Arguments: those of kda_preprocess for the raw inputs (q_in .. b_beta,
+ * conv_state: read as the history, then replaced by the last three raw
+ * tokens of each sequence) and of kda_prefill_chunked for the rest
+ * (out_gate, initial_state, final_state, out, workspace sized by
+ * kda_prefill_workspace_bytes with the same sizes).  Other head sizes or
+ * dtypes return KDA_ERR_UNSUPPORTED: use the two calls.
+ */
+int kda_prefill_layer(int64_t T_tot, int32_t H, int32_t dk, int32_t dv,
+                      const int32_t* cu_seqlens, int32_t N, int32_t x_dtype,
+                      const void* q_in, const void* k_in, const void* v_in,
+                      const void* w_q, const void* w_k, const void* w_v,
+                      const void* g_alpha, const void* b_beta,
+                      float* conv_state,
+                      const void* out_gate,
+                      const float* initial_state, float* final_state,
+                      void* out,
+                      void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/*
  * kda_decode_step -- one token per sequence, state updated in place.
  * For each (b, h):  S' = Diag(alpha) S;  u = S'^T k;  S <- S' + beta k (v - u)^T;
  *                   o = S^T q;  out = o * sigmoid(z) (or o without a gate).

@@ -1,0 +1,103 @@
+"""kda_prefill_layer (preprocess fused into the chunk kernel) against the fp64
+oracle's preprocess + token-by-token recurrence, on the same seeded raw
+inputs: ragged packed batches, conv history in and out, initial states,
+decay/write extremes, the full 4096-token layer, and bad arguments."""
+
+import numpy as np
+import pytest
+import torch
+
+from gated_delta_rule_64_amd import synth
+from kda_helpers import TOL, assert_close, f64, oracle_layer_inputs, to_dev, to_host64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def K():
+    from gated_delta_rule_64_amd import kda
+    return kda
+
+
+def fused(K, inp, conv_state=None):
+    H, dk, dv, T = inp["H"], inp["dk"], inp["dv"], inp["T_tot"]
+    z = to_dev(inp["z"]).view(T, H, dv) if inp["z"] is not None else None
+    S0 = to_dev(inp["S0"]) if inp["S0"] is not None else None
+    out, S = K.kda_prefill_layer(*(to_dev(inp[n]) for n in ("q_in", "k_in", "v_in", "w_q", "w_k", "w_v", "g", "b")),
+                                 H, dk, dv, out_gate=z, initial_state=S0, cu_seqlens=to_dev(inp["cu_seqlens"]),
+                                 conv_state=conv_state)
+    torch.cuda.synchronize()
+    return out, S
+
+
+@pytest.mark.parametrize("lengths", [(1000,), (130, 0, 64, 1, 700), (63, 65, 3, 2, 1)])
+def test_layer_matches_oracle(K, oracle_mod, lengths):
+    inp = synth.make("varlen_64", lengths=lengths, H=4)
+    print(f"fused layer lengths={lengths}", flush=True)
+    out, S = fused(K, inp)
+    ref = oracle_mod.layer(oracle_layer_inputs(inp))
+    assert_close("y", to_host64(out), ref["y"], TOL["bf16"])
+    assert_close("state", to_host64(S), ref["S"], TOL["bf16"])
+
+
+def test_layer_conv_history_in_and_out(K, oracle_mod):
+    """Sequences shorter and longer than the conv width, each starting from
+    a caller-given history; the history is rewritten with the last three raw
+    tokens (reaching back into the old one for short sequences)."""
+    inp = synth.make("decode_b256", lengths=(5, 70, 2, 130, 1), H=2)
+    assert inp["conv_state"] is not None
+    cs = to_dev(inp["conv_state"]).clone()
+    out, S = fused(K, inp, conv_state=cs)
+    ref = oracle_mod.layer(oracle_layer_inputs(inp), want_conv_state=True)
+    assert_close("y", to_host64(out), ref["y"], TOL["bf16"])
+    assert_close("state", to_host64(S), ref["S"], TOL["bf16"])
+    # the new history holds raw input values: exact
+    np.testing.assert_array_equal(cs.cpu().numpy().astype(np.float64), ref["conv_state"])
+
+
+def test_layer_agrees_with_two_calls(K, oracle_mod):
+    """Same inputs through kda_preprocess + kda_prefill_chunked: equal up to
+    rounding order (both inside the bf16 bar of each other)."""
+    inp = synth.make("varlen_64", lengths=(300, 77), H=3)
+    out_f, S_f = fused(K, inp)
+    H, dk, dv, T = inp["H"], inp["dk"], inp["dv"], inp["T_tot"]
+    cu = to_dev(inp["cu_seqlens"])
+    q, k, v, la, beta = K.kda_preprocess(*(to_dev(inp[n]) for n in ("q_in", "k_in", "v_in", "w_q", "w_k", "w_v",
+                                                                  "g", "b")), H, dk, dv, cu_seqlens=cu)
+    out_2, S_2 = K.kda_prefill_chunked(q, k, v, la, beta, out_gate=to_dev(inp["z"]).view(T, H, dv),
+                                       initial_state=to_dev(inp["S0"]), cu_seqlens=cu)
+    torch.cuda.synchronize()
+    assert_close("y fused vs two calls", to_host64(out_f), to_host64(out_2), 1e-2)
+    assert_close("state fused vs two calls", to_host64(S_f), to_host64(S_2), 1e-2)
+
+
+@pytest.mark.parametrize("case", ["fast_decay", "slow_decay", "beta_one", "zero_rows"])
+def test_layer_stress(K, oracle_mod, case):
+    kw = {"fast_decay": dict(g_mean=4.0), "slow_decay": dict(g_mean=-6.0),
+          "beta_one": dict(b_mean=12.0), "zero_rows": {}}[case]
+    inp = synth.make("long_t256k", lengths=(700, 1300), H=3, **kw)
+    if case == "zero_rows":
+        inp["q_in"][100:180] = 0
+        inp["k_in"][100:180] = 0
+    print(f"fused stress {case}", flush=True)
+    out, S = fused(K, inp)
+    ref = oracle_mod.layer(oracle_layer_inputs(inp))
+    assert_close("y", to_host64(out), ref["y"], TOL["bf16"])
+    assert_close("state", to_host64(S), ref["S"], TOL["bf16"])
+
+
+def test_layer_t4k_full(K, oracle_mod):
+    """The 4096-token, 32-head layer the bench times, every output checked."""
+    inp = synth.make("layer_t4k")
+    out, S = fused(K, inp)
+    ref = oracle_mod.layer(oracle_layer_inputs(inp))
+    assert_close("y", to_host64(out), ref["y"], TOL["bf16"])
+    assert_close("state", to_host64(S), ref["S"], TOL["bf16"])
+
+
+def test_layer_rejects_unsupported_shapes(K):
+    inp = synth.make("varlen_64", lengths=(10,), H=2, dk=64, dv=64)
+    from gated_delta_rule_64_amd._lib import KdaError
+    with pytest.raises(KdaError) as e:
+        fused(K, inp)
+    assert "KDA_ERR_UNSUPPORTED" in str(e.value)
