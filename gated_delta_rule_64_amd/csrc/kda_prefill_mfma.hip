@@ -157,6 +157,17 @@ template <> struct GateRaw<bf16> {
     }
 };
 
+// Sum over the 16 lanes of a DPP row (lanes 16k .. 16k + 15), all lanes
+// active: swaps within quads (quad_perm [1,0,3,2], [2,3,0,1]), then the
+// half-row and row mirrors pair the quads and the halves.  Vector ALU only.
+__device__ __forceinline__ float row16_sum(float x) {
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, false));
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, false));
+    return x;
+}
+
 // (R, S) of tile i in the lower block triangle, row-major order
 __device__ __forceinline__ void tile_rs(int i, int& R, int& S) {
     R = i >= 6 ? 3 : i >= 3 ? 2 : i >= 1 ? 1 : 0;
@@ -339,15 +350,17 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
                 }
             }
             lds_barrier();
-            // conv (tap 3 is the current token), then the L2 norm of q and k
-            // over the 128 channels held by a 16-lane group
+            // conv (tap 3 is the current token) of the thread's two rows of each
+            // tensor, all reads of a tensor issued before the arithmetic that
+            // needs them; then the L2 norm of q and k over the 128 channels a
+            // 16-lane row of the wave holds
+            const int ch8 = 8 * (tid & 15);
 #pragma unroll
             for (int tt = 0; tt < 3; ++tt) {
-                const int ch8 = 8 * (tid & 15);
                 float w[4][8];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) lds8f(taps + tt * 512 + j * 128 + ch8, w[j]);
-                uint16_t* dst = tt == 0 ? sQ : (tt == 1 ? sK : sV);
+                float y[2][8];
 #pragma unroll
                 for (int i = 0; i < 2; ++i) {
                     const int r = (tid + kIntraThreads * i) >> 4;
@@ -364,24 +377,30 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
                             else lds8f(hist + (tt * 3 + rr + 3) * 128 + ch8, xv[j]);
                         }
                     }
-                    float y[8];
 #pragma unroll
                     for (int c8 = 0; c8 < 8; ++c8)
-                        y[c8] = w[0][c8] * xv[0][c8] + w[1][c8] * xv[1][c8] + w[2][c8] * xv[2][c8] + w[3][c8] * xv[3][c8];
-                    if (tt < 2) {
+                        y[i][c8] = w[0][c8] * xv[0][c8] + w[1][c8] * xv[1][c8] + w[2][c8] * xv[2][c8] +
+                                   w[3][c8] * xv[3][c8];
+                }
+                if (tt < 2) {
+#pragma unroll
+                    for (int i = 0; i < 2; ++i) {
                         float ss = 0.f;
 #pragma unroll
-                        for (int c8 = 0; c8 < 8; ++c8) ss += y[c8] * y[c8];
+                        for (int c8 = 0; c8 < 8; ++c8) ss += y[i][c8] * y[i][c8];
+                        const float inv = __builtin_amdgcn_rsqf(row16_sum(ss) + kL2Eps);
 #pragma unroll
-                        for (int o = 8; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 16);
-                        const float inv = 1.f / sqrtf(ss + kL2Eps);
-#pragma unroll
-                        for (int c8 = 0; c8 < 8; ++c8) y[c8] *= inv;
+                        for (int c8 = 0; c8 < 8; ++c8) y[i][c8] *= inv;
                     }
+                }
+                uint16_t* dst = tt == 0 ? sQ : (tt == 1 ? sK : sV);
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const int r = (tid + kIntraThreads * i) >> 4;
                     const uint32_t m = r < L ? 0xffffffffu : 0u;  // padded rows: zero
                     *reinterpret_cast<uint4*>(dst + r * KS + ch8) =
-                        make_uint4(pack_bf16x2(y[0], y[1]) & m, pack_bf16x2(y[2], y[3]) & m,
-                                   pack_bf16x2(y[4], y[5]) & m, pack_bf16x2(y[6], y[7]) & m);
+                        make_uint4(pack_bf16x2(y[i][0], y[i][1]) & m, pack_bf16x2(y[i][2], y[i][3]) & m,
+                                   pack_bf16x2(y[i][4], y[i][5]) & m, pack_bf16x2(y[i][6], y[i][7]) & m);
                 }
             }
             lds_barrier();  // the raw rows, history and taps are dead
