@@ -26,7 +26,7 @@
 //    substitution (one column per lane, in registers), off-diagonal blocks
 //    from the inverses of the two 32 x 32 halves.
 //  - W, U~, Q', M U~ on the matrix cores; outputs stored per (head, chunk).
-// Phase 2 (mfma_state_kernel): per (sequence, head, half of the state
+// Phase 2 (mfma_state_kernel): per (sequence, head, group of state
 //  columns), compute waves carry the fp32 state in registers through the
 //  chunks in order while copy waves stream each chunk's factors into LDS.
 #include <stdlib.h>
