@@ -858,6 +858,19 @@ __device__ __forceinline__ void lds_copy16(const void* gsrc, char* lds_dst) {
     __builtin_amdgcn_global_load_lds(gsrc, (lds_void*)(lds_dst), 16, 0, 0);
 }
 
+// 16 bytes of LDS that no LDS-DMA copy writes (the output staging area).  The
+// compiler cannot tell which LDS bytes a copy in flight lands in, so before a
+// plain LDS read it waits for all of them (vmcnt 0), which would drain the
+// copy pipeline every step.  This read is inline asm instead, waited for
+// (lgkmcnt 0) in the same block.
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 lds_read16_staged(const char* p) {
+    u32x4_t v;
+    const uint32_t addr = static_cast<uint32_t>(reinterpret_cast<size_t>((lds_void*)(p)));
+    asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr) : "memory");
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // Tiles of 64 token rows x (2 SB) 16-byte pieces (gate logits, staged
 // output): piece q of row r is kept at slot q ^ (r mod 2 SB), so reads and
 // writes that walk 16 rows of one column group spread over the banks.
@@ -978,7 +991,7 @@ __global__ __launch_bounds__(64 * (NS + 4)) void mfma_state_kernel(MfmaK<GT> a) 
             for (int i = 0; i < kS; ++i) {
                 const int rl = i * ROWS_PER_PIECE + lane / PR;  // row within the wave's 16
                 const int r = 16 * wm + min(rl, 15);
-                const uint4 v = *reinterpret_cast<const uint4*>(stage + r * RB + wq * 16);
+                const uint4 v = lds_read16_staged(stage + r * RB + wq * 16);
                 const int q = tile_slot<SB>(r, wq);
                 // rows past the end exist only in a sequence's last chunk,
                 // after which no counted wait follows
@@ -1020,51 +1033,80 @@ __global__ __launch_bounds__(64 * (NS + 4)) void mfma_state_kernel(MfmaK<GT> a) 
             for (int ks = 0; ks < 4; ++ks) Sb[sw][ks] = to_bf16x8(S[sw][2 * ks], S[sw][2 * ks + 1]);
         // U = U~ - W S, and the output transposed: O^T = (M U~)^T + S^T Q'^T
         // (the state operand and the Q' operand swap roles): lane (g, c) holds
-        // token 16 mt + c, columns 16 slice + 4 g .. + 3
-        f32x4 U[SW][4];
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-            f32x4 o[SW];
+        // token 16 mt + c, columns 16 slice + 4 g .. + 3.  The LDS reads of
+        // row tile mt + 1 are issued before the products of tile mt, so their
+        // latency overlaps the matrix-core work.
+        struct TileOps {
+            uint2 up[SW], op[SW], zp[SW];
+            bf16x8 wa[4], qa[4];
+        };
+        auto stage_off = [&](int mt, int sw) {
+            // columns 16 ls + 4 g .. + 3 of the group: piece 2 ls + g/2, bytes 8 (g & 1)
+            const int ls = SW * wave + sw;
+            const int r = 16 * mt + c;
+            return r * RB + tile_slot<SB>(r, 2 * ls + (g >> 1)) * 16 + 8 * (g & 1);
+        };
+        auto load_tile = [&](int mt, TileOps& x) {
 #pragma unroll
             for (int sw = 0; sw < SW; ++sw) {
                 const int ls = SW * wave + sw;  // slice within the group
-                const uint2 up = *reinterpret_cast<const uint2*>(cur + C::B_UT + ((ls * 4 + mt) * 64 + lane) * 8);
-                const uint2 op = *reinterpret_cast<const uint2*>(cur + C::B_OI + ((ls * 4 + mt) * 64 + lane) * 8);
-                U[sw][mt] = f32x4{__uint_as_float(up.x << 16), __uint_as_float(up.x & 0xffff0000u),
-                                  __uint_as_float(up.y << 16), __uint_as_float(up.y & 0xffff0000u)};
-                o[sw] = f32x4{__uint_as_float(op.x << 16), __uint_as_float(op.x & 0xffff0000u),
-                              __uint_as_float(op.y << 16), __uint_as_float(op.y & 0xffff0000u)};
+                x.up[sw] = *reinterpret_cast<const uint2*>(cur + C::B_UT + ((ls * 4 + mt) * 64 + lane) * 8);
+                x.op[sw] = *reinterpret_cast<const uint2*>(cur + C::B_OI + ((ls * 4 + mt) * 64 + lane) * 8);
+                if (kGate) x.zp[sw] = *reinterpret_cast<const uint2*>(cur + C::B_Z + stage_off(mt, sw));
             }
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 const int blk = (mt * 4 + ks) * 64 + lane;
-                const bf16x8 wa = *reinterpret_cast<const bf16x8*>(cur + C::B_NEGW + blk * 16);
-                const bf16x8 qa = *reinterpret_cast<const bf16x8*>(cur + C::B_QP + blk * 16);
-#pragma unroll
-                for (int sw = 0; sw < SW; ++sw) {
-                    U[sw][mt] = mfma(wa, Sb[sw][ks], U[sw][mt]);
-                    o[sw] = mfma(Sb[sw][ks], qa, o[sw]);
-                }
+                x.wa[ks] = *reinterpret_cast<const bf16x8*>(cur + C::B_NEGW + blk * 16);
+                x.qa[ks] = *reinterpret_cast<const bf16x8*>(cur + C::B_QP + blk * 16);
             }
+        };
+        auto widen = [](uint2 p) {
+            return f32x4{__uint_as_float(p.x << 16), __uint_as_float(p.x & 0xffff0000u), __uint_as_float(p.y << 16),
+                         __uint_as_float(p.y & 0xffff0000u)};
+        };
+        f32x4 U[SW][4];
+        TileOps ops[2];
+        load_tile(0, ops[0]);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            TileOps& x = ops[mt & 1];
+            if (mt < 3) load_tile(mt + 1, ops[(mt + 1) & 1]);
+            f32x4 o[SW];
 #pragma unroll
             for (int sw = 0; sw < SW; ++sw) {
-                // columns 16 ls + 4 g .. + 3 of the group: piece 2 ls + g/2, bytes 8 (g & 1)
-                const int ls = SW * wave + sw;
-                const int r = 16 * mt + c;
-                const int off = r * RB + tile_slot<SB>(r, 2 * ls + (g >> 1)) * 16 + 8 * (g & 1);
+                U[sw][mt] = widen(x.up[sw]);
+                o[sw] = widen(x.op[sw]);
+            }
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+                for (int sw = 0; sw < SW; ++sw) {
+                    U[sw][mt] = mfma(x.wa[ks], Sb[sw][ks], U[sw][mt]);
+                    o[sw] = mfma(Sb[sw][ks], x.qa[ks], o[sw]);
+                }
+#pragma unroll
+            for (int sw = 0; sw < SW; ++sw) {
                 if (kGate) {
-                    const uint2 zp = *reinterpret_cast<const uint2*>(cur + C::B_Z + off);
-                    const float zf[4] = {__uint_as_float(zp.x << 16), __uint_as_float(zp.x & 0xffff0000u),
-                                         __uint_as_float(zp.y << 16), __uint_as_float(zp.y & 0xffff0000u)};
+                    const f32x4 zf = widen(x.zp[sw]);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) o[sw][i] *= sigmoid_fast(zf[i]);
                 }
-                *reinterpret_cast<uint2*>(stage + off) =
+                *reinterpret_cast<uint2*>(stage + stage_off(mt, sw)) =
                     make_uint2(pack_bf16x2(o[sw][0], o[sw][1]), pack_bf16x2(o[sw][2], o[sw][3]));
             }
         }
         lds_barrier();  // M_j: the output tile is staged; part B of chunk j is in LDS
-        // S <- Diag(gamma) S + K^T U
+        // S <- Diag(gamma) S + K^T U, with every K^T and gamma read issued first
+        bf16x8 ka[8][2];
+        float4 gm[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            gm[t] = *reinterpret_cast<const float4*>(cur + C::B_GAM + (16 * t + 4 * g) * 4);
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+                ka[t][ks] = *reinterpret_cast<const bf16x8*>(cur + C::B_KHT + ((t * 2 + ks) * 64 + lane) * 16);
+        }
         bf16x8 Ub[SW][2];
 #pragma unroll
         for (int sw = 0; sw < SW; ++sw)
@@ -1072,20 +1114,17 @@ __global__ __launch_bounds__(64 * (NS + 4)) void mfma_state_kernel(MfmaK<GT> a) 
             for (int ks = 0; ks < 2; ++ks) Ub[sw][ks] = to_bf16x8(U[sw][2 * ks], U[sw][2 * ks + 1]);
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-            const float4 gm = *reinterpret_cast<const float4*>(cur + C::B_GAM + (16 * t + 4 * g) * 4);
 #pragma unroll
             for (int sw = 0; sw < SW; ++sw) {
-                S[sw][t][0] *= gm.x;
-                S[sw][t][1] *= gm.y;
-                S[sw][t][2] *= gm.z;
-                S[sw][t][3] *= gm.w;
+                S[sw][t][0] *= gm[t].x;
+                S[sw][t][1] *= gm[t].y;
+                S[sw][t][2] *= gm[t].z;
+                S[sw][t][3] *= gm[t].w;
             }
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const bf16x8 ka = *reinterpret_cast<const bf16x8*>(cur + C::B_KHT + ((t * 2 + ks) * 64 + lane) * 16);
+            for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-                for (int sw = 0; sw < SW; ++sw) S[sw][t] = mfma(ka, Ub[sw][ks], S[sw][t]);
-            }
+                for (int sw = 0; sw < SW; ++sw) S[sw][t] = mfma(ka[t][ks], Ub[sw][ks], S[sw][t]);
         }
     }
     if (a.S_out) {
