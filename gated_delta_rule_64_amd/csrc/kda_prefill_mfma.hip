@@ -225,17 +225,18 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
     // This thread's share of a unit's inputs, loaded one unit ahead into
     // registers so the loads overlap the previous unit's work: rows
     // (tid + 512 i) / 16 of q, k, v (8 channels each), rows 4 rg .. 4 rg + 3 of
-    // the decay logs (4 channels), and beta for tid < 64.  Loads are
+    // the decay logs (4 channels), and beta of row tid % 64.  Loads are
     // branch-free: rows past the chunk end read row L-1 and are zeroed on use.
     const int fcq = ftid & 31, frg = ftid >> 5;
+    const int fw = __builtin_amdgcn_readfirstlane(ftid >> 6);  // the wave, as a uniform value
     uint4 pk[2], pq[2], pv[2];
     GateRaw<GT> px[4];  // decay logs (fused: decay logits) as loaded; converted when staged
     GT pb{};
-    // fused path: conv taps of 2 channels of one tensor (threads < 192) and
-    // one 8-channel piece of the 3-token conv history of one tensor
-    // (threads < 144), as loaded (bf16 bits, or fp32 from the caller's history)
+    // fused path: conv taps of 2 channels and one 8-channel piece of the
+    // 3-token conv history of tensor (wave mod 3), as loaded (bf16 bits, or
+    // fp32 from the caller's history)
     uint4 pw = make_uint4(0, 0, 0, 0);
-    uint32_t ph[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    uint32_t ph[8];
     // part p of a unit's loads: 0 keys, 1 queries, 2 values, 3 decay logs and beta
     auto fetch = [&](const Unit& u, int p) {
 #pragma unroll
@@ -251,29 +252,43 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 px[j].load(a.la + ((u.t0 + min(4 * frg + j, u.L - 1)) * H + u.h) * 128 + 4 * fcq);
-            if (ftid < 64) pb = a.beta[(u.t0 + min(ftid, u.L - 1)) * H + u.h];
+            // The last loads cover less than 512 threads' worth; every wave
+            // issues them anyway, repeating another wave's (and later writes
+            // the same bytes to the same LDS place).  Loads and their uses
+            // under conditions that skip whole waves would leave the compiler
+            // a path on which these registers still await their loads when
+            // the next unit's fetch reuses them, and it would wait there.
+            // The tensor a wave covers is uniform (fw is read from lane 0),
+            // so choosing its pointer is a scalar select.
+            pb = a.beta[(u.t0 + min(ftid & 63, u.L - 1)) * H + u.h];
             if (kFused) {
-                if (ftid < 192) {  // tensor ftid / 64 (q, k, v), channels 2 (ftid % 64) .. + 1
-                    const bf16* w = ftid < 64 ? a.w_q : (ftid < 128 ? a.w_k : a.w_v);
+                const int tt = fw % 3;
+                {  // tensor tt (q, k, v), channels 2 (tid % 64) .. + 1
+                    const bf16* w = tt == 0 ? a.w_q : (tt == 1 ? a.w_k : a.w_v);
                     pw = *reinterpret_cast<const uint4*>(w + (u.h * 128 + 2 * (ftid & 63)) * 4);
                 }
-                if (ftid < 144) {  // tensor ftid / 48, history token hr, channels 8 chh .. + 7
-                    const int tt = ftid / 48, hr = (ftid % 48) >> 4, chh = ftid & 15;
-                    if (!u.first) {
-                        const bf16* x = tt == 0 ? a.q : (tt == 1 ? a.k : a.v);
-                        const uint4 r = *reinterpret_cast<const uint4*>(x + ((u.t0 - 3 + hr) * H + u.h) * 128 + 8 * chh);
-                        ph[0] = r.x; ph[1] = r.y; ph[2] = r.z; ph[3] = r.w;
-                    } else if (a.cs != nullptr) {
+                {  // tensor tt, history token hr, channels 8 chh .. + 7
+                    // Two 16-byte loads every time, from addresses chosen by
+                    // uniform values (no branches: a load in one arm of a
+                    // branch is copied out at the merge, which waits for it).
+                    // Not the first chunk: the raw row t0 - 3 + hr (bf16, first
+                    // load).  First chunk with a caller history: its 8 fp32
+                    // values.  First chunk without: row t0, read and unused.
+                    const int hr = min((ftid & 63) >> 4, 2), chh = ftid & 15;  // lanes 48.. repeat token 2
+                    const bf16* x = tt == 0 ? a.q : (tt == 1 ? a.k : a.v);
+                    const int64_t row = u.first ? u.t0 : u.t0 - 3 + hr;
+                    const char* src = reinterpret_cast<const char*>(x + (row * H + u.h) * 128 + 8 * chh);
+                    int step = 0;
+                    if (u.first && a.cs != nullptr) {
                         const int64_t width = static_cast<int64_t>(H) * 384;  // q, k, v channels of all heads
-                        const float* c0 = a.cs + (static_cast<int64_t>(u.n) * 3 + hr) * width +
-                                          static_cast<int64_t>(tt) * H * 128 + u.h * 128 + 8 * chh;
-                        const float4 lo = reinterpret_cast<const float4*>(c0)[0];
-                        const float4 hi = reinterpret_cast<const float4*>(c0)[1];
-                        ph[0] = __float_as_uint(lo.x); ph[1] = __float_as_uint(lo.y);
-                        ph[2] = __float_as_uint(lo.z); ph[3] = __float_as_uint(lo.w);
-                        ph[4] = __float_as_uint(hi.x); ph[5] = __float_as_uint(hi.y);
-                        ph[6] = __float_as_uint(hi.z); ph[7] = __float_as_uint(hi.w);
+                        src = reinterpret_cast<const char*>(a.cs + (static_cast<int64_t>(u.n) * 3 + hr) * width +
+                                                            static_cast<int64_t>(tt) * H * 128 + u.h * 128 + 8 * chh);
+                        step = 16;
                     }
+                    const uint4 lo = *reinterpret_cast<const uint4*>(src);
+                    const uint4 hi = *reinterpret_cast<const uint4*>(src + step);
+                    ph[0] = lo.x; ph[1] = lo.y; ph[2] = lo.z; ph[3] = lo.w;
+                    ph[4] = hi.x; ph[5] = hi.y; ph[6] = hi.z; ph[7] = hi.w;
                 }
             }
         }
@@ -321,8 +336,14 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
                 *reinterpret_cast<uint4*>(raw + 2 * 64 * KS + r * KS + ch * 8) =
                     make_uint4(pv[i].x & m, pv[i].y & m, pv[i].z & m, pv[i].w & m);
             }
-            if (tid < 144) {
-                const int tt = tid / 48, hr = (tid % 48) >> 4, chh = tid & 15;
+            const int tw = __builtin_amdgcn_readfirstlane(tid >> 6) % 3;  // the tensor this wave fetched
+            {
+                const int tt = tw, hr = min((tid & 63) >> 4, 2), chh = tid & 15;
+                // the history as fetched for this unit (see fetch): raw bf16
+                // rows, the caller's fp32 values, or zeros.  Every path
+                // reads all eight registers (the raw rows fill four), so none
+                // is left awaiting its load when the next fetch reuses it.
+                asm volatile("" ::"v"(ph[4]), "v"(ph[5]), "v"(ph[6]), "v"(ph[7]));
                 float hv[8];
                 if (!u.first) {
 #pragma unroll
@@ -331,16 +352,17 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
                         hv[2 * e + 1] = __uint_as_float(ph[e] & 0xffff0000u);
                     }
                 } else {
+                    const uint32_t m = a.cs != nullptr ? 0xffffffffu : 0u;
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) hv[e] = __uint_as_float(ph[e]);  // zero without a history
+                    for (int e = 0; e < 8; ++e) hv[e] = __uint_as_float(ph[e] & m);
                 }
                 float4* d = reinterpret_cast<float4*>(hist + (tt * 3 + hr) * 128 + 8 * chh);
                 d[0] = make_float4(hv[0], hv[1], hv[2], hv[3]);
                 d[1] = make_float4(hv[4], hv[5], hv[6], hv[7]);
             }
-            if (tid < 192) {  // taps as [tensor][tap][channel]: a lane's 8 channels of one tap are contiguous
+            {  // taps as [tensor][tap][channel]: a lane's 8 channels of one tap are contiguous
                 const uint32_t w4[4] = {pw.x, pw.y, pw.z, pw.w};
-                float* d = taps + (tid >> 6) * 512 + 2 * (tid & 63);
+                float* d = taps + tw * 512 + 2 * (tid & 63);
 #pragma unroll
                 for (int e = 0; e < 2; ++e) {  // channel 2 (tid % 64) + e, taps 0..3
                     d[0 * 128 + e] = __uint_as_float(w4[2 * e] << 16);
@@ -413,9 +435,10 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
                 const float gv = px[j].get(e);
                 x[j][e] = 4 * rg + j < L ? (kFused ? -softplus_fast(gv) : gv) : 0.f;
             }
-        if (tid < 64) {
+        {
             const float bv = ld(&pb);
-            sB[tid] = tid < L ? (kFused ? sigmoid_fast(bv) : bv) : 0.f;
+            const int bt = tid & 63;  // every wave writes the same 64 values
+            sB[bt] = bt < L ? (kFused ? sigmoid_fast(bv) : bv) : 0.f;
         }
         if (tid < 4) sFlag[tid] = 0;
 #pragma unroll
@@ -437,7 +460,7 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
     Unit nxt = unit_of(v);
     fetch_all(nxt);
     stage_inputs(nxt, ftid);
-    for (; v < units; v += gridDim.x) {
+    for (;; v += gridDim.x) {
         // Lane-dependent values are rederived from an opaque copy of the thread
         // index in every unit, so the compiler does not hoist dozens of masks
         // and addresses out of the loop (they would not fit in registers).
@@ -802,7 +825,12 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
             if (tid < 128) reinterpret_cast<float*>(rec + R_GAM)[tid] = expf(sG[63 * GS + tid]);
         }
         lds_barrier();  // every LDS buffer is free for the next unit
-        if (more) stage_inputs(nxt, tid);
+        // Leave before staging rather than staging conditionally: the loop's
+        // back edge then comes only from a path where the staging has
+        // consumed (waited for) every prefetched register, so reusing those
+        // registers in the next unit needs no wait for loads in flight.
+        if (!more) break;
+        stage_inputs(nxt, tid);
     }
 }
 

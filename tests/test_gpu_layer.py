@@ -71,6 +71,50 @@ def test_layer_agrees_with_two_calls(K, oracle_mod):
     assert_close("state fused vs two calls", to_host64(S_f), to_host64(S_2), 1e-2)
 
 
+@pytest.mark.parametrize("history", [False, True])
+def test_layer_sequence_starts_in_later_units(K, oracle_mod, history):
+    """Forty sequences over 8 heads: the persistent chunk kernel walks several
+    (head, chunk) units per workgroup, so most first chunks are staged after
+    some other unit.  The first three rows of every sequence (the rows whose
+    short conv reads the history: zeros, or the caller's) are checked row by
+    row, so a wrong history on a single row cannot hide under the tensor-wide
+    bar.  A row's error is taken relative to its own largest value, floored
+    at the median of those over the checked rows: a row whose q.k nearly
+    cancels (a first token from a zero state has y = beta (q.k) v sigma(z))
+    carries the bf16 rounding of q and k at full size, while a wrong history
+    changes q, k and v themselves.  The bar, 0.1 on that scale, is four times
+    tighter than the tensor-wide 2e-2 of the largest output (about twenty
+    median row scales here); a wrong history moves these rows by O(1)."""
+    rng = np.random.default_rng(7)
+    lengths = tuple(int(x) for x in rng.integers(1, 400, size=40))
+    H = 8
+    inp = synth.make("decode_b256" if history else "varlen_64", lengths=lengths, H=H)
+    assert (inp["conv_state"] is not None) == history
+    T = inp["T_tot"]
+    assert H * ((T + 63) // 64 + len(lengths)) > 4 * 256  # several units per workgroup on any MI355X
+    cs = to_dev(inp["conv_state"]).clone() if history else None
+    print(f"fused layer, sequence starts, history={history}", flush=True)
+    out, S = fused(K, inp, conv_state=cs)
+    ref = oracle_mod.layer(oracle_layer_inputs(inp), want_conv_state=history)
+    y = to_host64(out).reshape(T, H, -1)
+    yr = np.asarray(ref["y"], dtype=np.float64).reshape(T, H, -1)
+    assert_close("y", y, yr, TOL["bf16"])
+    assert_close("state", to_host64(S), ref["S"], TOL["bf16"])
+    cu = inp["cu_seqlens"].astype(np.int64)
+    rows = [(n, t) for n in range(len(lengths)) for t in range(cu[n], min(cu[n] + 3, cu[n + 1]))]
+    scale = np.abs(yr[[t for _, t in rows]]).max(axis=-1)  # [rows, H]
+    floor = np.median(scale)
+    worst = 0.0
+    for i, (n, t) in enumerate(rows):
+        for h in range(H):
+            e = np.abs(y[t, h] - yr[t, h]).max() / max(scale[i, h], floor)
+            worst = max(worst, e)
+            assert e <= 0.1, f"sequence {n} token {t - cu[n]} head {h}: row rel err {e:.3e}"
+    print(f"  first rows: worst row rel err {worst:.3e} (floor {floor:.3e})", flush=True)
+    if history:
+        np.testing.assert_array_equal(cs.cpu().numpy().astype(np.float64), ref["conv_state"])
+
+
 @pytest.mark.parametrize("case", ["fast_decay", "slow_decay", "beta_one", "zero_rows"])
 def test_layer_stress(K, oracle_mod, case):
     kw = {"fast_decay": dict(g_mean=4.0), "slow_decay": dict(g_mean=-6.0),
