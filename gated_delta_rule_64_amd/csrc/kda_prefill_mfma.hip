@@ -53,6 +53,8 @@ constexpr int REC_BYTES = 82432;
 // intra-kernel LDS strides (padded rows avoid bank conflicts)
 constexpr int KS = 136;  // bf16 per row of K, Q, V
 constexpr int GS = 132;  // fp32 per row of G
+constexpr int MS = 68;   // fp32 per row of A, M and T (16 lanes reading 16 rows hit distinct banks)
+constexpr int SQS = 136; // bf16 per row of the Q' staging tile (the same bytes per row as A)
 constexpr float kDiagRange = 40.f;
 
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -107,7 +109,7 @@ struct MfmaK {
 // ---------------------------------------------------------------------------
 
 constexpr int kIntraThreads = 512;  // 8 waves: two per SIMD
-constexpr size_t kIntraLds = (3 * 64 * KS) * 2 + (64 * GS + 3 * 4096 + 64 + 16 * 128) * 4 + 16;
+constexpr size_t kIntraLds = (3 * 64 * KS) * 2 + (64 * GS + 3 * 64 * MS + 64 + 16 * 128) * 4 + 16;
 
 __device__ __forceinline__ void unpack8(uint4 v, float (&x)[8]) {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
@@ -185,14 +187,14 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
     uint16_t* sQ = sK + 64 * KS;                        // [64][KS] queries
     uint16_t* sV = sQ + 64 * KS;                        // [64][KS] values
     float* sG = reinterpret_cast<float*>(sV + 64 * KS);  // [64][GS] decay cumsums
-    float* sA = sG + 64 * GS;                           // [64][64]
-    float* sM = sA + 4096;                              // [64][64]
-    float* sT = sM + 4096;                              // [64][64]
-    float* sB = sT + 4096;                              // [64] beta
+    float* sA = sG + 64 * GS;                           // [64][MS]
+    float* sM = sA + 64 * MS;                           // [64][MS]
+    float* sT = sM + 64 * MS;                           // [64][MS]
+    float* sB = sT + 64 * MS;                           // [64] beta
     float* sTot = sB + 64;                              // [16][128] scan partials, later scratch
     int* sFlag = reinterpret_cast<int*>(sTot + 16 * 128);
     uint16_t* sStW = sV;                                // staging of -W  [64][KS]
-    uint16_t* sStQ = reinterpret_cast<uint16_t*>(sA);   // staging of Q'  [64][128]
+    uint16_t* sStQ = reinterpret_cast<uint16_t*>(sA);   // staging of Q'  [64][SQS]
 
     const int H = a.H;
     const int ftid = threadIdx.x;  // the thread index as the prefetch uses it
@@ -441,9 +443,8 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
             sB[bt] = bt < L ? (kFused ? sigmoid_fast(bv) : bv) : 0.f;
         }
         if (tid < 4) sFlag[tid] = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            reinterpret_cast<float4*>(sA)[tid + kIntraThreads * i] = make_float4(0.f, 0.f, 0.f, 0.f);  // sA, sM
+        for (int i = tid; i < 2 * 64 * MS / 4; i += kIntraThreads)
+            reinterpret_cast<float4*>(sA)[i] = make_float4(0.f, 0.f, 0.f, 0.f);  // sA, sM
 #pragma unroll
         for (int j = 1; j < 4; ++j)
 #pragma unroll
@@ -550,8 +551,8 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int r = 16 * R + 4 * g + i, s2 = 16 * S + c;
-                    sA[r * 64 + s2] = s2 < r ? accA[i] : 0.f;
-                    sM[r * 64 + s2] = s2 <= r ? accM[i] : 0.f;
+                    sA[r * MS + s2] = s2 < r ? accA[i] : 0.f;
+                    sM[r * MS + s2] = s2 <= r ? accM[i] : 0.f;
                 }
             };
             int R, S;
@@ -565,11 +566,11 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
             accA = f32x4{0.f, 0.f, 0.f, 0.f};
             accM = accA;
             tile_part(R, S, kp, kp + 1, accA, accM);
-            float* part = sT + wave * 512;  // [A 16x16][M 16x16], lane-major
+            float* part = sT + wave * 512;  // [A: 4 x 64 lanes][M: 4 x 64 lanes]
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                part[(4 * g + i) * 16 + c] = accA[i];
-                part[256 + (4 * g + i) * 16 + c] = accM[i];
+                part[i * 64 + lane] = accA[i];
+                part[256 + i * 64 + lane] = accM[i];
             }
             lds_barrier();
             if (wave < 2) {  // wave 0 sums tile 8, wave 1 tile 9, steps in order
@@ -580,8 +581,8 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
                     const float* q = sT + (4 * wave + k) * 512;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        sa[i] += q[(4 * g + i) * 16 + c];
-                        sm[i] += q[256 + (4 * g + i) * 16 + c];
+                        sa[i] += q[i * 64 + lane];
+                        sm[i] += q[256 + i * 64 + lane];
                     }
                 }
                 store_tile(R, S, sa, sm);
@@ -608,7 +609,7 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
                 float arow[16];
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4) {
-                    const float4 v4 = *reinterpret_cast<const float4*>(sA + (16 * R + r) * 64 + 16 * R + 4 * q4);
+                    const float4 v4 = *reinterpret_cast<const float4*>(sA + (16 * R + r) * MS + 16 * R + 4 * q4);
                     arow[4 * q4] = v4.x; arow[4 * q4 + 1] = v4.y; arow[4 * q4 + 2] = v4.z; arow[4 * q4 + 3] = v4.w;
                 }
                 float sum = 0.f;
@@ -618,7 +619,7 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
             }
             if (j < 16) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) sT[(16 * R + r) * 64 + 16 * R + j] = t[r];
+                for (int r = 0; r < 16; ++r) sT[(16 * R + r) * MS + 16 * R + j] = t[r];
             }
         }
         lds_barrier();
@@ -631,7 +632,11 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
         //            T_30 = -(T_32 X_20 + T_33 X_30),  T_31 = -(T_32 X_21 + T_33 X_31)
         // Lane (g, c) computes rows 4g .. 4g+3, column c of a 16 x 16 block.
         {
-            float* sX = sTot;  // 16 x 16 blocks with row stride 16 (the scan partials are dead)
+            // 16 x 16 blocks with row stride XS, XB floats apart (the scan
+            // partials are dead); 20 puts the four row groups a wave writes
+            // on distinct banks
+            constexpr int XS = 20, XB = 16 * XS;
+            float* sX = sTot;
             // acc[i] += sum_k P[4g+i][k] Q[k][c] over a 16 x 16 pair
             auto mm16 = [&](const float* P, int ldp, const float* Q, int ldq, float (&acc)[4]) {
                 float qc[16];
@@ -651,31 +656,31 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
             if (wave < 2) {
                 const int R = 2 * wave + 1, S = R - 1;
                 float y[4] = {0.f, 0.f, 0.f, 0.f};
-                mm16(sA + (16 * R) * 64 + 16 * S, 64, sT + (16 * S) * 64 + 16 * S, 64, y);
-                float* Y = sX + wave * 256;
+                mm16(sA + (16 * R) * MS + 16 * S, MS, sT + (16 * S) * MS + 16 * S, MS, y);
+                float* Y = sX + wave * XB;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) Y[(4 * g + i) * 16 + c] = sB[16 * R + 4 * g + i] * y[i];
+                for (int i = 0; i < 4; ++i) Y[(4 * g + i) * XS + c] = sB[16 * R + 4 * g + i] * y[i];
                 // (a wave's LDS operations are performed in order: Y is complete here)
                 float t[4] = {0.f, 0.f, 0.f, 0.f};
-                mm16(sT + (16 * R) * 64 + 16 * R, 64, Y, 16, t);
+                mm16(sT + (16 * R) * MS + 16 * R, MS, Y, XS, t);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) sT[(16 * R + 4 * g + i) * 64 + 16 * S + c] = -t[i];
+                for (int i = 0; i < 4; ++i) sT[(16 * R + 4 * g + i) * MS + 16 * S + c] = -t[i];
             }
             lds_barrier();
             const int R = 2 + (wave >> 1), S = wave & 1;  // block of waves 0..3
             if (wave < 4) {
                 float x[4] = {0.f, 0.f, 0.f, 0.f};
-                for (int J = S; J < 2; ++J) mm16(sA + (16 * R) * 64 + 16 * J, 64, sT + (16 * J) * 64 + 16 * S, 64, x);
+                for (int J = S; J < 2; ++J) mm16(sA + (16 * R) * MS + 16 * J, MS, sT + (16 * J) * MS + 16 * S, MS, x);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) sX[wave * 256 + (4 * g + i) * 16 + c] = sB[16 * R + 4 * g + i] * x[i];
+                for (int i = 0; i < 4; ++i) sX[wave * XB + (4 * g + i) * XS + c] = sB[16 * R + 4 * g + i] * x[i];
             }
             lds_barrier();
             if (wave < 4) {
                 float t[4] = {0.f, 0.f, 0.f, 0.f};
-                mm16(sT + (16 * R) * 64 + 32, 64, sX + S * 256, 16, t);                      // T_R2 X_2S
-                if (R == 3) mm16(sT + (16 * 3) * 64 + 48, 64, sX + (2 + S) * 256, 16, t);  // T_33 X_3S
+                mm16(sT + (16 * R) * MS + 32, MS, sX + S * XB, XS, t);                      // T_R2 X_2S
+                if (R == 3) mm16(sT + (16 * 3) * MS + 48, MS, sX + (2 + S) * XB, XS, t);  // T_33 X_3S
 #pragma unroll
-                for (int i = 0; i < 4; ++i) sT[(16 * R + 4 * g + i) * 64 + 16 * S + c] = -t[i];
+                for (int i = 0; i < 4; ++i) sT[(16 * R + 4 * g + i) * MS + 16 * S + c] = -t[i];
             }
         }
         lds_barrier();
@@ -694,7 +699,7 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
                 for (int ks = 0; ks < 2; ++ks) {
                     const int row = 16 * mt + c, col0 = 32 * ks + 8 * g;
                     float tv[8];
-                    lds8f(sT + row * 64 + col0, tv);
+                    lds8f(sT + row * MS + col0, tv);
 #pragma unroll
                     for (int e = 0; e < 8; ++e) tv[e] = col0 + e <= row ? tv[e] : 0.f;
                     Ta[mt][ks] = to_bf16x8(tv);
@@ -742,7 +747,7 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
             for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
-                    const float* mrow = sM + (16 * mt + c) * 64 + 32 * ks + 4 * g;
+                    const float* mrow = sM + (16 * mt + c) * MS + 32 * ks + 4 * g;
                     const float4 lo = *reinterpret_cast<const float4*>(mrow);
                     const float4 hi = *reinterpret_cast<const float4*>(mrow + 16);
                     const float mv[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
@@ -782,7 +787,7 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
                 for (int i = 0; i < 4; ++i) {
                     const int r = 16 * mt + 4 * g + i;
                     sStW[r * KS + chn] = f32_to_bf16(-accW[mt][i]);
-                    sStQ[r * 128 + chn] = f32_to_bf16(qp[i]);
+                    sStQ[r * SQS + chn] = f32_to_bf16(qp[i]);
                 }
             }
         }
@@ -798,8 +803,8 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
                 const int c0 = 32 * ks + 4 * g;
                 const uint2 wlo = *reinterpret_cast<const uint2*>(sStW + r * KS + c0);
                 const uint2 whi = *reinterpret_cast<const uint2*>(sStW + r * KS + c0 + 16);
-                const uint2 qlo = *reinterpret_cast<const uint2*>(sStQ + r * 128 + c0);
-                const uint2 qhi = *reinterpret_cast<const uint2*>(sStQ + r * 128 + c0 + 16);
+                const uint2 qlo = *reinterpret_cast<const uint2*>(sStQ + r * SQS + c0);
+                const uint2 qhi = *reinterpret_cast<const uint2*>(sStQ + r * SQS + c0 + 16);
                 const int blk = (mt * 4 + ks) * 64 + lane;
                 *reinterpret_cast<uint4*>(rec + R_NEGW + blk * 16) = make_uint4(wlo.x, wlo.y, whi.x, whi.y);
                 *reinterpret_cast<uint4*>(rec + R_QP + blk * 16) = make_uint4(qlo.x, qlo.y, qhi.x, qhi.y);
