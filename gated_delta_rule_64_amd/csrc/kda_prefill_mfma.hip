@@ -843,29 +843,34 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
 // phase 2
 // ---------------------------------------------------------------------------
 
-// One workgroup per (sequence, head, group of SB = NS x SW 16-column slices
-// of the state), with two roles.  NS compute waves each own SW slices (the
-// state columns of slices SB*part + SW*w .. + SW-1, in registers): inside the
-// chunk loop they touch only LDS, reading the chunk's factors (each factor
-// read serves all SW slices of the wave) and writing the gated output tile
-// to an LDS staging area.  Four memory waves do all global traffic: they copy
-// what a chunk needs into one of two LDS buffers with global_load_lds_dwordx4
-// and store the staged output as whole row pieces.  A chunk is copied in two
-// parts: the part the first half of a step reads (-W, Q', the group's U~ and
-// M U~ tiles, its gate logits) as soon as the compute waves are done with it
-// two chunks back, and the part the second half reads (K^T, gamma) one step
-// ahead.  Every memory wave issues the same number of operations every step
-// (a wave with no piece of some tile copies into a dump area), so a fixed
-// count (vmcnt) tells when a part has landed while later ones stay in flight:
+// One workgroup per (sequence, head, group of SB 16-column slices of the
+// state), with three roles.  Per slice, a chain wave keeps the slice's state
+// in registers and runs the recurrence, and an output wave computes the
+// gated output from the state the chain wave hands over in LDS (see the
+// compute section).  Inside the chunk loop they touch only LDS, reading the
+// chunk's factors and writing the gated output tile to an LDS staging area.
+// Four memory waves do all global traffic: they copy what a chunk needs into
+// one of two LDS buffers with global_load_lds_dwordx4 and store the staged
+// output as whole row pieces.  A chunk is copied in two parts: the part the
+// first half of a step reads (-W, Q', the group's U~ and M U~ tiles, its gate
+// logits) as soon as the compute waves are done with it two chunks back, and
+// the part the second half reads (K^T, gamma) one step ahead.  Every memory
+// wave issues the same number of operations every step (a wave with no piece
+// of some tile makes a one-lane copy into a dump area), so a fixed count
+// (vmcnt) tells when a part has landed while later ones stay in flight:
 // vector memory operations of one wave retire in issue order.
-// Smaller groups spread a head over more CUs, which suits few (sequence,
-// head) pairs; larger ones share each copied factor among more columns.
+// One slice per workgroup spreads a head over more CUs, which suits few
+// (sequence, head) pairs; two share each copied factor between two slices.
 template <int SB>
 struct StateCfg {
-    static_assert(SB == 1 || SB == 2 || SB == 4, "1, 2 or 4 slices per workgroup");
+    static_assert(SB == 1 || SB == 2, "1 or 2 slices per workgroup");
+    // memory waves: each issues its share of every copy (more of them do not
+    // move a chunk faster: the copies are bound by the CU's path into LDS)
+    static constexpr int kMemWaves = 4;
     static constexpr int kRowBytes = 32 * SB;             // one token row of the group's columns, bf16
     static constexpr int kPieces = 2 * SB;                // 1 KB pieces of each group tile (U~, M U~, z)
-    static constexpr int kPiecesPerWave = (kPieces + 3) / 4;
+    static constexpr int kPiecesPerWave = (kPieces + kMemWaves - 1) / kMemWaves;
+    static constexpr int kRowsPerWave = 64 / kMemWaves;   // output rows each memory wave stores
     // LDS buffer layout, bytes.  The first 48 KB mirror the record's first 48 KB.
     static constexpr int B_NEGW = 0;                      // -W, 16 KB
     static constexpr int B_QP = 16384;                    // Q', 16 KB
@@ -874,15 +879,19 @@ struct StateCfg {
     static constexpr int B_OI = B_UT + 1024 * kPieces;    // M U~, same layout
     static constexpr int B_Z = B_OI + 1024 * kPieces;     // gate logits [64 tokens][kRowBytes], swizzled
     static constexpr int B_GAM = B_Z + 1024 * kPieces;    // gamma, fp32 [128]
-    static constexpr int B_DUMP = B_GAM + 512;            // target of the filler copies, never read
-    static constexpr int B_BYTES = B_DUMP + 1024;
+    static constexpr int B_DUMP = B_GAM + 512;            // target of the one-lane filler copies, never read
+    static constexpr int B_BYTES = B_DUMP + 64;
     // operations one memory wave issues per part (wave 0 issues one more in
     // the second part: gamma) and per output tile
-    static constexpr int kPartA = 8 + 3 * kPiecesPerWave;
-    static constexpr int kPartB = 4;
-    static constexpr int kStores = (SB + 1) / 2;           // 16 rows of kRowBytes per wave (half
-                                                           // the lanes idle when SB = 1)
-    static constexpr size_t kLds = 2 * static_cast<size_t>(B_BYTES) + 64 * kRowBytes;
+    static constexpr int kPartA = 32 / kMemWaves + 3 * kPiecesPerWave;
+    static constexpr int kPartB = 16 / kMemWaves;
+    static constexpr int kRowsPerStore = 1024 / kRowBytes;  // rows of kRowBytes one 64-lane store covers
+    static constexpr int kStores = (kRowsPerWave + kRowsPerStore - 1) / kRowsPerStore;
+    // after the two buffers: the staged output tile, then per slice the bf16
+    // state operand the chain wave hands to the output wave
+    static constexpr int B_STAGE = 2 * B_BYTES;
+    static constexpr int B_SBX = B_STAGE + 64 * kRowBytes;  // [SB s][4 ks][64 lanes][16 B]
+    static constexpr size_t kLds = static_cast<size_t>(B_SBX) + 4096 * SB;
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -919,9 +928,9 @@ __device__ __forceinline__ void wait_vmcnt() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-template <typename GT, bool kGate, int NS, int SW>
-__global__ __launch_bounds__(64 * (NS + 4)) void mfma_state_kernel(MfmaK<GT> a) {
-    constexpr int SB = NS * SW;
+template <typename GT, bool kGate, int NS>
+__global__ __launch_bounds__(64 * (2 * NS + StateCfg<NS>::kMemWaves)) void mfma_state_kernel(MfmaK<GT> a) {
+    constexpr int SB = NS;
     using C = StateCfg<SB>;
     constexpr int P = 8 / SB;            // slice groups per head
     constexpr int RB = C::kRowBytes;
@@ -930,7 +939,7 @@ __global__ __launch_bounds__(64 * (NS + 4)) void mfma_state_kernel(MfmaK<GT> a) 
     extern __shared__ __align__(16) char smem[];
     char* const buf0 = smem;
     char* const buf1 = smem + C::B_BYTES;
-    char* const stage = smem + 2 * C::B_BYTES;  // gated output tile, bf16 [64][RB], swizzled
+    char* const stage = smem + C::B_STAGE;  // gated output tile, bf16 [64][RB], swizzled
     // blockIdx -> (sequence, head, part): all parts of a (sequence, head) land
     // on one XCD (workgroups are dealt round-robin over the 8 XCDs), so the
     // chunk records they share are read through one L2
@@ -951,40 +960,46 @@ __global__ __launch_bounds__(64 * (NS + 4)) void mfma_state_kernel(MfmaK<GT> a) 
     };
     auto buf_of = [&](int j) { return (j & 1) ? buf1 : buf0; };
 
-    if (wave >= NS) {
+    if (wave >= 2 * NS) {
         // ---- memory waves
         if (nch == 0) return;
-        const int wm = wave - NS;
+        const int wm = wave - 2 * NS;
         // part A of chunk min(j, nch-1): -W, Q', U~, M U~ and gate logits
         // (past the end it copies the last chunk again into the free buffer
         // the index selects, so that every step issues the same operations)
+        constexpr int MW = C::kMemWaves;
         auto issue_a = [&](int jn) {
             char* buf = buf_of(jn);
             const int j = min(jn, nch - 1);
             const char* rp = rec_of(j);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int b = wm + 4 * i;
+            for (int i = 0; i < 32 / MW; ++i) {
+                const int b = wm + MW * i;
                 lds_copy16(rp + b * 1024 + lane * 16, buf + b * 1024);
             }
             const int Lc = chunk_len(j);
             const int64_t tb = sb + static_cast<int64_t>(j) * kChunk;
 #pragma unroll
             for (int i = 0; i < C::kPiecesPerWave; ++i) {
-                const int b = wm + 4 * i;
+                const int b = wm + MW * i;
                 const bool real = b < C::kPieces;
                 const int bb = real ? b : 0;
                 const char* ut = rp + R_UT + part * (1024 * C::kPieces) + bb * 1024 + lane * 16;
                 const char* oi = rp + R_OI + part * (1024 * C::kPieces) + bb * 1024 + lane * 16;
-                lds_copy16(ut, real ? buf + C::B_UT + b * 1024 : buf + C::B_DUMP);
-                lds_copy16(oi, real ? buf + C::B_OI + b * 1024 : buf + C::B_DUMP);
+                // a filler copy (no piece here) moves 16 bytes from one lane:
+                // it is one operation all the same, which keeps the count fixed
+                if (real || lane == 0) {
+                    lds_copy16(ut, real ? buf + C::B_UT + b * 1024 : buf + C::B_DUMP);
+                    lds_copy16(oi, real ? buf + C::B_OI + b * 1024 : buf + C::B_DUMP);
+                }
                 const int r = bb * ROWS_PER_PIECE + lane / PR;
                 const int q = tile_slot<SB>(r, lane % PR);  // the slot map is its own inverse
                 // without a gate the tile is never read; copying keeps the count fixed
                 const void* zs = kGate ? static_cast<const void*>(a.z + ((tb + min(r, Lc - 1)) * H + h) * 128 +
                                                                   16 * SB * part + 8 * q)
                                        : static_cast<const void*>(ut);
-                lds_copy16(zs, (real && kGate) ? buf + C::B_Z + b * 1024 : buf + C::B_DUMP);
+                if ((real && kGate) || lane == 0)
+                    lds_copy16(zs, (real && kGate) ? buf + C::B_Z + b * 1024 : buf + C::B_DUMP);
             }
         };
         // part B of chunk min(j, nch-1): K^T and gamma
@@ -993,8 +1008,8 @@ __global__ __launch_bounds__(64 * (NS + 4)) void mfma_state_kernel(MfmaK<GT> a) 
             const int j = min(jn, nch - 1);
             const char* rp = rec_of(j);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int b = 32 + wm + 4 * i;
+            for (int i = 0; i < 16 / MW; ++i) {
+                const int b = 32 + wm + MW * i;
                 lds_copy16(rp + b * 1024 + lane * 16, buf + b * 1024);
             }
             if (wm == 0 && lane < 32) lds_copy16(rp + R_GAM + lane * 16, buf + C::B_GAM);
@@ -1009,8 +1024,9 @@ __global__ __launch_bounds__(64 * (NS + 4)) void mfma_state_kernel(MfmaK<GT> a) 
         issue_a(0);
         issue_b(0);
         issue_a(1);
-        // store role: rows 16 wm .. 16 wm + 15, ROWS_PER_PIECE of them per
+        // store role: rows RW wm .. RW wm + RW-1, ROWS_PER_PIECE of them per
         // instruction
+        constexpr int RW = C::kRowsPerWave;
         const int wq = lane % PR;
         for (int j = 0; j < nch; ++j) {
             if (j == 0) wait_vmcnt<kB + kA>(); else wait_vmcnt<kB + kS + kA>();
@@ -1022,13 +1038,13 @@ __global__ __launch_bounds__(64 * (NS + 4)) void mfma_state_kernel(MfmaK<GT> a) 
             const int64_t tb = sb + static_cast<int64_t>(j) * kChunk;
 #pragma unroll
             for (int i = 0; i < kS; ++i) {
-                const int rl = i * ROWS_PER_PIECE + lane / PR;  // row within the wave's 16
-                const int r = 16 * wm + min(rl, 15);
+                const int rl = i * ROWS_PER_PIECE + lane / PR;  // row within the wave's RW
+                const int r = RW * wm + min(rl, RW - 1);
                 const uint4 v = lds_read16_staged(stage + r * RB + wq * 16);
                 const int q = tile_slot<SB>(r, wq);
                 // rows past the end exist only in a sequence's last chunk,
                 // after which no counted wait follows
-                if (rl < 16 && r < Lc)
+                if (rl < RW && r < Lc)
                     *reinterpret_cast<uint4*>(a.out + ((tb + r) * H + h) * 128 + 16 * SB * part + 8 * q) = v;
             }
             issue_a(j + 2);
@@ -1037,166 +1053,177 @@ __global__ __launch_bounds__(64 * (NS + 4)) void mfma_state_kernel(MfmaK<GT> a) 
         return;
     }
 
-    // ---- compute waves: slices SW*wave .. SW*wave + SW-1 of the group
-    f32x4 S[SW][8];  // S[s][t][i] = state[16t + 4g + i][16 (SB part + SW wave + s) + c]
-    const int64_t sidx = grp * (128 * 128);
-    const int col0 = 16 * (SB * part + SW * wave) + c;
-    if (a.S0 != nullptr) {  // one uniform branch: all loads in flight together
+    // ---- compute waves: two per 16-column slice ls = wave / 2 of the group.
+    // The chain wave (even) keeps the slice's fp32 state in registers and runs
+    // the recurrence, U = U~ - W S and then S <- Diag(gamma) S + K^T U; after
+    // each update it leaves the state as the bf16 matrix-core operand in LDS.
+    // The output wave (odd) takes that operand for the chunk's gated output,
+    // O^T = (M U~)^T + S^T Q'^T, off the recurrence's critical path: row tiles
+    // 0-2; the chain wave, which has less to do before M_j, takes row tile 3.
+    // Inside the chunk loop both touch only LDS.  In a step the output wave
+    // reads the operand before M_j and the chain wave rewrites it after M_j.
+    const int ls = wave >> 1;
+    char* const sbx = smem + C::B_SBX + ls * 4096;
+    const int col0 = 16 * (SB * part + ls) + c;
+    auto widen = [](uint2 p) {
+        return f32x4{__uint_as_float(p.x << 16), __uint_as_float(p.x & 0xffff0000u), __uint_as_float(p.y << 16),
+                     __uint_as_float(p.y & 0xffff0000u)};
+    };
+    // one row tile of the output: lane (g, c) holds token 16 mt + c, columns
+    // 16 ls + 4 g .. + 3 (the state operand and the Q' operand swap roles)
+    struct OutOps {
+        uint2 op, zp;
+        bf16x8 qa[4];
+    };
+    auto stage_off = [&](int mt) {
+        // columns 16 ls + 4 g .. + 3 of the group: piece 2 ls + g/2, bytes 8 (g & 1)
+        const int r = 16 * mt + c;
+        return r * RB + tile_slot<SB>(r, 2 * ls + (g >> 1)) * 16 + 8 * (g & 1);
+    };
+    auto load_out = [&](const char* cur, int mt, OutOps& x) {
+        x.op = *reinterpret_cast<const uint2*>(cur + C::B_OI + ((ls * 4 + mt) * 64 + lane) * 8);
+        if (kGate) x.zp = *reinterpret_cast<const uint2*>(cur + C::B_Z + stage_off(mt));
 #pragma unroll
-        for (int sw = 0; sw < SW; ++sw)
+        for (int ks = 0; ks < 4; ++ks)
+            x.qa[ks] = *reinterpret_cast<const bf16x8*>(cur + C::B_QP + ((mt * 4 + ks) * 64 + lane) * 16);
+    };
+    auto out_tile = [&](int mt, const OutOps& x, const bf16x8 (&Sb)[4]) {
+        f32x4 o = widen(x.op);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) o = mfma(Sb[ks], x.qa[ks], o);
+        if (kGate) {
+            const f32x4 zf = widen(x.zp);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[i] *= sigmoid_fast(zf[i]);
+        }
+        *reinterpret_cast<uint2*>(stage + stage_off(mt)) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+    };
+    if ((wave & 1) == 0) {
+        f32x4 S[8];  // S[t][i] = state[16t + 4g + i][col0]
+        const int64_t sidx = grp * (128 * 128);
+        if (a.S0 != nullptr) {  // one uniform branch: all loads in flight together
 #pragma unroll
             for (int t = 0; t < 8; ++t)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) S[sw][t][i] = a.S0[sidx + (16 * t + 4 * g + i) * 128 + col0 + 16 * sw];
-    } else {
+                for (int i = 0; i < 4; ++i) S[t][i] = a.S0[sidx + (16 * t + 4 * g + i) * 128 + col0];
+        } else {
 #pragma unroll
-        for (int sw = 0; sw < SW; ++sw)
+            for (int t = 0; t < 8; ++t) S[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        bf16x8 Sb[4];
 #pragma unroll
-            for (int t = 0; t < 8; ++t) S[sw][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-
-    for (int j = 0; j < nch; ++j) {
-        const char* cur = buf_of(j);
-        lds_barrier();  // A_j: part A of chunk j is in LDS; the staging tile is free
-
-        bf16x8 Sb[SW][4];
+        for (int ks = 0; ks < 4; ++ks) {
+            Sb[ks] = to_bf16x8(S[2 * ks], S[2 * ks + 1]);
+            *reinterpret_cast<bf16x8*>(sbx + (ks * 64 + lane) * 16) = Sb[ks];
+        }
+        for (int j = 0; j < nch; ++j) {
+            const char* cur = buf_of(j);
+            lds_barrier();  // A_j: part A of chunk j is in LDS
+            // U = U~ - W S; the reads of row tile mt + 1 go out before the
+            // products of tile mt
+            struct ChainOps {
+                uint2 up;
+                bf16x8 wa[4];
+            };
+            auto load_tile = [&](int mt, ChainOps& x) {
+                x.up = *reinterpret_cast<const uint2*>(cur + C::B_UT + ((ls * 4 + mt) * 64 + lane) * 8);
 #pragma unroll
-        for (int sw = 0; sw < SW; ++sw)
+                for (int ks = 0; ks < 4; ++ks)
+                    x.wa[ks] = *reinterpret_cast<const bf16x8*>(cur + C::B_NEGW + ((mt * 4 + ks) * 64 + lane) * 16);
+            };
+            f32x4 U[4];
+            ChainOps ops[2];
+            OutOps oops;
+            load_tile(0, ops[0]);
+            load_out(cur, 3, oops);
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) Sb[sw][ks] = to_bf16x8(S[sw][2 * ks], S[sw][2 * ks + 1]);
-        // U = U~ - W S, and the output transposed: O^T = (M U~)^T + S^T Q'^T
-        // (the state operand and the Q' operand swap roles): lane (g, c) holds
-        // token 16 mt + c, columns 16 slice + 4 g .. + 3.  The LDS reads of
-        // row tile mt + 1 are issued before the products of tile mt, so their
-        // latency overlaps the matrix-core work.
-        struct TileOps {
-            uint2 up[SW], op[SW], zp[SW];
-            bf16x8 wa[4], qa[4];
-        };
-        auto stage_off = [&](int mt, int sw) {
-            // columns 16 ls + 4 g .. + 3 of the group: piece 2 ls + g/2, bytes 8 (g & 1)
-            const int ls = SW * wave + sw;
-            const int r = 16 * mt + c;
-            return r * RB + tile_slot<SB>(r, 2 * ls + (g >> 1)) * 16 + 8 * (g & 1);
-        };
-        auto load_tile = [&](int mt, TileOps& x) {
+            for (int mt = 0; mt < 4; ++mt) {
+                if (mt < 3) load_tile(mt + 1, ops[(mt + 1) & 1]);
+                const ChainOps& x = ops[mt & 1];
+                U[mt] = widen(x.up);
 #pragma unroll
-            for (int sw = 0; sw < SW; ++sw) {
-                const int ls = SW * wave + sw;  // slice within the group
-                x.up[sw] = *reinterpret_cast<const uint2*>(cur + C::B_UT + ((ls * 4 + mt) * 64 + lane) * 8);
-                x.op[sw] = *reinterpret_cast<const uint2*>(cur + C::B_OI + ((ls * 4 + mt) * 64 + lane) * 8);
-                if (kGate) x.zp[sw] = *reinterpret_cast<const uint2*>(cur + C::B_Z + stage_off(mt, sw));
+                for (int ks = 0; ks < 4; ++ks) U[mt] = mfma(x.wa[ks], Sb[ks], U[mt]);
+            }
+            out_tile(3, oops, Sb);
+            lds_barrier();  // M_j: part B of chunk j is in LDS; the output wave is done with the operand
+            // S <- Diag(gamma) S + K^T U, with every K^T and gamma read issued first
+            bf16x8 ka[8][2];
+            float4 gm[8];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                gm[t] = *reinterpret_cast<const float4*>(cur + C::B_GAM + (16 * t + 4 * g) * 4);
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+                    ka[t][ks] = *reinterpret_cast<const bf16x8*>(cur + C::B_KHT + ((t * 2 + ks) * 64 + lane) * 16);
+            }
+            const bf16x8 Ub[2] = {to_bf16x8(U[0], U[1]), to_bf16x8(U[2], U[3])};
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                S[t][0] *= gm[t].x;
+                S[t][1] *= gm[t].y;
+                S[t][2] *= gm[t].z;
+                S[t][3] *= gm[t].w;
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) S[t] = mfma(ka[t][ks], Ub[ks], S[t]);
             }
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
-                const int blk = (mt * 4 + ks) * 64 + lane;
-                x.wa[ks] = *reinterpret_cast<const bf16x8*>(cur + C::B_NEGW + blk * 16);
-                x.qa[ks] = *reinterpret_cast<const bf16x8*>(cur + C::B_QP + blk * 16);
-            }
-        };
-        auto widen = [](uint2 p) {
-            return f32x4{__uint_as_float(p.x << 16), __uint_as_float(p.x & 0xffff0000u), __uint_as_float(p.y << 16),
-                         __uint_as_float(p.y & 0xffff0000u)};
-        };
-        f32x4 U[SW][4];
-        TileOps ops[2];
-        load_tile(0, ops[0]);
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-            TileOps& x = ops[mt & 1];
-            if (mt < 3) load_tile(mt + 1, ops[(mt + 1) & 1]);
-            f32x4 o[SW];
-#pragma unroll
-            for (int sw = 0; sw < SW; ++sw) {
-                U[sw][mt] = widen(x.up[sw]);
-                o[sw] = widen(x.op[sw]);
-            }
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-                for (int sw = 0; sw < SW; ++sw) {
-                    U[sw][mt] = mfma(x.wa[ks], Sb[sw][ks], U[sw][mt]);
-                    o[sw] = mfma(Sb[sw][ks], x.qa[ks], o[sw]);
-                }
-#pragma unroll
-            for (int sw = 0; sw < SW; ++sw) {
-                if (kGate) {
-                    const f32x4 zf = widen(x.zp[sw]);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) o[sw][i] *= sigmoid_fast(zf[i]);
-                }
-                *reinterpret_cast<uint2*>(stage + stage_off(mt, sw)) =
-                    make_uint2(pack_bf16x2(o[sw][0], o[sw][1]), pack_bf16x2(o[sw][2], o[sw][3]));
+                Sb[ks] = to_bf16x8(S[2 * ks], S[2 * ks + 1]);
+                *reinterpret_cast<bf16x8*>(sbx + (ks * 64 + lane) * 16) = Sb[ks];
             }
         }
-        lds_barrier();  // M_j: the output tile is staged; part B of chunk j is in LDS
-        // S <- Diag(gamma) S + K^T U, with every K^T and gamma read issued first
-        bf16x8 ka[8][2];
-        float4 gm[8];
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            gm[t] = *reinterpret_cast<const float4*>(cur + C::B_GAM + (16 * t + 4 * g) * 4);
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
-                ka[t][ks] = *reinterpret_cast<const bf16x8*>(cur + C::B_KHT + ((t * 2 + ks) * 64 + lane) * 16);
-        }
-        bf16x8 Ub[SW][2];
-#pragma unroll
-        for (int sw = 0; sw < SW; ++sw)
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) Ub[sw][ks] = to_bf16x8(U[sw][2 * ks], U[sw][2 * ks + 1]);
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-#pragma unroll
-            for (int sw = 0; sw < SW; ++sw) {
-                S[sw][t][0] *= gm[t].x;
-                S[sw][t][1] *= gm[t].y;
-                S[sw][t][2] *= gm[t].z;
-                S[sw][t][3] *= gm[t].w;
-            }
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-                for (int sw = 0; sw < SW; ++sw) S[sw][t] = mfma(ka[t][ks], Ub[sw][ks], S[sw][t]);
-        }
-    }
-    if (a.S_out) {
-#pragma unroll
-        for (int sw = 0; sw < SW; ++sw)
+        if (a.S_out) {
 #pragma unroll
             for (int t = 0; t < 8; ++t)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) a.S_out[sidx + (16 * t + 4 * g + i) * 128 + col0 + 16 * sw] = S[sw][t][i];
+                for (int i = 0; i < 4; ++i) a.S_out[sidx + (16 * t + 4 * g + i) * 128 + col0] = S[t][i];
+        }
+    } else {
+        for (int j = 0; j < nch; ++j) {
+            const char* cur = buf_of(j);
+            lds_barrier();  // A_j: part A of chunk j and the state operand are in LDS; the staging tile is free
+            bf16x8 Sb[4];
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) Sb[ks] = *reinterpret_cast<const bf16x8*>(sbx + (ks * 64 + lane) * 16);
+            // row tiles 0-2; the reads of tile mt + 1 go out before the products of tile mt
+            OutOps ops[2];
+            load_out(cur, 0, ops[0]);
+#pragma unroll
+            for (int mt = 0; mt < 3; ++mt) {
+                if (mt < 2) load_out(cur, mt + 1, ops[(mt + 1) & 1]);
+                out_tile(mt, ops[mt & 1], Sb);
+            }
+            lds_barrier();  // M_j: the output tile is staged
+        }
     }
 }
 
-template <typename GT, bool kGate, int NS, int SW>
+template <typename GT, bool kGate, int NS>
 hipError_t launch_state(const MfmaK<GT>& k, hipStream_t s) {
-    using C = StateCfg<NS * SW>;
-    constexpr int P = 8 / (NS * SW);
-    const void* fn = reinterpret_cast<const void*>(&mfma_state_kernel<GT, kGate, NS, SW>);
+    using C = StateCfg<NS>;
+    constexpr int P = 8 / NS;
+    const void* fn = reinterpret_cast<const void*>(&mfma_state_kernel<GT, kGate, NS>);
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(C::kLds));
     if (e != hipSuccess) return e;
     const int64_t blocks = (k.groups + 7) / 8 * 8 * P;
-    hipLaunchKernelGGL((mfma_state_kernel<GT, kGate, NS, SW>), dim3(static_cast<unsigned>(blocks)),
-                       dim3(64 * (NS + 4)), C::kLds, s, k);
+    hipLaunchKernelGGL((mfma_state_kernel<GT, kGate, NS>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(64 * (2 * NS + C::kMemWaves)), C::kLds, s, k);
     return hipGetLastError();
 }
 
 // Workgroup shape of the state pass.  Few (sequence, head) pairs: spread
-// each head over 8 workgroups of one compute wave (one 16-column slice), so
-// every CU takes part.  Many: one workgroup of four compute waves per half
-// head, so each copied factor serves four slices.  KDA_STATE_SHAPE=1 or 4 in
-// the environment forces the number of compute waves (the tests use it to
-// cover both).
+// each head over 8 workgroups of one 16-column slice, so every CU takes
+// part.  Many: one workgroup per quarter head (two slices), so each copied
+// factor serves two slices.  KDA_STATE_SHAPE=1 or 2 in the environment forces
+// the number of slices per workgroup (the tests use it to cover both).
 template <typename GT, bool kGate>
 hipError_t launch_state_for(const MfmaK<GT>& k, hipStream_t s, int cus) {
-    int ns = k.groups * 8 <= cus ? 1 : 4;
+    int ns = k.groups * 8 <= cus ? 1 : 2;
     if (const char* env = getenv("KDA_STATE_SHAPE")) {
         const int f = atoi(env);
-        if (f == 1 || f == 4) ns = f;
+        if (f == 1 || f == 2) ns = f;
     }
-    return ns == 1 ? launch_state<GT, kGate, 1, 1>(k, s) : launch_state<GT, kGate, 4, 1>(k, s);
+    return ns == 1 ? launch_state<GT, kGate, 1>(k, s) : launch_state<GT, kGate, 2>(k, s);
 }
 
 // the two kernels of the chunked prefill; kFused: k.q, k.k, k.v, k.la and
