@@ -637,21 +637,17 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
             // on distinct banks
             constexpr int XS = 20, XB = 16 * XS;
             float* sX = sTot;
-            // acc[i] += sum_k P[4g+i][k] Q[k][c] over a 16 x 16 pair
+            // acc[i] += sum_k P[4g+i][k] Q[k][c] over a 16 x 16 pair, in fp32 on
+            // the matrix cores: v_mfma_f32_16x16x4_f32 takes A[c][g] and B[g][c]
+            // from lane (g, c) and leaves D[4g + i][c], four steps of 4 in k
             auto mm16 = [&](const float* P, int ldp, const float* Q, int ldq, float (&acc)[4]) {
-                float qc[16];
+                f32x4 d = {acc[0], acc[1], acc[2], acc[3]};
 #pragma unroll
-                for (int kk = 0; kk < 16; ++kk) qc[kk] = Q[kk * ldq + c];
+                for (int s4 = 0; s4 < 4; ++s4)
+                    d = __builtin_amdgcn_mfma_f32_16x16x4f32(P[c * ldp + 4 * s4 + g], Q[(4 * s4 + g) * ldq + c], d,
+                                                             0, 0, 0);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float4* prow = reinterpret_cast<const float4*>(P + (4 * g + i) * ldp);
-#pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4) {
-                        const float4 v4 = prow[q4];
-                        acc[i] += v4.x * qc[4 * q4] + v4.y * qc[4 * q4 + 1] + v4.z * qc[4 * q4 + 2] +
-                                  v4.w * qc[4 * q4 + 3];
-                    }
-                }
+                for (int i = 0; i < 4; ++i) acc[i] = d[i];
             };
             if (wave < 2) {
                 const int R = 2 * wave + 1, S = R - 1;
