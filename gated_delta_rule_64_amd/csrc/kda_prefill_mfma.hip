@@ -55,7 +55,8 @@ constexpr int KS = 136;  // bf16 per row of K, Q, V
 constexpr int GS = 132;  // fp32 per row of G
 constexpr int MS = 68;   // fp32 per row of A, M and T (16 lanes reading 16 rows hit distinct banks)
 constexpr int SQS = 136; // bf16 per row of the Q' staging tile (the same bytes per row as A)
-constexpr float kDiagRange = 40.f;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kDiagRange = 40.f * kLog2e;  // e^40, in the log2 units G is kept in
 
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -186,7 +187,7 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
     uint16_t* sK = reinterpret_cast<uint16_t*>(smem);   // [64][KS] keys (bf16)
     uint16_t* sQ = sK + 64 * KS;                        // [64][KS] queries
     uint16_t* sV = sQ + 64 * KS;                        // [64][KS] values
-    float* sG = reinterpret_cast<float*>(sV + 64 * KS);  // [64][GS] decay cumsums
+    float* sG = reinterpret_cast<float*>(sV + 64 * KS);  // [64][GS] decay cumsums G, in log2 units (G / ln 2)
     float* sA = sG + 64 * GS;                           // [64][MS]
     float* sM = sA + 64 * MS;                           // [64][MS]
     float* sT = sM + 64 * MS;                           // [64][MS]
@@ -435,7 +436,8 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const float gv = px[j].get(e);
-                x[j][e] = 4 * rg + j < L ? (kFused ? -softplus_fast(gv) : gv) : 0.f;
+                // decay logs in log2 units: every use of G is 2^(difference)
+                x[j][e] = 4 * rg + j < L ? (kFused ? -softplus_fast(gv) : gv) * kLog2e : 0.f;
             }
         {
             const float bv = ld(&pb);
@@ -515,7 +517,7 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
                         float av = 0.f, mv = 0.f;
                         if (s2 <= r) {
                             for (int ch = 32 * k0; ch < 32 * k1; ++ch) {
-                                const float ks = bfv(sK + s2 * KS + ch) * expf(sG[r * GS + ch] - sG[s2 * GS + ch]);
+                                const float ks = bfv(sK + s2 * KS + ch) * exp2f(sG[r * GS + ch] - sG[s2 * GS + ch]);
                                 av += bfv(sK + r * KS + ch) * ks;
                                 mv += bfv(sQ + r * KS + ch) * ks;
                             }
@@ -536,10 +538,10 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
                         lds8f(sG + sr * GS + ch0, gr);
 #pragma unroll
                         for (int e = 0; e < 8; ++e) {
-                            const float el = __expf(gl[e] - gb[e]);  // <= 1
+                            const float el = __builtin_amdgcn_exp2f(gl[e] - gb[e]);  // <= 1
                             kl[e] *= el;
                             ql[e] *= el;
-                            kr[e] *= __expf(gb[e] - gr[e]);
+                            kr[e] *= __builtin_amdgcn_exp2f(gb[e] - gr[e]);
                         }
                         const bf16x8 bk = to_bf16x8(kr);
                         accA = mfma(to_bf16x8(kl), bk, accA);
@@ -713,7 +715,7 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const int s2 = s0 + e;
-                    bk[e] = bt[e] * __expf(sG[s2 * GS + chn]) * bfv(sK + s2 * KS + chn);
+                    bk[e] = bt[e] * __builtin_amdgcn_exp2f(sG[s2 * GS + chn]) * bfv(sK + s2 * KS + chn);
                     bv[e] = bt[e] * bfv(sV + s2 * KS + chn);
                 }
                 const bf16x8 Bk = to_bf16x8(bk), Bv = to_bf16x8(bv);
@@ -765,7 +767,7 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int r = 16 * mt + 4 * g + i;
-                    qp[i] = __expf(sG[r * GS + chn]) * bfv(sQ + r * KS + chn);
+                    qp[i] = __builtin_amdgcn_exp2f(sG[r * GS + chn]) * bfv(sQ + r * KS + chn);
                 }
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
@@ -814,7 +816,7 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const int s2 = 32 * ks + perm(g, e);
-                    kv[e] = __expf(glast - sG[s2 * GS + ch]) * bfv(sK + s2 * KS + ch);
+                    kv[e] = __builtin_amdgcn_exp2f(glast - sG[s2 * GS + ch]) * bfv(sK + s2 * KS + ch);
                 }
                 uint4 p;
                 p.x = pack_bf16x2(kv[0], kv[1]);
@@ -823,7 +825,7 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
                 p.w = pack_bf16x2(kv[6], kv[7]);
                 *reinterpret_cast<uint4*>(rec + R_KHT + ((t * 2 + ks) * 64 + lane) * 16) = p;
             }
-            if (tid < 128) reinterpret_cast<float*>(rec + R_GAM)[tid] = expf(sG[63 * GS + tid]);
+            if (tid < 128) reinterpret_cast<float*>(rec + R_GAM)[tid] = exp2f(sG[63 * GS + tid]);
         }
         lds_barrier();  // every LDS buffer is free for the next unit
         // Leave before staging rather than staging conditionally: the loop's
