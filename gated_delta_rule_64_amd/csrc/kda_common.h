@@ -91,10 +91,15 @@ __device__ __forceinline__ float softplus(float x) {
 __device__ __forceinline__ float sigmoid(float x) { return 1.f / (1.f + expf(-x)); }
 // sigmoid with the hardware exponential and reciprocal (about 2 ulp)
 __device__ __forceinline__ float sigmoid_fast(float x) { return __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
-// softplus with the hardware exponential and logarithm
-__device__ __forceinline__ float softplus_fast(float x) {
-    return fmaxf(x, 0.f) + __logf(1.f + __expf(-fabsf(x)));
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+// softplus(x) / ln 2 with the hardware base-2 exponential and logarithm
+// (v_exp_f32, v_log_f32): log2(1 + e^x) = max(x, 0) log2(e) + log2(1 + 2^(-|x| log2 e)),
+// and the log's argument lies in (1, 2], so it needs no range handling
+__device__ __forceinline__ float softplus_log2(float x) {
+    return fmaxf(x, 0.f) * kLog2e + __builtin_amdgcn_logf(1.f + __builtin_amdgcn_exp2f(-fabsf(x) * kLog2e));
 }
+__device__ __forceinline__ float softplus_fast(float x) { return softplus_log2(x) * kLn2; }
 
 // the L2 norm's epsilon: x / sqrt(|x|^2 + eps)
 constexpr float kL2Eps = 1e-6f;

@@ -55,7 +55,6 @@ constexpr int KS = 136;  // bf16 per row of K, Q, V
 constexpr int GS = 132;  // fp32 per row of G
 constexpr int MS = 68;   // fp32 per row of A, M and T (16 lanes reading 16 rows hit distinct banks)
 constexpr int SQS = 136; // bf16 per row of the Q' staging tile (the same bytes per row as A)
-constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kDiagRange = 40.f * kLog2e;  // e^40, in the log2 units G is kept in
 
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -436,8 +435,10 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const float gv = px[j].get(e);
-                // decay logs in log2 units: every use of G is 2^(difference)
-                x[j][e] = 4 * rg + j < L ? (kFused ? -softplus_fast(gv) : gv) * kLog2e : 0.f;
+                // decay logs in log2 units: every use of G is 2^(difference);
+                // computed for every row, padded rows masked afterwards
+                const float lg = kFused ? -softplus_log2(gv) : gv * kLog2e;
+                x[j][e] = 4 * rg + j < L ? lg : 0.f;
             }
         {
             const float bv = ld(&pb);
