@@ -374,38 +374,37 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
                 }
             }
             lds_barrier();
-            // conv (tap 3 is the current token) of the thread's two rows of each
-            // tensor, all reads of a tensor issued before the arithmetic that
-            // needs them; then the L2 norm of q and k over the 128 channels a
-            // 16-lane row of the wave holds
-            const int ch8 = 8 * (tid & 15);
+            // conv (tap 3 is the current token) of the thread's two consecutive
+            // rows 2k, 2k+1 of each tensor, from the five raw rows 2k-3 .. 2k+1
+            // (the first ones reach into the history), all reads of a tensor
+            // issued before the arithmetic that needs them; then the L2 norm
+            // of q and k over the 128 channels a 16-lane group holds
+            const int ch8 = 8 * (tid & 15), r0 = 2 * (tid >> 4);
 #pragma unroll
             for (int tt = 0; tt < 3; ++tt) {
                 float w[4][8];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) lds8f(taps + tt * 512 + j * 128 + ch8, w[j]);
+                float xv[5][8];
+                if (r0 >= 4) {  // every tap inside the chunk: one straight run of reads
+#pragma unroll
+                    for (int m = 0; m < 5; ++m)
+                        unpack8(*reinterpret_cast<const uint4*>(raw + tt * 64 * KS + (r0 - 3 + m) * KS + ch8), xv[m]);
+                } else {
+#pragma unroll
+                    for (int m = 0; m < 5; ++m) {
+                        const int rr = r0 - 3 + m;
+                        if (rr >= 0) unpack8(*reinterpret_cast<const uint4*>(raw + tt * 64 * KS + rr * KS + ch8), xv[m]);
+                        else lds8f(hist + (tt * 3 + rr + 3) * 128 + ch8, xv[m]);
+                    }
+                }
                 float y[2][8];
 #pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    const int r = (tid + kIntraThreads * i) >> 4;
-                    float xv[4][8];
-                    if (r >= 3) {  // every tap inside the chunk: one straight run of reads
-#pragma unroll
-                        for (int j = 0; j < 4; ++j)
-                            unpack8(*reinterpret_cast<const uint4*>(raw + tt * 64 * KS + (r - 3 + j) * KS + ch8), xv[j]);
-                    } else {  // the first three rows reach into the history
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            const int rr = r - 3 + j;
-                            if (rr >= 0) unpack8(*reinterpret_cast<const uint4*>(raw + tt * 64 * KS + rr * KS + ch8), xv[j]);
-                            else lds8f(hist + (tt * 3 + rr + 3) * 128 + ch8, xv[j]);
-                        }
-                    }
+                for (int i = 0; i < 2; ++i)
 #pragma unroll
                     for (int c8 = 0; c8 < 8; ++c8)
-                        y[i][c8] = w[0][c8] * xv[0][c8] + w[1][c8] * xv[1][c8] + w[2][c8] * xv[2][c8] +
-                                   w[3][c8] * xv[3][c8];
-                }
+                        y[i][c8] = w[0][c8] * xv[i][c8] + w[1][c8] * xv[i + 1][c8] + w[2][c8] * xv[i + 2][c8] +
+                                   w[3][c8] * xv[i + 3][c8];
                 if (tt < 2) {
 #pragma unroll
                     for (int i = 0; i < 2; ++i) {
@@ -420,7 +419,7 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
                 uint16_t* dst = tt == 0 ? sQ : (tt == 1 ? sK : sV);
 #pragma unroll
                 for (int i = 0; i < 2; ++i) {
-                    const int r = (tid + kIntraThreads * i) >> 4;
+                    const int r = r0 + i;
                     const uint32_t m = r < L ? 0xffffffffu : 0u;  // padded rows: zero
                     *reinterpret_cast<uint4*>(dst + r * KS + ch8) =
                         make_uint4(pack_bf16x2(y[i][0], y[i][1]) & m, pack_bf16x2(y[i][2], y[i][3]) & m,
