@@ -40,6 +40,17 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2v __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
+
+// Record stores: non-temporal (streamed past the caches; measured faster for
+// both the writer and the state pass that reads the records back).
+__device__ __forceinline__ void rec_store8(char* p, uint2 v) {
+    __builtin_nontemporal_store(u32x2v{v.x, v.y}, reinterpret_cast<u32x2v*>(p));
+}
+__device__ __forceinline__ void rec_store16(char* p, uint4 v) {
+    __builtin_nontemporal_store(u32x4v{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4v*>(p));
+}
 
 // per (chunk slot, head) record, byte offsets
 constexpr int R_NEGW = 0;       // -W, A-operand layout, [4 m][4 k][64 lanes][8]
@@ -732,7 +743,7 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
                 uint2 p;
                 p.x = pack_bf16x2(accU[mt][0], accU[mt][1]);
                 p.y = pack_bf16x2(accU[mt][2], accU[mt][3]);
-                *reinterpret_cast<uint2*>(rec + R_UT + ((nt * 4 + mt) * 64 + lane) * 8) = p;
+                rec_store8(rec + R_UT + ((nt * 4 + mt) * 64 + lane) * 8, p);
             }
         }
         lds_barrier();  // V and A are dead: their buffers become the staging areas
@@ -780,7 +791,7 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
                 uint2 p;
                 p.x = pack_bf16x2(oi[0], oi[1]);
                 p.y = pack_bf16x2(oi[2], oi[3]);
-                *reinterpret_cast<uint2*>(rec + R_OI + ((nt * 4 + mt) * 64 + lane) * 8) = p;
+                rec_store8(rec + R_OI + ((nt * 4 + mt) * 64 + lane) * 8, p);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int r = 16 * mt + 4 * g + i;
@@ -804,8 +815,8 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
                 const uint2 qlo = *reinterpret_cast<const uint2*>(sStQ + r * SQS + c0);
                 const uint2 qhi = *reinterpret_cast<const uint2*>(sStQ + r * SQS + c0 + 16);
                 const int blk = (mt * 4 + ks) * 64 + lane;
-                *reinterpret_cast<uint4*>(rec + R_NEGW + blk * 16) = make_uint4(wlo.x, wlo.y, whi.x, whi.y);
-                *reinterpret_cast<uint4*>(rec + R_QP + blk * 16) = make_uint4(qlo.x, qlo.y, qhi.x, qhi.y);
+                rec_store16(rec + R_NEGW + blk * 16, make_uint4(wlo.x, wlo.y, whi.x, whi.y));
+                rec_store16(rec + R_QP + blk * 16, make_uint4(qlo.x, qlo.y, qhi.x, qhi.y));
             }
             const int t = wave;
             const int ch = 16 * t + c;
@@ -823,7 +834,7 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
                 p.y = pack_bf16x2(kv[2], kv[3]);
                 p.z = pack_bf16x2(kv[4], kv[5]);
                 p.w = pack_bf16x2(kv[6], kv[7]);
-                *reinterpret_cast<uint4*>(rec + R_KHT + ((t * 2 + ks) * 64 + lane) * 16) = p;
+                rec_store16(rec + R_KHT + ((t * 2 + ks) * 64 + lane) * 16, p);
             }
             if (tid < 128) reinterpret_cast<float*>(rec + R_GAM)[tid] = exp2f(sG[63 * GS + tid]);
         }
