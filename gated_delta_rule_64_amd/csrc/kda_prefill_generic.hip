@@ -17,8 +17,9 @@ __global__ __launch_bounds__(1024) void chunk_map_kernel(const int32_t* __restri
                                                          int64_t T, int32_t* __restrict__ base,
                                                          SlotInfo* __restrict__ slot_info) {
     __shared__ int32_t buf[1024];
+    __shared__ int32_t wsum[16];
     __shared__ int32_t carry_s;
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     if (tid == 0) carry_s = 0;
     __syncthreads();
     // sequences in blocks of 1024, one per thread
@@ -29,15 +30,28 @@ __global__ __launch_bounds__(1024) void chunk_map_kernel(const int32_t* __restri
             const int64_t L = seq_finish(cu, i, T) - seq_begin(cu, i);
             c = static_cast<int32_t>((L + kChunk - 1) / kChunk);
         }
-        buf[tid] = c;
-        __syncthreads();
-        // Hillis-Steele inclusive scan
-        for (int off = 1; off < 1024; off <<= 1) {
-            const int32_t x = tid >= off ? buf[tid - off] : 0;
-            __syncthreads();
-            buf[tid] += x;
-            __syncthreads();
+        // inclusive scan: within each wave by lane shuffles, then over the
+        // 16 wave totals in wave 0
+        int32_t x = c;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int32_t y = __shfl_up(x, off);
+            if (lane >= off) x += y;
         }
+        if (lane == 63) wsum[wave] = x;
+        __syncthreads();
+        if (wave == 0) {
+            int32_t w = lane < 16 ? wsum[lane] : 0;
+#pragma unroll
+            for (int off = 1; off < 16; off <<= 1) {
+                const int32_t y = __shfl_up(w, off);
+                if (lane >= off) w += y;
+            }
+            if (lane < 16) wsum[lane] = w;
+        }
+        __syncthreads();
+        buf[tid] = x + (wave > 0 ? wsum[wave - 1] : 0);
+        __syncthreads();
         const int32_t carry = carry_s;
         if (i < N) base[i] = carry + buf[tid] - c;
         // the block's slots, spread over all threads: slot carry + s belongs
