@@ -10,7 +10,9 @@ resident in HBM.  The same work as two calls (``kda_preprocess`` then
 
 The decode step (256 sequences x 32 heads x 128^2 fp32 state, in place) is
 timed in its own loop and reported under ``decode`` in GB/s of algorithmic
-traffic.  ``roofline`` covers the kernel with the largest share of the step:
+traffic; the fused serving call (raw token in, preprocess and step in one
+kernel, conv history and state rolled in place) likewise under
+``decode_layer``.  ``roofline`` covers the kernel with the largest share of the step:
 algorithmic bytes per launch / average launch time from HIP events recorded
 around each kernel during a second pass of the same K steps.  ``cpu_baseline``
 times the fp64 CPU oracle on the same workload (rank 0, one GPU only).
@@ -106,6 +108,16 @@ def prefill_kernel_bytes(name, w, x, g, rec, has_s0, has_gate):
 def decode_bytes(B, H, dk, dv, x, g, has_gate):
     per = 2 * dk * dv * 4 + x * (2 * dk + dv) + g * (dk + 1) + x * dv * (2 if has_gate else 1)
     return B * H * per
+
+
+def decode_layer_bytes(B, H, dk, dv, x, has_gate):
+    """Algorithmic bytes of one fused decode-layer call: per (sequence, head)
+    the state read and written, the raw token (q, k, v, decay and write
+    logits), the three-token conv history read and rewritten, the output (and
+    gate); per call the conv taps once."""
+    w = 2 * dk + dv
+    per = 2 * dk * dv * 4 + x * (w + dk + 1) + 2 * 3 * w * 4 + x * dv * (2 if has_gate else 1)
+    return B * H * per + H * w * 4 * x
 
 
 def traffic_entry(kernel):
@@ -245,6 +257,39 @@ def bench_decode(args):
             "roofline": roofline("decode", b, per_ms)}
 
 
+def bench_decode_layer(args):
+    """The fused serving call (raw token -> output, history and state rolled in
+    place) on the same 256 x 32 x 128^2 workload."""
+    import torch
+    from gated_delta_rule_64_amd import _lib, kda, synth
+
+    inp = synth.make("decode_b256")
+    H, dk, dv, B = inp["H"], inp["dk"], inp["dv"], inp["N"]
+    raw = [dev(inp[n]) for n in ("q_in", "k_in", "v_in", "w_q", "w_k", "w_v", "g", "b")]
+    cs = dev(inp["conv_state"])
+    z = dev(inp["z"]).view(B, H, dv)
+    state = dev(inp["S0"])
+    out = torch.empty((B, H, dv), dtype=torch.bfloat16, device="cuda")
+    for _ in range(args.warmup):
+        kda.kda_decode_layer(*raw, H, dk, dv, cs, state, out_gate=z, out=out)
+    torch.cuda.synchronize()
+    _lib.profile_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(args.decode_steps):
+        kda.kda_decode_layer(*raw, H, dk, dv, cs, state, out_gate=z, out=out)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    _lib.profile_enable(False)
+    n, ms = _lib.profile_collect()["decode_layer"]
+    per_ms = ms / n
+    b = decode_layer_bytes(B, H, dk, dv, 2, True)
+    return {"metric": "fused decode-layer achieved HBM GB/s", "value": round(b / (per_ms * 1e-3) / 1e9, 1),
+            "unit": "GB/s", "workload": "decode_b256", "B": B, "H": H, "dk": dk, "dv": dv,
+            "steps": args.decode_steps, "us_per_step_events": round(per_ms * 1e3, 2),
+            "us_per_step_wall": round(elapsed / args.decode_steps * 1e6, 2),
+            "roofline": roofline("decode_layer", b, per_ms)}
+
+
 def cpu_baseline(res, min_seconds=10.0, max_passes=100):
     """The fp64 oracle (preprocess + token-by-token recurrence) on the bench's
     own inputs, repeated whole until at least ``min_seconds`` of CPU work."""
@@ -326,6 +371,7 @@ def main():
         "ms_per_step_two_calls": round(res["elapsed_two_calls"] / args.steps * 1e3, 4),
     }
     line["decode"] = bench_decode(args)
+    line["decode_layer"] = bench_decode_layer(args)
     if args.copy_calibration:
         line["copy_calibration"] = copy_calibration()
     if not args.no_cpu_baseline:

@@ -34,6 +34,7 @@ PROTOTYPES = {
     "kda_decode_step": (ctypes.c_int, [_i32, _i32, _i32, _i32, _i32, _i32] + [_vp] * 6 + [_vp, _vp, _vp]),
     "kda_prefill_layer": (ctypes.c_int, [_i64, _i32, _i32, _i32, _vp, _i32, _i32] + [_vp] * 8 +
                           [_vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "kda_decode_layer": (ctypes.c_int, [_i32, _i32, _i32, _i32, _i32] + [_vp] * 8 + [_vp, _vp, _vp, _i32, _vp, _vp, _vp]),
 }
 
 

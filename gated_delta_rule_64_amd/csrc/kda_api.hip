@@ -86,6 +86,25 @@ int debug_check_cu(const int32_t* cu, int32_t N, int64_t T, hipStream_t s) {
     return KDA_OK;
 }
 
+// Optional host-side check that the valid entries of state_indices are
+// distinct (synchronises the stream).
+int debug_check_indices(const int32_t* idx, int32_t B, int32_t slots, hipStream_t s) {
+    const char* env = getenv("KDA_DEBUG_CHECK");
+    if (idx == nullptr || B == 0 || env == nullptr || strcmp(env, "1") != 0) return KDA_OK;
+    std::vector<int32_t> h(static_cast<size_t>(B));
+    hipError_t e = hipMemcpyAsync(h.data(), idx, h.size() * 4, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "copy of state_indices for KDA_DEBUG_CHECK");
+    std::vector<int32_t> seen(static_cast<size_t>(slots), -1);
+    for (int32_t b = 0; b < B; ++b) {
+        const int32_t i = h[b];
+        if (i < 0 || i >= slots) continue;
+        if (seen[i] >= 0) return fail(KDA_ERR_INVALID_ARGUMENT, "state_indices[%d] = state_indices[%d] = %d", seen[i], b, i);
+        seen[i] = b;
+    }
+    return KDA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -103,7 +122,7 @@ const char* kda_status_string(int status) {
 
 const char* kda_last_error_detail(void) { return g_detail; }
 
-int kda_abi_version(void) { return 100; }
+int kda_abi_version(void) { return 101; }
 
 int kda_preprocess(int64_t T_tot, int32_t H, int32_t dk, int32_t dv, const int32_t* cu_seqlens, int32_t N,
                    int32_t x_dtype, const void* q_in, const void* k_in, const void* v_in, const void* w_q,
@@ -305,6 +324,54 @@ int kda_decode_step(int32_t B, int32_t H, int32_t dk, int32_t dv, int32_t x_dtyp
     a.q = q; a.k = k; a.v = v; a.la = log_alpha; a.beta = beta; a.z = out_gate; a.state = state; a.out = out;
     hipError_t e = kda::launch_decode(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "decode launch");
+    return ok();
+}
+
+int kda_decode_layer(int32_t B, int32_t H, int32_t dk, int32_t dv, int32_t x_dtype, const void* q_in,
+                     const void* k_in, const void* v_in, const void* w_q, const void* w_k, const void* w_v,
+                     const void* g_alpha, const void* b_beta, float* conv_state, const void* out_gate,
+                     float* state, int32_t state_slots, const int32_t* state_indices, void* out, void* stream) {
+    if (B < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "B=%d must be >= 0", B);
+    if (H < 1 || H > 65535) return fail(KDA_ERR_INVALID_ARGUMENT, "H=%d out of range [1, 65535]", H);
+    if (!valid_head_dim(dk) || !valid_head_dim(dv))
+        return fail(KDA_ERR_UNSUPPORTED, "dk=%d, dv=%d: supported head sizes are 16, 32, 64, 128", dk, dv);
+    if (!valid_dtype(x_dtype)) return fail(KDA_ERR_INVALID_ARGUMENT, "x_dtype=%d is not KDA_F32 or KDA_BF16", x_dtype);
+    if (static_cast<int64_t>(B) * H >= (int64_t(1) << 31)) return fail(KDA_ERR_INVALID_ARGUMENT, "B*H too large");
+    if (state_indices == nullptr && state_slots != B)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "state_indices is NULL but state_slots=%d != B=%d", state_slots, B);
+    if (state_slots < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "state_slots=%d must be >= 0", state_slots);
+    if (static_cast<int64_t>(state_slots) * H >= (int64_t(1) << 31))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "state_slots*H too large");
+    const size_t xs = dsize(x_dtype);
+    const size_t BH = static_cast<size_t>(B) * H, SH = static_cast<size_t>(state_slots) * H;
+    const bool any = BH > 0;  // nothing is read or written when B == 0
+    std::vector<Span> sp = {
+        {"q_in", q_in, BH * dk * xs, false}, {"k_in", k_in, BH * dk * xs, false}, {"v_in", v_in, BH * dv * xs, false},
+        {"w_q", w_q, any ? static_cast<size_t>(H) * dk * 4 * xs : 0, false},
+        {"w_k", w_k, any ? static_cast<size_t>(H) * dk * 4 * xs : 0, false},
+        {"w_v", w_v, any ? static_cast<size_t>(H) * dv * 4 * xs : 0, false},
+        {"g_alpha", g_alpha, BH * dk * xs, false},
+        {"out_gate", out_gate, out_gate ? BH * dv * xs : 0, false},
+        {"conv_state", conv_state, any ? SH * 3 * (2 * dk + dv) * 4 : 0, true},
+        {"state", state, any ? SH * dk * dv * 4 : 0, true},
+        {"out", out, BH * dv * xs, true},
+    };
+    int st = check_spans(sp);
+    if (st != KDA_OK) return st;
+    if (any && (b_beta == nullptr || (reinterpret_cast<uintptr_t>(b_beta) % xs) != 0))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "b_beta is NULL or misaligned");
+    if (any && state_indices != nullptr && (reinterpret_cast<uintptr_t>(state_indices) & 3u) != 0)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "state_indices is not 4-byte aligned");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    st = debug_check_indices(state_indices, B, state_slots, s);
+    if (st != KDA_OK) return st;
+    kda::DecodeLayerArgs a;
+    a.B = B; a.H = H; a.dk = dk; a.dv = dv; a.x = static_cast<kda::DT>(x_dtype);
+    a.q_in = q_in; a.k_in = k_in; a.v_in = v_in; a.w_q = w_q; a.w_k = w_k; a.w_v = w_v;
+    a.g = g_alpha; a.b = b_beta; a.z = out_gate;
+    a.conv_state = conv_state; a.state = state; a.slots = state_slots; a.state_indices = state_indices; a.out = out;
+    hipError_t e = kda::launch_decode_layer(a, s);
+    if (e != hipSuccess) return hip_fail(e, "decode layer launch");
     return ok();
 }
 

@@ -27,6 +27,12 @@ __device__ __forceinline__ float ld(const bf16* p) { return bf16_to_f32(p->bits)
 __device__ __forceinline__ void st(float* p, float x) { *p = x; }
 __device__ __forceinline__ void st(bf16* p, float x) { p->bits = f32_to_bf16(x); }
 
+// x rounded to element type T and back (what a store and reload of x gives)
+template <typename T>
+__device__ __forceinline__ float round_to(float x) { return x; }
+template <>
+__device__ __forceinline__ float round_to<bf16>(float x) { return bf16_to_f32(f32_to_bf16(x)); }
+
 // 8 consecutive elements (16 B for bf16, 32 B for fp32), 16-byte aligned
 __device__ __forceinline__ void ld8(const float* p, float (&x)[8]) {
     const float4 a = reinterpret_cast<const float4*>(p)[0];

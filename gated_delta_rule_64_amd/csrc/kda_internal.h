@@ -42,6 +42,21 @@ struct DecodeArgs {
     void* out;
 };
 
+// One decode token per sequence with its preprocess fused in: raw q/k/v
+// projections, conv taps and gate logits in the input type; fp32 gates made
+// inside.  state and conv_state are pools of `slots` rows, row state_indices[b]
+// (b itself when state_indices is NULL) belonging to sequence b.
+struct DecodeLayerArgs {
+    int B, H, dk, dv;
+    DT x;
+    const void *q_in, *k_in, *v_in, *w_q, *w_k, *w_v, *g, *b, *z;
+    float* conv_state;
+    float* state;
+    int slots;
+    const int32_t* state_indices;
+    void* out;
+};
+
 // The whole layer (preprocess + chunked prefill) with the preprocess fused
 // into the chunk kernel; bf16 inputs, dk = dv = 128.
 struct LayerArgs {
@@ -63,6 +78,7 @@ hipError_t launch_conv_state_update(const PreprocessArgs& a, hipStream_t s);
 bool layer_fused_supported(int dk, int dv, DT x);
 hipError_t launch_layer(const LayerArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_decode_layer(const DecodeLayerArgs& a, hipStream_t s);
 
 // chunked prefill: workspace layout and the two implementations
 bool prefill_uses_mfma(int dk, int dv, DT x);

@@ -151,7 +151,7 @@ __global__ __launch_bounds__(256) void gen_intra_kernel(GenK<XT, GT> a) {
     __syncthreads();
     // K^ and gamma (G_last = G_63: padded rows add no decay)
     for (int i = tid; i < 64 * dk; i += 256) {
-        const int r = i / dk, c = i % dk;
+        const int c = i % dk;
         rec[R.Kh + i] = expf(sG[63 * dk + c] - sG[i]) * sK[i];
     }
     if (tid < dk) rec[R.gam + tid] = expf(sG[63 * dk + tid]);

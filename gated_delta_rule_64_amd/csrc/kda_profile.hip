@@ -12,6 +12,7 @@ namespace {
 struct Pending {
     const char* name;
     hipEvent_t start, stop;
+    bool stop_recorded;  // false if recording the stop event failed (a pooled event may hold an old time)
 };
 
 struct State {
@@ -40,12 +41,12 @@ LaunchTimer::LaunchTimer(const char* name, hipStream_t s) : slot_(-1), stream_(s
     hipEvent_t a = take_event(), b = take_event();
     if (a == nullptr || b == nullptr) return;
     if (hipEventRecord(a, s) != hipSuccess) return;
-    g_state.pending.push_back({name, a, b});
+    g_state.pending.push_back({name, a, b, false});
     slot_ = static_cast<int>(g_state.pending.size()) - 1;
 }
 
 LaunchTimer::~LaunchTimer() {
-    if (slot_ >= 0) hipEventRecord(g_state.pending[slot_].stop, stream_);
+    if (slot_ >= 0) g_state.pending[slot_].stop_recorded = hipEventRecord(g_state.pending[slot_].stop, stream_) == hipSuccess;
 }
 
 }  // namespace kda
@@ -63,7 +64,8 @@ int kda_profile_collect(kda_kernel_time_t* out, int max_entries) {
     int status = KDA_OK;
     for (const kda::Pending& p : g_state.pending) {
         float ms = 0.f;
-        if (hipEventSynchronize(p.stop) != hipSuccess || hipEventElapsedTime(&ms, p.start, p.stop) != hipSuccess)
+        if (!p.stop_recorded || hipEventSynchronize(p.stop) != hipSuccess ||
+            hipEventElapsedTime(&ms, p.start, p.stop) != hipSuccess)
             status = KDA_ERR_HIP;
         kda_kernel_time_t* hit = nullptr;
         for (auto& a : agg)

@@ -135,3 +135,24 @@ def kda_prefill_layer(q_in, k_in, v_in, w_q, w_k, w_v, g_alpha, b_beta, H, dk, d
                                   _ptr(initial_state), _ptr(final_state), _ptr(out),
                                   _ptr(workspace), workspace.numel(), _stream(dev)))
     return out, final_state
+
+
+def kda_decode_layer(q_in, k_in, v_in, w_q, w_k, w_v, g_alpha, b_beta, H, dk, dv, conv_state, state,
+                     out_gate=None, state_indices=None, out=None):
+    """One raw token per sequence through preprocess + decode step in one call.
+    Inputs [B, H*d] (or [B, H, d]) as for kda_preprocess; ``conv_state`` fp32
+    [S, 3, H*(2dk+dv)] and ``state`` fp32 [S, H, dk, dv] are pools updated in
+    place, sequence b using row ``state_indices[b]`` (int32 [B]; row b when
+    None, then S must be B; an index outside [0, S) marks a padding row whose
+    output is zero).  Returns out [B, H, dv]."""
+    B = q_in.shape[0]
+    slots = state.shape[0]
+    if state_indices is not None and state_indices.dtype != torch.int32:
+        raise TypeError("state_indices must be int32")
+    if out is None:
+        out = torch.empty((B, H, dv), dtype=q_in.dtype, device=q_in.device)
+    check(lib().kda_decode_layer(B, H, dk, dv, _dtype_code(q_in),
+                                 _ptr(q_in), _ptr(k_in), _ptr(v_in), _ptr(w_q), _ptr(w_k), _ptr(w_v),
+                                 _ptr(g_alpha), _ptr(b_beta), _ptr(conv_state), _ptr(out_gate),
+                                 _ptr(state), slots, _ptr(state_indices), _ptr(out), _stream(q_in.device)))
+    return out

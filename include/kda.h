@@ -196,6 +196,51 @@ int kda_decode_step(int32_t B, int32_t H, int32_t dk, int32_t dv,
                     void* stream);
 
 /*
+ * kda_decode_layer -- one token per sequence through the whole token mixer:
+ * kda_preprocess for that token (conv against the caller's conv history, L2
+ * norm, gates) fused with kda_decode_step, so a serving loop makes one call
+ * per layer and token.  The preprocessed q, k, v are rounded to x_dtype
+ * before the step (as kda_preprocess stores them); the gates stay fp32.
+ * The result equals kda_preprocess (T_tot = B, N = B, cu_seqlens = 0..B)
+ * followed by kda_decode_step with gate_dtype KDA_F32, up to rounding order.
+ * States live in a pool: sequence b uses row state_indices[b] of state and
+ * of conv_state (row b when state_indices is NULL, then state_slots must be
+ * B).  This is the decode-time form of the recurrence and the conv in the
+ * section "KDA: constant-size memory over a very long context" of the page
+ * "Ling-3.0-flash: a 124B open MoE ...".
+ * Arguments:
+ *   q_in, k_in [B, H, dk], v_in [B, H, dv], g_alpha [B, H, dk], b_beta [B, H]
+ *                 raw projections and gate logits of the new token (x_dtype);
+ *   w_q, w_k [H*dk, 4], w_v [H*dv, 4]   conv taps (x_dtype), as kda_preprocess;
+ *   conv_state    fp32 [state_slots, 3, H*(2*dk + dv)]: per slot the last
+ *                 three raw tokens (oldest first; q, then k, then v columns),
+ *                 the layout kda_preprocess reads and writes; rolled forward
+ *                 by one token in place;
+ *   out_gate      NULL or [B, H, dv] logits (x_dtype);
+ *   state         fp32 [state_slots, H, dk, dv], updated in place;
+ *   state_slots   rows in the two pools (>= 0);
+ *   state_indices NULL or device int32 [B].  An entry outside
+ *                 [0, state_slots) marks a padding row: its out row is set to
+ *                 zero and no state is read or written.  Valid entries must be
+ *                 distinct (two rows on one slot race); with the environment
+ *                 variable KDA_DEBUG_CHECK=1 the call copies the indices to the
+ *                 host, synchronising the stream, and rejects duplicates;
+ *   out           [B, H, dv] (x_dtype).
+ * Pool rows that no valid entry names are neither read nor written.
+ */
+int kda_decode_layer(int32_t B, int32_t H, int32_t dk, int32_t dv,
+                     int32_t x_dtype,
+                     const void* q_in, const void* k_in, const void* v_in,
+                     const void* w_q, const void* w_k, const void* w_v,
+                     const void* g_alpha, const void* b_beta,
+                     float* conv_state,
+                     const void* out_gate,
+                     float* state, int32_t state_slots,
+                     const int32_t* state_indices,
+                     void* out,
+                     void* stream);
+
+/*
  * Kernel timing for profiling tools (not needed for normal use).
  * kda_profile_enable(1) makes every later call on the calling host thread
  * bracket each kernel it launches with a pair of HIP events recorded on the

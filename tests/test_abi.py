@@ -36,7 +36,7 @@ def test_status_strings(lib):
     assert _lib.status_string(0) == "KDA_OK"
     assert _lib.status_string(3) == "KDA_ERR_WORKSPACE_TOO_SMALL"
     assert _lib.status_string(99) == "KDA_ERR_UNKNOWN"
-    assert lib.kda_abi_version() == 100
+    assert lib.kda_abi_version() == 101
 
 
 def test_workspace_bytes_bound(lib):
@@ -121,3 +121,30 @@ def test_preprocess_rejects_bad_arguments(lib):
     assert call(q_in=None) == _lib.KDA_ERR_INVALID_ARGUMENT
     assert call(q_out=FAKE + 64) == _lib.KDA_ERR_INVALID_ARGUMENT  # output overlaps q_in
     assert call(N=3) == _lib.KDA_ERR_INVALID_ARGUMENT
+
+
+def test_decode_layer_rejects_bad_arguments(lib):
+    def call(**kw):
+        a = dict(B=2, H=2, dk=16, dv=16, x=1, slots=2, idx=None, z=None)
+        names = ["q_in", "k_in", "v_in", "w_q", "w_k", "w_v", "g", "b", "cs", "state", "out"]
+        ptrs = {n: FAKE + i * 2**20 for i, n in enumerate(names)}
+        a.update(ptrs)
+        a.update(kw)
+        return lib.kda_decode_layer(a["B"], a["H"], a["dk"], a["dv"], a["x"],
+                                    *[P(a[n]) for n in names[:8]], P(a["cs"]), P(a["z"]), P(a["state"]),
+                                    a["slots"], P(a["idx"]), P(a["out"]), None)
+    assert call(dk=8) == _lib.KDA_ERR_UNSUPPORTED
+    assert call(x=3) == _lib.KDA_ERR_INVALID_ARGUMENT
+    assert call(slots=5) == _lib.KDA_ERR_INVALID_ARGUMENT  # no indices: one slot per row
+    assert "state_slots" in lib.kda_last_error_detail().decode()
+    assert call(slots=-1, idx=FAKE + 2**30) == _lib.KDA_ERR_INVALID_ARGUMENT
+    assert call(idx=FAKE + 2**30 + 2) == _lib.KDA_ERR_INVALID_ARGUMENT  # misaligned indices
+    assert call(cs=None) == _lib.KDA_ERR_INVALID_ARGUMENT  # the conv history is required
+    assert "conv_state is NULL" in lib.kda_last_error_detail().decode()
+    assert call(state=FAKE + 8 * 2**20 + 256) == _lib.KDA_ERR_INVALID_ARGUMENT  # overlaps conv_state
+    assert "overlaps" in lib.kda_last_error_detail().decode()
+    assert call(b=None) == _lib.KDA_ERR_INVALID_ARGUMENT
+    assert call(H=0) == _lib.KDA_ERR_INVALID_ARGUMENT
+    # an empty batch touches nothing: NULL pools and tokens are fine
+    assert call(B=0, slots=0, **{n: None for n in ["q_in", "k_in", "v_in", "w_q", "w_k", "w_v", "g", "b",
+                                                   "cs", "state", "out"]}) == _lib.KDA_OK
