@@ -12,7 +12,9 @@ The decode step (256 sequences x 32 heads x 128^2 fp32 state, in place) is
 timed in its own loop and reported under ``decode`` in GB/s of algorithmic
 traffic; the fused serving call (raw token in, preprocess and step in one
 kernel, conv history and state rolled in place) likewise under
-``decode_layer``.  ``roofline`` covers the kernel with the largest share of the step:
+``decode_layer``, and the speculative verify (one token plus three drafts per
+sequence, the previous call's four tokens committed first) under
+``spec_verify``.  ``roofline`` covers the kernel with the largest share of the step:
 algorithmic bytes per launch / average launch time from HIP events recorded
 around each kernel during a second pass of the same K steps.  ``cpu_baseline``
 times the fp64 CPU oracle on the same workload (rank 0, one GPU only).
@@ -117,6 +119,18 @@ def decode_layer_bytes(B, H, dk, dv, x, has_gate):
     gate); per call the conv taps once."""
     w = 2 * dk + dv
     per = 2 * dk * dv * 4 + x * (w + dk + 1) + 2 * 3 * w * 4 + x * dv * (2 if has_gate else 1)
+    return B * H * per + H * w * 4 * x
+
+
+def spec_bytes(B, H, dk, dv, T, na, x, has_gate):
+    """Algorithmic bytes of one speculative-verify call that commits na
+    tokens and verifies T: per (sequence, head) the state read and written
+    once, the conv history read and written, na raw tokens read back from the
+    draft buffer, T raw tokens read and written to it, T outputs (and gates);
+    per call the conv taps once."""
+    w = 2 * dk + dv
+    raw = x * (w + dk + 1)
+    per = 2 * dk * dv * 4 + 2 * 3 * w * 4 + (na + 2 * T) * raw + T * x * dv * (2 if has_gate else 1)
     return B * H * per + H * w * 4 * x
 
 
@@ -290,6 +304,50 @@ def bench_decode_layer(args):
             "roofline": roofline("decode_layer", b, per_ms)}
 
 
+def bench_spec(args):
+    """Speculative verify on the same 256 x 32 x 128^2 workload, one token plus
+    three drafts per call, every token of the previous call accepted (the
+    most work a call does: 4 tokens committed, 4 verified)."""
+    import torch
+    from gated_delta_rule_64_amd import _lib, kda, synth
+
+    T = 4
+    inp = synth.make("decode_b256", lengths=(T,) * 256)
+    H, dk, dv, B = inp["H"], inp["dk"], inp["dv"], inp["N"]
+    tok = [dev(inp[n]).view(B, T, -1) for n in ("q_in", "k_in", "v_in")]
+    w = [dev(inp[n]) for n in ("w_q", "w_k", "w_v")]
+    g, b, z = (dev(inp[n]).view(B, T, -1) for n in ("g", "b", "z"))
+    cs = dev(inp["conv_state"])
+    state = dev(inp["S0"])
+    drafts = torch.zeros(B * kda.kda_spec_draft_bytes(H, dk, dv, torch.bfloat16), dtype=torch.uint8, device="cuda")
+    acc = torch.full((B,), T, dtype=torch.int32, device="cuda")
+    out = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device="cuda")
+
+    def call(accepted):
+        kda.kda_spec_verify(*tok, *w, g, b, H, dk, dv, cs, state, drafts, accepted=accepted, out_gate=z, out=out)
+
+    call(None)  # fills the draft buffer
+    for _ in range(args.warmup):
+        call(acc)
+    torch.cuda.synchronize()
+    _lib.profile_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(args.decode_steps):
+        call(acc)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    _lib.profile_enable(False)
+    n, ms = _lib.profile_collect()["spec_verify"]
+    per_ms = ms / n
+    bts = spec_bytes(B, H, dk, dv, T, T, 2, True)
+    return {"metric": "speculative verify (1 + 3 drafts, 4 committed) achieved HBM GB/s",
+            "value": round(bts / (per_ms * 1e-3) / 1e9, 1), "unit": "GB/s", "workload": "decode_b256",
+            "B": B, "H": H, "dk": dk, "dv": dv, "tokens_verified": T, "tokens_committed": T,
+            "steps": args.decode_steps, "us_per_call_events": round(per_ms * 1e3, 2),
+            "us_per_call_wall": round(elapsed / args.decode_steps * 1e6, 2),
+            "roofline": roofline("spec_verify", bts, per_ms)}
+
+
 def cpu_baseline(res, min_seconds=10.0, max_passes=100):
     """The fp64 oracle (preprocess + token-by-token recurrence) on the bench's
     own inputs, repeated whole until at least ``min_seconds`` of CPU work."""
@@ -372,6 +430,7 @@ def main():
     }
     line["decode"] = bench_decode(args)
     line["decode_layer"] = bench_decode_layer(args)
+    line["spec_verify"] = bench_spec(args)
     if args.copy_calibration:
         line["copy_calibration"] = copy_calibration()
     if not args.no_cpu_baseline:

@@ -122,7 +122,7 @@ const char* kda_status_string(int status) {
 
 const char* kda_last_error_detail(void) { return g_detail; }
 
-int kda_abi_version(void) { return 101; }
+int kda_abi_version(void) { return 102; }
 
 int kda_preprocess(int64_t T_tot, int32_t H, int32_t dk, int32_t dv, const int32_t* cu_seqlens, int32_t N,
                    int32_t x_dtype, const void* q_in, const void* k_in, const void* v_in, const void* w_q,
@@ -372,6 +372,67 @@ int kda_decode_layer(int32_t B, int32_t H, int32_t dk, int32_t dv, int32_t x_dty
     a.conv_state = conv_state; a.state = state; a.slots = state_slots; a.state_indices = state_indices; a.out = out;
     hipError_t e = kda::launch_decode_layer(a, s);
     if (e != hipSuccess) return hip_fail(e, "decode layer launch");
+    return ok();
+}
+
+size_t kda_spec_draft_bytes(int32_t H, int32_t dk, int32_t dv, int32_t x_dtype) {
+    if (H < 1 || H > 65535 || !valid_head_dim(dk) || !valid_head_dim(dv) || !valid_dtype(x_dtype)) return 0;
+    return static_cast<size_t>(kda::kSpecMaxTokens) * H * kda::spec_draft_width(dk, dv) * dsize(x_dtype);
+}
+
+int kda_spec_verify(int32_t B, int32_t T, int32_t H, int32_t dk, int32_t dv, int32_t x_dtype, const void* q_in,
+                    const void* k_in, const void* v_in, const void* w_q, const void* w_k, const void* w_v,
+                    const void* g_alpha, const void* b_beta, float* conv_state, const void* out_gate,
+                    float* state, int32_t state_slots, const int32_t* state_indices, const int32_t* accepted,
+                    void* drafts, void* out, void* stream) {
+    if (B < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "B=%d must be >= 0", B);
+    if (T < 0 || T > kda::kSpecMaxTokens)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "T=%d out of range [0, %d]", T, kda::kSpecMaxTokens);
+    if (H < 1 || H > 65535) return fail(KDA_ERR_INVALID_ARGUMENT, "H=%d out of range [1, 65535]", H);
+    if (!valid_head_dim(dk) || !valid_head_dim(dv))
+        return fail(KDA_ERR_UNSUPPORTED, "dk=%d, dv=%d: supported head sizes are 16, 32, 64, 128", dk, dv);
+    if (!valid_dtype(x_dtype)) return fail(KDA_ERR_INVALID_ARGUMENT, "x_dtype=%d is not KDA_F32 or KDA_BF16", x_dtype);
+    if (static_cast<int64_t>(B) * H >= (int64_t(1) << 31)) return fail(KDA_ERR_INVALID_ARGUMENT, "B*H too large");
+    if (state_slots < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "state_slots=%d must be >= 0", state_slots);
+    if (state_indices == nullptr && state_slots != B)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "state_indices is NULL but state_slots=%d != B=%d", state_slots, B);
+    if (static_cast<int64_t>(state_slots) * H >= (int64_t(1) << 31))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "state_slots*H too large");
+    const size_t xs = dsize(x_dtype);
+    const size_t BTH = static_cast<size_t>(B) * T * H, SH = static_cast<size_t>(state_slots) * H;
+    const bool any = B > 0;
+    std::vector<Span> sp = {
+        {"q_in", q_in, BTH * dk * xs, false}, {"k_in", k_in, BTH * dk * xs, false},
+        {"v_in", v_in, BTH * dv * xs, false},
+        {"w_q", w_q, any ? static_cast<size_t>(H) * dk * 4 * xs : 0, false},
+        {"w_k", w_k, any ? static_cast<size_t>(H) * dk * 4 * xs : 0, false},
+        {"w_v", w_v, any ? static_cast<size_t>(H) * dv * 4 * xs : 0, false},
+        {"g_alpha", g_alpha, BTH * dk * xs, false},
+        {"out_gate", out_gate, out_gate ? BTH * dv * xs : 0, false},
+        {"conv_state", conv_state, any ? SH * 3 * (2 * dk + dv) * 4 : 0, true},
+        {"state", state, any ? SH * dk * dv * 4 : 0, true},
+        {"drafts", drafts, any ? static_cast<size_t>(state_slots) * kda_spec_draft_bytes(H, dk, dv, x_dtype) : 0, true},
+        {"out", out, BTH * dv * xs, true},
+    };
+    int st = check_spans(sp);
+    if (st != KDA_OK) return st;
+    if (BTH > 0 && (b_beta == nullptr || (reinterpret_cast<uintptr_t>(b_beta) % xs) != 0))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "b_beta is NULL or misaligned");
+    if (any && state_indices != nullptr && (reinterpret_cast<uintptr_t>(state_indices) & 3u) != 0)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "state_indices is not 4-byte aligned");
+    if (any && accepted != nullptr && (reinterpret_cast<uintptr_t>(accepted) & 3u) != 0)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "accepted is not 4-byte aligned");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    st = debug_check_indices(state_indices, B, state_slots, s);
+    if (st != KDA_OK) return st;
+    kda::SpecArgs a;
+    a.B = B; a.H = H; a.dk = dk; a.dv = dv; a.T = T; a.x = static_cast<kda::DT>(x_dtype);
+    a.q_in = q_in; a.k_in = k_in; a.v_in = v_in; a.w_q = w_q; a.w_k = w_k; a.w_v = w_v;
+    a.g = g_alpha; a.b = b_beta; a.z = out_gate;
+    a.conv_state = conv_state; a.state = state; a.slots = state_slots; a.state_indices = state_indices;
+    a.accepted = accepted; a.drafts = drafts; a.out = out;
+    hipError_t e = kda::launch_spec_verify(a, s);
+    if (e != hipSuccess) return hip_fail(e, "speculative verify launch");
     return ok();
 }
 

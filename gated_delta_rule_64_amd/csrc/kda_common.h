@@ -121,6 +121,40 @@ __device__ __forceinline__ int find_seq(const int32_t* cu, int N, int64_t t) {
     return lo;
 }
 
+// Cross-lane sums without the LDS path (a shuffle is an LDS round trip).
+// x + x rotated by N lanes within each row of 16 (DPP row_ror)
+template <int N>
+__device__ __forceinline__ float row_ror_add(float x) {
+    return x + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x120 + N, 0xF, 0xF, false));
+}
+// x + x of the lane 16 away (rows 0 and 1, rows 2 and 3 exchanged): one
+// v_permlane16_swap with both operands x returns the two rows of each pair
+__device__ __forceinline__ float xor16_add(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// x + x of the lane 32 away (the two halves exchanged)
+__device__ __forceinline__ float xor32_add(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// Sum over the lanes of the wave that agree in lane % S (S = 1, 2, 4, 8);
+// every lane gets the sum of its class (the order of the additions differs
+// between lanes, so lanes may differ in the last bit).
+template <int S>
+__device__ __forceinline__ float wave_sum_stride(float x) {
+    static_assert(S == 1 || S == 2 || S == 4 || S == 8, "stride within a row of 16");
+    if (S <= 1) x = row_ror_add<1>(x);
+    if (S <= 2) x = row_ror_add<2>(x);
+    if (S <= 4) x = row_ror_add<4>(x);
+    x = row_ror_add<8>(x);
+    return xor32_add(xor16_add(x));
+}
+// Sum over the whole wave, the same value in every lane (lane 0's)
+__device__ __forceinline__ float wave_sum(float x) {
+    return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(wave_sum_stride<1>(x))));
+}
+
 constexpr int kChunk = 64;  // tokens per chunk of the prefill
 
 // Workgroup barrier for LDS traffic only.  __syncthreads() fences all memory

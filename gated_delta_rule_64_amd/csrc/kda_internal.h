@@ -57,6 +57,27 @@ struct DecodeLayerArgs {
     void* out;
 };
 
+// Speculative verify with a deferred commit: `accepted[b]` (NULL: 0) tokens of
+// the previous call, kept raw in the draft buffer, are committed to the state
+// and conv history of slot state_indices[b]; then T new raw tokens are run
+// from that state (outputs only) and saved to the draft buffer.
+constexpr int kSpecMaxTokens = 8;
+// elements per (slot, token, head) in the draft buffer: raw q, k, v, decay
+// logits, then the write logit, padded to 16 bytes
+constexpr int spec_draft_width(int dk, int dv) { return 3 * dk + dv + 8; }
+struct SpecArgs {
+    int B, H, dk, dv, T;
+    DT x;
+    const void *q_in, *k_in, *v_in, *w_q, *w_k, *w_v, *g, *b, *z;
+    float* conv_state;
+    float* state;
+    int slots;
+    const int32_t* state_indices;
+    const int32_t* accepted;
+    void* drafts;
+    void* out;
+};
+
 // The whole layer (preprocess + chunked prefill) with the preprocess fused
 // into the chunk kernel; bf16 inputs, dk = dv = 128.
 struct LayerArgs {
@@ -79,6 +100,7 @@ bool layer_fused_supported(int dk, int dv, DT x);
 hipError_t launch_layer(const LayerArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_layer(const DecodeLayerArgs& a, hipStream_t s);
+hipError_t launch_spec_verify(const SpecArgs& a, hipStream_t s);
 
 // chunked prefill: workspace layout and the two implementations
 bool prefill_uses_mfma(int dk, int dv, DT x);

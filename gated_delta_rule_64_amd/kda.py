@@ -156,3 +156,30 @@ def kda_decode_layer(q_in, k_in, v_in, w_q, w_k, w_v, g_alpha, b_beta, H, dk, dv
                                  _ptr(g_alpha), _ptr(b_beta), _ptr(conv_state), _ptr(out_gate),
                                  _ptr(state), slots, _ptr(state_indices), _ptr(out), _stream(q_in.device)))
     return out
+
+
+def kda_spec_draft_bytes(H, dk, dv, x_dtype):
+    """Bytes of draft buffer per pool slot for kda_spec_verify."""
+    if isinstance(x_dtype, torch.dtype):
+        x_dtype = KDA_BF16 if x_dtype == torch.bfloat16 else KDA_F32
+    return int(lib().kda_spec_draft_bytes(H, dk, dv, x_dtype))
+
+
+def kda_spec_verify(q_in, k_in, v_in, w_q, w_k, w_v, g_alpha, b_beta, H, dk, dv, conv_state, state, drafts,
+                    accepted=None, out_gate=None, state_indices=None, out=None):
+    """Commit ``accepted[b]`` tokens of the previous call, then run the T new
+    raw tokens (inputs [B, T, H*d] or [B, T, H, d]) from that state without
+    advancing it.  ``drafts`` is a device buffer of S * kda_spec_draft_bytes
+    bytes (S = pool rows).  Returns out [B, T, H, dv]."""
+    B, T = q_in.shape[0], q_in.shape[1]
+    for t in (accepted, state_indices):
+        if t is not None and t.dtype != torch.int32:
+            raise TypeError("accepted and state_indices must be int32")
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=q_in.dtype, device=q_in.device)
+    check(lib().kda_spec_verify(B, T, H, dk, dv, _dtype_code(q_in),
+                                _ptr(q_in), _ptr(k_in), _ptr(v_in), _ptr(w_q), _ptr(w_k), _ptr(w_v),
+                                _ptr(g_alpha), _ptr(b_beta), _ptr(conv_state), _ptr(out_gate),
+                                _ptr(state), state.shape[0], _ptr(state_indices), _ptr(accepted),
+                                _ptr(drafts), _ptr(out), _stream(q_in.device)))
+    return out

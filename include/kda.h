@@ -241,6 +241,61 @@ int kda_decode_layer(int32_t B, int32_t H, int32_t dk, int32_t dv,
                      void* stream);
 
 /*
+ * Speculative decoding: verify 1 + n draft tokens per sequence, commit later.
+ *
+ * The decoding on the page "Ling-3.0-flash: a 124B open MoE ..." proposes
+ * three draft tokens per step (multi-token prediction) and verifies them in
+ * one pass; how many are accepted is known only after that pass.  Each call
+ * of kda_spec_verify, per sequence b and its pool row s = state_indices[b]:
+ *   1. commits: the first accepted[b] tokens of the previous call on slot s
+ *      (kept raw in the draft buffer) go through the conv (against the
+ *      slot's conv history), the L2 norm, the gates and the recurrence, as
+ *      kda_decode_layer would run them one by one; the slot's state and conv
+ *      history are written back, holding those tokens;
+ *   2. verifies: the T new raw tokens run from that state in order (token t's
+ *      output reads the state after tokens 0..t), and their outputs are
+ *      written; the state and conv history are NOT advanced by them.  Their
+ *      raw values replace the slot's draft buffer, for the next call to commit.
+ * So each call reads and writes the state once.  A call with T = 0 only
+ * commits (use it to bring a slot up to date, e.g. when a sequence leaves
+ * speculative mode).  The recurrence is that of kda_decode_step (section
+ * "KDA: constant-size memory over a very long context" of the same page).
+ * Arguments:
+ *   B, T          sequences and new tokens per sequence (0 <= T <= 8);
+ *   q_in, k_in [B, T, H, dk], v_in [B, T, H, dv], g_alpha [B, T, H, dk],
+ *   b_beta [B, T, H]   raw projections and gate logits (x_dtype);
+ *   w_q, w_k, w_v, conv_state, state, state_slots, state_indices
+ *                 as for kda_decode_layer (pools of state_slots rows);
+ *   out_gate      NULL or [B, T, H, dv] (x_dtype);
+ *   accepted      NULL (commit nothing) or device int32 [B]: how many of the
+ *                 previous call's tokens on that slot to commit, in
+ *                 [0, that call's T]; values are clamped to [0, 8], and a
+ *                 count above the previous T commits stale buffer contents;
+ *   drafts        per slot kda_spec_draft_bytes(H, dk, dv, x_dtype) bytes
+ *                 of device memory, owned by the caller, opaque (raw tokens
+ *                 of the last call, in x_dtype: every call on one buffer
+ *                 must use the same x_dtype, a commit-only call included);
+ *                 contents matter only where accepted > 0;
+ *   out           [B, T, H, dv] (x_dtype).
+ * Padding rows (index outside the pool) get zero outputs and touch nothing.
+ * A row with accepted = 0 and T = 0 is a no-op.
+ */
+size_t kda_spec_draft_bytes(int32_t H, int32_t dk, int32_t dv, int32_t x_dtype);
+int kda_spec_verify(int32_t B, int32_t T, int32_t H, int32_t dk, int32_t dv,
+                    int32_t x_dtype,
+                    const void* q_in, const void* k_in, const void* v_in,
+                    const void* w_q, const void* w_k, const void* w_v,
+                    const void* g_alpha, const void* b_beta,
+                    float* conv_state,
+                    const void* out_gate,
+                    float* state, int32_t state_slots,
+                    const int32_t* state_indices,
+                    const int32_t* accepted,
+                    void* drafts,
+                    void* out,
+                    void* stream);
+
+/*
  * Kernel timing for profiling tools (not needed for normal use).
  * kda_profile_enable(1) makes every later call on the calling host thread
  * bracket each kernel it launches with a pair of HIP events recorded on the

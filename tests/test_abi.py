@@ -36,7 +36,7 @@ def test_status_strings(lib):
     assert _lib.status_string(0) == "KDA_OK"
     assert _lib.status_string(3) == "KDA_ERR_WORKSPACE_TOO_SMALL"
     assert _lib.status_string(99) == "KDA_ERR_UNKNOWN"
-    assert lib.kda_abi_version() == 101
+    assert lib.kda_abi_version() == 102
 
 
 def test_workspace_bytes_bound(lib):
@@ -148,3 +148,29 @@ def test_decode_layer_rejects_bad_arguments(lib):
     # an empty batch touches nothing: NULL pools and tokens are fine
     assert call(B=0, slots=0, **{n: None for n in ["q_in", "k_in", "v_in", "w_q", "w_k", "w_v", "g", "b",
                                                    "cs", "state", "out"]}) == _lib.KDA_OK
+
+
+def test_spec_verify_rejects_bad_arguments(lib):
+    names = ["q_in", "k_in", "v_in", "w_q", "w_k", "w_v", "g", "b", "cs", "state", "acc", "drafts", "out"]
+
+    def call(**kw):
+        a = dict(B=2, T=4, H=2, dk=16, dv=16, x=1, slots=2, idx=None, z=None)
+        a.update({n: FAKE + i * 2**20 for i, n in enumerate(names)})
+        a.update(kw)
+        return lib.kda_spec_verify(a["B"], a["T"], a["H"], a["dk"], a["dv"], a["x"],
+                                   *[P(a[n]) for n in names[:8]], P(a["cs"]), P(a["z"]), P(a["state"]),
+                                   a["slots"], P(a["idx"]), P(a["acc"]), P(a["drafts"]), P(a["out"]), None)
+    per_slot = lib.kda_spec_draft_bytes(2, 16, 16, 1)
+    assert per_slot == 8 * 2 * (3 * 16 + 16 + 8) * 2
+    assert lib.kda_spec_draft_bytes(2, 16, 48, 1) == 0
+    assert call(T=9) == _lib.KDA_ERR_INVALID_ARGUMENT
+    assert "T=9" in lib.kda_last_error_detail().decode()
+    assert call(T=-1) == _lib.KDA_ERR_INVALID_ARGUMENT
+    assert call(dv=8) == _lib.KDA_ERR_UNSUPPORTED
+    assert call(drafts=None) == _lib.KDA_ERR_INVALID_ARGUMENT
+    assert call(drafts=FAKE + 9 * 2**20 + 2048) == _lib.KDA_ERR_INVALID_ARGUMENT  # overlaps state
+    assert "overlaps" in lib.kda_last_error_detail().decode()
+    assert call(acc=FAKE + 10 * 2**20 + 2) == _lib.KDA_ERR_INVALID_ARGUMENT  # misaligned
+    assert call(slots=3) == _lib.KDA_ERR_INVALID_ARGUMENT  # NULL indices need one slot per row
+    # a commit-only call (T = 0) needs no token inputs and no output
+    assert call(B=0, T=0, slots=0, **{n: None for n in names}) == _lib.KDA_OK
