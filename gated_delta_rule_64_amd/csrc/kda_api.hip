@@ -122,7 +122,7 @@ const char* kda_status_string(int status) {
 
 const char* kda_last_error_detail(void) { return g_detail; }
 
-int kda_abi_version(void) { return 102; }
+int kda_abi_version(void) { return 103; }
 
 int kda_preprocess(int64_t T_tot, int32_t H, int32_t dk, int32_t dv, const int32_t* cu_seqlens, int32_t N,
                    int32_t x_dtype, const void* q_in, const void* k_in, const void* v_in, const void* w_q,
@@ -177,11 +177,42 @@ size_t kda_prefill_workspace_bytes(int64_t T_tot, int32_t N, int32_t H, int32_t 
     return kda::prefill_workspace_bytes(T_tot, N, H, dk, dv, static_cast<kda::DT>(x_dtype));
 }
 
-int kda_prefill_chunked(int64_t T_tot, int32_t H, int32_t dk, int32_t dv, const int32_t* cu_seqlens, int32_t N,
-                        int32_t x_dtype, int32_t gate_dtype, const void* q, const void* k, const void* v,
-                        const void* log_alpha, const void* beta, const void* out_gate,
-                        const float* initial_state, float* final_state, void* out, void* workspace,
-                        size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// A request for state snapshots from the prefill (the *_snap entry points).
+struct SnapReq {
+    int32_t interval;
+    float* out;
+    int64_t capacity;
+    int32_t* offsets;
+};
+
+// Validates a snapshot request and adds its outputs to the overlap check.
+int check_snap(const SnapReq* r, int64_t T, int32_t N, int32_t H, int32_t dk, int32_t dv, std::vector<Span>& sp,
+               kda::Snapshots& out) {
+    out = kda::Snapshots{};
+    if (r == nullptr) return KDA_OK;
+    if (r->interval < 64 || r->interval % 64 != 0)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "snap_interval=%d is not a positive multiple of 64", r->interval);
+    const int64_t most = T / r->interval;  // sum over sequences of floor(len / interval) is at most this
+    if (r->capacity < most)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "snap_capacity=%lld < T_tot / snap_interval = %lld",
+                    static_cast<long long>(r->capacity), static_cast<long long>(most));
+    sp.push_back({"snapshots", r->out, static_cast<size_t>(most) * H * dk * dv * 4, true});
+    sp.push_back({"snap_offsets", r->offsets, static_cast<size_t>(N + 1) * 4, true});
+    out.chunks = r->interval / 64;
+    out.out = r->out;
+    out.off = r->offsets;
+    return KDA_OK;
+}
+
+int prefill_chunked_impl(int64_t T_tot, int32_t H, int32_t dk, int32_t dv, const int32_t* cu_seqlens, int32_t N,
+                         int32_t x_dtype, int32_t gate_dtype, const void* q, const void* k, const void* v,
+                         const void* log_alpha, const void* beta, const void* out_gate,
+                         const float* initial_state, float* final_state, void* out, void* workspace,
+                         size_t workspace_bytes, void* stream, const SnapReq* snap) {
     int st = check_sizes(T_tot, H, dk, dv, N);
     if (st != KDA_OK) return st;
     if ((T_tot / 64 + 1 + N) * static_cast<int64_t>(H) > 0xffffffffll)
@@ -215,6 +246,9 @@ int kda_prefill_chunked(int64_t T_tot, int32_t H, int32_t dk, int32_t dv, const 
         {"out", out, vv * xs, true},
         {"workspace", workspace, need, true},
     };
+    kda::Snapshots snaps;
+    st = check_snap(snap, T_tot, N, H, dk, dv, sp, snaps);
+    if (st != KDA_OK) return st;
     st = check_spans(sp);
     if (st != KDA_OK) return st;
     if (T * H > 0 && (beta == nullptr || (reinterpret_cast<uintptr_t>(beta) % gs) != 0))
@@ -227,16 +261,17 @@ int kda_prefill_chunked(int64_t T_tot, int32_t H, int32_t dk, int32_t dv, const 
     a.x = static_cast<kda::DT>(x_dtype); a.gate = static_cast<kda::DT>(gate_dtype);
     a.q = q; a.k = k; a.v = v; a.la = log_alpha; a.beta = beta; a.z = out_gate;
     a.S0 = initial_state; a.S_out = final_state; a.out = out; a.ws = workspace; a.ws_bytes = workspace_bytes;
+    a.snap = snaps;
     hipError_t e = kda::launch_prefill(a, s);
     if (e != hipSuccess) return hip_fail(e, "prefill launch");
     return ok();
 }
 
-int kda_prefill_layer(int64_t T_tot, int32_t H, int32_t dk, int32_t dv, const int32_t* cu_seqlens, int32_t N,
-                      int32_t x_dtype, const void* q_in, const void* k_in, const void* v_in, const void* w_q,
-                      const void* w_k, const void* w_v, const void* g_alpha, const void* b_beta,
-                      float* conv_state, const void* out_gate, const float* initial_state, float* final_state,
-                      void* out, void* workspace, size_t workspace_bytes, void* stream) {
+int prefill_layer_impl(int64_t T_tot, int32_t H, int32_t dk, int32_t dv, const int32_t* cu_seqlens, int32_t N,
+                       int32_t x_dtype, const void* q_in, const void* k_in, const void* v_in, const void* w_q,
+                       const void* w_k, const void* w_v, const void* g_alpha, const void* b_beta,
+                       float* conv_state, const void* out_gate, const float* initial_state, float* final_state,
+                       void* out, void* workspace, size_t workspace_bytes, void* stream, const SnapReq* snap) {
     int st = check_sizes(T_tot, H, dk, dv, N);
     if (st != KDA_OK) return st;
     if (!valid_dtype(x_dtype)) return fail(KDA_ERR_INVALID_ARGUMENT, "x_dtype=%d is not KDA_F32 or KDA_BF16", x_dtype);
@@ -277,6 +312,9 @@ int kda_prefill_layer(int64_t T_tot, int32_t H, int32_t dk, int32_t dv, const in
         {"out", out, vv * xs, true},
         {"workspace", workspace, need, true},
     };
+    kda::Snapshots snaps;
+    st = check_snap(snap, T_tot, N, H, dk, dv, sp, snaps);
+    if (st != KDA_OK) return st;
     st = check_spans(sp);
     if (st != KDA_OK) return st;
     // b_beta rows are H elements, read one at a time: element alignment suffices
@@ -290,9 +328,58 @@ int kda_prefill_layer(int64_t T_tot, int32_t H, int32_t dk, int32_t dv, const in
     a.q_in = q_in; a.k_in = k_in; a.v_in = v_in; a.w_q = w_q; a.w_k = w_k; a.w_v = w_v;
     a.g = g_alpha; a.b = b_beta; a.z = out_gate; a.conv_state = conv_state;
     a.S0 = initial_state; a.S_out = final_state; a.out = out; a.ws = workspace; a.ws_bytes = workspace_bytes;
+    a.snap = snaps;
     hipError_t e = kda::launch_layer(a, s);
     if (e != hipSuccess) return hip_fail(e, "layer launch");
     return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_prefill_chunked(int64_t T_tot, int32_t H, int32_t dk, int32_t dv, const int32_t* cu_seqlens, int32_t N,
+                        int32_t x_dtype, int32_t gate_dtype, const void* q, const void* k, const void* v,
+                        const void* log_alpha, const void* beta, const void* out_gate,
+                        const float* initial_state, float* final_state, void* out, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+    return prefill_chunked_impl(T_tot, H, dk, dv, cu_seqlens, N, x_dtype, gate_dtype, q, k, v, log_alpha, beta,
+                                out_gate, initial_state, final_state, out, workspace, workspace_bytes, stream,
+                                nullptr);
+}
+
+int kda_prefill_chunked_snap(int64_t T_tot, int32_t H, int32_t dk, int32_t dv, const int32_t* cu_seqlens,
+                             int32_t N, int32_t x_dtype, int32_t gate_dtype, const void* q, const void* k,
+                             const void* v, const void* log_alpha, const void* beta, const void* out_gate,
+                             const float* initial_state, float* final_state, void* out, void* workspace,
+                             size_t workspace_bytes, int32_t snap_interval, float* snapshots,
+                             int64_t snap_capacity, int32_t* snap_offsets, void* stream) {
+    const SnapReq r{snap_interval, snapshots, snap_capacity, snap_offsets};
+    return prefill_chunked_impl(T_tot, H, dk, dv, cu_seqlens, N, x_dtype, gate_dtype, q, k, v, log_alpha, beta,
+                                out_gate, initial_state, final_state, out, workspace, workspace_bytes, stream, &r);
+}
+
+int kda_prefill_layer(int64_t T_tot, int32_t H, int32_t dk, int32_t dv, const int32_t* cu_seqlens, int32_t N,
+                      int32_t x_dtype, const void* q_in, const void* k_in, const void* v_in, const void* w_q,
+                      const void* w_k, const void* w_v, const void* g_alpha, const void* b_beta,
+                      float* conv_state, const void* out_gate, const float* initial_state, float* final_state,
+                      void* out, void* workspace, size_t workspace_bytes, void* stream) {
+    return prefill_layer_impl(T_tot, H, dk, dv, cu_seqlens, N, x_dtype, q_in, k_in, v_in, w_q, w_k, w_v, g_alpha,
+                              b_beta, conv_state, out_gate, initial_state, final_state, out, workspace,
+                              workspace_bytes, stream, nullptr);
+}
+
+int kda_prefill_layer_snap(int64_t T_tot, int32_t H, int32_t dk, int32_t dv, const int32_t* cu_seqlens, int32_t N,
+                           int32_t x_dtype, const void* q_in, const void* k_in, const void* v_in, const void* w_q,
+                           const void* w_k, const void* w_v, const void* g_alpha, const void* b_beta,
+                           float* conv_state, const void* out_gate, const float* initial_state,
+                           float* final_state, void* out, void* workspace, size_t workspace_bytes,
+                           int32_t snap_interval, float* snapshots, int64_t snap_capacity,
+                           int32_t* snap_offsets, void* stream) {
+    const SnapReq r{snap_interval, snapshots, snap_capacity, snap_offsets};
+    return prefill_layer_impl(T_tot, H, dk, dv, cu_seqlens, N, x_dtype, q_in, k_in, v_in, w_q, w_k, w_v, g_alpha,
+                              b_beta, conv_state, out_gate, initial_state, final_state, out, workspace,
+                              workspace_bytes, stream, &r);
 }
 
 int kda_decode_step(int32_t B, int32_t H, int32_t dk, int32_t dv, int32_t x_dtype, int32_t gate_dtype,

@@ -10,6 +10,17 @@ namespace kda {
 
 enum class DT : int { F32 = 0, BF16 = 1 };
 
+// Optional state snapshots from the prefill: the state after every
+// `chunks` * 64 tokens of each sequence (counted from its start), written to
+// out[(off[n] + m - 1), h] for the m-th snapshot of sequence n.  off[n] is
+// filled by the chunk map (an exclusive scan of floor(len_n / (64 chunks))),
+// off[N] = the total.
+struct Snapshots {
+    int chunks = 0;  // 0: none
+    float* out = nullptr;
+    int32_t* off = nullptr;
+};
+
 struct PreprocessArgs {
     int64_t T;
     int H, dk, dv, N;
@@ -32,6 +43,7 @@ struct PrefillArgs {
     void* out;
     void* ws;
     size_t ws_bytes;
+    Snapshots snap;
 };
 
 struct DecodeArgs {
@@ -91,6 +103,7 @@ struct LayerArgs {
     void* out;
     void* ws;
     size_t ws_bytes;
+    Snapshots snap;
 };
 
 hipError_t launch_preprocess(const PreprocessArgs& a, hipStream_t s);

@@ -36,7 +36,9 @@ __device__ __forceinline__ int64_t seq_finish(const int32_t* cu, int n, int64_t 
 // The chunk map, built on the device by one workgroup of 1024 threads:
 //   base[0..N]       prefix sums of chunks per sequence;
 //   slot_info[slot]  for each used chunk slot, its first token, length and
-//                    sequence (slots past base[N] are left unwritten).
+//                    sequence (slots past base[N] are left unwritten);
+//   snap_off[0..N]   (snap_chunks > 0) prefix sums of floor(len / (64
+//                    snap_chunks)): where each sequence's state snapshots go.
 struct SlotInfo {
     int64_t t0;
     int32_t len;  // tokens in the chunk (bits 0..15); bit 16: the sequence's first chunk
@@ -46,7 +48,8 @@ static_assert(sizeof(SlotInfo) == 16, "one 16-byte record per slot");
 
 __global__ __launch_bounds__(1024) void chunk_map_kernel(const int32_t* __restrict__ cu, int N,
                                                          int64_t T, int32_t* __restrict__ base,
-                                                         SlotInfo* __restrict__ slot_info);
+                                                         SlotInfo* __restrict__ slot_info, int snap_chunks,
+                                                         int32_t* __restrict__ snap_off);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 

@@ -15,36 +15,41 @@ namespace kda {
 
 __global__ __launch_bounds__(1024) void chunk_map_kernel(const int32_t* __restrict__ cu, int N,
                                                          int64_t T, int32_t* __restrict__ base,
-                                                         SlotInfo* __restrict__ slot_info) {
-    __shared__ int32_t buf[1024];
-    __shared__ int32_t wsum[16];
-    __shared__ int32_t carry_s;
+                                                         SlotInfo* __restrict__ slot_info, int snap_chunks,
+                                                         int32_t* __restrict__ snap_off) {
+    // Both counts of a sequence (chunks in the low word, snapshots in the
+    // high word) go through one 64-bit scan: the chunk total stays below
+    // 2^26, so no carry crosses into the high word.
+    __shared__ int64_t buf[1024];
+    __shared__ int64_t wsum[16];
+    __shared__ int64_t carry_s;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     if (tid == 0) carry_s = 0;
     __syncthreads();
     // sequences in blocks of 1024, one per thread
     for (int start = 0; start < N; start += 1024) {
         const int i = start + tid;
-        int32_t c = 0;
+        int64_t c = 0;
         if (i < N) {
             const int64_t L = seq_finish(cu, i, T) - seq_begin(cu, i);
-            c = static_cast<int32_t>((L + kChunk - 1) / kChunk);
+            c = (L + kChunk - 1) / kChunk;
+            if (snap_chunks > 0) c |= (L / (static_cast<int64_t>(kChunk) * snap_chunks)) << 32;
         }
         // inclusive scan: within each wave by lane shuffles, then over the
         // 16 wave totals in wave 0
-        int32_t x = c;
+        int64_t x = c;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
-            const int32_t y = __shfl_up(x, off);
+            const int64_t y = __shfl_up(x, off);
             if (lane >= off) x += y;
         }
         if (lane == 63) wsum[wave] = x;
         __syncthreads();
         if (wave == 0) {
-            int32_t w = lane < 16 ? wsum[lane] : 0;
+            int64_t w = lane < 16 ? wsum[lane] : 0;
 #pragma unroll
             for (int off = 1; off < 16; off <<= 1) {
-                const int32_t y = __shfl_up(w, off);
+                const int64_t y = __shfl_up(w, off);
                 if (lane >= off) w += y;
             }
             if (lane < 16) wsum[lane] = w;
@@ -52,31 +57,40 @@ __global__ __launch_bounds__(1024) void chunk_map_kernel(const int32_t* __restri
         __syncthreads();
         buf[tid] = x + (wave > 0 ? wsum[wave - 1] : 0);
         __syncthreads();
-        const int32_t carry = carry_s;
-        if (i < N) base[i] = carry + buf[tid] - c;
+        const int64_t carry = carry_s;
+        const int32_t carry_c = static_cast<int32_t>(carry & 0xffffffff);
+        if (i < N) {
+            const int64_t excl = carry + buf[tid] - c;
+            base[i] = static_cast<int32_t>(excl & 0xffffffff);
+            if (snap_chunks > 0) snap_off[i] = static_cast<int32_t>(excl >> 32);
+        }
         // the block's slots, spread over all threads: slot carry + s belongs
         // to the first sequence j of the block whose inclusive count exceeds s
-        const int32_t total = buf[1023];
+        auto chunks_to = [&](int k) { return static_cast<int32_t>(buf[k] & 0xffffffff); };
+        const int32_t total = chunks_to(1023);
         for (int32_t s = tid; s < total; s += 1024) {
             int lo = 0, hi = 1023;
             while (lo < hi) {
                 const int mid = (lo + hi) >> 1;
-                if (buf[mid] > s) hi = mid; else lo = mid + 1;
+                if (chunks_to(mid) > s) hi = mid; else lo = mid + 1;
             }
             const int n = start + lo;
-            const int32_t j = s - (lo > 0 ? buf[lo - 1] : 0);  // chunk index inside the sequence
+            const int32_t j = s - (lo > 0 ? chunks_to(lo - 1) : 0);  // chunk index inside the sequence
             SlotInfo si;
             si.t0 = seq_begin(cu, n) + static_cast<int64_t>(j) * kChunk;
             si.len = static_cast<int32_t>(min(static_cast<int64_t>(kChunk), seq_finish(cu, n, T) - si.t0)) |
                      (j == 0 ? (1 << 16) : 0);
             si.seq = n;
-            slot_info[carry + s] = si;
+            slot_info[carry_c + s] = si;
         }
         __syncthreads();
         if (tid == 1023) carry_s = carry + buf[1023];
         __syncthreads();
     }
-    if (tid == 0) base[N] = carry_s;
+    if (tid == 0) {
+        base[N] = static_cast<int32_t>(carry_s & 0xffffffff);
+        if (snap_chunks > 0) snap_off[N] = static_cast<int32_t>(carry_s >> 32);
+    }
 }
 
 namespace {
@@ -109,6 +123,7 @@ struct GenK {
     float* S_out;
     XT* out;
     float* rec;
+    Snapshots snap;
 };
 
 // ---- phase 1: per (chunk slot, head), the state-independent factors ----
@@ -277,11 +292,18 @@ __global__ __launch_bounds__(256) void gen_state_kernel(GenK<XT, GT> a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) sU[r * 16 + c4 + i] = u[i];
         __syncthreads();
+        // a full chunk that ends a snapshot interval: the state after it is the m-th snapshot
+        const int sc = a.snap.chunks;
+        const bool snap = sc > 0 && (j + 1) % sc == 0 && L == kChunk;
+        float* snap_out = snap ? a.snap.out + ((static_cast<int64_t>(a.snap.off[n]) + (j + 1) / sc - 1) * a.H + h) *
+                                                  dk * dv
+                               : nullptr;
         for (int e = tid; e < dk * 16; e += 256) {
             const int c = e >> 4, jj = e & 15;
             float acc = rec[R.gam + c] * sS[e];
             for (int rr = 0; rr < 64; ++rr) acc += rec[R.Kh + rr * dk + c] * sU[rr * 16 + jj];
             sS[e] = acc;
+            if (snap) snap_out[c * dv + 16 * sl + jj] = acc;
         }
         __syncthreads();
     }
@@ -302,7 +324,7 @@ hipError_t launch_gen_typed(const PrefillArgs& a, hipStream_t s, int32_t* base, 
     k.q = static_cast<const XT*>(a.q); k.k = static_cast<const XT*>(a.k);
     k.v = static_cast<const XT*>(a.v); k.z = static_cast<const XT*>(a.z);
     k.la = static_cast<const GT*>(a.la); k.beta = static_cast<const GT*>(a.beta);
-    k.S0 = a.S0; k.S_out = a.S_out; k.out = static_cast<XT*>(a.out); k.rec = rec;
+    k.S0 = a.S0; k.S_out = a.S_out; k.out = static_cast<XT*>(a.out); k.rec = rec; k.snap = a.snap;
     const int64_t slots = chunk_slots_bound(a.T, a.N);
     const size_t lds = gen_lds_bytes(a.dk);
     if (slots > 0 && a.T > 0) {
@@ -340,7 +362,8 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
     hipError_t e;
     {
         LaunchTimer timer("chunk_map", s);
-        hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(1024), 0, s, a.cu, a.N, a.T, base, slot_info);
+        hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(1024), 0, s, a.cu, a.N, a.T, base, slot_info,
+                           a.snap.chunks, a.snap.off);
         e = hipGetLastError();
     }
     if (e != hipSuccess) return e;
@@ -363,7 +386,8 @@ hipError_t launch_layer(const LayerArgs& a, hipStream_t s) {
     hipError_t e;
     {
         LaunchTimer timer("chunk_map", s);
-        hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(1024), 0, s, a.cu, a.N, a.T, base, slot_info);
+        hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(1024), 0, s, a.cu, a.N, a.T, base, slot_info,
+                           a.snap.chunks, a.snap.off);
         e = hipGetLastError();
     }
     if (e != hipSuccess) return e;

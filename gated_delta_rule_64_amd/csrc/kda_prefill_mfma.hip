@@ -113,6 +113,7 @@ struct MfmaK {
     const float* cs;
     int64_t slots;   // chunk slots per head in the record array
     int64_t groups;  // N * H
+    Snapshots snap;  // optional states after every snap.chunks full chunks
 };
 
 // ---------------------------------------------------------------------------
@@ -1180,6 +1181,16 @@ __global__ __launch_bounds__(64 * (2 * NS + StateCfg<NS>::kMemWaves)) void mfma_
                 Sb[ks] = to_bf16x8(S[2 * ks], S[2 * ks + 1]);
                 *reinterpret_cast<bf16x8*>(sbx + (ks * 64 + lane) * 16) = Sb[ks];
             }
+            // a full chunk that ends a snapshot interval: the state after it
+            // is the sequence's m-th snapshot (this slice's columns)
+            const int sc = a.snap.chunks;
+            if (sc > 0 && (j + 1) % sc == 0 && chunk_len(j) == kChunk) {
+                float* so = a.snap.out + ((static_cast<int64_t>(a.snap.off[n]) + (j + 1) / sc - 1) * H + h) * (128 * 128);
+#pragma unroll
+                for (int t = 0; t < 8; ++t)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) so[(16 * t + 4 * g + i) * 128 + col0] = S[t][i];
+            }
         }
         if (a.S_out) {
 #pragma unroll
@@ -1270,7 +1281,7 @@ hipError_t launch_typed(const PrefillArgs& a, hipStream_t s, int32_t* base, cons
     k.q = static_cast<const bf16*>(a.q); k.k = static_cast<const bf16*>(a.k);
     k.v = static_cast<const bf16*>(a.v); k.z = static_cast<const bf16*>(a.z);
     k.la = static_cast<const GT*>(a.la); k.beta = static_cast<const GT*>(a.beta);
-    k.S0 = a.S0; k.S_out = a.S_out; k.out = static_cast<bf16*>(a.out); k.rec = recs;
+    k.S0 = a.S0; k.S_out = a.S_out; k.out = static_cast<bf16*>(a.out); k.rec = recs; k.snap = a.snap;
     return launch_kernels<GT, false>(k, s);
 }
 
@@ -1289,7 +1300,7 @@ hipError_t launch_layer_mfma(const LayerArgs& a, hipStream_t s, int32_t* base, c
     k.la = static_cast<const bf16*>(a.g); k.beta = static_cast<const bf16*>(a.b);
     k.w_q = static_cast<const bf16*>(a.w_q); k.w_k = static_cast<const bf16*>(a.w_k);
     k.w_v = static_cast<const bf16*>(a.w_v); k.cs = a.conv_state;
-    k.S0 = a.S0; k.S_out = a.S_out; k.out = static_cast<bf16*>(a.out); k.rec = recs;
+    k.S0 = a.S0; k.S_out = a.S_out; k.out = static_cast<bf16*>(a.out); k.rec = recs; k.snap = a.snap;
     return launch_kernels<bf16, true>(k, s);
 }
 

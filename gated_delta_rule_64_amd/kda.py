@@ -73,11 +73,23 @@ def kda_prefill_workspace_bytes(T_tot, N, H, dk, dv, x_dtype):
     return int(lib().kda_prefill_workspace_bytes(T_tot, N, H, dk, dv, x_dtype))
 
 
+def _snap_buffers(snap_interval, T, N, H, dk, dv, dev, snapshots, snap_offsets):
+    cap = T // snap_interval
+    if snapshots is None:
+        snapshots = torch.empty((max(cap, 1), H, dk, dv), dtype=torch.float32, device=dev)
+    if snap_offsets is None:
+        snap_offsets = torch.empty(N + 1, dtype=torch.int32, device=dev)
+    return snapshots, snap_offsets
+
+
 def kda_prefill_chunked(q, k, v, log_alpha, beta, out_gate=None, initial_state=None,
                         final_state=None, cu_seqlens=None, workspace=None, out=None,
-                        want_final_state=True):
+                        want_final_state=True, snap_interval=None, snapshots=None, snap_offsets=None):
     """Chunked recurrence over preprocessed tokens q,k [T,H,dk], v [T,H,dv].
-    Returns (out [T,H,dv], final_state fp32 [N,H,dk,dv] or None)."""
+    Returns (out [T,H,dv], final_state fp32 [N,H,dk,dv] or None); with
+    ``snap_interval`` (a multiple of 64) also (snapshots [C,H,dk,dv],
+    snap_offsets int32 [N+1]): the state after every ``snap_interval`` tokens
+    of each sequence, sequence n's m-th at row snap_offsets[n] + m - 1."""
     T, H, dk = q.shape
     dv = v.shape[2]
     N = _n_seqs(cu_seqlens)
@@ -91,11 +103,19 @@ def kda_prefill_chunked(q, k, v, log_alpha, beta, out_gate=None, initial_state=N
     need = kda_prefill_workspace_bytes(T, N, H, dk, dv, x)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
-    check(lib().kda_prefill_chunked(T, H, dk, dv, _ptr(cu_seqlens), N, x, g,
-                                    _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
-                                    _ptr(out_gate), _ptr(initial_state), _ptr(final_state), _ptr(out),
-                                    _ptr(workspace), workspace.numel(), _stream(dev)))
-    return out, final_state
+    if snap_interval is None:
+        check(lib().kda_prefill_chunked(T, H, dk, dv, _ptr(cu_seqlens), N, x, g,
+                                        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                                        _ptr(out_gate), _ptr(initial_state), _ptr(final_state), _ptr(out),
+                                        _ptr(workspace), workspace.numel(), _stream(dev)))
+        return out, final_state
+    snapshots, snap_offsets = _snap_buffers(snap_interval, T, N, H, dk, dv, dev, snapshots, snap_offsets)
+    check(lib().kda_prefill_chunked_snap(T, H, dk, dv, _ptr(cu_seqlens), N, x, g,
+                                         _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                                         _ptr(out_gate), _ptr(initial_state), _ptr(final_state), _ptr(out),
+                                         _ptr(workspace), workspace.numel(), snap_interval, _ptr(snapshots),
+                                         snapshots.shape[0], _ptr(snap_offsets), _stream(dev)))
+    return out, final_state, snapshots, snap_offsets
 
 
 def kda_decode_step(q, k, v, log_alpha, beta, state, out_gate=None, out=None):
@@ -113,7 +133,7 @@ def kda_decode_step(q, k, v, log_alpha, beta, state, out_gate=None, out=None):
 
 def kda_prefill_layer(q_in, k_in, v_in, w_q, w_k, w_v, g_alpha, b_beta, H, dk, dv, out_gate=None,
                       initial_state=None, final_state=None, cu_seqlens=None, conv_state=None, workspace=None,
-                      out=None, want_final_state=True):
+                      out=None, want_final_state=True, snap_interval=None, snapshots=None, snap_offsets=None):
     """kda_preprocess + kda_prefill_chunked in one call (bf16, dk = dv = 128):
     raw inputs [T, H*d] as for kda_preprocess, the rest as for
     kda_prefill_chunked.  Returns (out [T,H,dv], final_state fp32 [N,H,dk,dv] or None).
@@ -129,12 +149,21 @@ def kda_prefill_layer(q_in, k_in, v_in, w_q, w_k, w_v, g_alpha, b_beta, H, dk, d
     need = kda_prefill_workspace_bytes(T, N, H, dk, dv, x)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
-    check(lib().kda_prefill_layer(T, H, dk, dv, _ptr(cu_seqlens), N, x,
-                                  _ptr(q_in), _ptr(k_in), _ptr(v_in), _ptr(w_q), _ptr(w_k), _ptr(w_v),
-                                  _ptr(g_alpha), _ptr(b_beta), _ptr(conv_state), _ptr(out_gate),
-                                  _ptr(initial_state), _ptr(final_state), _ptr(out),
-                                  _ptr(workspace), workspace.numel(), _stream(dev)))
-    return out, final_state
+    if snap_interval is None:
+        check(lib().kda_prefill_layer(T, H, dk, dv, _ptr(cu_seqlens), N, x,
+                                      _ptr(q_in), _ptr(k_in), _ptr(v_in), _ptr(w_q), _ptr(w_k), _ptr(w_v),
+                                      _ptr(g_alpha), _ptr(b_beta), _ptr(conv_state), _ptr(out_gate),
+                                      _ptr(initial_state), _ptr(final_state), _ptr(out),
+                                      _ptr(workspace), workspace.numel(), _stream(dev)))
+        return out, final_state
+    snapshots, snap_offsets = _snap_buffers(snap_interval, T, N, H, dk, dv, dev, snapshots, snap_offsets)
+    check(lib().kda_prefill_layer_snap(T, H, dk, dv, _ptr(cu_seqlens), N, x,
+                                       _ptr(q_in), _ptr(k_in), _ptr(v_in), _ptr(w_q), _ptr(w_k), _ptr(w_v),
+                                       _ptr(g_alpha), _ptr(b_beta), _ptr(conv_state), _ptr(out_gate),
+                                       _ptr(initial_state), _ptr(final_state), _ptr(out),
+                                       _ptr(workspace), workspace.numel(), snap_interval, _ptr(snapshots),
+                                       snapshots.shape[0], _ptr(snap_offsets), _stream(dev)))
+    return out, final_state, snapshots, snap_offsets
 
 
 def kda_decode_layer(q_in, k_in, v_in, w_q, w_k, w_v, g_alpha, b_beta, H, dk, dv, conv_state, state,

@@ -177,6 +177,53 @@ int kda_prefill_layer(int64_t T_tot, int32_t H, int32_t dk, int32_t dv,
                       void* stream);
 
 /*
+ * State snapshots for prefix reuse: kda_prefill_chunked_snap and
+ * kda_prefill_layer_snap are kda_prefill_chunked and kda_prefill_layer that
+ * also write the state of each sequence after every snap_interval tokens
+ * (counted from the sequence's start), so a prefix cache can resume a later
+ * request from the longest cached prefix (the prefix caching of the page
+ * "Ling-3.0-flash: a 124B open MoE ..."; for KDA the whole per-sequence
+ * memory at a prefix is this fixed-size state plus the last three raw
+ * tokens, which the caller has).  Snapshot m (m = 1 .. floor(len_n /
+ * snap_interval)) of sequence n is the state after its first m *
+ * snap_interval tokens (starting from initial_state[n] if given).
+ * Extra arguments:
+ *   snap_interval  tokens between snapshots, a positive multiple of 64;
+ *   snapshots      fp32 [snap_capacity, H, dk, dv]; snapshot m of sequence n
+ *                  is row snap_offsets[n] + m - 1;
+ *   snap_capacity  rows available, at least T_tot / snap_interval (which
+ *                  bounds the total); else KDA_ERR_INVALID_ARGUMENT;
+ *   snap_offsets   device int32 [N + 1], written: the exclusive prefix sums
+ *                  of floor(len_n / snap_interval); snap_offsets[N] = total.
+ * The computation and every other output are those of the plain call.
+ */
+int kda_prefill_chunked_snap(int64_t T_tot, int32_t H, int32_t dk, int32_t dv,
+                             const int32_t* cu_seqlens, int32_t N,
+                             int32_t x_dtype, int32_t gate_dtype,
+                             const void* q, const void* k, const void* v,
+                             const void* log_alpha, const void* beta,
+                             const void* out_gate,
+                             const float* initial_state, float* final_state,
+                             void* out,
+                             void* workspace, size_t workspace_bytes,
+                             int32_t snap_interval, float* snapshots,
+                             int64_t snap_capacity, int32_t* snap_offsets,
+                             void* stream);
+int kda_prefill_layer_snap(int64_t T_tot, int32_t H, int32_t dk, int32_t dv,
+                           const int32_t* cu_seqlens, int32_t N, int32_t x_dtype,
+                           const void* q_in, const void* k_in, const void* v_in,
+                           const void* w_q, const void* w_k, const void* w_v,
+                           const void* g_alpha, const void* b_beta,
+                           float* conv_state,
+                           const void* out_gate,
+                           const float* initial_state, float* final_state,
+                           void* out,
+                           void* workspace, size_t workspace_bytes,
+                           int32_t snap_interval, float* snapshots,
+                           int64_t snap_capacity, int32_t* snap_offsets,
+                           void* stream);
+
+/*
  * kda_decode_step -- one token per sequence, state updated in place.
  * For each (b, h):  S' = Diag(alpha) S;  u = S'^T k;  S <- S' + beta k (v - u)^T;
  *                   o = S^T q;  out = o * sigmoid(z) (or o without a gate).

@@ -36,7 +36,7 @@ def test_status_strings(lib):
     assert _lib.status_string(0) == "KDA_OK"
     assert _lib.status_string(3) == "KDA_ERR_WORKSPACE_TOO_SMALL"
     assert _lib.status_string(99) == "KDA_ERR_UNKNOWN"
-    assert lib.kda_abi_version() == 102
+    assert lib.kda_abi_version() == 103
 
 
 def test_workspace_bytes_bound(lib):
@@ -174,3 +174,22 @@ def test_spec_verify_rejects_bad_arguments(lib):
     assert call(slots=3) == _lib.KDA_ERR_INVALID_ARGUMENT  # NULL indices need one slot per row
     # a commit-only call (T = 0) needs no token inputs and no output
     assert call(B=0, T=0, slots=0, **{n: None for n in names}) == _lib.KDA_OK
+
+
+def test_snapshot_requests_rejected(lib):
+    def call(**kw):
+        a = dict(T=1024, interval=128, snaps=FAKE + 2**32, cap=8, off=FAKE + 2**33)
+        a.update(kw)
+        ws = lib.kda_prefill_workspace_bytes(a["T"], 1, 2, 16, 16, 0)
+        return lib.kda_prefill_chunked_snap(a["T"], 2, 16, 16, None, 1, 0, 0,
+                                            *[P(FAKE + i * 2**22) for i in range(6)], None, None,
+                                            P(FAKE + 2**31), P(FAKE + 2**34), ws, a["interval"],
+                                            P(a["snaps"]), a["cap"], P(a["off"]), None)
+    assert call(interval=100) == _lib.KDA_ERR_INVALID_ARGUMENT
+    assert "multiple of 64" in lib.kda_last_error_detail().decode()
+    assert call(interval=0) == _lib.KDA_ERR_INVALID_ARGUMENT
+    assert call(cap=7) == _lib.KDA_ERR_INVALID_ARGUMENT  # 1024 / 128 = 8 rows needed
+    assert "snap_capacity" in lib.kda_last_error_detail().decode()
+    assert call(off=None) == _lib.KDA_ERR_INVALID_ARGUMENT
+    assert call(snaps=FAKE + 2**31 + 64) == _lib.KDA_ERR_INVALID_ARGUMENT  # overlaps out
+    assert "overlaps" in lib.kda_last_error_detail().decode()
