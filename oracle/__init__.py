@@ -48,6 +48,8 @@ def _load():
         lib.kdao_preprocess.restype = i32
         lib.kdao_recurrence.argtypes = [i64, i32, i32, i32, lp, i32] + [dp] * 7 + [dp, dp, i32]
         lib.kdao_recurrence.restype = i32
+        lib.kdao_recurrence_backward.argtypes = [i64, i32, i32, i32, lp, i32] + [dp] * 9 + [dp] * 7 + [i32]
+        lib.kdao_recurrence_backward.restype = i32
         _lib = lib
     return _lib
 
@@ -141,6 +143,33 @@ def recurrence(q, k, v, log_alpha, beta, z=None, S0=None, cu_seqlens=None, nthre
     if rc != 0:
         raise ValueError("oracle recurrence rejected its arguments")
     return y, S
+
+
+def recurrence_backward(q, k, v, log_alpha, beta, dy, z=None, S0=None, dS_final=None, cu_seqlens=None,
+                        nthreads=None):
+    """Gradients of the recurrence (reverse mode, fp64) for a loss with
+    gradients dy [T, H, dv] on the outputs and dS_final (None: zero) on the
+    final states.  Returns a dict with dq, dk, dlog_alpha [T, H, dk], dv
+    [T, H, dv], dbeta [T, H], dz [T, H, dv] (None without z) and dS0
+    [N, H, dk, dv] (the gradient with respect to the initial states)."""
+    q, k, v, log_alpha, beta, dy, z, S0, dS_final = (
+        _f64(x) for x in (q, k, v, log_alpha, beta, dy, z, S0, dS_final))
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    cu = _cu(cu_seqlens, T)
+    N = cu.shape[0] - 1
+    assert dy.shape == (T, H, dv)
+    out = {"dq": np.empty((T, H, dk)), "dk": np.empty((T, H, dk)), "dv": np.empty((T, H, dv)),
+           "dlog_alpha": np.empty((T, H, dk)), "dbeta": np.empty((T, H)),
+           "dz": np.empty((T, H, dv)) if z is not None else None, "dS0": np.empty((N, H, dk, dv))}
+    rc = _load().kdao_recurrence_backward(
+        T, H, dk, dv, cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), N,
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(z), _ptr(S0), _ptr(dy), _ptr(dS_final),
+        _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dlog_alpha"]), _ptr(out["dbeta"]),
+        _ptr(out["dz"]), _ptr(out["dS0"]), nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle backward rejected its arguments")
+    return out
 
 
 def layer(inputs: dict, nthreads=None, want_conv_state=False):

@@ -295,3 +295,168 @@ int kdao_recurrence(int64_t T, int H, int dk, int dv, const int64_t* cu, int N,
     run_items(rec_item, &R, (int64_t)N * H, nthreads);
     return 0;
 }
+
+/*
+ * Gradients of the recurrence above (reverse mode, fp64), for a scalar loss
+ * whose gradients with respect to the outputs y and the final state are dy
+ * and dS_final.  Each token's forward step is
+ *     S' = Diag(alpha) S_prev;  u = S'^T k;  d = beta (v - u);
+ *     S = S' + k d^T;  o = S^T q;  y = o * sigmoid(z)
+ * and the pass walks the tokens backwards applying the adjoint of each line
+ * in reverse order.  The states before every token are kept from a forward
+ * pass (memory grows with the sequence: small cases only).
+ */
+typedef struct {
+    int64_t T;
+    int H, dk, dv, N;
+    const int64_t* cu;
+    const double *q, *k, *v, *la, *beta, *z, *S0, *dy, *dSf;
+    double *dq, *dk_, *dv_, *dla, *dbeta, *dz, *dS0;
+} bwd_ctx;
+
+static void bwd_item(void* vctx, int64_t item) {
+    const bwd_ctx* R = (const bwd_ctx*)vctx;
+    int n = (int)(item / R->H), h = (int)(item % R->H);
+    int H = R->H, dk = R->dk, dv = R->dv;
+    int64_t t0 = R->cu[n], t1 = R->cu[n + 1], len = t1 - t0;
+    size_t sdim = (size_t)dk * dv;
+    double* hist = (double*)malloc(sizeof(double) * sdim * (size_t)(len + 1)); /* S before token t0 + i */
+    double* Sp = (double*)malloc(sizeof(double) * sdim);  /* S' */
+    double* St = (double*)malloc(sizeof(double) * sdim);  /* S after the token */
+    double* dS = (double*)malloc(sizeof(double) * sdim);
+    double* u = (double*)malloc(sizeof(double) * (size_t)dv);
+    double* dd = (double*)malloc(sizeof(double) * (size_t)dv);
+    double* o = (double*)malloc(sizeof(double) * (size_t)dv);
+    double* dO = (double*)malloc(sizeof(double) * (size_t)dv);
+    double* dvec = (double*)malloc(sizeof(double) * (size_t)dv);
+    const int64_t soff = ((int64_t)n * H + h) * (int64_t)sdim;
+    for (size_t i = 0; i < sdim; ++i) hist[i] = R->S0 ? R->S0[soff + i] : 0.0;
+
+    /* forward, keeping the state before each token */
+    for (int64_t t = t0; t < t1; ++t) {
+        const double* prev = hist + (size_t)(t - t0) * sdim;
+        double* next = hist + (size_t)(t - t0 + 1) * sdim;
+        const double* kt = R->k + (t * H + h) * dk;
+        const double* vt = R->v + (t * H + h) * dv;
+        const double* lat = R->la + (t * H + h) * dk;
+        double bt = R->beta[t * H + h];
+        for (int i = 0; i < dk; ++i) {
+            double a = exp(lat[i]);
+            for (int j = 0; j < dv; ++j) next[(size_t)i * dv + j] = a * prev[(size_t)i * dv + j];
+        }
+        for (int j = 0; j < dv; ++j) u[j] = 0.0;
+        for (int i = 0; i < dk; ++i)
+            for (int j = 0; j < dv; ++j) u[j] += next[(size_t)i * dv + j] * kt[i];
+        for (int i = 0; i < dk; ++i)
+            for (int j = 0; j < dv; ++j) next[(size_t)i * dv + j] += bt * kt[i] * (vt[j] - u[j]);
+    }
+
+    /* backward */
+    for (size_t i = 0; i < sdim; ++i) dS[i] = R->dSf ? R->dSf[soff + i] : 0.0;
+    for (int64_t t = t1 - 1; t >= t0; --t) {
+        const double* prev = hist + (size_t)(t - t0) * sdim;
+        const double* qt = R->q + (t * H + h) * dk;
+        const double* kt = R->k + (t * H + h) * dk;
+        const double* vt = R->v + (t * H + h) * dv;
+        const double* lat = R->la + (t * H + h) * dk;
+        const double* dyt = R->dy + (t * H + h) * dv;
+        double bt = R->beta[t * H + h];
+        /* recompute this token's forward values */
+        for (int i = 0; i < dk; ++i) {
+            double a = exp(lat[i]);
+            for (int j = 0; j < dv; ++j) Sp[(size_t)i * dv + j] = a * prev[(size_t)i * dv + j];
+        }
+        for (int j = 0; j < dv; ++j) u[j] = 0.0;
+        for (int i = 0; i < dk; ++i)
+            for (int j = 0; j < dv; ++j) u[j] += Sp[(size_t)i * dv + j] * kt[i];
+        for (int j = 0; j < dv; ++j) dvec[j] = bt * (vt[j] - u[j]);
+        for (int i = 0; i < dk; ++i)
+            for (int j = 0; j < dv; ++j) St[(size_t)i * dv + j] = Sp[(size_t)i * dv + j] + kt[i] * dvec[j];
+        for (int j = 0; j < dv; ++j) o[j] = 0.0;
+        for (int i = 0; i < dk; ++i)
+            for (int j = 0; j < dv; ++j) o[j] += St[(size_t)i * dv + j] * qt[i];
+        /* y = o * sigmoid(z) */
+        if (R->z) {
+            const double* zt = R->z + (t * H + h) * dv;
+            double* dzt = R->dz + (t * H + h) * dv;
+            for (int j = 0; j < dv; ++j) {
+                double s = sigmoid(zt[j]);
+                dO[j] = dyt[j] * s;
+                dzt[j] = dyt[j] * o[j] * s * (1.0 - s);
+            }
+        } else {
+            for (int j = 0; j < dv; ++j) dO[j] = dyt[j];
+        }
+        /* o = S^T q */
+        double* dqt = R->dq + (t * H + h) * dk;
+        for (int i = 0; i < dk; ++i) {
+            double acc = 0.0;
+            for (int j = 0; j < dv; ++j) {
+                acc += St[(size_t)i * dv + j] * dO[j];
+                dS[(size_t)i * dv + j] += qt[i] * dO[j];
+            }
+            dqt[i] = acc;
+        }
+        /* S = S' + k d^T */
+        double* dkt = R->dk_ + (t * H + h) * dk;
+        for (int j = 0; j < dv; ++j) dd[j] = 0.0;
+        for (int i = 0; i < dk; ++i) {
+            double acc = 0.0;
+            for (int j = 0; j < dv; ++j) {
+                acc += dS[(size_t)i * dv + j] * dvec[j];
+                dd[j] += dS[(size_t)i * dv + j] * kt[i];
+            }
+            dkt[i] = acc;
+        }
+        /* d = beta (v - u) */
+        double db = 0.0;
+        double* dvt = R->dv_ + (t * H + h) * dv;
+        for (int j = 0; j < dv; ++j) {
+            db += dd[j] * (vt[j] - u[j]);
+            dvt[j] = bt * dd[j];
+            dd[j] = -bt * dd[j]; /* now du */
+        }
+        R->dbeta[t * H + h] = db;
+        /* u = S'^T k: dS' = dS + k du^T; dk += S' du */
+        for (int i = 0; i < dk; ++i) {
+            double acc = 0.0;
+            for (int j = 0; j < dv; ++j) {
+                acc += Sp[(size_t)i * dv + j] * dd[j];
+                dS[(size_t)i * dv + j] += kt[i] * dd[j];
+            }
+            dkt[i] += acc;
+        }
+        /* S' = Diag(alpha) S_prev */
+        double* dlat = R->dla + (t * H + h) * dk;
+        for (int i = 0; i < dk; ++i) {
+            double a = exp(lat[i]), acc = 0.0;
+            for (int j = 0; j < dv; ++j) {
+                acc += dS[(size_t)i * dv + j] * prev[(size_t)i * dv + j];
+                dS[(size_t)i * dv + j] *= a;
+            }
+            dlat[i] = a * acc;
+        }
+    }
+    if (R->dS0) memcpy(R->dS0 + soff, dS, sizeof(double) * sdim);
+    free(dvec); free(dO); free(o); free(dd); free(u); free(dS); free(St); free(Sp); free(hist);
+}
+
+/*
+ * dq, dk, dla [T, H, dk]; dv [T, H, dv]; dbeta [T, H]; dz [T, H, dv] (only
+ * with z); dS0 NULL or [N, H, dk, dv].  dy [T, H, dv]; dS_final NULL (zero)
+ * or [N, H, dk, dv].  Returns 0, or -1 on a bad argument.
+ */
+int kdao_recurrence_backward(int64_t T, int H, int dk, int dv, const int64_t* cu, int N,
+                             const double* q, const double* k, const double* v, const double* la,
+                             const double* beta, const double* z, const double* S0,
+                             const double* dy, const double* dS_final,
+                             double* dq, double* dk_, double* dv_, double* dla, double* dbeta,
+                             double* dz, double* dS0, int nthreads) {
+    if (T < 0 || H <= 0 || dk <= 0 || dv <= 0 || N < 0 || !cu || !dy) return -1;
+    if (cu[0] != 0 || cu[N] != T) return -1;
+    if (z && !dz) return -1;
+    bwd_ctx R = {T, H, dk, dv, N, cu, q, k, v, la, beta, z, S0, dy, dS_final,
+                 dq, dk_, dv_, dla, dbeta, dz, dS0};
+    run_items(bwd_item, &R, (int64_t)N * H, nthreads);
+    return 0;
+}
