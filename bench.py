@@ -14,7 +14,8 @@ traffic; the fused serving call (raw token in, preprocess and step in one
 kernel, conv history and state rolled in place) likewise under
 ``decode_layer``, and the speculative verify (one token plus three drafts per
 sequence, the previous call's four tokens committed first) under
-``spec_verify``.  ``roofline`` covers the kernel with the largest share of the step:
+``spec_verify``; the gradients of the chunked recurrence on the 4096-token
+layer under ``backward``.  ``roofline`` covers the kernel with the largest share of the step:
 algorithmic bytes per launch / average launch time from HIP events recorded
 around each kernel during a second pass of the same K steps.  ``cpu_baseline``
 times the fp64 CPU oracle on the same workload (rank 0, one GPU only).
@@ -348,6 +349,42 @@ def bench_spec(args):
             "roofline": roofline("spec_verify", bts, per_ms)}
 
 
+def bench_backward(args):
+    """Gradients of the chunked recurrence (kda_prefill_backward) on the
+    4096-token layer: preprocessed q, k, v and gates of the bench's own
+    inputs, dy ~ N(0, 1) in bf16, initial state and output gate given."""
+    import torch
+    from gated_delta_rule_64_amd import _lib, kda, synth
+
+    inp = synth.make("layer_t4k")
+    H, dk, dv, T = inp["H"], inp["dk"], inp["dv"], inp["T_tot"]
+    q, k, v, la, beta = kda.kda_preprocess(*(dev(inp[n]) for n in ("q_in", "k_in", "v_in", "w_q", "w_k", "w_v",
+                                                                  "g", "b")), H, dk, dv)
+    z = dev(inp["z"]).view(T, H, dv)
+    S0 = torch.randn((1, H, dk, dv), generator=torch.Generator().manual_seed(7)).mul_(0.02).cuda()
+    dy = torch.randn((T, H, dv), generator=torch.Generator().manual_seed(8)).to(torch.bfloat16).cuda()
+    ws = torch.empty(kda.kda_backward_workspace_bytes(T, 1, H, dk, dv), dtype=torch.uint8, device="cuda")
+    steps = max(1, args.steps // 5)
+
+    def call():
+        return kda.kda_prefill_backward(q, k, v, la, beta, dy, out_gate=z, initial_state=S0, workspace=ws)
+
+    for _ in range(max(1, args.warmup // 2)):
+        call()
+    torch.cuda.synchronize()
+    _lib.profile_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        call()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    _lib.profile_enable(False)
+    kern = {name: round(ms / n * 1e3, 2) for name, (n, ms) in _lib.profile_collect().items()}
+    return {"metric": "backward tokens/s (dq, dk, dv, dlog_alpha, dbeta, dz, dS0)",
+            "value": round(T * steps / elapsed, 1), "unit": "tokens/s", "workload": "layer_t4k",
+            "steps": steps, "ms_per_step": round(elapsed / steps * 1e3, 3), "us_per_kernel": kern}
+
+
 def cpu_baseline(res, min_seconds=10.0, max_passes=100):
     """The fp64 oracle (preprocess + token-by-token recurrence) on the bench's
     own inputs, repeated whole until at least ``min_seconds`` of CPU work."""
@@ -431,6 +468,7 @@ def main():
     line["decode"] = bench_decode(args)
     line["decode_layer"] = bench_decode_layer(args)
     line["spec_verify"] = bench_spec(args)
+    line["backward"] = bench_backward(args)
     if args.copy_calibration:
         line["copy_calibration"] = copy_calibration()
     if not args.no_cpu_baseline:

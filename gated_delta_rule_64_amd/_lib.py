@@ -36,6 +36,9 @@ PROTOTYPES = {
                           [_vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "kda_decode_layer": (ctypes.c_int, [_i32, _i32, _i32, _i32, _i32] + [_vp] * 8 + [_vp, _vp, _vp, _i32, _vp, _vp, _vp]),
     "kda_spec_draft_bytes": (_sz, [_i32, _i32, _i32, _i32]),
+    "kda_backward_workspace_bytes": (_sz, [_i64, _i32, _i32, _i32, _i32]),
+    "kda_prefill_backward": (ctypes.c_int, [_i64, _i32, _i32, _i32, _vp, _i32, _i32, _i32] + [_vp] * 7 +
+                             [_vp, _vp] + [_vp] * 7 + [_vp, _sz, _vp]),
     "kda_prefill_chunked_snap": (ctypes.c_int, [_i64, _i32, _i32, _i32, _vp, _i32, _i32, _i32] + [_vp] * 6 +
                                  [_vp, _vp, _vp, _vp, _sz, _i32, _vp, _i64, _vp, _vp]),
     "kda_prefill_layer_snap": (ctypes.c_int, [_i64, _i32, _i32, _i32, _vp, _i32, _i32] + [_vp] * 8 +

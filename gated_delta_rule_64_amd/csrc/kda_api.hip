@@ -122,7 +122,7 @@ const char* kda_status_string(int status) {
 
 const char* kda_last_error_detail(void) { return g_detail; }
 
-int kda_abi_version(void) { return 103; }
+int kda_abi_version(void) { return 104; }
 
 int kda_preprocess(int64_t T_tot, int32_t H, int32_t dk, int32_t dv, const int32_t* cu_seqlens, int32_t N,
                    int32_t x_dtype, const void* q_in, const void* k_in, const void* v_in, const void* w_q,
@@ -520,6 +520,73 @@ int kda_spec_verify(int32_t B, int32_t T, int32_t H, int32_t dk, int32_t dv, int
     a.accepted = accepted; a.drafts = drafts; a.out = out;
     hipError_t e = kda::launch_spec_verify(a, s);
     if (e != hipSuccess) return hip_fail(e, "speculative verify launch");
+    return ok();
+}
+
+size_t kda_backward_workspace_bytes(int64_t T_tot, int32_t N, int32_t H, int32_t dk, int32_t dv) {
+    if (T_tot < 0 || T_tot >= (int64_t(1) << 31) || N < 1 || H < 1 || H > 65535 || !valid_head_dim(dk) ||
+        !valid_head_dim(dv))
+        return 0;
+    return kda::backward_workspace_bytes(T_tot, N, H, dk, dv);
+}
+
+int kda_prefill_backward(int64_t T_tot, int32_t H, int32_t dk, int32_t dv, const int32_t* cu_seqlens, int32_t N,
+                         int32_t x_dtype, int32_t gate_dtype, const void* q, const void* k, const void* v,
+                         const void* log_alpha, const void* beta, const void* out_gate,
+                         const float* initial_state, const void* dy, const float* dS_final, float* dq, float* dk_,
+                         float* dv_, float* dlog_alpha, float* dbeta, float* dz, float* dS0, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+    int st = check_sizes(T_tot, H, dk, dv, N);
+    if (st != KDA_OK) return st;
+    if (!valid_dtype(x_dtype)) return fail(KDA_ERR_INVALID_ARGUMENT, "x_dtype=%d is not KDA_F32 or KDA_BF16", x_dtype);
+    if (!valid_dtype(gate_dtype)) return fail(KDA_ERR_INVALID_ARGUMENT, "gate_dtype=%d is not KDA_F32 or KDA_BF16", gate_dtype);
+    if (cu_seqlens == nullptr && N != 1) return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens is NULL but N=%d", N);
+    if (cu_seqlens != nullptr && (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens is not 4-byte aligned");
+    if ((out_gate == nullptr) != (dz == nullptr))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "dz must be given exactly when out_gate is");
+    const size_t need = kda_backward_workspace_bytes(T_tot, N, H, dk, dv);
+    if (workspace_bytes < need)
+        return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "workspace_bytes=%zu < %zu needed", workspace_bytes, need);
+    if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "workspace is NULL or not 256-byte aligned");
+    const size_t xs = dsize(x_dtype), gs = dsize(gate_dtype);
+    const size_t T = static_cast<size_t>(T_tot);
+    const size_t qk = T * H * dk, vv = T * H * dv;
+    const size_t state = static_cast<size_t>(N) * H * dk * dv * 4;
+    std::vector<Span> sp = {
+        {"q", q, qk * xs, false}, {"k", k, qk * xs, false}, {"v", v, vv * xs, false},
+        {"log_alpha", log_alpha, qk * gs, false},
+        {"out_gate", out_gate, out_gate ? vv * xs : 0, false},
+        {"initial_state", initial_state, initial_state ? state : 0, false},
+        {"dy", dy, vv * xs, false},
+        {"dS_final", dS_final, dS_final ? state : 0, false},
+        {"dq", dq, qk * 4, true}, {"dk", dk_, qk * 4, true}, {"dv", dv_, vv * 4, true},
+        {"dlog_alpha", dlog_alpha, qk * 4, true}, {"dbeta", dbeta, T * H * 4, true},
+        {"dz", dz, dz ? vv * 4 : 0, true}, {"dS0", dS0, dS0 ? state : 0, true},
+        {"workspace", workspace, need, true},
+    };
+    // beta and dbeta rows are H elements, accessed one at a time: element alignment suffices
+    sp[12].bytes = 0;
+    st = check_spans(sp);
+    if (st != KDA_OK) return st;
+    if (T * H > 0 && (beta == nullptr || (reinterpret_cast<uintptr_t>(beta) % gs) != 0))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "beta is NULL or misaligned");
+    if (T * H > 0 && (dbeta == nullptr || (reinterpret_cast<uintptr_t>(dbeta) & 3u) != 0))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "dbeta is NULL or misaligned");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    st = debug_check_cu(cu_seqlens, N, T_tot, s);
+    if (st != KDA_OK) return st;
+    kda::BackwardArgs b{};
+    kda::PrefillArgs& a = b.f;
+    a.T = T_tot; a.H = H; a.dk = dk; a.dv = dv; a.N = N; a.cu = cu_seqlens;
+    a.x = static_cast<kda::DT>(x_dtype); a.gate = static_cast<kda::DT>(gate_dtype);
+    a.q = q; a.k = k; a.v = v; a.la = log_alpha; a.beta = beta; a.z = out_gate;
+    a.S0 = initial_state; a.ws = workspace; a.ws_bytes = workspace_bytes;
+    b.dy = dy; b.dS_final = dS_final;
+    b.dq = dq; b.dk = dk_; b.dv = dv_; b.dla = dlog_alpha; b.dbeta = dbeta; b.dz = dz; b.dS0 = dS0;
+    hipError_t e = kda::launch_backward(b, s);
+    if (e != hipSuccess) return hip_fail(e, "backward launch");
     return ok();
 }
 

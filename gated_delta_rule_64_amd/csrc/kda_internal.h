@@ -115,6 +115,20 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_layer(const DecodeLayerArgs& a, hipStream_t s);
 hipError_t launch_spec_verify(const SpecArgs& a, hipStream_t s);
 
+// Gradients of the chunked recurrence: everything kda_prefill_chunked takes,
+// the output and final-state gradients, and where the input gradients go
+// (all fp32).  dz only with z; dS0 may be NULL.
+struct BackwardArgs {
+    PrefillArgs f;  // the forward call's arguments (out, S_out unused)
+    const void* dy;  // [T, H, dv], x dtype
+    const float* dS_final;  // NULL: zero
+    float *dq, *dk, *dv, *dla, *dbeta, *dz, *dS0;
+};
+size_t backward_workspace_bytes(int64_t T, int N, int H, int dk, int dv);
+hipError_t launch_backward(const BackwardArgs& a, hipStream_t s);
+// the fp32 chunked forward alone (phase 1 records, phase 2 state pass)
+hipError_t launch_gen_forward(const PrefillArgs& a, hipStream_t s, int32_t* base, float* rec);
+
 // chunked prefill: workspace layout and the two implementations
 bool prefill_uses_mfma(int dk, int dv, DT x);
 size_t prefill_workspace_bytes(int64_t T, int N, int H, int dk, int dv, DT x);

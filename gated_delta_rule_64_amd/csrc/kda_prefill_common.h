@@ -53,6 +53,24 @@ __global__ __launch_bounds__(1024) void chunk_map_kernel(const int32_t* __restri
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Record of one (chunk slot, head) on the fp32 path, offsets in floats:
+// W [64][dk], U~ [64][dv], Q' [64][dk], K^ [64][dk], M U~ [64][dv], gamma [dk]
+struct GenRec {
+    int64_t W, U, Qp, Kh, Oi, gam, size;
+};
+
+__host__ __device__ inline GenRec gen_rec(int dk, int dv) {
+    GenRec r;
+    r.W = 0;
+    r.U = r.W + 64 * dk;
+    r.Qp = r.U + 64 * dv;
+    r.Kh = r.Qp + 64 * dk;
+    r.Oi = r.Kh + 64 * dk;
+    r.gam = r.Oi + 64 * dv;
+    r.size = (r.gam + dk + 63) / 64 * 64;
+    return r;
+}
+
 inline int64_t chunk_slots_bound(int64_t T, int N) { return (T + kChunk - 1) / kChunk + N; }
 
 inline size_t chunk_map_base_bytes(int N) { return align_up(static_cast<size_t>(N + 1) * 4, 256); }

@@ -95,22 +95,6 @@ __global__ __launch_bounds__(1024) void chunk_map_kernel(const int32_t* __restri
 
 namespace {
 
-struct GenRec {
-    int64_t W, U, Qp, Kh, Oi, gam, size;  // offsets in floats
-};
-
-__host__ __device__ inline GenRec gen_rec(int dk, int dv) {
-    GenRec r;
-    r.W = 0;
-    r.U = r.W + 64 * dk;
-    r.Qp = r.U + 64 * dv;
-    r.Kh = r.Qp + 64 * dk;
-    r.Oi = r.Kh + 64 * dk;
-    r.gam = r.Oi + 64 * dv;
-    r.size = (r.gam + dk + 63) / 64 * 64;
-    return r;
-}
-
 template <typename XT, typename GT>
 struct GenK {
     int64_t T;
@@ -279,7 +263,7 @@ __global__ __launch_bounds__(256) void gen_state_kernel(GenK<XT, GT> a) {
                 o[i] += qp * s;
             }
         }
-        if (r < L) {
+        if (r < L && a.out != nullptr) {  // (no output: a forward pass run for its records and states)
             const int64_t oidx = ((t0 + r) * a.H + h) * dv + 16 * sl + c4;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -346,6 +330,15 @@ hipError_t launch_gen_typed(const PrefillArgs& a, hipStream_t s, int32_t* base, 
 
 }  // namespace
 
+hipError_t launch_gen_forward(const PrefillArgs& a, hipStream_t s, int32_t* base, float* rec) {
+    if (a.x == DT::BF16) {
+        return a.gate == DT::BF16 ? launch_gen_typed<bf16, bf16>(a, s, base, rec)
+                                  : launch_gen_typed<bf16, float>(a, s, base, rec);
+    }
+    return a.gate == DT::BF16 ? launch_gen_typed<float, bf16>(a, s, base, rec)
+                              : launch_gen_typed<float, float>(a, s, base, rec);
+}
+
 bool prefill_uses_mfma(int dk, int dv, DT x) { return mfma_prefill_supports(dk, dv, x); }
 
 size_t prefill_workspace_bytes(int64_t T, int N, int H, int dk, int dv, DT x) {
@@ -368,13 +361,7 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
     }
     if (e != hipSuccess) return e;
     if (prefill_uses_mfma(a.dk, a.dv, a.x)) return launch_prefill_mfma(a, s, base, slot_info, recs);
-    float* rec = reinterpret_cast<float*>(recs);
-    if (a.x == DT::BF16) {
-        return a.gate == DT::BF16 ? launch_gen_typed<bf16, bf16>(a, s, base, rec)
-                                  : launch_gen_typed<bf16, float>(a, s, base, rec);
-    }
-    return a.gate == DT::BF16 ? launch_gen_typed<float, bf16>(a, s, base, rec)
-                              : launch_gen_typed<float, float>(a, s, base, rec);
+    return launch_gen_forward(a, s, base, reinterpret_cast<float*>(recs));
 }
 
 bool layer_fused_supported(int dk, int dv, DT x) { return prefill_uses_mfma(dk, dv, x); }

@@ -212,3 +212,35 @@ def kda_spec_verify(q_in, k_in, v_in, w_q, w_k, w_v, g_alpha, b_beta, H, dk, dv,
                                 _ptr(state), state.shape[0], _ptr(state_indices), _ptr(accepted),
                                 _ptr(drafts), _ptr(out), _stream(q_in.device)))
     return out
+
+
+def kda_backward_workspace_bytes(T_tot, N, H, dk, dv):
+    return int(lib().kda_backward_workspace_bytes(T_tot, N, H, dk, dv))
+
+
+def kda_prefill_backward(q, k, v, log_alpha, beta, dy, out_gate=None, initial_state=None, dS_final=None,
+                         cu_seqlens=None, workspace=None, want_dS0=True):
+    """Gradients of kda_prefill_chunked for output gradients dy [T,H,dv] (and
+    dS_final on the final states).  Returns a dict of fp32 tensors dq, dk,
+    dlog_alpha [T,H,dk], dv [T,H,dv], dbeta [T,H], dz (None without a gate)
+    and dS0 [N,H,dk,dv] (None if not wanted)."""
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    N = _n_seqs(cu_seqlens)
+    dev = q.device
+    f32 = dict(dtype=torch.float32, device=dev)
+    g = {"dq": torch.empty((T, H, dk), **f32), "dk": torch.empty((T, H, dk), **f32),
+         "dv": torch.empty((T, H, dv), **f32), "dlog_alpha": torch.empty((T, H, dk), **f32),
+         "dbeta": torch.empty((T, H), **f32),
+         "dz": torch.empty((T, H, dv), **f32) if out_gate is not None else None,
+         "dS0": torch.empty((N, H, dk, dv), **f32) if want_dS0 else None}
+    need = kda_backward_workspace_bytes(T, N, H, dk, dv)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    check(lib().kda_prefill_backward(T, H, dk, dv, _ptr(cu_seqlens), N, _dtype_code(q), _dtype_code(log_alpha),
+                                     _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(out_gate),
+                                     _ptr(initial_state), _ptr(dy), _ptr(dS_final),
+                                     _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["dlog_alpha"]),
+                                     _ptr(g["dbeta"]), _ptr(g["dz"]), _ptr(g["dS0"]),
+                                     _ptr(workspace), workspace.numel(), _stream(dev)))
+    return g

@@ -224,6 +224,45 @@ int kda_prefill_layer_snap(int64_t T_tot, int32_t H, int32_t dk, int32_t dv,
                            void* stream);
 
 /*
+ * Gradients of kda_prefill_chunked (training).  For a loss whose gradients
+ * with respect to the outputs y and the final states are dy and dS_final,
+ * returns the gradients with respect to every input of the recurrence: q, k,
+ * v, log_alpha, beta, the output-gate logits and the initial states.  They
+ * are the adjoint of the chunked form (the recurrence of the section "KDA:
+ * constant-size memory over a very long context" of the page "Ling-3.0-flash:
+ * a 124B open MoE ..."; the pages train KDA from the first step), computed in
+ * three passes: the forward again with the state kept at every chunk start,
+ * the state gradient carried backwards over each sequence's chunks, and every
+ * other gradient per chunk in parallel.  The gradient of the decay logits g
+ * follows as dlog_alpha * -sigmoid(g), since log_alpha = -softplus(g).
+ * Arguments: those of kda_prefill_chunked (any supported head size, both
+ * dtypes; the output and final state are not recomputed), plus
+ *   dy            [T_tot, H, dv] (x_dtype);
+ *   dS_final      NULL (zero) or fp32 [N, H, dk, dv];
+ *   grad_q, grad_k, grad_log_alpha [T_tot, H, dk], grad_v [T_tot, H, dv],
+ *   grad_beta [T_tot, H]: fp32 outputs;
+ *   grad_out_gate fp32 [T_tot, H, dv], required exactly when out_gate is given;
+ *   grad_initial_state  NULL or fp32 [N, H, dk, dv].
+ *   workspace     at least kda_backward_workspace_bytes(T_tot, N, H, dk, dv)
+ *                 bytes, 256-byte aligned.
+ */
+size_t kda_backward_workspace_bytes(int64_t T_tot, int32_t N, int32_t H,
+                                    int32_t dk, int32_t dv);
+int kda_prefill_backward(int64_t T_tot, int32_t H, int32_t dk, int32_t dv,
+                         const int32_t* cu_seqlens, int32_t N,
+                         int32_t x_dtype, int32_t gate_dtype,
+                         const void* q, const void* k, const void* v,
+                         const void* log_alpha, const void* beta,
+                         const void* out_gate,
+                         const float* initial_state,
+                         const void* dy, const float* dS_final,
+                         float* grad_q, float* grad_k, float* grad_v,
+                         float* grad_log_alpha, float* grad_beta,
+                         float* grad_out_gate, float* grad_initial_state,
+                         void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/*
  * kda_decode_step -- one token per sequence, state updated in place.
  * For each (b, h):  S' = Diag(alpha) S;  u = S'^T k;  S <- S' + beta k (v - u)^T;
  *                   o = S^T q;  out = o * sigmoid(z) (or o without a gate).

@@ -36,7 +36,7 @@ def test_status_strings(lib):
     assert _lib.status_string(0) == "KDA_OK"
     assert _lib.status_string(3) == "KDA_ERR_WORKSPACE_TOO_SMALL"
     assert _lib.status_string(99) == "KDA_ERR_UNKNOWN"
-    assert lib.kda_abi_version() == 103
+    assert lib.kda_abi_version() == 104
 
 
 def test_workspace_bytes_bound(lib):
