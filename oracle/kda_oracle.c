@@ -341,8 +341,8 @@ static void bwd_item(void* vctx, int64_t item) {
         const double* lat = R->la + (t * H + h) * dk;
         double bt = R->beta[t * H + h];
         for (int i = 0; i < dk; ++i) {
-            double a = exp(lat[i]);
-            for (int j = 0; j < dv; ++j) next[(size_t)i * dv + j] = a * prev[(size_t)i * dv + j];
+            const double al = exp(lat[i]);
+            for (int j = 0; j < dv; ++j) next[(size_t)i * dv + j] = al * prev[(size_t)i * dv + j];
         }
         for (int j = 0; j < dv; ++j) u[j] = 0.0;
         for (int i = 0; i < dk; ++i)
@@ -363,8 +363,8 @@ static void bwd_item(void* vctx, int64_t item) {
         double bt = R->beta[t * H + h];
         /* recompute this token's forward values */
         for (int i = 0; i < dk; ++i) {
-            double a = exp(lat[i]);
-            for (int j = 0; j < dv; ++j) Sp[(size_t)i * dv + j] = a * prev[(size_t)i * dv + j];
+            const double al = exp(lat[i]);
+            for (int j = 0; j < dv; ++j) Sp[(size_t)i * dv + j] = al * prev[(size_t)i * dv + j];
         }
         for (int j = 0; j < dv; ++j) u[j] = 0.0;
         for (int i = 0; i < dk; ++i)
@@ -429,12 +429,13 @@ static void bwd_item(void* vctx, int64_t item) {
         /* S' = Diag(alpha) S_prev */
         double* dlat = R->dla + (t * H + h) * dk;
         for (int i = 0; i < dk; ++i) {
-            double a = exp(lat[i]), acc = 0.0;
+            const double al = exp(lat[i]);
+            double acc = 0.0;
             for (int j = 0; j < dv; ++j) {
                 acc += dS[(size_t)i * dv + j] * prev[(size_t)i * dv + j];
-                dS[(size_t)i * dv + j] *= a;
+                dS[(size_t)i * dv + j] *= al;
             }
-            dlat[i] = a * acc;
+            dlat[i] = al * acc;
         }
     }
     if (R->dS0) memcpy(R->dS0 + soff, dS, sizeof(double) * sdim);
