@@ -15,8 +15,9 @@
 //     dY      = -T^T dT T^T   (Y = I + B A, T = Y^-1),  d(B A) = dY below the diagonal
 // and the chain rule through A, M (products of k, q and e^{G_r - G_s}), the
 // e^G factors and G = cumsum(log alpha).  Three passes:
-//   1. the forward: chunk records and the state at every chunk start
-//      (snapshots after every chunk);
+//   1. the forward: chunk records (a tiled version of the prefill's fp32
+//      record kernel) and the fp32 state pass with the state at every chunk
+//      start (snapshots after every chunk);
 //   2. the chain, chunks in reverse order per (sequence, head, 16 columns):
 //      dS_end of every chunk, and dS at the sequence start (d initial state);
 //   3. per (chunk, head) in parallel: everything else.
@@ -42,9 +43,182 @@ struct BwdK {
     const float* S0;
     const float* dSf;
     float* dSe;  // [slot][H][dk][dv]: dS at the end of each chunk
-    float* scratch;  // [slot][H]: U, dO, dU [64][dv]; dW, and the dq, dk, dG sums [64][dk]
+    float* scratch;  // [slot][H]: U, dO, dU [64][dv]; dW, the dq, dk, dG sums and K_e [64][dk]
     float *dq, *dk, *dv, *dla, *dbeta, *dz, *dS0;
 };
+
+// C = A B for 64 rows and N columns (N = 16 .. 128), K terms, by the 256
+// threads of the workgroup: thread (tr, tc) owns rows TR tr .. + TR-1 and
+// columns TC tc .. + TC-1, so a step of k loads TR + TC operands for TR x TC
+// products.  A(r, k), B(k, c) read the operands; out(r, c, acc) takes each
+// result (every (r, c) once, by the same thread for equal N).
+template <int N, typename FA, typename FB, typename FO>
+__device__ __forceinline__ void mm64(int K, FA A, FB B, FO out) {
+    constexpr int TC = N >= 128 ? 8 : 4;
+    constexpr int NCT = N / TC;     // column tiles
+    constexpr int TR = NCT / 4;     // rows per thread: NCT * 64 / TR = 256 threads
+    static_assert(N % TC == 0 && TR >= 1 && (64 / TR) * NCT == 256, "tile shape");
+    const int tc = threadIdx.x % NCT, tr = threadIdx.x / NCT;
+    float acc[TR][TC];
+#pragma unroll
+    for (int i = 0; i < TR; ++i)
+#pragma unroll
+        for (int jj = 0; jj < TC; ++jj) acc[i][jj] = 0.f;
+#pragma unroll 4
+    for (int k = 0; k < K; ++k) {
+        float av[TR], bv[TC];
+#pragma unroll
+        for (int i = 0; i < TR; ++i) av[i] = A(TR * tr + i, k);
+#pragma unroll
+        for (int jj = 0; jj < TC; ++jj) bv[jj] = B(k, TC * tc + jj);
+#pragma unroll
+        for (int i = 0; i < TR; ++i)
+#pragma unroll
+            for (int jj = 0; jj < TC; ++jj) acc[i][jj] += av[i] * bv[jj];
+    }
+#pragma unroll
+    for (int i = 0; i < TR; ++i)
+#pragma unroll
+        for (int jj = 0; jj < TC; ++jj) out(TR * tr + i, TC * tc + jj, acc[i][jj]);
+}
+
+// e^x for x <= 0 (a decay between two tokens of a chunk) through the
+// hardware base-2 exponential; x > 0 only occurs for entries that are masked
+// out, and is clamped to 0 so that nothing overflows
+__device__ __forceinline__ float decay(float x) { return __builtin_amdgcn_exp2f(fminf(x, 0.f) * kLog2e); }
+
+// A (strictly lower) and M (lower with diagonal) of a chunk, by 4 x 4 tiles
+// of (r, s) per thread; K, Q, G rows padded to DK + 1 floats in LDS.
+template <int DK>
+__device__ __forceinline__ void am_tiles(const float* sK, const float* sQ, const float* sG, float* sA, float* sM) {
+    constexpr int KP = DK + 1;
+    const int tid = threadIdx.x;
+        const int r0 = 4 * (tid >> 4), s0 = 4 * (tid & 15);
+        float av[4][4], mv[4][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) av[i][jj] = mv[i][jj] = 0.f;
+        if (s0 <= r0 + 3) {  // the tile reaches the lower triangle
+            for (int c = 0; c < DK; ++c) {
+                float kr[4], qr[4], gr[4], ks[4], gs[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    kr[i] = sK[(r0 + i) * KP + c];
+                    qr[i] = sQ[(r0 + i) * KP + c];
+                    gr[i] = sG[(r0 + i) * KP + c];
+                    ks[i] = sK[(s0 + i) * KP + c];
+                    gs[i] = sG[(s0 + i) * KP + c];
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        // e^{G_r - G_s}; above the diagonal the exponent is
+                        // clamped (those entries are dropped below)
+                        const float ke = ks[jj] * decay(gr[i] - gs[jj]);
+                        av[i][jj] += kr[i] * ke;
+                        mv[i][jj] += qr[i] * ke;
+                    }
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int r = r0 + i, s_ = s0 + jj;
+                sA[r * 64 + s_] = s_ < r ? av[i][jj] : 0.f;
+                sM[r * 64 + s_] = s_ <= r ? mv[i][jj] : 0.f;
+            }
+}
+
+// T = (I + Diag(beta) A)^-1 by forward substitution, one row at a time
+__device__ __forceinline__ void t_solve(const float* sA, const float* sB, float* sT) {
+    const int tid = threadIdx.x;
+    for (int r = 0; r < 64; ++r) {
+        if (tid < 64) {
+            const int c = tid;
+            float acc = r == c ? 1.f : 0.f;
+            if (c < r) {
+                float sum = 0.f;
+                for (int s = c; s < r; ++s) sum += sA[r * 64 + s] * sT[s * 64 + c];
+                acc = -sB[r] * sum;
+            }
+            sT[r * 64 + c] = acc;
+        }
+        __syncthreads();
+    }
+}
+
+// ---- pass 1a: the chunk records of the fp32 path (the same record as the
+// prefill's gen_intra_kernel: W, U~, Q', K^, M U~, gamma), with the tiled
+// products above
+template <int DK>
+constexpr size_t rec_lds_bytes() {
+    return (3 * 64 * (DK + 1) + 3 * 4096 + 64) * sizeof(float);  // K, Q, G; A, M, T; beta
+}
+
+template <int DK, int DV, typename XT, typename GT>
+__global__ __launch_bounds__(256) void bwd_rec_kernel(BwdK<XT, GT> a) {
+    extern __shared__ float smem[];
+    constexpr int KP = DK + 1;
+    float* sK = smem;
+    float* sQ = sK + 64 * KP;
+    float* sG = sQ + 64 * KP;
+    float* sA = sG + 64 * KP;
+    float* sM = sA + 4096;
+    float* sT = sM + 4096;
+    float* sB = sT + 4096;
+    const int slot = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+    if (slot >= a.base[a.N]) return;
+    const int n = find_seq(a.base, a.N, slot);
+    const int64_t t0 = seq_begin(a.cu, n) + static_cast<int64_t>(slot - a.base[n]) * kChunk;
+    const int L = static_cast<int>(min(static_cast<int64_t>(kChunk), seq_finish(a.cu, n, a.T) - t0));
+    const GenRec R = gen_rec(DK, DV);
+    float* rec = const_cast<float*>(a.rec) + (static_cast<int64_t>(slot) * a.H + h) * R.size;
+    auto tok = [&](int r) { return (t0 + r) * a.H + h; };
+    for (int i = tid; i < 64 * DK; i += 256) {
+        const int r = i / DK, c = i % DK;
+        const bool in = r < L;
+        sK[r * KP + c] = in ? ld(a.k + tok(r) * DK + c) : 0.f;
+        sQ[r * KP + c] = in ? ld(a.q + tok(r) * DK + c) : 0.f;
+        sG[r * KP + c] = in ? ld(a.la + tok(r) * DK + c) : 0.f;  // padded tokens: no decay, no write
+    }
+    if (tid < 64) sB[tid] = tid < L ? ld(a.beta + tok(tid)) : 0.f;
+    __syncthreads();
+    if (tid < DK) {
+        float acc = 0.f;
+        for (int r = 0; r < 64; ++r) {
+            acc += sG[r * KP + tid];
+            sG[r * KP + tid] = acc;
+        }
+    }
+    __syncthreads();
+    // K^ and gamma (G_last = G_63: padded rows add no decay)
+    for (int i = tid; i < 64 * DK; i += 256) {
+        const int r = i / DK, c = i % DK;
+        rec[R.Kh + i] = expf(sG[63 * KP + c] - sG[r * KP + c]) * sK[r * KP + c];
+    }
+    if (tid < DK) rec[R.gam + tid] = expf(sG[63 * KP + tid]);
+    am_tiles<DK>(sK, sQ, sG, sA, sM);
+    __syncthreads();
+    t_solve(sA, sB, sT);
+    // W = T (B e^G K),  U~ = T (B V)
+    mm64<DK>(64, [&](int r, int s_) { return sT[r * 64 + s_]; },
+             [&](int s_, int c) { return sB[s_] * expf(sG[s_ * KP + c]) * sK[s_ * KP + c]; },
+             [&](int r, int c, float acc) { rec[R.W + r * DK + c] = acc; });
+    mm64<DV>(64, [&](int r, int s_) { return sT[r * 64 + s_]; },
+             [&](int s_, int c) { return s_ < L ? sB[s_] * ld(a.v + tok(s_) * DV + c) : 0.f; },
+             [&](int r, int c, float acc) { rec[R.U + r * DV + c] = acc; });
+    __syncthreads();  // W and U~ are in the record
+    // Q' = e^G Q - M W,  M U~
+    mm64<DK>(64, [&](int r, int s_) { return sM[r * 64 + s_]; }, [&](int s_, int c) { return rec[R.W + s_ * DK + c]; },
+             [&](int r, int c, float acc) {
+                 rec[R.Qp + r * DK + c] = expf(sG[r * KP + c]) * sQ[r * KP + c] - acc;
+             });
+    mm64<DV>(64, [&](int r, int s_) { return sM[r * 64 + s_]; }, [&](int s_, int c) { return rec[R.U + s_ * DV + c]; },
+             [&](int r, int c, float acc) { rec[R.Oi + r * DV + c] = acc; });
+}
 
 // ---- pass 2: the chain, chunks in reverse order ----
 template <int DK, int DV, typename XT, typename GT>
@@ -110,21 +284,24 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdK<XT, GT> a) {
     }
 }
 
-constexpr size_t scratch_floats(int dk, int dv) { return 3 * 64 * static_cast<size_t>(dv) + 4 * 64 * static_cast<size_t>(dk); }
+constexpr size_t scratch_floats(int dk, int dv) { return 3 * 64 * static_cast<size_t>(dv) + 5 * 64 * static_cast<size_t>(dk); }
 
 template <int DK>
 constexpr size_t intra_lds_bytes() {
-    // K, G [64][DK]; A, M, T, dT, P [64][64]; beta, dbeta [64]; dG_last [DK]
-    return (2 * 64 * DK + 5 * 4096 + 2 * 64 + DK) * sizeof(float);
+    // K, G [64][DK + 1]; A, M, T, dT, P [64][64]; beta, dbeta [64]; dG_last [DK]
+    return (2 * 64 * (DK + 1) + 5 * 4096 + 2 * 64 + DK) * sizeof(float);
 }
 
 // ---- pass 3: per (chunk, head), every input gradient ----
 template <int DK, int DV, typename XT, typename GT>
 __global__ __launch_bounds__(256) void bwd_intra_kernel(BwdK<XT, GT> a) {
     extern __shared__ float smem[];
-    float* sK = smem;              // [64][DK] keys
-    float* sG = sK + 64 * DK;      // [64][DK] decay cumsums; at the end dG
-    float* sA = sG + 64 * DK;      // [64][64] A
+    // K and G rows padded to DK + 1 floats: the tiles below read 4 rows at
+    // one channel, which would otherwise land in one LDS bank
+    constexpr int KP = DK + 1;
+    float* sK = smem;              // [64][KP] keys
+    float* sG = sK + 64 * KP;      // [64][KP] decay cumsums; at the end dG
+    float* sA = sG + 64 * KP;      // [64][64] A
     float* sM = sA + 4096;         // [64][64] M, later dM
     float* sT = sM + 4096;         // [64][64] T
     float* sdT = sT + 4096;        // [64][64] dT, later dY
@@ -156,14 +333,15 @@ __global__ __launch_bounds__(256) void bwd_intra_kernel(BwdK<XT, GT> a) {
     float* gq = gdW + 64 * DK;
     float* gk = gq + 64 * DK;
     float* gG = gk + 64 * DK;
+    float* gKe = gG + 64 * DK;
     auto tok = [&](int r) { return (t0 + r) * a.H + h; };
 
     // ---- 0. the forward's chunk quantities: G, A, M, T
     for (int i = tid; i < 64 * DK; i += 256) {
         const int r = i / DK, c = i % DK;
         const bool in = r < L;
-        sK[i] = in ? ld(a.k + tok(r) * DK + c) : 0.f;
-        sG[i] = in ? ld(a.la + tok(r) * DK + c) : 0.f;
+        sK[r * KP + c] = in ? ld(a.k + tok(r) * DK + c) : 0.f;
+        sG[r * KP + c] = in ? ld(a.la + tok(r) * DK + c) : 0.f;
     }
     if (tid < 64) {
         sB[tid] = tid < L ? ld(a.beta + tok(tid)) : 0.f;
@@ -174,193 +352,200 @@ __global__ __launch_bounds__(256) void bwd_intra_kernel(BwdK<XT, GT> a) {
     if (tid < DK) {
         float acc = 0.f;
         for (int r = 0; r < 64; ++r) {
-            acc += sG[r * DK + tid];
-            sG[r * DK + tid] = acc;
+            acc += sG[r * KP + tid];
+            sG[r * KP + tid] = acc;
         }
     }
     __syncthreads();
-    for (int i = tid; i < 4096; i += 256) {
-        const int r = i >> 6, s = i & 63;
-        float av = 0.f, mv = 0.f;
-        if (s <= r && r < L) {
-            for (int c = 0; c < DK; ++c) {
-                const float ks = sK[s * DK + c] * expf(sG[r * DK + c] - sG[s * DK + c]);
-                av += sK[r * DK + c] * ks;
-                mv += ld(a.q + tok(r) * DK + c) * ks;
-            }
-        }
-        sA[i] = s < r ? av : 0.f;
-        sM[i] = mv;
-    }
-    __syncthreads();
-    for (int r = 0; r < 64; ++r) {
-        if (tid < 64) {
-            const int c = tid;
-            float acc = r == c ? 1.f : 0.f;
-            if (c < r) {
-                float sum = 0.f;
-                for (int s = c; s < r; ++s) sum += sA[r * 64 + s] * sT[s * 64 + c];
-                acc = -sB[r] * sum;
-            }
-            sT[r * 64 + c] = acc;
+    // A (strictly lower) and M (lower with diagonal) by 4 x 4 tiles of (r, s);
+    // the queries sit, padded like K, in the space of T, dT, P until T is made
+    {
+        float* sQ = sT;
+        for (int i = tid; i < 64 * DK; i += 256) {
+            const int r = i / DK, c = i % DK;
+            sQ[r * KP + c] = r < L ? ld(a.q + tok(r) * DK + c) : 0.f;
         }
         __syncthreads();
+        am_tiles<DK>(sK, sQ, sG, sA, sM);
+        __syncthreads();  // the queries are dead; T goes where they were
     }
+    t_solve(sA, sB, sT);
 
     // ---- 1. U = U~ - W S and O = Q' S + M U~; dO, dz
-    for (int i = tid; i < 64 * DV; i += 256) {
-        const int r = i / DV, c = i % DV;
-        float u = rec[R.U + i], o = rec[R.Oi + i];
-        if (S != nullptr) {
-            for (int kk = 0; kk < DK; ++kk) {
-                const float s = S[kk * DV + c];
-                u -= rec[R.W + r * DK + kk] * s;
-                o += rec[R.Qp + r * DK + kk] * s;
-            }
-        }
-        float d = 0.f;
-        if (r < L) {
-            const int64_t oidx = tok(r) * DV + c;
-            const float dy = ld(a.dy + oidx);
-            if (a.z) {
-                const float sg = sigmoid(ld(a.z + oidx));
-                d = dy * sg;
-                a.dz[oidx] = dy * o * sg * (1.f - sg);
-            } else {
-                d = dy;
-            }
-        }
-        gU[i] = u;
-        gdO[i] = d;
+    mm64<DV>(S != nullptr ? DK : 0, [&](int r, int kk) { return rec[R.W + r * DK + kk]; },
+             [&](int kk, int c) { return S[kk * DV + c]; },
+             [&](int r, int c, float acc) { gU[r * DV + c] = rec[R.U + r * DV + c] - acc; });
+    mm64<DV>(S != nullptr ? DK : 0, [&](int r, int kk) { return rec[R.Qp + r * DK + kk]; },
+             [&](int kk, int c) { return S[kk * DV + c]; },
+             [&](int r, int c, float acc) {
+                 const float o = rec[R.Oi + r * DV + c] + acc;
+                 float d = 0.f;
+                 if (r < L) {
+                     const int64_t oidx = tok(r) * DV + c;
+                     const float dy = ld(a.dy + oidx);
+                     if (a.z) {
+                         const float sg = sigmoid(ld(a.z + oidx));
+                         d = dy * sg;
+                         a.dz[oidx] = dy * o * sg * (1.f - sg);
+                     } else {
+                         d = dy;
+                     }
+                 }
+                 gdO[r * DV + c] = d;
+             });
+    // K_e = e^G K, for dT and d(B K_e) below
+    for (int e = tid; e < 64 * DK; e += 256) {
+        const int r = e / DK, c = e % DK;
+        gKe[e] = expf(sG[r * KP + c]) * sK[r * KP + c];
     }
     __syncthreads();
     // ---- 2. dU = M^T dO + K^ dS_end
-    for (int i = tid; i < 64 * DV; i += 256) {
-        const int r = i / DV, c = i % DV;
-        float acc = 0.f;
-        for (int s = r; s < 64; ++s) acc += sM[s * 64 + r] * gdO[s * DV + c];
-        for (int kk = 0; kk < DK; ++kk) acc += rec[R.Kh + r * DK + kk] * dSe[kk * DV + c];
-        gdU[i] = acc;
-    }
+    mm64<DV>(64, [&](int r, int s_) { return sM[s_ * 64 + r]; }, [&](int s_, int c) { return gdO[s_ * DV + c]; },
+             [&](int r, int c, float acc) { gdU[r * DV + c] = acc; });
+    mm64<DV>(DK, [&](int r, int kk) { return rec[R.Kh + r * DK + kk]; }, [&](int kk, int c) { return dSe[kk * DV + c]; },
+             [&](int r, int c, float acc) { gdU[r * DV + c] += acc; });  // (same thread, same element)
     __syncthreads();
-    // ---- 3. per owned (row, channel): dQ_e, dK^, dW; the sums of dq, dk,
-    // dG start here
-    for (int e = tid; e < 64 * DK; e += 256) {
-        const int r = e / DK, c = e % DK;
-        float dqe = 0.f, dkh = 0.f, dw = 0.f;
-        for (int col = 0; col < DV; ++col) {
-            const float s = S != nullptr ? S[c * DV + col] : 0.f;
-            dqe += gdO[r * DV + col] * s;
-            dkh += gU[r * DV + col] * dSe[c * DV + col];
-            dw -= gdU[r * DV + col] * s;
-        }
-        gdW[e] = dw;
-        const float g = sG[e], glast = sG[63 * DK + c];
-        const float eg = expf(g), eh = expf(glast - g);
-        const float qv = r < L ? ld(a.q + tok(r) * DK + c) : 0.f;
-        const float kv = sK[e];
-        gq[e] = eg * dqe;             // Q_e = e^G Q
-        gk[e] = eh * dkh;             // K^ = e^{G_last - G} K
-        gG[e] = eg * qv * dqe - eh * kv * dkh;
-        atomicAdd(&sdGl[c], eh * kv * dkh);  // (G_last's share of K^)
-    }
+    // ---- 3. dQ_e = dO S^T, dK^ = U dS_end^T, dW = -dU S^T; the sums of dq,
+    // dk, dG start here (Q_e = e^G Q, K^ = e^{G_last - G} K)
+    mm64<DK>(S != nullptr ? DV : 0, [&](int r, int col) { return gdO[r * DV + col]; },
+             [&](int col, int i) { return S[i * DV + col]; },
+             [&](int r, int c, float dqe) {
+                 const float eg = expf(sG[r * KP + c]);
+                 const float qv = r < L ? ld(a.q + tok(r) * DK + c) : 0.f;
+                 gq[r * DK + c] = eg * dqe;
+                 gG[r * DK + c] = eg * qv * dqe;
+             });
+    mm64<DK>(DV, [&](int r, int col) { return gU[r * DV + col]; }, [&](int col, int i) { return dSe[i * DV + col]; },
+             [&](int r, int c, float dkh) {
+                 const int e = r * DK + c;
+                 const float eh = expf(sG[63 * KP + c] - sG[r * KP + c]), kv = sK[r * KP + c];
+                 gk[e] = eh * dkh;
+                 gG[e] -= eh * kv * dkh;
+                 atomicAdd(&sdGl[c], eh * kv * dkh);  // (G_last's share of K^)
+             });
+    mm64<DK>(S != nullptr ? DV : 0, [&](int r, int col) { return gdU[r * DV + col]; },
+             [&](int col, int i) { return S[i * DV + col]; },
+             [&](int r, int c, float acc) { gdW[r * DK + c] = -acc; });
     if (tid < DK) {  // dgamma = diag(S^T dS_end); gamma = e^{G_last}
         float dg = 0.f;
-        for (int col = 0; col < DV; ++col) dg += (S != nullptr ? S[tid * DV + col] : 0.f) * dSe[tid * DV + col];
-        atomicAdd(&sdGl[tid], expf(sG[63 * DK + tid]) * dg);
+        if (S != nullptr)
+            for (int col = 0; col < DV; ++col) dg += S[tid * DV + col] * dSe[tid * DV + col];
+        atomicAdd(&sdGl[tid], expf(sG[63 * KP + tid]) * dg);
     }
     __syncthreads();
     // ---- 4. dM = dO U^T (into M's place); dT = dU (B V)^T + dW (B K_e)^T
-    for (int i = tid; i < 4096; i += 256) {
-        const int r = i >> 6, s = i & 63;
-        float dm = 0.f, dt = 0.f;
-        if (s <= r) {
-            for (int col = 0; col < DV; ++col) dm += gdO[r * DV + col] * gU[s * DV + col];
-        }
-        if (s < r && s < L) {
-            const float bs = sB[s];
-            for (int col = 0; col < DV; ++col) dt += gdU[r * DV + col] * bs * ld(a.v + tok(s) * DV + col);
-            for (int kk = 0; kk < DK; ++kk)
-                dt += gdW[r * DK + kk] * bs * expf(sG[s * DK + kk]) * sK[s * DK + kk];
-        }
-        sM[i] = dm;
-        sdT[i] = dt;
-    }
+    mm64<64>(DV, [&](int r, int col) { return gdO[r * DV + col]; }, [&](int col, int s_) { return gU[s_ * DV + col]; },
+             [&](int r, int s_, float acc) { sM[r * 64 + s_] = s_ <= r ? acc : 0.f; });
+    mm64<64>(DV, [&](int r, int col) { return gdU[r * DV + col]; },
+             [&](int col, int s_) { return s_ < L ? ld(a.v + tok(s_) * DV + col) : 0.f; },
+             [&](int r, int s_, float acc) { sdT[r * 64 + s_] = acc; });
+    mm64<64>(DK, [&](int r, int kk) { return gdW[r * DK + kk]; }, [&](int kk, int s_) { return gKe[s_ * DK + kk]; },
+             [&](int r, int s_, float acc) {  // (same thread, same element as just above)
+                 sdT[r * 64 + s_] = s_ < r ? sB[s_] * (sdT[r * 64 + s_] + acc) : 0.f;
+             });
     // d(B V) = T^T dU: dv, and beta's share
-    for (int i = tid; i < 64 * DV; i += 256) {
-        const int s = i / DV, c = i % DV;
-        if (s >= L) continue;
-        float acc = 0.f;
-        for (int r = s; r < 64; ++r) acc += sT[r * 64 + s] * gdU[r * DV + c];
-        a.dv[tok(s) * DV + c] = sB[s] * acc;
-        atomicAdd(&sdB[s], ld(a.v + tok(s) * DV + c) * acc);
-    }
-    // d(B K_e) = T^T dW: k's and G's and beta's shares
-    for (int e = tid; e < 64 * DK; e += 256) {
-        const int s = e / DK, c = e % DK;
-        float acc = 0.f;
-        for (int r = s; r < 64; ++r) acc += sT[r * 64 + s] * gdW[r * DK + c];
-        const float ke = expf(sG[e]) * sK[e];  // K_e
-        gk[e] += sB[s] * expf(sG[e]) * acc;
-        gG[e] += sB[s] * ke * acc;
-        if (s < L) atomicAdd(&sdB[s], ke * acc);
-    }
+    mm64<DV>(64, [&](int s_, int r) { return sT[r * 64 + s_]; }, [&](int r, int c) { return gdU[r * DV + c]; },
+             [&](int s_, int c, float acc) {
+                 if (s_ >= L) return;
+                 a.dv[tok(s_) * DV + c] = sB[s_] * acc;
+                 atomicAdd(&sdB[s_], ld(a.v + tok(s_) * DV + c) * acc);
+             });
+    // d(B K_e) = T^T dW: k's, G's and beta's shares
+    mm64<DK>(64, [&](int s_, int r) { return sT[r * 64 + s_]; }, [&](int r, int c) { return gdW[r * DK + c]; },
+             [&](int s_, int c, float acc) {
+                 const int e = s_ * DK + c;
+                 const float ke = gKe[e];
+                 gk[e] += sB[s_] * expf(sG[s_ * KP + c]) * acc;
+                 gG[e] += sB[s_] * ke * acc;
+                 if (s_ < L) atomicAdd(&sdB[s_], ke * acc);
+             });
     __syncthreads();
     // ---- 5. dY = -T^T dT T^T; d(B A) = dY below the diagonal
-    for (int i = tid; i < 4096; i += 256) {
-        const int r = i >> 6, c = i & 63;
-        float acc = 0.f;
-        for (int s = 0; s < 64; ++s) acc += sdT[r * 64 + s] * sT[c * 64 + s];
-        sP[i] = acc;
-    }
+    mm64<64>(64, [&](int r, int s_) { return sdT[r * 64 + s_]; }, [&](int s_, int c) { return sT[c * 64 + s_]; },
+             [&](int r, int c, float acc) { sP[r * 64 + c] = acc; });
     __syncthreads();
-    for (int i = tid; i < 4096; i += 256) {
-        const int a_ = i >> 6, c = i & 63;
-        float acc = 0.f;
-        for (int r = 0; r < 64; ++r) acc += sT[r * 64 + a_] * sP[r * 64 + c];
-        sdT[i] = c < a_ ? -acc : 0.f;  // dY, strictly lower part (B A has nothing else)
-    }
+    mm64<64>(64, [&](int a_, int r) { return sT[r * 64 + a_]; }, [&](int r, int c) { return sP[r * 64 + c]; },
+             [&](int a_, int c, float acc) { sdT[a_ * 64 + c] = c < a_ ? -acc : 0.f; });
     __syncthreads();
     if (tid < 64) {  // beta's share through B A: sum_s dY_rs A_rs
         float acc = 0.f;
-        for (int s = 0; s < tid; ++s) acc += sdT[tid * 64 + s] * sA[tid * 64 + s];
+        for (int s_ = 0; s_ < tid; ++s_) acc += sdT[tid * 64 + s_] * sA[tid * 64 + s_];
         atomicAdd(&sdB[tid], acc);
     }
-    // ---- 6. through A (dA = B dY) and M (dM), with E_rsc = e^{G_rc - G_sc}
-    for (int e = tid; e < 64 * DK; e += 256) {
-        const int r = e / DK, c = e % DK;
-        const float gr = sG[e], kr = sK[e];
-        const float qr = r < L ? ld(a.q + tok(r) * DK + c) : 0.f;
-        // this element as row r of A and M (s <= r)
-        float dkr = 0.f, dqr = 0.f, dgr = 0.f;
-        for (int s = 0; s <= r; ++s) {
-            const float ks = sK[s * DK + c] * expf(gr - sG[s * DK + c]);
-            const float da = s < r ? sB[r] * sdT[r * 64 + s] : 0.f;
-            const float dm = sM[r * 64 + s];
-            dkr += da * ks;
-            dqr += dm * ks;
-            dgr += (da * kr + dm * qr) * ks;
+    // ---- 6. through A (dA = B dY) and M (dM), with E_rsc = e^{G_rc - G_sc}.
+    // Thread tiles as in mm64<DK>: rows R0 .. R0+TR-1, channels C0 .. C0+TC-1.
+    // As row r of A and M:  dk_rc += sum_s dA_rs k_sc E,  dq_rc += sum_s dM_rs k_sc E,
+    //   and dG_rc gains k_rc (the first sum) + q_rc (the second);
+    // as column s of them:  dk_sc += sum_r w_rsc E with w = dA_rs k_rc + dM_rs q_rc,
+    //   and dG_sc loses k_sc times that sum.
+    {
+        constexpr int TC = DK >= 128 ? 8 : 4, NCT = DK / TC, TR = NCT / 4;
+        const int C0 = TC * (tid % NCT), R0 = TR * (tid / NCT);
+        float dkr[TR][TC], dqr[TR][TC], dks[TR][TC], gown[TR][TC];
+#pragma unroll
+        for (int i = 0; i < TR; ++i)
+#pragma unroll
+            for (int jj = 0; jj < TC; ++jj) {
+                dkr[i][jj] = dqr[i][jj] = dks[i][jj] = 0.f;
+                gown[i][jj] = sG[(R0 + i) * KP + C0 + jj];
+            }
+        for (int s_ = 0; s_ < R0 + TR; ++s_) {  // row role: s <= r
+            float da[TR], dm[TR], ks[TC], gs[TC];
+#pragma unroll
+            for (int i = 0; i < TR; ++i) {
+                da[i] = sB[R0 + i] * sdT[(R0 + i) * 64 + s_];  // (zero unless s < r)
+                dm[i] = sM[(R0 + i) * 64 + s_];                // (zero unless s <= r)
+            }
+#pragma unroll
+            for (int jj = 0; jj < TC; ++jj) {
+                ks[jj] = sK[s_ * KP + C0 + jj];
+                gs[jj] = sG[s_ * KP + C0 + jj];
+            }
+#pragma unroll
+            for (int i = 0; i < TR; ++i)
+#pragma unroll
+                for (int jj = 0; jj < TC; ++jj) {
+                    const float ke = ks[jj] * decay(gown[i][jj] - gs[jj]);
+                    dkr[i][jj] += da[i] * ke;
+                    dqr[i][jj] += dm[i] * ke;
+                }
         }
-        // this element as column s = r of A and M (rows r2 >= s)
-        float dks = 0.f, dgs = 0.f;
-        for (int r2 = r; r2 < 64; ++r2) {
-            const float E = expf(sG[r2 * DK + c] - gr);
-            const float da = r2 > r ? sB[r2] * sdT[r2 * 64 + r] : 0.f;
-            const float dm = sM[r2 * 64 + r];
-            const float q2 = r2 < L ? ld(a.q + tok(r2) * DK + c) : 0.f;
-            const float w = (da * sK[r2 * DK + c] + dm * q2) * E;
-            dks += w;
-            dgs -= w * kr;
+        for (int r2 = R0; r2 < 64; ++r2) {  // column role: r >= s
+            float da[TR], dm[TR], kr[TC], qr[TC], gr[TC];
+#pragma unroll
+            for (int i = 0; i < TR; ++i) {
+                da[i] = sB[r2] * sdT[r2 * 64 + R0 + i];
+                dm[i] = sM[r2 * 64 + R0 + i];
+            }
+#pragma unroll
+            for (int jj = 0; jj < TC; ++jj) {
+                kr[jj] = sK[r2 * KP + C0 + jj];
+                qr[jj] = r2 < L ? ld(a.q + tok(r2) * DK + C0 + jj) : 0.f;
+                gr[jj] = sG[r2 * KP + C0 + jj];
+            }
+#pragma unroll
+            for (int i = 0; i < TR; ++i)
+#pragma unroll
+                for (int jj = 0; jj < TC; ++jj)
+                    dks[i][jj] += (da[i] * kr[jj] + dm[i] * qr[jj]) * decay(gr[jj] - gown[i][jj]);
         }
-        gk[e] += dkr + dks;
-        gq[e] += dqr;
-        gG[e] += dgr + dgs;
+#pragma unroll
+        for (int i = 0; i < TR; ++i)
+#pragma unroll
+            for (int jj = 0; jj < TC; ++jj) {
+                const int r = R0 + i, c = C0 + jj, e = r * DK + c;
+                const float kv = sK[r * KP + c];
+                const float qv = r < L ? ld(a.q + tok(r) * DK + c) : 0.f;
+                gk[e] += dkr[i][jj] + dks[i][jj];
+                gq[e] += dqr[i][jj];
+                gG[e] += kv * dkr[i][jj] + qv * dqr[i][jj] - kv * dks[i][jj];
+            }
     }
     __syncthreads();  // every read of sK, sG, sdT, sM is done
     // ---- 7. dla = reverse cumsum of dG (G_last is G_63); outputs
     for (int e = tid; e < 64 * DK; e += 256) {
         const int r = e / DK, c = e % DK;
-        sG[e] = gG[e] + (r == 63 ? sdGl[c] : 0.f);
+        sG[r * KP + c] = gG[e] + (r == 63 ? sdGl[c] : 0.f);
         if (r < L) {
             a.dq[tok(r) * DK + c] = gq[e];
             a.dk[tok(r) * DK + c] = gk[e];
@@ -370,7 +555,7 @@ __global__ __launch_bounds__(256) void bwd_intra_kernel(BwdK<XT, GT> a) {
     if (tid < DK) {
         float acc = 0.f;
         for (int r = 63; r >= 0; --r) {
-            acc += sG[r * DK + tid];
+            acc += sG[r * KP + tid];
             if (r < L) a.dla[tok(r) * DK + tid] = acc;
         }
     }
@@ -398,7 +583,7 @@ BwdLayout bwd_layout(int64_t T, int N, int H, int dk, int dv) {
 }
 
 template <int DK, int DV, typename XT, typename GT>
-hipError_t launch_bwd_typed(const BackwardArgs& b, hipStream_t s, const BwdLayout& Lo) {
+hipError_t launch_bwd_typed(const BackwardArgs& b, const PrefillArgs& fa, hipStream_t s, const BwdLayout& Lo) {
     const PrefillArgs& f = b.f;
     char* ws = static_cast<char*>(f.ws);
     BwdK<XT, GT> k{};
@@ -414,6 +599,22 @@ hipError_t launch_bwd_typed(const BackwardArgs& b, hipStream_t s, const BwdLayou
     k.dSe = reinterpret_cast<float*>(ws + Lo.dse);
     k.scratch = reinterpret_cast<float*>(ws + Lo.scratch);
     k.dq = b.dq; k.dk = b.dk; k.dv = b.dv; k.dla = b.dla; k.dbeta = b.dbeta; k.dz = b.dz; k.dS0 = b.dS0;
+    const int64_t slots = chunk_slots_bound(f.T, f.N);
+    if (slots > 0 && f.T > 0) {
+        constexpr size_t lds = rec_lds_bytes<DK>();
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_rec_kernel<DK, DV, XT, GT>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+        if (e != hipSuccess) return e;
+        LaunchTimer timer("bwd_records", s);
+        hipLaunchKernelGGL((bwd_rec_kernel<DK, DV, XT, GT>), dim3(static_cast<unsigned>(slots), f.H), dim3(256), lds,
+                           s, k);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    {
+        hipError_t e = launch_gen_state(fa, s, const_cast<int32_t*>(k.base), const_cast<float*>(k.rec));
+        if (e != hipSuccess) return e;
+    }
     {
         const int64_t blocks = static_cast<int64_t>(f.N) * f.H * (DV / 16);
         LaunchTimer timer("bwd_chain", s);
@@ -422,7 +623,6 @@ hipError_t launch_bwd_typed(const BackwardArgs& b, hipStream_t s, const BwdLayou
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    const int64_t slots = chunk_slots_bound(f.T, f.N);
     if (slots == 0 || f.T == 0) return hipSuccess;
     constexpr size_t lds = intra_lds_bytes<DK>();
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_intra_kernel<DK, DV, XT, GT>),
@@ -435,22 +635,22 @@ hipError_t launch_bwd_typed(const BackwardArgs& b, hipStream_t s, const BwdLayou
 }
 
 template <int DK, int DV>
-hipError_t launch_bwd_dims(const BackwardArgs& b, hipStream_t s, const BwdLayout& Lo) {
+hipError_t launch_bwd_dims(const BackwardArgs& b, const PrefillArgs& fa, hipStream_t s, const BwdLayout& Lo) {
     if (b.f.x == DT::BF16) {
-        return b.f.gate == DT::BF16 ? launch_bwd_typed<DK, DV, bf16, bf16>(b, s, Lo)
-                                    : launch_bwd_typed<DK, DV, bf16, float>(b, s, Lo);
+        return b.f.gate == DT::BF16 ? launch_bwd_typed<DK, DV, bf16, bf16>(b, fa, s, Lo)
+                                    : launch_bwd_typed<DK, DV, bf16, float>(b, fa, s, Lo);
     }
-    return b.f.gate == DT::BF16 ? launch_bwd_typed<DK, DV, float, bf16>(b, s, Lo)
-                                : launch_bwd_typed<DK, DV, float, float>(b, s, Lo);
+    return b.f.gate == DT::BF16 ? launch_bwd_typed<DK, DV, float, bf16>(b, fa, s, Lo)
+                                : launch_bwd_typed<DK, DV, float, float>(b, fa, s, Lo);
 }
 
 template <int DK>
-hipError_t launch_bwd_dk(const BackwardArgs& b, hipStream_t s, const BwdLayout& Lo) {
+hipError_t launch_bwd_dk(const BackwardArgs& b, const PrefillArgs& fa, hipStream_t s, const BwdLayout& Lo) {
     switch (b.f.dv) {
-        case 16: return launch_bwd_dims<DK, 16>(b, s, Lo);
-        case 32: return launch_bwd_dims<DK, 32>(b, s, Lo);
-        case 64: return launch_bwd_dims<DK, 64>(b, s, Lo);
-        case 128: return launch_bwd_dims<DK, 128>(b, s, Lo);
+        case 16: return launch_bwd_dims<DK, 16>(b, fa, s, Lo);
+        case 32: return launch_bwd_dims<DK, 32>(b, fa, s, Lo);
+        case 64: return launch_bwd_dims<DK, 64>(b, fa, s, Lo);
+        case 128: return launch_bwd_dims<DK, 128>(b, fa, s, Lo);
         default: return hipErrorInvalidValue;
     }
 }
@@ -479,14 +679,12 @@ hipError_t launch_backward(const BackwardArgs& b, hipStream_t s) {
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipError_t e = launch_gen_forward(fa, s, base, reinterpret_cast<float*>(ws + Lo.rec));
-    if (e != hipSuccess) return e;
-    // 2. and 3.
+    // records (pass 1a), then the fp32 state pass over them (pass 1b), then 2. and 3.
     switch (f.dk) {
-        case 16: return launch_bwd_dk<16>(b, s, Lo);
-        case 32: return launch_bwd_dk<32>(b, s, Lo);
-        case 64: return launch_bwd_dk<64>(b, s, Lo);
-        case 128: return launch_bwd_dk<128>(b, s, Lo);
+        case 16: return launch_bwd_dk<16>(b, fa, s, Lo);
+        case 32: return launch_bwd_dk<32>(b, fa, s, Lo);
+        case 64: return launch_bwd_dk<64>(b, fa, s, Lo);
+        case 128: return launch_bwd_dk<128>(b, fa, s, Lo);
         default: return hipErrorInvalidValue;
     }
 }

@@ -126,8 +126,10 @@ struct BackwardArgs {
 };
 size_t backward_workspace_bytes(int64_t T, int N, int H, int dk, int dv);
 hipError_t launch_backward(const BackwardArgs& a, hipStream_t s);
-// the fp32 chunked forward alone (phase 1 records, phase 2 state pass)
+// the fp32 chunked forward alone (phase 1 records, phase 2 state pass), and
+// its state pass alone over records already made
 hipError_t launch_gen_forward(const PrefillArgs& a, hipStream_t s, int32_t* base, float* rec);
+hipError_t launch_gen_state(const PrefillArgs& a, hipStream_t s, int32_t* base, float* rec);
 
 // chunked prefill: workspace layout and the two implementations
 bool prefill_uses_mfma(int dk, int dv, DT x);

@@ -330,6 +330,29 @@ hipError_t launch_gen_typed(const PrefillArgs& a, hipStream_t s, int32_t* base, 
 
 }  // namespace
 
+template <typename XT, typename GT>
+hipError_t launch_gen_state_typed(const PrefillArgs& a, hipStream_t s, int32_t* base, float* rec) {
+    GenK<XT, GT> k;
+    k.T = a.T; k.H = a.H; k.dk = a.dk; k.dv = a.dv; k.N = a.N; k.cu = a.cu; k.base = base;
+    k.q = static_cast<const XT*>(a.q); k.k = static_cast<const XT*>(a.k);
+    k.v = static_cast<const XT*>(a.v); k.z = static_cast<const XT*>(a.z);
+    k.la = static_cast<const GT*>(a.la); k.beta = static_cast<const GT*>(a.beta);
+    k.S0 = a.S0; k.S_out = a.S_out; k.out = static_cast<XT*>(a.out); k.rec = rec; k.snap = a.snap;
+    const int64_t blocks = static_cast<int64_t>(a.N) * a.H * (a.dv / 16);
+    LaunchTimer timer("gen_state", s);
+    hipLaunchKernelGGL((gen_state_kernel<XT, GT>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, k);
+    return hipGetLastError();
+}
+
+hipError_t launch_gen_state(const PrefillArgs& a, hipStream_t s, int32_t* base, float* rec) {
+    if (a.x == DT::BF16) {
+        return a.gate == DT::BF16 ? launch_gen_state_typed<bf16, bf16>(a, s, base, rec)
+                                  : launch_gen_state_typed<bf16, float>(a, s, base, rec);
+    }
+    return a.gate == DT::BF16 ? launch_gen_state_typed<float, bf16>(a, s, base, rec)
+                              : launch_gen_state_typed<float, float>(a, s, base, rec);
+}
+
 hipError_t launch_gen_forward(const PrefillArgs& a, hipStream_t s, int32_t* base, float* rec) {
     if (a.x == DT::BF16) {
         return a.gate == DT::BF16 ? launch_gen_typed<bf16, bf16>(a, s, base, rec)
