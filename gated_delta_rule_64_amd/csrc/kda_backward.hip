@@ -150,16 +150,17 @@ __device__ __forceinline__ void t_solve(const float* sA, const float* sB, float*
     }
 }
 
-// ---- pass 1a: the chunk records of the fp32 path (the same record as the
-// prefill's gen_intra_kernel: W, U~, Q', K^, M U~, gamma), with the tiled
-// products above
+// ---- the chunk records of the fp32 path (W, U~, Q', K^, M U~, gamma; the
+// layout in kda_prefill_common.h), with the tiled products above.  The fp32
+// prefill makes its records here too, and pass 1 of the gradients remakes
+// them.
 template <int DK>
 constexpr size_t rec_lds_bytes() {
     return (3 * 64 * (DK + 1) + 3 * 4096 + 64) * sizeof(float);  // K, Q, G; A, M, T; beta
 }
 
 template <int DK, int DV, typename XT, typename GT>
-__global__ __launch_bounds__(256) void bwd_rec_kernel(BwdK<XT, GT> a) {
+__global__ __launch_bounds__(256) void chunk_records_kernel(BwdK<XT, GT> a) {
     extern __shared__ float smem[];
     constexpr int KP = DK + 1;
     float* sK = smem;
@@ -583,6 +584,50 @@ BwdLayout bwd_layout(int64_t T, int N, int H, int dk, int dv) {
 }
 
 template <int DK, int DV, typename XT, typename GT>
+hipError_t launch_records_typed(const BwdK<XT, GT>& k, const PrefillArgs& f, hipStream_t s) {
+    const int64_t slots = chunk_slots_bound(f.T, f.N);
+    if (slots == 0 || f.T == 0) return hipSuccess;
+    constexpr size_t lds = rec_lds_bytes<DK>();
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_records_kernel<DK, DV, XT, GT>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+    LaunchTimer timer("chunk_records", s);
+    hipLaunchKernelGGL((chunk_records_kernel<DK, DV, XT, GT>), dim3(static_cast<unsigned>(slots), f.H), dim3(256), lds,
+                       s, k);
+    return hipGetLastError();
+}
+
+template <int DK, int DV, typename XT, typename GT>
+hipError_t launch_records_args(const PrefillArgs& f, hipStream_t s, const int32_t* base, float* rec) {
+    BwdK<XT, GT> k{};
+    k.T = f.T; k.H = f.H; k.N = f.N; k.cu = f.cu; k.base = base; k.rec = rec;
+    k.q = static_cast<const XT*>(f.q); k.k = static_cast<const XT*>(f.k); k.v = static_cast<const XT*>(f.v);
+    k.la = static_cast<const GT*>(f.la); k.beta = static_cast<const GT*>(f.beta);
+    return launch_records_typed<DK, DV, XT, GT>(k, f, s);
+}
+
+template <int DK, int DV>
+hipError_t launch_records_dims(const PrefillArgs& f, hipStream_t s, const int32_t* base, float* rec) {
+    if (f.x == DT::BF16) {
+        return f.gate == DT::BF16 ? launch_records_args<DK, DV, bf16, bf16>(f, s, base, rec)
+                                  : launch_records_args<DK, DV, bf16, float>(f, s, base, rec);
+    }
+    return f.gate == DT::BF16 ? launch_records_args<DK, DV, float, bf16>(f, s, base, rec)
+                              : launch_records_args<DK, DV, float, float>(f, s, base, rec);
+}
+
+template <int DK>
+hipError_t launch_records_dk(const PrefillArgs& f, hipStream_t s, const int32_t* base, float* rec) {
+    switch (f.dv) {
+        case 16: return launch_records_dims<DK, 16>(f, s, base, rec);
+        case 32: return launch_records_dims<DK, 32>(f, s, base, rec);
+        case 64: return launch_records_dims<DK, 64>(f, s, base, rec);
+        case 128: return launch_records_dims<DK, 128>(f, s, base, rec);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <int DK, int DV, typename XT, typename GT>
 hipError_t launch_bwd_typed(const BackwardArgs& b, const PrefillArgs& fa, hipStream_t s, const BwdLayout& Lo) {
     const PrefillArgs& f = b.f;
     char* ws = static_cast<char*>(f.ws);
@@ -600,15 +645,8 @@ hipError_t launch_bwd_typed(const BackwardArgs& b, const PrefillArgs& fa, hipStr
     k.scratch = reinterpret_cast<float*>(ws + Lo.scratch);
     k.dq = b.dq; k.dk = b.dk; k.dv = b.dv; k.dla = b.dla; k.dbeta = b.dbeta; k.dz = b.dz; k.dS0 = b.dS0;
     const int64_t slots = chunk_slots_bound(f.T, f.N);
-    if (slots > 0 && f.T > 0) {
-        constexpr size_t lds = rec_lds_bytes<DK>();
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_rec_kernel<DK, DV, XT, GT>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-        if (e != hipSuccess) return e;
-        LaunchTimer timer("bwd_records", s);
-        hipLaunchKernelGGL((bwd_rec_kernel<DK, DV, XT, GT>), dim3(static_cast<unsigned>(slots), f.H), dim3(256), lds,
-                           s, k);
-        e = hipGetLastError();
+    {
+        hipError_t e = launch_records_typed<DK, DV, XT, GT>(k, f, s);
         if (e != hipSuccess) return e;
     }
     {
@@ -658,6 +696,16 @@ hipError_t launch_bwd_dk(const BackwardArgs& b, const PrefillArgs& fa, hipStream
 }  // namespace
 
 size_t backward_workspace_bytes(int64_t T, int N, int H, int dk, int dv) { return bwd_layout(T, N, H, dk, dv).total; }
+
+hipError_t launch_chunk_records(const PrefillArgs& f, hipStream_t s, const int32_t* base, float* rec) {
+    switch (f.dk) {
+        case 16: return launch_records_dk<16>(f, s, base, rec);
+        case 32: return launch_records_dk<32>(f, s, base, rec);
+        case 64: return launch_records_dk<64>(f, s, base, rec);
+        case 128: return launch_records_dk<128>(f, s, base, rec);
+        default: return hipErrorInvalidValue;
+    }
+}
 
 hipError_t launch_backward(const BackwardArgs& b, hipStream_t s) {
     const PrefillArgs& f = b.f;

@@ -130,6 +130,8 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t s);
 // its state pass alone over records already made
 hipError_t launch_gen_forward(const PrefillArgs& a, hipStream_t s, int32_t* base, float* rec);
 hipError_t launch_gen_state(const PrefillArgs& a, hipStream_t s, int32_t* base, float* rec);
+// the fp32 path's chunk records (phase 1) alone
+hipError_t launch_chunk_records(const PrefillArgs& a, hipStream_t s, const int32_t* base, float* rec);
 
 // chunked prefill: workspace layout and the two implementations
 bool prefill_uses_mfma(int dk, int dv, DT x);

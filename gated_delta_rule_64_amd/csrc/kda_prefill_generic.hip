@@ -110,118 +110,7 @@ struct GenK {
     Snapshots snap;
 };
 
-// ---- phase 1: per (chunk slot, head), the state-independent factors ----
-template <typename XT, typename GT>
-__global__ __launch_bounds__(256) void gen_intra_kernel(GenK<XT, GT> a) {
-    extern __shared__ float smem[];
-    const int dk = a.dk, dv = a.dv;
-    float* sK = smem;            // [64][dk] keys, later beta e^G K
-    float* sQ = sK + 64 * dk;    // [64][dk] queries, later e^G Q
-    float* sG = sQ + 64 * dk;    // [64][dk] decay cumsums, later W
-    float* sA = sG + 64 * dk;    // [64][64]
-    float* sM = sA + 4096;       // [64][64]
-    float* sT = sM + 4096;       // [64][64]
-    float* sB = sT + 4096;       // [64] beta
-    const int slot = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
-    if (slot >= a.base[a.N]) return;
-    const int n = find_seq(a.base, a.N, slot);
-    const int64_t t0 = seq_begin(a.cu, n) + static_cast<int64_t>(slot - a.base[n]) * kChunk;
-    const int L = static_cast<int>(min(static_cast<int64_t>(kChunk), seq_finish(a.cu, n, a.T) - t0));
-    const GenRec R = gen_rec(dk, dv);
-    float* rec = a.rec + (static_cast<int64_t>(slot) * a.H + h) * R.size;
-
-    for (int i = tid; i < 64 * dk; i += 256) {
-        const int r = i / dk, c = i % dk;
-        const bool in = r < L;
-        const int64_t idx = ((t0 + r) * a.H + h) * dk + c;
-        sK[i] = in ? ld(a.k + idx) : 0.f;
-        sQ[i] = in ? ld(a.q + idx) : 0.f;
-        sG[i] = in ? ld(a.la + idx) : 0.f;  // padded tokens: no decay, no write
-    }
-    if (tid < 64) sB[tid] = tid < L ? ld(a.beta + (t0 + tid) * a.H + h) : 0.f;
-    __syncthreads();
-    if (tid < dk) {
-        float acc = 0.f;
-        for (int r = 0; r < 64; ++r) {
-            acc += sG[r * dk + tid];
-            sG[r * dk + tid] = acc;
-        }
-    }
-    __syncthreads();
-    // K^ and gamma (G_last = G_63: padded rows add no decay)
-    for (int i = tid; i < 64 * dk; i += 256) {
-        const int c = i % dk;
-        rec[R.Kh + i] = expf(sG[63 * dk + c] - sG[i]) * sK[i];
-    }
-    if (tid < dk) rec[R.gam + tid] = expf(sG[63 * dk + tid]);
-    // A (strictly lower) and M (lower with diagonal)
-    for (int i = tid; i < 4096; i += 256) {
-        const int r = i >> 6, s = i & 63;
-        float av = 0.f, mv = 0.f;
-        if (s <= r) {
-            for (int c = 0; c < dk; ++c) {
-                const float ks = sK[s * dk + c] * expf(sG[r * dk + c] - sG[s * dk + c]);
-                av += sK[r * dk + c] * ks;
-                mv += sQ[r * dk + c] * ks;
-            }
-        }
-        sA[i] = s < r ? av : 0.f;
-        sM[i] = mv;
-    }
-    __syncthreads();
-    // T = (I + Diag(beta) A)^-1 by forward substitution, one row at a time
-    for (int r = 0; r < 64; ++r) {
-        if (tid < 64) {
-            const int c = tid;
-            float acc = r == c ? 1.f : 0.f;
-            if (c < r) {
-                float sum = 0.f;
-                for (int s = c; s < r; ++s) sum += sA[r * 64 + s] * sT[s * 64 + c];
-                acc = -sB[r] * sum;
-            }
-            sT[r * 64 + c] = acc;
-        }
-        __syncthreads();
-    }
-    // operands of the products: beta e^G K and e^G Q
-    for (int i = tid; i < 64 * dk; i += 256) {
-        const int r = i / dk;
-        const float e = expf(sG[i]);
-        sK[i] *= sB[r] * e;
-        sQ[i] *= e;
-    }
-    __syncthreads();
-    // W = T (beta e^G K), kept in LDS (over G) and stored
-    for (int i = tid; i < 64 * dk; i += 256) {
-        const int r = i / dk, c = i % dk;
-        float acc = 0.f;
-        for (int s = 0; s <= r; ++s) acc += sT[r * 64 + s] * sK[s * dk + c];
-        sG[i] = acc;
-        rec[R.W + i] = acc;
-    }
-    // U~ = T Diag(beta) V
-    for (int i = tid; i < 64 * dv; i += 256) {
-        const int r = i / dv, c = i % dv;
-        float acc = 0.f;
-        for (int s = 0; s <= r && s < L; ++s)
-            acc += sT[r * 64 + s] * sB[s] * ld(a.v + ((t0 + s) * a.H + h) * dv + c);
-        rec[R.U + i] = acc;
-    }
-    __syncthreads();
-    // Q' = e^G Q - M W;  M U~
-    for (int i = tid; i < 64 * dk; i += 256) {
-        const int r = i / dk, c = i % dk;
-        float acc = sQ[i];
-        for (int s = 0; s <= r; ++s) acc -= sM[r * 64 + s] * sG[s * dk + c];
-        rec[R.Qp + i] = acc;
-    }
-    for (int i = tid; i < 64 * dv; i += 256) {
-        const int r = i / dv, c = i % dv;
-        float acc = 0.f;
-        for (int s = 0; s <= r; ++s) acc += sM[r * 64 + s] * rec[R.U + s * dv + c];
-        rec[R.Oi + i] = acc;
-    }
-}
+// ---- phase 1, the records, is chunk_records_kernel (kda_backward.hip) ----
 
 // ---- phase 2: per (sequence, head, 16 state columns), chunks in order ----
 template <typename XT, typename GT>
@@ -299,8 +188,6 @@ __global__ __launch_bounds__(256) void gen_state_kernel(GenK<XT, GT> a) {
     }
 }
 
-size_t gen_lds_bytes(int dk) { return (3 * 64 * dk + 3 * 4096 + 64) * sizeof(float); }
-
 template <typename XT, typename GT>
 hipError_t launch_gen_typed(const PrefillArgs& a, hipStream_t s, int32_t* base, float* rec) {
     GenK<XT, GT> k;
@@ -309,17 +196,8 @@ hipError_t launch_gen_typed(const PrefillArgs& a, hipStream_t s, int32_t* base, 
     k.v = static_cast<const XT*>(a.v); k.z = static_cast<const XT*>(a.z);
     k.la = static_cast<const GT*>(a.la); k.beta = static_cast<const GT*>(a.beta);
     k.S0 = a.S0; k.S_out = a.S_out; k.out = static_cast<XT*>(a.out); k.rec = rec; k.snap = a.snap;
-    const int64_t slots = chunk_slots_bound(a.T, a.N);
-    const size_t lds = gen_lds_bytes(a.dk);
-    if (slots > 0 && a.T > 0) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gen_intra_kernel<XT, GT>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           static_cast<int>(lds));
-        if (e != hipSuccess) return e;
-        LaunchTimer timer("gen_intra", s);
-        hipLaunchKernelGGL((gen_intra_kernel<XT, GT>), dim3(static_cast<unsigned>(slots), a.H), dim3(256),
-                           lds, s, k);
-        e = hipGetLastError();
+    {
+        hipError_t e = launch_chunk_records(a, s, base, rec);
         if (e != hipSuccess) return e;
     }
     const int64_t blocks = static_cast<int64_t>(a.N) * a.H * (a.dv / 16);
