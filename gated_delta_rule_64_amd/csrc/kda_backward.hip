@@ -132,19 +132,53 @@ __device__ __forceinline__ void am_tiles(const float* sK, const float* sQ, const
             }
 }
 
-// T = (I + Diag(beta) A)^-1 by forward substitution, one row at a time
-__device__ __forceinline__ void t_solve(const float* sA, const float* sB, float* sT) {
-    const int tid = threadIdx.x;
-    for (int r = 0; r < 64; ++r) {
-        if (tid < 64) {
-            const int c = tid;
+// T = (I + Diag(beta) A)^-1 (unit lower triangular) by 16 x 16 blocks.
+// Wave w inverts diagonal block w by forward substitution inside the wave
+// (no workgroup barrier per row); then the blocks below the diagonal follow by
+// block distance d = 1, 2, 3:  T_ij = -T_ii sum_{k=j}^{i-1} (B A)_ik T_kj,
+// which is Y T = I (Y = I + B A) written for block (i, j).  sTmp holds
+// 3 x 16 x 16 floats.
+__device__ __forceinline__ void t_solve(const float* sA, const float* sB, float* sT, float* sTmp) {
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    // zero everything above the diagonal blocks' lower triangles first
+    for (int i = tid; i < 4096; i += 256) {
+        const int r = i >> 6, c = i & 63;
+        if (c > r || (r >> 4) != (c >> 4)) sT[i] = r == c ? 1.f : 0.f;
+    }
+    {
+        const int b0 = 16 * wave;
+        const int c = b0 + (lane & 15);
+        for (int rl = 0; rl < 16; ++rl) {
+            const int r = b0 + rl;
             float acc = r == c ? 1.f : 0.f;
             if (c < r) {
                 float sum = 0.f;
-                for (int s = c; s < r; ++s) sum += sA[r * 64 + s] * sT[s * 64 + c];
+                for (int s_ = c; s_ < r; ++s_) sum += sA[r * 64 + s_] * sT[s_ * 64 + c];
                 acc = -sB[r] * sum;
             }
-            sT[r * 64 + c] = acc;
+            if (lane < 16) sT[r * 64 + c] = acc;
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");  // row r is visible to the wave
+        }
+    }
+    __syncthreads();
+    for (int d = 1; d < 4; ++d) {
+        const int nb = 4 - d;  // blocks (j + d, j), j = 0 .. nb-1
+        // P_ij = sum_{k=j}^{i-1} (B A)_ik T_kj
+        for (int e = tid; e < nb * 256; e += 256) {
+            const int jb = e >> 8, rr = (e >> 4) & 15, cc = e & 15;
+            const int ib = jb + d, r = 16 * ib + rr, c = 16 * jb + cc;
+            float acc = 0.f;
+            for (int k = 16 * jb; k < 16 * ib; ++k) acc += sA[r * 64 + k] * sT[k * 64 + c];
+            sTmp[e] = sB[r] * acc;
+        }
+        __syncthreads();
+        // T_ij = -T_ii P_ij
+        for (int e = tid; e < nb * 256; e += 256) {
+            const int jb = e >> 8, rr = (e >> 4) & 15, cc = e & 15;
+            const int ib = jb + d, r = 16 * ib + rr, c = 16 * jb + cc;
+            float acc = 0.f;
+            for (int k = 0; k < 16; ++k) acc += sT[r * 64 + 16 * ib + k] * sTmp[(jb << 8) + k * 16 + cc];
+            sT[r * 64 + c] = -acc;
         }
         __syncthreads();
     }
@@ -156,7 +190,7 @@ __device__ __forceinline__ void t_solve(const float* sA, const float* sB, float*
 // them.
 template <int DK>
 constexpr size_t rec_lds_bytes() {
-    return (3 * 64 * (DK + 1) + 3 * 4096 + 64) * sizeof(float);  // K, Q, G; A, M, T; beta
+    return (3 * 64 * (DK + 1) + 3 * 4096 + 64 + 768) * sizeof(float);  // K, Q, G; A, M, T; beta; T's scratch
 }
 
 template <int DK, int DV, typename XT, typename GT>
@@ -170,6 +204,7 @@ __global__ __launch_bounds__(256) void chunk_records_kernel(BwdK<XT, GT> a) {
     float* sM = sA + 4096;
     float* sT = sM + 4096;
     float* sB = sT + 4096;
+    float* sTmp = sB + 64;
     const int slot = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
     if (slot >= a.base[a.N]) return;
     const int n = find_seq(a.base, a.N, slot);
@@ -203,7 +238,7 @@ __global__ __launch_bounds__(256) void chunk_records_kernel(BwdK<XT, GT> a) {
     if (tid < DK) rec[R.gam + tid] = expf(sG[63 * KP + tid]);
     am_tiles<DK>(sK, sQ, sG, sA, sM);
     __syncthreads();
-    t_solve(sA, sB, sT);
+    t_solve(sA, sB, sT, sTmp);
     // W = T (B e^G K),  U~ = T (B V)
     mm64<DK>(64, [&](int r, int s_) { return sT[r * 64 + s_]; },
              [&](int s_, int c) { return sB[s_] * expf(sG[s_ * KP + c]) * sK[s_ * KP + c]; },
@@ -222,11 +257,21 @@ __global__ __launch_bounds__(256) void chunk_records_kernel(BwdK<XT, GT> a) {
 }
 
 // ---- pass 2: the chain, chunks in reverse order ----
+template <int DK>
+constexpr size_t chain_lds_bytes() {
+    return (3 * 64 * (DK + 1) + DK * 16 + 2 * 64 * 16) * sizeof(float);  // K^, Q', W; dS; X, dO
+}
+
 template <int DK, int DV, typename XT, typename GT>
 __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdK<XT, GT> a) {
-    __shared__ float sD[DK * 16];  // dS, this block's 16 columns
-    __shared__ float sX[64 * 16];  // K^ dS
-    __shared__ float sO[64 * 16];  // dO
+    extern __shared__ float csm[];
+    constexpr int KP = DK + 1;
+    float* sKh = csm;              // [64][KP] this chunk's K^
+    float* sQp = sKh + 64 * KP;    // [64][KP] Q'
+    float* sW = sQp + 64 * KP;     // [64][KP] W
+    float* sD = sW + 64 * KP;      // [DK][16] dS, this block's 16 columns
+    float* sX = sD + DK * 16;      // [64][16] K^ dS
+    float* sO = sX + 64 * 16;      // [64][16] dO
     constexpr int NSL = DV / 16;
     const int sl = blockIdx.x % NSL;
     const int h = (blockIdx.x / NSL) % a.H;
@@ -241,12 +286,23 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdK<XT, GT> a) {
     const int64_t sb = seq_begin(a.cu, n), se = seq_finish(a.cu, n, a.T);
     const int nch = a.base[n + 1] - a.base[n];
     const int r = tid >> 2, c4 = (tid & 3) * 4;
+    auto stage = [&](float* dst, const float* src) {
+        for (int i = tid; i < 16 * DK; i += 256) {
+            const int rr = (4 * i) / DK, c = (4 * i) % DK;
+            const float4 v = *reinterpret_cast<const float4*>(src + rr * DK + c);
+            float* d = dst + rr * KP + c;
+            d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+        }
+    };
     for (int j = nch - 1; j >= 0; --j) {
         const int slot = a.base[n] + j;
         const float* rec = a.rec + (static_cast<int64_t>(slot) * a.H + h) * R.size;
         const int64_t t0 = sb + static_cast<int64_t>(j) * kChunk;
         const int L = static_cast<int>(min(static_cast<int64_t>(kChunk), se - t0));
-        __syncthreads();  // dS of this chunk's end is in sD
+        __syncthreads();  // dS of this chunk's end is in sD; the last chunk's operands are dead
+        stage(sKh, rec + R.Kh);
+        stage(sQp, rec + R.Qp);
+        stage(sW, rec + R.W);
         float* dse = a.dSe + (static_cast<int64_t>(slot) * a.H + h) * DK * DV;
         for (int e = tid; e < DK * 16; e += 256) dse[(e >> 4) * DV + 16 * sl + (e & 15)] = sD[e];
         // dO = dy * sigmoid(z) on the chunk's tokens, 0 on padding
@@ -260,23 +316,35 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdK<XT, GT> a) {
             }
             sO[r * 16 + c4 + i] = d;
         }
-        // X = K^ dS
+        __syncthreads();
+        // X = K^ dS (row r, columns c4 .. c4+3)
         float x[4] = {0.f, 0.f, 0.f, 0.f};
         for (int i = 0; i < DK; ++i) {
-            const float kh = rec[R.Kh + r * DK + i];
-#pragma unroll
-            for (int cc = 0; cc < 4; ++cc) x[cc] += kh * sD[i * 16 + c4 + cc];
+            const float kh = sKh[r * KP + i];
+            const float4 d4 = *reinterpret_cast<const float4*>(sD + i * 16 + c4);
+            x[0] += kh * d4.x; x[1] += kh * d4.y; x[2] += kh * d4.z; x[3] += kh * d4.w;
         }
 #pragma unroll
         for (int cc = 0; cc < 4; ++cc) sX[r * 16 + c4 + cc] = x[cc];
         __syncthreads();
-        // dS <- Q'^T dO + Diag(gamma) dS - W^T X
-        for (int e = tid; e < DK * 16; e += 256) {
-            const int i = e >> 4, c = e & 15;
-            float acc = rec[R.gam + i] * sD[e];
-            for (int rr = 0; rr < 64; ++rr)
-                acc += rec[R.Qp + rr * DK + i] * sO[rr * 16 + c] - rec[R.W + rr * DK + i] * sX[rr * 16 + c];
-            sD[e] = acc;  // (each element read and written by its own thread)
+        // dS <- Q'^T dO + Diag(gamma) dS - W^T X (channel i, columns j4 .. j4+3)
+        for (int e = tid; e < DK * 4; e += 256) {
+            const int i = e >> 2, j4 = (e & 3) * 4;
+            const float gm = rec[R.gam + i];
+            float acc[4];
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc) acc[cc] = gm * sD[i * 16 + j4 + cc];
+            for (int rr = 0; rr < 64; ++rr) {
+                const float qp = sQp[rr * KP + i], w = sW[rr * KP + i];
+                const float4 o4 = *reinterpret_cast<const float4*>(sO + rr * 16 + j4);
+                const float4 x4 = *reinterpret_cast<const float4*>(sX + rr * 16 + j4);
+                acc[0] += qp * o4.x - w * x4.x;
+                acc[1] += qp * o4.y - w * x4.y;
+                acc[2] += qp * o4.z - w * x4.z;
+                acc[3] += qp * o4.w - w * x4.w;
+            }
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc) sD[i * 16 + j4 + cc] = acc[cc];  // (read and written by its own thread)
         }
     }
     __syncthreads();
@@ -370,7 +438,7 @@ __global__ __launch_bounds__(256) void bwd_intra_kernel(BwdK<XT, GT> a) {
         am_tiles<DK>(sK, sQ, sG, sA, sM);
         __syncthreads();  // the queries are dead; T goes where they were
     }
-    t_solve(sA, sB, sT);
+    t_solve(sA, sB, sT, sP);  // (P's space is free until phase 5)
 
     // ---- 1. U = U~ - W S and O = Q' S + M U~; dO, dz
     mm64<DV>(S != nullptr ? DK : 0, [&](int r, int kk) { return rec[R.W + r * DK + kk]; },
@@ -655,10 +723,14 @@ hipError_t launch_bwd_typed(const BackwardArgs& b, const PrefillArgs& fa, hipStr
     }
     {
         const int64_t blocks = static_cast<int64_t>(f.N) * f.H * (DV / 16);
+        constexpr size_t clds = chain_lds_bytes<DK>();
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_chain_kernel<DK, DV, XT, GT>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(clds));
+        if (e != hipSuccess) return e;
         LaunchTimer timer("bwd_chain", s);
-        hipLaunchKernelGGL((bwd_chain_kernel<DK, DV, XT, GT>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
-                           k);
-        hipError_t e = hipGetLastError();
+        hipLaunchKernelGGL((bwd_chain_kernel<DK, DV, XT, GT>), dim3(static_cast<unsigned>(blocks)), dim3(256), clds,
+                           s, k);
+        e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     if (slots == 0 || f.T == 0) return hipSuccess;

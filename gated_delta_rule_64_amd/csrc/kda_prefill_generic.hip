@@ -113,11 +113,29 @@ struct GenK {
 // ---- phase 1, the records, is chunk_records_kernel (kda_backward.hip) ----
 
 // ---- phase 2: per (sequence, head, 16 state columns), chunks in order ----
+// One chunk's record matrix [64][dk] (16-byte aligned) into LDS rows of
+// dk + 1 floats (the padding keeps reads of one channel over many rows, or
+// of many rows at one channel, off a single bank).
+__device__ __forceinline__ void stage_rows(float* dst, const float* src, int dk) {
+    const int kp = dk + 1;
+    for (int i = threadIdx.x; i < 16 * dk; i += 256) {
+        const int r = (4 * i) / dk, c = (4 * i) % dk;
+        const float4 v = *reinterpret_cast<const float4*>(src + r * dk + c);
+        float* d = dst + r * kp + c;
+        d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+    }
+}
+
+size_t gen_state_lds_bytes(int dk) { return (2 * 64 * static_cast<size_t>(dk + 1) + 16 * dk + 64 * 16) * 4; }
+
 template <typename XT, typename GT>
 __global__ __launch_bounds__(256) void gen_state_kernel(GenK<XT, GT> a) {
-    __shared__ float sS[128 * 16];
-    __shared__ float sU[64 * 16];
-    const int dk = a.dk, dv = a.dv;
+    extern __shared__ float gsm[];
+    const int dk = a.dk, dv = a.dv, kp = dk + 1;
+    float* sWK = gsm;              // [64][kp]: W, then K^
+    float* sQp = sWK + 64 * kp;    // [64][kp]: Q'
+    float* sS = sQp + 64 * kp;     // [dk][16]: this block's 16 state columns
+    float* sU = sS + 16 * dk;      // [64][16]
     const int nsl = dv / 16;
     const int sl = blockIdx.x % nsl;
     const int h = (blockIdx.x / nsl) % a.H;
@@ -129,7 +147,6 @@ __global__ __launch_bounds__(256) void gen_state_kernel(GenK<XT, GT> a) {
         const int c = e >> 4, j = e & 15;
         sS[e] = a.S0 ? a.S0[sidx + c * dv + 16 * sl + j] : 0.f;
     }
-    __syncthreads();
     const int64_t sb = seq_begin(a.cu, n), se = seq_finish(a.cu, n, a.T);
     const int nch = a.base[n + 1] - a.base[n];
     const int r = tid >> 2, c4 = (tid & 3) * 4;
@@ -137,6 +154,11 @@ __global__ __launch_bounds__(256) void gen_state_kernel(GenK<XT, GT> a) {
         const float* rec = a.rec + (static_cast<int64_t>(a.base[n] + j) * a.H + h) * R.size;
         const int64_t t0 = sb + static_cast<int64_t>(j) * kChunk;
         const int L = static_cast<int>(min(static_cast<int64_t>(kChunk), se - t0));
+        __syncthreads();  // the last chunk's reads of sWK are done
+        stage_rows(sWK, rec + R.W, dk);
+        stage_rows(sQp, rec + R.Qp, dk);
+        __syncthreads();
+        // U = U~ - W S, O = Q' S + M U~ (row r, columns c4 .. c4+3)
         float u[4], o[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -144,13 +166,10 @@ __global__ __launch_bounds__(256) void gen_state_kernel(GenK<XT, GT> a) {
             o[i] = rec[R.Oi + r * dv + 16 * sl + c4 + i];
         }
         for (int c = 0; c < dk; ++c) {
-            const float w = rec[R.W + r * dk + c], qp = rec[R.Qp + r * dk + c];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float s = sS[c * 16 + c4 + i];
-                u[i] -= w * s;
-                o[i] += qp * s;
-            }
+            const float w = sWK[r * kp + c], qp = sQp[r * kp + c];
+            const float4 s4 = *reinterpret_cast<const float4*>(sS + c * 16 + c4);
+            u[0] -= w * s4.x; u[1] -= w * s4.y; u[2] -= w * s4.z; u[3] -= w * s4.w;
+            o[0] += qp * s4.x; o[1] += qp * s4.y; o[2] += qp * s4.z; o[3] += qp * s4.w;
         }
         if (r < L && a.out != nullptr) {  // (no output: a forward pass run for its records and states)
             const int64_t oidx = ((t0 + r) * a.H + h) * dv + 16 * sl + c4;
@@ -161,25 +180,37 @@ __global__ __launch_bounds__(256) void gen_state_kernel(GenK<XT, GT> a) {
                 st(a.out + oidx + i, y);
             }
         }
-        __syncthreads();
+        __syncthreads();  // every read of W and of S is done
 #pragma unroll
         for (int i = 0; i < 4; ++i) sU[r * 16 + c4 + i] = u[i];
+        stage_rows(sWK, rec + R.Kh, dk);
         __syncthreads();
-        // a full chunk that ends a snapshot interval: the state after it is the m-th snapshot
+        // S <- Diag(gamma) S + K^T U (channel c, columns j4 .. j4+3); a full
+        // chunk that ends a snapshot interval: the state after it is the m-th snapshot
         const int sc = a.snap.chunks;
         const bool snap = sc > 0 && (j + 1) % sc == 0 && L == kChunk;
         float* snap_out = snap ? a.snap.out + ((static_cast<int64_t>(a.snap.off[n]) + (j + 1) / sc - 1) * a.H + h) *
                                                   dk * dv
                                : nullptr;
-        for (int e = tid; e < dk * 16; e += 256) {
-            const int c = e >> 4, jj = e & 15;
-            float acc = rec[R.gam + c] * sS[e];
-            for (int rr = 0; rr < 64; ++rr) acc += rec[R.Kh + rr * dk + c] * sU[rr * 16 + jj];
-            sS[e] = acc;
-            if (snap) snap_out[c * dv + 16 * sl + jj] = acc;
+        for (int e = tid; e < dk * 4; e += 256) {
+            const int c = e >> 2, j4 = (e & 3) * 4;
+            const float gm = rec[R.gam + c];
+            float acc[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] = gm * sS[c * 16 + j4 + i];
+            for (int rr = 0; rr < 64; ++rr) {
+                const float kh = sWK[rr * kp + c];
+                const float4 u4 = *reinterpret_cast<const float4*>(sU + rr * 16 + j4);
+                acc[0] += kh * u4.x; acc[1] += kh * u4.y; acc[2] += kh * u4.z; acc[3] += kh * u4.w;
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                sS[c * 16 + j4 + i] = acc[i];  // (each element read and written by its own thread)
+                if (snap) snap_out[c * dv + 16 * sl + j4 + i] = acc[i];
+            }
         }
-        __syncthreads();
     }
+    __syncthreads();
     if (a.S_out) {
         for (int e = tid; e < dk * 16; e += 256) {
             const int c = e >> 4, jj = e & 15;
@@ -201,8 +232,12 @@ hipError_t launch_gen_typed(const PrefillArgs& a, hipStream_t s, int32_t* base, 
         if (e != hipSuccess) return e;
     }
     const int64_t blocks = static_cast<int64_t>(a.N) * a.H * (a.dv / 16);
+    const size_t lds = gen_state_lds_bytes(a.dk);
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gen_state_kernel<XT, GT>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (e != hipSuccess) return e;
     LaunchTimer timer("gen_state", s);
-    hipLaunchKernelGGL((gen_state_kernel<XT, GT>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, k);
+    hipLaunchKernelGGL((gen_state_kernel<XT, GT>), dim3(static_cast<unsigned>(blocks)), dim3(256), lds, s, k);
     return hipGetLastError();
 }
 
@@ -217,8 +252,12 @@ hipError_t launch_gen_state_typed(const PrefillArgs& a, hipStream_t s, int32_t* 
     k.la = static_cast<const GT*>(a.la); k.beta = static_cast<const GT*>(a.beta);
     k.S0 = a.S0; k.S_out = a.S_out; k.out = static_cast<XT*>(a.out); k.rec = rec; k.snap = a.snap;
     const int64_t blocks = static_cast<int64_t>(a.N) * a.H * (a.dv / 16);
+    const size_t lds = gen_state_lds_bytes(a.dk);
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gen_state_kernel<XT, GT>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (e != hipSuccess) return e;
     LaunchTimer timer("gen_state", s);
-    hipLaunchKernelGGL((gen_state_kernel<XT, GT>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, k);
+    hipLaunchKernelGGL((gen_state_kernel<XT, GT>), dim3(static_cast<unsigned>(blocks)), dim3(256), lds, s, k);
     return hipGetLastError();
 }
 
