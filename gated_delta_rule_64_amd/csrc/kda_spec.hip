@@ -66,7 +66,7 @@ __global__ __launch_bounds__(256) void spec_kernel(SpecK<XT> a) {
     __shared__ float s_k[NJ][DK], s_a[NJ][DK], s_v[NJ][DV], s_q[kMaxTok][DK], s_z[kMaxTok][DV];
     __shared__ float s_beta[NJ];
     __shared__ float s_ss[NJ][2][2];
-    __shared__ float s_qk[kMaxTok][2];
+    __shared__ float s_qk[kMaxTok];
 
     const int slot = a.idx ? a.idx[bb] : bb;
     if (slot < 0 || slot >= a.slots) {  // padding row: zero outputs, nothing else
@@ -197,26 +197,25 @@ __global__ __launch_bounds__(256) void spec_kernel(SpecK<XT> a) {
     if (J > NB) preprocess(NB);
     lds_barrier();
     // L2 norms, rounding to the input type (as kda_preprocess stores q^, k^),
-    // and q^.k^ of each new token
-    if (lower) {
-        for (int j = 0; j < J; ++j) {
-            const float ik = 1.f / sqrtf(s_ss[j][1][0] + s_ss[j][1][1] + kL2Eps);
-            float kk = 0.f;
-            if (act1) {
-                kk = round_to<XT>(s_k[j][c] * ik);
-                s_k[j][c] = kk;
+    // and q^.k^ of each new token: wave w takes tokens w, w + 4, ..., its
+    // lanes the channels (all four waves busy, the tokens independent)
+    for (int j = wave; j < J; j += 4) {
+        const float ik = __builtin_amdgcn_rsqf(s_ss[j][1][0] + s_ss[j][1][1] + kL2Eps);
+        const bool vt = j >= na;
+        const float iq = vt ? __builtin_amdgcn_rsqf(s_ss[j][0][0] + s_ss[j][0][1] + kL2Eps) : 0.f;
+        float qk = 0.f;
+        for (int ch = lane; ch < DK; ch += 64) {
+            const float kk = round_to<XT>(s_k[j][ch] * ik);
+            s_k[j][ch] = kk;
+            if (vt) {
+                const float qq = round_to<XT>(s_q[j - na][ch] * iq);
+                s_q[j - na][ch] = qq;
+                qk += qq * kk;
             }
-            if (j >= na) {
-                const float iq = 1.f / sqrtf(s_ss[j][0][0] + s_ss[j][0][1] + kL2Eps);
-                float qk = 0.f;
-                if (act1) {
-                    const float qq = round_to<XT>(s_q[j - na][c] * iq);
-                    s_q[j - na][c] = qq;
-                    qk = qq * kk;
-                }
-                qk = wave_sum(qk);
-                if (lane == 0) s_qk[j - na][wave] = qk;
-            }
+        }
+        if (vt) {
+            qk = wave_sum(qk);
+            if (lane == 0) s_qk[j - na] = qk;
         }
     }
     lds_barrier();
@@ -268,7 +267,7 @@ __global__ __launch_bounds__(256) void spec_kernel(SpecK<XT> a) {
             }
         }
         if (verify && rg == 0) {
-            const float qk = s_qk[t][0] + s_qk[t][1];
+            const float qk = s_qk[t];
             float o[4];
 #pragma unroll
             for (int cc = 0; cc < 4; ++cc) o[cc] = p[cc] + qk * d[cc];
