@@ -158,3 +158,20 @@ def test_decode_layer_b256_agrees_with_two_calls(K, oracle_mod):
     assert_close("y vs two calls", to_host64(out1), to_host64(out2), 2e-3)
     assert_close("state vs two calls", to_host64(st1), to_host64(st2), 2e-3)
     assert torch.equal(cs1, cs2)
+
+
+def test_debug_check_rejects_duplicate_state_indices(K, monkeypatch):
+    """With KDA_DEBUG_CHECK=1 the call copies state_indices to the host and
+    rejects two rows on one slot before launching anything."""
+    from gated_delta_rule_64_amd import _lib
+    B, H, dk, dv = 3, 2, 16, 16
+    inp = _decode_inputs(B, H, dk, dv, "f32")
+    st = torch.zeros((5, H, dk, dv), device="cuda")
+    cs = torch.zeros((5, 3, H * (2 * dk + dv)), device="cuda")
+    monkeypatch.setenv("KDA_DEBUG_CHECK", "1")
+    with pytest.raises(_lib.KdaError) as e:
+        _call(K, inp, cs, st, idx=to_dev(np.array([4, 1, 4], dtype=np.int32)))
+    assert "state_indices" in str(e.value)
+    out = _call(K, inp, cs, st, idx=to_dev(np.array([4, 1, -1], dtype=np.int32)))  # distinct: accepted
+    torch.cuda.synchronize()
+    assert torch.all(out[2] == 0)

@@ -143,3 +143,21 @@ def test_state_workgroup_shapes_agree(K, oracle_mod, monkeypatch, gate):
         assert_close(f"y (shape {shape})", to_host64(out), ref["y"], TOL["bf16"])
         assert_close(f"state (shape {shape})", to_host64(S), ref["S"], TOL["bf16"])
     assert torch.equal(res["2"][0], res["1"][0]) and torch.equal(res["2"][1], res["1"][1])
+
+
+def test_debug_check_rejects_bad_cu_seqlens(monkeypatch):
+    """With KDA_DEBUG_CHECK=1 the prefill copies cu_seqlens to the host and
+    rejects a map that does not end at T_tot, or that decreases, before any
+    launch.  (Both maps stay inside the 64 tokens, so even a launch would
+    read nothing out of range.)"""
+    from gated_delta_rule_64_amd import _lib, kda
+    c = synth.core(41, [30, 34], 2, 16, 16, x_dtype="f32")
+    args = [to_dev(c[n]) for n in ("q", "k", "v", "log_alpha", "beta")]
+    monkeypatch.setenv("KDA_DEBUG_CHECK", "1")
+    for bad, what in (([0, 30, 63], "expected T_tot"), ([0, 34, 30], "decreases")):
+        with pytest.raises(_lib.KdaError) as e:
+            kda.kda_prefill_chunked(*args, cu_seqlens=torch.tensor(bad, dtype=torch.int32, device="cuda"))
+        assert what in str(e.value)
+    out, _ = kda.kda_prefill_chunked(*args, cu_seqlens=to_dev(c["cu_seqlens"]))  # the right map passes
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
