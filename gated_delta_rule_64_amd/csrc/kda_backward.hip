@@ -47,17 +47,32 @@ struct BwdK {
     float *dq, *dk, *dv, *dla, *dbeta, *dz, *dS0;
 };
 
-// C = A B for 64 rows and N columns (N = 16 .. 128), K terms, by the 256
+// Threads of the per-chunk kernels.  Their LDS allows one workgroup per CU.
+// The record kernel runs 16 waves (measured: 1.58 -> 1.15 ms on the
+// 4096-token layer against 4 waves); the gradient kernel keeps 4 waves and
+// the larger register tiles they allow (measured: 5.5 ms against 6.9 ms).
+constexpr int kRecThreads = 1024;
+constexpr int kGradThreads = 256;
+
+// Per-thread tile of a 64-row, N-column result shared by NT threads:
+// TR rows x TC columns, TR * TC = 64 N / NT.
+template <int N, int NT>
+struct Tile64 {
+    static constexpr int OUT = 64 * N / NT;
+    static constexpr int TR = OUT >= 16 ? 4 : (OUT >= 8 ? 2 : 1);
+    static constexpr int TC = OUT / TR;
+    static constexpr int NCT = N / TC;  // column tiles
+    static_assert(TR * TC == OUT && OUT >= 1 && NCT * (64 / TR) == NT, "tile shape");
+};
+
+// C = A B for 64 rows and N columns (N = 16 .. 128), K terms, by the NT
 // threads of the workgroup: thread (tr, tc) owns rows TR tr .. + TR-1 and
 // columns TC tc .. + TC-1, so a step of k loads TR + TC operands for TR x TC
 // products.  A(r, k), B(k, c) read the operands; out(r, c, acc) takes each
 // result (every (r, c) once, by the same thread for equal N).
-template <int N, typename FA, typename FB, typename FO>
+template <int N, int NT, typename FA, typename FB, typename FO>
 __device__ __forceinline__ void mm64(int K, FA A, FB B, FO out) {
-    constexpr int TC = N >= 128 ? 8 : 4;
-    constexpr int NCT = N / TC;     // column tiles
-    constexpr int TR = NCT / 4;     // rows per thread: NCT * 64 / TR = 256 threads
-    static_assert(N % TC == 0 && TR >= 1 && (64 / TR) * NCT == 256, "tile shape");
+    constexpr int TC = Tile64<N, NT>::TC, TR = Tile64<N, NT>::TR, NCT = Tile64<N, NT>::NCT;
     const int tc = threadIdx.x % NCT, tr = threadIdx.x / NCT;
     float acc[TR][TC];
 #pragma unroll
@@ -87,23 +102,25 @@ __device__ __forceinline__ void mm64(int K, FA A, FB B, FO out) {
 // out, and is clamped to 0 so that nothing overflows
 __device__ __forceinline__ float decay(float x) { return __builtin_amdgcn_exp2f(fminf(x, 0.f) * kLog2e); }
 
-// A (strictly lower) and M (lower with diagonal) of a chunk, by 4 x 4 tiles
-// of (r, s) per thread; K, Q, G rows padded to DK + 1 floats in LDS.
-template <int DK>
+// A (strictly lower) and M (lower with diagonal) of a chunk, by AT x AT
+// tiles of (r, s) per thread; K, Q, G rows padded to DK + 1 floats in LDS.
+template <int DK, int NT>
 __device__ __forceinline__ void am_tiles(const float* sK, const float* sQ, const float* sG, float* sA, float* sM) {
     constexpr int KP = DK + 1;
+    constexpr int AT = NT == 256 ? 4 : 2, GD = 64 / AT;
+    static_assert(GD * GD == NT, "one tile per thread");
     const int tid = threadIdx.x;
-        const int r0 = 4 * (tid >> 4), s0 = 4 * (tid & 15);
-        float av[4][4], mv[4][4];
+        const int r0 = AT * (tid / GD), s0 = AT * (tid % GD);
+        float av[AT][AT], mv[AT][AT];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < AT; ++i)
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) av[i][jj] = mv[i][jj] = 0.f;
-        if (s0 <= r0 + 3) {  // the tile reaches the lower triangle
+            for (int jj = 0; jj < AT; ++jj) av[i][jj] = mv[i][jj] = 0.f;
+        if (s0 <= r0 + AT - 1) {  // the tile reaches the lower triangle
             for (int c = 0; c < DK; ++c) {
-                float kr[4], qr[4], gr[4], ks[4], gs[4];
+                float kr[AT], qr[AT], gr[AT], ks[AT], gs[AT];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
+                for (int i = 0; i < AT; ++i) {
                     kr[i] = sK[(r0 + i) * KP + c];
                     qr[i] = sQ[(r0 + i) * KP + c];
                     gr[i] = sG[(r0 + i) * KP + c];
@@ -111,9 +128,9 @@ __device__ __forceinline__ void am_tiles(const float* sK, const float* sQ, const
                     gs[i] = sG[(s0 + i) * KP + c];
                 }
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
+                for (int i = 0; i < AT; ++i)
 #pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) {
+                    for (int jj = 0; jj < AT; ++jj) {
                         // e^{G_r - G_s}; above the diagonal the exponent is
                         // clamped (those entries are dropped below)
                         const float ke = ks[jj] * decay(gr[i] - gs[jj]);
@@ -123,9 +140,9 @@ __device__ __forceinline__ void am_tiles(const float* sK, const float* sQ, const
             }
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < AT; ++i)
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
+            for (int jj = 0; jj < AT; ++jj) {
                 const int r = r0 + i, s_ = s0 + jj;
                 sA[r * 64 + s_] = s_ < r ? av[i][jj] : 0.f;
                 sM[r * 64 + s_] = s_ <= r ? mv[i][jj] : 0.f;
@@ -138,14 +155,15 @@ __device__ __forceinline__ void am_tiles(const float* sK, const float* sQ, const
 // block distance d = 1, 2, 3:  T_ij = -T_ii sum_{k=j}^{i-1} (B A)_ik T_kj,
 // which is Y T = I (Y = I + B A) written for block (i, j).  sTmp holds
 // 3 x 16 x 16 floats.
+template <int NT>
 __device__ __forceinline__ void t_solve(const float* sA, const float* sB, float* sT, float* sTmp) {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     // zero everything above the diagonal blocks' lower triangles first
-    for (int i = tid; i < 4096; i += 256) {
+    for (int i = tid; i < 4096; i += NT) {
         const int r = i >> 6, c = i & 63;
         if (c > r || (r >> 4) != (c >> 4)) sT[i] = r == c ? 1.f : 0.f;
     }
-    {
+    if (wave < 4) {
         const int b0 = 16 * wave;
         const int c = b0 + (lane & 15);
         for (int rl = 0; rl < 16; ++rl) {
@@ -164,7 +182,7 @@ __device__ __forceinline__ void t_solve(const float* sA, const float* sB, float*
     for (int d = 1; d < 4; ++d) {
         const int nb = 4 - d;  // blocks (j + d, j), j = 0 .. nb-1
         // P_ij = sum_{k=j}^{i-1} (B A)_ik T_kj
-        for (int e = tid; e < nb * 256; e += 256) {
+        for (int e = tid; e < nb * 256; e += NT) {
             const int jb = e >> 8, rr = (e >> 4) & 15, cc = e & 15;
             const int ib = jb + d, r = 16 * ib + rr, c = 16 * jb + cc;
             float acc = 0.f;
@@ -173,7 +191,7 @@ __device__ __forceinline__ void t_solve(const float* sA, const float* sB, float*
         }
         __syncthreads();
         // T_ij = -T_ii P_ij
-        for (int e = tid; e < nb * 256; e += 256) {
+        for (int e = tid; e < nb * 256; e += NT) {
             const int jb = e >> 8, rr = (e >> 4) & 15, cc = e & 15;
             const int ib = jb + d, r = 16 * ib + rr, c = 16 * jb + cc;
             float acc = 0.f;
@@ -194,7 +212,7 @@ constexpr size_t rec_lds_bytes() {
 }
 
 template <int DK, int DV, typename XT, typename GT>
-__global__ __launch_bounds__(256) void chunk_records_kernel(BwdK<XT, GT> a) {
+__global__ __launch_bounds__(kRecThreads) void chunk_records_kernel(BwdK<XT, GT> a) {
     extern __shared__ float smem[];
     constexpr int KP = DK + 1;
     float* sK = smem;
@@ -213,7 +231,7 @@ __global__ __launch_bounds__(256) void chunk_records_kernel(BwdK<XT, GT> a) {
     const GenRec R = gen_rec(DK, DV);
     float* rec = const_cast<float*>(a.rec) + (static_cast<int64_t>(slot) * a.H + h) * R.size;
     auto tok = [&](int r) { return (t0 + r) * a.H + h; };
-    for (int i = tid; i < 64 * DK; i += 256) {
+    for (int i = tid; i < 64 * DK; i += kRecThreads) {
         const int r = i / DK, c = i % DK;
         const bool in = r < L;
         sK[r * KP + c] = in ? ld(a.k + tok(r) * DK + c) : 0.f;
@@ -231,28 +249,28 @@ __global__ __launch_bounds__(256) void chunk_records_kernel(BwdK<XT, GT> a) {
     }
     __syncthreads();
     // K^ and gamma (G_last = G_63: padded rows add no decay)
-    for (int i = tid; i < 64 * DK; i += 256) {
+    for (int i = tid; i < 64 * DK; i += kRecThreads) {
         const int r = i / DK, c = i % DK;
         rec[R.Kh + i] = expf(sG[63 * KP + c] - sG[r * KP + c]) * sK[r * KP + c];
     }
     if (tid < DK) rec[R.gam + tid] = expf(sG[63 * KP + tid]);
-    am_tiles<DK>(sK, sQ, sG, sA, sM);
+    am_tiles<DK, kRecThreads>(sK, sQ, sG, sA, sM);
     __syncthreads();
-    t_solve(sA, sB, sT, sTmp);
+    t_solve<kRecThreads>(sA, sB, sT, sTmp);
     // W = T (B e^G K),  U~ = T (B V)
-    mm64<DK>(64, [&](int r, int s_) { return sT[r * 64 + s_]; },
+    mm64<DK, kRecThreads>(64, [&](int r, int s_) { return sT[r * 64 + s_]; },
              [&](int s_, int c) { return sB[s_] * expf(sG[s_ * KP + c]) * sK[s_ * KP + c]; },
              [&](int r, int c, float acc) { rec[R.W + r * DK + c] = acc; });
-    mm64<DV>(64, [&](int r, int s_) { return sT[r * 64 + s_]; },
+    mm64<DV, kRecThreads>(64, [&](int r, int s_) { return sT[r * 64 + s_]; },
              [&](int s_, int c) { return s_ < L ? sB[s_] * ld(a.v + tok(s_) * DV + c) : 0.f; },
              [&](int r, int c, float acc) { rec[R.U + r * DV + c] = acc; });
     __syncthreads();  // W and U~ are in the record
     // Q' = e^G Q - M W,  M U~
-    mm64<DK>(64, [&](int r, int s_) { return sM[r * 64 + s_]; }, [&](int s_, int c) { return rec[R.W + s_ * DK + c]; },
+    mm64<DK, kRecThreads>(64, [&](int r, int s_) { return sM[r * 64 + s_]; }, [&](int s_, int c) { return rec[R.W + s_ * DK + c]; },
              [&](int r, int c, float acc) {
                  rec[R.Qp + r * DK + c] = expf(sG[r * KP + c]) * sQ[r * KP + c] - acc;
              });
-    mm64<DV>(64, [&](int r, int s_) { return sM[r * 64 + s_]; }, [&](int s_, int c) { return rec[R.U + s_ * DV + c]; },
+    mm64<DV, kRecThreads>(64, [&](int r, int s_) { return sM[r * 64 + s_]; }, [&](int s_, int c) { return rec[R.U + s_ * DV + c]; },
              [&](int r, int c, float acc) { rec[R.Oi + r * DV + c] = acc; });
 }
 
@@ -363,7 +381,7 @@ constexpr size_t intra_lds_bytes() {
 
 // ---- pass 3: per (chunk, head), every input gradient ----
 template <int DK, int DV, typename XT, typename GT>
-__global__ __launch_bounds__(256) void bwd_intra_kernel(BwdK<XT, GT> a) {
+__global__ __launch_bounds__(kGradThreads) void bwd_intra_kernel(BwdK<XT, GT> a) {
     extern __shared__ float smem[];
     // K and G rows padded to DK + 1 floats: the tiles below read 4 rows at
     // one channel, which would otherwise land in one LDS bank
@@ -406,7 +424,7 @@ __global__ __launch_bounds__(256) void bwd_intra_kernel(BwdK<XT, GT> a) {
     auto tok = [&](int r) { return (t0 + r) * a.H + h; };
 
     // ---- 0. the forward's chunk quantities: G, A, M, T
-    for (int i = tid; i < 64 * DK; i += 256) {
+    for (int i = tid; i < 64 * DK; i += kGradThreads) {
         const int r = i / DK, c = i % DK;
         const bool in = r < L;
         sK[r * KP + c] = in ? ld(a.k + tok(r) * DK + c) : 0.f;
@@ -430,21 +448,21 @@ __global__ __launch_bounds__(256) void bwd_intra_kernel(BwdK<XT, GT> a) {
     // the queries sit, padded like K, in the space of T, dT, P until T is made
     {
         float* sQ = sT;
-        for (int i = tid; i < 64 * DK; i += 256) {
+        for (int i = tid; i < 64 * DK; i += kGradThreads) {
             const int r = i / DK, c = i % DK;
             sQ[r * KP + c] = r < L ? ld(a.q + tok(r) * DK + c) : 0.f;
         }
         __syncthreads();
-        am_tiles<DK>(sK, sQ, sG, sA, sM);
+        am_tiles<DK, kGradThreads>(sK, sQ, sG, sA, sM);
         __syncthreads();  // the queries are dead; T goes where they were
     }
-    t_solve(sA, sB, sT, sP);  // (P's space is free until phase 5)
+    t_solve<kGradThreads>(sA, sB, sT, sP);  // (P's space is free until phase 5)
 
     // ---- 1. U = U~ - W S and O = Q' S + M U~; dO, dz
-    mm64<DV>(S != nullptr ? DK : 0, [&](int r, int kk) { return rec[R.W + r * DK + kk]; },
+    mm64<DV, kGradThreads>(S != nullptr ? DK : 0, [&](int r, int kk) { return rec[R.W + r * DK + kk]; },
              [&](int kk, int c) { return S[kk * DV + c]; },
              [&](int r, int c, float acc) { gU[r * DV + c] = rec[R.U + r * DV + c] - acc; });
-    mm64<DV>(S != nullptr ? DK : 0, [&](int r, int kk) { return rec[R.Qp + r * DK + kk]; },
+    mm64<DV, kGradThreads>(S != nullptr ? DK : 0, [&](int r, int kk) { return rec[R.Qp + r * DK + kk]; },
              [&](int kk, int c) { return S[kk * DV + c]; },
              [&](int r, int c, float acc) {
                  const float o = rec[R.Oi + r * DV + c] + acc;
@@ -463,20 +481,20 @@ __global__ __launch_bounds__(256) void bwd_intra_kernel(BwdK<XT, GT> a) {
                  gdO[r * DV + c] = d;
              });
     // K_e = e^G K, for dT and d(B K_e) below
-    for (int e = tid; e < 64 * DK; e += 256) {
+    for (int e = tid; e < 64 * DK; e += kGradThreads) {
         const int r = e / DK, c = e % DK;
         gKe[e] = expf(sG[r * KP + c]) * sK[r * KP + c];
     }
     __syncthreads();
     // ---- 2. dU = M^T dO + K^ dS_end
-    mm64<DV>(64, [&](int r, int s_) { return sM[s_ * 64 + r]; }, [&](int s_, int c) { return gdO[s_ * DV + c]; },
+    mm64<DV, kGradThreads>(64, [&](int r, int s_) { return sM[s_ * 64 + r]; }, [&](int s_, int c) { return gdO[s_ * DV + c]; },
              [&](int r, int c, float acc) { gdU[r * DV + c] = acc; });
-    mm64<DV>(DK, [&](int r, int kk) { return rec[R.Kh + r * DK + kk]; }, [&](int kk, int c) { return dSe[kk * DV + c]; },
+    mm64<DV, kGradThreads>(DK, [&](int r, int kk) { return rec[R.Kh + r * DK + kk]; }, [&](int kk, int c) { return dSe[kk * DV + c]; },
              [&](int r, int c, float acc) { gdU[r * DV + c] += acc; });  // (same thread, same element)
     __syncthreads();
     // ---- 3. dQ_e = dO S^T, dK^ = U dS_end^T, dW = -dU S^T; the sums of dq,
     // dk, dG start here (Q_e = e^G Q, K^ = e^{G_last - G} K)
-    mm64<DK>(S != nullptr ? DV : 0, [&](int r, int col) { return gdO[r * DV + col]; },
+    mm64<DK, kGradThreads>(S != nullptr ? DV : 0, [&](int r, int col) { return gdO[r * DV + col]; },
              [&](int col, int i) { return S[i * DV + col]; },
              [&](int r, int c, float dqe) {
                  const float eg = expf(sG[r * KP + c]);
@@ -484,7 +502,7 @@ __global__ __launch_bounds__(256) void bwd_intra_kernel(BwdK<XT, GT> a) {
                  gq[r * DK + c] = eg * dqe;
                  gG[r * DK + c] = eg * qv * dqe;
              });
-    mm64<DK>(DV, [&](int r, int col) { return gU[r * DV + col]; }, [&](int col, int i) { return dSe[i * DV + col]; },
+    mm64<DK, kGradThreads>(DV, [&](int r, int col) { return gU[r * DV + col]; }, [&](int col, int i) { return dSe[i * DV + col]; },
              [&](int r, int c, float dkh) {
                  const int e = r * DK + c;
                  const float eh = expf(sG[63 * KP + c] - sG[r * KP + c]), kv = sK[r * KP + c];
@@ -492,7 +510,7 @@ __global__ __launch_bounds__(256) void bwd_intra_kernel(BwdK<XT, GT> a) {
                  gG[e] -= eh * kv * dkh;
                  atomicAdd(&sdGl[c], eh * kv * dkh);  // (G_last's share of K^)
              });
-    mm64<DK>(S != nullptr ? DV : 0, [&](int r, int col) { return gdU[r * DV + col]; },
+    mm64<DK, kGradThreads>(S != nullptr ? DV : 0, [&](int r, int col) { return gdU[r * DV + col]; },
              [&](int col, int i) { return S[i * DV + col]; },
              [&](int r, int c, float acc) { gdW[r * DK + c] = -acc; });
     if (tid < DK) {  // dgamma = diag(S^T dS_end); gamma = e^{G_last}
@@ -503,24 +521,24 @@ __global__ __launch_bounds__(256) void bwd_intra_kernel(BwdK<XT, GT> a) {
     }
     __syncthreads();
     // ---- 4. dM = dO U^T (into M's place); dT = dU (B V)^T + dW (B K_e)^T
-    mm64<64>(DV, [&](int r, int col) { return gdO[r * DV + col]; }, [&](int col, int s_) { return gU[s_ * DV + col]; },
+    mm64<64, kGradThreads>(DV, [&](int r, int col) { return gdO[r * DV + col]; }, [&](int col, int s_) { return gU[s_ * DV + col]; },
              [&](int r, int s_, float acc) { sM[r * 64 + s_] = s_ <= r ? acc : 0.f; });
-    mm64<64>(DV, [&](int r, int col) { return gdU[r * DV + col]; },
+    mm64<64, kGradThreads>(DV, [&](int r, int col) { return gdU[r * DV + col]; },
              [&](int col, int s_) { return s_ < L ? ld(a.v + tok(s_) * DV + col) : 0.f; },
              [&](int r, int s_, float acc) { sdT[r * 64 + s_] = acc; });
-    mm64<64>(DK, [&](int r, int kk) { return gdW[r * DK + kk]; }, [&](int kk, int s_) { return gKe[s_ * DK + kk]; },
+    mm64<64, kGradThreads>(DK, [&](int r, int kk) { return gdW[r * DK + kk]; }, [&](int kk, int s_) { return gKe[s_ * DK + kk]; },
              [&](int r, int s_, float acc) {  // (same thread, same element as just above)
                  sdT[r * 64 + s_] = s_ < r ? sB[s_] * (sdT[r * 64 + s_] + acc) : 0.f;
              });
     // d(B V) = T^T dU: dv, and beta's share
-    mm64<DV>(64, [&](int s_, int r) { return sT[r * 64 + s_]; }, [&](int r, int c) { return gdU[r * DV + c]; },
+    mm64<DV, kGradThreads>(64, [&](int s_, int r) { return sT[r * 64 + s_]; }, [&](int r, int c) { return gdU[r * DV + c]; },
              [&](int s_, int c, float acc) {
                  if (s_ >= L) return;
                  a.dv[tok(s_) * DV + c] = sB[s_] * acc;
                  atomicAdd(&sdB[s_], ld(a.v + tok(s_) * DV + c) * acc);
              });
     // d(B K_e) = T^T dW: k's, G's and beta's shares
-    mm64<DK>(64, [&](int s_, int r) { return sT[r * 64 + s_]; }, [&](int r, int c) { return gdW[r * DK + c]; },
+    mm64<DK, kGradThreads>(64, [&](int s_, int r) { return sT[r * 64 + s_]; }, [&](int r, int c) { return gdW[r * DK + c]; },
              [&](int s_, int c, float acc) {
                  const int e = s_ * DK + c;
                  const float ke = gKe[e];
@@ -530,10 +548,10 @@ __global__ __launch_bounds__(256) void bwd_intra_kernel(BwdK<XT, GT> a) {
              });
     __syncthreads();
     // ---- 5. dY = -T^T dT T^T; d(B A) = dY below the diagonal
-    mm64<64>(64, [&](int r, int s_) { return sdT[r * 64 + s_]; }, [&](int s_, int c) { return sT[c * 64 + s_]; },
+    mm64<64, kGradThreads>(64, [&](int r, int s_) { return sdT[r * 64 + s_]; }, [&](int s_, int c) { return sT[c * 64 + s_]; },
              [&](int r, int c, float acc) { sP[r * 64 + c] = acc; });
     __syncthreads();
-    mm64<64>(64, [&](int a_, int r) { return sT[r * 64 + a_]; }, [&](int r, int c) { return sP[r * 64 + c]; },
+    mm64<64, kGradThreads>(64, [&](int a_, int r) { return sT[r * 64 + a_]; }, [&](int r, int c) { return sP[r * 64 + c]; },
              [&](int a_, int c, float acc) { sdT[a_ * 64 + c] = c < a_ ? -acc : 0.f; });
     __syncthreads();
     if (tid < 64) {  // beta's share through B A: sum_s dY_rs A_rs
@@ -548,7 +566,7 @@ __global__ __launch_bounds__(256) void bwd_intra_kernel(BwdK<XT, GT> a) {
     // as column s of them:  dk_sc += sum_r w_rsc E with w = dA_rs k_rc + dM_rs q_rc,
     //   and dG_sc loses k_sc times that sum.
     {
-        constexpr int TC = DK >= 128 ? 8 : 4, NCT = DK / TC, TR = NCT / 4;
+        constexpr int TC = Tile64<DK, kGradThreads>::TC, NCT = Tile64<DK, kGradThreads>::NCT, TR = Tile64<DK, kGradThreads>::TR;
         const int C0 = TC * (tid % NCT), R0 = TR * (tid / NCT);
         float dkr[TR][TC], dqr[TR][TC], dks[TR][TC], gown[TR][TC];
 #pragma unroll
@@ -612,7 +630,7 @@ __global__ __launch_bounds__(256) void bwd_intra_kernel(BwdK<XT, GT> a) {
     }
     __syncthreads();  // every read of sK, sG, sdT, sM is done
     // ---- 7. dla = reverse cumsum of dG (G_last is G_63); outputs
-    for (int e = tid; e < 64 * DK; e += 256) {
+    for (int e = tid; e < 64 * DK; e += kGradThreads) {
         const int r = e / DK, c = e % DK;
         sG[r * KP + c] = gG[e] + (r == 63 ? sdGl[c] : 0.f);
         if (r < L) {
@@ -660,8 +678,8 @@ hipError_t launch_records_typed(const BwdK<XT, GT>& k, const PrefillArgs& f, hip
                                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e != hipSuccess) return e;
     LaunchTimer timer("chunk_records", s);
-    hipLaunchKernelGGL((chunk_records_kernel<DK, DV, XT, GT>), dim3(static_cast<unsigned>(slots), f.H), dim3(256), lds,
-                       s, k);
+    hipLaunchKernelGGL((chunk_records_kernel<DK, DV, XT, GT>), dim3(static_cast<unsigned>(slots), f.H),
+                       dim3(kRecThreads), lds, s, k);
     return hipGetLastError();
 }
 
@@ -739,7 +757,7 @@ hipError_t launch_bwd_typed(const BackwardArgs& b, const PrefillArgs& fa, hipStr
                                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e != hipSuccess) return e;
     LaunchTimer timer("bwd_intra", s);
-    hipLaunchKernelGGL((bwd_intra_kernel<DK, DV, XT, GT>), dim3(static_cast<unsigned>(slots), f.H), dim3(256), lds,
+    hipLaunchKernelGGL((bwd_intra_kernel<DK, DV, XT, GT>), dim3(static_cast<unsigned>(slots), f.H), dim3(kGradThreads), lds,
                        s, k);
     return hipGetLastError();
 }
