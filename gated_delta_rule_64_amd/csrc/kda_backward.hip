@@ -1,5 +1,6 @@
-// Gradients of the chunked recurrence (fp32 vector path, any supported head
-// size, fp32 or bf16 inputs).
+// Gradients of the chunked recurrence (fp32 arithmetic, any supported head
+// size, fp32 or bf16 inputs; the dense 64-row products on the fp32 matrix
+// cores, the rest on the vector ALUs).
 //
 // The forward of one chunk (the chunked form of the recurrence in
 // kda_prefill_common.h; decays G, A, M, T, W, U~, Q', K^, gamma as there,
@@ -65,36 +66,65 @@ struct Tile64 {
     static_assert(TR * TC == OUT && OUT >= 1 && NCT * (64 / TR) == NT, "tile shape");
 };
 
-// C = A B for 64 rows and N columns (N = 16 .. 128), K terms, by the NT
-// threads of the workgroup: thread (tr, tc) owns rows TR tr .. + TR-1 and
-// columns TC tc .. + TC-1, so a step of k loads TR + TC operands for TR x TC
-// products.  A(r, k), B(k, c) read the operands; out(r, c, acc) takes each
-// result (every (r, c) once, by the same thread for equal N).
+// Row stride (floats) of the 64 x 64 matrices in LDS (A, M, T, dT, P): the
+// products below read 16 rows at one column and 16 columns at one row, and
+// at a 64-float stride the first would land in one bank.
+constexpr int MS = 68;
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// C = A B for 64 rows and N columns (N = 16 .. 128), K terms (a multiple of
+// 16), by the NT threads of the workgroup, on the fp32 matrix cores
+// (v_mfma_f32_16x16x4_f32: lane (g, c) = (lane / 16, lane % 16) gives
+// A[c][g] and B[g][c] and holds D[4g + i][c]; fp32 products, fp32 sums).
+// The output's 16 x 16 tiles are dealt to the waves: a wave takes RPW row
+// tiles of CPW column tiles, so each operand it loads serves several
+// products.  Lane (g, c) takes the terms k0 + 4g .. k0 + 4g + 3 of every run
+// of 16, four consecutive elements of a row-major A row.  A(r, k), B(k, c)
+// read the operands; out(r, c, acc) takes each result once, and for equal N
+// the same thread always gets the same (r, c).
 template <int N, int NT, typename FA, typename FB, typename FO>
 __device__ __forceinline__ void mm64(int K, FA A, FB B, FO out) {
-    constexpr int TC = Tile64<N, NT>::TC, TR = Tile64<N, NT>::TR, NCT = Tile64<N, NT>::NCT;
-    const int tc = threadIdx.x % NCT, tr = threadIdx.x / NCT;
-    float acc[TR][TC];
+    constexpr int W = NT / 64, CT = N / 16;
+    constexpr int CPW = CT >= W ? CT / W : 1;    // column tiles per wave
+    constexpr int WPC = CT >= W ? 1 : W / CT;    // waves per column tile
+    constexpr int RPW = WPC >= 4 ? 1 : 4 / WPC;  // row tiles per wave
+    static_assert(CT * 16 == N && (CT >= W ? CT % W == 0 : W % CT == 0), "tile deal");
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
+    const int part = CT >= W ? 0 : wave % WPC;
+    if (part * RPW >= 4) return;  // (more waves than tiles; wave-uniform)
+    const int r0 = 16 * part * RPW, c0 = 16 * (CT >= W ? wave * CPW : wave / WPC);
+    f32x4 acc[RPW][CPW];
 #pragma unroll
-    for (int i = 0; i < TR; ++i)
+    for (int i = 0; i < RPW; ++i)
 #pragma unroll
-        for (int jj = 0; jj < TC; ++jj) acc[i][jj] = 0.f;
-#pragma unroll 4
-    for (int k = 0; k < K; ++k) {
-        float av[TR], bv[TC];
+        for (int jj = 0; jj < CPW; ++jj) acc[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+    for (int k0 = 0; k0 < K; k0 += 16) {
+        const int kk = k0 + 4 * g;
+        float av[RPW][4], bv[CPW][4];
 #pragma unroll
-        for (int i = 0; i < TR; ++i) av[i] = A(TR * tr + i, k);
+        for (int i = 0; i < RPW; ++i)
 #pragma unroll
-        for (int jj = 0; jj < TC; ++jj) bv[jj] = B(k, TC * tc + jj);
+            for (int j = 0; j < 4; ++j) av[i][j] = A(r0 + 16 * i + c, kk + j);
 #pragma unroll
-        for (int i = 0; i < TR; ++i)
+        for (int jj = 0; jj < CPW; ++jj)
 #pragma unroll
-            for (int jj = 0; jj < TC; ++jj) acc[i][jj] += av[i] * bv[jj];
+            for (int j = 0; j < 4; ++j) bv[jj][j] = B(kk + j, c0 + 16 * jj + c);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int i = 0; i < RPW; ++i)
+#pragma unroll
+                for (int jj = 0; jj < CPW; ++jj)
+                    acc[i][jj] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[i][j], bv[jj][j], acc[i][jj], 0, 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < TR; ++i)
+    for (int i = 0; i < RPW; ++i)
 #pragma unroll
-        for (int jj = 0; jj < TC; ++jj) out(TR * tr + i, TC * tc + jj, acc[i][jj]);
+        for (int jj = 0; jj < CPW; ++jj)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) out(r0 + 16 * i + 4 * g + e, c0 + 16 * jj + c, acc[i][jj][e]);
 }
 
 // e^x for x <= 0 (a decay between two tokens of a chunk) through the
@@ -144,8 +174,8 @@ __device__ __forceinline__ void am_tiles(const float* sK, const float* sQ, const
 #pragma unroll
             for (int jj = 0; jj < AT; ++jj) {
                 const int r = r0 + i, s_ = s0 + jj;
-                sA[r * 64 + s_] = s_ < r ? av[i][jj] : 0.f;
-                sM[r * 64 + s_] = s_ <= r ? mv[i][jj] : 0.f;
+                sA[r * MS + s_] = s_ < r ? av[i][jj] : 0.f;
+                sM[r * MS + s_] = s_ <= r ? mv[i][jj] : 0.f;
             }
 }
 
@@ -161,7 +191,7 @@ __device__ __forceinline__ void t_solve(const float* sA, const float* sB, float*
     // zero everything above the diagonal blocks' lower triangles first
     for (int i = tid; i < 4096; i += NT) {
         const int r = i >> 6, c = i & 63;
-        if (c > r || (r >> 4) != (c >> 4)) sT[i] = r == c ? 1.f : 0.f;
+        if (c > r || (r >> 4) != (c >> 4)) sT[r * MS + c] = r == c ? 1.f : 0.f;
     }
     if (wave < 4) {
         const int b0 = 16 * wave;
@@ -171,10 +201,10 @@ __device__ __forceinline__ void t_solve(const float* sA, const float* sB, float*
             float acc = r == c ? 1.f : 0.f;
             if (c < r) {
                 float sum = 0.f;
-                for (int s_ = c; s_ < r; ++s_) sum += sA[r * 64 + s_] * sT[s_ * 64 + c];
+                for (int s_ = c; s_ < r; ++s_) sum += sA[r * MS + s_] * sT[s_ * MS + c];
                 acc = -sB[r] * sum;
             }
-            if (lane < 16) sT[r * 64 + c] = acc;
+            if (lane < 16) sT[r * MS + c] = acc;
             __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");  // row r is visible to the wave
         }
     }
@@ -186,7 +216,7 @@ __device__ __forceinline__ void t_solve(const float* sA, const float* sB, float*
             const int jb = e >> 8, rr = (e >> 4) & 15, cc = e & 15;
             const int ib = jb + d, r = 16 * ib + rr, c = 16 * jb + cc;
             float acc = 0.f;
-            for (int k = 16 * jb; k < 16 * ib; ++k) acc += sA[r * 64 + k] * sT[k * 64 + c];
+            for (int k = 16 * jb; k < 16 * ib; ++k) acc += sA[r * MS + k] * sT[k * MS + c];
             sTmp[e] = sB[r] * acc;
         }
         __syncthreads();
@@ -195,8 +225,8 @@ __device__ __forceinline__ void t_solve(const float* sA, const float* sB, float*
             const int jb = e >> 8, rr = (e >> 4) & 15, cc = e & 15;
             const int ib = jb + d, r = 16 * ib + rr, c = 16 * jb + cc;
             float acc = 0.f;
-            for (int k = 0; k < 16; ++k) acc += sT[r * 64 + 16 * ib + k] * sTmp[(jb << 8) + k * 16 + cc];
-            sT[r * 64 + c] = -acc;
+            for (int k = 0; k < 16; ++k) acc += sT[r * MS + 16 * ib + k] * sTmp[(jb << 8) + k * 16 + cc];
+            sT[r * MS + c] = -acc;
         }
         __syncthreads();
     }
@@ -208,7 +238,7 @@ __device__ __forceinline__ void t_solve(const float* sA, const float* sB, float*
 // them.
 template <int DK>
 constexpr size_t rec_lds_bytes() {
-    return (3 * 64 * (DK + 1) + 3 * 4096 + 64 + 768) * sizeof(float);  // K, Q, G; A, M, T; beta; T's scratch
+    return (3 * 64 * (DK + 1) + 3 * 64 * MS + 64 + 768) * sizeof(float);  // K, Q, G; A, M, T; beta; T's scratch
 }
 
 template <int DK, int DV, typename XT, typename GT>
@@ -219,9 +249,9 @@ __global__ __launch_bounds__(kRecThreads) void chunk_records_kernel(BwdK<XT, GT>
     float* sQ = sK + 64 * KP;
     float* sG = sQ + 64 * KP;
     float* sA = sG + 64 * KP;
-    float* sM = sA + 4096;
-    float* sT = sM + 4096;
-    float* sB = sT + 4096;
+    float* sM = sA + 64 * MS;
+    float* sT = sM + 64 * MS;
+    float* sB = sT + 64 * MS;
     float* sTmp = sB + 64;
     const int slot = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
     if (slot >= a.base[a.N]) return;
@@ -258,19 +288,19 @@ __global__ __launch_bounds__(kRecThreads) void chunk_records_kernel(BwdK<XT, GT>
     __syncthreads();
     t_solve<kRecThreads>(sA, sB, sT, sTmp);
     // W = T (B e^G K),  U~ = T (B V)
-    mm64<DK, kRecThreads>(64, [&](int r, int s_) { return sT[r * 64 + s_]; },
+    mm64<DK, kRecThreads>(64, [&](int r, int s_) { return sT[r * MS + s_]; },
              [&](int s_, int c) { return sB[s_] * expf(sG[s_ * KP + c]) * sK[s_ * KP + c]; },
              [&](int r, int c, float acc) { rec[R.W + r * DK + c] = acc; });
-    mm64<DV, kRecThreads>(64, [&](int r, int s_) { return sT[r * 64 + s_]; },
+    mm64<DV, kRecThreads>(64, [&](int r, int s_) { return sT[r * MS + s_]; },
              [&](int s_, int c) { return s_ < L ? sB[s_] * ld(a.v + tok(s_) * DV + c) : 0.f; },
              [&](int r, int c, float acc) { rec[R.U + r * DV + c] = acc; });
     __syncthreads();  // W and U~ are in the record
     // Q' = e^G Q - M W,  M U~
-    mm64<DK, kRecThreads>(64, [&](int r, int s_) { return sM[r * 64 + s_]; }, [&](int s_, int c) { return rec[R.W + s_ * DK + c]; },
+    mm64<DK, kRecThreads>(64, [&](int r, int s_) { return sM[r * MS + s_]; }, [&](int s_, int c) { return rec[R.W + s_ * DK + c]; },
              [&](int r, int c, float acc) {
                  rec[R.Qp + r * DK + c] = expf(sG[r * KP + c]) * sQ[r * KP + c] - acc;
              });
-    mm64<DV, kRecThreads>(64, [&](int r, int s_) { return sM[r * 64 + s_]; }, [&](int s_, int c) { return rec[R.U + s_ * DV + c]; },
+    mm64<DV, kRecThreads>(64, [&](int r, int s_) { return sM[r * MS + s_]; }, [&](int s_, int c) { return rec[R.U + s_ * DV + c]; },
              [&](int r, int c, float acc) { rec[R.Oi + r * DV + c] = acc; });
 }
 
@@ -375,8 +405,8 @@ constexpr size_t scratch_floats(int dk, int dv) { return 3 * 64 * static_cast<si
 
 template <int DK>
 constexpr size_t intra_lds_bytes() {
-    // K, G [64][DK + 1]; A, M, T, dT, P [64][64]; beta, dbeta [64]; dG_last [DK]
-    return (2 * 64 * (DK + 1) + 5 * 4096 + 2 * 64 + DK) * sizeof(float);
+    // K, G [64][DK + 1]; A, M, T, dT, P [64][MS]; beta, dbeta [64]; dG_last [DK]
+    return (2 * 64 * (DK + 1) + 5 * 64 * MS + 2 * 64 + DK) * sizeof(float);
 }
 
 // ---- pass 3: per (chunk, head), every input gradient ----
@@ -388,12 +418,12 @@ __global__ __launch_bounds__(kGradThreads) void bwd_intra_kernel(BwdK<XT, GT> a)
     constexpr int KP = DK + 1;
     float* sK = smem;              // [64][KP] keys
     float* sG = sK + 64 * KP;      // [64][KP] decay cumsums; at the end dG
-    float* sA = sG + 64 * KP;      // [64][64] A
-    float* sM = sA + 4096;         // [64][64] M, later dM
-    float* sT = sM + 4096;         // [64][64] T
-    float* sdT = sT + 4096;        // [64][64] dT, later dY
-    float* sP = sdT + 4096;        // [64][64] dT T^T
-    float* sB = sP + 4096;         // [64] beta
+    float* sA = sG + 64 * KP;      // [64][MS] A
+    float* sM = sA + 64 * MS;      // [64][MS] M, later dM
+    float* sT = sM + 64 * MS;      // [64][MS] T
+    float* sdT = sT + 64 * MS;     // [64][MS] dT, later dY
+    float* sP = sdT + 64 * MS;     // [64][MS] dT T^T
+    float* sB = sP + 64 * MS;         // [64] beta
     float* sdB = sB + 64;          // [64] dbeta
     float* sdGl = sdB + 64;        // [DK] gradient of G_last
 
@@ -415,8 +445,9 @@ __global__ __launch_bounds__(kGradThreads) void bwd_intra_kernel(BwdK<XT, GT> a)
     float* gdO = gU + 64 * DV;
     float* gdU = gdO + 64 * DV;
     float* gdW = gdU + 64 * DV;
-    // running sums of dq, dk, dG: element e = (row, channel) is only ever
-    // touched by thread e % 256, so plain read-modify-writes suffice
+    // running sums of dq, dk, dG: between two barriers, element (row,
+    // channel) is touched by one thread only (every product of width DK
+    // gives it to the same thread), so plain read-modify-writes suffice
     float* gq = gdW + 64 * DK;
     float* gk = gq + 64 * DK;
     float* gG = gk + 64 * DK;
@@ -487,7 +518,7 @@ __global__ __launch_bounds__(kGradThreads) void bwd_intra_kernel(BwdK<XT, GT> a)
     }
     __syncthreads();
     // ---- 2. dU = M^T dO + K^ dS_end
-    mm64<DV, kGradThreads>(64, [&](int r, int s_) { return sM[s_ * 64 + r]; }, [&](int s_, int c) { return gdO[s_ * DV + c]; },
+    mm64<DV, kGradThreads>(64, [&](int r, int s_) { return sM[s_ * MS + r]; }, [&](int s_, int c) { return gdO[s_ * DV + c]; },
              [&](int r, int c, float acc) { gdU[r * DV + c] = acc; });
     mm64<DV, kGradThreads>(DK, [&](int r, int kk) { return rec[R.Kh + r * DK + kk]; }, [&](int kk, int c) { return dSe[kk * DV + c]; },
              [&](int r, int c, float acc) { gdU[r * DV + c] += acc; });  // (same thread, same element)
@@ -522,23 +553,23 @@ __global__ __launch_bounds__(kGradThreads) void bwd_intra_kernel(BwdK<XT, GT> a)
     __syncthreads();
     // ---- 4. dM = dO U^T (into M's place); dT = dU (B V)^T + dW (B K_e)^T
     mm64<64, kGradThreads>(DV, [&](int r, int col) { return gdO[r * DV + col]; }, [&](int col, int s_) { return gU[s_ * DV + col]; },
-             [&](int r, int s_, float acc) { sM[r * 64 + s_] = s_ <= r ? acc : 0.f; });
+             [&](int r, int s_, float acc) { sM[r * MS + s_] = s_ <= r ? acc : 0.f; });
     mm64<64, kGradThreads>(DV, [&](int r, int col) { return gdU[r * DV + col]; },
              [&](int col, int s_) { return s_ < L ? ld(a.v + tok(s_) * DV + col) : 0.f; },
-             [&](int r, int s_, float acc) { sdT[r * 64 + s_] = acc; });
+             [&](int r, int s_, float acc) { sdT[r * MS + s_] = acc; });
     mm64<64, kGradThreads>(DK, [&](int r, int kk) { return gdW[r * DK + kk]; }, [&](int kk, int s_) { return gKe[s_ * DK + kk]; },
              [&](int r, int s_, float acc) {  // (same thread, same element as just above)
-                 sdT[r * 64 + s_] = s_ < r ? sB[s_] * (sdT[r * 64 + s_] + acc) : 0.f;
+                 sdT[r * MS + s_] = s_ < r ? sB[s_] * (sdT[r * MS + s_] + acc) : 0.f;
              });
     // d(B V) = T^T dU: dv, and beta's share
-    mm64<DV, kGradThreads>(64, [&](int s_, int r) { return sT[r * 64 + s_]; }, [&](int r, int c) { return gdU[r * DV + c]; },
+    mm64<DV, kGradThreads>(64, [&](int s_, int r) { return sT[r * MS + s_]; }, [&](int r, int c) { return gdU[r * DV + c]; },
              [&](int s_, int c, float acc) {
                  if (s_ >= L) return;
                  a.dv[tok(s_) * DV + c] = sB[s_] * acc;
                  atomicAdd(&sdB[s_], ld(a.v + tok(s_) * DV + c) * acc);
              });
     // d(B K_e) = T^T dW: k's, G's and beta's shares
-    mm64<DK, kGradThreads>(64, [&](int s_, int r) { return sT[r * 64 + s_]; }, [&](int r, int c) { return gdW[r * DK + c]; },
+    mm64<DK, kGradThreads>(64, [&](int s_, int r) { return sT[r * MS + s_]; }, [&](int r, int c) { return gdW[r * DK + c]; },
              [&](int s_, int c, float acc) {
                  const int e = s_ * DK + c;
                  const float ke = gKe[e];
@@ -548,19 +579,19 @@ __global__ __launch_bounds__(kGradThreads) void bwd_intra_kernel(BwdK<XT, GT> a)
              });
     __syncthreads();
     // ---- 5. dY = -T^T dT T^T; d(B A) = dY below the diagonal
-    mm64<64, kGradThreads>(64, [&](int r, int s_) { return sdT[r * 64 + s_]; }, [&](int s_, int c) { return sT[c * 64 + s_]; },
-             [&](int r, int c, float acc) { sP[r * 64 + c] = acc; });
+    mm64<64, kGradThreads>(64, [&](int r, int s_) { return sdT[r * MS + s_]; }, [&](int s_, int c) { return sT[c * MS + s_]; },
+             [&](int r, int c, float acc) { sP[r * MS + c] = acc; });
     __syncthreads();
-    mm64<64, kGradThreads>(64, [&](int a_, int r) { return sT[r * 64 + a_]; }, [&](int r, int c) { return sP[r * 64 + c]; },
-             [&](int a_, int c, float acc) { sdT[a_ * 64 + c] = c < a_ ? -acc : 0.f; });
+    mm64<64, kGradThreads>(64, [&](int a_, int r) { return sT[r * MS + a_]; }, [&](int r, int c) { return sP[r * MS + c]; },
+             [&](int a_, int c, float acc) { sdT[a_ * MS + c] = c < a_ ? -acc : 0.f; });
     __syncthreads();
     if (tid < 64) {  // beta's share through B A: sum_s dY_rs A_rs
         float acc = 0.f;
-        for (int s_ = 0; s_ < tid; ++s_) acc += sdT[tid * 64 + s_] * sA[tid * 64 + s_];
+        for (int s_ = 0; s_ < tid; ++s_) acc += sdT[tid * MS + s_] * sA[tid * MS + s_];
         atomicAdd(&sdB[tid], acc);
     }
     // ---- 6. through A (dA = B dY) and M (dM), with E_rsc = e^{G_rc - G_sc}.
-    // Thread tiles as in mm64<DK>: rows R0 .. R0+TR-1, channels C0 .. C0+TC-1.
+    // Thread tiles of Tile64<DK>: rows R0 .. R0+TR-1, channels C0 .. C0+TC-1.
     // As row r of A and M:  dk_rc += sum_s dA_rs k_sc E,  dq_rc += sum_s dM_rs k_sc E,
     //   and dG_rc gains k_rc (the first sum) + q_rc (the second);
     // as column s of them:  dk_sc += sum_r w_rsc E with w = dA_rs k_rc + dM_rs q_rc,
@@ -580,8 +611,8 @@ __global__ __launch_bounds__(kGradThreads) void bwd_intra_kernel(BwdK<XT, GT> a)
             float da[TR], dm[TR], ks[TC], gs[TC];
 #pragma unroll
             for (int i = 0; i < TR; ++i) {
-                da[i] = sB[R0 + i] * sdT[(R0 + i) * 64 + s_];  // (zero unless s < r)
-                dm[i] = sM[(R0 + i) * 64 + s_];                // (zero unless s <= r)
+                da[i] = sB[R0 + i] * sdT[(R0 + i) * MS + s_];  // (zero unless s < r)
+                dm[i] = sM[(R0 + i) * MS + s_];                // (zero unless s <= r)
             }
 #pragma unroll
             for (int jj = 0; jj < TC; ++jj) {
@@ -601,8 +632,8 @@ __global__ __launch_bounds__(kGradThreads) void bwd_intra_kernel(BwdK<XT, GT> a)
             float da[TR], dm[TR], kr[TC], qr[TC], gr[TC];
 #pragma unroll
             for (int i = 0; i < TR; ++i) {
-                da[i] = sB[r2] * sdT[r2 * 64 + R0 + i];
-                dm[i] = sM[r2 * 64 + R0 + i];
+                da[i] = sB[r2] * sdT[r2 * MS + R0 + i];
+                dm[i] = sM[r2 * MS + R0 + i];
             }
 #pragma unroll
             for (int jj = 0; jj < TC; ++jj) {
