@@ -305,99 +305,165 @@ __global__ __launch_bounds__(kRecThreads) void chunk_records_kernel(BwdK<XT, GT>
 }
 
 // ---- pass 2: the chain, chunks in reverse order ----
-template <int DK>
-constexpr size_t chain_lds_bytes() {
-    return (3 * 64 * (DK + 1) + DK * 16 + 2 * 64 * 16) * sizeof(float);  // K^, Q', W; dS; X, dO
-}
+// Four waves on the fp32 matrix cores, laid out as the forward state pass:
+// per chunk, wave w makes token rows 16w .. 16w + 15 of X = K^ dS and of
+// dO = dy * sigmoid(z); then the waves that own rows of dS update them,
+//     dS <- Diag(gamma) dS + Q'^T dO - W^T X.
+// dS (the B operand of K^ dS) and X, dO (of the update) are shared through
+// LDS; a wave keeps its rows of dS as matrix-core accumulators, and reloads
+// each operand it takes from the record, for the next chunk, as soon as the
+// products that use it are issued.
+constexpr int kCS = 20;  // LDS row stride of dS, X, dO (16 columns): rows 4g + jj of lanes (g, c) hit distinct banks
 
 template <int DK, int DV, typename XT, typename GT>
 __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdK<XT, GT> a) {
-    extern __shared__ float csm[];
-    constexpr int KP = DK + 1;
-    float* sKh = csm;              // [64][KP] this chunk's K^
-    float* sQp = sKh + 64 * KP;    // [64][KP] Q'
-    float* sW = sQp + 64 * KP;     // [64][KP] W
-    float* sD = sW + 64 * KP;      // [DK][16] dS, this block's 16 columns
-    float* sX = sD + DK * 16;      // [64][16] K^ dS
-    float* sO = sX + 64 * 16;      // [64][16] dO
+    constexpr int KB = DK / 16, ST = DK / 16, SPW = ST >= 4 ? ST / 4 : 1;
+    __shared__ float sD[DK * kCS];
+    __shared__ float sX[64 * kCS];
+    __shared__ float sO[64 * kCS];
     constexpr int NSL = DV / 16;
-    const int sl = blockIdx.x % NSL;
-    const int h = (blockIdx.x / NSL) % a.H;
-    const int n = blockIdx.x / (NSL * a.H);
-    const int tid = threadIdx.x;
+    const SliceBlock sbk = slice_block(blockIdx.x, NSL);
+    if (sbk.grp >= static_cast<int64_t>(a.N) * a.H) return;
+    const int sl = sbk.sl, h = static_cast<int>(sbk.grp % a.H), n = static_cast<int>(sbk.grp / a.H);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, c = lane & 15;
+    const bool owner = wave * SPW < ST;  // (below d = 64 some waves own no rows of dS)
+    auto i0 = [&](int t) { return owner ? 16 * (wave * SPW + t) : 0; };
     const GenRec R = gen_rec(DK, DV);
     const int64_t sidx = (static_cast<int64_t>(n) * a.H + h) * DK * DV;
-    for (int e = tid; e < DK * 16; e += 256) {
-        const int i = e >> 4, c = e & 15;
-        sD[e] = a.dSf ? a.dSf[sidx + i * DV + 16 * sl + c] : 0.f;
-    }
+    const int col = 16 * sl + c;
+    const bool has_z = a.z != nullptr;
+    const XT* zp = has_z ? a.z : a.v;  // (same [T][H][dv] layout; read but unused without a gate)
     const int64_t sb = seq_begin(a.cu, n), se = seq_finish(a.cu, n, a.T);
     const int nch = a.base[n + 1] - a.base[n];
-    const int r = tid >> 2, c4 = (tid & 3) * 4;
-    auto stage = [&](float* dst, const float* src) {
-        for (int i = tid; i < 16 * DK; i += 256) {
-            const int rr = (4 * i) / DK, c = (4 * i) % DK;
-            const float4 v = *reinterpret_cast<const float4*>(src + rr * DK + c);
-            float* d = dst + rr * KP + c;
-            d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+    auto rec_of = [&](int j) { return a.rec + (static_cast<int64_t>(a.base[n] + j) * a.H + h) * R.size; };
+    auto len_of = [&](int j) {
+        return static_cast<int>(min(static_cast<int64_t>(kChunk), se - (sb + static_cast<int64_t>(j) * kChunk)));
+    };
+    // a wave's operands of one chunk
+    f32x4 kA[KB];          // K^[16 wave + c][16 kb + 4g .. + 3]
+    float qT[SPW][4][4];   // Q'[16 kb + 4g + jj][i0 + c]
+    float wT[SPW][4][4];   // -W[16 kb + 4g + jj][i0 + c]
+    float gam[SPW][4];     // gamma[i0 + 4g + e]
+    float dyv[4], zv[4];   // dy, z at token 16 wave + 4g + e, column col
+    auto load_k = [&](const float* rec) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+            kA[kb] = *reinterpret_cast<const f32x4*>(rec + R.Kh + (16 * wave + c) * DK + 16 * kb + 4 * g);
+    };
+    auto load_io = [&](int j) {
+        const int L = len_of(j);
+        const int64_t t0 = sb + static_cast<int64_t>(j) * kChunk;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int64_t oidx = ((t0 + min(16 * wave + 4 * g + e, L - 1)) * a.H + h) * DV + col;
+            dyv[e] = ld(a.dy + oidx);
+            zv[e] = ld(zp + oidx);
         }
     };
-    for (int j = nch - 1; j >= 0; --j) {
-        const int slot = a.base[n] + j;
-        const float* rec = a.rec + (static_cast<int64_t>(slot) * a.H + h) * R.size;
-        const int64_t t0 = sb + static_cast<int64_t>(j) * kChunk;
-        const int L = static_cast<int>(min(static_cast<int64_t>(kChunk), se - t0));
-        __syncthreads();  // dS of this chunk's end is in sD; the last chunk's operands are dead
-        stage(sKh, rec + R.Kh);
-        stage(sQp, rec + R.Qp);
-        stage(sW, rec + R.W);
-        float* dse = a.dSe + (static_cast<int64_t>(slot) * a.H + h) * DK * DV;
-        for (int e = tid; e < DK * 16; e += 256) dse[(e >> 4) * DV + 16 * sl + (e & 15)] = sD[e];
-        // dO = dy * sigmoid(z) on the chunk's tokens, 0 on padding
+    auto load_t = [&](const float* rec) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float d = 0.f;
-            if (r < L) {
-                const int64_t oidx = ((t0 + r) * a.H + h) * DV + 16 * sl + c4 + i;
-                d = ld(a.dy + oidx);
-                if (a.z) d *= sigmoid(ld(a.z + oidx));
-            }
-            sO[r * 16 + c4 + i] = d;
+        for (int t = 0; t < SPW; ++t) {
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int64_t off = (16 * kb + 4 * g + jj) * DK + i0(t) + c;
+                    qT[t][kb][jj] = rec[R.Qp + off];
+                    wT[t][kb][jj] = -rec[R.W + off];
+                }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) gam[t][e] = rec[R.gam + i0(t) + 4 * g + e];
         }
-        __syncthreads();
-        // X = K^ dS (row r, columns c4 .. c4+3)
-        float x[4] = {0.f, 0.f, 0.f, 0.f};
-        for (int i = 0; i < DK; ++i) {
-            const float kh = sKh[r * KP + i];
-            const float4 d4 = *reinterpret_cast<const float4*>(sD + i * 16 + c4);
-            x[0] += kh * d4.x; x[1] += kh * d4.y; x[2] += kh * d4.z; x[3] += kh * d4.w;
+    };
+    // this wave's rows of dS: tile t holds rows i0(t) + 4g + e, column col
+    f32x4 D[SPW];
+#pragma unroll
+    for (int t = 0; t < SPW; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int row = i0(t) + 4 * g + e;
+            D[t][e] = a.dSf && owner ? a.dSf[sidx + row * DV + col] : 0.f;
+            if (owner) sD[row * kCS + c] = D[t][e];
         }
-#pragma unroll
-        for (int cc = 0; cc < 4; ++cc) sX[r * 16 + c4 + cc] = x[cc];
-        __syncthreads();
-        // dS <- Q'^T dO + Diag(gamma) dS - W^T X (channel i, columns j4 .. j4+3)
-        for (int e = tid; e < DK * 4; e += 256) {
-            const int i = e >> 2, j4 = (e & 3) * 4;
-            const float gm = rec[R.gam + i];
-            float acc[4];
-#pragma unroll
-            for (int cc = 0; cc < 4; ++cc) acc[cc] = gm * sD[i * 16 + j4 + cc];
-            for (int rr = 0; rr < 64; ++rr) {
-                const float qp = sQp[rr * KP + i], w = sW[rr * KP + i];
-                const float4 o4 = *reinterpret_cast<const float4*>(sO + rr * 16 + j4);
-                const float4 x4 = *reinterpret_cast<const float4*>(sX + rr * 16 + j4);
-                acc[0] += qp * o4.x - w * x4.x;
-                acc[1] += qp * o4.y - w * x4.y;
-                acc[2] += qp * o4.z - w * x4.z;
-                acc[3] += qp * o4.w - w * x4.w;
-            }
-#pragma unroll
-            for (int cc = 0; cc < 4; ++cc) sD[i * 16 + j4 + cc] = acc[cc];  // (read and written by its own thread)
-        }
+    if (nch > 0) {
+        const float* rec = rec_of(nch - 1);
+        load_k(rec);
+        load_io(nch - 1);
+        load_t(rec);
     }
     __syncthreads();
-    if (a.dS0) {
-        for (int e = tid; e < DK * 16; e += 256) a.dS0[sidx + (e >> 4) * DV + 16 * sl + (e & 15)] = sD[e];
+    for (int j = nch - 1; j >= 0; --j) {
+        const int slot = a.base[n] + j;
+        const int L = len_of(j);
+        const int jn = max(j - 1, 0);  // (the last step reloads its own chunk, unused)
+        const float* rec_next = rec_of(jn);
+        // dS at this chunk's end
+        if (owner) {
+            float* dse = a.dSe + (static_cast<int64_t>(slot) * a.H + h) * DK * DV;
+#pragma unroll
+            for (int t = 0; t < SPW; ++t)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) dse[(i0(t) + 4 * g + e) * DV + col] = D[t][e];
+        }
+        // dO = dy * sigmoid(z) on the chunk's tokens, 0 on padding
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = 16 * wave + 4 * g + e;
+            const float d = has_z ? dyv[e] * sigmoid(zv[e]) : dyv[e];
+            sO[r * kCS + c] = r < L ? d : 0.f;
+        }
+        load_io(jn);
+        // X = K^ dS, rows 16 wave .. + 15 (all of dS's operand values read first)
+        float bd[KB][4];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) bd[kb][jj] = sD[(16 * kb + 4 * g + jj) * kCS + c];
+        f32x4 xa = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) xa = __builtin_amdgcn_mfma_f32_16x16x4f32(kA[kb][jj], bd[kb][jj], xa, 0, 0, 0);
+        load_k(rec_next);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sX[(16 * wave + 4 * g + e) * kCS + c] = xa[e];
+        __syncthreads();  // X and dO are complete; every read of dS is done
+        if (owner) {
+            float bo[4][4], bx[4][4];
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    bo[kb][jj] = sO[(16 * kb + 4 * g + jj) * kCS + c];
+                    bx[kb][jj] = sX[(16 * kb + 4 * g + jj) * kCS + c];
+                }
+#pragma unroll
+            for (int t = 0; t < SPW; ++t) {
+                f32x4 acc;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[e] = gam[t][e] * D[t][e];
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qT[t][kb][jj], bo[kb][jj], acc, 0, 0, 0);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(wT[t][kb][jj], bx[kb][jj], acc, 0, 0, 0);
+                    }
+                D[t] = acc;
+            }
+            load_t(rec_next);
+#pragma unroll
+            for (int t = 0; t < SPW; ++t)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sD[(i0(t) + 4 * g + e) * kCS + c] = D[t][e];
+        }
+        __syncthreads();  // dS is complete; every read of X and dO is done
+    }
+    if (a.dS0 && owner) {
+#pragma unroll
+        for (int t = 0; t < SPW; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) a.dS0[sidx + (i0(t) + 4 * g + e) * DV + col] = D[t][e];
     }
 }
 
@@ -771,15 +837,10 @@ hipError_t launch_bwd_typed(const BackwardArgs& b, const PrefillArgs& fa, hipStr
         if (e != hipSuccess) return e;
     }
     {
-        const int64_t blocks = static_cast<int64_t>(f.N) * f.H * (DV / 16);
-        constexpr size_t clds = chain_lds_bytes<DK>();
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_chain_kernel<DK, DV, XT, GT>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(clds));
-        if (e != hipSuccess) return e;
+        const int64_t blocks = slice_grid(static_cast<int64_t>(f.N) * f.H, DV / 16);
         LaunchTimer timer("bwd_chain", s);
-        hipLaunchKernelGGL((bwd_chain_kernel<DK, DV, XT, GT>), dim3(static_cast<unsigned>(blocks)), dim3(256), clds,
-                           s, k);
-        e = hipGetLastError();
+        hipLaunchKernelGGL((bwd_chain_kernel<DK, DV, XT, GT>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, k);
+        hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     if (slots == 0 || f.T == 0) return hipSuccess;

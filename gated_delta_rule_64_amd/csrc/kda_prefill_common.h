@@ -53,6 +53,21 @@ __global__ __launch_bounds__(1024) void chunk_map_kernel(const int32_t* __restri
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// The state passes run one workgroup per (sequence, head, 16-column slice).
+// Block b -> (group = sequence * H + head, slice) such that all slices of a
+// group share an XCD (workgroups are dealt round-robin over the 8 XCDs), so
+// the chunk records they all read go through one L2.  The grid is rounded up
+// to whole sets of 8 groups; a block past the last group has grp >= groups.
+struct SliceBlock {
+    int64_t grp;
+    int sl;
+};
+__device__ __forceinline__ SliceBlock slice_block(int bid, int nsl) {
+    const int q = bid >> 3;
+    return {static_cast<int64_t>(q / nsl) * 8 + (bid & 7), q % nsl};
+}
+inline int64_t slice_grid(int64_t groups, int nsl) { return (groups + 7) / 8 * 8 * nsl; }
+
 // Record of one (chunk slot, head) on the fp32 path, offsets in floats:
 // W [64][dk], U~ [64][dv], Q' [64][dk], K^ [64][dk], M U~ [64][dv], gamma [dk]
 struct GenRec {

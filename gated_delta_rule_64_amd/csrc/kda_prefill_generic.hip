@@ -113,110 +113,203 @@ struct GenK {
 // ---- phase 1, the records, is chunk_records_kernel (kda_backward.hip) ----
 
 // ---- phase 2: per (sequence, head, 16 state columns), chunks in order ----
-// One chunk's record matrix [64][dk] (16-byte aligned) into LDS rows of
-// dk + 1 floats (the padding keeps reads of one channel over many rows, or
-// of many rows at one channel, off a single bank).
-__device__ __forceinline__ void stage_rows(float* dst, const float* src, int dk) {
-    const int kp = dk + 1;
-    for (int i = threadIdx.x; i < 16 * dk; i += 256) {
-        const int r = (4 * i) / dk, c = (4 * i) % dk;
-        const float4 v = *reinterpret_cast<const float4*>(src + r * dk + c);
-        float* d = dst + r * kp + c;
-        d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+// Four waves on the fp32 matrix cores (v_mfma_f32_16x16x4_f32: lane (g, c) =
+// (lane / 16, lane % 16) gives A[c][g] and B[g][c] and holds D[4g + e][c];
+// here the MFMA's term g of step jj is term 4g + jj of a run of 16).  Per
+// chunk, wave w makes token rows 16w .. 16w + 15 of
+//     U = U~ - W S   and   O = Q' S + M U~,
+// then the waves that own state rows update them:  S <- Diag(gamma) S + K^T U.
+// A wave keeps its state rows as matrix-core accumulators; S (the B operand
+// of W S and Q' S) and U (of K^T U) are shared through LDS.  Each operand a
+// wave takes from the record is reloaded, for the next chunk, as soon as the
+// products that use it are issued, so its load overlaps the rest of the step.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kGS = 20;  // LDS row stride of S and U (16 columns): rows 4g + jj of lanes (g, c) fall in distinct banks
+
+template <int DK>
+struct GenOps {
+    static constexpr int KB = DK / 16;                // 16-term runs of W S
+    static constexpr int ST = DK / 16;                // 16-row tiles of S
+    static constexpr int SPW = ST >= 4 ? ST / 4 : 1;  // state tiles per wave
+    float kh[SPW][4][4];  // K^[16 kb + 4g + jj][i0 + c]
+    float gam[SPW][4];    // gamma[i0 + 4g + e]
+    float u[4], oi[4];    // U~, M U~ at [16 wave + 4g + e][16 sl + c]
+    float z[4];           // gate logits of the same outputs
+};
+
+template <int DK, typename XT, typename GT>
+__global__ __launch_bounds__(256) void gen_state_kernel(GenK<XT, GT> a) {
+    using Ops = GenOps<DK>;
+    constexpr int KB = Ops::KB, ST = Ops::ST, SPW = Ops::SPW;
+    __shared__ float sS[DK * kGS];
+    __shared__ float sU[64 * kGS];
+    const int dv = a.dv, nsl = dv / 16;
+    const SliceBlock sbk = slice_block(blockIdx.x, nsl);
+    if (sbk.grp >= static_cast<int64_t>(a.N) * a.H) return;
+    const int sl = sbk.sl, h = static_cast<int>(sbk.grp % a.H), n = static_cast<int>(sbk.grp / a.H);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, c = lane & 15;
+    const bool owner = wave * SPW < ST;  // (below d = 64 some waves own no state rows)
+    const GenRec R = gen_rec(DK, dv);
+    const int64_t sidx = (static_cast<int64_t>(n) * a.H + h) * DK * dv;
+    const int col = 16 * sl + c;
+    auto i0 = [&](int t) { return owner ? 16 * (wave * SPW + t) : 0; };
+    const int64_t sb = seq_begin(a.cu, n), se = seq_finish(a.cu, n, a.T);
+    const int nch = a.base[n + 1] - a.base[n];
+    const bool has_z = a.z != nullptr;
+    const XT* zp = has_z ? a.z : a.v;  // (same [T][H][dv] layout; read but unused without a gate)
+    auto rec_of = [&](int j) { return a.rec + (static_cast<int64_t>(a.base[n] + j) * a.H + h) * R.size; };
+    auto len_of = [&](int j) {
+        return static_cast<int>(min(static_cast<int64_t>(kChunk), se - (sb + static_cast<int64_t>(j) * kChunk)));
+    };
+    Ops o;
+    // W, Q' at row 16 wave + c, terms 16 kb + 4g .. + 3: two register sets,
+    // chunk j in set j % 2, so the next chunk's loads are issued a whole step
+    // before they are used
+    f32x4 w0[KB], q0[KB], w1[KB], q1[KB];
+    auto load_wq = [&](const float* rec, f32x4 (&w)[KB], f32x4 (&q)[KB]) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            const int64_t off = (16 * wave + c) * DK + 16 * kb + 4 * g;
+            w[kb] = *reinterpret_cast<const f32x4*>(rec + R.W + off);
+            q[kb] = *reinterpret_cast<const f32x4*>(rec + R.Qp + off);
+        }
+    };
+    auto load_rows = [&](const float* rec, int j) {  // U~, M U~, gate logits
+        const int L = len_of(j);
+        const int64_t t0 = sb + static_cast<int64_t>(j) * kChunk;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = 16 * wave + 4 * g + e;
+            o.u[e] = rec[R.U + r * dv + col];
+            o.oi[e] = rec[R.Oi + r * dv + col];
+            o.z[e] = ld(zp + ((t0 + min(r, L - 1)) * a.H + h) * dv + col);
+        }
+    };
+    auto load_k = [&](const float* rec) {
+#pragma unroll
+        for (int t = 0; t < SPW; ++t) {
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) o.kh[t][kb][jj] = rec[R.Kh + (16 * kb + 4 * g + jj) * DK + i0(t) + c];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o.gam[t][e] = rec[R.gam + i0(t) + 4 * g + e];
+        }
+    };
+    // the state rows of this wave: tile t holds rows i0(t) + 4g + e, column col
+    f32x4 S[SPW];
+#pragma unroll
+    for (int t = 0; t < SPW; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int row = i0(t) + 4 * g + e;
+            S[t][e] = a.S0 && owner ? a.S0[sidx + row * dv + col] : 0.f;
+            if (owner) sS[row * kGS + c] = S[t][e];
+        }
+    if (nch > 0) {
+        const float* rec = rec_of(0);
+        load_wq(rec, w0, q0);
+        load_rows(rec, 0);
+        load_k(rec);
+    }
+    __syncthreads();
+    auto step = [&](int j, f32x4 (&w)[KB], f32x4 (&q)[KB], f32x4 (&wn)[KB], f32x4 (&qn)[KB]) {
+        const int L = len_of(j);
+        const int64_t t0 = sb + static_cast<int64_t>(j) * kChunk;
+        const float* rec_next = rec_of(min(j + 1, nch - 1));  // (the last step reloads its own chunk, unused)
+        load_wq(rec_next, wn, qn);
+        // U and O rows 16 wave .. + 15
+        // (all of S's operand values are read from LDS before the products start)
+        float bs[KB][4];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) bs[kb][jj] = sS[(16 * kb + 4 * g + jj) * kGS + c];
+        f32x4 ua = {0.f, 0.f, 0.f, 0.f}, oa = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                ua = __builtin_amdgcn_mfma_f32_16x16x4f32(w[kb][jj], bs[kb][jj], ua, 0, 0, 0);
+                oa = __builtin_amdgcn_mfma_f32_16x16x4f32(q[kb][jj], bs[kb][jj], oa, 0, 0, 0);
+            }
+        float y[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            sU[(16 * wave + 4 * g + e) * kGS + c] = o.u[e] - ua[e];
+            const float out = o.oi[e] + oa[e];
+            y[e] = has_z ? out * sigmoid_fast(o.z[e]) : out;
+        }
+        load_rows(rec_next, min(j + 1, nch - 1));
+        if (a.out != nullptr) {  // (no output: a forward pass run for its records and states)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * wave + 4 * g + e;
+                if (r < L) st(a.out + ((t0 + r) * a.H + h) * dv + col, y[e]);
+            }
+        }
+        __syncthreads();  // U is complete; every read of S is done
+        // a full chunk that ends a snapshot interval: the state after it is the m-th snapshot
+        const int sc = a.snap.chunks;
+        const bool snap = sc > 0 && (j + 1) % sc == 0 && L == kChunk;
+        if (owner) {
+            float bu[4][4];
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) bu[kb][jj] = sU[(16 * kb + 4 * g + jj) * kGS + c];
+#pragma unroll
+            for (int t = 0; t < SPW; ++t) {
+                f32x4 acc;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[e] = o.gam[t][e] * S[t][e];
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj)
+                        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(o.kh[t][kb][jj], bu[kb][jj], acc, 0, 0, 0);
+                S[t] = acc;
+            }
+            load_k(rec_next);
+#pragma unroll
+            for (int t = 0; t < SPW; ++t)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sS[(i0(t) + 4 * g + e) * kGS + c] = S[t][e];
+            if (snap) {
+                float* so = a.snap.out + ((static_cast<int64_t>(a.snap.off[n]) + (j + 1) / sc - 1) * a.H + h) * DK * dv;
+#pragma unroll
+                for (int t = 0; t < SPW; ++t)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) so[(i0(t) + 4 * g + e) * dv + col] = S[t][e];
+            }
+        }
+        __syncthreads();  // S is complete; every read of U is done
+    };
+    for (int j = 0; j < nch; j += 2) {
+        step(j, w0, q0, w1, q1);
+        if (j + 1 < nch) step(j + 1, w1, q1, w0, q0);
+    }
+    if (a.S_out && owner) {
+#pragma unroll
+        for (int t = 0; t < SPW; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) a.S_out[sidx + (i0(t) + 4 * g + e) * dv + col] = S[t][e];
     }
 }
 
-size_t gen_state_lds_bytes(int dk) { return (2 * 64 * static_cast<size_t>(dk + 1) + 16 * dk + 64 * 16) * 4; }
-
 template <typename XT, typename GT>
-__global__ __launch_bounds__(256) void gen_state_kernel(GenK<XT, GT> a) {
-    extern __shared__ float gsm[];
-    const int dk = a.dk, dv = a.dv, kp = dk + 1;
-    float* sWK = gsm;              // [64][kp]: W, then K^
-    float* sQp = sWK + 64 * kp;    // [64][kp]: Q'
-    float* sS = sQp + 64 * kp;     // [dk][16]: this block's 16 state columns
-    float* sU = sS + 16 * dk;      // [64][16]
-    const int nsl = dv / 16;
-    const int sl = blockIdx.x % nsl;
-    const int h = (blockIdx.x / nsl) % a.H;
-    const int n = blockIdx.x / (nsl * a.H);
-    const int tid = threadIdx.x;
-    const GenRec R = gen_rec(dk, dv);
-    const int64_t sidx = (static_cast<int64_t>(n) * a.H + h) * dk * dv;
-    for (int e = tid; e < dk * 16; e += 256) {
-        const int c = e >> 4, j = e & 15;
-        sS[e] = a.S0 ? a.S0[sidx + c * dv + 16 * sl + j] : 0.f;
+hipError_t launch_gen_state_kernel(const GenK<XT, GT>& k, hipStream_t s) {
+    const int64_t blocks = slice_grid(static_cast<int64_t>(k.N) * k.H, k.dv / 16);
+    LaunchTimer timer("gen_state", s);
+    switch (k.dk) {
+        case 16: hipLaunchKernelGGL((gen_state_kernel<16, XT, GT>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, k); break;
+        case 32: hipLaunchKernelGGL((gen_state_kernel<32, XT, GT>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, k); break;
+        case 64: hipLaunchKernelGGL((gen_state_kernel<64, XT, GT>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, k); break;
+        case 128: hipLaunchKernelGGL((gen_state_kernel<128, XT, GT>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, k); break;
+        default: return hipErrorInvalidValue;
     }
-    const int64_t sb = seq_begin(a.cu, n), se = seq_finish(a.cu, n, a.T);
-    const int nch = a.base[n + 1] - a.base[n];
-    const int r = tid >> 2, c4 = (tid & 3) * 4;
-    for (int j = 0; j < nch; ++j) {
-        const float* rec = a.rec + (static_cast<int64_t>(a.base[n] + j) * a.H + h) * R.size;
-        const int64_t t0 = sb + static_cast<int64_t>(j) * kChunk;
-        const int L = static_cast<int>(min(static_cast<int64_t>(kChunk), se - t0));
-        __syncthreads();  // the last chunk's reads of sWK are done
-        stage_rows(sWK, rec + R.W, dk);
-        stage_rows(sQp, rec + R.Qp, dk);
-        __syncthreads();
-        // U = U~ - W S, O = Q' S + M U~ (row r, columns c4 .. c4+3)
-        float u[4], o[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            u[i] = rec[R.U + r * dv + 16 * sl + c4 + i];
-            o[i] = rec[R.Oi + r * dv + 16 * sl + c4 + i];
-        }
-        for (int c = 0; c < dk; ++c) {
-            const float w = sWK[r * kp + c], qp = sQp[r * kp + c];
-            const float4 s4 = *reinterpret_cast<const float4*>(sS + c * 16 + c4);
-            u[0] -= w * s4.x; u[1] -= w * s4.y; u[2] -= w * s4.z; u[3] -= w * s4.w;
-            o[0] += qp * s4.x; o[1] += qp * s4.y; o[2] += qp * s4.z; o[3] += qp * s4.w;
-        }
-        if (r < L && a.out != nullptr) {  // (no output: a forward pass run for its records and states)
-            const int64_t oidx = ((t0 + r) * a.H + h) * dv + 16 * sl + c4;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float y = o[i];
-                if (a.z) y *= sigmoid(ld(a.z + oidx + i));
-                st(a.out + oidx + i, y);
-            }
-        }
-        __syncthreads();  // every read of W and of S is done
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sU[r * 16 + c4 + i] = u[i];
-        stage_rows(sWK, rec + R.Kh, dk);
-        __syncthreads();
-        // S <- Diag(gamma) S + K^T U (channel c, columns j4 .. j4+3); a full
-        // chunk that ends a snapshot interval: the state after it is the m-th snapshot
-        const int sc = a.snap.chunks;
-        const bool snap = sc > 0 && (j + 1) % sc == 0 && L == kChunk;
-        float* snap_out = snap ? a.snap.out + ((static_cast<int64_t>(a.snap.off[n]) + (j + 1) / sc - 1) * a.H + h) *
-                                                  dk * dv
-                               : nullptr;
-        for (int e = tid; e < dk * 4; e += 256) {
-            const int c = e >> 2, j4 = (e & 3) * 4;
-            const float gm = rec[R.gam + c];
-            float acc[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i] = gm * sS[c * 16 + j4 + i];
-            for (int rr = 0; rr < 64; ++rr) {
-                const float kh = sWK[rr * kp + c];
-                const float4 u4 = *reinterpret_cast<const float4*>(sU + rr * 16 + j4);
-                acc[0] += kh * u4.x; acc[1] += kh * u4.y; acc[2] += kh * u4.z; acc[3] += kh * u4.w;
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                sS[c * 16 + j4 + i] = acc[i];  // (each element read and written by its own thread)
-                if (snap) snap_out[c * dv + 16 * sl + j4 + i] = acc[i];
-            }
-        }
-    }
-    __syncthreads();
-    if (a.S_out) {
-        for (int e = tid; e < dk * 16; e += 256) {
-            const int c = e >> 4, jj = e & 15;
-            a.S_out[sidx + c * dv + 16 * sl + jj] = sS[e];
-        }
-    }
+    return hipGetLastError();
 }
 
 template <typename XT, typename GT>
@@ -231,14 +324,7 @@ hipError_t launch_gen_typed(const PrefillArgs& a, hipStream_t s, int32_t* base, 
         hipError_t e = launch_chunk_records(a, s, base, rec);
         if (e != hipSuccess) return e;
     }
-    const int64_t blocks = static_cast<int64_t>(a.N) * a.H * (a.dv / 16);
-    const size_t lds = gen_state_lds_bytes(a.dk);
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gen_state_kernel<XT, GT>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-    if (e != hipSuccess) return e;
-    LaunchTimer timer("gen_state", s);
-    hipLaunchKernelGGL((gen_state_kernel<XT, GT>), dim3(static_cast<unsigned>(blocks)), dim3(256), lds, s, k);
-    return hipGetLastError();
+    return launch_gen_state_kernel(k, s);
 }
 
 }  // namespace
@@ -251,14 +337,7 @@ hipError_t launch_gen_state_typed(const PrefillArgs& a, hipStream_t s, int32_t* 
     k.v = static_cast<const XT*>(a.v); k.z = static_cast<const XT*>(a.z);
     k.la = static_cast<const GT*>(a.la); k.beta = static_cast<const GT*>(a.beta);
     k.S0 = a.S0; k.S_out = a.S_out; k.out = static_cast<XT*>(a.out); k.rec = rec; k.snap = a.snap;
-    const int64_t blocks = static_cast<int64_t>(a.N) * a.H * (a.dv / 16);
-    const size_t lds = gen_state_lds_bytes(a.dk);
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gen_state_kernel<XT, GT>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-    if (e != hipSuccess) return e;
-    LaunchTimer timer("gen_state", s);
-    hipLaunchKernelGGL((gen_state_kernel<XT, GT>), dim3(static_cast<unsigned>(blocks)), dim3(256), lds, s, k);
-    return hipGetLastError();
+    return launch_gen_state_kernel(k, s);
 }
 
 hipError_t launch_gen_state(const PrefillArgs& a, hipStream_t s, int32_t* base, float* rec) {
