@@ -99,10 +99,9 @@ __device__ __forceinline__ void mm64(int K, FA A, FB B, FO out) {
     for (int i = 0; i < RPW; ++i)
 #pragma unroll
         for (int jj = 0; jj < CPW; ++jj) acc[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 1
-    for (int k0 = 0; k0 < K; k0 += 16) {
+    // the operands of run k0 (terms k0 .. k0 + 15) into registers
+    auto load = [&](int k0, float (&av)[RPW][4], float (&bv)[CPW][4]) {
         const int kk = k0 + 4 * g;
-        float av[RPW][4], bv[CPW][4];
 #pragma unroll
         for (int i = 0; i < RPW; ++i)
 #pragma unroll
@@ -111,6 +110,8 @@ __device__ __forceinline__ void mm64(int K, FA A, FB B, FO out) {
         for (int jj = 0; jj < CPW; ++jj)
 #pragma unroll
             for (int j = 0; j < 4; ++j) bv[jj][j] = B(kk + j, c0 + 16 * jj + c);
+    };
+    auto mma = [&](const float (&av)[RPW][4], const float (&bv)[CPW][4]) {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -118,6 +119,20 @@ __device__ __forceinline__ void mm64(int K, FA A, FB B, FO out) {
 #pragma unroll
                 for (int jj = 0; jj < CPW; ++jj)
                     acc[i][jj] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[i][j], bv[jj][j], acc[i][jj], 0, 0, 0);
+    };
+    // two register sets: the next run's loads are in flight while this run's
+    // products are issued (a clamped run index repeats a load that is not used)
+    float a0[RPW][4], b0[CPW][4], a1[RPW][4], b1[CPW][4];
+    if (K > 0) load(0, a0, b0);
+#pragma unroll 1
+    for (int k0 = 0; k0 < K; k0 += 32) {
+        const bool two = k0 + 16 < K;
+        load(two ? k0 + 16 : k0, a1, b1);
+        mma(a0, b0);
+        if (two) {
+            load(k0 + 32 < K ? k0 + 32 : k0 + 16, a0, b0);
+            mma(a1, b1);
+        }
     }
 #pragma unroll
     for (int i = 0; i < RPW; ++i)
@@ -656,6 +671,15 @@ __global__ __launch_bounds__(kGradThreads) void bwd_intra_kernel(BwdK<XT, GT> a)
         for (int s_ = 0; s_ < tid; ++s_) acc += sdT[tid * MS + s_] * sA[tid * MS + s_];
         atomicAdd(&sdB[tid], acc);
     }
+    __syncthreads();  // every read of A and T is done: the queries go there
+    // the queries for the loops below, channels 0 .. 63 in A's space and
+    // 64 .. 127 in T's (a thread's channels never straddle the two)
+    auto qs = [&](int r, int c) -> float& { return (c < 64 ? sA : sT)[r * MS + (c & 63)]; };
+    for (int i = tid; i < 64 * DK; i += kGradThreads) {
+        const int r = i / DK, c = i % DK;
+        qs(r, c) = r < L ? ld(a.q + tok(r) * DK + c) : 0.f;
+    }
+    __syncthreads();
     // ---- 6. through A (dA = B dY) and M (dM), with E_rsc = e^{G_rc - G_sc}.
     // Thread tiles of Tile64<DK>: rows R0 .. R0+TR-1, channels C0 .. C0+TC-1.
     // As row r of A and M:  dk_rc += sum_s dA_rs k_sc E,  dq_rc += sum_s dM_rs k_sc E,
@@ -704,7 +728,7 @@ __global__ __launch_bounds__(kGradThreads) void bwd_intra_kernel(BwdK<XT, GT> a)
 #pragma unroll
             for (int jj = 0; jj < TC; ++jj) {
                 kr[jj] = sK[r2 * KP + C0 + jj];
-                qr[jj] = r2 < L ? ld(a.q + tok(r2) * DK + C0 + jj) : 0.f;
+                qr[jj] = qs(r2, C0 + jj);
                 gr[jj] = sG[r2 * KP + C0 + jj];
             }
 #pragma unroll
@@ -718,8 +742,7 @@ __global__ __launch_bounds__(kGradThreads) void bwd_intra_kernel(BwdK<XT, GT> a)
 #pragma unroll
             for (int jj = 0; jj < TC; ++jj) {
                 const int r = R0 + i, c = C0 + jj, e = r * DK + c;
-                const float kv = sK[r * KP + c];
-                const float qv = r < L ? ld(a.q + tok(r) * DK + c) : 0.f;
+                const float kv = sK[r * KP + c], qv = qs(r, c);
                 gk[e] += dkr[i][jj] + dks[i][jj];
                 gq[e] += dqr[i][jj];
                 gG[e] += kv * dkr[i][jj] + qv * dqr[i][jj] - kv * dks[i][jj];
