@@ -48,12 +48,13 @@ struct BwdK {
     float *dq, *dk, *dv, *dla, *dbeta, *dz, *dS0;
 };
 
-// Threads of the per-chunk kernels.  Their LDS allows one workgroup per CU.
-// The record kernel runs 16 waves (measured: 1.58 -> 1.15 ms on the
-// 4096-token layer against 4 waves); the gradient kernel keeps 4 waves and
-// the larger register tiles they allow (measured: 5.5 ms against 6.9 ms).
+// Threads of the per-chunk kernels.  Their LDS allows one workgroup per CU,
+// and their phases are latency-bound, so both run 16 waves (measured on the
+// 4096-token layer: the record kernel 1.58 -> 1.15 ms against 4 waves; the
+// gradient kernel, with its products on the matrix cores, 3.17 ms with 4
+// waves, 2.70 with 8, 2.38 with 16).
 constexpr int kRecThreads = 1024;
-constexpr int kGradThreads = 256;
+constexpr int kGradThreads = 1024;
 
 // Per-thread tile of a 64-row, N-column result shared by NT threads:
 // TR rows x TC columns, TR * TC = 64 N / NT.
@@ -148,14 +149,15 @@ __device__ __forceinline__ void mm64(int K, FA A, FB B, FO out) {
 __device__ __forceinline__ float decay(float x) { return __builtin_amdgcn_exp2f(fminf(x, 0.f) * kLog2e); }
 
 // A (strictly lower) and M (lower with diagonal) of a chunk, by AT x AT
-// tiles of (r, s) per thread; K, Q, G rows padded to DK + 1 floats in LDS.
+// tiles of (r, s) per thread (one tile, or two for 512 threads); K, Q, G
+// rows padded to DK + 1 floats in LDS.
 template <int DK, int NT>
 __device__ __forceinline__ void am_tiles(const float* sK, const float* sQ, const float* sG, float* sA, float* sM) {
     constexpr int KP = DK + 1;
     constexpr int AT = NT == 256 ? 4 : 2, GD = 64 / AT;
-    static_assert(GD * GD == NT, "one tile per thread");
-    const int tid = threadIdx.x;
-        const int r0 = AT * (tid / GD), s0 = AT * (tid % GD);
+    static_assert(GD * GD == NT || GD * GD == 2 * NT, "one or two tiles per thread");
+    for (int tile = threadIdx.x; tile < GD * GD; tile += NT) {
+        const int r0 = AT * (tile / GD), s0 = AT * (tile % GD);
         float av[AT][AT], mv[AT][AT];
 #pragma unroll
         for (int i = 0; i < AT; ++i)
@@ -192,6 +194,7 @@ __device__ __forceinline__ void am_tiles(const float* sK, const float* sQ, const
                 sA[r * MS + s_] = s_ < r ? av[i][jj] : 0.f;
                 sM[r * MS + s_] = s_ <= r ? mv[i][jj] : 0.f;
             }
+    }
 }
 
 // T = (I + Diag(beta) A)^-1 (unit lower triangular) by 16 x 16 blocks.
