@@ -371,15 +371,15 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
     int32_t* base = static_cast<int32_t*>(a.ws);
     SlotInfo* slot_info = reinterpret_cast<SlotInfo*>(static_cast<char*>(a.ws) + chunk_map_base_bytes(a.N));
     char* recs = static_cast<char*>(a.ws) + chunk_map_bytes(a.T, a.N);
-    hipError_t e;
-    {
+    const bool mfma = prefill_uses_mfma(a.dk, a.dv, a.x);
+    if (!mfma || !mfma_inline_map(a.N, a.snap)) {
         LaunchTimer timer("chunk_map", s);
         hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(1024), 0, s, a.cu, a.N, a.T, base, slot_info,
                            a.snap.chunks, a.snap.off);
-        e = hipGetLastError();
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
     }
-    if (e != hipSuccess) return e;
-    if (prefill_uses_mfma(a.dk, a.dv, a.x)) return launch_prefill_mfma(a, s, base, slot_info, recs);
+    if (mfma) return launch_prefill_mfma(a, s, base, slot_info, recs);
     return launch_gen_forward(a, s, base, reinterpret_cast<float*>(recs));
 }
 
@@ -390,13 +390,13 @@ hipError_t launch_layer(const LayerArgs& a, hipStream_t s) {
     SlotInfo* slot_info = reinterpret_cast<SlotInfo*>(static_cast<char*>(a.ws) + chunk_map_base_bytes(a.N));
     char* recs = static_cast<char*>(a.ws) + chunk_map_bytes(a.T, a.N);
     hipError_t e;
-    {
+    if (!mfma_inline_map(a.N, a.snap)) {
         LaunchTimer timer("chunk_map", s);
         hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(1024), 0, s, a.cu, a.N, a.T, base, slot_info,
                            a.snap.chunks, a.snap.off);
         e = hipGetLastError();
+        if (e != hipSuccess) return e;
     }
-    if (e != hipSuccess) return e;
     e = launch_layer_mfma(a, s, base, slot_info, recs);
     if (e != hipSuccess) return e;
     // the chunk kernel has read the old conv history; now it is replaced

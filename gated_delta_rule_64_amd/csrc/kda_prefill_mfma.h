@@ -11,6 +11,10 @@
 namespace kda {
 
 bool mfma_prefill_supports(int dk, int dv, DT x);
+// Whether the matrix-core kernels derive each chunk slot from cu_seqlens
+// themselves (then no chunk map is built before them): up to 64 sequences,
+// no snapshots.
+bool mfma_inline_map(int N, const Snapshots& snap);
 size_t mfma_record_bytes();
 hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t s, int32_t* base, const SlotInfo* slot_info,
                                char* recs);

@@ -113,6 +113,7 @@ struct MfmaK {
     const float* cs;
     int64_t slots;   // chunk slots per head in the record array
     int64_t groups;  // N * H
+    bool inline_map;  // no chunk map: the kernels derive each slot from cu (N <= 64)
     Snapshots snap;  // optional states after every snap.chunks full chunks
 };
 
@@ -153,6 +154,36 @@ __device__ __forceinline__ i32x4 scalar_load4(const int32_t* p) {
     i32x4 v;
     asm volatile("s_load_dwordx4 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
     return v;
+}
+
+// Chunk slots without the chunk map, for at most 64 sequences: lane i of the
+// wave gets the number of chunks in sequences 0 .. i (an inclusive scan over
+// the lanes; lanes past the last sequence hold the total).  Every lane of the
+// wave must be active.
+__device__ __forceinline__ int chunk_prefix_lane(const int32_t* cu, int N, int64_t T) {
+    const int lane = threadIdx.x & 63;
+    int c = 0;
+    if (lane < N) c = static_cast<int>((seq_finish(cu, lane, T) - seq_begin(cu, lane) + kChunk - 1) / kChunk);
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(c, off);
+        if (lane >= off) c += y;
+    }
+    return c;
+}
+// With that prefix (uniform results): the sequence that holds a slot (the
+// number of sequences that end at or before it), and the slots before
+// sequence n.
+__device__ __forceinline__ int seq_of_slot(int incl, int64_t slot) {
+    return static_cast<int>(__popcll(__ballot(incl <= slot)));
+}
+__device__ __forceinline__ int slots_before(int incl, int n) {
+    return n > 0 ? __builtin_amdgcn_readlane(incl, n - 1) : 0;
+}
+// A uniform sequence boundary, through the scalar cache.
+__device__ __forceinline__ int64_t seq_bound(const int32_t* cu, int n, int64_t T, bool finish) {
+    if (cu == nullptr) return finish ? T : 0;
+    return scalar_load(cu + n + (finish ? 1 : 0));
 }
 
 // Four consecutive gate values of one row, kept as loaded until used.
@@ -212,7 +243,9 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
     const int ftid = threadIdx.x;  // the thread index as the prefetch uses it
     // Units are (head, chunk slot) pairs, head-major; the grid is persistent
     // (one workgroup per CU) and walks them with stride gridDim.x.
-    const int nslots = scalar_load(a.base + a.N);
+    const int incl = a.inline_map ? chunk_prefix_lane(a.cu, a.N, a.T) : 0;
+    const int nslots = a.inline_map ? (a.N > 0 ? __builtin_amdgcn_readlane(incl, a.N - 1) : 0)
+                                    : scalar_load(a.base + a.N);
     const int64_t units = static_cast<int64_t>(H) * nslots;
     struct Unit {
         int h, L, n;
@@ -228,6 +261,14 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
         const uint32_t v32 = static_cast<uint32_t>(v), ns = static_cast<uint32_t>(nslots);
         u.h = static_cast<int>(v32 / ns);
         u.slot = v32 % ns;
+        if (a.inline_map) {
+            u.n = seq_of_slot(incl, u.slot);
+            const int s0 = slots_before(incl, u.n);
+            u.first = u.slot == s0;
+            u.t0 = seq_bound(a.cu, u.n, a.T, false) + (u.slot - s0) * kChunk;
+            u.L = static_cast<int>(min(static_cast<int64_t>(kChunk), seq_bound(a.cu, u.n, a.T, true) - u.t0));
+            return u;
+        }
         const i32x4 si = scalar_load4(reinterpret_cast<const int32_t*>(a.slot_info + u.slot));
         u.t0 = static_cast<int64_t>((static_cast<uint64_t>(static_cast<uint32_t>(si[1])) << 32) |
                                     static_cast<uint32_t>(si[0]));
@@ -962,8 +1003,15 @@ __global__ __launch_bounds__(64 * (2 * NS + StateCfg<NS>::kMemWaves)) void mfma_
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, c = lane & 15;
 
     const int64_t sb = seq_begin(a.cu, n), se = seq_finish(a.cu, n, a.T);
-    const int slot0 = a.base[n];
-    const int nch = a.base[n + 1] - slot0;
+    int slot0, nch;
+    if (a.inline_map) {
+        const int incl = chunk_prefix_lane(a.cu, a.N, a.T);
+        slot0 = slots_before(incl, n);
+        nch = __builtin_amdgcn_readlane(incl, n) - slot0;
+    } else {
+        slot0 = a.base[n];
+        nch = a.base[n + 1] - slot0;
+    }
     auto rec_of = [&](int j) { return a.rec + (h * a.slots + slot0 + j) * REC_BYTES; };
     auto chunk_len = [&](int j) {
         return static_cast<int>(min(static_cast<int64_t>(kChunk), se - (sb + static_cast<int64_t>(j) * kChunk)));
@@ -1253,6 +1301,7 @@ hipError_t launch_kernels(MfmaK<GT>& k, hipStream_t s) {
     const int64_t slots = chunk_slots_bound(k.T, k.N);
     k.slots = slots;
     k.groups = static_cast<int64_t>(k.N) * k.H;
+    k.inline_map = mfma_inline_map(k.N, k.snap);
     int dev = 0, cus = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
@@ -1288,6 +1337,8 @@ hipError_t launch_typed(const PrefillArgs& a, hipStream_t s, int32_t* base, cons
 }  // namespace
 
 bool mfma_prefill_supports(int dk, int dv, DT x) { return dk == 128 && dv == 128 && x == DT::BF16; }
+
+bool mfma_inline_map(int N, const Snapshots& snap) { return N >= 1 && N <= 64 && snap.chunks == 0; }
 
 size_t mfma_record_bytes() { return REC_BYTES; }
 

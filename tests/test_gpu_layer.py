@@ -40,6 +40,40 @@ def test_layer_matches_oracle(K, oracle_mod, lengths):
     assert_close("state", to_host64(S), ref["S"], TOL["bf16"])
 
 
+def test_layer_many_sequences_use_the_chunk_map(K, oracle_mod):
+    """Past 64 sequences the chunk kernels read a chunk map built on the device
+    before them (up to 64 they derive each chunk from cu_seqlens themselves):
+    70 short sequences, some empty, against the oracle."""
+    rng = np.random.default_rng(70)
+    lengths = tuple(int(x) for x in rng.integers(0, 150, size=70))
+    inp = synth.make("varlen_64", lengths=lengths, H=2)
+    print(f"fused layer, {len(lengths)} sequences", flush=True)
+    out, S = fused(K, inp)
+    ref = oracle_mod.layer(oracle_layer_inputs(inp))
+    assert_close("y", to_host64(out), ref["y"], TOL["bf16"])
+    assert_close("state", to_host64(S), ref["S"], TOL["bf16"])
+
+
+@pytest.mark.parametrize("lengths", [(1000,), (130, 0, 64, 1, 700), (63, 65, 3, 2, 1)])
+def test_layer_inline_chunk_lookup_equals_chunk_map(K, lengths):
+    """Without snapshots and with at most 64 sequences the kernels find each
+    chunk's sequence, first token and length themselves; asking for snapshots
+    at an interval no sequence reaches builds the chunk map instead.  The
+    arithmetic is the same, so the results are bit-identical."""
+    inp = synth.make("varlen_64", lengths=lengths, H=3)
+    H, dk, dv, T = inp["H"], inp["dk"], inp["dv"], inp["T_tot"]
+    print(f"fused layer inline lookup vs chunk map, lengths={lengths}", flush=True)
+    out1, S1 = fused(K, inp)
+    args = [to_dev(inp[n]) for n in ("q_in", "k_in", "v_in", "w_q", "w_k", "w_v", "g", "b")]
+    out2, S2, _, off = K.kda_prefill_layer(*args, H, dk, dv, out_gate=to_dev(inp["z"]).view(T, H, dv),
+                                           initial_state=to_dev(inp["S0"]) if inp["S0"] is not None else None,
+                                           cu_seqlens=to_dev(inp["cu_seqlens"]), snap_interval=64 * 1024)
+    torch.cuda.synchronize()
+    assert torch.all(off == 0)
+    assert torch.equal(out1, out2)
+    assert torch.equal(S1, S2)
+
+
 def test_layer_conv_history_in_and_out(K, oracle_mod):
     """Sequences shorter and longer than the conv width, each starting from
     a caller-given history; the history is rewritten with the last three raw
