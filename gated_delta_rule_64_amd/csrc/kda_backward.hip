@@ -261,7 +261,7 @@ constexpr size_t rec_lds_bytes() {
 
 template <int DK, int DV, typename XT, typename GT>
 __global__ __launch_bounds__(kRecThreads) void chunk_records_kernel(BwdK<XT, GT> a) {
-    extern __shared__ float smem[];
+    extern __shared__ __align__(16) float smem[];
     constexpr int KP = DK + 1;
     float* sK = smem;
     float* sQ = sK + 64 * KP;
@@ -496,7 +496,7 @@ constexpr size_t intra_lds_bytes() {
 // ---- pass 3: per (chunk, head), every input gradient ----
 template <int DK, int DV, typename XT, typename GT>
 __global__ __launch_bounds__(kGradThreads) void bwd_intra_kernel(BwdK<XT, GT> a) {
-    extern __shared__ float smem[];
+    extern __shared__ __align__(16) float smem[];
     // K and G rows padded to DK + 1 floats: the tiles below read 4 rows at
     // one channel, which would otherwise land in one LDS bank
     constexpr int KP = DK + 1;
