@@ -54,6 +54,7 @@ class KernelTime(ctypes.Structure):
 
 PROTOTYPES["kda_profile_enable"] = (ctypes.c_int, [ctypes.c_int])
 PROTOTYPES["kda_profile_collect"] = (ctypes.c_int, [ctypes.POINTER(KernelTime), ctypes.c_int])
+PROTOTYPES["kda_probe_peak"] = (ctypes.c_int, [_i32, _i32, _i32, _vp, _i64, _vp, _vp])
 
 
 class KdaError(RuntimeError):

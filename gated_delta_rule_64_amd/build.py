@@ -33,8 +33,16 @@ def _hipcc() -> str:
     return cand if os.path.exists(cand) else "hipcc"
 
 
-def _compile(src: str) -> str:
+def _headers_mtime() -> float:
+    hdrs = glob.glob(os.path.join(CSRC, "*.h")) + glob.glob(os.path.join(ROOT, "include", "*.h"))
+    return max((os.path.getmtime(h) for h in hdrs), default=0.0)
+
+
+def _compile(src: str, force: bool = True) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+    if not force and os.path.exists(obj) and \
+            os.path.getmtime(obj) > max(os.path.getmtime(src), _headers_mtime()):
+        return obj
     cmd = [_hipcc(), *FLAGS, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -42,11 +50,13 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False, jobs: int = 8) -> str:
+def build(verbose: bool = False, jobs: int = 8, force: bool = True) -> str:
+    """Compile and link libkda.so.  force=False reuses objects that are newer
+    than their source and every header (for quick rebuilds while editing)."""
     os.makedirs(BUILD, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     with ThreadPoolExecutor(max(1, jobs)) as ex:
-        objs = list(ex.map(_compile, srcs))
+        objs = list(ex.map(lambda s: _compile(s, force), srcs))
     tmp = LIB + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -59,4 +69,4 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    build(verbose=True, force="--changed" not in sys.argv)

@@ -29,8 +29,6 @@
 // Phase 2 (mfma_state_kernel): per (sequence, head, group of state
 //  columns), compute waves carry the fp32 state in registers through the
 //  chunks in order while copy waves stream each chunk's factors into LDS.
-#include <stdlib.h>
-
 #include "kda_prefill_common.h"
 #include "kda_prefill_mfma.h"
 #include "kda_profile.h"
@@ -1279,18 +1277,13 @@ hipError_t launch_state(const MfmaK<GT>& k, hipStream_t s) {
     return hipGetLastError();
 }
 
-// Workgroup shape of the state pass.  Few (sequence, head) pairs: spread
-// each head over 8 workgroups of one 16-column slice, so every CU takes
-// part.  Many: one workgroup per quarter head (two slices), so each copied
-// factor serves two slices.  KDA_STATE_SHAPE=1 or 2 in the environment forces
-// the number of slices per workgroup (the tests use it to cover both).
+// Workgroup shape of the state pass, from the problem size alone.  Few
+// (sequence, head) pairs: spread each head over 8 workgroups of one 16-column
+// slice, so every CU takes part.  Many: one workgroup per quarter head (two
+// slices), so each copied factor serves two slices.
 template <typename GT, bool kGate>
 hipError_t launch_state_for(const MfmaK<GT>& k, hipStream_t s, int cus) {
-    int ns = k.groups * 8 <= cus ? 1 : 2;
-    if (const char* env = getenv("KDA_STATE_SHAPE")) {
-        const int f = atoi(env);
-        if (f == 1 || f == 2) ns = f;
-    }
+    const int ns = k.groups * 8 <= cus ? 1 : 2;
     return ns == 1 ? launch_state<GT, kGate, 1>(k, s) : launch_state<GT, kGate, 2>(k, s);
 }
 

@@ -49,9 +49,88 @@ LaunchTimer::~LaunchTimer() {
     if (slot_ >= 0) g_state.pending[slot_].stop_recorded = hipEventRecord(g_state.pending[slot_].stop, stream_) == hipSuccess;
 }
 
+// ---------------------------------------------------------------------------
+// Peak-rate probes: what the matrix cores and HBM sustain on this device,
+// measured beside the published peaks.
+
+typedef __bf16 probe_bf16x8 __attribute__((ext_vector_type(8)));
+typedef float probe_f32x4 __attribute__((ext_vector_type(4)));
+
+// Each wave runs `iters` rounds of four independent matrix-core products
+// (16 x 16 outputs, fp32 accumulators), so the matrix core of every SIMD
+// always has work queued.  Operands depend on the lane so nothing folds; one
+// value per thread is written so nothing is dead.
+__global__ __launch_bounds__(256) void probe_mfma_bf16_kernel(int iters, float* __restrict__ out) {
+    const int t = threadIdx.x;
+    probe_bf16x8 a, b;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        a[e] = static_cast<__bf16>(1.f + 1e-3f * static_cast<float>((t + e) & 7));
+        b[e] = static_cast<__bf16>(1e-3f * static_cast<float>((t * 3 + e) & 15));
+    }
+    probe_f32x4 acc[4] = {};
+    for (int i = 0; i < iters; ++i) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[j], 0, 0, 0);
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s += acc[j][0] + acc[j][1] + acc[j][2] + acc[j][3];
+    out[static_cast<int64_t>(blockIdx.x) * 256 + t] = s;
+}
+
+__global__ __launch_bounds__(256) void probe_mfma_f32_kernel(int iters, float* __restrict__ out) {
+    const int t = threadIdx.x;
+    const float a = 1.f + 1e-3f * static_cast<float>(t & 7), b = 1e-3f * static_cast<float>((t * 3) & 15);
+    probe_f32x4 acc[4] = {};
+    for (int i = 0; i < iters; ++i) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc[j], 0, 0, 0);
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s += acc[j][0] + acc[j][1] + acc[j][2] + acc[j][3];
+    out[static_cast<int64_t>(blockIdx.x) * 256 + t] = s;
+}
+
+// Streaming read of n16 16-byte words (grid-stride), one sum per thread out.
+__global__ __launch_bounds__(256) void probe_read_kernel(const uint4* __restrict__ src, int64_t n16,
+                                                         float* __restrict__ out) {
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
+    uint32_t acc = 0;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n16; i += stride) {
+        const uint4 v = src[i];
+        acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+    out[static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x] = static_cast<float>(acc & 0xffff);
+}
+
 }  // namespace kda
 
 extern "C" {
+
+int kda_probe_peak(int32_t kind, int32_t blocks, int32_t iters, const void* src, int64_t src_bytes, float* out,
+                   void* stream) {
+    if (blocks <= 0 || out == nullptr) return KDA_ERR_INVALID_ARGUMENT;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    kda::LaunchTimer timer(kind == 0 ? "probe_mfma_bf16" : kind == 1 ? "probe_mfma_f32" : "probe_read", s);
+    if (kind == 0 || kind == 1) {
+        if (iters <= 0) return KDA_ERR_INVALID_ARGUMENT;
+        if (kind == 0)
+            hipLaunchKernelGGL(kda::probe_mfma_bf16_kernel, dim3(blocks), dim3(256), 0, s, iters, out);
+        else
+            hipLaunchKernelGGL(kda::probe_mfma_f32_kernel, dim3(blocks), dim3(256), 0, s, iters, out);
+    } else if (kind == 2) {
+        if (src == nullptr || src_bytes <= 0 || src_bytes % 16 != 0 ||
+            reinterpret_cast<uintptr_t>(src) % 16 != 0)
+            return KDA_ERR_INVALID_ARGUMENT;
+        hipLaunchKernelGGL(kda::probe_read_kernel, dim3(blocks), dim3(256), 0, s, static_cast<const uint4*>(src),
+                           src_bytes / 16, out);
+    } else {
+        return KDA_ERR_INVALID_ARGUMENT;
+    }
+    return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
 
 int kda_profile_enable(int on) {
     kda::g_state.on = on != 0;

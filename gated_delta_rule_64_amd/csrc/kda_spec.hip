@@ -169,9 +169,15 @@ __global__ __launch_bounds__(256) void spec_kernel(SpecK<XT> a) {
             }
             if (j >= na) {  // new token: keep its raw values for the next call
                 XT* p = dr + static_cast<int64_t>(j - na) * H * W;
+                // Every element of a draft slot has one owner thread, which
+                // both reads the committed value (first loop) and writes the
+                // new one, so a slot is never rewritten by a thread other
+                // than the one that read it: q / k channel c by thread c, v /
+                // decay channel c by thread 128 + c, and the write logit by
+                // thread 128, the thread that turns it into beta below.
                 if (act0) st(p + d_off0, x0[jb]);
                 if (act1) st(p + d_off1, x1[jb]);
-                if (tid == 0) st(p + 3 * DK + DV, xb[jb]);
+                if (tid == 128) st(p + 3 * DK + DV, xb[jb]);
             }
             if (lower) {
                 const float sk = wave_sum(act1 ? y1 * y1 : 0.f);

@@ -244,3 +244,14 @@ def kda_prefill_backward(q, k, v, log_alpha, beta, dy, out_gate=None, initial_st
                                      _ptr(g["dbeta"]), _ptr(g["dz"]), _ptr(g["dS0"]),
                                      _ptr(workspace), workspace.numel(), _stream(dev)))
     return g
+
+
+def kda_probe_peak(kind, blocks, iters=0, src=None, out=None):
+    """Peak-rate probe (see kda.h): kind 0 bf16 matrix-core loop, 1 fp32
+    matrix-core loop, 2 streaming read of ``src``.  Returns ``out``."""
+    dev = src.device if src is not None else torch.device("cuda")
+    if out is None:
+        out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    nbytes = src.numel() * src.element_size() if src is not None else 0
+    check(lib().kda_probe_peak(kind, blocks, iters, _ptr(src), nbytes, _ptr(out), _stream(dev)))
+    return out

@@ -38,6 +38,11 @@
  *    T_tot >= 0 and below 2^31; sequences of length 0 are allowed.
  *  - Thread safety: no global mutable state; the error text and the optional
  *    kernel-timing records (kda_profile_enable) are per host thread.
+ *  - Types: every call returns a kda_status_t value as a plain int, takes
+ *    each dtype as an int32_t holding a kda_dtype_t value, and takes the
+ *    stream as a void* holding a hipStream_t.  They are the same bits on the
+ *    ABI; plain types keep this header free of the HIP headers, so a caller
+ *    can bind it from any language (the Python binding uses ctypes).
  */
 #ifndef KDA_H
 #define KDA_H
@@ -73,6 +78,12 @@ int kda_abi_version(void);
 
 /*
  * kda_preprocess -- fused short conv, L2 norm and gates for a packed batch.
+ * These are the steps the section "KDA: constant-size memory over a very
+ * long context" of the page "Ling-3.0-flash: a 124B open MoE ..." applies
+ * before the recurrence: q and k through a short causal conv and an L2 norm,
+ * v through a conv, the decay from a softplus gate and the write strength
+ * from a sigmoid (the conv width of 4 is in the "Every architecture field"
+ * table of the page "Ling 3.0 Flash").
  *
  * For every sequence n (tokens cu_seqlens[n] .. cu_seqlens[n+1]-1), head h
  * and channel c:
@@ -118,8 +129,11 @@ size_t kda_prefill_workspace_bytes(int64_t T_tot, int32_t N, int32_t H, int32_t 
 
 /*
  * kda_prefill_chunked -- the recurrence over a packed batch of preprocessed
- * tokens, in chunks of 64 tokens.  The result is that of the token-by-token
- * recurrence above (chunking changes only rounding): within a chunk the
+ * tokens, in chunks of 64 tokens.  The recurrence is the constant-size state
+ * update and query read of the section "KDA: constant-size memory over a very
+ * long context" of the page "Ling-3.0-flash: a 124B open MoE ...", with the
+ * sigmoid output gate of the same section.  The result is that of the
+ * token-by-token recurrence above (chunking changes only rounding): within a chunk the
  * writes are collected into a WY-style form (a unit-lower-triangular solve
  * over the chunk's keys) and the fp32 state is carried across chunks in
  * order, per sequence and head.
@@ -263,7 +277,11 @@ int kda_prefill_backward(int64_t T_tot, int32_t H, int32_t dk, int32_t dv,
                          void* stream);
 
 /*
- * kda_decode_step -- one token per sequence, state updated in place.
+ * kda_decode_step -- one token per sequence, state updated in place: the
+ * decode-time form of the recurrence of the section "KDA: constant-size
+ * memory over a very long context" of the page "Ling-3.0-flash: a 124B open
+ * MoE ..." (each new token costs the same fixed state read and write,
+ * whatever the context length).
  * For each (b, h):  S' = Diag(alpha) S;  u = S'^T k;  S <- S' + beta k (v - u)^T;
  *                   o = S^T q;  out = o * sigmoid(z) (or o without a gate).
  * The state is read once and written once.
@@ -399,6 +417,24 @@ typedef struct kda_kernel_time {
 
 int kda_profile_enable(int on);
 int kda_profile_collect(kda_kernel_time_t* out, int max_entries);
+
+/*
+ * Peak-rate probes for measurement tools (not part of the token mixer): what
+ * this device sustains, to report beside the published peaks.  Launches
+ * `blocks` workgroups of 256 threads on `stream`:
+ *   kind 0  each wave issues iters x 4 bf16 matrix-core products of
+ *           16 x 16 x 32 (16,384 flops each): blocks * 4 * iters * 4 * 16384
+ *           flops in all;
+ *   kind 1  the same with fp32 products of 16 x 16 x 4 (2,048 flops each);
+ *   kind 2  reads src_bytes (a multiple of 16, 16-byte aligned device memory
+ *           at src) once, grid-stride.
+ * out: device fp32 [blocks * 256], written (a checksum per thread).  Returns
+ * KDA_ERR_INVALID_ARGUMENT for bad arguments.  The launch is timed by
+ * kda_profile_enable like any kernel of the library ("probe_mfma_bf16",
+ * "probe_mfma_f32", "probe_read").
+ */
+int kda_probe_peak(int32_t kind, int32_t blocks, int32_t iters, const void* src, int64_t src_bytes,
+                   float* out, void* stream);
 
 #ifdef __cplusplus
 }

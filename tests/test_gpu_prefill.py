@@ -124,25 +124,35 @@ def test_stress_cases(K, oracle_mod, case):
 
 
 @pytest.mark.parametrize("gate", [True, False])
-def test_state_workgroup_shapes_agree(K, oracle_mod, monkeypatch, gate):
+def test_state_workgroup_shapes_agree(K, oracle_mod, gate):
     """The state pass runs one or two 16-column slices (a chain wave and an
-    output wave each) per workgroup, chosen by problem size; KDA_STATE_SHAPE
-    forces one.
-    Each slice does the same arithmetic in the same order, so both shapes
-    give bit-identical results, and each matches the oracle."""
-    inp = synth.make("varlen_64", lengths=(130, 0, 64, 1, 700), H=3)
-    if not gate:
-        inp["z"] = None
+    output wave each) per workgroup, chosen by problem size alone: one while
+    8 * N * H fits the CUs, two beyond.  The same five sequences run once on
+    their own (3 heads: one slice per workgroup) and once followed by seven
+    more sequences (12 x 3 groups: two slices per workgroup).  Each slice does
+    the same arithmetic in the same order, and a sequence's outputs depend
+    only on its own tokens, so the five sequences' outputs and states are
+    bit-identical between the two runs, and each matches the oracle."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    small = (130, 0, 64, 1, 700)
+    extra = (90, 65, 3, 128, 40, 200, 77)
+    H = 3
+    assert 8 * len(small) * H <= cus < 8 * (len(small) + len(extra)) * H
     res = {}
-    for shape in ("1", "2"):
-        monkeypatch.setenv("KDA_STATE_SHAPE", shape)
-        print(f"state shape {shape}, gate {gate}", flush=True)
-        res[shape] = gpu_layer(K, inp)
-    ref = oracle_mod.layer(oracle_layer_inputs(inp))
-    for shape, (out, S) in res.items():
-        assert_close(f"y (shape {shape})", to_host64(out), ref["y"], TOL["bf16"])
-        assert_close(f"state (shape {shape})", to_host64(S), ref["S"], TOL["bf16"])
-    assert torch.equal(res["2"][0], res["1"][0]) and torch.equal(res["2"][1], res["1"][1])
+    for name, lengths in (("one slice", small), ("two slices", small + extra)):
+        inp = synth.make("varlen_64", lengths=lengths, H=H)
+        if not gate:
+            inp["z"] = None
+        print(f"state pass, {name} per workgroup, gate {gate}", flush=True)
+        out, S = gpu_layer(K, inp)
+        ref = oracle_mod.layer(oracle_layer_inputs(inp))
+        assert_close(f"y ({name})", to_host64(out), ref["y"], TOL["bf16"])
+        assert_close(f"state ({name})", to_host64(S), ref["S"], TOL["bf16"])
+        res[name] = (out, S)
+    t_small = sum(small)
+    out1, S1 = res["one slice"]
+    out2, S2 = res["two slices"]
+    assert torch.equal(out2[:t_small], out1) and torch.equal(S2[:len(small)], S1)
 
 
 def test_debug_check_rejects_bad_cu_seqlens(monkeypatch):
