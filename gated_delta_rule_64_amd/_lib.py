@@ -18,6 +18,7 @@ KDA_ERR_INVALID_ARGUMENT = 1
 KDA_ERR_UNSUPPORTED = 2
 KDA_ERR_WORKSPACE_TOO_SMALL = 3
 KDA_ERR_HIP = 4
+KDA_NOALLOC_SCRATCH_BYTES = 64 << 20  # mirrors kda.h
 KDA_F32 = 0
 KDA_BF16 = 1
 
@@ -34,6 +35,8 @@ PROTOTYPES = {
     "kda_decode_step": (ctypes.c_int, [_i32, _i32, _i32, _i32, _i32, _i32] + [_vp] * 6 + [_vp, _vp, _vp]),
     "kda_prefill_layer": (ctypes.c_int, [_i64, _i32, _i32, _i32, _vp, _i32, _i32] + [_vp] * 8 +
                           [_vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "kda_prefill_layer_noalloc": (ctypes.c_int, [_i64, _i32, _i32, _i32, _vp, _i32, _i32] + [_vp] * 8 +
+                                  [_vp, _vp, _vp, _vp, _vp, _vp]),
     "kda_decode_layer": (ctypes.c_int, [_i32, _i32, _i32, _i32, _i32] + [_vp] * 8 + [_vp, _vp, _vp, _i32, _vp, _vp, _vp]),
     "kda_spec_draft_bytes": (_sz, [_i32, _i32, _i32, _i32]),
     "kda_backward_workspace_bytes": (_sz, [_i64, _i32, _i32, _i32, _i32]),

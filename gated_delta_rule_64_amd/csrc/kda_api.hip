@@ -4,6 +4,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "kda.h"
@@ -588,6 +589,74 @@ int kda_prefill_backward(int64_t T_tot, int32_t H, int32_t dk, int32_t dv, const
     hipError_t e = kda::launch_backward(b, s);
     if (e != hipSuccess) return hip_fail(e, "backward launch");
     return ok();
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// kda_prefill_layer_noalloc: the layer prefill with its workspace in a fixed
+// device array instead of caller memory.  Each GPU the library runs on holds
+// its own copy of the array until the process ends; every call on that GPU
+// shares it (the last call's contents stay; nothing in it needs to start at
+// zero, since every record is written before it is read).  Calls that overlap
+// on one GPU race on it.
+static __device__ __align__(256) char scratch[KDA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};  // device address of `scratch` per device ordinal
+
+// The current device's copy of `scratch`.  In host code the array's name is a
+// host-side stand-in, not a device address, so its device address is looked
+// up once per device, with that device current, and only that pointer ever
+// reaches a kernel.
+int noalloc_scratch(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(KDA_ERR_UNSUPPORTED, "device ordinal %d: the no-allocation scratch is kept for devices 0..%d",
+                    dev, kMaxDevices - 1);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_dev[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress of the no-allocation scratch");
+        if (p == nullptr || (reinterpret_cast<uintptr_t>(p) & 255u) != 0)
+            return fail(KDA_ERR_HIP, "the no-allocation scratch has no 256-byte aligned device address");
+        g_scratch_dev[dev] = p;
+    }
+    *out = g_scratch_dev[dev];
+    return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_prefill_layer_noalloc(int64_t T_tot, int32_t H, int32_t dk, int32_t dv, const int32_t* cu_seqlens,
+                              int32_t N, int32_t x_dtype, const void* q_in, const void* k_in, const void* v_in,
+                              const void* w_q, const void* w_k, const void* w_v, const void* g_alpha,
+                              const void* b_beta, float* conv_state, const void* out_gate,
+                              const float* initial_state, float* final_state, void* out, void* stream) {
+    // the size limit first, before any device work
+    int st = check_sizes(T_tot, H, dk, dv, N);
+    if (st != KDA_OK) return st;
+    if (!valid_dtype(x_dtype)) return fail(KDA_ERR_INVALID_ARGUMENT, "x_dtype=%d is not KDA_F32 or KDA_BF16", x_dtype);
+    const size_t need = kda_prefill_workspace_bytes(T_tot, N, H, dk, dv, x_dtype);
+    if (need > static_cast<size_t>(KDA_NOALLOC_SCRATCH_BYTES))
+        return fail(KDA_ERR_WORKSPACE_TOO_SMALL,
+                    "kda_prefill_layer_noalloc: T_tot=%lld, N=%d, H=%d need %zu bytes of scratch, more than its "
+                    "fixed %zu; use kda_prefill_layer with a workspace",
+                    static_cast<long long>(T_tot), N, H, need, static_cast<size_t>(KDA_NOALLOC_SCRATCH_BYTES));
+    void* ws = nullptr;
+    st = noalloc_scratch(&ws);
+    if (st != KDA_OK) return st;
+    return prefill_layer_impl(T_tot, H, dk, dv, cu_seqlens, N, x_dtype, q_in, k_in, v_in, w_q, w_k, w_v, g_alpha,
+                              b_beta, conv_state, out_gate, initial_state, final_state, out, ws,
+                              static_cast<size_t>(KDA_NOALLOC_SCRATCH_BYTES), stream, nullptr);
 }
 
 }  // extern "C"

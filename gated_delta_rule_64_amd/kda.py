@@ -166,6 +166,26 @@ def kda_prefill_layer(q_in, k_in, v_in, w_q, w_k, w_v, g_alpha, b_beta, H, dk, d
     return out, final_state, snapshots, snap_offsets
 
 
+def kda_prefill_layer_noalloc(q_in, k_in, v_in, w_q, w_k, w_v, g_alpha, b_beta, H, dk, dv, out_gate=None,
+                              initial_state=None, final_state=None, cu_seqlens=None, conv_state=None, out=None,
+                              want_final_state=True):
+    """kda_prefill_layer without a workspace: the library's fixed scratch
+    (KDA_NOALLOC_SCRATCH_BYTES per GPU) holds it.  Returns (out, final_state)."""
+    T = q_in.shape[0]
+    N = _n_seqs(cu_seqlens)
+    x = _dtype_code(q_in)
+    dev = q_in.device
+    if out is None:
+        out = torch.empty((T, H, dv), dtype=q_in.dtype, device=dev)
+    if final_state is None and want_final_state:
+        final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    check(lib().kda_prefill_layer_noalloc(T, H, dk, dv, _ptr(cu_seqlens), N, x,
+                                          _ptr(q_in), _ptr(k_in), _ptr(v_in), _ptr(w_q), _ptr(w_k), _ptr(w_v),
+                                          _ptr(g_alpha), _ptr(b_beta), _ptr(conv_state), _ptr(out_gate),
+                                          _ptr(initial_state), _ptr(final_state), _ptr(out), _stream(dev)))
+    return out, final_state
+
+
 def kda_decode_layer(q_in, k_in, v_in, w_q, w_k, w_v, g_alpha, b_beta, H, dk, dv, conv_state, state,
                      out_gate=None, state_indices=None, out=None):
     """One raw token per sequence through preprocess + decode step in one call.

@@ -191,6 +191,38 @@ int kda_prefill_layer(int64_t T_tot, int32_t H, int32_t dk, int32_t dv,
                       void* stream);
 
 /*
+ * kda_prefill_layer_noalloc -- kda_prefill_layer for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops
+ * and harnesses that forbid allocation.  Same computation, arguments and
+ * errors as kda_prefill_layer, without the workspace: the call uses a fixed
+ * scratch array of KDA_NOALLOC_SCRATCH_BYTES inside the library instead, and
+ * allocates nothing (no hipMalloc, hipFree or allocating routine).
+ *  - Each GPU the library runs on holds its own copy of the array, from the
+ *    library's load until the process ends.  The first call on a device
+ *    looks the copy up (no allocation); a caller that captures graphs can
+ *    make that first call before capturing (T_tot = 0 is enough).
+ *  - Sizes whose kda_prefill_workspace_bytes() exceeds
+ *    KDA_NOALLOC_SCRATCH_BYTES are rejected with KDA_ERR_WORKSPACE_TOO_SMALL
+ *    before any device work (at H = 32, d = 128, one sequence fits up to
+ *    1,536 tokens).
+ *  - Every call on one GPU shares that GPU's array, which keeps the last
+ *    call's contents (nothing in it needs to start at zero).  Calls that
+ *    overlap on one GPU (two host threads, or two streams) race on it and
+ *    give undefined results: serialise them.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES (64u << 20)
+int kda_prefill_layer_noalloc(int64_t T_tot, int32_t H, int32_t dk, int32_t dv,
+                              const int32_t* cu_seqlens, int32_t N, int32_t x_dtype,
+                              const void* q_in, const void* k_in, const void* v_in,
+                              const void* w_q, const void* w_k, const void* w_v,
+                              const void* g_alpha, const void* b_beta,
+                              float* conv_state,
+                              const void* out_gate,
+                              const float* initial_state, float* final_state,
+                              void* out,
+                              void* stream);
+
+/*
  * State snapshots for prefix reuse: kda_prefill_chunked_snap and
  * kda_prefill_layer_snap are kda_prefill_chunked and kda_prefill_layer that
  * also write the state of each sequence after every snap_interval tokens
