@@ -65,6 +65,12 @@ constexpr int GS = 132;  // fp32 per row of G
 constexpr int MS = 68;   // fp32 per row of A, M and T (16 lanes reading 16 rows hit distinct banks)
 constexpr int SQS = 136; // bf16 per row of the Q' staging tile (the same bytes per row as A)
 constexpr float kDiagRange = 40.f * kLog2e;  // e^40, in the log2 units G is kept in
+// Largest decay over a chunk (log2 units, per channel) for which the chunk's
+// operands are scaled against one reference per channel, the midpoint of the
+// channel's range: every factor then stays within 2^+-100, far inside the
+// bf16 and fp32 exponent range.  Steeper chunks take the exact tile path.
+constexpr float kFastRange = 200.f;
+constexpr int TBS = 72;  // bf16 per row of the T Diag(beta) and M operand copies (16 lanes, 16 rows: distinct banks)
 
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -120,7 +126,9 @@ struct MfmaK {
 // ---------------------------------------------------------------------------
 
 constexpr int kIntraThreads = 512;  // 8 waves: two per SIMD
-constexpr size_t kIntraLds = (3 * 64 * KS) * 2 + (64 * GS + 3 * 64 * MS + 64 + 16 * 128) * 4 + 16;
+constexpr size_t kIntraLds = (3 * 64 * KS) * 2 + (64 * GS + 3 * 64 * MS + 64 + 16 * 128) * 4 + 32;
+static_assert(64 * KS * 2 + 64 * TBS * 2 <= 64 * GS * 4, "K^ and the M operand copy share the space of G");
+static_assert(64 * TBS * 2 <= 64 * MS * 4, "the T Diag(beta) operand copy takes the space of A");
 
 __device__ __forceinline__ void unpack8(uint4 v, float (&x)[8]) {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
@@ -233,7 +241,18 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
     float* sT = sM + 64 * MS;                           // [64][MS]
     float* sB = sT + 64 * MS;                           // [64] beta
     float* sTot = sB + 64;                              // [16][128] scan partials, later scratch
-    int* sFlag = reinterpret_cast<int*>(sTot + 16 * 128);
+    int* sFlag = reinterpret_cast<int*>(sTot + 16 * 128);  // [0..3] steep diagonal blocks, [4] steep chunk
+    // Per channel, from the operand preparation to the end of the unit (in the
+    // part of sTot that the T solve's scratch leaves free): the references
+    // the key and query operands are scaled against, and G of the last row.
+    float* sRefL = sTot + 1536;
+    float* sRefR = sTot + 1664;
+    float* sGl = sTot + 1792;
+    // After the operand preparation: K^ scaled against refR (the space of G),
+    // and after the T solve the bf16 operand copies of M and T Diag(beta).
+    uint16_t* sKr = reinterpret_cast<uint16_t*>(sG);  // [64][KS]
+    uint16_t* sMb = sKr + 64 * KS;                     // [64][TBS]
+    uint16_t* sTb = reinterpret_cast<uint16_t*>(sA);   // [64][TBS]
     uint16_t* sStW = sV;                                // staging of -W  [64][KS]
     uint16_t* sStQ = reinterpret_cast<uint16_t*>(sA);   // staging of Q'  [64][SQS]
 
@@ -495,7 +514,7 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
             const int bt = tid & 63;  // every wave writes the same 64 values
             sB[bt] = bt < L ? (kFused ? sigmoid_fast(bv) : bv) : 0.f;
         }
-        if (tid < 4) sFlag[tid] = 0;
+        if (tid < 5) sFlag[tid] = 0;
         for (int i = tid; i < 2 * 64 * MS / 4; i += kIntraThreads)
             reinterpret_cast<float4*>(sA)[i] = make_float4(0.f, 0.f, 0.f, 0.f);  // sA, sM
 #pragma unroll
@@ -542,23 +561,152 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
             }
         }
         lds_barrier();
-        // sub-blocks whose decay inside 16 tokens is too steep for the factored form
+        // Decay ranges: a chunk whose decay over its 64 tokens stays within
+        // kFastRange in every channel scales its operands against one
+        // reference per channel; a steeper one takes the exact tile path, for
+        // which the flags also mark the 16-token sub-blocks too steep for its
+        // factored form.
         if (tid < 128) {
 #pragma unroll
             for (int R = 0; R < 4; ++R) {
                 const float d = sG[(16 * R) * GS + tid] - sG[(16 * R + 15) * GS + tid];
                 if (d > kDiagRange) sFlag[R] = 1;  // benign race: every writer stores 1
             }
+            if (sG[tid] - sG[63 * GS + tid] > kFastRange) sFlag[4] = 1;
         }
         lds_barrier();
+        const bool steep = __builtin_amdgcn_readfirstlane(sFlag[4]) != 0;
+
+        // The bf16 matrix-core operands of the chunk, once for every product:
+        //   Kl = e^{G - refL} K,  Ql = e^{G - refL} Q  (in place of K and Q),
+        //   Kr = e^{refR - G} K                       (in the space of G).
+        // Then A_rs = sum_c Kl_rc Kr_sc e^{refL_c - refR_c}, and every other
+        // factor follows with a per-channel scale: e^G K = Kl 2^{refL},
+        // e^G Q = Ql 2^{refL}, K^ = Kr 2^{G_last - refR}.  refL = refR = the
+        // midpoint of the channel's range normally (so Kl Kr^T gives A
+        // directly); refL = 0, refR = G_last on the steep path (every factor
+        // <= 1, no overflow), which computes A and M from K, Q and G first.
+        auto prep = [&](bool mid) {
+            const int cg8 = 8 * (tid & 15), r0 = tid >> 4;  // channels cg8 .. + 7 of rows r0 and r0 + 32
+            float g0[8], gl[8], rl[8], rr[8];
+            lds8f(sG + cg8, g0);
+            lds8f(sG + 63 * GS + cg8, gl);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                rl[e] = mid ? 0.5f * (g0[e] + gl[e]) : 0.f;
+                rr[e] = mid ? rl[e] : gl[e];
+            }
+            uint4 kraw[2], qraw[2];
+            float gv[2][8];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int r = r0 + 32 * i;
+                kraw[i] = *reinterpret_cast<const uint4*>(sK + r * KS + cg8);
+                qraw[i] = *reinterpret_cast<const uint4*>(sQ + r * KS + cg8);
+                lds8f(sG + r * GS + cg8, gv[i]);
+            }
+            lds_barrier();  // every thread holds its K, Q and G: the operands may overwrite them
+            if (r0 == 0) {
+                *reinterpret_cast<float4*>(sRefL + cg8) = make_float4(rl[0], rl[1], rl[2], rl[3]);
+                *reinterpret_cast<float4*>(sRefL + cg8 + 4) = make_float4(rl[4], rl[5], rl[6], rl[7]);
+                *reinterpret_cast<float4*>(sRefR + cg8) = make_float4(rr[0], rr[1], rr[2], rr[3]);
+                *reinterpret_cast<float4*>(sRefR + cg8 + 4) = make_float4(rr[4], rr[5], rr[6], rr[7]);
+                *reinterpret_cast<float4*>(sGl + cg8) = make_float4(gl[0], gl[1], gl[2], gl[3]);
+                *reinterpret_cast<float4*>(sGl + cg8 + 4) = make_float4(gl[4], gl[5], gl[6], gl[7]);
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int r = r0 + 32 * i;
+                float k8[8], q8[8], kl[8], ql[8], kr[8];
+                unpack8(kraw[i], k8);
+                unpack8(qraw[i], q8);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float el = __builtin_amdgcn_exp2f(gv[i][e] - rl[e]);
+                    const float er = __builtin_amdgcn_exp2f(rr[e] - gv[i][e]);
+                    kl[e] = k8[e] * el;
+                    ql[e] = q8[e] * el;
+                    kr[e] = k8[e] * er;
+                }
+                *reinterpret_cast<uint4*>(sK + r * KS + cg8) =
+                    make_uint4(pack_bf16x2(kl[0], kl[1]), pack_bf16x2(kl[2], kl[3]), pack_bf16x2(kl[4], kl[5]),
+                               pack_bf16x2(kl[6], kl[7]));
+                *reinterpret_cast<uint4*>(sQ + r * KS + cg8) =
+                    make_uint4(pack_bf16x2(ql[0], ql[1]), pack_bf16x2(ql[2], ql[3]), pack_bf16x2(ql[4], ql[5]),
+                               pack_bf16x2(ql[6], ql[7]));
+                *reinterpret_cast<uint4*>(sKr + r * KS + cg8) =
+                    make_uint4(pack_bf16x2(kr[0], kr[1]), pack_bf16x2(kr[2], kr[3]), pack_bf16x2(kr[4], kr[5]),
+                               pack_bf16x2(kr[6], kr[7]));
+            }
+        };
 
         // ---- A and M: 10 tiles (R >= S) of 4 contraction steps each.  Wave w
         // computes tile w whole; the steps of tiles 8 and 9 go one per wave
         // (tile 8 + w/4, step w%4), and their partial tiles are summed in a fixed
         // order afterwards, so the result does not depend on timing.
-        {
-            // A and M partials of tile (R, S) over contraction steps [k0, k1)
-            auto tile_part = [&](int R, int S, int k0, int k1, f32x4& accA, f32x4& accM) {
+            auto store_tile = [&](int R, int S, const f32x4& accA, const f32x4& accM) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 16 * R + 4 * g + i, s2 = 16 * S + c;
+                    sA[r * MS + s2] = s2 < r ? accA[i] : 0.f;
+                    sM[r * MS + s2] = s2 <= r ? accM[i] : 0.f;
+                }
+            };
+        auto am_tiles = [&](auto&& part) {
+            int R, S;
+            f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accM = accA;
+            tile_rs(wave, R, S);
+            part(R, S, 0, 4, accA, accM);
+            store_tile(R, S, accA, accM);
+            // one step of tile 8 or 9 into a partial block in sT (free until T is built)
+            const int tp = 8 + (wave >> 2), kp = wave & 3;
+            tile_rs(tp, R, S);
+            accA = f32x4{0.f, 0.f, 0.f, 0.f};
+            accM = accA;
+            part(R, S, kp, kp + 1, accA, accM);
+            float* pt = sT + wave * 512;  // [A: 4 x 64 lanes][M: 4 x 64 lanes]
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                pt[i * 64 + lane] = accA[i];
+                pt[256 + i * 64 + lane] = accM[i];
+            }
+            lds_barrier();
+            if (wave < 2) {  // wave 0 sums tile 8, wave 1 tile 9, steps in order
+                tile_rs(8 + wave, R, S);
+                f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sm = sa;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const float* q = sT + (4 * wave + k) * 512;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        sa[i] += q[i * 64 + lane];
+                        sm[i] += q[256 + i * 64 + lane];
+                    }
+                }
+                store_tile(R, S, sa, sm);
+            }
+        };
+        if (!steep) {
+            prep(true);
+            lds_barrier();
+            // A and M are plain products of the prepared operands: Kl and Ql
+            // rows of block R against Kr rows of block S.  (Above the
+            // diagonal the products may overflow; those entries are masked.)
+            am_tiles([&](int R, int S, int k0, int k1, f32x4& accA, f32x4& accM) {
+                const int rl = 16 * R + c, sr = 16 * S + c;
+                for (int ks = k0; ks < k1; ++ks) {
+                    const int ch0 = 32 * ks + 8 * g;
+                    const bf16x8 kl = *reinterpret_cast<const bf16x8*>(sK + rl * KS + ch0);
+                    const bf16x8 ql = *reinterpret_cast<const bf16x8*>(sQ + rl * KS + ch0);
+                    const bf16x8 kr = *reinterpret_cast<const bf16x8*>(sKr + sr * KS + ch0);
+                    accA = mfma(kl, kr, accA);
+                    accM = mfma(ql, kr, accM);
+                }
+            });
+        } else {
+            // exact tile path: factored decays referenced to each row block's
+            // first token, pairwise decays on steep diagonal blocks
+            am_tiles([&](int R, int S, int k0, int k1, f32x4& accA, f32x4& accM) {
                 const int b = 16 * R;
                 if (R == S && sFlag[R]) {
                     // exact pairwise decays (steep decay inside the block)
@@ -599,47 +747,9 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
                         accM = mfma(to_bf16x8(ql), bk, accM);
                     }
                 }
-            };
-            auto store_tile = [&](int R, int S, const f32x4& accA, const f32x4& accM) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = 16 * R + 4 * g + i, s2 = 16 * S + c;
-                    sA[r * MS + s2] = s2 < r ? accA[i] : 0.f;
-                    sM[r * MS + s2] = s2 <= r ? accM[i] : 0.f;
-                }
-            };
-            int R, S;
-            f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accM = accA;
-            tile_rs(wave, R, S);
-            tile_part(R, S, 0, 4, accA, accM);
-            store_tile(R, S, accA, accM);
-            // one step of tile 8 or 9 into a partial block in sT (free until T is built)
-            const int tp = 8 + (wave >> 2), kp = wave & 3;
-            tile_rs(tp, R, S);
-            accA = f32x4{0.f, 0.f, 0.f, 0.f};
-            accM = accA;
-            tile_part(R, S, kp, kp + 1, accA, accM);
-            float* part = sT + wave * 512;  // [A: 4 x 64 lanes][M: 4 x 64 lanes]
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                part[i * 64 + lane] = accA[i];
-                part[256 + i * 64 + lane] = accM[i];
-            }
+            });
             lds_barrier();
-            if (wave < 2) {  // wave 0 sums tile 8, wave 1 tile 9, steps in order
-                tile_rs(8 + wave, R, S);
-                f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sm = sa;
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const float* q = sT + (4 * wave + k) * 512;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        sa[i] += q[i * 64 + lane];
-                        sm[i] += q[256 + i * 64 + lane];
-                    }
-                }
-                store_tile(R, S, sa, sm);
-            }
+            prep(false);
         }
         lds_barrier();
 
@@ -735,24 +845,43 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
         lds_barrier();
         // blocks of T above the diagonal are never written; every reader masks them
 
+        // T Diag(beta) and M as bf16 matrix-core operands, once for all waves
+        // (zero above the diagonal): row r = tid / 8, columns 8 (tid % 8) .. + 7
+        {
+            const int r = tid >> 3, c0 = 8 * (tid & 7);
+            float t8[8], m8[8], b8[8], tv[8], mv[8];
+            lds8f(sT + r * MS + c0, t8);
+            lds8f(sM + r * MS + c0, m8);
+            lds8f(sB + c0, b8);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                tv[e] = c0 + e <= r ? t8[e] * b8[e] : 0.f;
+                mv[e] = c0 + e <= r ? m8[e] : 0.f;
+            }
+            *reinterpret_cast<uint4*>(sTb + r * TBS + c0) =
+                make_uint4(pack_bf16x2(tv[0], tv[1]), pack_bf16x2(tv[2], tv[3]), pack_bf16x2(tv[4], tv[5]),
+                           pack_bf16x2(tv[6], tv[7]));
+            *reinterpret_cast<uint4*>(sMb + r * TBS + c0) =
+                make_uint4(pack_bf16x2(mv[0], mv[1]), pack_bf16x2(mv[2], mv[3]), pack_bf16x2(mv[4], mv[5]),
+                           pack_bf16x2(mv[6], mv[7]));
+        }
+        lds_barrier();
+
         if (more) fetch(nxt, 2);
-        // ---- W = T (beta e^G K) and U~ = T (beta V): column tile nt = wave
+        // ---- W = T Diag(beta) e^G K and U~ = T Diag(beta) V: column tile nt = wave.
+        // The key operand is Kl = e^{G - refL} K, so W = (T Diag(beta) Kl) 2^{refL}
+        // column by column.
         const int nt = wave;
         const int chn = 16 * nt + c;
+        const float sl = __builtin_amdgcn_exp2f(sRefL[chn]);  // 2^{refL} of channel chn
         f32x4 accW[4], accU[4];
         {
             bf16x8 Ta[4][2];
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    const int row = 16 * mt + c, col0 = 32 * ks + 8 * g;
-                    float tv[8];
-                    lds8f(sT + row * MS + col0, tv);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) tv[e] = col0 + e <= row ? tv[e] : 0.f;
-                    Ta[mt][ks] = to_bf16x8(tv);
-                }
+                for (int ks = 0; ks < 2; ++ks)
+                    Ta[mt][ks] = *reinterpret_cast<const bf16x8*>(sTb + (16 * mt + c) * TBS + 32 * ks + 8 * g);
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
                 accW[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -761,15 +890,12 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
                 const int s0 = 32 * ks + 8 * g;
-                float bt[8], bk[8], bv[8];
-                lds8f(sB + s0, bt);
+                bf16x8 Bk, Bv;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const int s2 = s0 + e;
-                    bk[e] = bt[e] * __builtin_amdgcn_exp2f(sG[s2 * GS + chn]) * bfv(sK + s2 * KS + chn);
-                    bv[e] = bt[e] * bfv(sV + s2 * KS + chn);
+                    Bk[e] = __builtin_bit_cast(__bf16, sK[(s0 + e) * KS + chn]);
+                    Bv[e] = __builtin_bit_cast(__bf16, sV[(s0 + e) * KS + chn]);
                 }
-                const bf16x8 Bk = to_bf16x8(bk), Bv = to_bf16x8(bv);
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt) {
                     if (32 * ks > 16 * mt + 15) continue;  // T is lower triangular
@@ -777,6 +903,10 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
                     accU[mt] = mfma(Ta[mt][ks], Bv, accU[mt]);
                 }
             }
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) accW[mt][i] *= sl;
             // U~ in result layout, slice nt
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
@@ -786,30 +916,28 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
                 rec_store8(rec + R_UT + ((nt * 4 + mt) * 64 + lane) * 8, p);
             }
         }
-        lds_barrier();  // V and A are dead: their buffers become the staging areas
+        lds_barrier();  // V and T Diag(beta) are dead: their buffers become the staging areas
 
         if (more) fetch(nxt, 3);
-        // ---- Q' = e^G Q - M W and M U~; stage -W and Q' for the transposes
+        // ---- Q' = e^G Q - M W and M U~; stage -W and Q' for the transposes.
+        // The query operand is Ql = e^{G - refL} Q, so e^G Q = Ql 2^{refL}.
         {
-            bf16x8 Mneg[4][2], Mpos[4][2];
+            // M in the A-operand layout with the permuted contraction index
+            // (4 g + e, 16 + 4 g + e), the layout of the W and U~ result pairs
+            bf16x8 Mb[4][2];
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
-                    const float* mrow = sM + (16 * mt + c) * MS + 32 * ks + 4 * g;
-                    const float4 lo = *reinterpret_cast<const float4*>(mrow);
-                    const float4 hi = *reinterpret_cast<const float4*>(mrow + 16);
-                    const float mv[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-                    float mn[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) mn[e] = -mv[e];
-                    Mpos[mt][ks] = to_bf16x8(mv);
-                    Mneg[mt][ks] = to_bf16x8(mn);
+                    const uint16_t* mrow = sMb + (16 * mt + c) * TBS + 32 * ks + 4 * g;
+                    const uint2 lo = *reinterpret_cast<const uint2*>(mrow);
+                    const uint2 hi = *reinterpret_cast<const uint2*>(mrow + 16);
+                    Mb[mt][ks] = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
                 }
-            bf16x8 Bw[2], Bu[2];
+            bf16x8 Bwn[2], Bu[2];
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                Bw[ks] = to_bf16x8(accW[2 * ks], accW[2 * ks + 1]);
+                Bwn[ks] = to_bf16x8(-accW[2 * ks], -accW[2 * ks + 1]);
                 Bu[ks] = to_bf16x8(accU[2 * ks], accU[2 * ks + 1]);
             }
 #pragma unroll
@@ -818,15 +946,15 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int r = 16 * mt + 4 * g + i;
-                    qp[i] = __builtin_amdgcn_exp2f(sG[r * GS + chn]) * bfv(sQ + r * KS + chn);
+                    qp[i] = sl * bfv(sQ + r * KS + chn);
                 }
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
                     if (32 * ks > 16 * mt + 15) continue;  // M is lower triangular
-                    qp = mfma(Mneg[mt][ks], Bw[ks], qp);
+                    qp = mfma(Mb[mt][ks], Bwn[ks], qp);
                     // (M U~)^T = U~^T M^T: the operands swap roles, so lane (g, c)
                     // ends up with M U~[16mt + c][16nt + 4g + i]
-                    oi = mfma(Bu[ks], Mpos[mt][ks], oi);
+                    oi = mfma(Bu[ks], Mb[mt][ks], oi);
                 }
                 uint2 p;
                 p.x = pack_bf16x2(oi[0], oi[1]);
@@ -858,16 +986,17 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
                 rec_store16(rec + R_NEGW + blk * 16, make_uint4(wlo.x, wlo.y, whi.x, whi.y));
                 rec_store16(rec + R_QP + blk * 16, make_uint4(qlo.x, qlo.y, qhi.x, qhi.y));
             }
+            // K^ = Kr 2^{G_last - refR}
             const int t = wave;
             const int ch = 16 * t + c;
-            const float glast = sG[63 * GS + ch];
+            const float sk = __builtin_amdgcn_exp2f(sGl[ch] - sRefR[ch]);
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
                 float kv[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const int s2 = 32 * ks + perm(g, e);
-                    kv[e] = __builtin_amdgcn_exp2f(glast - sG[s2 * GS + ch]) * bfv(sK + s2 * KS + ch);
+                    kv[e] = sk * bfv(sKr + s2 * KS + ch);
                 }
                 uint4 p;
                 p.x = pack_bf16x2(kv[0], kv[1]);
@@ -876,7 +1005,7 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
                 p.w = pack_bf16x2(kv[6], kv[7]);
                 rec_store16(rec + R_KHT + ((t * 2 + ks) * 64 + lane) * 16, p);
             }
-            if (tid < 128) reinterpret_cast<float*>(rec + R_GAM)[tid] = exp2f(sG[63 * GS + tid]);
+            if (tid < 128) reinterpret_cast<float*>(rec + R_GAM)[tid] = exp2f(sGl[tid]);
         }
         lds_barrier();  // every LDS buffer is free for the next unit
         // Leave before staging rather than staging conditionally: the loop's

@@ -13,6 +13,26 @@ from kda_helpers import TOL, assert_close, f64, oracle_layer_inputs, to_dev, to_
 pytestmark = pytest.mark.gpu
 
 
+def chunk_decay_split(inp, limit=200.0):
+    """How many (chunk, head) units have a decay range over their tokens of
+    at most ``limit`` (log2 units, largest over the key channels), and how
+    many more: the decay logs come from the oracle's own definition,
+    log alpha = -softplus(g), on the host.  Chunks start at each sequence's
+    first token; the range of a chunk is G(first row) - G(last row)."""
+    H, dk = inp["H"], inp["dk"]
+    g = synth.to_f64(inp["g"]).reshape(-1, H, dk)
+    la2 = -np.logaddexp(0.0, g) / np.log(2.0)
+    cu = inp["cu_seqlens"]
+    fast = steep = 0
+    for n in range(len(cu) - 1):
+        for t0 in range(int(cu[n]), int(cu[n + 1]), 64):
+            t1 = min(t0 + 64, int(cu[n + 1]))
+            rng = -la2[t0 + 1:t1].sum(axis=0).max(axis=1)  # per head
+            steep += int((rng > limit).sum())
+            fast += int((rng <= limit).sum())
+    return fast, steep
+
+
 @pytest.fixture(scope="module")
 def K():
     from gated_delta_rule_64_amd import kda
@@ -149,11 +169,20 @@ def test_layer_sequence_starts_in_later_units(K, oracle_mod, history):
         np.testing.assert_array_equal(cs.cpu().numpy().astype(np.float64), ref["conv_state"])
 
 
-@pytest.mark.parametrize("case", ["fast_decay", "slow_decay", "beta_one", "zero_rows"])
+@pytest.mark.parametrize("case", ["fast_decay", "slow_decay", "beta_one", "zero_rows", "strong_decay",
+                                  "decay_near_threshold"])
 def test_layer_stress(K, oracle_mod, case):
     kw = {"fast_decay": dict(g_mean=4.0), "slow_decay": dict(g_mean=-6.0),
-          "beta_one": dict(b_mean=12.0), "zero_rows": {}}[case]
+          "beta_one": dict(b_mean=12.0), "zero_rows": {},
+          # decay over a chunk near 2^-100 (one reference per channel), and
+          # around 2^-200, beyond which the exact tile path takes over: chunks
+          # fall on both sides
+          "strong_decay": dict(g_mean=0.5), "decay_near_threshold": dict(g_mean=2.4)}[case]
     inp = synth.make("long_t256k", lengths=(700, 1300), H=3, **kw)
+    if case == "decay_near_threshold":
+        fast, steep = chunk_decay_split(inp)
+        print(f"  chunk-heads with decay range <= 200 (log2): {fast}, above: {steep}", flush=True)
+        assert fast > 0 and steep > 0
     if case == "zero_rows":
         inp["q_in"][100:180] = 0
         inp["k_in"][100:180] = 0
