@@ -1045,6 +1045,12 @@ struct StateCfg {
     // memory waves: each issues its share of every copy (more of them do not
     // move a chunk faster: the copies are bound by the CU's path into LDS)
     static constexpr int kMemWaves = 4;
+    // output waves per slice: two with one slice per workgroup; with two
+    // slices one, which keeps the workgroup at 8 waves (2 per SIMD, so the
+    // chain wave's operands fit in registers)
+    static constexpr int kOutWaves = SB == 1 ? 2 : 1;
+    static constexpr int kCompWaves = 1 + kOutWaves;  // per slice
+    static constexpr int kThreads = 64 * (SB * kCompWaves + kMemWaves);
     static constexpr int kRowBytes = 32 * SB;             // one token row of the group's columns, bf16
     static constexpr int kPieces = 2 * SB;                // 1 KB pieces of each group tile (U~, M U~, z)
     static constexpr int kPiecesPerWave = (kPieces + kMemWaves - 1) / kMemWaves;
@@ -1107,7 +1113,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 template <typename GT, bool kGate, int NS>
-__global__ __launch_bounds__(64 * (2 * NS + StateCfg<NS>::kMemWaves)) void mfma_state_kernel(MfmaK<GT> a) {
+__global__ __launch_bounds__(StateCfg<NS>::kThreads) void mfma_state_kernel(MfmaK<GT> a) {
     constexpr int SB = NS;
     using C = StateCfg<SB>;
     constexpr int P = 8 / SB;            // slice groups per head
@@ -1145,21 +1151,27 @@ __global__ __launch_bounds__(64 * (2 * NS + StateCfg<NS>::kMemWaves)) void mfma_
     };
     auto buf_of = [&](int j) { return (j & 1) ? buf1 : buf0; };
 
-    if (wave >= 2 * NS) {
+    constexpr int CW = C::kCompWaves;
+    if (wave >= CW * NS) {
         // ---- memory waves
         if (nch == 0) return;
-        const int wm = wave - 2 * NS;
+        const int wm = wave - CW * NS;
         // part A of chunk min(j, nch-1): -W, Q', U~, M U~ and gate logits
         // (past the end it copies the last chunk again into the free buffer
         // the index selects, so that every step issues the same operations)
         constexpr int MW = C::kMemWaves;
+        // The workgroups of one head copy the same factors at the same time;
+        // each starts its walk over the 1 KB blocks at a different block, so
+        // their requests meet different L2 channels.  (A wave still copies the
+        // blocks of its own residue mod MW, so the counts do not change.)
+        const int rot = MW * part;
         auto issue_a = [&](int jn) {
             char* buf = buf_of(jn);
             const int j = min(jn, nch - 1);
             const char* rp = rec_of(j);
 #pragma unroll
             for (int i = 0; i < 32 / MW; ++i) {
-                const int b = wm + MW * i;
+                const int b = (wm + MW * i + rot) & 31;
                 lds_copy16(rp + b * 1024 + lane * 16, buf + b * 1024);
             }
             const int Lc = chunk_len(j);
@@ -1194,17 +1206,16 @@ __global__ __launch_bounds__(64 * (2 * NS + StateCfg<NS>::kMemWaves)) void mfma_
             const char* rp = rec_of(j);
 #pragma unroll
             for (int i = 0; i < 16 / MW; ++i) {
-                const int b = 32 + wm + MW * i;
+                const int b = 32 + ((wm + MW * i + rot) & 15);
                 lds_copy16(rp + b * 1024 + lane * 16, buf + b * 1024);
             }
             if (wm == 0 && lane < 32) lds_copy16(rp + R_GAM + lane * 16, buf + C::B_GAM);
         };
         // issue order per step j: [A_j] B(j+1) [M_j] stores(j), A(j+2).
-        // Before A_j part A of chunk j must be in; after it came B(j),
-        // stores(j-1) and A(j+1).  Before M_j part B of chunk j must be in;
-        // after it came stores(j-1), A(j+1) and B(j+1).  (Wave 0's gamma copy
-        // is left out of the counts: it waits for one operation more than
-        // needed.)  In step 0 there were no stores(-1).
+        // Before A_j parts A and B of chunk j must be in (the chain wave reads
+        // both right after A_j); after B(j) came stores(j-1) and A(j+1).  In
+        // step 0 there were no stores(-1).  (Wave 0's gamma copy is inside
+        // B(j), so the counts after it are the same for every wave.)
         constexpr int kA = C::kPartA, kB = C::kPartB, kS = C::kStores;
         issue_a(0);
         issue_b(0);
@@ -1214,11 +1225,10 @@ __global__ __launch_bounds__(64 * (2 * NS + StateCfg<NS>::kMemWaves)) void mfma_
         constexpr int RW = C::kRowsPerWave;
         const int wq = lane % PR;
         for (int j = 0; j < nch; ++j) {
-            if (j == 0) wait_vmcnt<kB + kA>(); else wait_vmcnt<kB + kS + kA>();
-            lds_barrier();  // A_j: part A of chunk j is in LDS; part B of chunk j+1 may be copied
+            if (j == 0) wait_vmcnt<kA>(); else wait_vmcnt<kS + kA>();
+            lds_barrier();  // A_j: parts A and B of chunk j are in LDS; part B of chunk j+1 may be copied
             issue_b(j + 1);
-            if (j == 0) wait_vmcnt<kA + kB>(); else wait_vmcnt<kS + kA + kB>();
-            lds_barrier();  // M_j: part B of chunk j is in; the output tile of chunk j is staged
+            lds_barrier();  // M_j: the output tile of chunk j is staged
             const int Lc = chunk_len(j);
             const int64_t tb = sb + static_cast<int64_t>(j) * kChunk;
 #pragma unroll
@@ -1238,16 +1248,19 @@ __global__ __launch_bounds__(64 * (2 * NS + StateCfg<NS>::kMemWaves)) void mfma_
         return;
     }
 
-    // ---- compute waves: two per 16-column slice ls = wave / 2 of the group.
-    // The chain wave (even) keeps the slice's fp32 state in registers and runs
-    // the recurrence, U = U~ - W S and then S <- Diag(gamma) S + K^T U; after
-    // each update it leaves the state as the bf16 matrix-core operand in LDS.
-    // The output wave (odd) takes that operand for the chunk's gated output,
-    // O^T = (M U~)^T + S^T Q'^T, off the recurrence's critical path: row tiles
-    // 0-2; the chain wave, which has less to do before M_j, takes row tile 3.
-    // Inside the chunk loop both touch only LDS.  In a step the output wave
-    // reads the operand before M_j and the chain wave rewrites it after M_j.
-    const int ls = wave >> 1;
+    // ---- compute waves: CW per 16-column slice ls = wave / CW of the group.
+    // The chain wave (wave % CW == 0) keeps the slice's fp32 state in
+    // registers and runs the recurrence, U = U~ - W S and then S <- Diag(gamma)
+    // S + K^T U; after each update it leaves the state as the bf16
+    // matrix-core operand in LDS.  Its products go contraction step by
+    // contraction step across all row tiles, so the tiles' accumulations are
+    // independent and the matrix core never waits for its own previous result.
+    // The output waves take that operand for the chunk's gated output, O^T =
+    // (M U~)^T + S^T Q'^T, 4 / kOutWaves row tiles each, off the recurrence's
+    // critical path.  Inside the chunk loop the compute waves touch only LDS.
+    // In a step the output waves read the operand before M_j and the chain
+    // wave rewrites it after M_j.
+    const int ls = wave / CW, role = wave - CW * ls;
     char* const sbx = smem + C::B_SBX + ls * 4096;
     const int col0 = 16 * (SB * part + ls) + c;
     auto widen = [](uint2 p) {
@@ -1272,18 +1285,7 @@ __global__ __launch_bounds__(64 * (2 * NS + StateCfg<NS>::kMemWaves)) void mfma_
         for (int ks = 0; ks < 4; ++ks)
             x.qa[ks] = *reinterpret_cast<const bf16x8*>(cur + C::B_QP + ((mt * 4 + ks) * 64 + lane) * 16);
     };
-    auto out_tile = [&](int mt, const OutOps& x, const bf16x8 (&Sb)[4]) {
-        f32x4 o = widen(x.op);
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) o = mfma(Sb[ks], x.qa[ks], o);
-        if (kGate) {
-            const f32x4 zf = widen(x.zp);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) o[i] *= sigmoid_fast(zf[i]);
-        }
-        *reinterpret_cast<uint2*>(stage + stage_off(mt)) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
-    };
-    if ((wave & 1) == 0) {
+    if (role == 0) {
         f32x4 S[8];  // S[t][i] = state[16t + 4g + i][col0]
         const int64_t sidx = grp * (128 * 128);
         if (a.S0 != nullptr) {  // one uniform branch: all loads in flight together
@@ -1303,35 +1305,18 @@ __global__ __launch_bounds__(64 * (2 * NS + StateCfg<NS>::kMemWaves)) void mfma_
         }
         for (int j = 0; j < nch; ++j) {
             const char* cur = buf_of(j);
-            lds_barrier();  // A_j: part A of chunk j is in LDS
-            // U = U~ - W S; the reads of row tile mt + 1 go out before the
-            // products of tile mt
-            struct ChainOps {
-                uint2 up;
-                bf16x8 wa[4];
-            };
-            auto load_tile = [&](int mt, ChainOps& x) {
-                x.up = *reinterpret_cast<const uint2*>(cur + C::B_UT + ((ls * 4 + mt) * 64 + lane) * 8);
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks)
-                    x.wa[ks] = *reinterpret_cast<const bf16x8*>(cur + C::B_NEGW + ((mt * 4 + ks) * 64 + lane) * 16);
-            };
-            f32x4 U[4];
-            ChainOps ops[2];
-            OutOps oops;
-            load_tile(0, ops[0]);
-            load_out(cur, 3, oops);
+            lds_barrier();  // A_j: parts A and B of chunk j are in LDS
+            // U = U~ - W S: every operand of the four row tiles read first
+            uint2 up[4];
+            bf16x8 wa[4][4];
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
-                if (mt < 3) load_tile(mt + 1, ops[(mt + 1) & 1]);
-                const ChainOps& x = ops[mt & 1];
-                U[mt] = widen(x.up);
+                up[mt] = *reinterpret_cast<const uint2*>(cur + C::B_UT + ((ls * 4 + mt) * 64 + lane) * 8);
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks) U[mt] = mfma(x.wa[ks], Sb[ks], U[mt]);
+                for (int ks = 0; ks < 4; ++ks)
+                    wa[mt][ks] = *reinterpret_cast<const bf16x8*>(cur + C::B_NEGW + ((mt * 4 + ks) * 64 + lane) * 16);
             }
-            out_tile(3, oops, Sb);
-            lds_barrier();  // M_j: part B of chunk j is in LDS; the output wave is done with the operand
-            // S <- Diag(gamma) S + K^T U, with every K^T and gamma read issued first
+            // K^T and gamma of the state update, read now so they arrive while U is made
             bf16x8 ka[8][2];
             float4 gm[8];
 #pragma unroll
@@ -1341,6 +1326,15 @@ __global__ __launch_bounds__(64 * (2 * NS + StateCfg<NS>::kMemWaves)) void mfma_
                 for (int ks = 0; ks < 2; ++ks)
                     ka[t][ks] = *reinterpret_cast<const bf16x8*>(cur + C::B_KHT + ((t * 2 + ks) * 64 + lane) * 16);
             }
+            f32x4 U[4];
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) U[mt] = widen(up[mt]);
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) U[mt] = mfma(wa[mt][ks], Sb[ks], U[mt]);
+            lds_barrier();  // M_j: the output waves are done with the state operand
+            // S <- Diag(gamma) S + K^T U
             const bf16x8 Ub[2] = {to_bf16x8(U[0], U[1]), to_bf16x8(U[2], U[3])};
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
@@ -1348,9 +1342,11 @@ __global__ __launch_bounds__(64 * (2 * NS + StateCfg<NS>::kMemWaves)) void mfma_
                 S[t][1] *= gm[t].y;
                 S[t][2] *= gm[t].z;
                 S[t][3] *= gm[t].w;
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) S[t] = mfma(ka[t][ks], Ub[ks], S[t]);
             }
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int t = 0; t < 8; ++t) S[t] = mfma(ka[t][ks], Ub[ks], S[t]);
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 Sb[ks] = to_bf16x8(S[2 * ks], S[2 * ks + 1]);
@@ -1374,19 +1370,33 @@ __global__ __launch_bounds__(64 * (2 * NS + StateCfg<NS>::kMemWaves)) void mfma_
                 for (int i = 0; i < 4; ++i) a.S_out[sidx + (16 * t + 4 * g + i) * 128 + col0] = S[t][i];
         }
     } else {
+        constexpr int TPW = 4 / C::kOutWaves;  // row tiles per output wave
+        const int mt0 = TPW * (role - 1);     // row tiles mt0 .. mt0 + TPW - 1
         for (int j = 0; j < nch; ++j) {
             const char* cur = buf_of(j);
             lds_barrier();  // A_j: part A of chunk j and the state operand are in LDS; the staging tile is free
             bf16x8 Sb[4];
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) Sb[ks] = *reinterpret_cast<const bf16x8*>(sbx + (ks * 64 + lane) * 16);
-            // row tiles 0-2; the reads of tile mt + 1 go out before the products of tile mt
-            OutOps ops[2];
-            load_out(cur, 0, ops[0]);
+            OutOps ops[TPW];
 #pragma unroll
-            for (int mt = 0; mt < 3; ++mt) {
-                if (mt < 2) load_out(cur, mt + 1, ops[(mt + 1) & 1]);
-                out_tile(mt, ops[mt & 1], Sb);
+            for (int u = 0; u < TPW; ++u) load_out(cur, mt0 + u, ops[u]);
+            f32x4 o[TPW];
+#pragma unroll
+            for (int u = 0; u < TPW; ++u) o[u] = widen(ops[u].op);
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+                for (int u = 0; u < TPW; ++u) o[u] = mfma(Sb[ks], ops[u].qa[ks], o[u]);
+#pragma unroll
+            for (int u = 0; u < TPW; ++u) {
+                if (kGate) {
+                    const f32x4 zf = widen(ops[u].zp);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) o[u][i] *= sigmoid_fast(zf[i]);
+                }
+                *reinterpret_cast<uint2*>(stage + stage_off(mt0 + u)) =
+                    make_uint2(pack_bf16x2(o[u][0], o[u][1]), pack_bf16x2(o[u][2], o[u][3]));
             }
             lds_barrier();  // M_j: the output tile is staged
         }
@@ -1402,7 +1412,7 @@ hipError_t launch_state(const MfmaK<GT>& k, hipStream_t s) {
     if (e != hipSuccess) return e;
     const int64_t blocks = (k.groups + 7) / 8 * 8 * P;
     hipLaunchKernelGGL((mfma_state_kernel<GT, kGate, NS>), dim3(static_cast<unsigned>(blocks)),
-                       dim3(64 * (2 * NS + C::kMemWaves)), C::kLds, s, k);
+                       dim3(C::kThreads), C::kLds, s, k);
     return hipGetLastError();
 }
 
