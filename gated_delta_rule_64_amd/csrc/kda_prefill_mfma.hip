@@ -219,6 +219,19 @@ __device__ __forceinline__ float row16_sum(float x) {
     return x;
 }
 
+// x of the lane N below within each row of 16 lanes (DPP row_shr); the
+// first N lanes of a row get 0.  All lanes must be active.
+template <int N>
+__device__ __forceinline__ float row_shr(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + N, 0xF, 0xF, false));
+}
+
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+// a.lo * b.lo + a.hi * b.hi + acc for words holding two bf16 values
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, a), __builtin_bit_cast(bf16x2v, b), acc, false);
+}
+
 // (R, S) of tile i in the lower block triangle, row-major order
 __device__ __forceinline__ void tile_rs(int i, int& R, int& S) {
     R = i >= 6 ? 3 : i >= 3 ? 2 : i >= 1 ? 1 : 0;
@@ -296,10 +309,11 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
     };
     // This thread's share of a unit's inputs, loaded one unit ahead into
     // registers so the loads overlap the previous unit's work: rows
-    // (tid + 512 i) / 16 of q, k, v (8 channels each), rows 4 rg .. 4 rg + 3 of
-    // the decay logs (4 channels), and beta of row tid % 64.  Loads are
-    // branch-free: rows past the chunk end read row L-1 and are zeroed on use.
-    const int fcq = ftid & 31, frg = ftid >> 5;
+    // (tid + 512 i) / 16 of q, k, v (8 channels each), rows 4 rq .. 4 rq + 3
+    // (rq = tid % 16) of the decay logs (channels 4 (tid / 16) .. + 3), and
+    // beta of row tid % 64.  Loads are branch-free: rows past the chunk end
+    // read row L-1 and are zeroed on use.
+    const int frq = ftid & 15, fcq = ftid >> 4;
     const int fw = __builtin_amdgcn_readfirstlane(ftid >> 6);  // the wave, as a uniform value
     uint4 pk[2], pq[2], pv[2];
     GateRaw<GT> px[4];  // decay logs (fused: decay logits) as loaded; converted when staged
@@ -323,7 +337,7 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
         if (p == 3) {
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                px[j].load(a.la + ((u.t0 + min(4 * frg + j, u.L - 1)) * H + u.h) * 128 + 4 * fcq);
+                px[j].load(a.la + ((u.t0 + min(4 * frq + j, u.L - 1)) * H + u.h) * 128 + 4 * fcq);
             // The last loads cover less than 512 threads' worth; every wave
             // issues them anyway, repeating another wave's (and later writes
             // the same bytes to the same LDS place).  Loads and their uses
@@ -374,7 +388,7 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
     // write), the first level of the decay scan, and cleared A, M and flags.
     // Runs once the LDS buffers are free.
     auto stage_inputs = [&](const Unit& u, int tid) {
-        const int cq = tid & 31, rg = tid >> 5;
+        const int rq = tid & 15, cq = tid >> 4;
         const int L = u.L;
         if (!kFused) {
 #pragma unroll
@@ -390,22 +404,25 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
                     make_uint4(pv[i].x & m, pv[i].y & m, pv[i].z & m, pv[i].w & m);
             }
         } else {
-            // Raw rows (bf16, [64][KS] per tensor), the 3-token history (fp32
-            // [3][128] per tensor) and the conv taps (fp32 [3 tensors][4 taps][128]) go to
-            // buffers that are free until the gates are staged.
+            // Raw rows (bf16, [3 + 64][KS] per tensor: the 3 tokens before the
+            // chunk, then its 64), the caller's fp32 history of a sequence's
+            // first chunk ([3][128] per tensor) and the conv taps (bf16 as
+            // loaded, [3 tensors][128 channels][4 taps]) go to buffers that are
+            // free until the gates are staged.
+            constexpr int RR = 3 + 64;
             uint16_t* raw = reinterpret_cast<uint16_t*>(sG);
-            float* hist = reinterpret_cast<float*>(raw + 3 * 64 * KS);
-            float* taps = sTot;
+            float* hist = reinterpret_cast<float*>(raw + 3 * RR * KS);
+            uint16_t* taps = reinterpret_cast<uint16_t*>(sTot);
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 const int idx = tid + kIntraThreads * i;
                 const int r = idx >> 4, ch = idx & 15;
                 const uint32_t m = r < L ? 0xffffffffu : 0u;
-                *reinterpret_cast<uint4*>(raw + r * KS + ch * 8) =
+                *reinterpret_cast<uint4*>(raw + (3 + r) * KS + ch * 8) =
                     make_uint4(pq[i].x & m, pq[i].y & m, pq[i].z & m, pq[i].w & m);
-                *reinterpret_cast<uint4*>(raw + 64 * KS + r * KS + ch * 8) =
+                *reinterpret_cast<uint4*>(raw + (RR + 3 + r) * KS + ch * 8) =
                     make_uint4(pk[i].x & m, pk[i].y & m, pk[i].z & m, pk[i].w & m);
-                *reinterpret_cast<uint4*>(raw + 2 * 64 * KS + r * KS + ch * 8) =
+                *reinterpret_cast<uint4*>(raw + (2 * RR + 3 + r) * KS + ch * 8) =
                     make_uint4(pv[i].x & m, pv[i].y & m, pv[i].z & m, pv[i].w & m);
             }
             const int tw = __builtin_amdgcn_readfirstlane(tid >> 6) % 3;  // the tensor this wave fetched
@@ -416,65 +433,82 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
                 // reads all eight registers (the raw rows fill four), so none
                 // is left awaiting its load when the next fetch reuses it.
                 asm volatile("" ::"v"(ph[4]), "v"(ph[5]), "v"(ph[6]), "v"(ph[7]));
-                float hv[8];
-                if (!u.first) {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        hv[2 * e] = __uint_as_float(ph[e] << 16);
-                        hv[2 * e + 1] = __uint_as_float(ph[e] & 0xffff0000u);
-                    }
-                } else {
-                    const uint32_t m = a.cs != nullptr ? 0xffffffffu : 0u;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) hv[e] = __uint_as_float(ph[e] & m);
-                }
-                float4* d = reinterpret_cast<float4*>(hist + (tt * 3 + hr) * 128 + 8 * chh);
-                d[0] = make_float4(hv[0], hv[1], hv[2], hv[3]);
-                d[1] = make_float4(hv[4], hv[5], hv[6], hv[7]);
-            }
-            {  // taps as [tensor][tap][channel]: a lane's 8 channels of one tap are contiguous
-                const uint32_t w4[4] = {pw.x, pw.y, pw.z, pw.w};
-                float* d = taps + tw * 512 + 2 * (tid & 63);
-#pragma unroll
-                for (int e = 0; e < 2; ++e) {  // channel 2 (tid % 64) + e, taps 0..3
-                    d[0 * 128 + e] = __uint_as_float(w4[2 * e] << 16);
-                    d[1 * 128 + e] = __uint_as_float(w4[2 * e] & 0xffff0000u);
-                    d[2 * 128 + e] = __uint_as_float(w4[2 * e + 1] << 16);
-                    d[3 * 128 + e] = __uint_as_float(w4[2 * e + 1] & 0xffff0000u);
+                // raw row hr - 3: the previous tokens of the sequence as bf16,
+                // or zeros at a sequence start (a caller history then goes to
+                // the fp32 buffer, added to the first rows' conv separately)
+                const uint32_t mr = u.first ? 0u : 0xffffffffu;
+                *reinterpret_cast<uint4*>(raw + (tt * RR + hr) * KS + 8 * chh) =
+                    make_uint4(ph[0] & mr, ph[1] & mr, ph[2] & mr, ph[3] & mr);
+                if (u.first && a.cs != nullptr) {
+                    float4* d = reinterpret_cast<float4*>(hist + (tt * 3 + hr) * 128 + 8 * chh);
+                    d[0] = make_float4(__uint_as_float(ph[0]), __uint_as_float(ph[1]), __uint_as_float(ph[2]),
+                                       __uint_as_float(ph[3]));
+                    d[1] = make_float4(__uint_as_float(ph[4]), __uint_as_float(ph[5]), __uint_as_float(ph[6]),
+                                       __uint_as_float(ph[7]));
                 }
             }
+            // taps of channels 2 (tid % 64), + 1 as loaded: per channel the words
+            // (tap 0, tap 1) and (tap 2, tap 3)
+            *reinterpret_cast<uint4*>(taps + (tw * 128 + 2 * (tid & 63)) * 4) = pw;
             lds_barrier();
             // conv (tap 3 is the current token) of the thread's two consecutive
             // rows 2k, 2k+1 of each tensor, from the five raw rows 2k-3 .. 2k+1
-            // (the first ones reach into the history), all reads of a tensor
-            // issued before the arithmetic that needs them; then the L2 norm
-            // of q and k over the 128 channels a 16-lane group holds
+            // (the first reach into the 3 rows before the chunk); then the L2
+            // norm of q and k over the 128 channels a 16-lane group holds.  The
+            // products are bf16 pair dot products: a channel's raw values of two
+            // consecutive tokens are paired in one word (v_perm) against its
+            // (tap 0, tap 1) and (tap 2, tap 3) words.  At a sequence start with
+            // a caller history (fp32) the rows before the chunk are zero there,
+            // and the history's terms are added in fp32 afterwards.
             const int ch8 = 8 * (tid & 15), r0 = 2 * (tid >> 4);
+            const bool fp32_hist = u.first && a.cs != nullptr;  // uniform
 #pragma unroll
             for (int tt = 0; tt < 3; ++tt) {
-                float w[4][8];
+                uint32_t tw8[16];  // word 2 c: (tap 0, tap 1) of channel ch8 + c; word 2 c + 1: (tap 2, tap 3)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) lds8f(taps + tt * 512 + j * 128 + ch8, w[j]);
-                float xv[5][8];
-                if (r0 >= 4) {  // every tap inside the chunk: one straight run of reads
-#pragma unroll
-                    for (int m = 0; m < 5; ++m)
-                        unpack8(*reinterpret_cast<const uint4*>(raw + tt * 64 * KS + (r0 - 3 + m) * KS + ch8), xv[m]);
-                } else {
-#pragma unroll
-                    for (int m = 0; m < 5; ++m) {
-                        const int rr = r0 - 3 + m;
-                        if (rr >= 0) unpack8(*reinterpret_cast<const uint4*>(raw + tt * 64 * KS + rr * KS + ch8), xv[m]);
-                        else lds8f(hist + (tt * 3 + rr + 3) * 128 + ch8, xv[m]);
-                    }
+                for (int q = 0; q < 4; ++q) {
+                    const uint4 t4 = *reinterpret_cast<const uint4*>(taps + (tt * 128 + ch8 + 2 * q) * 4);
+                    tw8[4 * q] = t4.x; tw8[4 * q + 1] = t4.y; tw8[4 * q + 2] = t4.z; tw8[4 * q + 3] = t4.w;
                 }
                 float y[2][8];
+                uint32_t xr[5][4];  // word q of raw row r0 - 3 + m: channels ch8 + 2 q, + 1
+#pragma unroll
+                for (int m = 0; m < 5; ++m) {
+                    const uint4 v4 = *reinterpret_cast<const uint4*>(raw + (tt * RR + r0 + m) * KS + ch8);
+                    xr[m][0] = v4.x; xr[m][1] = v4.y; xr[m][2] = v4.z; xr[m][3] = v4.w;
+                }
 #pragma unroll
                 for (int i = 0; i < 2; ++i)
 #pragma unroll
-                    for (int c8 = 0; c8 < 8; ++c8)
-                        y[i][c8] = w[0][c8] * xv[i][c8] + w[1][c8] * xv[i + 1][c8] + w[2][c8] * xv[i + 2][c8] +
-                                   w[3][c8] * xv[i + 3][c8];
+                    for (int q = 0; q < 4; ++q) {
+                        // (x_{r-3}, x_{r-2}) and (x_{r-1}, x_r) of channel ch8 + 2 q (low halves)
+                        // and of channel ch8 + 2 q + 1 (high halves)
+                        const uint32_t a_lo = __builtin_amdgcn_perm(xr[i + 1][q], xr[i][q], 0x05040100u);
+                        const uint32_t b_lo = __builtin_amdgcn_perm(xr[i + 3][q], xr[i + 2][q], 0x05040100u);
+                        const uint32_t a_hi = __builtin_amdgcn_perm(xr[i + 1][q], xr[i][q], 0x07060302u);
+                        const uint32_t b_hi = __builtin_amdgcn_perm(xr[i + 3][q], xr[i + 2][q], 0x07060302u);
+                        y[i][2 * q] = dot2_bf16(b_lo, tw8[4 * q + 1], dot2_bf16(a_lo, tw8[4 * q], 0.f));
+                        y[i][2 * q + 1] = dot2_bf16(b_hi, tw8[4 * q + 3], dot2_bf16(a_hi, tw8[4 * q + 2], 0.f));
+                    }
+                if (fp32_hist && r0 < 4) {
+                    // rows 0 .. 2: taps j < 3 - r read history row r + j
+#pragma unroll
+                    for (int i = 0; i < 2; ++i) {
+                        const int r = r0 + i;
+#pragma unroll
+                        for (int j = 0; j < 3; ++j) {
+                            if (r + j >= 3) continue;
+                            float hv[8];
+                            lds8f(hist + (tt * 3 + r + j) * 128 + ch8, hv);
+#pragma unroll
+                            for (int c8 = 0; c8 < 8; ++c8) {
+                                const uint32_t tw = tw8[2 * c8 + (j >> 1)];
+                                const float wj = __uint_as_float((j & 1) ? (tw & 0xffff0000u) : (tw << 16));
+                                y[i][c8] += wj * hv[c8];
+                            }
+                        }
+                    }
+                }
                 if (tt < 2) {
 #pragma unroll
                     for (int i = 0; i < 2; ++i) {
@@ -507,7 +541,7 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
                 // decay logs in log2 units: every use of G is 2^(difference);
                 // computed for every row, padded rows masked afterwards
                 const float lg = kFused ? -softplus_log2(gv) : gv * kLog2e;
-                x[j][e] = 4 * rg + j < L ? lg : 0.f;
+                x[j][e] = 4 * rq + j < L ? lg : 0.f;
             }
         {
             const float bv = ld(&pb);
@@ -517,15 +551,28 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
         if (tid < 5) sFlag[tid] = 0;
         for (int i = tid; i < 2 * 64 * MS / 4; i += kIntraThreads)
             reinterpret_cast<float4*>(sA)[i] = make_float4(0.f, 0.f, 0.f, 0.f);  // sA, sM
+        // G: the cumulative sum over the chunk's rows, within the thread's
+        // four rows, then over the 16 row groups of a 16-lane row (the lanes
+        // rq = 0 .. 15 hold the same four channels) by a DPP scan
 #pragma unroll
         for (int j = 1; j < 4; ++j)
 #pragma unroll
             for (int e = 0; e < 4; ++e) x[j][e] += x[j - 1][e];
 #pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float incl = x[3][e];
+            incl += row_shr<1>(incl);
+            incl += row_shr<2>(incl);
+            incl += row_shr<4>(incl);
+            incl += row_shr<8>(incl);
+            const float excl = row_shr<1>(incl);  // sum of the row groups before this one
+#pragma unroll
+            for (int j = 0; j < 4; ++j) x[j][e] += excl;
+        }
+#pragma unroll
         for (int j = 0; j < 4; ++j)
-            *reinterpret_cast<float4*>(sG + (4 * rg + j) * GS + 4 * cq) =
+            *reinterpret_cast<float4*>(sG + (4 * rq + j) * GS + 4 * cq) =
                 make_float4(x[j][0], x[j][1], x[j][2], x[j][3]);
-        *reinterpret_cast<float4*>(sTot + rg * 128 + 4 * cq) = make_float4(x[3][0], x[3][1], x[3][2], x[3][3]);
     };
 
     int64_t v = blockIdx.x;
@@ -540,27 +587,12 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
         int tid = ftid;
         asm volatile("" : "+v"(tid));
         const int wave = tid >> 6, lane = tid & 63, g = lane >> 4, c = lane & 15;
-        const int cq = tid & 31, rg = tid >> 5;
         const Unit cur = nxt;
         const int h = cur.h;
         const int64_t slot = cur.slot;
         char* rec = a.rec + (h * a.slots + slot) * REC_BYTES;  // a head's chunks are contiguous
         const bool more = v + gridDim.x < units;
-        lds_barrier();
-        {
-            float off[4] = {0.f, 0.f, 0.f, 0.f};
-            for (int q2 = 0; q2 < rg; ++q2) {
-                const float4 t4 = *reinterpret_cast<const float4*>(sTot + q2 * 128 + 4 * cq);
-                off[0] += t4.x; off[1] += t4.y; off[2] += t4.z; off[3] += t4.w;
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                float4* p = reinterpret_cast<float4*>(sG + (4 * rg + j) * GS + 4 * cq);
-                const float4 x4 = *p;
-                *p = make_float4(x4.x + off[0], x4.y + off[1], x4.z + off[2], x4.w + off[3]);
-            }
-        }
-        lds_barrier();
+        lds_barrier();  // the unit's staged inputs and G are in LDS
         // Decay ranges: a chunk whose decay over its 64 tokens stays within
         // kFastRange in every channel scales its operands against one
         // reference per channel; a steeper one takes the exact tile path, for
@@ -754,12 +786,13 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
         lds_barrier();
 
         // The next unit's loads go out in four parts, one after each of the
-        // phases from here on, and land during the rest of this unit's work.
-        // All workgroups run in near lockstep, so one burst of loads per unit
-        // would saturate HBM while it lasts and idle it the rest of the time.
+        // phases from here on, and land during the rest of this unit's work
+        // (issued as one burst they hold the issuing waves for thousands of
+        // cycles).  The scattered part (decay and write logits, taps,
+        // history) goes first.
         if (more) {
             nxt = unit_of(v + gridDim.x);
-            fetch(nxt, 0);
+            fetch(nxt, 3);
         }
 
         // ---- T = (I + Diag(beta) A)^-1
@@ -786,7 +819,7 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
             }
         }
         lds_barrier();
-        if (more) fetch(nxt, 1);
+        if (more) fetch(nxt, 0);
         // Off-diagonal blocks of T from the two 32 x 32 halves (L = Diag(beta) A):
         //   level 1: T_10 = -T_11 L_10 T_00,  T_32 = -T_33 L_32 T_22          (waves 0, 1)
         //   level 2: X = L_hi,lo T_lo:  X_20 = L_20 T_00 + L_21 T_10,  X_21 = L_21 T_11,
@@ -867,7 +900,7 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
         }
         lds_barrier();
 
-        if (more) fetch(nxt, 2);
+        if (more) fetch(nxt, 1);
         // ---- W = T Diag(beta) e^G K and U~ = T Diag(beta) V: column tile nt = wave.
         // The key operand is Kl = e^{G - refL} K, so W = (T Diag(beta) Kl) 2^{refL}
         // column by column.
@@ -918,7 +951,7 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
         }
         lds_barrier();  // V and T Diag(beta) are dead: their buffers become the staging areas
 
-        if (more) fetch(nxt, 3);
+        if (more) fetch(nxt, 2);
         // ---- Q' = e^G Q - M W and M U~; stage -W and Q' for the transposes.
         // The query operand is Ql = e^{G - refL} Q, so e^G Q = Ql 2^{refL}.
         {
