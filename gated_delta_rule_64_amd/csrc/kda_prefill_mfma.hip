@@ -548,7 +548,6 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
             const int bt = tid & 63;  // every wave writes the same 64 values
             sB[bt] = bt < L ? (kFused ? sigmoid_fast(bv) : bv) : 0.f;
         }
-        if (tid < 5) sFlag[tid] = 0;
         for (int i = tid; i < 2 * 64 * MS / 4; i += kIntraThreads)
             reinterpret_cast<float4*>(sA)[i] = make_float4(0.f, 0.f, 0.f, 0.f);  // sA, sM
         // G: the cumulative sum over the chunk's rows, within the thread's
@@ -573,10 +572,22 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
         for (int j = 0; j < 4; ++j)
             *reinterpret_cast<float4*>(sG + (4 * rq + j) * GS + 4 * cq) =
                 make_float4(x[j][0], x[j][1], x[j][2], x[j][3]);
+        // the chunk's decay range per channel, G(row 0) - G(row 63), from the
+        // first and last lane of the 16-lane row: beyond kFastRange the chunk
+        // takes the exact tile path (flag cleared at the end of the previous unit)
+        {
+            const int row0 = (tid & 63) & ~15;
+            bool over = false;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                over |= __shfl(x[0][e], row0) - __shfl(x[3][e], row0 | 15) > kFastRange;
+            if (over) sFlag[4] = 1;  // benign race: every writer stores 1
+        }
     };
 
     int64_t v = blockIdx.x;
     if (v >= units) return;
+    if (ftid < 5) sFlag[ftid] = 0;  // (staging's first barrier orders this before its flag writes)
     Unit nxt = unit_of(v);
     fetch_all(nxt);
     stage_inputs(nxt, ftid);
@@ -594,19 +605,9 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
         const bool more = v + gridDim.x < units;
         lds_barrier();  // the unit's staged inputs and G are in LDS
         // Decay ranges: a chunk whose decay over its 64 tokens stays within
-        // kFastRange in every channel scales its operands against one
-        // reference per channel; a steeper one takes the exact tile path, for
-        // which the flags also mark the 16-token sub-blocks too steep for its
-        // factored form.
-        if (tid < 128) {
-#pragma unroll
-            for (int R = 0; R < 4; ++R) {
-                const float d = sG[(16 * R) * GS + tid] - sG[(16 * R + 15) * GS + tid];
-                if (d > kDiagRange) sFlag[R] = 1;  // benign race: every writer stores 1
-            }
-            if (sG[tid] - sG[63 * GS + tid] > kFastRange) sFlag[4] = 1;
-        }
-        lds_barrier();
+        // kFastRange in every channel (checked at staging) scales its operands
+        // against one reference per channel; a steeper one takes the exact
+        // tile path.
         const bool steep = __builtin_amdgcn_readfirstlane(sFlag[4]) != 0;
 
         // The bf16 matrix-core operands of the chunk, once for every product:
@@ -737,7 +738,16 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
             });
         } else {
             // exact tile path: factored decays referenced to each row block's
-            // first token, pairwise decays on steep diagonal blocks
+            // first token, pairwise decays on the 16-token sub-blocks too steep
+            // for the factored form
+            if (tid < 128) {
+#pragma unroll
+                for (int R = 0; R < 4; ++R) {
+                    const float d = sG[(16 * R) * GS + tid] - sG[(16 * R + 15) * GS + tid];
+                    if (d > kDiagRange) sFlag[R] = 1;  // benign race: every writer stores 1
+                }
+            }
+            lds_barrier();
             am_tiles([&](int R, int S, int k0, int k1, f32x4& accA, f32x4& accM) {
                 const int b = 16 * R;
                 if (R == S && sFlag[R]) {
@@ -797,8 +807,17 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
 
         // ---- T = (I + Diag(beta) A)^-1
         // diagonal blocks: wave R < 4, lane j < 16 owns column j of T_RR in registers
+        // (the dot products of a row in four partial sums, to shorten the
+        // dependent chain).  Meanwhile waves 4..7, idle here, write the K^
+        // blocks and gamma of the record: they depend only on the operands.
         if (wave < 4) {
             const int R = wave, j = lane;
+            float bR[16];
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const float4 b4 = *reinterpret_cast<const float4*>(sB + 16 * R + 4 * q4);
+                bR[4 * q4] = b4.x; bR[4 * q4 + 1] = b4.y; bR[4 * q4 + 2] = b4.z; bR[4 * q4 + 3] = b4.w;
+            }
             float t[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -808,15 +827,39 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
                     const float4 v4 = *reinterpret_cast<const float4*>(sA + (16 * R + r) * MS + 16 * R + 4 * q4);
                     arow[4 * q4] = v4.x; arow[4 * q4 + 1] = v4.y; arow[4 * q4 + 2] = v4.z; arow[4 * q4 + 3] = v4.w;
                 }
-                float sum = 0.f;
+                float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int s2 = 0; s2 < r; ++s2) sum += arow[s2] * t[s2];
-                t[r] = (r == j ? 1.f : 0.f) - sB[16 * R + r] * sum;
+                for (int s2 = 0; s2 < r; ++s2) ps[s2 & 3] += arow[s2] * t[s2];
+                t[r] = (r == j ? 1.f : 0.f) - bR[r] * ((ps[0] + ps[1]) + (ps[2] + ps[3]));
             }
             if (j < 16) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) sT[(16 * R + r) * MS + 16 * R + j] = t[r];
             }
+        } else {
+            // K^ = Kr 2^{G_last - refR}: channel tiles 2 (wave - 4), + 1
+#pragma unroll
+            for (int t2 = 0; t2 < 2; ++t2) {
+                const int t = 2 * (wave - 4) + t2;
+                const int ch = 16 * t + c;
+                const float sk = __builtin_amdgcn_exp2f(sGl[ch] - sRefR[ch]);
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    float kv[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int s2 = 32 * ks + perm(g, e);
+                        kv[e] = sk * bfv(sKr + s2 * KS + ch);
+                    }
+                    uint4 p;
+                    p.x = pack_bf16x2(kv[0], kv[1]);
+                    p.y = pack_bf16x2(kv[2], kv[3]);
+                    p.z = pack_bf16x2(kv[4], kv[5]);
+                    p.w = pack_bf16x2(kv[6], kv[7]);
+                    rec_store16(rec + R_KHT + ((t * 2 + ks) * 64 + lane) * 16, p);
+                }
+            }
+            if (tid < 384) reinterpret_cast<float*>(rec + R_GAM)[tid - 256] = exp2f(sGl[tid - 256]);
         }
         lds_barrier();
         if (more) fetch(nxt, 0);
@@ -1003,7 +1046,7 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
         }
         lds_barrier();
 
-        // ---- stores in the A-operand layout: -W, Q' (2 blocks per wave each), K^T
+        // ---- stores in the A-operand layout: -W, Q' (2 blocks per wave each)
         {
             const int mt = wave >> 1;
 #pragma unroll
@@ -1019,26 +1062,7 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
                 rec_store16(rec + R_NEGW + blk * 16, make_uint4(wlo.x, wlo.y, whi.x, whi.y));
                 rec_store16(rec + R_QP + blk * 16, make_uint4(qlo.x, qlo.y, qhi.x, qhi.y));
             }
-            // K^ = Kr 2^{G_last - refR}
-            const int t = wave;
-            const int ch = 16 * t + c;
-            const float sk = __builtin_amdgcn_exp2f(sGl[ch] - sRefR[ch]);
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                float kv[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int s2 = 32 * ks + perm(g, e);
-                    kv[e] = sk * bfv(sKr + s2 * KS + ch);
-                }
-                uint4 p;
-                p.x = pack_bf16x2(kv[0], kv[1]);
-                p.y = pack_bf16x2(kv[2], kv[3]);
-                p.z = pack_bf16x2(kv[4], kv[5]);
-                p.w = pack_bf16x2(kv[6], kv[7]);
-                rec_store16(rec + R_KHT + ((t * 2 + ks) * 64 + lane) * 16, p);
-            }
-            if (tid < 128) reinterpret_cast<float*>(rec + R_GAM)[tid] = exp2f(sGl[tid]);
+            if (tid < 5) sFlag[tid] = 0;  // for the next unit's staging (steep was read long ago)
         }
         lds_barrier();  // every LDS buffer is free for the next unit
         // Leave before staging rather than staging conditionally: the loop's
@@ -1249,7 +1273,7 @@ __global__ __launch_bounds__(StateCfg<NS>::kThreads) void mfma_state_kernel(Mfma
         // both right after A_j); after B(j) came stores(j-1) and A(j+1).  In
         // step 0 there were no stores(-1).  (Wave 0's gamma copy is inside
         // B(j), so the counts after it are the same for every wave.)
-        constexpr int kA = C::kPartA, kB = C::kPartB, kS = C::kStores;
+        constexpr int kA = C::kPartA, kS = C::kStores;
         issue_a(0);
         issue_b(0);
         issue_a(1);
