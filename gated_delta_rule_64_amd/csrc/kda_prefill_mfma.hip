@@ -128,7 +128,7 @@ struct MfmaK {
 constexpr int kIntraThreads = 512;  // 8 waves: two per SIMD
 constexpr size_t kIntraLds = (3 * 64 * KS) * 2 + (64 * GS + 3 * 64 * MS + 64 + 16 * 128) * 4 + 32;
 static_assert(64 * KS * 2 + 64 * TBS * 2 <= 64 * GS * 4, "K^ and the M operand copy share the space of G");
-static_assert(64 * TBS * 2 <= 64 * MS * 4, "the T Diag(beta) operand copy takes the space of A");
+static_assert(64 * TBS <= 64 * KS, "the T Diag(beta) operand copy takes the space of K^");
 
 __device__ __forceinline__ void unpack8(uint4 v, float (&x)[8]) {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
@@ -262,10 +262,12 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
     float* sRefR = sTot + 1664;
     float* sGl = sTot + 1792;
     // After the operand preparation: K^ scaled against refR (the space of G),
-    // and after the T solve the bf16 operand copies of M and T Diag(beta).
+    // then the bf16 operand copy of M beside it; once the K^ record is
+    // written (T diagonal phase), the bf16 operand copy of T Diag(beta) takes
+    // the space of K^.
     uint16_t* sKr = reinterpret_cast<uint16_t*>(sG);  // [64][KS]
     uint16_t* sMb = sKr + 64 * KS;                     // [64][TBS]
-    uint16_t* sTb = reinterpret_cast<uint16_t*>(sA);   // [64][TBS]
+    uint16_t* sTb = sKr;                               // [64][TBS]
     uint16_t* sStW = sV;                                // staging of -W  [64][KS]
     uint16_t* sStQ = reinterpret_cast<uint16_t*>(sA);   // staging of Q'  [64][SQS]
 
@@ -860,6 +862,19 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
                 }
             }
             if (tid < 384) reinterpret_cast<float*>(rec + R_GAM)[tid - 256] = exp2f(sGl[tid - 256]);
+            // M as the bf16 matrix-core operand: row (tid - 256) / 4, columns
+            // 16 ((tid - 256) % 4) .. + 15 (zero above the diagonal)
+            const int r = (tid - 256) >> 2, c0 = 16 * (tid & 3);
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+                float m8[8];
+                lds8f(sM + r * MS + c0 + 8 * h2, m8);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) m8[e] = c0 + 8 * h2 + e <= r ? m8[e] : 0.f;
+                *reinterpret_cast<uint4*>(sMb + r * TBS + c0 + 8 * h2) =
+                    make_uint4(pack_bf16x2(m8[0], m8[1]), pack_bf16x2(m8[2], m8[3]), pack_bf16x2(m8[4], m8[5]),
+                               pack_bf16x2(m8[6], m8[7]));
+            }
         }
         lds_barrier();
         if (more) fetch(nxt, 0);
@@ -870,6 +885,10 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
         //   level 3: T_hi,lo = -T_hi X:  T_20 = -T_22 X_20,  T_21 = -T_22 X_21,
         //            T_30 = -(T_32 X_20 + T_33 X_30),  T_31 = -(T_32 X_21 + T_33 X_31)
         // Lane (g, c) computes rows 4g .. 4g+3, column c of a 16 x 16 block.
+        // Every block of T also goes, times beta of its column, into the bf16
+        // operand copy of T Diag(beta): the off-diagonal ones from their
+        // writers, the diagonal ones copied by waves 2, 3 during level 1 (wave
+        // 4 zeroes the two blocks above the diagonal that readers touch).
         {
             // 16 x 16 blocks with row stride XS, XB floats apart (the scan
             // partials are dead); 20 puts the four row groups a wave writes
@@ -898,8 +917,27 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
                 // (a wave's LDS operations are performed in order: Y is complete here)
                 float t[4] = {0.f, 0.f, 0.f, 0.f};
                 mm16(sT + (16 * R) * MS + 16 * R, MS, Y, XS, t);
+                const float bc = sB[16 * S + c];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) sT[(16 * R + 4 * g + i) * MS + 16 * S + c] = -t[i];
+                for (int i = 0; i < 4; ++i) {
+                    sT[(16 * R + 4 * g + i) * MS + 16 * S + c] = -t[i];
+                    sTb[(16 * R + 4 * g + i) * TBS + 16 * S + c] = f32_to_bf16(-t[i] * bc);
+                }
+            } else if (wave < 4) {
+                // diagonal block R = tt / 32, row (tt % 32) / 2, columns 8 (tt % 2) .. + 7
+                const int tt = tid - 128, R = tt >> 5, r = (tt & 31) >> 1, c0 = 8 * (tt & 1);
+                float t8[8], b8[8];
+                lds8f(sT + (16 * R + r) * MS + 16 * R + c0, t8);
+                lds8f(sB + 16 * R + c0, b8);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) t8[e] = c0 + e <= r ? t8[e] * b8[e] : 0.f;
+                *reinterpret_cast<uint4*>(sTb + (16 * R + r) * TBS + 16 * R + c0) =
+                    make_uint4(pack_bf16x2(t8[0], t8[1]), pack_bf16x2(t8[2], t8[3]), pack_bf16x2(t8[4], t8[5]),
+                               pack_bf16x2(t8[6], t8[7]));
+            } else if (wave == 4) {
+                // blocks (0, 1) and (2, 3): rows 32 (lane / 32) + (lane % 32) / 2, 8 columns each
+                const int r = 32 * (lane >> 5) + ((lane & 31) >> 1), c0 = 32 * (lane >> 5) + 16 + 8 * (lane & 1);
+                *reinterpret_cast<uint4*>(sTb + r * TBS + c0) = make_uint4(0u, 0u, 0u, 0u);
             }
             lds_barrier();
             const int R = 2 + (wave >> 1), S = wave & 1;  // block of waves 0..3
@@ -914,32 +952,10 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
                 float t[4] = {0.f, 0.f, 0.f, 0.f};
                 mm16(sT + (16 * R) * MS + 32, MS, sX + S * XB, XS, t);                      // T_R2 X_2S
                 if (R == 3) mm16(sT + (16 * 3) * MS + 48, MS, sX + (2 + S) * XB, XS, t);  // T_33 X_3S
+                const float bc = sB[16 * S + c];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) sT[(16 * R + 4 * g + i) * MS + 16 * S + c] = -t[i];
+                for (int i = 0; i < 4; ++i) sTb[(16 * R + 4 * g + i) * TBS + 16 * S + c] = f32_to_bf16(-t[i] * bc);
             }
-        }
-        lds_barrier();
-        // blocks of T above the diagonal are never written; every reader masks them
-
-        // T Diag(beta) and M as bf16 matrix-core operands, once for all waves
-        // (zero above the diagonal): row r = tid / 8, columns 8 (tid % 8) .. + 7
-        {
-            const int r = tid >> 3, c0 = 8 * (tid & 7);
-            float t8[8], m8[8], b8[8], tv[8], mv[8];
-            lds8f(sT + r * MS + c0, t8);
-            lds8f(sM + r * MS + c0, m8);
-            lds8f(sB + c0, b8);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                tv[e] = c0 + e <= r ? t8[e] * b8[e] : 0.f;
-                mv[e] = c0 + e <= r ? m8[e] : 0.f;
-            }
-            *reinterpret_cast<uint4*>(sTb + r * TBS + c0) =
-                make_uint4(pack_bf16x2(tv[0], tv[1]), pack_bf16x2(tv[2], tv[3]), pack_bf16x2(tv[4], tv[5]),
-                           pack_bf16x2(tv[6], tv[7]));
-            *reinterpret_cast<uint4*>(sMb + r * TBS + c0) =
-                make_uint4(pack_bf16x2(mv[0], mv[1]), pack_bf16x2(mv[2], mv[3]), pack_bf16x2(mv[4], mv[5]),
-                           pack_bf16x2(mv[6], mv[7]));
         }
         lds_barrier();
 
