@@ -8,12 +8,28 @@
 //      values sit in a small per-slot draft buffer, so the conv, norm, gates
 //      and state updates are simply run again for them, and the state and conv
 //      history are written back once;
-//   2. runs the new tokens from that state, in registers: each token's output
-//      reads the state after the tokens before it (the recurrence of the
-//      section "KDA: constant-size memory over a very long context" of the
-//      page "Ling-3.0-flash: a 124B open MoE ..."), and the state is not
-//      written; the new raw tokens go to the draft buffer for the next call.
+//   2. runs the new tokens from that state: each token's output reads the
+//      state after the tokens before it (the recurrence of the section "KDA:
+//      constant-size memory over a very long context" of the page
+//      "Ling-3.0-flash: a 124B open MoE ..."), and the state is not written;
+//      the new raw tokens go to the draft buffer for the next call.
 // So a step reads and writes each state once, like a plain decode step.
+//
+// The J = na + T tokens of a call (na committed, then T new) are one short
+// chunk, computed in the chunked form (the exact rewrite the prefill uses).
+// With S0 the slot's state and G_j the running sum of the log decays through
+// token j (per key channel, base 2 here):
+//   P    = X S0,  X = rows 2^{G_j} k_j (j < J), then 2^{G_{na+t}} q_t (t < T)
+//   A_jl = beta_j sum_c k_jc k_lc 2^{G_jc - G_lc}                  (l < j)
+//   u_j  = beta_j (v_j - P_j) - sum_{l<j} A_jl u_l        (the delta-rule writes)
+//   o_t  = P_{J+t} + sum_{i <= na+t} M_ti u_i,  M_ti = sum_c q_tc k_ic 2^{G_{na+t},c - G_ic}
+//   S    = Diag(2^{G_{na-1}}) S0 + sum_{i<na} (2^{G_{na-1} - G_i} * k_i) u_i^T
+// (the last line is the committed state).  Every exponent is a later running
+// sum minus an earlier one, taken element by element, so none is positive and
+// nothing overflows however strong the decay.  The state is read once into
+// registers, feeds P on the fp32 matrix cores (v_mfma_f32_16x16x4_f32) as
+// their B operand, takes the rank-na update in place and is stored once; the
+// token-by-token chain shrinks to the J x J solve on 16-element vectors.
 #include "kda_common.h"
 #include "kda_internal.h"
 #include "kda_profile.h"
@@ -22,8 +38,15 @@ namespace kda {
 namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+// buffer resource word 3 for raw (unformatted) 32-bit data on gfx9-family
+// parts, and the cache-policy bit of a streaming (non-temporal) access
+constexpr int kBufferDword3 = 0x00020000;
+constexpr int kNonTemporal = 2;
 
 constexpr int kMaxTok = kSpecMaxTokens;
+constexpr int kNJ = 2 * kMaxTok;  // committed + new tokens at most
 
 template <typename XT>
 struct SpecK {
@@ -37,21 +60,64 @@ struct SpecK {
     XT* out;
 };
 
-// One 256-thread workgroup per (sequence, head).  The dv columns of the state
-// evolve independently, so wave w owns columns [w dv/4, (w+1) dv/4) over all
-// dk rows: lane (rg, cg) holds rows rg + NRG*i, columns 4cg .. 4cg+3 of its
-// wave's quarter, the reductions over rows stay inside the wave (shuffles),
-// and the token loop needs no barrier.  Preprocess roles: threads 0..127 run
-// channel tid of q and k, threads 128..255 channel tid-128 of v and of the
-// decay logits (both wave-uniform).
+// How the four waves share the dk x dv state for the products: NWC groups of
+// columns times NWK groups of rows.  In v_mfma_f32_16x16x4_f32, lane l = 16 q + n
+// gives A[n][q] and B[q][n] and receives D[4q + i][n] (i = 0..3).  Contraction
+// step s of wave (wc, wk) takes state rows wk KW + SP q + s (q = 0..3) as the
+// four contraction indices, and the V instructions of the step take columns
+// wc 16 V + V n + j (j < V) as their sixteen result columns: each lane holds V
+// adjacent floats of one row per step (16 lanes read 16 V contiguous floats
+// of a row), and its A operands X[n][wk KW + SP q + s] are contiguous in s.
+template <int DK, int DV>
+struct SpecSplit {
+    static constexpr int NWC = DV / 16 < 4 ? DV / 16 : 4;
+    static constexpr int NWK = 4 / NWC;
+    static constexpr int V = DV / (16 * NWC);  // adjacent columns per lane
+    static constexpr int KW = DK / NWK;        // state rows per wave
+    static constexpr int SP = KW / 4;          // contraction steps per wave
+    static constexpr int XS = DK + 4;          // LDS row stride of X (floats)
+    static constexpr int PS = DV + 4;          // LDS row stride of P
+    static_assert(NWC * NWK == 4 && V >= 1 && V <= 2 && SP >= 1, "head sizes 16..128");
+};
+
+// Dynamic LDS of one workgroup, float offsets; jm = kMaxTok + T token rows at
+// most, X and P padded to whole 16-row passes.
+template <int DK, int DV>
+struct SpecLds {
+    int k, G, v, q, z, xp, kh, u, ab, m, beta, ss, total;
+    __host__ __device__ explicit SpecLds(int T) {
+        typedef SpecSplit<DK, DV> Sp;
+        const int jm = kMaxTok + T, xr = 16 * ((jm + T + 15) / 16);
+        const int xsz = xr * Sp::XS, psz = Sp::NWK * xr * Sp::PS;
+        k = 0;                          // normalized k      [jm][DK]
+        G = k + jm * DK;                // running log2 decay [jm][DK]
+        v = G + jm * DK;                // v                 [jm][DV]
+        q = v + jm * DV;                // normalized q      [T][DK]
+        z = q + T * DK;                 // sigmoid(out gate) [T][DV]
+        xp = z + T * DV;                // X, then P
+        kh = xp + (xsz > psz ? xsz : psz);  // commit factors [1 + kMaxTok][DK]
+        // U of the committed tokens [kMaxTok][DV]: in k's place once k is read
+        u = kMaxTok * DV <= jm * DK ? k : kh + (1 + kMaxTok) * DK;
+        ab = (u == k ? kh + (1 + kMaxTok) * DK : u + kMaxTok * DV);  // beta_j A_jl [kNJ][kNJ]
+        m = ab + kNJ * kNJ;             // M [kMaxTok][kNJ]
+        beta = m + kMaxTok * kNJ;       // [kNJ]
+        ss = beta + kNJ;                // norm partial sums [kNJ][2][2]
+        total = ss + 4 * kNJ;
+    }
+};
+
+// One 256-thread workgroup per (sequence, head).  Preprocess roles: threads
+// 0..127 run channel tid of q and k, threads 128..255 channel tid-128 of v
+// and of the decay logits (both wave-uniform).  Register budget: three
+// workgroups per CU (at four the 128 x 128 state spills, which measured
+// slower).
 template <int DK, int DV, typename XT>
-__global__ __launch_bounds__(256) void spec_kernel(SpecK<XT> a) {
-    constexpr int CPW = DV / 4;              // columns per wave
-    constexpr int CG = CPW / 4;              // 4-column groups per wave
-    constexpr int NRG = 64 / CG;             // row groups per wave
-    constexpr int RPT = (DK + NRG - 1) / NRG;  // rows per lane
+__global__ __launch_bounds__(256, 3) void spec_kernel(SpecK<XT> a) {
+    typedef SpecSplit<DK, DV> Sp;
     constexpr int W = spec_draft_width(DK, DV);
-    constexpr int NJ = 2 * kMaxTok;  // committed + new tokens at most
+    constexpr int SP = Sp::SP, V = Sp::V;
+    extern __shared__ f32x4 spec_smem[];
+    float* const sm = reinterpret_cast<float*>(spec_smem);
 
     const int64_t bh = blockIdx.x;
     const int H = a.H, T = a.T;
@@ -59,21 +125,11 @@ __global__ __launch_bounds__(256) void spec_kernel(SpecK<XT> a) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int cg = lane % CG;
-    const int rg = lane / CG;
-    const int col = wave * CPW + 4 * cg;  // this lane's first state column
-
-    __shared__ float s_k[NJ][DK], s_a[NJ][DK], s_v[NJ][DV], s_q[kMaxTok][DK], s_z[kMaxTok][DV];
-    __shared__ float s_beta[NJ];
-    __shared__ float s_ss[NJ][2][2];
-    __shared__ float s_qk[kMaxTok];
 
     const int slot = a.idx ? a.idx[bb] : bb;
     if (slot < 0 || slot >= a.slots) {  // padding row: zero outputs, nothing else
-        if (rg == 0) {
-            const float zero[4] = {0.f, 0.f, 0.f, 0.f};
-            for (int t = 0; t < T; ++t) st4(a.out + ((static_cast<int64_t>(bb) * T + t) * H + h) * DV + col, zero);
-        }
+        if (tid < DV)
+            for (int t = 0; t < T; ++t) st(a.out + ((static_cast<int64_t>(bb) * T + t) * H + h) * DV + tid, 0.f);
         return;
     }
     int na = a.acc ? a.acc[bb] : 0;
@@ -81,18 +137,35 @@ __global__ __launch_bounds__(256) void spec_kernel(SpecK<XT> a) {
     const int J = na + T;
     if (J == 0) return;  // nothing to commit, nothing to verify
 
+    const SpecLds<DK, DV> L(T);
+    float* const s_k = sm + L.k;
+    float* const s_G = sm + L.G;
+    float* const s_v = sm + L.v;
+    float* const s_q = sm + L.q;
+    float* const s_z = sm + L.z;
+    float* const s_X = sm + L.xp;
+    float* const s_kh = sm + L.kh;
+    float* const s_U = sm + L.u;
+    float* const s_ab = sm + L.ab;
+    float* const s_M = sm + L.m;
+    float* const s_beta = sm + L.beta;
+    float* const s_ss = sm + L.ss;
+
+    // this lane's part of the state (see SpecSplit)
+    const int wc = wave % Sp::NWC, wk = wave / Sp::NWC;
+    const int ln = lane & 15, lq = lane >> 4;
+    const int row0 = wk * Sp::KW + SP * lq;
+    const int col0 = wc * 16 * V + V * ln;
     const int64_t sbh = static_cast<int64_t>(slot) * H + h;
-    float* __restrict__ Sp = a.state + sbh * (DK * DV);
+    // The state patch is read and written with buffer instructions over the
+    // head's dk x dv x 4 bytes: a byte offset per lane plus a per-row
+    // constant, so that no 64-bit address per row is kept in registers
+    // between the load and the store.
+    const __amdgpu_buffer_rsrc_t srsrc =
+        __builtin_amdgcn_make_buffer_rsrc(a.state + sbh * (DK * DV), 0, DK * DV * 4, kBufferDword3);
+    const int Soff = 4 * (row0 * DV + col0);
 
-    // 1. the state patch (only read when there is something to commit or verify)
-    f32x4 S[RPT];
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-        const int r = rg + NRG * i;
-        if (r < DK) S[i] = *reinterpret_cast<const f32x4*>(Sp + r * DV + col);
-    }
-
-    // 2. where this thread's raw values live: committed token j < na in the
+    // where this thread's raw values live: committed token j < na in the
     // draft buffer, new token t = j - na in the inputs; its conv taps and the
     // committed conv history
     const bool lower = tid < 128;           // q, k  |  v, decay logit
@@ -109,46 +182,48 @@ __global__ __launch_bounds__(256) void spec_kernel(SpecK<XT> a) {
     const int d_off1 = lower ? DK + c1 : 2 * DK + DV + c1;  // k | g
     const XT* in0 = lower ? a.q_in : a.v_in;
     const XT* in1 = lower ? a.k_in : a.g;
-    const int64_t row0 = lower ? static_cast<int64_t>(H) * DK : static_cast<int64_t>(H) * DV;
-    const int64_t col0 = lower ? static_cast<int64_t>(h) * DK + c0 : static_cast<int64_t>(h) * DV + c0;
-    const int64_t col1 = static_cast<int64_t>(h) * DK + c1;
-    const int64_t row1 = static_cast<int64_t>(H) * DK;
+    const int64_t row0_in = lower ? static_cast<int64_t>(H) * DK : static_cast<int64_t>(H) * DV;
+    const int64_t col0_in = lower ? static_cast<int64_t>(h) * DK + c0 : static_cast<int64_t>(h) * DV + c0;
+    const int64_t col1_in = static_cast<int64_t>(h) * DK + c1;
+    const int64_t row1_in = static_cast<int64_t>(H) * DK;
     float w0[4], w1[4], h0[3], h1[3];
-    ld4((lower ? a.w_q : a.w_v) + col0 * 4, w0);
-    ld4(a.w_k + col1 * 4, w1);
+    ld4((lower ? a.w_q : a.w_v) + col0_in * 4, w0);
+    ld4(a.w_k + col1_in * 4, w1);
 #pragma unroll
     for (int m = 0; m < 3; ++m) {
         h0[m] = hp0[m * cs_width];
         h1[m] = hp1[m * cs_width];
     }
 
-    // 3. preprocess every token in order, eight token slots at a time (the
+    // 1. preprocess every token in order, eight token slots at a time (the
     // second eight only when there are more than eight tokens; a slot past J
     // re-reads token J-1, no extra traffic, and is ignored): conv against
     // the running history (written back to the pool once the committed tokens
     // are through), new raw tokens saved to the draft buffer, the norms'
-    // partial sums, the gates.
+    // partial sums, the gates and the running log decay.
     constexpr int NB = 8;
     const bool has_z = a.z != nullptr;
     const int64_t row_z = static_cast<int64_t>(H) * DV, col_z = static_cast<int64_t>(h) * DV + (c & (DV - 1));
-    auto preprocess = [&](const int j0) {
-        float x0[NB], x1[NB], xb[NB], xz[NB];
+    float x0[NB], x1[NB], xb[NB], xz[NB];
+    auto load_batch = [&](const int j0) {
 #pragma unroll
         for (int jb = 0; jb < NB; ++jb) {
             const int j = j0 + jb;
             const int jj = j < J ? j : J - 1;
-            // the source by selects, not branches: a load inside a branch
-            // would have its value converted there, and the wait for it would
-            // also wait for the state loads still in flight
+            // the source by selects, not branches (a load inside a branch
+            // would have its value converted, and waited for, there)
             const bool draft = jj < na;
             const XT* pd = dr + static_cast<int64_t>(jj) * H * W;
             const int64_t t = static_cast<int64_t>(bb) * T + (draft ? 0 : jj - na);
-            x0[jb] = ld(draft ? pd + d_off0 : in0 + t * row0 + col0);
-            x1[jb] = ld(draft ? pd + d_off1 : in1 + t * row1 + col1);
+            x0[jb] = ld(draft ? pd + d_off0 : in0 + t * row0_in + col0_in);
+            x1[jb] = ld(draft ? pd + d_off1 : in1 + t * row1_in + col1_in);
             xb[jb] = ld(draft ? pd + 3 * DK + DV : a.b + t * H + h);
             // output-gate logit of a new token (any valid address otherwise)
             xz[jb] = ld(draft || !has_z ? pd : a.z + t * row_z + col_z);
         }
+    };
+    float gl = 0.f;  // running log2 decay of channel c (upper half)
+    auto compute_batch = [&](const int j0) {
 #pragma unroll
         for (int jb = 0; jb < NB; ++jb) {
             const int j = j0 + jb;
@@ -183,103 +258,272 @@ __global__ __launch_bounds__(256) void spec_kernel(SpecK<XT> a) {
                 const float sk = wave_sum(act1 ? y1 * y1 : 0.f);
                 const float sq = j >= na ? wave_sum(act0 ? y0 * y0 : 0.f) : 0.f;
                 if (lane == 0) {
-                    s_ss[j][0][wave] = sq;
-                    s_ss[j][1][wave] = sk;
+                    s_ss[j * 4 + wave] = sq;
+                    s_ss[j * 4 + 2 + wave] = sk;
                 }
                 if (act1) {
-                    s_k[j][c] = y1;
-                    if (j >= na) s_q[j - na][c] = y0;
+                    s_k[j * DK + c] = y1;
+                    if (j >= na) s_q[(j - na) * DK + c] = y0;
                 }
             } else {
-                if (act0) s_v[j][c] = round_to<XT>(y0);
-                if (act0 && j >= na) s_z[j - na][c] = has_z ? sigmoid(xz[jb]) : 1.f;
-                if (act1) s_a[j][c] = expf(-softplus_fast(x1[jb]));
+                if (act0) s_v[j * DV + c] = round_to<XT>(y0);
+                if (act0 && j >= na) s_z[(j - na) * DV + c] = has_z ? sigmoid(xz[jb]) : 1.f;
+                gl -= softplus_log2(x1[jb]);
+                if (act1) s_G[j * DK + c] = gl;
                 if (tid == 128) s_beta[j] = sigmoid_fast(xb[jb]);
             }
         }
     };
-    static_assert(NJ == 2 * NB, "two batches of token slots");
-    preprocess(0);
-    if (J > NB) preprocess(NB);
-    lds_barrier();
-    // L2 norms, rounding to the input type (as kda_preprocess stores q^, k^),
-    // and q^.k^ of each new token: wave w takes tokens w, w + 4, ..., its
-    // lanes the channels (all four waves busy, the tokens independent)
-    for (int j = wave; j < J; j += 4) {
-        const float ik = __builtin_amdgcn_rsqf(s_ss[j][1][0] + s_ss[j][1][1] + kL2Eps);
-        const bool vt = j >= na;
-        const float iq = vt ? __builtin_amdgcn_rsqf(s_ss[j][0][0] + s_ss[j][0][1] + kL2Eps) : 0.f;
-        float qk = 0.f;
-        for (int ch = lane; ch < DK; ch += 64) {
-            const float kk = round_to<XT>(s_k[j][ch] * ik);
-            s_k[j][ch] = kk;
-            if (vt) {
-                const float qq = round_to<XT>(s_q[j - na][ch] * iq);
-                s_q[j - na][ch] = qq;
-                qk += qq * kk;
-            }
+    static_assert(kNJ == 2 * NB, "two batches of token slots");
+    load_batch(0);
+    // the state, into registers: read once, right behind the first batch's
+    // token loads, so that it is in flight through the preprocess, the norms
+    // and the small operands
+    float Sr[SP][V];
+#pragma unroll
+    for (int s = 0; s < SP; ++s) {
+        if constexpr (V == 2) {
+            const i32x2 x = __builtin_amdgcn_raw_buffer_load_b64(srsrc, Soff, 4 * DV * s, 0);
+            Sr[s][0] = __int_as_float(x.x);
+            Sr[s][1] = __int_as_float(x.y);
+        } else {
+            Sr[s][0] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(srsrc, Soff, 4 * DV * s, 0));
         }
-        if (vt) {
-            qk = wave_sum(qk);
-            if (lane == 0) s_qk[j - na] = qk;
+    }
+    compute_batch(0);
+    if (J > NB) {
+        load_batch(NB);
+        compute_batch(NB);
+    }
+
+    lds_barrier();
+    // L2 norms, rounding to the input type (as kda_preprocess stores q^, k^):
+    // wave w takes tokens w, w + 4, ..., its lanes the channels
+    for (int j = wave; j < J; j += 4) {
+        const float ik = __builtin_amdgcn_rsqf(s_ss[j * 4 + 2] + s_ss[j * 4 + 3] + kL2Eps);
+        const bool vt = j >= na;
+        const float iq = vt ? __builtin_amdgcn_rsqf(s_ss[j * 4] + s_ss[j * 4 + 1] + kL2Eps) : 0.f;
+        for (int ch = lane; ch < DK; ch += 64) {
+            s_k[j * DK + ch] = round_to<XT>(s_k[j * DK + ch] * ik);
+            if (vt) s_q[(j - na) * DK + ch] = round_to<XT>(s_q[(j - na) * DK + ch] * iq);
         }
     }
     lds_barrier();
 
-    // 4. the state, token by token (each wave on its own columns, no barrier):
-    // decay, then u = S'^T k and p = S'^T q,
-    // then S = S' + beta k (v - u)^T and, for a new token, the output
-    // o = p + (q.k) beta (v - u).  One loop over all tokens keeps a single
-    // copy of S in registers; a committed token computes p with k in place of
-    // q (a few FMAs, no branch) and stores no output.  The committed state is
-    // stored once, after the last committed token.
-    for (int j = 0; j < J; ++j) {
-        const bool verify = j >= na;
-        const int t = j - na;
-        const float* qrow = verify ? s_q[t] : s_k[j];
-        float u[4] = {0.f, 0.f, 0.f, 0.f}, p[4] = {0.f, 0.f, 0.f, 0.f};
+    // 3. the call's small operands: X (zero rows pad it to whole 16-row
+    // passes), the commit factors, and A and M, one 16-lane row per entry
+    const int npass = (J + T + 15) >> 4;
+    const int XR = 16 * npass;
+    // (fixed trip counts, unrolled, so that each thread's LDS reads are
+    // issued together rather than one round trip at a time)
+    constexpr int kXPer = (32 * DK + 255) / 256;  // X elements per thread for two passes
 #pragma unroll
-        for (int i = 0; i < RPT; ++i) {
-            const int r = rg + NRG * i;
-            if (r < DK) {
-                const float al = s_a[j][r], kk = s_k[j][r], qq = qrow[r];
-                S[i].x *= al; S[i].y *= al; S[i].z *= al; S[i].w *= al;
-                u[0] += S[i].x * kk; u[1] += S[i].y * kk; u[2] += S[i].z * kk; u[3] += S[i].w * kk;
-                p[0] += S[i].x * qq; p[1] += S[i].y * qq; p[2] += S[i].z * qq; p[3] += S[i].w * qq;
+    for (int m = 0; m < kXPer; ++m) {
+        const int e = tid + 256 * m;
+        const int r = e / DK, ch = e % DK;
+        if (r < XR) {
+            const bool isk = r < J, isq = !isk && r < J + T;
+            const int gr = isk ? r : na + r - J;
+            const float* vrow = isk ? s_k + r * DK : s_q + (r - J) * DK;
+            const float x = (isk || isq) ? __builtin_amdgcn_exp2f(s_G[(isk || isq ? gr : 0) * DK + ch]) * vrow[ch] : 0.f;
+            s_X[r * Sp::XS + ch] = x;
+        }
+    }
+    if (na > 0) {
+        // row 0: 2^{G_{na-1}}; row 1 + i: 2^{G_{na-1} - G_i} k_i (zero for i >= na)
+        constexpr int kKhPer = ((1 + kMaxTok) * DK + 255) / 256;
+#pragma unroll
+        for (int m = 0; m < kKhPer; ++m) {
+            const int e = tid + 256 * m;
+            if (e >= (1 + kMaxTok) * DK) break;
+            const int i = e / DK - 1, ch = e % DK;
+            const float gl_c = s_G[(na - 1) * DK + ch];
+            float f;
+            if (i < 0) f = __builtin_amdgcn_exp2f(gl_c);
+            else if (i < na) f = __builtin_amdgcn_exp2f(gl_c - s_G[i * DK + ch]) * s_k[i * DK + ch];
+            else f = 0.f;
+            s_kh[e] = f;
+        }
+    }
+    {
+        const int npa = J * (J - 1) / 2, npm = T * na + T * (T + 1) / 2;
+        const int grp = tid >> 4, li = tid & 15;
+        for (int p0 = 0; p0 < npa + npm; p0 += 16) {
+            const int p = p0 + grp;
+            int ra, rb;        // rows of the entry's two vectors and its running sums
+            const float* va;   // its left vector (k or q)
+            int dst;
+            if (p < npa) {     // A_jl: j = ra, l = rb
+                int i = 1, base = 0;
+                while (base + i <= p) {
+                    base += i;
+                    ++i;
+                }
+                ra = i;
+                rb = p - base;
+                va = s_k + ra * DK;
+                dst = ra * kNJ + rb;
+            } else {           // M_ti: running sum of token na + t, i = rb
+                const int qq = p < npa + npm ? p - npa : 0;
+                int t = 0, base = 0;
+                while (base + na + t + 1 <= qq) {
+                    base += na + t + 1;
+                    ++t;
+                }
+                ra = na + t;
+                rb = qq - base;
+                va = s_q + t * DK;
+                dst = t * kNJ + rb;
+            }
+            float acc = 0.f;
+            if (p < npa + npm) {
+#pragma unroll
+                for (int m = 0; m < DK / 16; ++m) {
+                    const int ch = li + 16 * m;
+                    acc += va[ch] * s_k[rb * DK + ch] * __builtin_amdgcn_exp2f(s_G[ra * DK + ch] - s_G[rb * DK + ch]);
+                }
+            }
+            acc = row_ror_add<8>(row_ror_add<4>(row_ror_add<2>(row_ror_add<1>(acc))));
+            if (p < npa + npm && li == 0) {
+                if (p < npa) s_ab[dst] = s_beta[ra] * acc;
+                else s_M[dst] = acc;
             }
         }
+    }
+    lds_barrier();
+
+    // 4. P = X S0 on the matrix cores, fp32
+    f32x4 pacc[2][V];
 #pragma unroll
-        for (int cc = 0; cc < 4; ++cc) {  // sums over the wave's row groups
-            u[cc] = wave_sum_stride<CG>(u[cc]);
-            p[cc] = wave_sum_stride<CG>(p[cc]);
-        }
-        const float bt = s_beta[j];
-        float d[4];
+    for (int pp = 0; pp < 2; ++pp)
 #pragma unroll
-        for (int cc = 0; cc < 4; ++cc) d[cc] = bt * (s_v[j][col + cc] - u[cc]);
+        for (int j = 0; j < V; ++j) pacc[pp][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < RPT; ++i) {
-            const int r = rg + NRG * i;
-            if (r < DK) {
-                const float kk = s_k[j][r];
-                S[i].x += kk * d[0]; S[i].y += kk * d[1]; S[i].z += kk * d[2]; S[i].w += kk * d[3];
+    for (int pp = 0; pp < 2; ++pp) {
+        if (pp < npass) {
+            const float* xa = s_X + (16 * pp + ln) * Sp::XS + row0;
+            if constexpr (SP >= 4) {
+                // one group of four A operands ahead (the fences keep the
+                // compiler from reading them all at once, which would hold
+                // SP more registers beside the state)
+                f32x4 av = *reinterpret_cast<const f32x4*>(xa);
+#pragma unroll
+                for (int s4 = 0; s4 < SP; s4 += 4) {
+                    const f32x4 an = *reinterpret_cast<const f32x4*>(xa + (s4 + 4 < SP ? s4 + 4 : s4));
+                    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+#pragma unroll
+                        for (int j = 0; j < V; ++j)
+                            pacc[pp][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[e], Sr[s4 + e][j], pacc[pp][j], 0, 0, 0);
+                    av = an;
+                }
+            } else {
+#pragma unroll
+                for (int s = 0; s < SP; ++s)
+#pragma unroll
+                    for (int j = 0; j < V; ++j)
+                        pacc[pp][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[s], Sr[s][j], pacc[pp][j], 0, 0, 0);
             }
         }
-        if (j + 1 == na) {  // the committed state
+    }
+    lds_barrier();  // every wave is done with X: P takes its place
+    float* const s_P = s_X;  // [NWK][XR][PS], the row groups' partial sums
 #pragma unroll
-            for (int i = 0; i < RPT; ++i) {
-                const int r = rg + NRG * i;
-                if (r < DK) __builtin_nontemporal_store(S[i], reinterpret_cast<f32x4*>(Sp + r * DV + col));
+    for (int pp = 0; pp < 2; ++pp) {
+        if (pp < npass) {
+#pragma unroll
+            for (int j = 0; j < V; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    s_P[(wk * XR + 16 * pp + 4 * lq + i) * Sp::PS + col0 + j] = pacc[pp][j][i];
+        }
+    }
+    lds_barrier();
+
+    // 5. the delta-rule writes u_j by forward substitution and the outputs,
+    // one column per thread
+    if (tid < DV) {
+        const int cc = tid;
+        float u[kNJ];
+#pragma unroll
+        for (int i = 0; i < kNJ; ++i) {
+            u[i] = 0.f;
+            if (i < J) {
+                float pk = 0.f;
+#pragma unroll
+                for (int w = 0; w < Sp::NWK; ++w) pk += s_P[(w * XR + i) * Sp::PS + cc];
+                float r = s_beta[i] * (s_v[i * DV + cc] - pk);
+#pragma unroll
+                for (int l = 0; l < i; ++l) r -= s_ab[i * kNJ + l] * u[l];
+                u[i] = r;
             }
         }
-        if (verify && rg == 0) {
-            const float qk = s_qk[t];
-            float o[4];
+        // (U of the committed tokens goes where k was: every read of k is done)
 #pragma unroll
-            for (int cc = 0; cc < 4; ++cc) o[cc] = p[cc] + qk * d[cc];
+        for (int i = 0; i < kMaxTok; ++i)
+            if (i < na) s_U[i * DV + cc] = u[i];
 #pragma unroll
-            for (int cc = 0; cc < 4; ++cc) o[cc] *= s_z[t][col + cc];  // (1 without a gate)
-            st4(a.out + ((static_cast<int64_t>(bb) * T + t) * H + h) * DV + col, o);
+        for (int t = 0; t < kMaxTok; ++t) {
+            if (t < T) {
+                float o = 0.f;
+#pragma unroll
+                for (int w = 0; w < Sp::NWK; ++w) o += s_P[(w * XR + J + t) * Sp::PS + cc];
+#pragma unroll
+                for (int i = 0; i < kNJ; ++i)
+                    if (i <= na + t) o += s_M[t * kNJ + i] * u[i];
+                st(a.out + ((static_cast<int64_t>(bb) * T + t) * H + h) * DV + cc, o * s_z[t * DV + cc]);
+            }
+        }
+    }
+    if (na == 0) return;  // nothing committed: the state stays as it is
+    lds_barrier();
+
+    // 6. the committed state, in place: S = Diag(2^{G_{na-1}}) S0 + sum_i K^_i u_i^T
+    // f: the factors of this lane's rows in one row of the table (2^G, or
+    // K^ of committed token i); applied four rows at a time
+    auto rows4 = [&](const float* f, const int s4, float (&fv)[4]) {
+        if constexpr (SP >= 4) {
+            const f32x4 x = *reinterpret_cast<const f32x4*>(f + row0 + s4);
+            fv[0] = x.x; fv[1] = x.y; fv[2] = x.z; fv[3] = x.w;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) fv[e] = s4 + e < SP ? f[row0 + s4 + e] : 0.f;
+        }
+    };
+#pragma unroll
+    for (int s4 = 0; s4 < SP; s4 += 4) {
+        float fv[4];
+        rows4(s_kh, s4, fv);
+#pragma unroll
+        for (int e = 0; e < 4 && s4 + e < SP; ++e)
+#pragma unroll
+            for (int j = 0; j < V; ++j) Sr[s4 + e][j] *= fv[e];
+    }
+#pragma unroll
+    for (int i = 0; i < kMaxTok; ++i) {
+        if (i < na) {
+            float ui[V];
+#pragma unroll
+            for (int j = 0; j < V; ++j) ui[j] = s_U[i * DV + col0 + j];
+#pragma unroll
+            for (int s4 = 0; s4 < SP; s4 += 4) {
+                float fv[4];
+                rows4(s_kh + (1 + i) * DK, s4, fv);
+#pragma unroll
+                for (int e = 0; e < 4 && s4 + e < SP; ++e)
+#pragma unroll
+                    for (int j = 0; j < V; ++j) Sr[s4 + e][j] += fv[e] * ui[j];
+            }
+        }
+    }
+#pragma unroll
+    for (int s = 0; s < SP; ++s) {
+        if constexpr (V == 2) {
+            __builtin_amdgcn_raw_buffer_store_b64(i32x2{__float_as_int(Sr[s][0]), __float_as_int(Sr[s][1])}, srsrc,
+                                                  Soff, 4 * DV * s, kNonTemporal);
+        } else {
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(Sr[s][0]), srsrc, Soff, 4 * DV * s, kNonTemporal);
         }
     }
 }
@@ -296,8 +540,9 @@ hipError_t launch_typed(const SpecArgs& s, hipStream_t st) {
     k.drafts = static_cast<XT*>(s.drafts); k.out = static_cast<XT*>(s.out);
     const int64_t grid = static_cast<int64_t>(s.B) * s.H;
     if (grid == 0) return hipSuccess;
+    const size_t lds = static_cast<size_t>(SpecLds<DK, DV>(s.T).total) * sizeof(float);
     LaunchTimer timer("spec_verify", st);
-    hipLaunchKernelGGL((spec_kernel<DK, DV, XT>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, st, k);
+    hipLaunchKernelGGL((spec_kernel<DK, DV, XT>), dim3(static_cast<unsigned>(grid)), dim3(256), lds, st, k);
     return hipGetLastError();
 }
 
