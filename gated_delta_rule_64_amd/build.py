@@ -58,7 +58,9 @@ def build(verbose: bool = False, jobs: int = 8, force: bool = True) -> str:
     with ThreadPoolExecutor(max(1, jobs)) as ex:
         objs = list(ex.map(lambda s: _compile(s, force), srcs))
     tmp = LIB + ".tmp"
-    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    # --no-undefined: a symbol left undefined (e.g. a kernel whose host-side
+    # launch stub was not emitted) fails the build here, not at load time
+    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,--no-undefined", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")

@@ -45,6 +45,23 @@ typedef int i32x2 __attribute__((ext_vector_type(2)));
 constexpr int kBufferDword3 = 0x00020000;
 constexpr int kNonTemporal = 2;
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 16 bytes from global memory straight into LDS: lane l's bytes land at
+// lds_dst + 16 l (lds_dst is the same for the whole wave)
+__device__ __forceinline__ void lds_copy16(const void* gsrc, char* lds_dst) {
+    __builtin_amdgcn_global_load_lds(gsrc, (lds_void*)(lds_dst), 16, 0, 0);
+}
+
+// wait until at most N of this wave's global memory operations are in flight
+template <int N>
+__device__ __forceinline__ void wait_vmem_but() {
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 constexpr int kMaxTok = kSpecMaxTokens;
 constexpr int kNJ = 2 * kMaxTok;  // committed + new tokens at most
 
@@ -81,10 +98,11 @@ struct SpecSplit {
 };
 
 // Dynamic LDS of one workgroup, float offsets; jm = kMaxTok + T token rows at
-// most, X and P padded to whole 16-row passes.
-template <int DK, int DV>
+// most, X and P padded to whole 16-row passes; XB bytes per input element.
+template <int DK, int DV, int XB>
 struct SpecLds {
-    int k, G, v, q, z, xp, kh, u, ab, m, beta, ss, total;
+    static constexpr int MW = DK > DV ? DK : DV;  // row width of the raw staging
+    int k, G, v, q, z, beta, xp, kh, u, ab, m, st, total;
     __host__ __device__ explicit SpecLds(int T) {
         typedef SpecSplit<DK, DV> Sp;
         const int jm = kMaxTok + T, xr = 16 * ((jm + T + 15) / 16);
@@ -94,25 +112,31 @@ struct SpecLds {
         v = G + jm * DK;                // v                 [jm][DV]
         q = v + jm * DV;                // normalized q      [T][DK]
         z = q + T * DK;                 // sigmoid(out gate) [T][DV]
-        xp = z + T * DV;                // X, then P
+        beta = z + T * DV;              // [kNJ]
+        // from here on, space that is first written after the preprocess
+        xp = beta + 16 * ((kNJ + 15) / 16);  // X, then P (16-float aligned)
         kh = xp + (xsz > psz ? xsz : psz);  // commit factors [1 + kMaxTok][DK]
         // U of the committed tokens [kMaxTok][DV]: in k's place once k is read
         u = kMaxTok * DV <= jm * DK ? k : kh + (1 + kMaxTok) * DK;
         ab = (u == k ? kh + (1 + kMaxTok) * DK : u + kMaxTok * DV);  // beta_j A_jl [kNJ][kNJ]
         m = ab + kNJ * kNJ;             // M [kMaxTok][kNJ]
-        beta = m + kMaxTok * kNJ;       // [kNJ]
-        ss = beta + kNJ;                // norm partial sums [kNJ][2][2]
-        total = ss + 4 * kNJ;
+        const int end = m + kMaxTok * kNJ;
+        // the call's raw rows as loaded, for the preprocess: [4 jm][MW] (q, k,
+        // v, g of every token), then [T][MW] output-gate logits; over X and
+        // what follows it
+        st = xp;
+        const int st_end = st + (4 * jm + T) * MW * XB / 4;
+        total = end > st_end ? end : st_end;
     }
 };
 
 // One 256-thread workgroup per (sequence, head).  Preprocess roles: threads
 // 0..127 run channel tid of q and k, threads 128..255 channel tid-128 of v
-// and of the decay logits (both wave-uniform).  Register budget: three
-// workgroups per CU (at four the 128 x 128 state spills, which measured
-// slower).
+// and of the decay logits (both wave-uniform).  Register budget: four
+// workgroups per CU (128 VGPRs; at d = 128 one 64-bit value spills, reloaded
+// only after the state has arrived), measured faster than three.
 template <int DK, int DV, typename XT>
-__global__ __launch_bounds__(256, 3) void spec_kernel(SpecK<XT> a) {
+__global__ __launch_bounds__(256, 4) void spec_kernel(SpecK<XT> a) {
     typedef SpecSplit<DK, DV> Sp;
     constexpr int W = spec_draft_width(DK, DV);
     constexpr int SP = Sp::SP, V = Sp::V;
@@ -137,7 +161,7 @@ __global__ __launch_bounds__(256, 3) void spec_kernel(SpecK<XT> a) {
     const int J = na + T;
     if (J == 0) return;  // nothing to commit, nothing to verify
 
-    const SpecLds<DK, DV> L(T);
+    const SpecLds<DK, DV, sizeof(XT)> L(T);
     float* const s_k = sm + L.k;
     float* const s_G = sm + L.G;
     float* const s_v = sm + L.v;
@@ -149,7 +173,8 @@ __global__ __launch_bounds__(256, 3) void spec_kernel(SpecK<XT> a) {
     float* const s_ab = sm + L.ab;
     float* const s_M = sm + L.m;
     float* const s_beta = sm + L.beta;
-    float* const s_ss = sm + L.ss;
+    XT* const s_raw = reinterpret_cast<XT*>(sm + L.st);
+    constexpr int MW = SpecLds<DK, DV, sizeof(XT)>::MW;
 
     // this lane's part of the state (see SpecSplit)
     const int wc = wave % Sp::NWC, wk = wave / Sp::NWC;
@@ -165,8 +190,7 @@ __global__ __launch_bounds__(256, 3) void spec_kernel(SpecK<XT> a) {
         __builtin_amdgcn_make_buffer_rsrc(a.state + sbh * (DK * DV), 0, DK * DV * 4, kBufferDword3);
     const int Soff = 4 * (row0 * DV + col0);
 
-    // where this thread's raw values live: committed token j < na in the
-    // draft buffer, new token t = j - na in the inputs; its conv taps and the
+    // this thread's channel of its two tensors, their conv taps and the
     // committed conv history
     const bool lower = tid < 128;           // q, k  |  v, decay logit
     const int c = lower ? tid : tid - 128;  // channel
@@ -178,14 +202,8 @@ __global__ __launch_bounds__(256, 3) void spec_kernel(SpecK<XT> a) {
     float* hp0 = cs + (lower ? static_cast<int64_t>(h) * DK : static_cast<int64_t>(2) * H * DK + static_cast<int64_t>(h) * DV) + c0;
     float* hp1 = cs + static_cast<int64_t>(H) * DK + static_cast<int64_t>(h) * DK + c1;
     XT* dr = a.drafts + (static_cast<int64_t>(slot) * kMaxTok * H + h) * W;  // token j at dr + j*H*W
-    const int d_off0 = lower ? c0 : 2 * DK + c0;      // q | v
-    const int d_off1 = lower ? DK + c1 : 2 * DK + DV + c1;  // k | g
-    const XT* in0 = lower ? a.q_in : a.v_in;
-    const XT* in1 = lower ? a.k_in : a.g;
-    const int64_t row0_in = lower ? static_cast<int64_t>(H) * DK : static_cast<int64_t>(H) * DV;
     const int64_t col0_in = lower ? static_cast<int64_t>(h) * DK + c0 : static_cast<int64_t>(h) * DV + c0;
     const int64_t col1_in = static_cast<int64_t>(h) * DK + c1;
-    const int64_t row1_in = static_cast<int64_t>(H) * DK;
     float w0[4], w1[4], h0[3], h1[3];
     ld4((lower ? a.w_q : a.w_v) + col0_in * 4, w0);
     ld4(a.w_k + col1_in * 4, w1);
@@ -195,31 +213,70 @@ __global__ __launch_bounds__(256, 3) void spec_kernel(SpecK<XT> a) {
         h1[m] = hp1[m * cs_width];
     }
 
-    // 1. preprocess every token in order, eight token slots at a time (the
-    // second eight only when there are more than eight tokens; a slot past J
-    // re-reads token J-1, no extra traffic, and is ignored): conv against
-    // the running history (written back to the pool once the committed tokens
-    // are through), new raw tokens saved to the draft buffer, the norms'
-    // partial sums, the gates and the running log decay.
-    constexpr int NB = 8;
+    // 1. The call's raw rows go to LDS first, with 16-byte copies straight
+    // into LDS (q, k, v, g of every token, committed ones from the draft
+    // buffer, new ones from the inputs, and the new tokens' output-gate
+    // logits): a wave moves 1 KB per copy, and the per-channel preprocess
+    // below reads its values from there.
     const bool has_z = a.z != nullptr;
-    const int64_t row_z = static_cast<int64_t>(H) * DV, col_z = static_cast<int64_t>(h) * DV + (c & (DV - 1));
-    float x0[NB], x1[NB], xb[NB], xz[NB];
+    {
+        constexpr int CPR = MW * static_cast<int>(sizeof(XT)) / 16;  // 16-byte chunks per staged row
+        constexpr int EPC = 16 / static_cast<int>(sizeof(XT));       // elements per chunk
+        const int nrow = 4 * J + (has_z ? T : 0);
+        const int nblk = (nrow * CPR + 63) / 64;
+        for (int blk = wave; blk < nblk; blk += 4) {
+            const int e = 64 * blk + lane;
+            const int rho = e / CPR, el = (e % CPR) * EPC;
+            const XT* src = nullptr;
+            int width = 0;
+            if (rho < 4 * J) {
+                const int j = rho >> 2, tau = rho & 3;  // q, k, v, g
+                width = tau == 2 ? DV : DK;
+                if (j < na) {
+                    const int off = tau == 0 ? 0 : (tau == 1 ? DK : (tau == 2 ? 2 * DK : 2 * DK + DV));
+                    src = dr + static_cast<int64_t>(j) * H * W + off;
+                } else {
+                    const int64_t t = static_cast<int64_t>(bb) * T + (j - na);
+                    const XT* base = tau == 0 ? a.q_in : (tau == 1 ? a.k_in : (tau == 2 ? a.v_in : a.g));
+                    src = base + (t * H + h) * width;
+                }
+            } else if (rho < nrow) {
+                width = DV;
+                src = a.z + ((static_cast<int64_t>(bb) * T + (rho - 4 * J)) * H + h) * DV;
+            }
+            if (el < width) lds_copy16(src + el, reinterpret_cast<char*>(s_raw) + blk * 1024);
+        }
+    }
+
+    // Then the preprocess of every token in order, eight token slots at a
+    // time (the second eight only when there are more than eight tokens; a
+    // slot past J re-reads token J-1 and is ignored): conv against the
+    // running history (written back to the pool once the committed tokens are
+    // through), the norms' partial sums, the gates and the running log decay.
+    constexpr int NB = 8;
+    const int zc = c & (DV - 1);
+    float x0[NB], x1[NB], xz[NB];
+    // The write logits: lane j of wave 2 loads token j's (one load for all
+    // tokens, issued with the staging copies), turns it into beta and, for a
+    // new token, keeps it in the draft buffer.  A lane's store follows its own
+    // load, and all of the wave's loads are one instruction, so a committed
+    // logit is read before any new one replaces it.
+    // (Every wave issues the load, lanes past J on token 0's address: a load
+    // under a branch would be waited for inside it, before the state's loads
+    // go out.)
+    const int jl = lane < J ? lane : 0;
+    const int64_t tl = static_cast<int64_t>(bb) * T + (jl < na ? 0 : jl - na);
+    const float bj = ld(jl < na ? dr + static_cast<int64_t>(jl) * H * W + 3 * DK + DV : a.b + tl * H + h);
     auto load_batch = [&](const int j0) {
+        const int tau0 = lower ? 0 : 2, tau1 = lower ? 1 : 3;
 #pragma unroll
         for (int jb = 0; jb < NB; ++jb) {
             const int j = j0 + jb;
             const int jj = j < J ? j : J - 1;
-            // the source by selects, not branches (a load inside a branch
-            // would have its value converted, and waited for, there)
-            const bool draft = jj < na;
-            const XT* pd = dr + static_cast<int64_t>(jj) * H * W;
-            const int64_t t = static_cast<int64_t>(bb) * T + (draft ? 0 : jj - na);
-            x0[jb] = ld(draft ? pd + d_off0 : in0 + t * row0_in + col0_in);
-            x1[jb] = ld(draft ? pd + d_off1 : in1 + t * row1_in + col1_in);
-            xb[jb] = ld(draft ? pd + 3 * DK + DV : a.b + t * H + h);
-            // output-gate logit of a new token (any valid address otherwise)
-            xz[jb] = ld(draft || !has_z ? pd : a.z + t * row_z + col_z);
+            x0[jb] = ld(s_raw + (4 * jj + tau0) * MW + c0);
+            x1[jb] = ld(s_raw + (4 * jj + tau1) * MW + c1);
+            // output-gate logit of a new token (staged only for those)
+            xz[jb] = has_z && jj >= na ? ld(s_raw + (4 * J + (jj - na)) * MW + zc) : 0.f;
         }
     };
     float gl = 0.f;  // running log2 decay of channel c (upper half)
@@ -242,25 +299,7 @@ __global__ __launch_bounds__(256, 3) void spec_kernel(SpecK<XT> a) {
                     for (int m = 0; m < 3; ++m) hp1[m * cs_width] = h1[m];
                 }
             }
-            if (j >= na) {  // new token: keep its raw values for the next call
-                XT* p = dr + static_cast<int64_t>(j - na) * H * W;
-                // Every element of a draft slot has one owner thread, which
-                // both reads the committed value (first loop) and writes the
-                // new one, so a slot is never rewritten by a thread other
-                // than the one that read it: q / k channel c by thread c, v /
-                // decay channel c by thread 128 + c, and the write logit by
-                // thread 128, the thread that turns it into beta below.
-                if (act0) st(p + d_off0, x0[jb]);
-                if (act1) st(p + d_off1, x1[jb]);
-                if (tid == 128) st(p + 3 * DK + DV, xb[jb]);
-            }
             if (lower) {
-                const float sk = wave_sum(act1 ? y1 * y1 : 0.f);
-                const float sq = j >= na ? wave_sum(act0 ? y0 * y0 : 0.f) : 0.f;
-                if (lane == 0) {
-                    s_ss[j * 4 + wave] = sq;
-                    s_ss[j * 4 + 2 + wave] = sk;
-                }
                 if (act1) {
                     s_k[j * DK + c] = y1;
                     if (j >= na) s_q[(j - na) * DK + c] = y0;
@@ -270,15 +309,16 @@ __global__ __launch_bounds__(256, 3) void spec_kernel(SpecK<XT> a) {
                 if (act0 && j >= na) s_z[(j - na) * DV + c] = has_z ? sigmoid(xz[jb]) : 1.f;
                 gl -= softplus_log2(x1[jb]);
                 if (act1) s_G[j * DK + c] = gl;
-                if (tid == 128) s_beta[j] = sigmoid_fast(xb[jb]);
             }
         }
     };
     static_assert(kNJ == 2 * NB, "two batches of token slots");
-    load_batch(0);
-    // the state, into registers: read once, right behind the first batch's
-    // token loads, so that it is in flight through the preprocess, the norms
-    // and the small operands
+    // (no memory operation moves across: the counted wait below relies on
+    // the state's loads being the last ones issued)
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    // the state, into registers: read once, right behind the staging copies,
+    // so that it is in flight through the preprocess, the norms and the small
+    // operands
     float Sr[SP][V];
 #pragma unroll
     for (int s = 0; s < SP; ++s) {
@@ -290,6 +330,29 @@ __global__ __launch_bounds__(256, 3) void spec_kernel(SpecK<XT> a) {
             Sr[s][0] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(srsrc, Soff, 4 * DV * s, 0));
         }
     }
+    // the staging copies (and the write logits) have landed once no more than
+    // the state's loads are in flight
+    wait_vmem_but<SP>();
+    if (wave == 2 && lane < J) {
+        s_beta[lane] = sigmoid_fast(bj);
+        if (lane >= na) st(dr + static_cast<int64_t>(lane - na) * H * W + 3 * DK + DV, bj);
+    }
+    lds_barrier();
+    // The new tokens' raw q, k, v, g rows to the draft buffer for the next
+    // call (16-byte copies out of the staging rows).  Every read of the
+    // buffer's committed rows landed before the barrier above.
+    {
+        constexpr int EPC = 16 / static_cast<int>(sizeof(XT));
+        constexpr int CPT = (3 * DK + DV) / EPC;  // chunks of one draft row's q, k, v, g
+        for (int e = tid; e < T * CPT; e += 256) {
+            const int t = e / CPT, el = (e % CPT) * EPC;
+            const int tau = el < DK ? 0 : (el < 2 * DK ? 1 : (el < 2 * DK + DV ? 2 : 3));
+            const int off = tau == 0 ? 0 : (tau == 1 ? DK : (tau == 2 ? 2 * DK : 2 * DK + DV));
+            const uint4 v4 = *reinterpret_cast<const uint4*>(s_raw + (4 * (na + t) + tau) * MW + (el - off));
+            *reinterpret_cast<uint4*>(dr + static_cast<int64_t>(t) * H * W + el) = v4;
+        }
+    }
+    load_batch(0);
     compute_batch(0);
     if (J > NB) {
         load_batch(NB);
@@ -298,14 +361,31 @@ __global__ __launch_bounds__(256, 3) void spec_kernel(SpecK<XT> a) {
 
     lds_barrier();
     // L2 norms, rounding to the input type (as kda_preprocess stores q^, k^):
-    // wave w takes tokens w, w + 4, ..., its lanes the channels
+    // wave w takes tokens w, w + 4, ..., its lanes the channels (DK / 64 or
+    // one each), and sums the squares across the wave
+    constexpr int CPL = DK >= 64 ? DK / 64 : 1;  // channels per lane
     for (int j = wave; j < J; j += 4) {
-        const float ik = __builtin_amdgcn_rsqf(s_ss[j * 4 + 2] + s_ss[j * 4 + 3] + kL2Eps);
         const bool vt = j >= na;
-        const float iq = vt ? __builtin_amdgcn_rsqf(s_ss[j * 4] + s_ss[j * 4 + 1] + kL2Eps) : 0.f;
-        for (int ch = lane; ch < DK; ch += 64) {
-            s_k[j * DK + ch] = round_to<XT>(s_k[j * DK + ch] * ik);
-            if (vt) s_q[(j - na) * DK + ch] = round_to<XT>(s_q[(j - na) * DK + ch] * iq);
+        const int tq = vt ? j - na : 0;
+        float kv[CPL], qv[CPL], sk = 0.f, sq = 0.f;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const int ch = lane + 64 * i;
+            const bool in = ch < DK;
+            kv[i] = in ? s_k[j * DK + ch] : 0.f;
+            qv[i] = in && vt ? s_q[tq * DK + ch] : 0.f;
+            sk += kv[i] * kv[i];
+            sq += qv[i] * qv[i];
+        }
+        const float ik = __builtin_amdgcn_rsqf(wave_sum(sk) + kL2Eps);
+        const float iq = __builtin_amdgcn_rsqf(wave_sum(sq) + kL2Eps);
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const int ch = lane + 64 * i;
+            if (ch < DK) {
+                s_k[j * DK + ch] = round_to<XT>(kv[i] * ik);
+                if (vt) s_q[tq * DK + ch] = round_to<XT>(qv[i] * iq);
+            }
         }
     }
     lds_barrier();
@@ -353,25 +433,24 @@ __global__ __launch_bounds__(256, 3) void spec_kernel(SpecK<XT> a) {
             int ra, rb;        // rows of the entry's two vectors and its running sums
             const float* va;   // its left vector (k or q)
             int dst;
-            if (p < npa) {     // A_jl: j = ra, l = rb
-                int i = 1, base = 0;
-                while (base + i <= p) {
-                    base += i;
-                    ++i;
-                }
+            if (p < npa) {     // A_jl: j = ra, l = rb; row j starts at entry j (j - 1) / 2
+                int i = static_cast<int>((1.f + __builtin_sqrtf(1.f + 8.f * p)) * 0.5f);
+                i += (i * (i + 1)) / 2 <= p;   // (the float root may land one off)
+                i -= (i * (i - 1)) / 2 > p;
                 ra = i;
-                rb = p - base;
+                rb = p - (i * (i - 1)) / 2;
                 va = s_k + ra * DK;
                 dst = ra * kNJ + rb;
-            } else {           // M_ti: running sum of token na + t, i = rb
+            } else {           // M_ti: running sum of token na + t, i = rb; row t holds
+                               // na + 1 + t entries, starting at entry t (na + 1) + t (t - 1) / 2
                 const int qq = p < npa + npm ? p - npa : 0;
-                int t = 0, base = 0;
-                while (base + na + t + 1 <= qq) {
-                    base += na + t + 1;
-                    ++t;
-                }
+                const float b2 = 2.f * na + 1.f;
+                int t = static_cast<int>((__builtin_sqrtf(b2 * b2 + 8.f * qq) - b2) * 0.5f);
+                t = t < 0 ? 0 : t;
+                t += (t + 1) * (na + 1) + ((t + 1) * t) / 2 <= qq;
+                t -= t * (na + 1) + (t * (t - 1)) / 2 > qq;
                 ra = na + t;
-                rb = qq - base;
+                rb = qq - (t * (na + 1) + (t * (t - 1)) / 2);
                 va = s_q + t * DK;
                 dst = t * kNJ + rb;
             }
@@ -442,27 +521,27 @@ __global__ __launch_bounds__(256, 3) void spec_kernel(SpecK<XT> a) {
     lds_barrier();
 
     // 5. the delta-rule writes u_j by forward substitution and the outputs,
-    // one column per thread
+    // one column per thread.  Branch-free over the 16 token slots (slots past
+    // J read row 0 and are zeroed by a select), so the compiler can issue the
+    // LDS reads of all steps together instead of one step at a time.
     if (tid < DV) {
         const int cc = tid;
         float u[kNJ];
 #pragma unroll
         for (int i = 0; i < kNJ; ++i) {
-            u[i] = 0.f;
-            if (i < J) {
-                float pk = 0.f;
+            const int ir = i < J ? i : 0;
+            float pk = 0.f;
 #pragma unroll
-                for (int w = 0; w < Sp::NWK; ++w) pk += s_P[(w * XR + i) * Sp::PS + cc];
-                float r = s_beta[i] * (s_v[i * DV + cc] - pk);
+            for (int w = 0; w < Sp::NWK; ++w) pk += s_P[(w * XR + ir) * Sp::PS + cc];
+            float r = s_beta[ir] * (s_v[ir * DV + cc] - pk);
 #pragma unroll
-                for (int l = 0; l < i; ++l) r -= s_ab[i * kNJ + l] * u[l];
-                u[i] = r;
-            }
+            for (int l = 0; l < i; ++l) r -= s_ab[i * kNJ + l] * u[l];
+            u[i] = i < J ? r : 0.f;
         }
-        // (U of the committed tokens goes where k was: every read of k is done)
+        // (U of the committed tokens goes where k was: every read of k is
+        // done; the commit reads rows i < na only)
 #pragma unroll
-        for (int i = 0; i < kMaxTok; ++i)
-            if (i < na) s_U[i * DV + cc] = u[i];
+        for (int i = 0; i < kMaxTok; ++i) s_U[i * DV + cc] = u[i];
 #pragma unroll
         for (int t = 0; t < kMaxTok; ++t) {
             if (t < T) {
@@ -470,8 +549,7 @@ __global__ __launch_bounds__(256, 3) void spec_kernel(SpecK<XT> a) {
 #pragma unroll
                 for (int w = 0; w < Sp::NWK; ++w) o += s_P[(w * XR + J + t) * Sp::PS + cc];
 #pragma unroll
-                for (int i = 0; i < kNJ; ++i)
-                    if (i <= na + t) o += s_M[t * kNJ + i] * u[i];
+                for (int i = 0; i < kNJ; ++i) o += (i <= na + t ? s_M[t * kNJ + i] : 0.f) * u[i];
                 st(a.out + ((static_cast<int64_t>(bb) * T + t) * H + h) * DV + cc, o * s_z[t * DV + cc]);
             }
         }
@@ -540,7 +618,11 @@ hipError_t launch_typed(const SpecArgs& s, hipStream_t st) {
     k.drafts = static_cast<XT*>(s.drafts); k.out = static_cast<XT*>(s.out);
     const int64_t grid = static_cast<int64_t>(s.B) * s.H;
     if (grid == 0) return hipSuccess;
-    const size_t lds = static_cast<size_t>(SpecLds<DK, DV>(s.T).total) * sizeof(float);
+    const size_t lds = static_cast<size_t>(SpecLds<DK, DV, sizeof(XT)>(s.T).total) * sizeof(float);
+    // (above 64 KB only for fp32 inputs with many tokens at d = 128)
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&spec_kernel<DK, DV, XT>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (e != hipSuccess) return e;
     LaunchTimer timer("spec_verify", st);
     hipLaunchKernelGGL((spec_kernel<DK, DV, XT>), dim3(static_cast<unsigned>(grid)), dim3(256), lds, st, k);
     return hipGetLastError();
