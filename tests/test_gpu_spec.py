@@ -137,6 +137,15 @@ def test_spec_session_token_counts(K, oracle_mod, T):
     _session(K, oracle_mod, B=3, H=2, dk=64, dv=64, x_dtype="f32", T=T, ncalls=3, seed=10 + T, pool_extra=1)
 
 
+def test_spec_session_largest_call(K, oracle_mod):
+    """The largest call the kernel takes: 8 new and up to 8 committed tokens
+    at d = 128 with fp32 inputs, whose LDS (raw rows staged as fp32, two
+    16-row product passes) is above the 64 KB a launch gets by default, and
+    a non-square head (dk = 16, dv = 128) with the same token counts."""
+    _session(K, oracle_mod, B=3, H=2, dk=128, dv=128, x_dtype="f32", T=8, ncalls=3, seed=88, pool_extra=1)
+    _session(K, oracle_mod, B=3, H=2, dk=16, dv=128, x_dtype="f32", T=8, ncalls=3, seed=89)
+
+
 def test_spec_session_commit_each_call(K, oracle_mod):
     """Verify, then a commit-only call (T = 0), every step."""
     _session(K, oracle_mod, B=4, H=2, dk=128, dv=64, x_dtype="bf16", T=4, ncalls=3, seed=5, lazy=False)
