@@ -1095,60 +1095,73 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
 // ---------------------------------------------------------------------------
 
 // One workgroup per (sequence, head, group of SB 16-column slices of the
-// state), with three roles.  Per slice, a chain wave keeps the slice's state
-// in registers and runs the recurrence, and an output wave computes the
-// gated output from the state the chain wave hands over in LDS (see the
-// compute section).  Inside the chunk loop they touch only LDS, reading the
-// chunk's factors and writing the gated output tile to an LDS staging area.
-// Four memory waves do all global traffic: they copy what a chunk needs into
-// one of two LDS buffers with global_load_lds_dwordx4 and store the staged
-// output as whole row pieces.  A chunk is copied in two parts: the part the
-// first half of a step reads (-W, Q', the group's U~ and M U~ tiles, its gate
-// logits) as soon as the compute waves are done with it two chunks back, and
-// the part the second half reads (K^T, gamma) one step ahead.  Every memory
-// wave issues the same number of operations every step (a wave with no piece
-// of some tile makes a one-lane copy into a dump area), so a fixed count
-// (vmcnt) tells when a part has landed while later ones stay in flight:
-// vector memory operations of one wave retire in issue order.
+// state), with three roles.  Per slice, chain waves keep the slice's state in
+// registers and run the recurrence: with one slice per workgroup two of them,
+// each holding half of the state's rows (one wave reads LDS at a limited
+// rate, and a step reads 40 KB of factors; split, each wave reads half and
+// the two swap their partial products of U once a step), with two slices one
+// (the LDS has no room for the partial products).  Two output waves compute
+// the gated output from the state operand the chain waves hand over in LDS
+// (see the compute section); each takes half of the row tiles of every
+// slice, so that between them they load the chunk's Q' (the same for every
+// slice) once, straight from the record into registers, one chunk ahead.
+// Four memory waves do the rest of the global traffic: they copy what the
+// chain and output waves read from LDS (-W, K^T, gamma, the group's U~ and
+// M U~ tiles and its gate logits) into one of three LDS slots with
+// global_load_lds_dwordx4, and store the staged output as whole row pieces.
+// Chunk j+2's copies go out in step j, half after each of its two barriers:
+// its slot held chunk j-1, whose readers are done by then.  So the copies
+// overlap the compute waves' work instead of holding back a barrier (the
+// CU's path into LDS bounds them, and a chunk's copies and Q' loads keep it
+// busy for about a whole step), and each chunk has about two steps to land.
+// Every memory wave issues the same number of copies per chunk (a wave with
+// no piece of some tile makes a one-lane copy into a dump area), so a fixed
+// count (vmcnt) tells when a chunk has landed while the next one stays in
+// flight: vector memory operations of one wave retire in issue order.
 // One slice per workgroup spreads a head over more CUs, which suits few
 // (sequence, head) pairs; two share each copied factor between two slices.
 template <int SB>
 struct StateCfg {
     static_assert(SB == 1 || SB == 2, "1 or 2 slices per workgroup");
     // memory waves: each issues its share of every copy (more of them do not
-    // move a chunk faster: the copies are bound by the CU's path into LDS)
+    // move a chunk faster: the CU's path into LDS bounds the copies)
     static constexpr int kMemWaves = 4;
-    // output waves per slice: two with one slice per workgroup; with two
-    // slices one, which keeps the workgroup at 8 waves (2 per SIMD, so the
-    // chain wave's operands fit in registers)
-    static constexpr int kOutWaves = SB == 1 ? 2 : 1;
-    static constexpr int kCompWaves = 1 + kOutWaves;  // per slice
-    static constexpr int kThreads = 64 * (SB * kCompWaves + kMemWaves);
+    // chain waves per slice, and output waves, each with kOutTiles row tiles
+    // of every slice
+    static constexpr int kChain = SB == 1 ? 2 : 1;
+    static constexpr int kOutWaves = 2;
+    static constexpr int kOutTiles = 4 / kOutWaves;
+    static constexpr int kThreads = 64 * (SB * kChain + kOutWaves + kMemWaves);
     static constexpr int kRowBytes = 32 * SB;             // one token row of the group's columns, bf16
     static constexpr int kPieces = 2 * SB;                // 1 KB pieces of each group tile (U~, M U~, z)
     static constexpr int kPiecesPerWave = (kPieces + kMemWaves - 1) / kMemWaves;
     static constexpr int kRowsPerWave = 64 / kMemWaves;   // output rows each memory wave stores
-    // LDS buffer layout, bytes.  The first 48 KB mirror the record's first 48 KB.
-    static constexpr int B_NEGW = 0;                      // -W, 16 KB
-    static constexpr int B_QP = 16384;                    // Q', 16 KB
-    static constexpr int B_KHT = 32768;                   // K^T, 16 KB
-    static constexpr int B_UT = 49152;                    // U~ of the group's slices, [SB s][4 m][64][4]
+    // LDS slot layout, bytes
+    static constexpr int B_NEGW = 0;                      // -W, 16 KB (the record's first 16 KB)
+    static constexpr int B_KHT = 16384;                   // K^T, 16 KB
+    static constexpr int B_UT = 32768;                    // U~ of the group's slices, [SB s][4 m][64][4]
     static constexpr int B_OI = B_UT + 1024 * kPieces;    // M U~, same layout
     static constexpr int B_Z = B_OI + 1024 * kPieces;     // gate logits [64 tokens][kRowBytes], swizzled
     static constexpr int B_GAM = B_Z + 1024 * kPieces;    // gamma, fp32 [128]
     static constexpr int B_DUMP = B_GAM + 512;            // target of the one-lane filler copies, never read
     static constexpr int B_BYTES = B_DUMP + 64;
-    // operations one memory wave issues per part (wave 0 issues one more in
-    // the second part: gamma) and per output tile
-    static constexpr int kPartA = 32 / kMemWaves + 3 * kPiecesPerWave;
-    static constexpr int kPartB = 16 / kMemWaves;
+    static constexpr int kSlots = 3;
+    // copies one memory wave issues per chunk, in two parts: its -W blocks
+    // and pieces of the three group tiles; its K^T blocks and gamma (a
+    // filler on waves but 0)
+    static constexpr int kCopiesA = 16 / kMemWaves + 3 * kPiecesPerWave;
+    static constexpr int kCopiesB = 16 / kMemWaves + 1;
+    static constexpr int kCopies = kCopiesA + kCopiesB;
     static constexpr int kRowsPerStore = 1024 / kRowBytes;  // rows of kRowBytes one 64-lane store covers
     static constexpr int kStores = (kRowsPerWave + kRowsPerStore - 1) / kRowsPerStore;
-    // after the two buffers: the staged output tile, then per slice the bf16
-    // state operand the chain wave hands to the output wave
-    static constexpr int B_STAGE = 2 * B_BYTES;
+    // after the slots: the staged output tile, per slice the bf16 state
+    // operand the chain waves hand to the output waves, and with two chain
+    // waves a slice their fp32 partial products of U
+    static constexpr int B_STAGE = kSlots * B_BYTES;
     static constexpr int B_SBX = B_STAGE + 64 * kRowBytes;  // [SB s][4 ks][64 lanes][16 B]
-    static constexpr size_t kLds = static_cast<size_t>(B_SBX) + 4096 * SB;
+    static constexpr int B_PART = B_SBX + 4096 * SB;        // [SB s][2 half][4 m][64 lanes][4 fp32]
+    static constexpr size_t kLds = static_cast<size_t>(B_PART) + (kChain == 2 ? 8192 * SB : 0);
+    static_assert(kLds <= 160 * 1024, "one workgroup's LDS");
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -1194,8 +1207,6 @@ __global__ __launch_bounds__(StateCfg<NS>::kThreads) void mfma_state_kernel(Mfma
     constexpr int PR = 2 * SB;           // 16-byte pieces per tile row
     constexpr int ROWS_PER_PIECE = 1024 / RB;
     extern __shared__ __align__(16) char smem[];
-    char* const buf0 = smem;
-    char* const buf1 = smem + C::B_BYTES;
     char* const stage = smem + C::B_STAGE;  // gated output tile, bf16 [64][RB], swizzled
     // blockIdx -> (sequence, head, part): all parts of a (sequence, head) land
     // on one XCD (workgroups are dealt round-robin over the 8 XCDs), so the
@@ -1222,30 +1233,31 @@ __global__ __launch_bounds__(StateCfg<NS>::kThreads) void mfma_state_kernel(Mfma
     auto chunk_len = [&](int j) {
         return static_cast<int>(min(static_cast<int64_t>(kChunk), se - (sb + static_cast<int64_t>(j) * kChunk)));
     };
-    auto buf_of = [&](int j) { return (j & 1) ? buf1 : buf0; };
+    auto slot_of = [&](int j) { return smem + (j % C::kSlots) * C::B_BYTES; };
 
-    constexpr int CW = C::kCompWaves;
-    if (wave >= CW * NS) {
+    constexpr int NO = C::kOutWaves, CH = C::kChain;
+    if (wave >= SB * CH + NO) {
         // ---- memory waves
         if (nch == 0) return;
-        const int wm = wave - CW * NS;
-        // part A of chunk min(j, nch-1): -W, Q', U~, M U~ and gate logits
-        // (past the end it copies the last chunk again into the free buffer
-        // the index selects, so that every step issues the same operations)
+        const int wm = wave - SB * CH - NO;
         constexpr int MW = C::kMemWaves;
         // The workgroups of one head copy the same factors at the same time;
         // each starts its walk over the 1 KB blocks at a different block, so
         // their requests meet different L2 channels.  (A wave still copies the
         // blocks of its own residue mod MW, so the counts do not change.)
         const int rot = MW * part;
+        // Part A (-W and the group tiles) and part B (K^T and gamma) of chunk
+        // min(jn, nch-1) into the slot of jn (past the end they copy the last
+        // chunk again into the free slot the index selects, so that every step
+        // issues the same operations)
         auto issue_a = [&](int jn) {
-            char* buf = buf_of(jn);
+            char* buf = slot_of(jn);
             const int j = min(jn, nch - 1);
             const char* rp = rec_of(j);
 #pragma unroll
-            for (int i = 0; i < 32 / MW; ++i) {
-                const int b = (wm + MW * i + rot) & 31;
-                lds_copy16(rp + b * 1024 + lane * 16, buf + b * 1024);
+            for (int i = 0; i < 16 / MW; ++i) {
+                const int b = (wm + MW * i + rot) & 15;
+                lds_copy16(rp + R_NEGW + b * 1024 + lane * 16, buf + C::B_NEGW + b * 1024);
             }
             const int Lc = chunk_len(j);
             const int64_t tb = sb + static_cast<int64_t>(j) * kChunk;
@@ -1272,35 +1284,33 @@ __global__ __launch_bounds__(StateCfg<NS>::kThreads) void mfma_state_kernel(Mfma
                     lds_copy16(zs, (real && kGate) ? buf + C::B_Z + b * 1024 : buf + C::B_DUMP);
             }
         };
-        // part B of chunk min(j, nch-1): K^T and gamma
         auto issue_b = [&](int jn) {
-            char* buf = buf_of(jn);
-            const int j = min(jn, nch - 1);
-            const char* rp = rec_of(j);
+            char* buf = slot_of(jn);
+            const char* rp = rec_of(min(jn, nch - 1));
 #pragma unroll
             for (int i = 0; i < 16 / MW; ++i) {
-                const int b = 32 + ((wm + MW * i + rot) & 15);
-                lds_copy16(rp + b * 1024 + lane * 16, buf + b * 1024);
+                const int b = (wm + MW * i + rot) & 15;
+                lds_copy16(rp + R_KHT + b * 1024 + lane * 16, buf + C::B_KHT + b * 1024);
             }
-            if (wm == 0 && lane < 32) lds_copy16(rp + R_GAM + lane * 16, buf + C::B_GAM);
+            if (wm == 0 ? lane < 32 : lane == 0)
+                lds_copy16(rp + R_GAM + (wm == 0 ? lane * 16 : 0), wm == 0 ? buf + C::B_GAM : buf + C::B_DUMP);
         };
-        // issue order per step j: [A_j] B(j+1) [M_j] stores(j), A(j+2).
-        // Before A_j parts A and B of chunk j must be in (the chain wave reads
-        // both right after A_j); after B(j) came stores(j-1) and A(j+1).  In
-        // step 0 there were no stores(-1).  (Wave 0's gamma copy is inside
-        // B(j), so the counts after it are the same for every wave.)
-        constexpr int kA = C::kPartA, kS = C::kStores;
+        // issue order per step j: [A_j] A(j+2) [M_j] stores(j), B(j+2).
+        // Before A_j chunk j must be in; after its part B came A(j+1),
+        // stores(j-1) and B(j+1) (in step 0, after B(0) only chunk 1).
+        constexpr int kC = C::kCopies, kS = C::kStores;
         issue_a(0);
         issue_b(0);
         issue_a(1);
+        issue_b(1);
         // store role: rows RW wm .. RW wm + RW-1, ROWS_PER_PIECE of them per
         // instruction
         constexpr int RW = C::kRowsPerWave;
         const int wq = lane % PR;
         for (int j = 0; j < nch; ++j) {
-            if (j == 0) wait_vmcnt<kA>(); else wait_vmcnt<kS + kA>();
-            lds_barrier();  // A_j: parts A and B of chunk j are in LDS; part B of chunk j+1 may be copied
-            issue_b(j + 1);
+            if (j == 0) wait_vmcnt<kC>(); else wait_vmcnt<kC + kS>();
+            lds_barrier();  // A_j: chunk j is in LDS, and the slot of chunk j-1 is free
+            issue_a(j + 2);
             lds_barrier();  // M_j: the output tile of chunk j is staged
             const int Lc = chunk_len(j);
             const int64_t tb = sb + static_cast<int64_t>(j) * kChunk;
@@ -1315,102 +1325,106 @@ __global__ __launch_bounds__(StateCfg<NS>::kThreads) void mfma_state_kernel(Mfma
                 if (rl < RW && r < Lc)
                     *reinterpret_cast<uint4*>(a.out + ((tb + r) * H + h) * 128 + 16 * SB * part + 8 * q) = v;
             }
-            issue_a(j + 2);
+            issue_b(j + 2);
         }
         wait_vmcnt<0>();  // no copy may land after the workgroup has ended
         return;
     }
 
-    // ---- compute waves: CW per 16-column slice ls = wave / CW of the group.
-    // The chain wave (wave % CW == 0) keeps the slice's fp32 state in
-    // registers and runs the recurrence, U = U~ - W S and then S <- Diag(gamma)
-    // S + K^T U; after each update it leaves the state as the bf16
-    // matrix-core operand in LDS.  Its products go contraction step by
-    // contraction step across all row tiles, so the tiles' accumulations are
-    // independent and the matrix core never waits for its own previous result.
-    // The output waves take that operand for the chunk's gated output, O^T =
-    // (M U~)^T + S^T Q'^T, 4 / kOutWaves row tiles each, off the recurrence's
-    // critical path.  Inside the chunk loop the compute waves touch only LDS.
-    // In a step the output waves read the operand before M_j and the chain
-    // wave rewrites it after M_j.
-    const int ls = wave / CW, role = wave - CW * ls;
-    char* const sbx = smem + C::B_SBX + ls * 4096;
-    const int col0 = 16 * (SB * part + ls) + c;
     auto widen = [](uint2 p) {
         return f32x4{__uint_as_float(p.x << 16), __uint_as_float(p.x & 0xffff0000u), __uint_as_float(p.y << 16),
                      __uint_as_float(p.y & 0xffff0000u)};
     };
-    // one row tile of the output: lane (g, c) holds token 16 mt + c, columns
-    // 16 ls + 4 g .. + 3 (the state operand and the Q' operand swap roles)
-    struct OutOps {
-        uint2 op, zp;
-        bf16x8 qa[4];
-    };
-    auto stage_off = [&](int mt) {
-        // columns 16 ls + 4 g .. + 3 of the group: piece 2 ls + g/2, bytes 8 (g & 1)
-        const int r = 16 * mt + c;
-        return r * RB + tile_slot<SB>(r, 2 * ls + (g >> 1)) * 16 + 8 * (g & 1);
-    };
-    auto load_out = [&](const char* cur, int mt, OutOps& x) {
-        x.op = *reinterpret_cast<const uint2*>(cur + C::B_OI + ((ls * 4 + mt) * 64 + lane) * 8);
-        if (kGate) x.zp = *reinterpret_cast<const uint2*>(cur + C::B_Z + stage_off(mt));
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-            x.qa[ks] = *reinterpret_cast<const bf16x8*>(cur + C::B_QP + ((mt * 4 + ks) * 64 + lane) * 16);
-    };
-    if (role == 0) {
-        f32x4 S[8];  // S[t][i] = state[16t + 4g + i][col0]
+    // ---- compute waves.  The CH chain waves of slice ls keep the slice's
+    // fp32 state in registers, 128 / CH rows each, and run the recurrence,
+    // U = U~ - W S and then S <- Diag(gamma) S + K^T U.  Each makes the part
+    // of W S that its rows contribute (the first adds U~); with two, each
+    // hands its part to the other in LDS and both add the two in the same
+    // order-free way (a + b = b + a), so they hold the same U.  After each
+    // update a wave leaves its rows of the state as the bf16 matrix-core
+    // operand in LDS.  Its products go contraction step by contraction step
+    // across all row tiles, so the tiles' accumulations are independent and
+    // the matrix core never waits for its own previous result.  The output
+    // waves take that operand for the chunk's gated output, O^T = (M U~)^T +
+    // S^T Q'^T, off the recurrence's critical path.  In a step the output
+    // waves read the operand before M_j and the chain waves rewrite it after
+    // M_j; the parts of U are written before M_j and read after it.
+    if (wave < SB * CH) {
+        constexpr int NT = 8 / CH;  // 16-row tiles of the state a chain wave holds
+        constexpr int NK = 4 / CH;  // 32-row contraction blocks of W S it makes
+        const int ls = wave / CH, hf = wave % CH;
+        const int t0 = NT * hf;     // its first row tile
+        char* const sbx = smem + C::B_SBX + ls * 4096;
+        f32x4* const part_mine = reinterpret_cast<f32x4*>(smem + C::B_PART + (ls * 2 + hf) * 4096);
+        const f32x4* const part_other = reinterpret_cast<const f32x4*>(smem + C::B_PART + (ls * 2 + 1 - hf) * 4096);
+        const int col0 = 16 * (SB * part + ls) + c;
+        f32x4 S[NT];  // S[t][i] = state[16 (t0 + t) + 4g + i][col0]
         const int64_t sidx = grp * (128 * 128);
         if (a.S0 != nullptr) {  // one uniform branch: all loads in flight together
 #pragma unroll
-            for (int t = 0; t < 8; ++t)
+            for (int t = 0; t < NT; ++t)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) S[t][i] = a.S0[sidx + (16 * t + 4 * g + i) * 128 + col0];
+                for (int i = 0; i < 4; ++i) S[t][i] = a.S0[sidx + (16 * (t0 + t) + 4 * g + i) * 128 + col0];
         } else {
 #pragma unroll
-            for (int t = 0; t < 8; ++t) S[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int t = 0; t < NT; ++t) S[t] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-        bf16x8 Sb[4];
+        bf16x8 Sb[NK];  // contraction blocks NK hf + k
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            Sb[ks] = to_bf16x8(S[2 * ks], S[2 * ks + 1]);
-            *reinterpret_cast<bf16x8*>(sbx + (ks * 64 + lane) * 16) = Sb[ks];
+        for (int k = 0; k < NK; ++k) {
+            Sb[k] = to_bf16x8(S[2 * k], S[2 * k + 1]);
+            *reinterpret_cast<bf16x8*>(sbx + ((NK * hf + k) * 64 + lane) * 16) = Sb[k];
         }
         for (int j = 0; j < nch; ++j) {
-            const char* cur = buf_of(j);
-            lds_barrier();  // A_j: parts A and B of chunk j are in LDS
-            // U = U~ - W S: every operand of the four row tiles read first
+            const char* cur = slot_of(j);
+            lds_barrier();  // A_j: chunk j is in LDS
+            // every operand of the four row tiles of U read first
             uint2 up[4];
-            bf16x8 wa[4][4];
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
+            for (int mt = 0; mt < 4; ++mt)
                 up[mt] = *reinterpret_cast<const uint2*>(cur + C::B_UT + ((ls * 4 + mt) * 64 + lane) * 8);
+            bf16x8 wa[4][NK];
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks)
-                    wa[mt][ks] = *reinterpret_cast<const bf16x8*>(cur + C::B_NEGW + ((mt * 4 + ks) * 64 + lane) * 16);
-            }
-            // K^T and gamma of the state update, read now so they arrive while U is made
-            bf16x8 ka[8][2];
-            float4 gm[8];
+            for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                gm[t] = *reinterpret_cast<const float4*>(cur + C::B_GAM + (16 * t + 4 * g) * 4);
+                for (int k = 0; k < NK; ++k)
+                    wa[mt][k] = *reinterpret_cast<const bf16x8*>(cur + C::B_NEGW + ((mt * 4 + NK * hf + k) * 64 + lane) * 16);
+            // K^T and gamma of the state update (this wave's rows), read now so
+            // they arrive while U is made
+            bf16x8 ka[NT][2];
+            float4 gm[NT];
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                gm[t] = *reinterpret_cast<const float4*>(cur + C::B_GAM + (16 * (t0 + t) + 4 * g) * 4);
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks)
-                    ka[t][ks] = *reinterpret_cast<const bf16x8*>(cur + C::B_KHT + ((t * 2 + ks) * 64 + lane) * 16);
+                    ka[t][ks] = *reinterpret_cast<const bf16x8*>(cur + C::B_KHT + (((t0 + t) * 2 + ks) * 64 + lane) * 16);
             }
-            f32x4 U[4];
+            // Keep the products below every read: interleaved, the compiler
+            // waits for each read in turn, and the step pays the LDS latency
+            // once per read instead of once.  (A single chain wave a slice
+            // has no registers for all of its operands at once.)
+            if constexpr (CH == 2) __builtin_amdgcn_sched_barrier(0);
+            f32x4 U[4];  // U~ (the first wave) + this wave's part of W S
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) U[mt] = widen(up[mt]);
+            for (int mt = 0; mt < 4; ++mt) U[mt] = widen(hf == 0 ? up[mt] : make_uint2(0u, 0u));
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
+            for (int k = 0; k < NK; ++k)
 #pragma unroll
-                for (int mt = 0; mt < 4; ++mt) U[mt] = mfma(wa[mt][ks], Sb[ks], U[mt]);
-            lds_barrier();  // M_j: the output waves are done with the state operand
+                for (int mt = 0; mt < 4; ++mt) U[mt] = mfma(wa[mt][k], Sb[k], U[mt]);
+            if (CH == 2) {
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) part_mine[mt * 64 + lane] = U[mt];
+            }
+            lds_barrier();  // M_j: the output waves are done with the state operand; the parts of U are in
+            if (CH == 2) {
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) U[mt] += part_other[mt * 64 + lane];
+            }
             // S <- Diag(gamma) S + K^T U
             const bf16x8 Ub[2] = {to_bf16x8(U[0], U[1]), to_bf16x8(U[2], U[3])};
 #pragma unroll
-            for (int t = 0; t < 8; ++t) {
+            for (int t = 0; t < NT; ++t) {
                 S[t][0] *= gm[t].x;
                 S[t][1] *= gm[t].y;
                 S[t][2] *= gm[t].z;
@@ -1419,59 +1433,100 @@ __global__ __launch_bounds__(StateCfg<NS>::kThreads) void mfma_state_kernel(Mfma
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-                for (int t = 0; t < 8; ++t) S[t] = mfma(ka[t][ks], Ub[ks], S[t]);
+                for (int t = 0; t < NT; ++t) S[t] = mfma(ka[t][ks], Ub[ks], S[t]);
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                Sb[ks] = to_bf16x8(S[2 * ks], S[2 * ks + 1]);
-                *reinterpret_cast<bf16x8*>(sbx + (ks * 64 + lane) * 16) = Sb[ks];
+            for (int k = 0; k < NK; ++k) {
+                Sb[k] = to_bf16x8(S[2 * k], S[2 * k + 1]);
+                *reinterpret_cast<bf16x8*>(sbx + ((NK * hf + k) * 64 + lane) * 16) = Sb[k];
             }
             // a full chunk that ends a snapshot interval: the state after it
-            // is the sequence's m-th snapshot (this slice's columns)
+            // is the sequence's m-th snapshot (this wave's part of the slice)
             const int sc = a.snap.chunks;
             if (sc > 0 && (j + 1) % sc == 0 && chunk_len(j) == kChunk) {
                 float* so = a.snap.out + ((static_cast<int64_t>(a.snap.off[n]) + (j + 1) / sc - 1) * H + h) * (128 * 128);
 #pragma unroll
-                for (int t = 0; t < 8; ++t)
+                for (int t = 0; t < NT; ++t)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) so[(16 * t + 4 * g + i) * 128 + col0] = S[t][i];
+                    for (int i = 0; i < 4; ++i) so[(16 * (t0 + t) + 4 * g + i) * 128 + col0] = S[t][i];
             }
         }
         if (a.S_out) {
 #pragma unroll
-            for (int t = 0; t < 8; ++t)
+            for (int t = 0; t < NT; ++t)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) a.S_out[sidx + (16 * t + 4 * g + i) * 128 + col0] = S[t][i];
+                for (int i = 0; i < 4; ++i) a.S_out[sidx + (16 * (t0 + t) + 4 * g + i) * 128 + col0] = S[t][i];
         }
     } else {
-        constexpr int TPW = 4 / C::kOutWaves;  // row tiles per output wave
-        const int mt0 = TPW * (role - 1);     // row tiles mt0 .. mt0 + TPW - 1
-        for (int j = 0; j < nch; ++j) {
-            const char* cur = buf_of(j);
-            lds_barrier();  // A_j: part A of chunk j and the state operand are in LDS; the staging tile is free
-            bf16x8 Sb[4];
+        // output wave ow: row tiles mt0 .. mt0 + TPW-1 of every slice.  Lane
+        // (g, c) of a tile holds token 16 mt + c, columns 16 ls + 4 g .. + 3
+        // (the state operand and the Q' operand swap roles).
+        constexpr int TPW = C::kOutTiles;
+        const int mt0 = TPW * (wave - SB * CH);
+        auto stage_off = [&](int ls, int mt) {
+            // columns 16 ls + 4 g .. + 3 of the group: piece 2 ls + g/2, bytes 8 (g & 1)
+            const int r = 16 * mt + c;
+            return r * RB + tile_slot<SB>(r, 2 * ls + (g >> 1)) * 16 + 8 * (g & 1);
+        };
+        // Q' of chunk min(j, nch-1), the wave's row tiles, in the A-operand layout
+        auto load_q = [&](int j, bf16x8 (&q)[TPW][4]) {
+            const char* rp = rec_of(min(j, nch - 1)) + R_QP;
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) Sb[ks] = *reinterpret_cast<const bf16x8*>(sbx + (ks * 64 + lane) * 16);
-            OutOps ops[TPW];
+            for (int u = 0; u < TPW; ++u)
 #pragma unroll
-            for (int u = 0; u < TPW; ++u) load_out(cur, mt0 + u, ops[u]);
-            f32x4 o[TPW];
+                for (int ks = 0; ks < 4; ++ks)
+                    q[u][ks] = *reinterpret_cast<const bf16x8*>(rp + (((mt0 + u) * 4 + ks) * 64 + lane) * 16);
+        };
+        // one step: chunk j's output is made with qc (loaded a step earlier),
+        // and chunk j+1's Q' loads go out after A_j, in the same half-step as
+        // part A of the copies (the other half has part B and the stores)
+        auto step = [&](int j, const bf16x8 (&qc)[TPW][4], bf16x8 (&qn)[TPW][4]) {
+            const char* cur = slot_of(j);
+            lds_barrier();  // A_j: chunk j and the state operand are in LDS; the staging tile is free
+            load_q(j + 1, qn);  // (past the end it reloads the last chunk, unused)
+            // every LDS operand first (the state operand, M U~ and gate logits
+            // of each slice), so that the reads are in flight together
+            bf16x8 Sb[SB][4];
+            uint2 op[SB][TPW], zp[SB][TPW];
 #pragma unroll
-            for (int u = 0; u < TPW; ++u) o[u] = widen(ops[u].op);
+            for (int ls = 0; ls < SB; ++ls) {
+                const char* sbx = smem + C::B_SBX + ls * 4096;
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
+                for (int ks = 0; ks < 4; ++ks) Sb[ls][ks] = *reinterpret_cast<const bf16x8*>(sbx + (ks * 64 + lane) * 16);
 #pragma unroll
-                for (int u = 0; u < TPW; ++u) o[u] = mfma(Sb[ks], ops[u].qa[ks], o[u]);
-#pragma unroll
-            for (int u = 0; u < TPW; ++u) {
-                if (kGate) {
-                    const f32x4 zf = widen(ops[u].zp);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) o[u][i] *= sigmoid_fast(zf[i]);
+                for (int u = 0; u < TPW; ++u) {
+                    op[ls][u] = *reinterpret_cast<const uint2*>(cur + C::B_OI + ((ls * 4 + mt0 + u) * 64 + lane) * 8);
+                    if (kGate) zp[ls][u] = *reinterpret_cast<const uint2*>(cur + C::B_Z + stage_off(ls, mt0 + u));
                 }
-                *reinterpret_cast<uint2*>(stage + stage_off(mt0 + u)) =
-                    make_uint2(pack_bf16x2(o[u][0], o[u][1]), pack_bf16x2(o[u][2], o[u][3]));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int ls = 0; ls < SB; ++ls) {
+                f32x4 o[TPW];
+#pragma unroll
+                for (int u = 0; u < TPW; ++u) o[u] = widen(op[ls][u]);
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+                    for (int u = 0; u < TPW; ++u) o[u] = mfma(Sb[ls][ks], qc[u][ks], o[u]);
+#pragma unroll
+                for (int u = 0; u < TPW; ++u) {
+                    if (kGate) {
+                        const f32x4 zf = widen(zp[ls][u]);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) o[u][i] *= sigmoid_fast(zf[i]);
+                    }
+                    *reinterpret_cast<uint2*>(stage + stage_off(ls, mt0 + u)) =
+                        make_uint2(pack_bf16x2(o[u][0], o[u][1]), pack_bf16x2(o[u][2], o[u][3]));
+                }
             }
             lds_barrier();  // M_j: the output tile is staged
+        };
+        // two register sets in turn: a loop of two steps keeps their indices fixed
+        bf16x8 q0[TPW][4], q1[TPW][4];
+        if (nch > 0) load_q(0, q0);
+        for (int j = 0; j < nch; j += 2) {
+            step(j, q0, q1);
+            if (j + 1 < nch) step(j + 1, q1, q0);
         }
     }
 }
