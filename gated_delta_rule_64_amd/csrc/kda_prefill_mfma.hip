@@ -63,7 +63,7 @@ constexpr int REC_BYTES = 82432;
 constexpr int KS = 136;  // bf16 per row of K, Q, V
 constexpr int GS = 132;  // fp32 per row of G
 constexpr int MS = 68;   // fp32 per row of A, M and T (16 lanes reading 16 rows hit distinct banks)
-constexpr int SQS = 136; // bf16 per row of the Q' staging tile (the same bytes per row as A)
+constexpr int STS = 68;  // bf16 per row of the channel-major -W and Q' staging tiles [128][STS]
 constexpr float kDiagRange = 40.f * kLog2e;  // e^40, in the log2 units G is kept in
 // Largest decay over a chunk (log2 units, per channel) for which the chunk's
 // operands are scaled against one reference per channel, the midpoint of the
@@ -129,6 +129,7 @@ constexpr int kIntraThreads = 512;  // 8 waves: two per SIMD
 constexpr size_t kIntraLds = (3 * 64 * KS) * 2 + (64 * GS + 3 * 64 * MS + 64 + 16 * 128) * 4 + 32;
 static_assert(64 * KS * 2 + 64 * TBS * 2 <= 64 * GS * 4, "K^ and the M operand copy share the space of G");
 static_assert(64 * TBS <= 64 * KS, "the T Diag(beta) operand copy takes the space of K^");
+static_assert(128 * STS * 2 <= 64 * KS * 2 && 128 * STS * 2 <= 64 * MS * 4, "the staging tiles fit the V and A buffers");
 
 __device__ __forceinline__ void unpack8(uint4 v, float (&x)[8]) {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
@@ -238,6 +239,18 @@ __device__ __forceinline__ void tile_rs(int i, int& R, int& S) {
     S = i - R * (R + 1) / 2;
 }
 
+// ds_read_b64_tr_b16, the transposing LDS read: in each group of 16 lanes,
+// lane j names four consecutive 16-bit values a[j][0..3], and lane i
+// receives a[(i >> 2) + 4 m][i & 3], m = 0..3.  So when lane c of a group
+// names row r0 + (c >> 2) of a row-major bf16 matrix at column
+// col + 4 (c & 3), it receives column col + c of rows r0 .. r0 + 3: four
+// elements of a matrix-core operand column in one read instead of four.
+typedef short tr16_v4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
+    const tr16_v4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) tr16_v4*)(p));
+    return __builtin_bit_cast(uint2, v);
+}
+
 // kFused: the unit's inputs are the raw layer inputs, and staging them
 // applies the short conv, the L2 norm and the gates first (as kda_preprocess
 // does, in the same fp32 arithmetic), so the preprocessed tensors never go
@@ -268,8 +281,8 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
     uint16_t* sKr = reinterpret_cast<uint16_t*>(sG);  // [64][KS]
     uint16_t* sMb = sKr + 64 * KS;                     // [64][TBS]
     uint16_t* sTb = sKr;                               // [64][TBS]
-    uint16_t* sStW = sV;                                // staging of -W  [64][KS]
-    uint16_t* sStQ = reinterpret_cast<uint16_t*>(sA);   // staging of Q'  [64][SQS]
+    uint16_t* sStW = sV;                                // staging of -W, channel-major [128][STS]
+    uint16_t* sStQ = reinterpret_cast<uint16_t*>(sA);   // staging of Q', channel-major [128][STS]
 
     const int H = a.H;
     const int ftid = threadIdx.x;  // the thread index as the prefetch uses it
@@ -675,10 +688,12 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
             }
         };
 
-        // ---- A and M: 10 tiles (R >= S) of 4 contraction steps each.  Wave w
-        // computes tile w whole; the steps of tiles 8 and 9 go one per wave
-        // (tile 8 + w/4, step w%4), and their partial tiles are summed in a fixed
-        // order afterwards, so the result does not depend on timing.
+        // ---- A and M: 10 tiles (R >= S) of 4 contraction steps each.  On the
+        // exact path (below) wave w computes tile w whole, and the steps of
+        // tiles 8 and 9 go one per wave (tile 8 + w/4, step w%4): their
+        // diagonal tiles are vector work that one wave would take long over.
+        // The partial tiles are summed in a fixed order afterwards, so the
+        // result does not depend on timing.
             auto store_tile = [&](int R, int S, const f32x4& accA, const f32x4& accM) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -727,17 +742,37 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
             // A and M are plain products of the prepared operands: Kl and Ql
             // rows of block R against Kr rows of block S.  (Above the
             // diagonal the products may overflow; those entries are masked.)
-            am_tiles([&](int R, int S, int k0, int k1, f32x4& accA, f32x4& accM) {
-                const int rl = 16 * R + c, sr = 16 * S + c;
-                for (int ks = k0; ks < k1; ++ks) {
+            // Wave w makes tile w whole, and waves 0 and 1 tiles 8 and 9 as
+            // well; every operand read goes out before the first product.
+            const bool two = wave < 2;
+            int R[2], S[2];
+            tile_rs(wave, R[0], S[0]);
+            tile_rs(8 + (wave & 1), R[1], S[1]);
+            bf16x8 kl[2][4], ql[2][4], kr[2][4];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                if (t == 1 && !two) break;
+                const int rl = 16 * R[t] + c, sr = 16 * S[t] + c;
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
                     const int ch0 = 32 * ks + 8 * g;
-                    const bf16x8 kl = *reinterpret_cast<const bf16x8*>(sK + rl * KS + ch0);
-                    const bf16x8 ql = *reinterpret_cast<const bf16x8*>(sQ + rl * KS + ch0);
-                    const bf16x8 kr = *reinterpret_cast<const bf16x8*>(sKr + sr * KS + ch0);
-                    accA = mfma(kl, kr, accA);
-                    accM = mfma(ql, kr, accM);
+                    kl[t][ks] = *reinterpret_cast<const bf16x8*>(sK + rl * KS + ch0);
+                    ql[t][ks] = *reinterpret_cast<const bf16x8*>(sQ + rl * KS + ch0);
+                    kr[t][ks] = *reinterpret_cast<const bf16x8*>(sKr + sr * KS + ch0);
                 }
-            });
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                if (t == 1 && !two) break;
+                f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accM = accA;
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    accA = mfma(kl[t][ks], kr[t][ks], accA);
+                    accM = mfma(ql[t][ks], kr[t][ks], accM);
+                }
+                store_tile(R[t], S[t], accA, accM);
+            }
         } else {
             // exact tile path: factored decays referenced to each row block's
             // first token, pairwise decays on the 16-token sub-blocks too steep
@@ -981,13 +1016,13 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
             }
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
+                // column chn of rows s0 .. s0 + 7 of K and V, by transposing reads
                 const int s0 = 32 * ks + 8 * g;
-                bf16x8 Bk, Bv;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    Bk[e] = __builtin_bit_cast(__bf16, sK[(s0 + e) * KS + chn]);
-                    Bv[e] = __builtin_bit_cast(__bf16, sV[(s0 + e) * KS + chn]);
-                }
+                const int ta = (s0 + (c >> 2)) * KS + 16 * nt + 4 * (c & 3);
+                const uint2 k0 = lds_read_tr16(sK + ta), k1 = lds_read_tr16(sK + ta + 4 * KS);
+                const uint2 v0 = lds_read_tr16(sV + ta), v1 = lds_read_tr16(sV + ta + 4 * KS);
+                const bf16x8 Bk = __builtin_bit_cast(bf16x8, make_uint4(k0.x, k0.y, k1.x, k1.y));
+                const bf16x8 Bv = __builtin_bit_cast(bf16x8, make_uint4(v0.x, v0.y, v1.x, v1.y));
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt) {
                     if (32 * ks > 16 * mt + 15) continue;  // T is lower triangular
@@ -1035,10 +1070,13 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
                 f32x4 qp, oi = {0.f, 0.f, 0.f, 0.f};
+                {
+                    // column chn of rows 16 mt + 4 g .. + 3 of Ql, by a transposing read
+                    const uint2 qv = lds_read_tr16(sQ + (16 * mt + 4 * g + (c >> 2)) * KS + 16 * nt + 4 * (c & 3));
+                    const float q4[4] = {__uint_as_float(qv.x << 16), __uint_as_float(qv.x & 0xffff0000u),
+                                         __uint_as_float(qv.y << 16), __uint_as_float(qv.y & 0xffff0000u)};
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = 16 * mt + 4 * g + i;
-                    qp[i] = sl * bfv(sQ + r * KS + chn);
+                    for (int i = 0; i < 4; ++i) qp[i] = sl * q4[i];
                 }
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
@@ -1052,12 +1090,11 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
                 p.x = pack_bf16x2(oi[0], oi[1]);
                 p.y = pack_bf16x2(oi[2], oi[3]);
                 rec_store8(rec + R_OI + ((nt * 4 + mt) * 64 + lane) * 8, p);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = 16 * mt + 4 * g + i;
-                    sStW[r * KS + chn] = f32_to_bf16(-accW[mt][i]);
-                    sStQ[r * SQS + chn] = f32_to_bf16(qp[i]);
-                }
+                // tokens 16 mt + 4 g .. + 3 of channel chn: one 8-byte write each
+                *reinterpret_cast<uint2*>(sStW + chn * STS + 16 * mt + 4 * g) =
+                    make_uint2(pack_bf16x2(-accW[mt][0], -accW[mt][1]), pack_bf16x2(-accW[mt][2], -accW[mt][3]));
+                *reinterpret_cast<uint2*>(sStQ + chn * STS + 16 * mt + 4 * g) =
+                    make_uint2(pack_bf16x2(qp[0], qp[1]), pack_bf16x2(qp[2], qp[3]));
             }
         }
         lds_barrier();
@@ -1068,12 +1105,11 @@ __global__ __launch_bounds__(kIntraThreads) void mfma_intra_kernel(MfmaK<GT> a) 
 #pragma unroll
             for (int k2 = 0; k2 < 2; ++k2) {
                 const int ks = 2 * (wave & 1) + k2;
-                const int r = 16 * mt + c;
-                const int c0 = 32 * ks + 4 * g;
-                const uint2 wlo = *reinterpret_cast<const uint2*>(sStW + r * KS + c0);
-                const uint2 whi = *reinterpret_cast<const uint2*>(sStW + r * KS + c0 + 16);
-                const uint2 qlo = *reinterpret_cast<const uint2*>(sStQ + r * SQS + c0);
-                const uint2 qhi = *reinterpret_cast<const uint2*>(sStQ + r * SQS + c0 + 16);
+                // token 16 mt + c, channels 32 ks + 4 g .. + 3 and 32 ks + 16 + 4 g .. + 3,
+                // by transposing reads of the channel-major tiles
+                const int ta = (32 * ks + 4 * g + (c >> 2)) * STS + 16 * mt + 4 * (c & 3);
+                const uint2 wlo = lds_read_tr16(sStW + ta), whi = lds_read_tr16(sStW + ta + 16 * STS);
+                const uint2 qlo = lds_read_tr16(sStQ + ta), qhi = lds_read_tr16(sStQ + ta + 16 * STS);
                 const int blk = (mt * 4 + ks) * 64 + lane;
                 rec_store16(rec + R_NEGW + blk * 16, make_uint4(wlo.x, wlo.y, whi.x, whi.y));
                 rec_store16(rec + R_QP + blk * 16, make_uint4(qlo.x, qlo.y, qhi.x, qhi.y));
