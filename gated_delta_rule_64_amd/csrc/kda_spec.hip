@@ -316,23 +316,31 @@ __global__ __launch_bounds__(256, 4) void spec_kernel(SpecK<XT> a) {
     // (no memory operation moves across: the counted wait below relies on
     // the state's loads being the last ones issued)
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    // the state, into registers: read once, right behind the staging copies,
-    // so that it is in flight through the preprocess, the norms and the small
-    // operands
+    // the state, into registers, read once in two halves: the first right
+    // behind the staging copies, in flight through the preprocess and the
+    // norms, the second after the norms, in flight through the small
+    // operands.  (All of it at once leaves the preprocess so few registers
+    // that the compiler spills a state register, and waits for its load to
+    // do so, right after issuing it.)
+    constexpr int SA = SP > 1 ? SP / 2 : SP;  // steps loaded first
     float Sr[SP][V];
+    auto load_state = [&](int s0, int s1) {
 #pragma unroll
-    for (int s = 0; s < SP; ++s) {
-        if constexpr (V == 2) {
-            const i32x2 x = __builtin_amdgcn_raw_buffer_load_b64(srsrc, Soff, 4 * DV * s, 0);
-            Sr[s][0] = __int_as_float(x.x);
-            Sr[s][1] = __int_as_float(x.y);
-        } else {
-            Sr[s][0] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(srsrc, Soff, 4 * DV * s, 0));
+        for (int s = 0; s < SP; ++s) {
+            if (s < s0 || s >= s1) continue;
+            if constexpr (V == 2) {
+                const i32x2 x = __builtin_amdgcn_raw_buffer_load_b64(srsrc, Soff, 4 * DV * s, 0);
+                Sr[s][0] = __int_as_float(x.x);
+                Sr[s][1] = __int_as_float(x.y);
+            } else {
+                Sr[s][0] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(srsrc, Soff, 4 * DV * s, 0));
+            }
         }
-    }
+    };
+    load_state(0, SA);
     // the staging copies (and the write logits) have landed once no more than
     // the state's loads are in flight
-    wait_vmem_but<SP>();
+    wait_vmem_but<SA>();
     if (wave == 2 && lane < J) {
         s_beta[lane] = sigmoid_fast(bj);
         if (lane >= na) st(dr + static_cast<int64_t>(lane - na) * H * W + 3 * DK + DV, bj);
@@ -389,6 +397,7 @@ __global__ __launch_bounds__(256, 4) void spec_kernel(SpecK<XT> a) {
         }
     }
     lds_barrier();
+    load_state(SA, SP);
 
     // 3. the call's small operands: X (zero rows pad it to whole 16-row
     // passes), the commit factors, and A and M, one 16-lane row per entry
