@@ -148,52 +148,122 @@ __device__ __forceinline__ void mm64(int K, FA A, FB B, FO out) {
 // out, and is clamped to 0 so that nothing overflows
 __device__ __forceinline__ float decay(float x) { return __builtin_amdgcn_exp2f(fminf(x, 0.f) * kLog2e); }
 
-// A (strictly lower) and M (lower with diagonal) of a chunk, by AT x AT
-// tiles of (r, s) per thread (one tile, or two for 512 threads); K, Q, G
-// rows padded to DK + 1 floats in LDS.
+// Row stride (floats) of the per-chunk key, query and decay rows in LDS:
+// rows stay 16-byte aligned for four-channel reads, and the 4-float pad
+// puts 16 rows at one channel on distinct banks.
+template <int DK>
+constexpr int kKP = DK + 4;
+
+// A diagonal 16 x 16 block whose decay over its 16 rows exceeds this (in any
+// channel, natural-log units) is "steep": its factored form below would need
+// e^{span}, which leaves the fp32 range near 88.
+constexpr float kSpanMax = 80.f;
+
+// (R, S) of tile i in the lower block triangle of a 64 x 64 matrix
+// (16 x 16 blocks, R >= S), row-major order
+__device__ __forceinline__ void lower_tile(int i, int& R, int& S) {
+    R = i >= 6 ? 3 : i >= 3 ? 2 : i >= 1 ? 1 : 0;
+    S = i - R * (R + 1) / 2;
+}
+
+// A (strictly lower) and M (lower with diagonal) of a chunk,
+//   A_rs = sum_c k_rc k_sc e^{G_rc - G_sc},  M_rs = sum_c q_rc k_sc e^{G_rc - G_sc},
+// by 16 x 16 blocks (R, S), R >= S, one wave each (waves 0 .. 9).  The
+// pairwise decay factors through the first row of block R:
+//   e^{G_r - G_s} = e^{G_r - G_16R} e^{G_16R - G_s},
+// so a block is a product over the channels of (K_R or Q_R) * e^{G_R - G_16R}
+// and (K_S * e^{G_16R - G_S})^T, on the fp32 matrix cores.  Below the
+// diagonal (R > S) both factors are at most 1, since G does not increase
+// along the chunk.  On a diagonal block the right factor grows with the decay
+// inside the block; where that could leave the fp32 range (a steep block)
+// the block is summed pair by pair instead.  K, Q, G rows have stride kKP.
 template <int DK, int NT>
-__device__ __forceinline__ void am_tiles(const float* sK, const float* sQ, const float* sG, float* sA, float* sM) {
-    constexpr int KP = DK + 1;
-    constexpr int AT = NT == 256 ? 4 : 2, GD = 64 / AT;
-    static_assert(GD * GD == NT || GD * GD == 2 * NT, "one or two tiles per thread");
-    for (int tile = threadIdx.x; tile < GD * GD; tile += NT) {
-        const int r0 = AT * (tile / GD), s0 = AT * (tile % GD);
-        float av[AT][AT], mv[AT][AT];
+__device__ __forceinline__ void am_mfma(const float* sK, const float* sQ, const float* sG, float* sA, float* sM) {
+    static_assert(NT >= 640 && DK % 16 == 0, "ten waves; whole runs of 16 channels");
+    constexpr int KP = kKP<DK>, CW = DK / 4;  // lane (g, c) takes channels CW g .. CW g + CW - 1
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
+    if (wave >= 10) return;
+    int R, S;
+    lower_tile(wave, R, S);
+    const bool diag = R == S;
+    bool steep = false;
+    if (diag) {
+        float span = 0.f;
+        for (int ch = lane; ch < DK; ch += 64) span = fmaxf(span, sG[(16 * R) * KP + ch] - sG[(16 * R + 15) * KP + ch]);
+        steep = __ballot(span >= kSpanMax) != 0;
+    }
+    if (!steep) {
+        // v_mfma_f32_16x16x4_f32: lane (g, c) gives A[c][g] and B[g][c] and
+        // holds D[4g + i][c]; the left rows are 16R + c, the right ones 16S + c
+        const float* kr = sK + (16 * R + c) * KP + CW * g;
+        const float* qr = sQ + (16 * R + c) * KP + CW * g;
+        const float* gr = sG + (16 * R + c) * KP + CW * g;
+        const float* gf = sG + (16 * R) * KP + CW * g;
+        const float* ks = sK + (16 * S + c) * KP + CW * g;
+        const float* gs = sG + (16 * S + c) * KP + CW * g;
+        // exponent bounds: the left factor at most 1; the right one at most
+        // 1 below the diagonal and e^{kSpanMax} on it (the bounds only bind
+        // for decays that grow, which the inputs do not hold)
+        const float rmax = diag ? kSpanMax * kLog2e : 0.f;
+        f32x4 aa = {0.f, 0.f, 0.f, 0.f}, am = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < AT; ++i)
+        for (int u = 0; u < CW / 4; ++u) {
+            const float4 k4 = reinterpret_cast<const float4*>(kr)[u], q4 = reinterpret_cast<const float4*>(qr)[u];
+            const float4 g4 = reinterpret_cast<const float4*>(gr)[u], f4 = reinterpret_cast<const float4*>(gf)[u];
+            const float4 s4 = reinterpret_cast<const float4*>(ks)[u], h4 = reinterpret_cast<const float4*>(gs)[u];
+            const float kv[4] = {k4.x, k4.y, k4.z, k4.w}, qv[4] = {q4.x, q4.y, q4.z, q4.w};
+            const float gv[4] = {g4.x, g4.y, g4.z, g4.w}, fv[4] = {f4.x, f4.y, f4.z, f4.w};
+            const float sv[4] = {s4.x, s4.y, s4.z, s4.w}, hv[4] = {h4.x, h4.y, h4.z, h4.w};
 #pragma unroll
-            for (int jj = 0; jj < AT; ++jj) av[i][jj] = mv[i][jj] = 0.f;
-        if (s0 <= r0 + AT - 1) {  // the tile reaches the lower triangle
-            for (int c = 0; c < DK; ++c) {
-                float kr[AT], qr[AT], gr[AT], ks[AT], gs[AT];
-#pragma unroll
-                for (int i = 0; i < AT; ++i) {
-                    kr[i] = sK[(r0 + i) * KP + c];
-                    qr[i] = sQ[(r0 + i) * KP + c];
-                    gr[i] = sG[(r0 + i) * KP + c];
-                    ks[i] = sK[(s0 + i) * KP + c];
-                    gs[i] = sG[(s0 + i) * KP + c];
-                }
-#pragma unroll
-                for (int i = 0; i < AT; ++i)
-#pragma unroll
-                    for (int jj = 0; jj < AT; ++jj) {
-                        // e^{G_r - G_s}; above the diagonal the exponent is
-                        // clamped (those entries are dropped below)
-                        const float ke = ks[jj] * decay(gr[i] - gs[jj]);
-                        av[i][jj] += kr[i] * ke;
-                        mv[i][jj] += qr[i] * ke;
-                    }
+            for (int j = 0; j < 4; ++j) {
+                const float fl = __builtin_amdgcn_exp2f(fminf((gv[j] - fv[j]) * kLog2e, 0.f));
+                const float fr = __builtin_amdgcn_exp2f(fminf((fv[j] - hv[j]) * kLog2e, rmax));
+                const float b = sv[j] * fr;
+                aa = __builtin_amdgcn_mfma_f32_16x16x4f32(kv[j] * fl, b, aa, 0, 0, 0);
+                am = __builtin_amdgcn_mfma_f32_16x16x4f32(qv[j] * fl, b, am, 0, 0, 0);
             }
         }
+        const int s_ = 16 * S + c;
 #pragma unroll
-        for (int i = 0; i < AT; ++i)
-#pragma unroll
-            for (int jj = 0; jj < AT; ++jj) {
-                const int r = r0 + i, s_ = s0 + jj;
-                sA[r * MS + s_] = s_ < r ? av[i][jj] : 0.f;
-                sM[r * MS + s_] = s_ <= r ? mv[i][jj] : 0.f;
+        for (int i = 0; i < 4; ++i) {
+            const int r = 16 * R + 4 * g + i;
+            sA[r * MS + s_] = s_ < r ? aa[i] : 0.f;
+            sM[r * MS + s_] = s_ <= r ? am[i] : 0.f;
+        }
+    } else {
+        // the 136 pairs s <= r of the block, pair by pair over the channels;
+        // the lane of pair (r, s), s < r, also clears (s, r)
+        for (int p = lane; p < 136; p += 64) {
+            int rl = static_cast<int>((sqrtf(8.f * p + 1.f) - 1.f) * 0.5f);
+            if ((rl + 1) * (rl + 2) / 2 <= p) ++rl;
+            if (rl * (rl + 1) / 2 > p) --rl;
+            const int sl = p - rl * (rl + 1) / 2, r = 16 * R + rl, s_ = 16 * R + sl;
+            float av = 0.f, mv = 0.f;
+            for (int ch = 0; ch < DK; ch += 4) {
+                const float4 k4 = *reinterpret_cast<const float4*>(sK + r * KP + ch);
+                const float4 q4 = *reinterpret_cast<const float4*>(sQ + r * KP + ch);
+                const float4 g4 = *reinterpret_cast<const float4*>(sG + r * KP + ch);
+                const float4 s4 = *reinterpret_cast<const float4*>(sK + s_ * KP + ch);
+                const float4 h4 = *reinterpret_cast<const float4*>(sG + s_ * KP + ch);
+                const float e0 = s4.x * decay(g4.x - h4.x), e1 = s4.y * decay(g4.y - h4.y);
+                const float e2 = s4.z * decay(g4.z - h4.z), e3 = s4.w * decay(g4.w - h4.w);
+                av += k4.x * e0 + k4.y * e1 + k4.z * e2 + k4.w * e3;
+                mv += q4.x * e0 + q4.y * e1 + q4.z * e2 + q4.w * e3;
             }
+            sA[r * MS + s_] = sl < rl ? av : 0.f;
+            sM[r * MS + s_] = mv;
+            if (sl < rl) {
+                sA[s_ * MS + r] = 0.f;
+                sM[s_ * MS + r] = 0.f;
+            }
+        }
+    }
+    if (!diag) {  // the block (S, R) above the diagonal
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            sA[(16 * S + 4 * g + i) * MS + 16 * R + c] = 0.f;
+            sM[(16 * S + 4 * g + i) * MS + 16 * R + c] = 0.f;
+        }
     }
 }
 
@@ -256,13 +326,13 @@ __device__ __forceinline__ void t_solve(const float* sA, const float* sB, float*
 // them.
 template <int DK>
 constexpr size_t rec_lds_bytes() {
-    return (3 * 64 * (DK + 1) + 3 * 64 * MS + 64 + 768) * sizeof(float);  // K, Q, G; A, M, T; beta; T's scratch
+    return (3 * 64 * kKP<DK> + 3 * 64 * MS + 64 + 768) * sizeof(float);  // K, Q, G; A, M, T; beta; T's scratch
 }
 
 template <int DK, int DV, typename XT, typename GT>
 __global__ __launch_bounds__(kRecThreads) void chunk_records_kernel(BwdK<XT, GT> a) {
     extern __shared__ __align__(16) float smem[];
-    constexpr int KP = DK + 1;
+    constexpr int KP = kKP<DK>;
     float* sK = smem;
     float* sQ = sK + 64 * KP;
     float* sG = sQ + 64 * KP;
@@ -302,7 +372,7 @@ __global__ __launch_bounds__(kRecThreads) void chunk_records_kernel(BwdK<XT, GT>
         rec[R.Kh + i] = expf(sG[63 * KP + c] - sG[r * KP + c]) * sK[r * KP + c];
     }
     if (tid < DK) rec[R.gam + tid] = expf(sG[63 * KP + tid]);
-    am_tiles<DK, kRecThreads>(sK, sQ, sG, sA, sM);
+    am_mfma<DK, kRecThreads>(sK, sQ, sG, sA, sM);
     __syncthreads();
     t_solve<kRecThreads>(sA, sB, sT, sTmp);
     // W = T (B e^G K),  U~ = T (B V)
@@ -489,17 +559,17 @@ constexpr size_t scratch_floats(int dk, int dv) { return 3 * 64 * static_cast<si
 
 template <int DK>
 constexpr size_t intra_lds_bytes() {
-    // K, G [64][DK + 1]; A, M, T, dT, P [64][MS]; beta, dbeta [64]; dG_last [DK]
-    return (2 * 64 * (DK + 1) + 5 * 64 * MS + 2 * 64 + DK) * sizeof(float);
+    // K, G [64][kKP]; A, M, T, dT, P [64][MS]; beta, dbeta [64]; dG_last [DK]
+    return (2 * 64 * kKP<DK> + 5 * 64 * MS + 2 * 64 + DK) * sizeof(float);
 }
 
 // ---- pass 3: per (chunk, head), every input gradient ----
 template <int DK, int DV, typename XT, typename GT>
 __global__ __launch_bounds__(kGradThreads) void bwd_intra_kernel(BwdK<XT, GT> a) {
     extern __shared__ __align__(16) float smem[];
-    // K and G rows padded to DK + 1 floats: the tiles below read 4 rows at
-    // one channel, which would otherwise land in one LDS bank
-    constexpr int KP = DK + 1;
+    // K and G rows padded to kKP floats: the tiles below read 4 rows at one
+    // channel, which would otherwise land in one LDS bank
+    constexpr int KP = kKP<DK>;
     float* sK = smem;              // [64][KP] keys
     float* sG = sK + 64 * KP;      // [64][KP] decay cumsums; at the end dG
     float* sA = sG + 64 * KP;      // [64][MS] A
@@ -559,8 +629,9 @@ __global__ __launch_bounds__(kGradThreads) void bwd_intra_kernel(BwdK<XT, GT> a)
         }
     }
     __syncthreads();
-    // A (strictly lower) and M (lower with diagonal) by 4 x 4 tiles of (r, s);
-    // the queries sit, padded like K, in the space of T, dT, P until T is made
+    // A (strictly lower) and M (lower with diagonal), by blocks on the matrix
+    // cores; the queries sit, padded like K, in the space of T, dT, P until T
+    // is made
     {
         float* sQ = sT;
         for (int i = tid; i < 64 * DK; i += kGradThreads) {
@@ -568,7 +639,7 @@ __global__ __launch_bounds__(kGradThreads) void bwd_intra_kernel(BwdK<XT, GT> a)
             sQ[r * KP + c] = r < L ? ld(a.q + tok(r) * DK + c) : 0.f;
         }
         __syncthreads();
-        am_tiles<DK, kGradThreads>(sK, sQ, sG, sA, sM);
+        am_mfma<DK, kGradThreads>(sK, sQ, sG, sA, sM);
         __syncthreads();  // the queries are dead; T goes where they were
     }
     t_solve<kGradThreads>(sA, sB, sT, sP);  // (P's space is free until phase 5)
