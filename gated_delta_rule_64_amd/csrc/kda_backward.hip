@@ -56,17 +56,6 @@ struct BwdK {
 constexpr int kRecThreads = 1024;
 constexpr int kGradThreads = 1024;
 
-// Per-thread tile of a 64-row, N-column result shared by NT threads:
-// TR rows x TC columns, TR * TC = 64 N / NT.
-template <int N, int NT>
-struct Tile64 {
-    static constexpr int OUT = 64 * N / NT;
-    static constexpr int TR = OUT >= 16 ? 4 : (OUT >= 8 ? 2 : 1);
-    static constexpr int TC = OUT / TR;
-    static constexpr int NCT = N / TC;  // column tiles
-    static_assert(TR * TC == OUT && OUT >= 1 && NCT * (64 / TR) == NT, "tile shape");
-};
-
 // Row stride (floats) of the 64 x 64 matrices in LDS (A, M, T, dT, P): the
 // products below read 16 rows at one column and 16 columns at one row, and
 // at a 64-float stride the first would land in one bank.
@@ -754,73 +743,90 @@ __global__ __launch_bounds__(kGradThreads) void bwd_intra_kernel(BwdK<XT, GT> a)
         qs(r, c) = r < L ? ld(a.q + tok(r) * DK + c) : 0.f;
     }
     __syncthreads();
-    // ---- 6. through A (dA = B dY) and M (dM), with E_rsc = e^{G_rc - G_sc}.
-    // Thread tiles of Tile64<DK>: rows R0 .. R0+TR-1, channels C0 .. C0+TC-1.
-    // As row r of A and M:  dk_rc += sum_s dA_rs k_sc E,  dq_rc += sum_s dM_rs k_sc E,
-    //   and dG_rc gains k_rc (the first sum) + q_rc (the second);
-    // as column s of them:  dk_sc += sum_r w_rsc E with w = dA_rs k_rc + dM_rs q_rc,
-    //   and dG_sc loses k_sc times that sum.
+    // ---- 6. through A (dA = B dY) and M (dM), with E_rsc = e^{G_rc - G_sc}:
+    //   as row r of A and M:  dk_rc += sum_s dA_rs k_sc E,  dq_rc += sum_s dM_rs k_sc E,
+    //     and dG_rc gains k_rc (the first sum) + q_rc (the second);
+    //   as column s of them:  dk_sc += sum_r (dA_rs k_rc + dM_rs q_rc) E,
+    //     and dG_sc loses k_sc times that sum.
+    // By 16-row blocks on the fp32 matrix cores, the decay factored as in
+    // am_mfma: for output rows in block B, the row sums over blocks S <= B
+    // take e^{G_r - G_16B} e^{G_16B - G_s}, and the column sums over blocks
+    // R >= B take e^{G_r - G_16R} e^{G_16R - G_s}.  A wave takes output tiles
+    // (B, channels 16 j .. 16 j + 15); lane (g, c) owns rows 16 B + 4 g + i
+    // of channel 16 j + c.  Where the diagonal block is steep (over the
+    // tile's channels) its share is summed pair by pair instead.
     {
-        constexpr int TC = Tile64<DK, kGradThreads>::TC, NCT = Tile64<DK, kGradThreads>::NCT, TR = Tile64<DK, kGradThreads>::TR;
-        const int C0 = TC * (tid % NCT), R0 = TR * (tid / NCT);
-        float dkr[TR][TC], dqr[TR][TC], dks[TR][TC], gown[TR][TC];
-#pragma unroll
-        for (int i = 0; i < TR; ++i)
-#pragma unroll
-            for (int jj = 0; jj < TC; ++jj) {
-                dkr[i][jj] = dqr[i][jj] = dks[i][jj] = 0.f;
-                gown[i][jj] = sG[(R0 + i) * KP + C0 + jj];
+        constexpr int NJ = DK / 16;
+        const int wave = tid >> 6, lane = tid & 63, g = lane >> 4, c = lane & 15;
+        const float rmax = kSpanMax * kLog2e;  // (binds on diagonal blocks only)
+#pragma unroll 1
+        for (int t = wave; t < 4 * NJ; t += kGradThreads / 64) {
+            const int B = t & 3, ch = 16 * (t >> 2) + c;
+            const float* qcol = (ch < 64 ? sA : sT) + (ch & 63);  // the queries: qcol[r * MS]
+            const float gB = sG[(16 * B) * KP + ch];
+            const bool steep = __ballot(gB - sG[(16 * B + 15) * KP + ch] >= kSpanMax) != 0;
+            // row sums: dA_B,S (K_S e^{G_16B - G_S}) over S, and the same with dM
+            f32x4 xk = {0.f, 0.f, 0.f, 0.f}, xq = {0.f, 0.f, 0.f, 0.f};
+            const int s_end = steep ? 16 * B : 16 * B + 16;
+#pragma unroll 2
+            for (int s0 = 0; s0 < s_end; s0 += 4) {
+                const int s_ = s0 + g, ra = 16 * B + c;
+                const float kr = sK[s_ * KP + ch] * __builtin_amdgcn_exp2f(fminf((gB - sG[s_ * KP + ch]) * kLog2e, rmax));
+                xk = __builtin_amdgcn_mfma_f32_16x16x4f32(sB[ra] * sdT[ra * MS + s_], kr, xk, 0, 0, 0);
+                xq = __builtin_amdgcn_mfma_f32_16x16x4f32(sM[ra * MS + s_], kr, xq, 0, 0, 0);
             }
-        for (int s_ = 0; s_ < R0 + TR; ++s_) {  // row role: s <= r
-            float da[TR], dm[TR], ks[TC], gs[TC];
+            float dkr[4], dqr[4], dks[4], gown[4];
 #pragma unroll
-            for (int i = 0; i < TR; ++i) {
-                da[i] = sB[R0 + i] * sdT[(R0 + i) * MS + s_];  // (zero unless s < r)
-                dm[i] = sM[(R0 + i) * MS + s_];                // (zero unless s <= r)
+            for (int i = 0; i < 4; ++i) {
+                gown[i] = sG[(16 * B + 4 * g + i) * KP + ch];
+                const float fl = __builtin_amdgcn_exp2f(fminf((gown[i] - gB) * kLog2e, 0.f));
+                dkr[i] = fl * xk[i];
+                dqr[i] = fl * xq[i];
+                dks[i] = 0.f;
             }
+            // column sums: dA_R,B^T (K_R e^{G_R - G_16R}) + dM_R,B^T (Q_R e^{G_R - G_16R}),
+            // then times e^{G_16R - G_s}, for each R
+#pragma unroll 1
+            for (int R = steep ? B + 1 : B; R < 4; ++R) {
+                const float gR = sG[(16 * R) * KP + ch];
+                f32x4 y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int jj = 0; jj < TC; ++jj) {
-                ks[jj] = sK[s_ * KP + C0 + jj];
-                gs[jj] = sG[s_ * KP + C0 + jj];
-            }
-#pragma unroll
-            for (int i = 0; i < TR; ++i)
-#pragma unroll
-                for (int jj = 0; jj < TC; ++jj) {
-                    const float ke = ks[jj] * decay(gown[i][jj] - gs[jj]);
-                    dkr[i][jj] += da[i] * ke;
-                    dqr[i][jj] += dm[i] * ke;
+                for (int r0 = 0; r0 < 16; r0 += 4) {
+                    const int r = 16 * R + r0 + g, sc = 16 * B + c;
+                    const float f = __builtin_amdgcn_exp2f(fminf((sG[r * KP + ch] - gR) * kLog2e, 0.f));
+                    y = __builtin_amdgcn_mfma_f32_16x16x4f32(sB[r] * sdT[r * MS + sc], sK[r * KP + ch] * f, y, 0, 0, 0);
+                    y = __builtin_amdgcn_mfma_f32_16x16x4f32(sM[r * MS + sc], qcol[r * MS] * f, y, 0, 0, 0);
                 }
+                const float smax = R == B ? rmax : 0.f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dks[i] += __builtin_amdgcn_exp2f(fminf((gR - gown[i]) * kLog2e, smax)) * y[i];
+            }
+            if (steep) {  // the diagonal block pair by pair
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 16 * B + 4 * g + i;
+#pragma unroll 1
+                    for (int u = 16 * B; u < 16 * B + 16; ++u) {
+                        const float gu = sG[u * KP + ch], ku = sK[u * KP + ch];
+                        if (u <= r) {  // row r, column u (dA is zero on the diagonal)
+                            const float e = ku * decay(gown[i] - gu);
+                            dkr[i] += sB[r] * sdT[r * MS + u] * e;
+                            dqr[i] += sM[r * MS + u] * e;
+                        }
+                        if (u >= r)  // row u, column r
+                            dks[i] += (sB[u] * sdT[u * MS + r] * ku + sM[u * MS + r] * qcol[u * MS]) * decay(gu - gown[i]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * B + 4 * g + i, e = r * DK + ch;
+                const float kv = sK[r * KP + ch], qv = qcol[r * MS];
+                gk[e] += dkr[i] + dks[i];
+                gq[e] += dqr[i];
+                gG[e] += kv * dkr[i] + qv * dqr[i] - kv * dks[i];
+            }
         }
-        for (int r2 = R0; r2 < 64; ++r2) {  // column role: r >= s
-            float da[TR], dm[TR], kr[TC], qr[TC], gr[TC];
-#pragma unroll
-            for (int i = 0; i < TR; ++i) {
-                da[i] = sB[r2] * sdT[r2 * MS + R0 + i];
-                dm[i] = sM[r2 * MS + R0 + i];
-            }
-#pragma unroll
-            for (int jj = 0; jj < TC; ++jj) {
-                kr[jj] = sK[r2 * KP + C0 + jj];
-                qr[jj] = qs(r2, C0 + jj);
-                gr[jj] = sG[r2 * KP + C0 + jj];
-            }
-#pragma unroll
-            for (int i = 0; i < TR; ++i)
-#pragma unroll
-                for (int jj = 0; jj < TC; ++jj)
-                    dks[i][jj] += (da[i] * kr[jj] + dm[i] * qr[jj]) * decay(gr[jj] - gown[i][jj]);
-        }
-#pragma unroll
-        for (int i = 0; i < TR; ++i)
-#pragma unroll
-            for (int jj = 0; jj < TC; ++jj) {
-                const int r = R0 + i, c = C0 + jj, e = r * DK + c;
-                const float kv = sK[r * KP + c], qv = qs(r, c);
-                gk[e] += dkr[i][jj] + dks[i][jj];
-                gq[e] += dqr[i][jj];
-                gG[e] += kv * dkr[i][jj] + qv * dqr[i][jj] - kv * dks[i][jj];
-            }
     }
     __syncthreads();  // every read of sK, sG, sdT, sM is done
     // ---- 7. dla = reverse cumsum of dG (G_last is G_63); outputs
