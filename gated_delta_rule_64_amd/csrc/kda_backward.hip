@@ -44,7 +44,7 @@ struct BwdK {
     const float* S0;
     const float* dSf;
     float* dSe;  // [slot][H][dk][dv]: dS at the end of each chunk
-    float* scratch;  // [slot][H]: U, dO, dU [64][dv]; dW, the dq, dk, dG sums and K_e [64][dk]
+    float* scratch;  // [slot][H]: U, dO, dU [64][dv]; dW [64][dk]
     float *dq, *dk, *dv, *dla, *dbeta, *dz, *dS0;
 };
 
@@ -63,27 +63,46 @@ constexpr int MS = 68;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// How a 64-row, N-column result (N = 16 .. 128) is dealt to the NT / 64
+// waves of a workgroup as 16 x 16 tiles: a wave takes RPW row tiles of CPW
+// column tiles, starting at row r0 and column c0; waves past the tiles take
+// none.  Every product of width N below, and the chain rule through A and M,
+// use this deal, so a (row, channel) result always lives in the same lane.
+template <int N, int NT>
+struct Deal64 {
+    static constexpr int W = NT / 64, CT = N / 16;
+    static constexpr int CPW = CT >= W ? CT / W : 1;    // column tiles per wave
+    static constexpr int WPC = CT >= W ? 1 : W / CT;    // waves per column tile
+    static constexpr int RPW = WPC >= 4 ? 1 : 4 / WPC;  // row tiles per wave
+    static constexpr int PER_LANE = RPW * CPW * 4;     // results per lane
+    static_assert(CT * 16 == N && (CT >= W ? CT % W == 0 : W % CT == 0), "tile deal");
+    int r0, c0;
+    bool active;
+    __device__ explicit Deal64(int wave) {
+        const int part = CT >= W ? 0 : wave % WPC;
+        active = part * RPW < 4;
+        r0 = 16 * part * RPW;
+        c0 = 16 * (CT >= W ? wave * CPW : wave / WPC);
+    }
+};
+
 // C = A B for 64 rows and N columns (N = 16 .. 128), K terms (a multiple of
 // 16), by the NT threads of the workgroup, on the fp32 matrix cores
 // (v_mfma_f32_16x16x4_f32: lane (g, c) = (lane / 16, lane % 16) gives
-// A[c][g] and B[g][c] and holds D[4g + i][c]; fp32 products, fp32 sums).
-// The output's 16 x 16 tiles are dealt to the waves: a wave takes RPW row
-// tiles of CPW column tiles, so each operand it loads serves several
+// A[c][g] and B[g][c] and holds D[4g + i][c]; fp32 products, fp32 sums),
+// tiles dealt as Deal64 says, so each operand a wave loads serves several
 // products.  Lane (g, c) takes the terms k0 + 4g .. k0 + 4g + 3 of every run
 // of 16, four consecutive elements of a row-major A row.  A(r, k), B(k, c)
-// read the operands; out(r, c, acc) takes each result once, and for equal N
-// the same thread always gets the same (r, c).
+// read the operands; out(idx, r, c, acc) takes each result once, idx being
+// its index among the lane's PER_LANE results (a constant once unrolled).
 template <int N, int NT, typename FA, typename FB, typename FO>
-__device__ __forceinline__ void mm64(int K, FA A, FB B, FO out) {
-    constexpr int W = NT / 64, CT = N / 16;
-    constexpr int CPW = CT >= W ? CT / W : 1;    // column tiles per wave
-    constexpr int WPC = CT >= W ? 1 : W / CT;    // waves per column tile
-    constexpr int RPW = WPC >= 4 ? 1 : 4 / WPC;  // row tiles per wave
-    static_assert(CT * 16 == N && (CT >= W ? CT % W == 0 : W % CT == 0), "tile deal");
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
-    const int part = CT >= W ? 0 : wave % WPC;
-    if (part * RPW >= 4) return;  // (more waves than tiles; wave-uniform)
-    const int r0 = 16 * part * RPW, c0 = 16 * (CT >= W ? wave * CPW : wave / WPC);
+__device__ __forceinline__ void mm64i(int K, FA A, FB B, FO out) {
+    using D = Deal64<N, NT>;
+    constexpr int RPW = D::RPW, CPW = D::CPW;
+    const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
+    const D d(threadIdx.x >> 6);
+    if (!d.active) return;  // (more waves than tiles; wave-uniform)
+    const int r0 = d.r0, c0 = d.c0;
     f32x4 acc[RPW][CPW];
 #pragma unroll
     for (int i = 0; i < RPW; ++i)
@@ -129,7 +148,14 @@ __device__ __forceinline__ void mm64(int K, FA A, FB B, FO out) {
 #pragma unroll
         for (int jj = 0; jj < CPW; ++jj)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) out(r0 + 16 * i + 4 * g + e, c0 + 16 * jj + c, acc[i][jj][e]);
+            for (int e = 0; e < 4; ++e)
+                out((i * CPW + jj) * 4 + e, r0 + 16 * i + 4 * g + e, c0 + 16 * jj + c, acc[i][jj][e]);
+}
+
+// mm64i for callers that need no result index
+template <int N, int NT, typename FA, typename FB, typename FO>
+__device__ __forceinline__ void mm64(int K, FA A, FB B, FO out) {
+    mm64i<N, NT>(K, A, B, [&](int, int r, int c, float v) { out(r, c, v); });
 }
 
 // e^x for x <= 0 (a decay between two tokens of a chunk) through the
@@ -544,7 +570,7 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdK<XT, GT> a) {
     }
 }
 
-constexpr size_t scratch_floats(int dk, int dv) { return 3 * 64 * static_cast<size_t>(dv) + 5 * 64 * static_cast<size_t>(dk); }
+constexpr size_t scratch_floats(int dk, int dv) { return 3 * 64 * static_cast<size_t>(dv) + 64 * static_cast<size_t>(dk); }
 
 template <int DK>
 constexpr size_t intra_lds_bytes() {
@@ -588,13 +614,13 @@ __global__ __launch_bounds__(kGradThreads) void bwd_intra_kernel(BwdK<XT, GT> a)
     float* gdO = gU + 64 * DV;
     float* gdU = gdO + 64 * DV;
     float* gdW = gdU + 64 * DV;
-    // running sums of dq, dk, dG: between two barriers, element (row,
-    // channel) is touched by one thread only (every product of width DK
-    // gives it to the same thread), so plain read-modify-writes suffice
-    float* gq = gdW + 64 * DK;
-    float* gk = gq + 64 * DK;
-    float* gG = gk + 64 * DK;
-    float* gKe = gG + 64 * DK;
+    // The running sums of dq, dk, dG stay in registers: every product of
+    // width DK, and the chain rule through A and M, deal element (row,
+    // channel) to the same lane (Deal64), which holds it at the same index.
+    constexpr int NS = Deal64<DK, kGradThreads>::PER_LANE;
+    float sq[NS], sk[NS], sg[NS];
+    // K_e = e^G K, for dT and d(B K_e) below
+    auto ke_at = [&](int r, int c) { return expf(sG[r * KP + c]) * sK[r * KP + c]; };
     auto tok = [&](int r) { return (t0 + r) * a.H + h; };
 
     // ---- 0. the forward's chunk quantities: G, A, M, T
@@ -655,11 +681,6 @@ __global__ __launch_bounds__(kGradThreads) void bwd_intra_kernel(BwdK<XT, GT> a)
                  }
                  gdO[r * DV + c] = d;
              });
-    // K_e = e^G K, for dT and d(B K_e) below
-    for (int e = tid; e < 64 * DK; e += kGradThreads) {
-        const int r = e / DK, c = e % DK;
-        gKe[e] = expf(sG[r * KP + c]) * sK[r * KP + c];
-    }
     __syncthreads();
     // ---- 2. dU = M^T dO + K^ dS_end
     mm64<DV, kGradThreads>(64, [&](int r, int s_) { return sM[s_ * MS + r]; }, [&](int s_, int c) { return gdO[s_ * DV + c]; },
@@ -669,20 +690,19 @@ __global__ __launch_bounds__(kGradThreads) void bwd_intra_kernel(BwdK<XT, GT> a)
     __syncthreads();
     // ---- 3. dQ_e = dO S^T, dK^ = U dS_end^T, dW = -dU S^T; the sums of dq,
     // dk, dG start here (Q_e = e^G Q, K^ = e^{G_last - G} K)
-    mm64<DK, kGradThreads>(S != nullptr ? DV : 0, [&](int r, int col) { return gdO[r * DV + col]; },
+    mm64i<DK, kGradThreads>(S != nullptr ? DV : 0, [&](int r, int col) { return gdO[r * DV + col]; },
              [&](int col, int i) { return S[i * DV + col]; },
-             [&](int r, int c, float dqe) {
+             [&](int x, int r, int c, float dqe) {
                  const float eg = expf(sG[r * KP + c]);
                  const float qv = r < L ? ld(a.q + tok(r) * DK + c) : 0.f;
-                 gq[r * DK + c] = eg * dqe;
-                 gG[r * DK + c] = eg * qv * dqe;
+                 sq[x] = eg * dqe;
+                 sg[x] = eg * qv * dqe;
              });
-    mm64<DK, kGradThreads>(DV, [&](int r, int col) { return gU[r * DV + col]; }, [&](int col, int i) { return dSe[i * DV + col]; },
-             [&](int r, int c, float dkh) {
-                 const int e = r * DK + c;
+    mm64i<DK, kGradThreads>(DV, [&](int r, int col) { return gU[r * DV + col]; }, [&](int col, int i) { return dSe[i * DV + col]; },
+             [&](int x, int r, int c, float dkh) {
                  const float eh = expf(sG[63 * KP + c] - sG[r * KP + c]), kv = sK[r * KP + c];
-                 gk[e] = eh * dkh;
-                 gG[e] -= eh * kv * dkh;
+                 sk[x] = eh * dkh;
+                 sg[x] -= eh * kv * dkh;
                  atomicAdd(&sdGl[c], eh * kv * dkh);  // (G_last's share of K^)
              });
     mm64<DK, kGradThreads>(S != nullptr ? DV : 0, [&](int r, int col) { return gdU[r * DV + col]; },
@@ -701,7 +721,7 @@ __global__ __launch_bounds__(kGradThreads) void bwd_intra_kernel(BwdK<XT, GT> a)
     mm64<64, kGradThreads>(DV, [&](int r, int col) { return gdU[r * DV + col]; },
              [&](int col, int s_) { return s_ < L ? ld(a.v + tok(s_) * DV + col) : 0.f; },
              [&](int r, int s_, float acc) { sdT[r * MS + s_] = acc; });
-    mm64<64, kGradThreads>(DK, [&](int r, int kk) { return gdW[r * DK + kk]; }, [&](int kk, int s_) { return gKe[s_ * DK + kk]; },
+    mm64<64, kGradThreads>(DK, [&](int r, int kk) { return gdW[r * DK + kk]; }, [&](int kk, int s_) { return ke_at(s_, kk); },
              [&](int r, int s_, float acc) {  // (same thread, same element as just above)
                  sdT[r * MS + s_] = s_ < r ? sB[s_] * (sdT[r * MS + s_] + acc) : 0.f;
              });
@@ -713,12 +733,11 @@ __global__ __launch_bounds__(kGradThreads) void bwd_intra_kernel(BwdK<XT, GT> a)
                  atomicAdd(&sdB[s_], ld(a.v + tok(s_) * DV + c) * acc);
              });
     // d(B K_e) = T^T dW: k's, G's and beta's shares
-    mm64<DK, kGradThreads>(64, [&](int s_, int r) { return sT[r * MS + s_]; }, [&](int r, int c) { return gdW[r * DK + c]; },
-             [&](int s_, int c, float acc) {
-                 const int e = s_ * DK + c;
-                 const float ke = gKe[e];
-                 gk[e] += sB[s_] * expf(sG[s_ * KP + c]) * acc;
-                 gG[e] += sB[s_] * ke * acc;
+    mm64i<DK, kGradThreads>(64, [&](int s_, int r) { return sT[r * MS + s_]; }, [&](int r, int c) { return gdW[r * DK + c]; },
+             [&](int x, int s_, int c, float acc) {
+                 const float eg = expf(sG[s_ * KP + c]), ke = eg * sK[s_ * KP + c];
+                 sk[x] += sB[s_] * eg * acc;
+                 sg[x] += sB[s_] * ke * acc;
                  if (s_ < L) atomicAdd(&sdB[s_], ke * acc);
              });
     __syncthreads();
@@ -752,23 +771,26 @@ __global__ __launch_bounds__(kGradThreads) void bwd_intra_kernel(BwdK<XT, GT> a)
     // am_mfma: for output rows in block B, the row sums over blocks S <= B
     // take e^{G_r - G_16B} e^{G_16B - G_s}, and the column sums over blocks
     // R >= B take e^{G_r - G_16R} e^{G_16R - G_s}.  A wave takes output tiles
-    // (B, channels 16 j .. 16 j + 15); lane (g, c) owns rows 16 B + 4 g + i
-    // of channel 16 j + c.  Where the diagonal block is steep (over the
-    // tile's channels) its share is summed pair by pair instead.
+    // (B, channels 16 j .. 16 j + 15) as Deal64 deals them; lane (g, c) owns
+    // rows 16 B + 4 g + i of channel 16 j + c.  Where the diagonal block is
+    // steep (over the tile's channels) its share is summed pair by pair.
     {
-        constexpr int NJ = DK / 16;
-        const int wave = tid >> 6, lane = tid & 63, g = lane >> 4, c = lane & 15;
+        using D = Deal64<DK, kGradThreads>;
+        static_assert(D::CPW == 1, "one column tile per wave");
+        const int lane = tid & 63, g = lane >> 4, c = lane & 15;
+        const D dl(tid >> 6);
         const float rmax = kSpanMax * kLog2e;  // (binds on diagonal blocks only)
-#pragma unroll 1
-        for (int t = wave; t < 4 * NJ; t += kGradThreads / 64) {
-            const int B = t & 3, ch = 16 * (t >> 2) + c;
+#pragma unroll
+        for (int t = 0; t < D::RPW; ++t) {
+            if (!dl.active) continue;
+            const int B = dl.r0 / 16 + t, ch = dl.c0 + c;
             const float* qcol = (ch < 64 ? sA : sT) + (ch & 63);  // the queries: qcol[r * MS]
             const float gB = sG[(16 * B) * KP + ch];
             const bool steep = __ballot(gB - sG[(16 * B + 15) * KP + ch] >= kSpanMax) != 0;
             // row sums: dA_B,S (K_S e^{G_16B - G_S}) over S, and the same with dM
             f32x4 xk = {0.f, 0.f, 0.f, 0.f}, xq = {0.f, 0.f, 0.f, 0.f};
             const int s_end = steep ? 16 * B : 16 * B + 16;
-#pragma unroll 2
+#pragma unroll 1
             for (int s0 = 0; s0 < s_end; s0 += 4) {
                 const int s_ = s0 + g, ra = 16 * B + c;
                 const float kr = sK[s_ * KP + ch] * __builtin_amdgcn_exp2f(fminf((gB - sG[s_ * KP + ch]) * kLog2e, rmax));
@@ -820,22 +842,35 @@ __global__ __launch_bounds__(kGradThreads) void bwd_intra_kernel(BwdK<XT, GT> a)
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int r = 16 * B + 4 * g + i, e = r * DK + ch;
+                const int r = 16 * B + 4 * g + i, x = 4 * t + i;
                 const float kv = sK[r * KP + ch], qv = qcol[r * MS];
-                gk[e] += dkr[i] + dks[i];
-                gq[e] += dqr[i];
-                gG[e] += kv * dkr[i] + qv * dqr[i] - kv * dks[i];
+                sk[x] += dkr[i] + dks[i];
+                sq[x] += dqr[i];
+                sg[x] += kv * dkr[i] + qv * dqr[i] - kv * dks[i];
             }
         }
     }
     __syncthreads();  // every read of sK, sG, sdT, sM is done
     // ---- 7. dla = reverse cumsum of dG (G_last is G_63); outputs
-    for (int e = tid; e < 64 * DK; e += kGradThreads) {
-        const int r = e / DK, c = e % DK;
-        sG[r * KP + c] = gG[e] + (r == 63 ? sdGl[c] : 0.f);
-        if (r < L) {
-            a.dq[tok(r) * DK + c] = gq[e];
-            a.dk[tok(r) * DK + c] = gk[e];
+    {
+        using D = Deal64<DK, kGradThreads>;
+        const int lane = tid & 63, g = lane >> 4, cl = lane & 15;
+        const D dl(tid >> 6);
+        if (dl.active) {
+#pragma unroll
+            for (int i = 0; i < D::RPW; ++i)
+#pragma unroll
+                for (int jj = 0; jj < D::CPW; ++jj)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int x = (i * D::CPW + jj) * 4 + e;
+                        const int r = dl.r0 + 16 * i + 4 * g + e, c = dl.c0 + 16 * jj + cl;
+                        sG[r * KP + c] = sg[x] + (r == 63 ? sdGl[c] : 0.f);
+                        if (r < L) {
+                            a.dq[tok(r) * DK + c] = sq[x];
+                            a.dk[tok(r) * DK + c] = sk[x];
+                        }
+                    }
         }
     }
     __syncthreads();
