@@ -183,7 +183,7 @@ __device__ __forceinline__ void lower_tile(int i, int& R, int& S) {
 
 // A (strictly lower) and M (lower with diagonal) of a chunk,
 //   A_rs = sum_c k_rc k_sc e^{G_rc - G_sc},  M_rs = sum_c q_rc k_sc e^{G_rc - G_sc},
-// by 16 x 16 blocks (R, S), R >= S, one wave each (waves 0 .. 9).  The
+// by 16 x 16 blocks (R, S), R >= S, one wave each (ten blocks).  The
 // pairwise decay factors through the first row of block R:
 //   e^{G_r - G_s} = e^{G_r - G_16R} e^{G_16R - G_s},
 // so a block is a product over the channels of (K_R or Q_R) * e^{G_R - G_16R}
@@ -194,90 +194,92 @@ __device__ __forceinline__ void lower_tile(int i, int& R, int& S) {
 // the block is summed pair by pair instead.  K, Q, G rows have stride kKP.
 template <int DK, int NT>
 __device__ __forceinline__ void am_mfma(const float* sK, const float* sQ, const float* sG, float* sA, float* sM) {
-    static_assert(NT >= 640 && DK % 16 == 0, "ten waves; whole runs of 16 channels");
+    static_assert(NT % 64 == 0 && DK % 16 == 0, "whole waves; whole runs of 16 channels");
     constexpr int KP = kKP<DK>, CW = DK / 4;  // lane (g, c) takes channels CW g .. CW g + CW - 1
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
-    if (wave >= 10) return;
-    int R, S;
-    lower_tile(wave, R, S);
-    const bool diag = R == S;
-    bool steep = false;
-    if (diag) {
-        float span = 0.f;
-        for (int ch = lane; ch < DK; ch += 64) span = fmaxf(span, sG[(16 * R) * KP + ch] - sG[(16 * R + 15) * KP + ch]);
-        steep = __ballot(span >= kSpanMax) != 0;
-    }
-    if (!steep) {
-        // v_mfma_f32_16x16x4_f32: lane (g, c) gives A[c][g] and B[g][c] and
-        // holds D[4g + i][c]; the left rows are 16R + c, the right ones 16S + c
-        const float* kr = sK + (16 * R + c) * KP + CW * g;
-        const float* qr = sQ + (16 * R + c) * KP + CW * g;
-        const float* gr = sG + (16 * R + c) * KP + CW * g;
-        const float* gf = sG + (16 * R) * KP + CW * g;
-        const float* ks = sK + (16 * S + c) * KP + CW * g;
-        const float* gs = sG + (16 * S + c) * KP + CW * g;
-        // exponent bounds: the left factor at most 1; the right one at most
-        // 1 below the diagonal and e^{kSpanMax} on it (the bounds only bind
-        // for decays that grow, which the inputs do not hold)
-        const float rmax = diag ? kSpanMax * kLog2e : 0.f;
-        f32x4 aa = {0.f, 0.f, 0.f, 0.f}, am = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+    for (int tile = wave; tile < 10; tile += NT / 64) {
+        int R, S;
+        lower_tile(tile, R, S);
+        const bool diag = R == S;
+        bool steep = false;
+        if (diag) {
+            float span = 0.f;
+            for (int ch = lane; ch < DK; ch += 64) span = fmaxf(span, sG[(16 * R) * KP + ch] - sG[(16 * R + 15) * KP + ch]);
+            steep = __ballot(span >= kSpanMax) != 0;
+        }
+        if (!steep) {
+            // v_mfma_f32_16x16x4_f32: lane (g, c) gives A[c][g] and B[g][c] and
+            // holds D[4g + i][c]; the left rows are 16R + c, the right ones 16S + c
+            const float* kr = sK + (16 * R + c) * KP + CW * g;
+            const float* qr = sQ + (16 * R + c) * KP + CW * g;
+            const float* gr = sG + (16 * R + c) * KP + CW * g;
+            const float* gf = sG + (16 * R) * KP + CW * g;
+            const float* ks = sK + (16 * S + c) * KP + CW * g;
+            const float* gs = sG + (16 * S + c) * KP + CW * g;
+            // exponent bounds: the left factor at most 1; the right one at most
+            // 1 below the diagonal and e^{kSpanMax} on it (the bounds only bind
+            // for decays that grow, which the inputs do not hold)
+            const float rmax = diag ? kSpanMax * kLog2e : 0.f;
+            f32x4 aa = {0.f, 0.f, 0.f, 0.f}, am = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int u = 0; u < CW / 4; ++u) {
-            const float4 k4 = reinterpret_cast<const float4*>(kr)[u], q4 = reinterpret_cast<const float4*>(qr)[u];
-            const float4 g4 = reinterpret_cast<const float4*>(gr)[u], f4 = reinterpret_cast<const float4*>(gf)[u];
-            const float4 s4 = reinterpret_cast<const float4*>(ks)[u], h4 = reinterpret_cast<const float4*>(gs)[u];
-            const float kv[4] = {k4.x, k4.y, k4.z, k4.w}, qv[4] = {q4.x, q4.y, q4.z, q4.w};
-            const float gv[4] = {g4.x, g4.y, g4.z, g4.w}, fv[4] = {f4.x, f4.y, f4.z, f4.w};
-            const float sv[4] = {s4.x, s4.y, s4.z, s4.w}, hv[4] = {h4.x, h4.y, h4.z, h4.w};
+            for (int u = 0; u < CW / 4; ++u) {
+                const float4 k4 = reinterpret_cast<const float4*>(kr)[u], q4 = reinterpret_cast<const float4*>(qr)[u];
+                const float4 g4 = reinterpret_cast<const float4*>(gr)[u], f4 = reinterpret_cast<const float4*>(gf)[u];
+                const float4 s4 = reinterpret_cast<const float4*>(ks)[u], h4 = reinterpret_cast<const float4*>(gs)[u];
+                const float kv[4] = {k4.x, k4.y, k4.z, k4.w}, qv[4] = {q4.x, q4.y, q4.z, q4.w};
+                const float gv[4] = {g4.x, g4.y, g4.z, g4.w}, fv[4] = {f4.x, f4.y, f4.z, f4.w};
+                const float sv[4] = {s4.x, s4.y, s4.z, s4.w}, hv[4] = {h4.x, h4.y, h4.z, h4.w};
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float fl = __builtin_amdgcn_exp2f(fminf((gv[j] - fv[j]) * kLog2e, 0.f));
-                const float fr = __builtin_amdgcn_exp2f(fminf((fv[j] - hv[j]) * kLog2e, rmax));
-                const float b = sv[j] * fr;
-                aa = __builtin_amdgcn_mfma_f32_16x16x4f32(kv[j] * fl, b, aa, 0, 0, 0);
-                am = __builtin_amdgcn_mfma_f32_16x16x4f32(qv[j] * fl, b, am, 0, 0, 0);
+                for (int j = 0; j < 4; ++j) {
+                    const float fl = __builtin_amdgcn_exp2f(fminf((gv[j] - fv[j]) * kLog2e, 0.f));
+                    const float fr = __builtin_amdgcn_exp2f(fminf((fv[j] - hv[j]) * kLog2e, rmax));
+                    const float b = sv[j] * fr;
+                    aa = __builtin_amdgcn_mfma_f32_16x16x4f32(kv[j] * fl, b, aa, 0, 0, 0);
+                    am = __builtin_amdgcn_mfma_f32_16x16x4f32(qv[j] * fl, b, am, 0, 0, 0);
+                }
+            }
+            const int s_ = 16 * S + c;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * R + 4 * g + i;
+                sA[r * MS + s_] = s_ < r ? aa[i] : 0.f;
+                sM[r * MS + s_] = s_ <= r ? am[i] : 0.f;
+            }
+        } else {
+            // the 136 pairs s <= r of the block, pair by pair over the channels;
+            // the lane of pair (r, s), s < r, also clears (s, r)
+            for (int p = lane; p < 136; p += 64) {
+                int rl = static_cast<int>((sqrtf(8.f * p + 1.f) - 1.f) * 0.5f);
+                if ((rl + 1) * (rl + 2) / 2 <= p) ++rl;
+                if (rl * (rl + 1) / 2 > p) --rl;
+                const int sl = p - rl * (rl + 1) / 2, r = 16 * R + rl, s_ = 16 * R + sl;
+                float av = 0.f, mv = 0.f;
+                for (int ch = 0; ch < DK; ch += 4) {
+                    const float4 k4 = *reinterpret_cast<const float4*>(sK + r * KP + ch);
+                    const float4 q4 = *reinterpret_cast<const float4*>(sQ + r * KP + ch);
+                    const float4 g4 = *reinterpret_cast<const float4*>(sG + r * KP + ch);
+                    const float4 s4 = *reinterpret_cast<const float4*>(sK + s_ * KP + ch);
+                    const float4 h4 = *reinterpret_cast<const float4*>(sG + s_ * KP + ch);
+                    const float e0 = s4.x * decay(g4.x - h4.x), e1 = s4.y * decay(g4.y - h4.y);
+                    const float e2 = s4.z * decay(g4.z - h4.z), e3 = s4.w * decay(g4.w - h4.w);
+                    av += k4.x * e0 + k4.y * e1 + k4.z * e2 + k4.w * e3;
+                    mv += q4.x * e0 + q4.y * e1 + q4.z * e2 + q4.w * e3;
+                }
+                sA[r * MS + s_] = sl < rl ? av : 0.f;
+                sM[r * MS + s_] = mv;
+                if (sl < rl) {
+                    sA[s_ * MS + r] = 0.f;
+                    sM[s_ * MS + r] = 0.f;
+                }
             }
         }
-        const int s_ = 16 * S + c;
+        if (!diag) {  // the block (S, R) above the diagonal
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = 16 * R + 4 * g + i;
-            sA[r * MS + s_] = s_ < r ? aa[i] : 0.f;
-            sM[r * MS + s_] = s_ <= r ? am[i] : 0.f;
-        }
-    } else {
-        // the 136 pairs s <= r of the block, pair by pair over the channels;
-        // the lane of pair (r, s), s < r, also clears (s, r)
-        for (int p = lane; p < 136; p += 64) {
-            int rl = static_cast<int>((sqrtf(8.f * p + 1.f) - 1.f) * 0.5f);
-            if ((rl + 1) * (rl + 2) / 2 <= p) ++rl;
-            if (rl * (rl + 1) / 2 > p) --rl;
-            const int sl = p - rl * (rl + 1) / 2, r = 16 * R + rl, s_ = 16 * R + sl;
-            float av = 0.f, mv = 0.f;
-            for (int ch = 0; ch < DK; ch += 4) {
-                const float4 k4 = *reinterpret_cast<const float4*>(sK + r * KP + ch);
-                const float4 q4 = *reinterpret_cast<const float4*>(sQ + r * KP + ch);
-                const float4 g4 = *reinterpret_cast<const float4*>(sG + r * KP + ch);
-                const float4 s4 = *reinterpret_cast<const float4*>(sK + s_ * KP + ch);
-                const float4 h4 = *reinterpret_cast<const float4*>(sG + s_ * KP + ch);
-                const float e0 = s4.x * decay(g4.x - h4.x), e1 = s4.y * decay(g4.y - h4.y);
-                const float e2 = s4.z * decay(g4.z - h4.z), e3 = s4.w * decay(g4.w - h4.w);
-                av += k4.x * e0 + k4.y * e1 + k4.z * e2 + k4.w * e3;
-                mv += q4.x * e0 + q4.y * e1 + q4.z * e2 + q4.w * e3;
+            for (int i = 0; i < 4; ++i) {
+                sA[(16 * S + 4 * g + i) * MS + 16 * R + c] = 0.f;
+                sM[(16 * S + 4 * g + i) * MS + 16 * R + c] = 0.f;
             }
-            sA[r * MS + s_] = sl < rl ? av : 0.f;
-            sM[r * MS + s_] = mv;
-            if (sl < rl) {
-                sA[s_ * MS + r] = 0.f;
-                sM[s_ * MS + r] = 0.f;
-            }
-        }
-    }
-    if (!diag) {  // the block (S, R) above the diagonal
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            sA[(16 * S + 4 * g + i) * MS + 16 * R + c] = 0.f;
-            sM[(16 * S + 4 * g + i) * MS + 16 * R + c] = 0.f;
         }
     }
 }
