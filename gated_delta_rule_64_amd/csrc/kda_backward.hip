@@ -366,12 +366,27 @@ __global__ __launch_bounds__(kRecThreads) void chunk_records_kernel(BwdK<XT, GT>
     const GenRec R = gen_rec(DK, DV);
     float* rec = const_cast<float*>(a.rec) + (static_cast<int64_t>(slot) * a.H + h) * R.size;
     auto tok = [&](int r) { return (t0 + r) * a.H + h; };
-    for (int i = tid; i < 64 * DK; i += kRecThreads) {
-        const int r = i / DK, c = i % DK;
-        const bool in = r < L;
-        sK[r * KP + c] = in ? ld(a.k + tok(r) * DK + c) : 0.f;
-        sQ[r * KP + c] = in ? ld(a.q + tok(r) * DK + c) : 0.f;
-        sG[r * KP + c] = in ? ld(a.la + tok(r) * DK + c) : 0.f;  // padded tokens: no decay, no write
+    {
+        // every load of the chunk's keys, queries and decays goes out before
+        // the first is stored (padded tokens: no decay, no write)
+        constexpr int NP = 64 * DK / kRecThreads;
+        static_assert(NP * kRecThreads == 64 * DK, "whole passes");
+        float kv[NP], qv[NP], gv[NP];
+#pragma unroll
+        for (int it = 0; it < NP; ++it) {
+            const int i = tid + it * kRecThreads, r = i / DK, c = i % DK;
+            const bool in = r < L;
+            kv[it] = in ? ld(a.k + tok(r) * DK + c) : 0.f;
+            qv[it] = in ? ld(a.q + tok(r) * DK + c) : 0.f;
+            gv[it] = in ? ld(a.la + tok(r) * DK + c) : 0.f;
+        }
+#pragma unroll
+        for (int it = 0; it < NP; ++it) {
+            const int i = tid + it * kRecThreads, r = i / DK, c = i % DK;
+            sK[r * KP + c] = kv[it];
+            sQ[r * KP + c] = qv[it];
+            sG[r * KP + c] = gv[it];
+        }
     }
     if (tid < 64) sB[tid] = tid < L ? ld(a.beta + tok(tid)) : 0.f;
     __syncthreads();
@@ -625,12 +640,28 @@ __global__ __launch_bounds__(kGradThreads) void bwd_intra_kernel(BwdK<XT, GT> a)
     auto ke_at = [&](int r, int c) { return expf(sG[r * KP + c]) * sK[r * KP + c]; };
     auto tok = [&](int r) { return (t0 + r) * a.H + h; };
 
-    // ---- 0. the forward's chunk quantities: G, A, M, T
-    for (int i = tid; i < 64 * DK; i += kGradThreads) {
-        const int r = i / DK, c = i % DK;
-        const bool in = r < L;
-        sK[r * KP + c] = in ? ld(a.k + tok(r) * DK + c) : 0.f;
-        sG[r * KP + c] = in ? ld(a.la + tok(r) * DK + c) : 0.f;
+    // ---- 0. the forward's chunk quantities: G, A, M, T.  The queries sit,
+    // padded like K, in the space of T, dT, P until T is made.
+    constexpr int NP = 64 * DK / kGradThreads;
+    static_assert(NP * kGradThreads == 64 * DK, "whole passes");
+    {
+        // every load goes out before the first is stored
+        float kv[NP], qv[NP], gv[NP];
+#pragma unroll
+        for (int it = 0; it < NP; ++it) {
+            const int i = tid + it * kGradThreads, r = i / DK, c = i % DK;
+            const bool in = r < L;
+            kv[it] = in ? ld(a.k + tok(r) * DK + c) : 0.f;
+            qv[it] = in ? ld(a.q + tok(r) * DK + c) : 0.f;
+            gv[it] = in ? ld(a.la + tok(r) * DK + c) : 0.f;
+        }
+#pragma unroll
+        for (int it = 0; it < NP; ++it) {
+            const int i = tid + it * kGradThreads, r = i / DK, c = i % DK;
+            sK[r * KP + c] = kv[it];
+            sT[r * KP + c] = qv[it];
+            sG[r * KP + c] = gv[it];
+        }
     }
     if (tid < 64) {
         sB[tid] = tid < L ? ld(a.beta + tok(tid)) : 0.f;
@@ -646,19 +677,9 @@ __global__ __launch_bounds__(kGradThreads) void bwd_intra_kernel(BwdK<XT, GT> a)
         }
     }
     __syncthreads();
-    // A (strictly lower) and M (lower with diagonal), by blocks on the matrix
-    // cores; the queries sit, padded like K, in the space of T, dT, P until T
-    // is made
-    {
-        float* sQ = sT;
-        for (int i = tid; i < 64 * DK; i += kGradThreads) {
-            const int r = i / DK, c = i % DK;
-            sQ[r * KP + c] = r < L ? ld(a.q + tok(r) * DK + c) : 0.f;
-        }
-        __syncthreads();
-        am_mfma<DK, kGradThreads>(sK, sQ, sG, sA, sM);
-        __syncthreads();  // the queries are dead; T goes where they were
-    }
+    // A (strictly lower) and M (lower with diagonal), by blocks on the matrix cores
+    am_mfma<DK, kGradThreads>(sK, sT, sG, sA, sM);
+    __syncthreads();  // the queries are dead; T goes where they were
     t_solve<kGradThreads>(sA, sB, sT, sP);  // (P's space is free until phase 5)
 
     // ---- 1. U = U~ - W S and O = Q' S + M U~; dO, dz
@@ -743,7 +764,15 @@ __global__ __launch_bounds__(kGradThreads) void bwd_intra_kernel(BwdK<XT, GT> a)
                  if (s_ < L) atomicAdd(&sdB[s_], ke * acc);
              });
     __syncthreads();
-    // ---- 5. dY = -T^T dT T^T; d(B A) = dY below the diagonal
+    // ---- 5. dY = -T^T dT T^T; d(B A) = dY below the diagonal.  The queries
+    // for the chain rule through A and M are loaded now and stored once every
+    // read of A and T is done.
+    float qn[NP];
+#pragma unroll
+    for (int it = 0; it < NP; ++it) {
+        const int i = tid + it * kGradThreads, r = i / DK, c = i % DK;
+        qn[it] = r < L ? ld(a.q + tok(r) * DK + c) : 0.f;
+    }
     mm64<64, kGradThreads>(64, [&](int r, int s_) { return sdT[r * MS + s_]; }, [&](int s_, int c) { return sT[c * MS + s_]; },
              [&](int r, int c, float acc) { sP[r * MS + c] = acc; });
     __syncthreads();
@@ -758,10 +787,10 @@ __global__ __launch_bounds__(kGradThreads) void bwd_intra_kernel(BwdK<XT, GT> a)
     __syncthreads();  // every read of A and T is done: the queries go there
     // the queries for the loops below, channels 0 .. 63 in A's space and
     // 64 .. 127 in T's (a thread's channels never straddle the two)
-    auto qs = [&](int r, int c) -> float& { return (c < 64 ? sA : sT)[r * MS + (c & 63)]; };
-    for (int i = tid; i < 64 * DK; i += kGradThreads) {
-        const int r = i / DK, c = i % DK;
-        qs(r, c) = r < L ? ld(a.q + tok(r) * DK + c) : 0.f;
+#pragma unroll
+    for (int it = 0; it < NP; ++it) {
+        const int i = tid + it * kGradThreads, r = i / DK, c = i % DK;
+        (c < 64 ? sA : sT)[r * MS + (c & 63)] = qn[it];
     }
     __syncthreads();
     // ---- 6. through A (dA = B dY) and M (dM), with E_rsc = e^{G_rc - G_sc}:
