@@ -152,6 +152,72 @@ __device__ __forceinline__ void mm64i(int K, FA A, FB B, FO out) {
                 out((i * CPW + jj) * 4 + e, r0 + 16 * i + 4 * g + e, c0 + 16 * jj + c, acc[i][jj][e]);
 }
 
+// Two products that share their B operand, C1 = A1 B and C2 = A2 B, in one
+// pass: each run's B values are loaded once and serve both, and both
+// products' runs wait on the same memory round trips.  Every sum is made in
+// the same order as mm64i would make it.
+template <int N, int NT, typename FA1, typename FA2, typename FB, typename FO1, typename FO2>
+__device__ __forceinline__ void mm64i2(int K, FA1 A1, FA2 A2, FB B, FO1 out1, FO2 out2) {
+    using D = Deal64<N, NT>;
+    constexpr int RPW = D::RPW, CPW = D::CPW;
+    const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
+    const D d(threadIdx.x >> 6);
+    if (!d.active) return;
+    const int r0 = d.r0, c0 = d.c0;
+    f32x4 acc1[RPW][CPW], acc2[RPW][CPW];
+#pragma unroll
+    for (int i = 0; i < RPW; ++i)
+#pragma unroll
+        for (int jj = 0; jj < CPW; ++jj) acc1[i][jj] = acc2[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto load = [&](int k0, float (&av1)[RPW][4], float (&av2)[RPW][4], float (&bv)[CPW][4]) {
+        const int kk = k0 + 4 * g;
+#pragma unroll
+        for (int i = 0; i < RPW; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                av1[i][j] = A1(r0 + 16 * i + c, kk + j);
+                av2[i][j] = A2(r0 + 16 * i + c, kk + j);
+            }
+#pragma unroll
+        for (int jj = 0; jj < CPW; ++jj)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) bv[jj][j] = B(kk + j, c0 + 16 * jj + c);
+    };
+    auto mma = [&](const float (&av1)[RPW][4], const float (&av2)[RPW][4], const float (&bv)[CPW][4]) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int i = 0; i < RPW; ++i)
+#pragma unroll
+                for (int jj = 0; jj < CPW; ++jj) {
+                    acc1[i][jj] = __builtin_amdgcn_mfma_f32_16x16x4f32(av1[i][j], bv[jj][j], acc1[i][jj], 0, 0, 0);
+                    acc2[i][jj] = __builtin_amdgcn_mfma_f32_16x16x4f32(av2[i][j], bv[jj][j], acc2[i][jj], 0, 0, 0);
+                }
+    };
+    float p0[RPW][4], q0[RPW][4], b0[CPW][4], p1[RPW][4], q1[RPW][4], b1[CPW][4];
+    if (K > 0) load(0, p0, q0, b0);
+#pragma unroll 1
+    for (int k0 = 0; k0 < K; k0 += 32) {
+        const bool two = k0 + 16 < K;
+        load(two ? k0 + 16 : k0, p1, q1, b1);
+        mma(p0, q0, b0);
+        if (two) {
+            load(k0 + 32 < K ? k0 + 32 : k0 + 16, p0, q0, b0);
+            mma(p1, q1, b1);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < RPW; ++i)
+#pragma unroll
+        for (int jj = 0; jj < CPW; ++jj)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int x = (i * CPW + jj) * 4 + e, r = r0 + 16 * i + 4 * g + e, cc = c0 + 16 * jj + c;
+                out1(x, r, cc, acc1[i][jj][e]);
+                out2(x, r, cc, acc2[i][jj][e]);
+            }
+}
+
 // mm64i for callers that need no result index
 template <int N, int NT, typename FA, typename FB, typename FO>
 __device__ __forceinline__ void mm64(int K, FA A, FB B, FO out) {
@@ -682,13 +748,12 @@ __global__ __launch_bounds__(kGradThreads) void bwd_intra_kernel(BwdK<XT, GT> a)
     __syncthreads();  // the queries are dead; T goes where they were
     t_solve<kGradThreads>(sA, sB, sT, sP);  // (P's space is free until phase 5)
 
-    // ---- 1. U = U~ - W S and O = Q' S + M U~; dO, dz
-    mm64<DV, kGradThreads>(S != nullptr ? DK : 0, [&](int r, int kk) { return rec[R.W + r * DK + kk]; },
+    // ---- 1. U = U~ - W S and O = Q' S + M U~ (one pass over S); dO, dz
+    mm64i2<DV, kGradThreads>(S != nullptr ? DK : 0, [&](int r, int kk) { return rec[R.W + r * DK + kk]; },
+             [&](int r, int kk) { return rec[R.Qp + r * DK + kk]; },
              [&](int kk, int c) { return S[kk * DV + c]; },
-             [&](int r, int c, float acc) { gU[r * DV + c] = rec[R.U + r * DV + c] - acc; });
-    mm64<DV, kGradThreads>(S != nullptr ? DK : 0, [&](int r, int kk) { return rec[R.Qp + r * DK + kk]; },
-             [&](int kk, int c) { return S[kk * DV + c]; },
-             [&](int r, int c, float acc) {
+             [&](int, int r, int c, float acc) { gU[r * DV + c] = rec[R.U + r * DV + c] - acc; },
+             [&](int, int r, int c, float acc) {
                  const float o = rec[R.Oi + r * DV + c] + acc;
                  float d = 0.f;
                  if (r < L) {
