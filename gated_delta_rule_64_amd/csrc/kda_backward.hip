@@ -605,11 +605,15 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdK<XT, GT> a) {
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) bd[kb][jj] = sD[(16 * kb + 4 * g + jj) * kCS + c];
-        f32x4 xa = {0.f, 0.f, 0.f, 0.f};
+        // (two accumulators, even and odd blocks of terms: two independent
+        // chains of products instead of one)
+        f32x4 xa2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) xa = __builtin_amdgcn_mfma_f32_16x16x4f32(kA[kb][jj], bd[kb][jj], xa, 0, 0, 0);
+            for (int jj = 0; jj < 4; ++jj)
+                xa2[kb & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(kA[kb][jj], bd[kb][jj], xa2[kb & 1], 0, 0, 0);
+        const f32x4 xa = xa2[0] + xa2[1];
         load_k(rec_next);
 #pragma unroll
         for (int e = 0; e < 4; ++e) sX[(16 * wave + 4 * g + e) * kCS + c] = xa[e];
@@ -623,20 +627,27 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdK<XT, GT> a) {
                     bo[kb][jj] = sO[(16 * kb + 4 * g + jj) * kCS + c];
                     bx[kb][jj] = sX[(16 * kb + 4 * g + jj) * kCS + c];
                 }
+            // (two accumulators a tile, Q'^T dO onto Diag(gamma) dS and W^T X
+            // from zero: independent chains of products)
+            f32x4 acc[SPW][2];
 #pragma unroll
-            for (int t = 0; t < SPW; ++t) {
-                f32x4 acc;
+            for (int t = 0; t < SPW; ++t)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) acc[e] = gam[t][e] * D[t][e];
+                for (int e = 0; e < 4; ++e) {
+                    acc[t][0][e] = gam[t][e] * D[t][e];
+                    acc[t][1][e] = 0.f;
+                }
 #pragma unroll
-                for (int kb = 0; kb < 4; ++kb)
+            for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) {
-                        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qT[t][kb][jj], bo[kb][jj], acc, 0, 0, 0);
-                        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(wT[t][kb][jj], bx[kb][jj], acc, 0, 0, 0);
+                for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+                    for (int t = 0; t < SPW; ++t) {
+                        acc[t][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(qT[t][kb][jj], bo[kb][jj], acc[t][0], 0, 0, 0);
+                        acc[t][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(wT[t][kb][jj], bx[kb][jj], acc[t][1], 0, 0, 0);
                     }
-                D[t] = acc;
-            }
+#pragma unroll
+            for (int t = 0; t < SPW; ++t) D[t] = acc[t][0] + acc[t][1];
             load_t(rec_next);
 #pragma unroll
             for (int t = 0; t < SPW; ++t)
