@@ -759,27 +759,56 @@ __global__ __launch_bounds__(kGradThreads) void bwd_intra_kernel(BwdK<XT, GT> a)
     __syncthreads();  // the queries are dead; T goes where they were
     t_solve<kGradThreads>(sA, sB, sT, sP);  // (P's space is free until phase 5)
 
-    // ---- 1. U = U~ - W S and O = Q' S + M U~ (one pass over S); dO, dz
-    mm64i2<DV, kGradThreads>(S != nullptr ? DK : 0, [&](int r, int kk) { return rec[R.W + r * DK + kk]; },
-             [&](int r, int kk) { return rec[R.Qp + r * DK + kk]; },
-             [&](int kk, int c) { return S[kk * DV + c]; },
-             [&](int, int r, int c, float acc) { gU[r * DV + c] = rec[R.U + r * DV + c] - acc; },
-             [&](int, int r, int c, float acc) {
-                 const float o = rec[R.Oi + r * DV + c] + acc;
-                 float d = 0.f;
-                 if (r < L) {
-                     const int64_t oidx = tok(r) * DV + c;
-                     const float dy = ld(a.dy + oidx);
-                     if (a.z) {
-                         const float sg = sigmoid(ld(a.z + oidx));
-                         d = dy * sg;
-                         a.dz[oidx] = dy * o * sg * (1.f - sg);
-                     } else {
-                         d = dy;
-                     }
-                 }
-                 gdO[r * DV + c] = d;
-             });
+    // ---- 1. U = U~ - W S and O = Q' S + M U~ (one pass over S); dO, dz.
+    // The products leave their sums in registers; every load the results
+    // need (U~, M U~, dy, z) is then issued before the first store.  Taken
+    // result by result, each load waited for the store before it, since the
+    // compiler cannot tell the record from the scratch and output it writes.
+    {
+        using D1 = Deal64<DV, kGradThreads>;
+        constexpr int NX = D1::PER_LANE;
+        float sU[NX], sO[NX];
+        int rx[NX], cx[NX];
+        mm64i2<DV, kGradThreads>(S != nullptr ? DK : 0, [&](int r, int kk) { return rec[R.W + r * DK + kk]; },
+                 [&](int r, int kk) { return rec[R.Qp + r * DK + kk]; },
+                 [&](int kk, int c) { return S[kk * DV + c]; },
+                 [&](int x, int r, int c, float acc) { sU[x] = acc; rx[x] = r; cx[x] = c; },
+                 [&](int x, int, int, float acc) { sO[x] = acc; });
+        const D1 d1(tid >> 6);
+        if (d1.active) {
+            float vu[NX], vo[NX], vdy[NX], vz[NX];
+            // without a gate, z's loads read dy again (same shape) and are
+            // not used: no branch between a load and the next
+            const XT* zp = a.z ? a.z : a.dy;
+#pragma unroll
+            for (int x = 0; x < NX; ++x) {
+                const int r = rx[x], c = cx[x];
+                // rows past the chunk's end read row 0 (L >= 1) and are not used
+                const int64_t oidx = tok(r < L ? r : 0) * DV + c;
+                vu[x] = rec[R.U + r * DV + c];
+                vo[x] = rec[R.Oi + r * DV + c];
+                vdy[x] = ld(a.dy + oidx);
+                vz[x] = ld(zp + oidx);
+            }
+#pragma unroll
+            for (int x = 0; x < NX; ++x) {
+                const int r = rx[x], c = cx[x];
+                gU[r * DV + c] = vu[x] - sU[x];
+                const float o = vo[x] + sO[x];
+                float d = 0.f;
+                if (r < L) {
+                    if (a.z) {
+                        const float sg = sigmoid(vz[x]);
+                        d = vdy[x] * sg;
+                        a.dz[tok(r) * DV + c] = vdy[x] * o * sg * (1.f - sg);
+                    } else {
+                        d = vdy[x];
+                    }
+                }
+                gdO[r * DV + c] = d;
+            }
+        }
+    }
     __syncthreads();
     // ---- 2. dU = M^T dO + K^ dS_end
     mm64<DV, kGradThreads>(64, [&](int r, int s_) { return sM[s_ * MS + r]; }, [&](int s_, int c) { return gdO[s_ * DV + c]; },
@@ -793,7 +822,10 @@ __global__ __launch_bounds__(kGradThreads) void bwd_intra_kernel(BwdK<XT, GT> a)
              [&](int col, int i) { return S[i * DV + col]; },
              [&](int x, int r, int c, float dqe) {
                  const float eg = expf(sG[r * KP + c]);
-                 const float qv = r < L ? ld(a.q + tok(r) * DK + c) : 0.f;
+                 // (rows past the chunk's end read row 0 and drop it: a load
+                 // under no branch, so the lane's loads go out together)
+                 const float qraw = ld(a.q + tok(r < L ? r : 0) * DK + c);
+                 const float qv = r < L ? qraw : 0.f;
                  sq[x] = eg * dqe;
                  sg[x] = eg * qv * dqe;
              });
@@ -807,18 +839,35 @@ __global__ __launch_bounds__(kGradThreads) void bwd_intra_kernel(BwdK<XT, GT> a)
     mm64<DK, kGradThreads>(S != nullptr ? DV : 0, [&](int r, int col) { return gdU[r * DV + col]; },
              [&](int col, int i) { return S[i * DV + col]; },
              [&](int r, int c, float acc) { gdW[r * DK + c] = -acc; });
-    if (tid < DK) {  // dgamma = diag(S^T dS_end); gamma = e^{G_last}
+    if (S != nullptr) {  // dgamma = diag(S dS_end^T); gamma = e^{G_last}
+        // TPR threads per state row, each loading its columns in one batch,
+        // then a sum across those lanes (a row's threads share a wave)
+        constexpr int TPR = kGradThreads / DK, NCOL = (DV + TPR - 1) / TPR;
+        static_assert(TPR * DK == kGradThreads && TPR <= 64, "rows dealt to lane groups");
+        const int row = tid / TPR, part = tid % TPR;
+        float sv[NCOL], ev[NCOL];
+#pragma unroll
+        for (int i = 0; i < NCOL; ++i) {
+            const int col = part + TPR * i;
+            sv[i] = col < DV ? S[row * DV + col] : 0.f;
+            ev[i] = col < DV ? dSe[row * DV + col] : 0.f;
+        }
         float dg = 0.f;
-        if (S != nullptr)
-            for (int col = 0; col < DV; ++col) dg += S[tid * DV + col] * dSe[tid * DV + col];
-        atomicAdd(&sdGl[tid], expf(sG[63 * KP + tid]) * dg);
+#pragma unroll
+        for (int i = 0; i < NCOL; ++i) dg += sv[i] * ev[i];
+#pragma unroll
+        for (int off = TPR / 2; off > 0; off >>= 1) dg += __shfl_xor(dg, off, TPR);
+        if (part == 0) atomicAdd(&sdGl[row], expf(sG[63 * KP + row]) * dg);
     }
     __syncthreads();
     // ---- 4. dM = dO U^T (into M's place); dT = dU (B V)^T + dW (B K_e)^T
     mm64<64, kGradThreads>(DV, [&](int r, int col) { return gdO[r * DV + col]; }, [&](int col, int s_) { return gU[s_ * DV + col]; },
              [&](int r, int s_, float acc) { sM[r * MS + s_] = s_ <= r ? acc : 0.f; });
     mm64<64, kGradThreads>(DV, [&](int r, int col) { return gdU[r * DV + col]; },
-             [&](int col, int s_) { return s_ < L ? ld(a.v + tok(s_) * DV + col) : 0.f; },
+             [&](int col, int s_) {
+                 const float vv = ld(a.v + tok(s_ < L ? s_ : 0) * DV + col);
+                 return s_ < L ? vv : 0.f;
+             },
              [&](int r, int s_, float acc) { sdT[r * MS + s_] = acc; });
     mm64<64, kGradThreads>(DK, [&](int r, int kk) { return gdW[r * DK + kk]; }, [&](int kk, int s_) { return ke_at(s_, kk); },
              [&](int r, int s_, float acc) {  // (same thread, same element as just above)
@@ -827,9 +876,10 @@ __global__ __launch_bounds__(kGradThreads) void bwd_intra_kernel(BwdK<XT, GT> a)
     // d(B V) = T^T dU: dv, and beta's share
     mm64<DV, kGradThreads>(64, [&](int s_, int r) { return sT[r * MS + s_]; }, [&](int r, int c) { return gdU[r * DV + c]; },
              [&](int s_, int c, float acc) {
+                 const float vv = ld(a.v + tok(s_ < L ? s_ : 0) * DV + c);
                  if (s_ >= L) return;
                  a.dv[tok(s_) * DV + c] = sB[s_] * acc;
-                 atomicAdd(&sdB[s_], ld(a.v + tok(s_) * DV + c) * acc);
+                 atomicAdd(&sdB[s_], vv * acc);
              });
     // d(B K_e) = T^T dW: k's, G's and beta's shares
     mm64i<DK, kGradThreads>(64, [&](int s_, int r) { return sT[r * MS + s_]; }, [&](int r, int c) { return gdW[r * DK + c]; },
