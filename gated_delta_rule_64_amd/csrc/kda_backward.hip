@@ -441,10 +441,14 @@ __global__ __launch_bounds__(kRecThreads) void chunk_records_kernel(BwdK<XT, GT>
 #pragma unroll
         for (int it = 0; it < NP; ++it) {
             const int i = tid + it * kRecThreads, r = i / DK, c = i % DK;
+            // rows past the chunk's end read row 0 (L >= 1) and drop it, so
+            // no load sits under a branch that would wait for it
             const bool in = r < L;
-            kv[it] = in ? ld(a.k + tok(r) * DK + c) : 0.f;
-            qv[it] = in ? ld(a.q + tok(r) * DK + c) : 0.f;
-            gv[it] = in ? ld(a.la + tok(r) * DK + c) : 0.f;
+            const int64_t o = tok(in ? r : 0) * DK + c;
+            const float kr = ld(a.k + o), qr = ld(a.q + o), gr = ld(a.la + o);
+            kv[it] = in ? kr : 0.f;
+            qv[it] = in ? qr : 0.f;
+            gv[it] = in ? gr : 0.f;
         }
 #pragma unroll
         for (int it = 0; it < NP; ++it) {
@@ -478,7 +482,10 @@ __global__ __launch_bounds__(kRecThreads) void chunk_records_kernel(BwdK<XT, GT>
              [&](int s_, int c) { return sB[s_] * expf(sG[s_ * KP + c]) * sK[s_ * KP + c]; },
              [&](int r, int c, float acc) { rec[R.W + r * DK + c] = acc; });
     mm64<DV, kRecThreads>(64, [&](int r, int s_) { return sT[r * MS + s_]; },
-             [&](int s_, int c) { return s_ < L ? sB[s_] * ld(a.v + tok(s_) * DV + c) : 0.f; },
+             [&](int s_, int c) {
+                 const float vv = ld(a.v + tok(s_ < L ? s_ : 0) * DV + c);
+                 return s_ < L ? sB[s_] * vv : 0.f;
+             },
              [&](int r, int c, float acc) { rec[R.U + r * DV + c] = acc; });
     __syncthreads();  // W and U~ are in the record
     // Q' = e^G Q - M W,  M U~
@@ -727,10 +734,14 @@ __global__ __launch_bounds__(kGradThreads) void bwd_intra_kernel(BwdK<XT, GT> a)
 #pragma unroll
         for (int it = 0; it < NP; ++it) {
             const int i = tid + it * kGradThreads, r = i / DK, c = i % DK;
+            // rows past the chunk's end read row 0 (L >= 1) and drop it, so
+            // no load sits under a branch that would wait for it
             const bool in = r < L;
-            kv[it] = in ? ld(a.k + tok(r) * DK + c) : 0.f;
-            qv[it] = in ? ld(a.q + tok(r) * DK + c) : 0.f;
-            gv[it] = in ? ld(a.la + tok(r) * DK + c) : 0.f;
+            const int64_t o = tok(in ? r : 0) * DK + c;
+            const float kr = ld(a.k + o), qr = ld(a.q + o), gr = ld(a.la + o);
+            kv[it] = in ? kr : 0.f;
+            qv[it] = in ? qr : 0.f;
+            gv[it] = in ? gr : 0.f;
         }
 #pragma unroll
         for (int it = 0; it < NP; ++it) {
@@ -821,13 +832,8 @@ __global__ __launch_bounds__(kGradThreads) void bwd_intra_kernel(BwdK<XT, GT> a)
     mm64i<DK, kGradThreads>(S != nullptr ? DV : 0, [&](int r, int col) { return gdO[r * DV + col]; },
              [&](int col, int i) { return S[i * DV + col]; },
              [&](int x, int r, int c, float dqe) {
-                 const float eg = expf(sG[r * KP + c]);
-                 // (rows past the chunk's end read row 0 and drop it: a load
-                 // under no branch, so the lane's loads go out together)
-                 const float qraw = ld(a.q + tok(r < L ? r : 0) * DK + c);
-                 const float qv = r < L ? qraw : 0.f;
-                 sq[x] = eg * dqe;
-                 sg[x] = eg * qv * dqe;
+                 sq[x] = expf(sG[r * KP + c]) * dqe;
+                 sg[x] = 0.f;  // (q's share, q e^G dQ_e, joins where q is in LDS)
              });
     mm64i<DK, kGradThreads>(DV, [&](int r, int col) { return gU[r * DV + col]; }, [&](int col, int i) { return dSe[i * DV + col]; },
              [&](int x, int r, int c, float dkh) {
@@ -897,7 +903,8 @@ __global__ __launch_bounds__(kGradThreads) void bwd_intra_kernel(BwdK<XT, GT> a)
 #pragma unroll
     for (int it = 0; it < NP; ++it) {
         const int i = tid + it * kGradThreads, r = i / DK, c = i % DK;
-        qn[it] = r < L ? ld(a.q + tok(r) * DK + c) : 0.f;
+        const float qraw = ld(a.q + tok(r < L ? r : 0) * DK + c);  // (a load under no branch)
+        qn[it] = r < L ? qraw : 0.f;
     }
     mm64<64, kGradThreads>(64, [&](int r, int s_) { return sdT[r * MS + s_]; }, [&](int s_, int c) { return sT[c * MS + s_]; },
              [&](int r, int c, float acc) { sP[r * MS + c] = acc; });
@@ -1001,9 +1008,10 @@ __global__ __launch_bounds__(kGradThreads) void bwd_intra_kernel(BwdK<XT, GT> a)
             for (int i = 0; i < 4; ++i) {
                 const int r = 16 * B + 4 * g + i, x = 4 * t + i;
                 const float kv = sK[r * KP + ch], qv = qcol[r * MS];
+                // sq holds e^G dQ_e until here: q's share of dG through it
+                sg[x] += qv * sq[x] + kv * dkr[i] + qv * dqr[i] - kv * dks[i];
                 sk[x] += dkr[i] + dks[i];
                 sq[x] += dqr[i];
-                sg[x] += kv * dkr[i] + qv * dqr[i] - kv * dks[i];
             }
         }
     }
@@ -1014,6 +1022,10 @@ __global__ __launch_bounds__(kGradThreads) void bwd_intra_kernel(BwdK<XT, GT> a)
         const int lane = tid & 63, g = lane >> 4, cl = lane & 15;
         const D dl(tid >> 6);
         if (dl.active) {
+            // Every sum is taken into a register before the first store: a
+            // sum the compiler left in scratch is otherwise reloaded between
+            // stores, and each reload then waits for the stores before it.
+            float vq[NS], vk[NS];
 #pragma unroll
             for (int i = 0; i < D::RPW; ++i)
 #pragma unroll
@@ -1023,9 +1035,22 @@ __global__ __launch_bounds__(kGradThreads) void bwd_intra_kernel(BwdK<XT, GT> a)
                         const int x = (i * D::CPW + jj) * 4 + e;
                         const int r = dl.r0 + 16 * i + 4 * g + e, c = dl.c0 + 16 * jj + cl;
                         sG[r * KP + c] = sg[x] + (r == 63 ? sdGl[c] : 0.f);
+                        vq[x] = sq[x];
+                        vk[x] = sk[x];
+                        asm volatile("" : "+v"(vq[x]), "+v"(vk[x]));
+                    }
+            asm volatile("" ::: "memory");
+#pragma unroll
+            for (int i = 0; i < D::RPW; ++i)
+#pragma unroll
+                for (int jj = 0; jj < D::CPW; ++jj)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int x = (i * D::CPW + jj) * 4 + e;
+                        const int r = dl.r0 + 16 * i + 4 * g + e, c = dl.c0 + 16 * jj + cl;
                         if (r < L) {
-                            a.dq[tok(r) * DK + c] = sq[x];
-                            a.dk[tok(r) * DK + c] = sk[x];
+                            a.dq[tok(r) * DK + c] = vq[x];
+                            a.dk[tok(r) * DK + c] = vk[x];
                         }
                     }
         }
