@@ -55,6 +55,9 @@ struct BwdK {
 // waves, 2.70 with 8, 2.38 with 16).
 constexpr int kRecThreads = 1024;
 constexpr int kGradThreads = 1024;
+// runs of 16 terms a product of the gradient kernel keeps in flight ahead of
+// the one it multiplies, where an operand comes from global memory
+constexpr int kAhead = 2;
 
 // Row stride (floats) of the 64 x 64 matrices in LDS (A, M, T, dT, P): the
 // products below read 16 rows at one column and 16 columns at one row, and
@@ -95,8 +98,9 @@ struct Deal64 {
 // of 16, four consecutive elements of a row-major A row.  A(r, k), B(k, c)
 // read the operands; out(idx, r, c, acc) takes each result once, idx being
 // its index among the lane's PER_LANE results (a constant once unrolled).
-template <int N, int NT, typename FA, typename FB, typename FO>
+template <int N, int NT, int AHEAD = 1, typename FA, typename FB, typename FO>
 __device__ __forceinline__ void mm64i(int K, FA A, FB B, FO out) {
+    static_assert(AHEAD == 1 || AHEAD == 2, "one or two runs in flight");
     using D = Deal64<N, NT>;
     constexpr int RPW = D::RPW, CPW = D::CPW;
     const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
@@ -129,18 +133,45 @@ __device__ __forceinline__ void mm64i(int K, FA A, FB B, FO out) {
                 for (int jj = 0; jj < CPW; ++jj)
                     acc[i][jj] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[i][j], bv[jj][j], acc[i][jj], 0, 0, 0);
     };
-    // two register sets: the next run's loads are in flight while this run's
-    // products are issued (a clamped run index repeats a load that is not used)
     float a0[RPW][4], b0[CPW][4], a1[RPW][4], b1[CPW][4];
-    if (K > 0) load(0, a0, b0);
+    if constexpr (AHEAD == 1) {
+        // two register sets: the next run's loads are in flight while this
+        // run's products are issued (a clamped run index repeats a load that
+        // is not used)
+        if (K > 0) load(0, a0, b0);
 #pragma unroll 1
-    for (int k0 = 0; k0 < K; k0 += 32) {
-        const bool two = k0 + 16 < K;
-        load(two ? k0 + 16 : k0, a1, b1);
-        mma(a0, b0);
-        if (two) {
-            load(k0 + 32 < K ? k0 + 32 : k0 + 16, a0, b0);
-            mma(a1, b1);
+        for (int k0 = 0; k0 < K; k0 += 32) {
+            const bool two = k0 + 16 < K;
+            load(two ? k0 + 16 : k0, a1, b1);
+            mma(a0, b0);
+            if (two) {
+                load(k0 + 32 < K ? k0 + 32 : k0 + 16, a0, b0);
+                mma(a1, b1);
+            }
+        }
+    } else {
+        // three register sets: the two next runs' loads are in flight while
+        // this run's products are issued, for operands that come from global
+        // memory (one round trip then covers two runs); the runs are
+        // multiplied in the same order as above
+        float a2[RPW][4], b2[CPW][4];
+        auto cl = [&](int k) { return k < K ? k : K - 16; };
+        if (K > 0) {
+            load(0, a0, b0);
+            load(cl(16), a1, b1);
+        }
+#pragma unroll 1
+        for (int k0 = 0; k0 < K; k0 += 48) {
+            load(cl(k0 + 32), a2, b2);
+            mma(a0, b0);
+            if (k0 + 16 < K) {
+                load(cl(k0 + 48), a0, b0);
+                mma(a1, b1);
+                if (k0 + 32 < K) {
+                    load(cl(k0 + 64), a1, b1);
+                    mma(a2, b2);
+                }
+            }
         }
     }
 #pragma unroll
@@ -219,9 +250,9 @@ __device__ __forceinline__ void mm64i2(int K, FA1 A1, FA2 A2, FB B, FO1 out1, FO
 }
 
 // mm64i for callers that need no result index
-template <int N, int NT, typename FA, typename FB, typename FO>
+template <int N, int NT, int AHEAD = 1, typename FA, typename FB, typename FO>
 __device__ __forceinline__ void mm64(int K, FA A, FB B, FO out) {
-    mm64i<N, NT>(K, A, B, [&](int, int r, int c, float v) { out(r, c, v); });
+    mm64i<N, NT, AHEAD>(K, A, B, [&](int, int r, int c, float v) { out(r, c, v); });
 }
 
 // e^x for x <= 0 (a decay between two tokens of a chunk) through the
@@ -822,27 +853,27 @@ __global__ __launch_bounds__(kGradThreads) void bwd_intra_kernel(BwdK<XT, GT> a)
     }
     __syncthreads();
     // ---- 2. dU = M^T dO + K^ dS_end
-    mm64<DV, kGradThreads>(64, [&](int r, int s_) { return sM[s_ * MS + r]; }, [&](int s_, int c) { return gdO[s_ * DV + c]; },
+    mm64<DV, kGradThreads, kAhead>(64, [&](int r, int s_) { return sM[s_ * MS + r]; }, [&](int s_, int c) { return gdO[s_ * DV + c]; },
              [&](int r, int c, float acc) { gdU[r * DV + c] = acc; });
-    mm64<DV, kGradThreads>(DK, [&](int r, int kk) { return rec[R.Kh + r * DK + kk]; }, [&](int kk, int c) { return dSe[kk * DV + c]; },
+    mm64<DV, kGradThreads, kAhead>(DK, [&](int r, int kk) { return rec[R.Kh + r * DK + kk]; }, [&](int kk, int c) { return dSe[kk * DV + c]; },
              [&](int r, int c, float acc) { gdU[r * DV + c] += acc; });  // (same thread, same element)
     __syncthreads();
     // ---- 3. dQ_e = dO S^T, dK^ = U dS_end^T, dW = -dU S^T; the sums of dq,
     // dk, dG start here (Q_e = e^G Q, K^ = e^{G_last - G} K)
-    mm64i<DK, kGradThreads>(S != nullptr ? DV : 0, [&](int r, int col) { return gdO[r * DV + col]; },
+    mm64i<DK, kGradThreads, kAhead>(S != nullptr ? DV : 0, [&](int r, int col) { return gdO[r * DV + col]; },
              [&](int col, int i) { return S[i * DV + col]; },
              [&](int x, int r, int c, float dqe) {
                  sq[x] = expf(sG[r * KP + c]) * dqe;
                  sg[x] = 0.f;  // (q's share, q e^G dQ_e, joins where q is in LDS)
              });
-    mm64i<DK, kGradThreads>(DV, [&](int r, int col) { return gU[r * DV + col]; }, [&](int col, int i) { return dSe[i * DV + col]; },
+    mm64i<DK, kGradThreads, kAhead>(DV, [&](int r, int col) { return gU[r * DV + col]; }, [&](int col, int i) { return dSe[i * DV + col]; },
              [&](int x, int r, int c, float dkh) {
                  const float eh = expf(sG[63 * KP + c] - sG[r * KP + c]), kv = sK[r * KP + c];
                  sk[x] = eh * dkh;
                  sg[x] -= eh * kv * dkh;
                  atomicAdd(&sdGl[c], eh * kv * dkh);  // (G_last's share of K^)
              });
-    mm64<DK, kGradThreads>(S != nullptr ? DV : 0, [&](int r, int col) { return gdU[r * DV + col]; },
+    mm64<DK, kGradThreads, kAhead>(S != nullptr ? DV : 0, [&](int r, int col) { return gdU[r * DV + col]; },
              [&](int col, int i) { return S[i * DV + col]; },
              [&](int r, int c, float acc) { gdW[r * DK + c] = -acc; });
     if (S != nullptr) {  // dgamma = diag(S dS_end^T); gamma = e^{G_last}
