@@ -898,9 +898,9 @@ __global__ __launch_bounds__(kGradThreads) void bwd_intra_kernel(BwdK<XT, GT> a)
     }
     __syncthreads();
     // ---- 4. dM = dO U^T (into M's place); dT = dU (B V)^T + dW (B K_e)^T
-    mm64<64, kGradThreads>(DV, [&](int r, int col) { return gdO[r * DV + col]; }, [&](int col, int s_) { return gU[s_ * DV + col]; },
+    mm64<64, kGradThreads, kAhead>(DV, [&](int r, int col) { return gdO[r * DV + col]; }, [&](int col, int s_) { return gU[s_ * DV + col]; },
              [&](int r, int s_, float acc) { sM[r * MS + s_] = s_ <= r ? acc : 0.f; });
-    mm64<64, kGradThreads>(DV, [&](int r, int col) { return gdU[r * DV + col]; },
+    mm64<64, kGradThreads, kAhead>(DV, [&](int r, int col) { return gdU[r * DV + col]; },
              [&](int col, int s_) {
                  const float vv = ld(a.v + tok(s_ < L ? s_ : 0) * DV + col);
                  return s_ < L ? vv : 0.f;
