@@ -255,6 +255,30 @@ __device__ __forceinline__ void mm64(int K, FA A, FB B, FO out) {
     mm64i<N, NT, AHEAD>(K, A, B, [&](int, int r, int c, float v) { out(r, c, v); });
 }
 
+// In place, the running sum down the 64 rows of each of the DK channels of
+// sG (row stride KP), by all NT threads: each sums RPS consecutive rows of
+// one channel, and the segments' totals are combined through tmp (NT floats,
+// distinct from sG).  The caller synchronises before and after.
+template <int DK, int NT, int KP>
+__device__ __forceinline__ void cumsum_rows(float* sG, float* tmp) {
+    constexpr int NSEG = NT / DK, RPS = 64 / NSEG;
+    static_assert(NSEG * DK == NT && NSEG * RPS == 64, "whole segments");
+    const int c = threadIdx.x % DK, seg = threadIdx.x / DK;
+    float v[RPS];
+    float run = 0.f;
+#pragma unroll
+    for (int i = 0; i < RPS; ++i) {
+        run += sG[(seg * RPS + i) * KP + c];
+        v[i] = run;
+    }
+    tmp[seg * DK + c] = run;
+    __syncthreads();
+    float off = 0.f;
+    for (int q = 0; q < seg; ++q) off += tmp[q * DK + c];
+#pragma unroll
+    for (int i = 0; i < RPS; ++i) sG[(seg * RPS + i) * KP + c] = v[i] + off;
+}
+
 // e^x for x <= 0 (a decay between two tokens of a chunk) through the
 // hardware base-2 exponential; x > 0 only occurs for entries that are masked
 // out, and is clamped to 0 so that nothing overflows
@@ -491,13 +515,7 @@ __global__ __launch_bounds__(kRecThreads) void chunk_records_kernel(BwdK<XT, GT>
     }
     if (tid < 64) sB[tid] = tid < L ? ld(a.beta + tok(tid)) : 0.f;
     __syncthreads();
-    if (tid < DK) {
-        float acc = 0.f;
-        for (int r = 0; r < 64; ++r) {
-            acc += sG[r * KP + tid];
-            sG[r * KP + tid] = acc;
-        }
-    }
+    cumsum_rows<DK, kRecThreads, KP>(sG, sA);  // (A is made after this)
     __syncthreads();
     // K^ and gamma (G_last = G_63: padded rows add no decay)
     for (int i = tid; i < 64 * DK; i += kRecThreads) {
@@ -788,13 +806,7 @@ __global__ __launch_bounds__(kGradThreads) void bwd_intra_kernel(BwdK<XT, GT> a)
     }
     if (tid < DK) sdGl[tid] = 0.f;
     __syncthreads();
-    if (tid < DK) {
-        float acc = 0.f;
-        for (int r = 0; r < 64; ++r) {
-            acc += sG[r * KP + tid];
-            sG[r * KP + tid] = acc;
-        }
-    }
+    cumsum_rows<DK, kGradThreads, KP>(sG, sA);  // (A is made after this)
     __syncthreads();
     // A (strictly lower) and M (lower with diagonal), by blocks on the matrix cores
     am_mfma<DK, kGradThreads>(sK, sT, sG, sA, sM);
